@@ -1,0 +1,135 @@
+"""Seeded synthetic inputs for the prefill and decode workloads.
+
+This module draws random numbers and rounds them to the storage dtype; it
+holds none of the method's arithmetic (no feature map, no state, no
+readout).  It is the one piece of code that both the HIP path's callers
+(tests, benchmark) and the fp64 oracle's callers use, so both sides see the
+very same values.
+
+Draw order per workload, all with ``torch.Generator('cpu').manual_seed(seed)``
+and fp32 ``randn`` / ``rand``:
+
+* prefill: Q, K, V (each [B, H, n, d], scaled by ``qk_std`` / ``v_std``),
+  then omega [d, m] = randn / sqrt(d) (Performer only), then u [H] ~ U(0, 1)
+  with the per-head decay a = 1 - 10^(lo + (hi - lo) u) (decayed only);
+* decode: mu = |randn| * ctx, nu = |randn| * ctx, then q, k, v, then omega.
+
+Tensors with bf16 storage are rounded once, fp32 -> bf16 round-to-nearest-even,
+here; omega, decay, mu and nu stay fp32.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import torch
+
+MAP_IDENTITY, MAP_ELU1, MAP_PERFORMER = 0, 1, 2
+MAP_NAMES = {MAP_IDENTITY: "identity", MAP_ELU1: "elu1",
+             MAP_PERFORMER: "performer"}
+
+
+@dataclasses.dataclass(frozen=True)
+class PrefillConfig:
+    name: str
+    B: int
+    H: int
+    n: int
+    d: int
+    dtype: torch.dtype = torch.bfloat16
+    mapk: int = MAP_ELU1
+    m: int = 0                       # Performer feature count (d_feat)
+    qk_std: float = 1.0
+    v_std: float = 1.0
+    decay: Optional[tuple] = None    # (lo, hi): 1 - a = 10^U(lo, hi)
+    causal: bool = True
+
+    @property
+    def d_feat(self) -> int:
+        return self.m if self.mapk == MAP_PERFORMER else self.d
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.H * self.n
+
+    def replace(self, **kw) -> "PrefillConfig":
+        return dataclasses.replace(self, **kw)
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    S: int
+    H: int
+    d: int
+    dtype: torch.dtype = torch.bfloat16
+    mapk: int = MAP_ELU1
+    m: int = 0
+    ctx: float = 4096.0              # state magnitude ~ context length
+    a: Optional[float] = 0.99        # one decay value for every head
+
+    @property
+    def d_feat(self) -> int:
+        return self.m if self.mapk == MAP_PERFORMER else self.d
+
+    def replace(self, **kw) -> "DecodeConfig":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads of the method's hot path, by what they are.
+TINY_FP32 = PrefillConfig("tiny_fp32_elu1_B1H1n256d16", B=1, H=1, n=256, d=16,
+                          dtype=torch.float32)
+ELU1_CAUSAL = PrefillConfig("elu1_causal_B4H8n4096d64", B=4, H=8, n=4096, d=64)
+DECAYED = PrefillConfig("decayed_elu1_B2H16n65536d128", B=2, H=16, n=65536,
+                        d=128, decay=(-3.0, -1.0))
+PERFORMER = PrefillConfig("performer_B4H8n8192d64m256", B=4, H=8, n=8192, d=64,
+                          mapk=MAP_PERFORMER, m=256, qk_std=0.5)
+DECODE = DecodeConfig("decode_S256H32d128_a0.99", S=256, H=32, d=128)
+
+PREFILL_CONFIGS = {c.name: c for c in (TINY_FP32, ELU1_CAUSAL, DECAYED,
+                                       PERFORMER)}
+
+
+def _round(x: torch.Tensor, dtype: torch.dtype) -> torch.Tensor:
+    return x.to(dtype) if dtype != torch.float32 else x
+
+
+def make_prefill(cfg: PrefillConfig, seed: int = 0) -> dict:
+    """CPU tensors q, k, v (storage dtype), omega (fp32 or None),
+    decay (fp32 [H] or None)."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    shape = (cfg.B, cfg.H, cfg.n, cfg.d)
+    q = torch.randn(shape, generator=g) * cfg.qk_std
+    k = torch.randn(shape, generator=g) * cfg.qk_std
+    v = torch.randn(shape, generator=g) * cfg.v_std
+    omega = None
+    if cfg.mapk == MAP_PERFORMER:
+        omega = torch.randn((cfg.d, cfg.m), generator=g) / (cfg.d ** 0.5)
+    decay = None
+    if cfg.decay is not None:
+        lo, hi = cfg.decay
+        u = torch.rand((cfg.H,), generator=g)
+        decay = (1.0 - torch.pow(10.0, lo + (hi - lo) * u)).to(torch.float32)
+    return {"q": _round(q, cfg.dtype), "k": _round(k, cfg.dtype),
+            "v": _round(v, cfg.dtype), "omega": omega, "decay": decay}
+
+
+def make_decode(cfg: DecodeConfig, seed: int = 0) -> dict:
+    """CPU tensors mu [S,H,d_feat,d], nu [S,H,d_feat] (fp32); q, k, v [S,H,d]
+    (storage dtype); omega; decay [H] fp32 or None."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    df = cfg.d_feat
+    mu = torch.randn((cfg.S, cfg.H, df, cfg.d), generator=g).abs() * cfg.ctx
+    nu = torch.randn((cfg.S, cfg.H, df), generator=g).abs() * cfg.ctx
+    q = torch.randn((cfg.S, cfg.H, cfg.d), generator=g)
+    k = torch.randn((cfg.S, cfg.H, cfg.d), generator=g)
+    v = torch.randn((cfg.S, cfg.H, cfg.d), generator=g)
+    omega = None
+    if cfg.mapk == MAP_PERFORMER:
+        omega = torch.randn((cfg.d, cfg.m), generator=g) / (cfg.d ** 0.5)
+    decay = None
+    if cfg.a is not None:
+        decay = torch.full((cfg.H,), float(cfg.a), dtype=torch.float32)
+    return {"mu": mu, "nu": nu, "q": _round(q, cfg.dtype),
+            "k": _round(k, cfg.dtype), "v": _round(v, cfg.dtype),
+            "omega": omega, "decay": decay}

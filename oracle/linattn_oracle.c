@@ -1,0 +1,186 @@
+/*
+ * Plain fp64 CPU oracle for causal kernelized linear attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header, table or helper with
+ * the HIP library; it is written directly from the pages' equations.
+ *
+ * Sources (page titles, sections, equations):
+ *   [LA]  "2.2 Linear Attention" (efficient2 page): feature-mapped Q' = phi(Q),
+ *         K' = phi(K) (text before eq 6); eq 6 (D^-1 (Q'(K'^T V)));
+ *         eqs 7-8 (running sums mu_j, nu_j); eq 9 and its causal form
+ *         (readout q'_j mu_j / q'_j nu_j); eqs 10-11 (decayed sums with a).
+ *   [KM]  "3.2 Reducing d" (efficient1 page): eqs 22-27, the kernelized
+ *         attention c_i = phi(q_i) (sum phi(k_j)^T v_j) / phi(q_i) (sum phi(k_j)^T),
+ *         and the remark that both sums are kept and updated as new keys and
+ *         values arrive.
+ *   [RF]  "Linear attention research 2026" page, section on Performer random
+ *         features: phi(x) = exp(x . omega - |x|^2 / 2) / sqrt(m); section on
+ *         the Linear Transformer: phi(x) = elu(x) + 1.
+ *
+ * Readings where the pages leave a step open (each also listed in the design
+ * notes): elu's alpha is 1; the mask is inclusive (position i sees itself);
+ * the prefill state starts at zero; no epsilon is added to the denominator;
+ * the decode readout is taken after the state update; omega [d, m] is an
+ * input shared by every batch and head; decay is one value a per head.
+ *
+ * Arithmetic is IEEE fp64 throughout, in the order the equations state: the
+ * literal per-position recurrence, no chunking, no blocking, no reordering.
+ * Inputs arrive already widened to fp64 from whatever storage precision the
+ * caller used.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORC_MAP_IDENTITY = 0, ORC_MAP_ELU1 = 1, ORC_MAP_PERFORMER = 2 };
+
+/* [RF] Linear Transformer: phi(x) = elu(x) + 1 with alpha = 1, i.e. x + 1 for
+ * x > 0 and exp(x) otherwise. */
+static double elu_plus_one(double x) { return x > 0.0 ? x + 1.0 : exp(x); }
+
+/* Feature map of one row x[0..d) into y[0..dfeat).  d is the width of the
+ * q/k rows as stored.
+ *   IDENTITY : y = x (dfeat == d), the caller already feature-mapped.
+ *   ELU1     : y_c = elu(x_c) + 1 (dfeat == d)                       [RF]
+ *   PERFORMER: u_r = sum_c x_c omega[c][r]; y_r = exp(u_r - |x|^2/2)/sqrt(m)
+ *              with omega stored row-major [d][m] (dfeat == m)       [RF]   */
+static void feature_row(const double *x, double *y, int d, int dfeat, int map,
+                        const double *omega) {
+  if (map == ORC_MAP_IDENTITY) {
+    for (int c = 0; c < d; ++c) y[c] = x[c];
+  } else if (map == ORC_MAP_ELU1) {
+    for (int c = 0; c < d; ++c) y[c] = elu_plus_one(x[c]);
+  } else {
+    double sq = 0.0;
+    for (int c = 0; c < d; ++c) sq += x[c] * x[c];
+    const double inv_sqrt_m = 1.0 / sqrt((double)dfeat);
+    for (int r = 0; r < dfeat; ++r) {
+      double u = 0.0;
+      for (int c = 0; c < d; ++c) u += x[c] * omega[(int64_t)c * dfeat + r];
+      y[r] = exp(u - 0.5 * sq) * inv_sqrt_m;
+    }
+  }
+}
+
+/* Row-wise feature map over `rows` rows: x [rows][d] -> y [rows][dfeat]. */
+void oracle_featmap(const double *x, double *y, const double *omega,
+                    int64_t rows, int d, int dfeat, int map) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < rows; ++i)
+    feature_row(x + i * d, y + i * dfeat, d, dfeat, map, omega);
+}
+
+/* One state update, eqs 7-8 (no decay) or eqs 10-11 (decay a):
+ *   mu <- a mu + (1-a) k'^T v,   nu <- a nu + (1-a) k'
+ * mu is [dfeat][d] row-major: mu[f][e] accumulates k'_f v_e.            [LA] */
+static void state_update(double *mu, double *nu, const double *kf,
+                         const double *v, int d, int dfeat, int has_decay,
+                         double a) {
+  if (has_decay) {
+    const double b = 1.0 - a;
+    for (int f = 0; f < dfeat; ++f) {
+      for (int e = 0; e < d; ++e)
+        mu[f * d + e] = a * mu[f * d + e] + b * kf[f] * v[e];
+      nu[f] = a * nu[f] + b * kf[f];
+    }
+  } else {
+    for (int f = 0; f < dfeat; ++f) {
+      for (int e = 0; e < d; ++e) mu[f * d + e] += kf[f] * v[e];
+      nu[f] += kf[f];
+    }
+  }
+}
+
+/* Readout, eq 9 (and its causal form): out = (q' mu) / (q' . nu).  No epsilon:
+ * IEEE division, so a zero denominator gives inf or nan.                 [LA] */
+static void readout(const double *mu, const double *nu, const double *qf,
+                    double *out, int d, int dfeat) {
+  double den = 0.0;
+  for (int f = 0; f < dfeat; ++f) den += qf[f] * nu[f];
+  for (int e = 0; e < d; ++e) {
+    double num = 0.0;
+    for (int f = 0; f < dfeat; ++f) num += qf[f] * mu[f * d + e];
+    out[e] = num / den;
+  }
+}
+
+/* Full forward pass over B*H independent (batch, head) units.
+ *   q, k : [B][H][n][dqk]    v, out : [B][H][n][d]
+ *   dqk = d for ELU1 and PERFORMER, dqk = dfeat for IDENTITY.
+ *   omega: [d][dfeat] (PERFORMER only), decay: [H] or NULL (eqs 7-8).
+ * causal = 1: out_j reads mu_j, nu_j after position j is added (inclusive).
+ * causal = 0: every out_j reads the final mu_n, nu_n (eq 9).
+ * The state starts at zero for every unit.                                 */
+void oracle_forward(const double *q, const double *k, const double *v,
+                    double *out, int B, int H, int64_t n, int d, int dqk,
+                    int dfeat, int map, const double *omega,
+                    const double *decay, int causal) {
+  const int64_t units = (int64_t)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t u = 0; u < units; ++u) {
+    const int h = (int)(u % H);
+    const double *qu = q + u * n * dqk, *ku = k + u * n * dqk;
+    const double *vu = v + u * n * d;
+    double *ou = out + u * n * d;
+    double *mu = (double *)calloc((size_t)dfeat * d, sizeof(double));
+    double *nu = (double *)calloc((size_t)dfeat, sizeof(double));
+    double *qf = (double *)malloc(sizeof(double) * dfeat);
+    double *kf = (double *)malloc(sizeof(double) * dfeat);
+    const int has_decay = decay != NULL;
+    const double a = has_decay ? decay[h] : 1.0;
+    for (int64_t j = 0; j < n; ++j) {
+      feature_row(ku + j * dqk, kf, dqk, dfeat, map, omega);
+      state_update(mu, nu, kf, vu + j * d, d, dfeat, has_decay, a);
+      if (causal) {
+        feature_row(qu + j * dqk, qf, dqk, dfeat, map, omega);
+        readout(mu, nu, qf, ou + j * d, d, dfeat);
+      }
+    }
+    if (!causal) {
+      for (int64_t j = 0; j < n; ++j) {
+        feature_row(qu + j * dqk, qf, dqk, dfeat, map, omega);
+        readout(mu, nu, qf, ou + j * d, d, dfeat);
+      }
+    }
+    free(mu); free(nu); free(qf); free(kf);
+  }
+}
+
+/* One decode step per (sequence, head) unit: mu, nu hold the running sums of
+ * everything seen so far; a new (q, k, v) arrives; the sums are updated in
+ * place (eqs 7-8 or 10-11) and the new token's output is read out from the
+ * updated sums ([KM] remark after eq 27; [LA] causal form of eq 9).
+ *   mu: [S][H][dfeat][d]  nu: [S][H][dfeat]  q, k: [S][H][dqk]
+ *   v, out: [S][H][d]   (dqk = dfeat for IDENTITY, d otherwise)            */
+void oracle_decode(double *mu, double *nu, const double *q, const double *k,
+                   const double *v, double *out, int S, int H, int d, int dqk,
+                   int dfeat, int map, const double *omega,
+                   const double *decay) {
+  const int64_t units = (int64_t)S * H;
+#pragma omp parallel for schedule(static)
+  for (int64_t u = 0; u < units; ++u) {
+    const int h = (int)(u % H);
+    double *qf = (double *)malloc(sizeof(double) * dfeat);
+    double *kf = (double *)malloc(sizeof(double) * dfeat);
+    const int has_decay = decay != NULL;
+    const double a = has_decay ? decay[h] : 1.0;
+    double *muu = mu + u * (int64_t)dfeat * d, *nuu = nu + u * (int64_t)dfeat;
+    feature_row(k + u * dqk, kf, dqk, dfeat, map, omega);
+    state_update(muu, nuu, kf, v + u * d, d, dfeat, has_decay, a);
+    feature_row(q + u * dqk, qf, dqk, dfeat, map, omega);
+    readout(muu, nuu, qf, out + u * d, d, dfeat);
+    free(qf); free(kf);
+  }
+}
+
+/* Number of OpenMP threads a parallel region here would use (1 without
+ * OpenMP); reported beside the oracle's timing. */
+#ifdef _OPENMP
+#include <omp.h>
+int oracle_num_threads(void) { return omp_get_max_threads(); }
+#else
+int oracle_num_threads(void) { return 1; }
+#endif

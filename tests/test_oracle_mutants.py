@@ -1,0 +1,185 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each case copies the oracle's C source, plants one plausible mistake by a
+textual edit (a dropped term, a wrong sign, a swapped factor, a transposed
+operand, an off-by-one in the mask), compiles the copy into a temporary
+library, and runs the pin checks of ``test_oracle_pins`` against it.  The
+unmodified source must pass every check; every mutant must fail at least one.
+Everything runs on the CPU.
+"""
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import brute
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "linattn_oracle.c")
+
+MUTANTS = {
+    "exclusive_mask": (
+        "      state_update(mu, nu, kf, vu + j * d, d, dfeat, has_decay, a);\n"
+        "      if (causal) {\n"
+        "        feature_row(qu + j * dqk, qf, dqk, dfeat, map, omega);\n"
+        "        readout(mu, nu, qf, ou + j * d, d, dfeat);\n"
+        "      }\n",
+        "      if (causal) {\n"
+        "        feature_row(qu + j * dqk, qf, dqk, dfeat, map, omega);\n"
+        "        readout(mu, nu, qf, ou + j * d, d, dfeat);\n"
+        "      }\n"
+        "      state_update(mu, nu, kf, vu + j * d, d, dfeat, has_decay, a);\n"),
+    "nu_missing_one_minus_a": ("nu[f] = a * nu[f] + b * kf[f];",
+                               "nu[f] = a * nu[f] + kf[f];"),
+    "decay_factors_swapped": ("a * mu[f * d + e] + b * kf[f] * v[e]",
+                              "b * mu[f * d + e] + a * kf[f] * v[e]"),
+    "state_transposed_in_readout": ("num += qf[f] * mu[f * d + e];",
+                                    "num += qf[f] * mu[e * dfeat + f];"),
+    "denominator_dropped": ("out[e] = num / den;", "out[e] = num;"),
+    "elu_wrong_sign": ("x > 0.0 ? x + 1.0 : exp(x)",
+                       "x > 0.0 ? x + 1.0 : exp(-x)"),
+    "elu_no_plus_one": ("x > 0.0 ? x + 1.0 : exp(x)",
+                        "x > 0.0 ? x : exp(x) - 1.0"),
+    "performer_norm_sign": ("exp(u - 0.5 * sq)", "exp(u + 0.5 * sq)"),
+    "performer_no_half": ("exp(u - 0.5 * sq)", "exp(u - sq)"),
+    "performer_no_sqrt_m": ("y[r] = exp(u - 0.5 * sq) * inv_sqrt_m;",
+                            "y[r] = exp(u - 0.5 * sq);"),
+    "performer_omega_transposed": ("omega[(int64_t)c * dfeat + r]",
+                                   "omega[(int64_t)r * d + c]"),
+    "decode_readout_before_update": (
+        "    state_update(muu, nuu, kf, v + u * d, d, dfeat, has_decay, a);\n"
+        "    feature_row(q + u * dqk, qf, dqk, dfeat, map, omega);\n"
+        "    readout(muu, nuu, qf, out + u * d, d, dfeat);\n",
+        "    feature_row(q + u * dqk, qf, dqk, dfeat, map, omega);\n"
+        "    readout(muu, nuu, qf, out + u * d, d, dfeat);\n"
+        "    state_update(muu, nuu, kf, v + u * d, d, dfeat, has_decay, a);\n"),
+    "noncausal_reads_first_state": (
+        "    if (!causal) {\n      for (int64_t j = 0; j < n; ++j) {",
+        "    if (!causal) {\n      memset(mu, 0, sizeof(double) * dfeat * d);\n"
+        "      for (int64_t j = 0; j < n; ++j) {"),
+}
+
+
+def _compile(src_text, tmp_path, tag):
+    c = tmp_path / f"{tag}.c"
+    so = tmp_path / f"lib{tag}.so"
+    c.write_text(src_text)
+    subprocess.check_call(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared",
+                           "-std=c99", "-o", str(so), str(c), "-lm"])
+    lib = ctypes.CDLL(str(so))
+    P = ctypes.POINTER(ctypes.c_double)
+    i64, i32 = ctypes.c_int64, ctypes.c_int
+    lib.oracle_featmap.argtypes = [P, P, P, i64, i32, i32, i32]
+    lib.oracle_forward.argtypes = [P, P, P, P, i32, i32, i64, i32, i32, i32,
+                                   i32, P, P, i32]
+    lib.oracle_decode.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                  i32, P, P]
+    lib.oracle_num_threads.restype = i32
+    return lib
+
+
+def _close(a, b, tol):
+    a, b = np.asarray(a), np.asarray(b)
+    if not np.all(np.isfinite(a)):
+        return False
+    return np.max(np.abs(a - b)) <= tol * max(np.max(np.abs(b)), 1e-300)
+
+
+# ---- pin checks (each returns True when the pin holds) ---------------------
+
+def chk_bruteforce():
+    rng = np.random.default_rng(5)
+    for mapk in (oracle.MAP_ELU1, oracle.MAP_PERFORMER, oracle.MAP_IDENTITY):
+        for dec in (None, np.array([0.9, 0.7])):
+            for causal in (True, False):
+                d, m, n = 6, 8, 25
+                dqk = m if mapk == oracle.MAP_IDENTITY else d
+                q = rng.standard_normal((1, 2, n, dqk)) * 0.7
+                k = rng.standard_normal((1, 2, n, dqk)) * 0.7
+                if mapk == oracle.MAP_IDENTITY:
+                    q, k = np.abs(q) + 0.05, np.abs(k) + 0.05
+                v = rng.standard_normal((1, 2, n, d))
+                om = rng.standard_normal((d, m)) / math.sqrt(d)
+                got = oracle.forward(q, k, v, mapk, om, dec, causal)
+                want = brute.attention(q, k, v, mapk, om, dec, causal)
+                if not _close(got, want, 1e-12):
+                    return False
+    return True
+
+
+def chk_hand_examples():
+    q = np.ones((1, 1, 3, 1))
+    k = np.array([1.0, 2.0, 3.0]).reshape(1, 1, 3, 1)
+    v = np.array([2.0, 4.0, 6.0]).reshape(1, 1, 3, 1)
+    ok = _close(oracle.forward(q, k, v, oracle.MAP_IDENTITY).ravel(),
+                [2.0, 10 / 3, 28 / 6], 1e-15)
+    ok &= _close(oracle.forward(q, k, v, oracle.MAP_IDENTITY,
+                                decay=np.array([0.5])).ravel(),
+                 [2.0, 3.6, 11.25 / 2.125], 1e-15)
+    ok &= _close(oracle.forward(q, k, v, oracle.MAP_IDENTITY,
+                                causal=False).ravel(), [28 / 6] * 3, 1e-15)
+    return bool(ok)
+
+
+def chk_featmaps():
+    x = np.array([[0.0, 1.0, -1.0, 2.5]])
+    e = oracle.featmap(x, oracle.MAP_ELU1)[0]
+    if not _close(e, [1.0, 2.0, math.exp(-1.0), 3.5], 1e-15):
+        return False
+    d, m, t = 4, 6, 0.8
+    om = np.zeros((d, m))
+    om[0, 1] = 1.0
+    xx = np.zeros((1, d))
+    xx[0, 0] = t
+    want = np.full(m, math.exp(-t * t / 2) / math.sqrt(m))
+    want[1] = math.exp(t - t * t / 2) / math.sqrt(m)
+    return _close(oracle.featmap(xx, oracle.MAP_PERFORMER, om)[0], want, 1e-15)
+
+
+def chk_decode():
+    out, mu, nu = oracle.decode(np.full((1, 1, 1, 1), 2.0), np.ones((1, 1, 1)),
+                                np.ones((1, 1, 1)), np.ones((1, 1, 1)),
+                                np.full((1, 1, 1), 4.0), oracle.MAP_IDENTITY,
+                                decay=np.array([0.5]))
+    return out.item() == 3.0 and mu.item() == 3.0 and nu.item() == 1.0
+
+
+def chk_constant_v():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((1, 1, 40, 4))
+    k = rng.standard_normal((1, 1, 40, 4))
+    c = np.array([1.0, -2.0, 0.5, 3.0])
+    v = np.broadcast_to(c, (1, 1, 40, 4)).copy()
+    for dec in (None, np.array([0.8])):
+        if not _close(oracle.forward(q, k, v, oracle.MAP_ELU1, decay=dec),
+                      np.broadcast_to(c, v.shape), 1e-13):
+            return False
+    return True
+
+
+CHECKS = [chk_bruteforce, chk_hand_examples, chk_featmaps, chk_decode,
+          chk_constant_v]
+
+
+def _run_checks(lib, monkeypatch):
+    monkeypatch.setattr(oracle, "_lib", lib)
+    return {c.__name__: bool(c()) for c in CHECKS}
+
+
+def test_unmodified_oracle_passes_all_checks(tmp_path, monkeypatch):
+    lib = _compile(open(SRC).read(), tmp_path, "clean")
+    res = _run_checks(lib, monkeypatch)
+    assert all(res.values()), res
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path, monkeypatch):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique/found"
+    lib = _compile(src.replace(old, new), tmp_path, name)
+    res = _run_checks(lib, monkeypatch)
+    assert not all(res.values()), f"mutant {name} passed every pin: {res}"
