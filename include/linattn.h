@@ -1,0 +1,142 @@
+/*
+ * linattn.h -- C ABI of the MI355X (gfx950) causal kernelized linear-attention
+ * library (liblinattn.so).
+ *
+ * What it computes.  Per (batch, head) unit, with a positive feature map phi
+ * applied row by row, Q' = phi(Q), K' = phi(K) in R^{n x d'}:
+ *
+ *   mu_j = g mu_{j-1} + b k'_j^T v_j      (d' x d state)
+ *   nu_j = g nu_{j-1} + b k'_j^T          (d' normaliser)
+ *   out_j = (q'_j mu_j) / (q'_j . nu_j)   (causal: j reads its own state)
+ *
+ * with g = b = 1 (no decay) or g = a, b = 1 - a (decay a per head), and zero
+ * initial state.  Non-causal: every out_j reads mu_n, nu_n.
+ * Sources: "2.2 Linear Attention" (efficient2 page), the feature-mapped Q', K'
+ * before eq 6, eq 6, eqs 7-8 (running sums), eq 9 and its causal form, eqs
+ * 10-11 (decayed sums); "3.2 Reducing d" (efficient1 page) eqs 22-27 and the
+ * remark that both sums are kept and updated as new keys and values arrive;
+ * "Linear attention research 2026" page: elu(x) + 1 (Linear Transformer) and
+ * exp(x omega - |x|^2/2)/sqrt(m) (Performer random features).
+ *
+ * Conventions for every entry point.
+ *   - Every tensor pointer is DEVICE memory owned by the caller.  The library
+ *     never allocates, frees or retains caller memory.
+ *   - Row-major, contiguous, no padding.  Prefill tensors are [B][H][n][.],
+ *     decode tensors [S][H][.].
+ *   - `dtype` is the storage type of q, k, v and out (LA_F32 or LA_BF16).
+ *     omega, decay, mu and nu are always fp32.  Arithmetic is fp32 with bf16
+ *     (LA_BF16) or fp32 (LA_F32) matrix-core operands.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.
+ *     Calls are asynchronous: they return once the work is enqueued.
+ *   - Arguments are validated on the host before anything is enqueued; no
+ *     device memory is read for validation.  Decay values and NaN/Inf in the
+ *     data are not checked: a must lie in [0, 1].
+ *   - Zero sizes (B, H, n, S or rows equal to 0) are a no-op returning LA_OK.
+ *   - On error nothing is enqueued (LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED,
+ *     LA_ERR_WORKSPACE) or the launch failed (LA_ERR_HIP).  A description of
+ *     the last error of the calling thread is kept for la_last_error().
+ *   - No C++ exception crosses the ABI.
+ */
+#ifndef LINATTN_H
+#define LINATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum la_status {
+  LA_OK = 0,
+  LA_ERR_INVALID_ARG = 1, /* null pointer, negative size, inconsistent sizes */
+  LA_ERR_UNSUPPORTED = 2, /* valid request outside the built kernel set      */
+  LA_ERR_WORKSPACE = 3,   /* workspace NULL but required                     */
+  LA_ERR_HIP = 4          /* a HIP launch or runtime call failed             */
+} la_status;
+
+typedef enum la_map {
+  LA_MAP_IDENTITY = 0,  /* q, k are already features: d_feat wide          */
+  LA_MAP_ELU1 = 1,      /* phi(x) = elu(x) + 1 (alpha 1), d_feat == d       */
+  LA_MAP_PERFORMER = 2  /* phi(x) = exp(x omega - |x|^2/2)/sqrt(m), d_feat == m */
+} la_map;
+
+typedef enum la_dtype { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
+
+/*
+ * la_featmap -- phi applied row by row: x [rows][d] -> x_feat [rows][d_feat].
+ *   "Linear attention research 2026" page, Performer and Linear Transformer
+ *   sections; Q' = phi(Q) of "2.2 Linear Attention".
+ *   x      : device, in_dt, [rows][d]
+ *   x_feat : device, out_dt, [rows][d_feat] with d_feat = m (PERFORMER) or d
+ *   omega  : device fp32 [d][m] for PERFORMER (one projection shared by all
+ *            rows); ignored (may be NULL) otherwise
+ *   m      : feature count for PERFORMER; ignored otherwise
+ *   Supported: d in {16, 32, 64, 128}; m a multiple of 16 in [16, 256].
+ */
+la_status la_featmap(const void *x, void *x_feat, const float *omega,
+                     int64_t rows, int d, int m, la_map map, la_dtype in_dt,
+                     la_dtype out_dt, void *stream);
+
+/*
+ * la_forward_workspace_bytes -- device workspace la_forward needs for these
+ * sizes (0 when none).  Pure host function, never fails: returns 0 for
+ * arguments la_forward would reject.
+ */
+size_t la_forward_workspace_bytes(int B, int H, int64_t n, int d, int d_feat,
+                                  la_map map, la_dtype dtype, int causal);
+
+/*
+ * la_forward -- causal (causal = 1) or non-causal (causal = 0) kernelized
+ * attention over B*H independent units, state starting at zero.
+ *   "2.2 Linear Attention" eqs 7-11 and the causal form of eq 9; non-causal
+ *   is eq 9 with mu_n, nu_n (eq 6; "3.2 Reducing d" eq 27).
+ *   q, k     : device, dtype, [B][H][n][d] (ELU1, PERFORMER) or
+ *              [B][H][n][d_feat] (IDENTITY: already feature-mapped)
+ *   v, out   : device, dtype, [B][H][n][d]; out may not alias q, k or v
+ *   d_feat   : d for ELU1, m for PERFORMER, the feature width for IDENTITY
+ *   omega    : device fp32 [d][d_feat] for PERFORMER, else ignored
+ *   decay    : device fp32 [H], one a per head, or NULL for eqs 7-8
+ *   workspace: device, at least la_forward_workspace_bytes(...) bytes; NULL
+ *              allowed only when that is 0.  Scratch only: no content is
+ *              expected on entry or kept on exit.
+ *   Supported: d in {16, 32, 64, 128}; d_feat in {16, 32, 64, 128, 256}.
+ *   No epsilon is added to the denominator: with IDENTITY features whose
+ *   q'.nu is zero the output is inf/nan (IEEE).
+ */
+la_status la_forward(const void *q, const void *k, const void *v, void *out,
+                     int B, int H, int64_t n, int d, int d_feat, la_map map,
+                     const float *omega, const float *decay, int causal,
+                     la_dtype dtype, void *workspace, void *stream);
+
+/*
+ * la_decode_step -- one autoregressive step per (sequence, head) unit: the
+ * running sums are updated in place by the new (k, v) and the new token's
+ * output is read out from the UPDATED sums (it attends to itself).
+ *   "3.2 Reducing d", remark after eq 27 (keep both sums, update them as new
+ *   keys and values arrive); "2.2 Linear Attention" eqs 7-8 / 10-11 and the
+ *   causal form of eq 9.
+ *   mu    : device fp32 [S][H][d_feat][d], read and overwritten
+ *   nu    : device fp32 [S][H][d_feat], read and overwritten
+ *   q, k  : device, dtype, [S][H][d] (or [S][H][d_feat] for IDENTITY)
+ *   v, out: device, dtype, [S][H][d]
+ *   omega : device fp32 [d][d_feat] for PERFORMER, else ignored
+ *   decay : device fp32 [H] or NULL (no decay: mu += k'^T v, nu += k')
+ *   Supported: d in {16, 32, 64, 128}; d_feat in {16, 32, 64, 128, 256}.
+ */
+la_status la_decode_step(float *mu, float *nu, const void *q, const void *k,
+                         const void *v, void *out, int S, int H, int d,
+                         int d_feat, la_map map, const float *omega,
+                         const float *decay, la_dtype dtype, void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *la_status_str(la_status status);
+
+/* Description of the calling thread's last error ("" if none). */
+const char *la_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_H */

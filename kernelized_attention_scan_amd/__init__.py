@@ -1,0 +1,14 @@
+"""Causal kernelized linear attention for AMD Instinct MI355X (gfx950).
+
+The computation runs in hand-written HIP kernels behind the C ABI of
+``liblinattn.so`` (include/linattn.h); this package is its thin Python binding
+(``forward``, ``decode_step``, ``featmap``) plus the seeded input generators in
+``inputs``.  Build the library with ``python -m kernelized_attention_scan_amd.build``.
+"""
+from ._binding import (LA_BF16, LA_F32, LIB_PATH, MAP_ELU1, MAP_IDENTITY,
+                       MAP_PERFORMER, SYMBOLS, LinAttnError, decode_step,
+                       featmap, forward, forward_workspace_bytes, load_library)
+
+__all__ = ["forward", "decode_step", "featmap", "forward_workspace_bytes",
+           "load_library", "LinAttnError", "LIB_PATH", "SYMBOLS", "MAP_IDENTITY",
+           "MAP_ELU1", "MAP_PERFORMER", "LA_F32", "LA_BF16"]

@@ -1,0 +1,217 @@
+"""ctypes binding of liblinattn.so (the C ABI declared in include/linattn.h).
+
+Argument marshalling only: tensor checks, raw device pointers, the caller's
+current HIP stream, and a workspace tensor from torch's allocator.  Every step
+of the computation runs in the library's HIP kernels; there is no fallback.
+If the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch
+
+LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP = \
+    range(5)
+MAP_IDENTITY, MAP_ELU1, MAP_PERFORMER = 0, 1, 2
+LA_F32, LA_BF16 = 0, 1
+
+_MAPS = {"identity": MAP_IDENTITY, "elu1": MAP_ELU1, "performer": MAP_PERFORMER}
+_DTYPES = {torch.float32: LA_F32, torch.bfloat16: LA_BF16}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                        "liblinattn.so")
+
+# Exported symbols, in the order include/linattn.h declares them.
+SYMBOLS = ("la_featmap", "la_forward_workspace_bytes", "la_forward",
+           "la_decode_step", "la_status_str", "la_last_error")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class LinAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load liblinattn.so once; raise if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build the HIP library first "
+                "(python -m kernelized_attention_scan_amd.build)")
+        lib = ctypes.CDLL(path)
+        vp, i32, i64, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                            ctypes.c_size_t)
+        lib.la_featmap.argtypes = [vp, vp, vp, i64, i32, i32, i32, i32, i32, vp]
+        lib.la_featmap.restype = i32
+        lib.la_forward_workspace_bytes.argtypes = [i32, i32, i64, i32, i32,
+                                                   i32, i32, i32]
+        lib.la_forward_workspace_bytes.restype = sz
+        lib.la_forward.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32,
+                                   i32, vp, vp, i32, i32, vp, vp]
+        lib.la_forward.restype = i32
+        lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                       i32, i32, vp, vp, i32, vp]
+        lib.la_decode_step.restype = i32
+        lib.la_status_str.argtypes = [i32]
+        lib.la_status_str.restype = ctypes.c_char_p
+        lib.la_last_error.argtypes = []
+        lib.la_last_error.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != LA_OK:
+        lib = load_library()
+        msg = lib.la_last_error().decode()
+        name = lib.la_status_str(status).decode()
+        raise LinAttnError(status, f"{what}: {name}: {msg}")
+
+
+def _map_code(feature_map) -> int:
+    if isinstance(feature_map, int):
+        return feature_map
+    try:
+        return _MAPS[feature_map]
+    except KeyError:
+        raise ValueError(f"unknown feature map {feature_map!r}") from None
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    try:
+        return _DTYPES[t]
+    except KeyError:
+        raise TypeError(f"unsupported storage dtype {t}") from None
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _f32(t: Optional[torch.Tensor], name: str) -> Optional[torch.Tensor]:
+    if t is None:
+        return None
+    _dev(t, name)
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32")
+    return t
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def forward_workspace_bytes(B: int, H: int, n: int, d: int, d_feat: int,
+                            feature_map="elu1", dtype=torch.bfloat16,
+                            causal: bool = True) -> int:
+    """Device workspace la_forward needs (0 if none or if rejected)."""
+    return int(load_library().la_forward_workspace_bytes(
+        B, H, n, d, d_feat, _map_code(feature_map), _dtype_code(dtype),
+        int(bool(causal))))
+
+
+def featmap(x: torch.Tensor, feature_map="elu1", omega=None,
+            out_dtype: Optional[torch.dtype] = None,
+            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """phi row by row over the last axis: [..., d] -> [..., d_feat]."""
+    lib = load_library()
+    _dev(x, "x")
+    mapk = _map_code(feature_map)
+    d = x.shape[-1]
+    m = omega.shape[1] if mapk == MAP_PERFORMER else d
+    out_dtype = out_dtype or x.dtype
+    if out is None:
+        out = torch.empty(x.shape[:-1] + (m,), dtype=out_dtype, device=x.device)
+    _dev(out, "out")
+    _f32(omega, "omega")
+    st = lib.la_featmap(_ptr(x), _ptr(out), _ptr(omega), x.numel() // d, d, m,
+                        mapk, _dtype_code(x.dtype), _dtype_code(out.dtype),
+                        _stream(x.device))
+    _check(st, "la_featmap")
+    return out
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+            feature_map="elu1", omega: Optional[torch.Tensor] = None,
+            decay: Optional[torch.Tensor] = None, causal: bool = True,
+            out: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Kernelized linear attention over q, k [B,H,n,d_qk], v [B,H,n,d]."""
+    lib = load_library()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, nm)
+    if q.dim() != 4 or v.dim() != 4 or q.shape != k.shape:
+        raise ValueError("q, k must be [B,H,n,d_qk] and v [B,H,n,d]")
+    B, H, n, d = v.shape
+    if q.shape[:3] != v.shape[:3]:
+        raise ValueError("q, k, v disagree on B, H, n")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    mapk = _map_code(feature_map)
+    d_feat = omega.shape[1] if mapk == MAP_PERFORMER else q.shape[-1]
+    if mapk != MAP_IDENTITY and q.shape[-1] != d:
+        raise ValueError("q, k must have width d for elu1 and performer")
+    _f32(omega, "omega")
+    _f32(decay, "decay")
+    if out is None:
+        out = torch.empty_like(v)
+    _dev(out, "out")
+    dt = _dtype_code(v.dtype)
+    need = lib.la_forward_workspace_bytes(B, H, n, d, d_feat, mapk, dt,
+                                          int(bool(causal)))
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=v.device)
+    st = lib.la_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, n, d,
+                        d_feat, mapk, _ptr(omega), _ptr(decay),
+                        int(bool(causal)), dt,
+                        _ptr(workspace) if need else None, _stream(v.device))
+    _check(st, "la_forward")
+    return out
+
+
+def decode_step(mu: torch.Tensor, nu: torch.Tensor, q: torch.Tensor,
+                k: torch.Tensor, v: torch.Tensor, feature_map="elu1",
+                omega: Optional[torch.Tensor] = None,
+                decay: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step; mu [S,H,d_feat,d] and nu [S,H,d_feat] are updated in
+    place.  Returns out [S,H,d]."""
+    lib = load_library()
+    _f32(mu, "mu")
+    _f32(nu, "nu")
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, nm)
+    S, H, d = v.shape
+    d_feat = mu.shape[2]
+    if mu.shape != (S, H, d_feat, d) or nu.shape != (S, H, d_feat):
+        raise ValueError("mu must be [S,H,d_feat,d] and nu [S,H,d_feat]")
+    _f32(omega, "omega")
+    _f32(decay, "decay")
+    if out is None:
+        out = torch.empty_like(v)
+    _dev(out, "out")
+    st = lib.la_decode_step(_ptr(mu), _ptr(nu), _ptr(q), _ptr(k), _ptr(v),
+                            _ptr(out), S, H, d, d_feat, _map_code(feature_map),
+                            _ptr(omega), _ptr(decay), _dtype_code(v.dtype),
+                            _stream(v.device))
+    _check(st, "la_decode_step")
+    return out

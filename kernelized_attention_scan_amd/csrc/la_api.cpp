@@ -1,0 +1,259 @@
+// C ABI of liblinattn.so: argument validation, workspace planning and kernel
+// dispatch.  Validation is pure host code that runs before any HIP call, so
+// invalid requests never touch a device.  See include/linattn.h for the
+// contract of every entry point.
+#include "linattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "la_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+la_status fail(la_status st, const char *fmt, ...)
+    __attribute__((format(printf, 2, 3)));
+la_status fail(la_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+la_status ok() {
+  g_last_error.clear();
+  return LA_OK;
+}
+
+la_status hip_fail(hipError_t e, const char *what) {
+  return fail(LA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool valid_map(int m) { return m == LA_MAP_IDENTITY || m == LA_MAP_ELU1 || m == LA_MAP_PERFORMER; }
+bool valid_dtype(int t) { return t == LA_F32 || t == LA_BF16; }
+bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool supported_feat(int f) {
+  return f == 16 || f == 32 || f == 64 || f == 128 || f == 256;
+}
+size_t elem_size(int t) { return t == LA_BF16 ? 2 : 4; }
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Sequence split of the chunked forward: about kTargetGroups workgroups in
+// total (two per compute unit of a 256-CU MI355X), segments of whole chunks.
+constexpr int64_t kTargetGroups = 512;
+
+struct FwdPlan {
+  const la::FwdOps *ops = nullptr;
+  int64_t seg_len = 0;
+  int nseg = 0;
+  bool need_states = false;
+  size_t feat_bytes = 0;    // one of Q', K' (PERFORMER only)
+  size_t state_bytes = 0;
+  size_t total() const { return 2 * feat_bytes + state_bytes; }
+};
+
+// Validates la_forward's sizes and enums (not pointers) and fills the plan.
+la_status plan_forward(int B, int H, int64_t n, int d, int d_feat, int map,
+                       int dtype, int causal, FwdPlan *p) {
+  if (B < 0 || H < 0 || n < 0)
+    return fail(LA_ERR_INVALID_ARG, "negative size: B=%d H=%d n=%lld", B, H,
+                static_cast<long long>(n));
+  if (!valid_map(map)) return fail(LA_ERR_INVALID_ARG, "unknown map %d", map);
+  if (!valid_dtype(dtype)) return fail(LA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (causal != 0 && causal != 1)
+    return fail(LA_ERR_INVALID_ARG, "causal must be 0 or 1, got %d", causal);
+  if (d <= 0 || d_feat <= 0)
+    return fail(LA_ERR_INVALID_ARG, "non-positive d=%d d_feat=%d", d, d_feat);
+  if (map == LA_MAP_ELU1 && d_feat != d)
+    return fail(LA_ERR_INVALID_ARG, "ELU1 needs d_feat == d (got %d, %d)", d_feat, d);
+  if (!supported_d(d) || !supported_feat(d_feat))
+    return fail(LA_ERR_UNSUPPORTED, "unsupported d=%d d_feat=%d", d, d_feat);
+  p->ops = dtype == LA_BF16 ? la::fwd_ops_bf16(d, d_feat) : la::fwd_ops_f32(d, d_feat);
+  if (!p->ops)
+    return fail(LA_ERR_UNSUPPORTED, "no %s kernel for d=%d d_feat=%d (LDS)",
+                dtype == LA_BF16 ? "bf16" : "fp32", d, d_feat);
+  const int64_t units = static_cast<int64_t>(B) * H;
+  if (units == 0 || n == 0) return LA_OK;
+  if (units > (int64_t{1} << 30) || n > (int64_t{1} << 40) ||
+      units * n > (int64_t{1} << 46))
+    return fail(LA_ERR_UNSUPPORTED, "sizes too large");
+  const int64_t C = p->ops->C;
+  const int64_t nchunks = (n + C - 1) / C;
+  int64_t per_unit = (kTargetGroups + units - 1) / units;
+  if (per_unit < 1) per_unit = 1;
+  if (per_unit > nchunks) per_unit = nchunks;
+  const int64_t cps = (nchunks + per_unit - 1) / per_unit;
+  p->seg_len = cps * C;
+  p->nseg = static_cast<int>((n + p->seg_len - 1) / p->seg_len);
+  if (units * p->nseg > (int64_t{1} << 31) - 1)
+    return fail(LA_ERR_UNSUPPORTED, "too many workgroups");
+  p->need_states = !causal || p->nseg > 1;
+  p->state_bytes = p->need_states
+                       ? align256(static_cast<size_t>(units) * (p->nseg + 1) *
+                                  p->ops->slot_floats * sizeof(float))
+                       : 0;
+  p->feat_bytes = map == LA_MAP_PERFORMER
+                      ? align256(static_cast<size_t>(units * n) * d_feat *
+                                 elem_size(dtype))
+                      : 0;
+  return LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *la_status_str(la_status s) {
+  switch (s) {
+    case LA_OK: return "LA_OK";
+    case LA_ERR_INVALID_ARG: return "LA_ERR_INVALID_ARG";
+    case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED";
+    case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE";
+    case LA_ERR_HIP: return "LA_ERR_HIP";
+  }
+  return "LA_ERR_UNKNOWN";
+}
+
+const char *la_last_error(void) { return g_last_error.c_str(); }
+
+la_status la_featmap(const void *x, void *x_feat, const float *omega,
+                     int64_t rows, int d, int m, la_map map, la_dtype in_dt,
+                     la_dtype out_dt, void *stream) {
+  try {
+    if (rows < 0) return fail(LA_ERR_INVALID_ARG, "negative rows");
+    if (!valid_map(map)) return fail(LA_ERR_INVALID_ARG, "unknown map %d", map);
+    if (!valid_dtype(in_dt) || !valid_dtype(out_dt))
+      return fail(LA_ERR_INVALID_ARG, "unknown dtype");
+    if (d <= 0) return fail(LA_ERR_INVALID_ARG, "non-positive d=%d", d);
+    if (map == LA_MAP_PERFORMER && m <= 0)
+      return fail(LA_ERR_INVALID_ARG, "non-positive m=%d", m);
+    if (!supported_d(d)) return fail(LA_ERR_UNSUPPORTED, "unsupported d=%d", d);
+    if (map == LA_MAP_PERFORMER && (m % 16 != 0 || m > 256))
+      return fail(LA_ERR_UNSUPPORTED, "unsupported m=%d (multiple of 16, <= 256)", m);
+    if (rows == 0) return ok();
+    if (!x || !x_feat) return fail(LA_ERR_INVALID_ARG, "null x or x_feat");
+    if (map == LA_MAP_PERFORMER && !omega)
+      return fail(LA_ERR_INVALID_ARG, "PERFORMER needs omega");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (map == LA_MAP_PERFORMER)
+      e = la::launch_featmap_performer(x, x_feat, omega, rows, d, m, in_dt,
+                                       out_dt, s);
+    else
+      e = la::launch_featmap_elementwise(x, x_feat, rows * d,
+                                         map == LA_MAP_ELU1, in_dt, out_dt, s);
+    if (e != hipSuccess) return hip_fail(e, "la_featmap launch");
+    return ok();
+  } catch (...) {
+    return fail(LA_ERR_HIP, "unexpected exception in la_featmap");
+  }
+}
+
+size_t la_forward_workspace_bytes(int B, int H, int64_t n, int d, int d_feat,
+                                  la_map map, la_dtype dtype, int causal) {
+  try {
+    const std::string saved = g_last_error;
+    FwdPlan p;
+    const la_status st = plan_forward(B, H, n, d, d_feat, map, dtype, causal, &p);
+    g_last_error = saved;
+    if (st != LA_OK) return 0;
+    return p.total();
+  } catch (...) {
+    return 0;
+  }
+}
+
+la_status la_forward(const void *q, const void *k, const void *v, void *out,
+                     int B, int H, int64_t n, int d, int d_feat, la_map map,
+                     const float *omega, const float *decay, int causal,
+                     la_dtype dtype, void *workspace, void *stream) {
+  try {
+    FwdPlan p;
+    const la_status st = plan_forward(B, H, n, d, d_feat, map, dtype, causal, &p);
+    if (st != LA_OK) return st;
+    const int64_t units = static_cast<int64_t>(B) * H;
+    if (units == 0 || n == 0) return ok();
+    if (!q || !k || !v || !out)
+      return fail(LA_ERR_INVALID_ARG, "null q, k, v or out");
+    if (map == LA_MAP_PERFORMER && !omega)
+      return fail(LA_ERR_INVALID_ARG, "PERFORMER needs omega");
+    if (p.total() > 0 && !workspace)
+      return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes required", p.total());
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    const void *qf = q, *kf = k;
+    if (map == LA_MAP_PERFORMER) {
+      // Q', K' into the workspace, then the identity-map forward over them.
+      hipError_t e = la::launch_featmap_performer(q, ws, omega, units * n, d,
+                                                  d_feat, dtype, dtype, s);
+      if (e == hipSuccess)
+        e = la::launch_featmap_performer(k, ws + p.feat_bytes, omega,
+                                         units * n, d, d_feat, dtype, dtype, s);
+      if (e != hipSuccess) return hip_fail(e, "la_forward feature map");
+      qf = ws;
+      kf = ws + p.feat_bytes;
+    }
+    la::FwdArgs a;
+    a.q = qf;
+    a.k = kf;
+    a.v = v;
+    a.out = out;
+    a.decay = decay;
+    a.states = p.need_states
+                   ? reinterpret_cast<float *>(ws + 2 * p.feat_bytes)
+                   : nullptr;
+    a.H = H;
+    a.n = n;
+    a.seg_len = p.seg_len;
+    a.nseg = p.nseg;
+    a.elu1 = map == LA_MAP_ELU1;
+    const hipError_t e = p.ops->run(a, units, causal, s);
+    if (e != hipSuccess) return hip_fail(e, "la_forward launch");
+    return ok();
+  } catch (...) {
+    return fail(LA_ERR_HIP, "unexpected exception in la_forward");
+  }
+}
+
+la_status la_decode_step(float *mu, float *nu, const void *q, const void *k,
+                         const void *v, void *out, int S, int H, int d,
+                         int d_feat, la_map map, const float *omega,
+                         const float *decay, la_dtype dtype, void *stream) {
+  try {
+    if (S < 0 || H < 0) return fail(LA_ERR_INVALID_ARG, "negative size");
+    if (!valid_map(map)) return fail(LA_ERR_INVALID_ARG, "unknown map %d", map);
+    if (!valid_dtype(dtype)) return fail(LA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    if (d <= 0 || d_feat <= 0)
+      return fail(LA_ERR_INVALID_ARG, "non-positive d=%d d_feat=%d", d, d_feat);
+    if (map == LA_MAP_ELU1 && d_feat != d)
+      return fail(LA_ERR_INVALID_ARG, "ELU1 needs d_feat == d");
+    if (!supported_d(d) || !la::decode_supported(d, d_feat))
+      return fail(LA_ERR_UNSUPPORTED, "unsupported d=%d d_feat=%d", d, d_feat);
+    const int64_t units = static_cast<int64_t>(S) * H;
+    if (units == 0) return ok();
+    if (units > (int64_t{1} << 31) - 1)
+      return fail(LA_ERR_UNSUPPORTED, "too many units");
+    if (!mu || !nu || !q || !k || !v || !out)
+      return fail(LA_ERR_INVALID_ARG, "null pointer argument");
+    if (map == LA_MAP_PERFORMER && !omega)
+      return fail(LA_ERR_INVALID_ARG, "PERFORMER needs omega");
+    const hipError_t e =
+        la::launch_decode(mu, nu, q, k, v, out, units, H, d, d_feat, map, omega,
+                          decay, dtype, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "la_decode_step launch");
+    return ok();
+  } catch (...) {
+    return fail(LA_ERR_HIP, "unexpected exception in la_decode_step");
+  }
+}
+
+}  // extern "C"

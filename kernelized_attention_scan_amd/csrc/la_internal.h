@@ -1,0 +1,58 @@
+// Host-side interface between the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace la {
+
+// Arguments of the chunked forward kernels.
+struct FwdArgs {
+  const void *q, *k, *v;
+  void *out;
+  const float *decay;   // [H] or null
+  float *states;        // [units][nseg + 1][slot] or null
+  int H;
+  int64_t n;
+  int64_t seg_len;      // multiple of the chunk length
+  int nseg;
+  int elu1;             // 1: phi = elu + 1 on q, k; 0: q, k are features
+};
+
+// Exclusive prefix of the segment aggregates, in place (slot nseg = total).
+hipError_t launch_scan(float *states, const float *decay, int H, int64_t n,
+                       int64_t seg_len, int nseg, int64_t units, int slot,
+                       int used, hipStream_t stream);
+
+// Launch set of one (storage type, d, d_feat) instance of the chunked forward.
+struct FwdOps {
+  int C;              // chunk rows
+  int slot_floats;    // floats per fp32 state slot
+  size_t lds_fwd, lds_agg;
+  // Enqueue: [agg + scan when args.states], then the forward kernel.
+  hipError_t (*run)(const FwdArgs &args, int64_t units, int causal,
+                    hipStream_t stream);
+};
+
+// nullptr when the combination is not built (unsupported size or LDS).
+const FwdOps *fwd_ops_bf16(int d, int d_feat);
+const FwdOps *fwd_ops_f32(int d, int d_feat);
+
+// Feature map launchers.  dtype codes: 0 fp32, 1 bf16.
+hipError_t launch_featmap_elementwise(const void *x, void *y, int64_t count,
+                                      int elu1, int in_dt, int out_dt,
+                                      hipStream_t stream);
+// Returns hipErrorInvalidValue for sizes it was not built for.
+hipError_t launch_featmap_performer(const void *x, void *y, const float *omega,
+                                    int64_t rows, int d, int m, int in_dt,
+                                    int out_dt, hipStream_t stream);
+
+// Decode step launcher (map: 0 identity, 1 elu1, 2 performer).
+hipError_t launch_decode(float *mu, float *nu, const void *q, const void *k,
+                         const void *v, void *out, int64_t units, int H, int d,
+                         int d_feat, int map, const float *omega,
+                         const float *decay, int dtype, hipStream_t stream);
+bool decode_supported(int d, int d_feat);
+
+}  // namespace la

@@ -1,0 +1,154 @@
+"""Host-side tests of the C ABI (no GPU, no compute call).
+
+The library must load, export every function include/linattn.h declares, and
+reject invalid arguments on the host with the documented status before any
+HIP call; zero sizes are a no-op.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import kernelized_attention_scan_amd as K
+from kernelized_attention_scan_amd import _binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(
+    __file__))), "include", "linattn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(K.LIB_PATH):
+        pytest.fail("liblinattn.so not built: run python -m "
+                    "kernelized_attention_scan_amd.build")
+    return K.load_library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert header_functions() == sorted(B.SYMBOLS)
+
+
+def test_library_exports_every_header_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
+
+
+def test_status_strings(lib):
+    names = [lib.la_status_str(i).decode() for i in range(5)]
+    assert names == ["LA_OK", "LA_ERR_INVALID_ARG", "LA_ERR_UNSUPPORTED",
+                     "LA_ERR_WORKSPACE", "LA_ERR_HIP"]
+    assert lib.la_status_str(99).decode() == "LA_ERR_UNKNOWN"
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def fwd(lib, B=1, H=1, n=64, d=64, df=64, mapk=1, omega=None, decay=None,
+        causal=1, dtype=1, ws=None, ptr=FAKE):
+    return lib.la_forward(ptr, ptr, ptr, ptr, B, H, n, d, df, mapk, omega,
+                          decay, causal, dtype, ws, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), B.LA_ERR_INVALID_ARG),
+    (dict(H=-2), B.LA_ERR_INVALID_ARG),
+    (dict(n=-5), B.LA_ERR_INVALID_ARG),
+    (dict(mapk=7), B.LA_ERR_INVALID_ARG),
+    (dict(dtype=5), B.LA_ERR_INVALID_ARG),
+    (dict(causal=2), B.LA_ERR_INVALID_ARG),
+    (dict(d=0), B.LA_ERR_INVALID_ARG),
+    (dict(df=-1), B.LA_ERR_INVALID_ARG),
+    (dict(df=32), B.LA_ERR_INVALID_ARG),             # ELU1 needs d_feat == d
+    (dict(d=48, df=48), B.LA_ERR_UNSUPPORTED),
+    (dict(d=256, df=256), B.LA_ERR_UNSUPPORTED),
+    (dict(mapk=0, df=512), B.LA_ERR_UNSUPPORTED),
+    (dict(mapk=2, df=256, omega=None), B.LA_ERR_INVALID_ARG),  # no omega
+    (dict(ptr=None), B.LA_ERR_INVALID_ARG),
+    (dict(B=8, n=4096, ws=None), B.LA_ERR_WORKSPACE),          # segments
+    (dict(causal=0, ws=None), B.LA_ERR_WORKSPACE),             # total state
+])
+def test_forward_rejects(lib, kw, status):
+    assert fwd(lib, **kw) == status
+    assert lib.la_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(n=0),
+                                dict(B=0, ptr=None)])
+def test_forward_zero_sizes_are_noops(lib, kw):
+    assert fwd(lib, **kw) == B.LA_OK
+
+
+def test_workspace_bytes(lib):
+    # single segment, causal, elu1: no workspace
+    assert K.forward_workspace_bytes(1, 1, 64, 64, 64) == 0
+    # rejected arguments report 0
+    assert K.forward_workspace_bytes(-1, 1, 64, 64, 64) == 0
+    assert K.forward_workspace_bytes(1, 1, 64, 48, 48) == 0
+    # segmented: units * (nseg + 1) fp32 slots of d' x d + d' (rounded to 64)
+    ws = K.forward_workspace_bytes(4, 8, 4096, 64, 64)
+    units, C = 32, 64
+    nseg = 16                                  # 512 target groups / 32 units
+    slot = (64 * 64 + 64 + 63) // 64 * 64
+    assert ws == (units * (nseg + 1) * slot * 4 + 255) // 256 * 256
+    # Performer adds Q' and K' (bf16, d_feat = m wide)
+    wp = K.forward_workspace_bytes(4, 8, 8192, 64, 256, "performer")
+    assert wp >= 2 * 4 * 8 * 8192 * 256 * 2
+    # non-causal always needs the total state
+    assert K.forward_workspace_bytes(1, 1, 64, 64, 64, causal=False) > 0
+    # fp32 storage with d_feat 256 and d 128 does not fit in LDS
+    assert K.forward_workspace_bytes(1, 1, 64, 128, 256, "identity",
+                                     dtype=__import__("torch").float32) == 0
+
+
+def test_featmap_rejects(lib):
+    f = lib.la_featmap
+    assert f(FAKE, FAKE, None, -1, 64, 0, 1, 1, 1, None) == B.LA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, None, 10, 64, 0, 9, 1, 1, None) == B.LA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, None, 10, 64, 0, 1, 3, 1, None) == B.LA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, None, 10, 48, 0, 1, 1, 1, None) == B.LA_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, None, 10, 64, 256, 2, 1, 1, None) == B.LA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, 10, 64, 250, 2, 1, 1, None) == B.LA_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, 10, 64, 512, 2, 1, 1, None) == B.LA_ERR_UNSUPPORTED
+    assert f(None, FAKE, None, 10, 64, 0, 1, 1, 1, None) == B.LA_ERR_INVALID_ARG
+    assert f(None, None, None, 0, 64, 0, 1, 1, 1, None) == B.LA_OK
+
+
+def test_decode_rejects(lib):
+    f = lib.la_decode_step
+    P = FAKE
+    assert f(P, P, P, P, P, P, -1, 1, 64, 64, 1, None, None, 1, None) == \
+        B.LA_ERR_INVALID_ARG
+    assert f(P, P, P, P, P, P, 1, 1, 64, 32, 1, None, None, 1, None) == \
+        B.LA_ERR_INVALID_ARG
+    assert f(P, P, P, P, P, P, 1, 1, 64, 64, 4, None, None, 1, None) == \
+        B.LA_ERR_INVALID_ARG
+    assert f(P, P, P, P, P, P, 1, 1, 48, 48, 1, None, None, 1, None) == \
+        B.LA_ERR_UNSUPPORTED
+    assert f(P, P, P, P, P, P, 1, 1, 64, 256, 2, None, None, 1, None) == \
+        B.LA_ERR_INVALID_ARG
+    assert f(None, P, P, P, P, P, 1, 1, 64, 64, 1, None, None, 1, None) == \
+        B.LA_ERR_INVALID_ARG
+    assert f(None, None, None, None, None, None, 0, 5, 64, 64, 1, None, None,
+             1, None) == B.LA_OK
+
+
+def test_last_error_is_cleared_on_success(lib):
+    assert fwd(lib, B=-1) == B.LA_ERR_INVALID_ARG
+    assert lib.la_last_error().decode() != ""
+    assert fwd(lib, B=0) == B.LA_OK
+    assert lib.la_last_error().decode() == ""
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 16)
+    with pytest.raises(ValueError):
+        K.forward(x, x, x)
