@@ -149,9 +149,8 @@ def main() -> int:
         x = I.make_prefill(cfg, args.seed + i)
         sets.append({k: (None if t is None else t.to(dev)) for k, t in x.items()})
     outs = [torch.empty_like(s["v"]) for s in sets]
-    wsb = K.forward_workspace_bytes(cfg.B, cfg.H, cfg.n, cfg.d, cfg.d_feat,
-                                    mapname, cfg.dtype, cfg.causal)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    ws = K.new_workspace(cfg.B, cfg.H, cfg.n, cfg.d, cfg.d_feat, mapname,
+                         cfg.dtype, cfg.causal, device=dev)
 
     def step(i):
         s = sets[i % nsets]

@@ -7,8 +7,10 @@ The computation runs in hand-written HIP kernels behind the C ABI of
 """
 from ._binding import (LA_BF16, LA_F32, LIB_PATH, MAP_ELU1, MAP_IDENTITY,
                        MAP_PERFORMER, SYMBOLS, LinAttnError, decode_step,
-                       featmap, forward, forward_workspace_bytes, load_library)
+                       featmap, forward, forward_workspace_bytes, load_library,
+                       new_workspace)
 
 __all__ = ["forward", "decode_step", "featmap", "forward_workspace_bytes",
+           "new_workspace",
            "load_library", "LinAttnError", "LIB_PATH", "SYMBOLS", "MAP_IDENTITY",
            "MAP_ELU1", "MAP_PERFORMER", "LA_F32", "LA_BF16"]

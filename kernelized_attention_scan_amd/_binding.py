@@ -31,6 +31,10 @@ SYMBOLS = ("la_featmap", "la_forward_workspace_bytes", "la_forward",
 
 _lock = threading.Lock()
 _lib = None
+# Zero-initialised workspaces, one per (device, stream): the library keeps the
+# barrier words at their start zero between calls, so a workspace is zeroed
+# once when it is allocated and then reused by every call on that stream.
+_workspaces = {}
 
 
 class LinAttnError(RuntimeError):
@@ -120,6 +124,25 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _workspace(need: int, device) -> torch.Tensor:
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(need, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def new_workspace(B: int, H: int, n: int, d: int, d_feat: int,
+                  feature_map="elu1", dtype=torch.bfloat16, causal: bool = True,
+                  device="cuda") -> torch.Tensor:
+    """A zero-initialised workspace for forward() with these sizes (the
+    first 256 bytes must be zero before the first call; calls keep them so)."""
+    need = forward_workspace_bytes(B, H, n, d, d_feat, feature_map, dtype,
+                                   causal)
+    return torch.zeros(max(need, 1), dtype=torch.uint8, device=device)
+
+
 def forward_workspace_bytes(B: int, H: int, n: int, d: int, d_feat: int,
                             feature_map="elu1", dtype=torch.bfloat16,
                             causal: bool = True) -> int:
@@ -155,7 +178,10 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             decay: Optional[torch.Tensor] = None, causal: bool = True,
             out: Optional[torch.Tensor] = None,
             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Kernelized linear attention over q, k [B,H,n,d_qk], v [B,H,n,d]."""
+    """Kernelized linear attention over q, k [B,H,n,d_qk], v [B,H,n,d].
+
+    workspace: optional uint8 device tensor from new_workspace(); by default a
+    cached zero-initialised one per (device, stream) is used."""
     lib = load_library()
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _dev(t, nm)
@@ -178,8 +204,11 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     dt = _dtype_code(v.dtype)
     need = lib.la_forward_workspace_bytes(B, H, n, d, d_feat, mapk, dt,
                                           int(bool(causal)))
-    if need and (workspace is None or workspace.numel() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=v.device)
+    if need and workspace is None:
+        workspace = _workspace(need, v.device)
+    if need and workspace.numel() < need:
+        raise ValueError(f"workspace of {workspace.numel()} bytes is smaller "
+                         f"than the {need} bytes required")
     st = lib.la_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, n, d,
                         d_feat, mapk, _ptr(omega), _ptr(decay),
                         int(bool(causal)), dt,

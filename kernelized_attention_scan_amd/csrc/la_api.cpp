@@ -47,9 +47,15 @@ bool supported_feat(int f) {
 size_t elem_size(int t) { return t == LA_BF16 ? 2 : 4; }
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Sequence split of the chunked forward: about kTargetGroups workgroups in
-// total (two per compute unit of a 256-CU MI355X), segments of whole chunks.
+// Sequence split of the fused forward: about kTargetGroups workgroups in
+// total (two 512-thread workgroups per compute unit of a 256-CU MI355X), at
+// most la::kMaxSegments segments of whole chunks per (batch, head) unit.  The
+// launcher shrinks the split when fewer workgroups fit on the device.
 constexpr int64_t kTargetGroups = 512;
+constexpr int64_t kMaxSegments = la::kMaxSegments;
+// The workspace starts with the grid-barrier words of the multi-segment
+// kernel; they must be zero before first use and every call leaves them zero.
+constexpr size_t kBarrierBytes = 256;
 
 struct FwdPlan {
   const la::FwdOps *ops = nullptr;
@@ -57,13 +63,13 @@ struct FwdPlan {
   int nseg = 0;
   bool need_states = false;
   size_t feat_bytes = 0;    // one of Q', K' (PERFORMER only)
-  size_t state_bytes = 0;
-  size_t total() const { return 2 * feat_bytes + state_bytes; }
+  size_t state_bytes = 0;   // barrier words + segment states
+  size_t total() const { return state_bytes + 2 * feat_bytes; }
 };
 
 // Validates la_forward's sizes and enums (not pointers) and fills the plan.
 la_status plan_forward(int B, int H, int64_t n, int d, int d_feat, int map,
-                       int dtype, int causal, FwdPlan *p) {
+                       int dtype, int causal, bool decay, FwdPlan *p) {
   if (B < 0 || H < 0 || n < 0)
     return fail(LA_ERR_INVALID_ARG, "negative size: B=%d H=%d n=%lld", B, H,
                 static_cast<long long>(n));
@@ -78,9 +84,10 @@ la_status plan_forward(int B, int H, int64_t n, int d, int d_feat, int map,
   if (!supported_d(d) || !supported_feat(d_feat))
     return fail(LA_ERR_UNSUPPORTED, "unsupported d=%d d_feat=%d", d, d_feat);
   p->ops = dtype == LA_BF16 ? la::fwd_ops_bf16(d, d_feat) : la::fwd_ops_f32(d, d_feat);
-  if (!p->ops)
-    return fail(LA_ERR_UNSUPPORTED, "no %s kernel for d=%d d_feat=%d (LDS)",
-                dtype == LA_BF16 ? "bf16" : "fp32", d, d_feat);
+  if (!p->ops || (decay && !p->ops->decay_ok))
+    return fail(LA_ERR_UNSUPPORTED, "no %s%s kernel for d=%d d_feat=%d (LDS)",
+                dtype == LA_BF16 ? "bf16" : "fp32", decay ? " decayed" : "", d,
+                d_feat);
   const int64_t units = static_cast<int64_t>(B) * H;
   if (units == 0 || n == 0) return LA_OK;
   if (units > (int64_t{1} << 30) || n > (int64_t{1} << 40) ||
@@ -89,6 +96,7 @@ la_status plan_forward(int B, int H, int64_t n, int d, int d_feat, int map,
   const int64_t C = p->ops->C;
   const int64_t nchunks = (n + C - 1) / C;
   int64_t per_unit = (kTargetGroups + units - 1) / units;
+  if (per_unit > kMaxSegments) per_unit = kMaxSegments;
   if (per_unit < 1) per_unit = 1;
   if (per_unit > nchunks) per_unit = nchunks;
   const int64_t cps = (nchunks + per_unit - 1) / per_unit;
@@ -96,10 +104,11 @@ la_status plan_forward(int B, int H, int64_t n, int d, int d_feat, int map,
   p->nseg = static_cast<int>((n + p->seg_len - 1) / p->seg_len);
   if (units * p->nseg > (int64_t{1} << 31) - 1)
     return fail(LA_ERR_UNSUPPORTED, "too many workgroups");
-  p->need_states = !causal || p->nseg > 1;
+  p->need_states = p->nseg > 1;
   p->state_bytes = p->need_states
-                       ? align256(static_cast<size_t>(units) * (p->nseg + 1) *
-                                  p->ops->slot_floats * sizeof(float))
+                       ? kBarrierBytes +
+                             align256(static_cast<size_t>(units) * (p->nseg + 1) *
+                                      p->ops->slot_floats * sizeof(float))
                        : 0;
   p->feat_bytes = map == LA_MAP_PERFORMER
                       ? align256(static_cast<size_t>(units * n) * d_feat *
@@ -163,7 +172,9 @@ size_t la_forward_workspace_bytes(int B, int H, int64_t n, int d, int d_feat,
   try {
     const std::string saved = g_last_error;
     FwdPlan p;
-    const la_status st = plan_forward(B, H, n, d, d_feat, map, dtype, causal, &p);
+    // The workspace does not depend on decay; size it for the plain variant.
+    const la_status st =
+        plan_forward(B, H, n, d, d_feat, map, dtype, causal, false, &p);
     g_last_error = saved;
     if (st != LA_OK) return 0;
     return p.total();
@@ -178,7 +189,8 @@ la_status la_forward(const void *q, const void *k, const void *v, void *out,
                      la_dtype dtype, void *workspace, void *stream) {
   try {
     FwdPlan p;
-    const la_status st = plan_forward(B, H, n, d, d_feat, map, dtype, causal, &p);
+    const la_status st = plan_forward(B, H, n, d, d_feat, map, dtype, causal,
+                                      decay != nullptr, &p);
     if (st != LA_OK) return st;
     const int64_t units = static_cast<int64_t>(B) * H;
     if (units == 0 || n == 0) return ok();
@@ -193,14 +205,15 @@ la_status la_forward(const void *q, const void *k, const void *v, void *out,
     const void *qf = q, *kf = k;
     if (map == LA_MAP_PERFORMER) {
       // Q', K' into the workspace, then the identity-map forward over them.
-      hipError_t e = la::launch_featmap_performer(q, ws, omega, units * n, d,
+      unsigned char *fq = ws + p.state_bytes, *fk = fq + p.feat_bytes;
+      hipError_t e = la::launch_featmap_performer(q, fq, omega, units * n, d,
                                                   d_feat, dtype, dtype, s);
       if (e == hipSuccess)
-        e = la::launch_featmap_performer(k, ws + p.feat_bytes, omega,
-                                         units * n, d, d_feat, dtype, dtype, s);
+        e = la::launch_featmap_performer(k, fk, omega, units * n, d, d_feat,
+                                         dtype, dtype, s);
       if (e != hipSuccess) return hip_fail(e, "la_forward feature map");
-      qf = ws;
-      kf = ws + p.feat_bytes;
+      qf = fq;
+      kf = fk;
     }
     la::FwdArgs a;
     a.q = qf;
@@ -208,9 +221,9 @@ la_status la_forward(const void *q, const void *k, const void *v, void *out,
     a.v = v;
     a.out = out;
     a.decay = decay;
-    a.states = p.need_states
-                   ? reinterpret_cast<float *>(ws + 2 * p.feat_bytes)
-                   : nullptr;
+    a.barrier = p.need_states ? reinterpret_cast<unsigned *>(ws) : nullptr;
+    a.states = p.need_states ? reinterpret_cast<float *>(ws + kBarrierBytes)
+                             : nullptr;
     a.H = H;
     a.n = n;
     a.seg_len = p.seg_len;

@@ -47,14 +47,18 @@ template <typename T> __device__ __forceinline__ float round_to(float x) {
 // ---------------------------------------------------------------------------
 // 16-byte vectors: 8 bf16 or 4 fp32 elements.
 // ---------------------------------------------------------------------------
+// Native 16-byte vector (kept in registers; HIP's uint4 struct can end up in
+// scratch memory when copied as a whole).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 template <typename T> struct Vec16;
 template <> struct Vec16<bf16> {
   static constexpr int N = 8;
-  union { uint4 raw; bf16 e[8]; };
+  union { u32x4 raw; bf16 e[8]; };
 };
 template <> struct Vec16<float> {
   static constexpr int N = 4;
-  union { uint4 raw; float e[4]; };
+  union { u32x4 raw; float e[4]; };
 };
 
 // ---------------------------------------------------------------------------
@@ -104,6 +108,56 @@ __device__ __forceinline__ void load_frag44(Frag<float> &f, const float *p0,
   f.v[4] = b[0]; f.v[5] = b[1]; f.v[6] = b[2]; f.v[7] = b[3];
 }
 
+// ---------------------------------------------------------------------------
+// Fragments of a row-major [k][n] tile in LDS whose contraction index k runs
+// along rows: lane (g = l / 16, i = l % 16) receives column n0 + i at 8 rows.
+//   contiguous assignment: rows k0 + 8g + e, e = 0..7
+//   split assignment     : rows k0 + 4g + e and k0 + 16 + 4g + e, e = 0..3
+// bf16: gfx950's transposing LDS read (ds_read_b64_tr_b16).  Within each
+// 16-lane block, source lane j supplies 4 consecutive 16-bit values and output
+// lane i receives value i % 4 of source lanes i/4 + 4e (e = 0..3).  Pointing
+// source lane j at row r0 + j/4, columns n0 + 4 (j % 4) therefore hands output
+// lane i the 4 values of column n0 + i at rows r0 .. r0 + 3.
+// fp32: one 4-byte read per value (16 lanes read 16 consecutive columns).
+// ---------------------------------------------------------------------------
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ s16x4 ds_read_tr4(const bf16 *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4 *)(const_cast<bf16 *>(p)));
+}
+
+// 4 rows r0..r0+3 of column n0 + i (bf16), as elements e0..e0+3 of f.  The
+// whole 64-bit result is reinterpreted at once (per-element bit casts of the
+// returned vector are not reliable with this compiler).
+__device__ __forceinline__ void tr_rows4(Frag<bf16> &f, int e0, const bf16 *base,
+                                         int ld, int r0, int n0, int i) {
+  const s16x4 v = ds_read_tr4(base + (r0 + i / 4) * ld + n0 + 4 * (i % 4));
+  const bf16x4 b = __builtin_bit_cast(bf16x4, v);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) f.v[e0 + e] = b[e];
+}
+__device__ __forceinline__ void tr_rows4(Frag<float> &f, int e0, const float *base,
+                                         int ld, int r0, int n0, int i) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) f.v[e0 + e] = base[(r0 + e) * ld + n0 + i];
+}
+
+template <typename T>
+__device__ __forceinline__ void load_frag_tr8(Frag<T> &f, const T *base, int ld,
+                                              int k0, int n0, int g, int i) {
+  tr_rows4(f, 0, base, ld, k0 + 8 * g, n0, i);
+  tr_rows4(f, 4, base, ld, k0 + 8 * g + 4, n0, i);
+}
+
+template <typename T>
+__device__ __forceinline__ void load_frag_tr44(Frag<T> &f, const T *base, int ld,
+                                               int k0, int n0, int g, int i) {
+  tr_rows4(f, 0, base, ld, k0 + 4 * g, n0, i);
+  tr_rows4(f, 4, base, ld, k0 + 16 + 4 * g, n0, i);
+}
+
 // Split-assignment fragment from two stacked accumulator tiles (top: k = 0..15
 // of the block, bottom: k = 16..31), rounded to the operand type.
 template <typename T>
@@ -137,6 +191,14 @@ __device__ __forceinline__ void store4(float *p, float a, float b, float c,
 // elu(x) + 1 with alpha = 1: x + 1 for x > 0, exp(x) otherwise.
 __device__ __forceinline__ float elu_plus_one(float x) {
   return x > 0.f ? x + 1.f : expf(x);
+}
+
+// The same map with exp(x) as the hardware 2^(x log2 e): relative error a few
+// 1e-7 for the x <= 0 branch, far below the bf16 rounding that follows, and
+// computed with no branch (both sides evaluated, then selected).
+__device__ __forceinline__ float elu_plus_one_fast(float x) {
+  const float e = __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+  return x > 0.f ? x + 1.f : e;
 }
 
 // g^k for an integer k >= 0, with g^0 = 1 exactly (also for g = 0).

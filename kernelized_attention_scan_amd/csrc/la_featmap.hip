@@ -40,14 +40,14 @@ __global__ __launch_bounds__(kFmThreads) void la_featmap_elem_kernel(
 // 8 consecutive stored elements as fp32 (zeros when !ok).
 __device__ __forceinline__ void load8(float *f, const bf16 *p, bool ok) {
   Vec16<bf16> v;
-  v.raw = ok ? *reinterpret_cast<const uint4 *>(p) : make_uint4(0, 0, 0, 0);
+  v.raw = ok ? *reinterpret_cast<const u32x4 *>(p) : u32x4{0, 0, 0, 0};
 #pragma unroll
   for (int e = 0; e < 8; ++e) f[e] = to_f32(v.e[e]);
 }
 __device__ __forceinline__ void load8(float *f, const float *p, bool ok) {
   Vec16<float> a, b;
-  a.raw = ok ? *reinterpret_cast<const uint4 *>(p) : make_uint4(0, 0, 0, 0);
-  b.raw = ok ? *reinterpret_cast<const uint4 *>(p + 4) : make_uint4(0, 0, 0, 0);
+  a.raw = ok ? *reinterpret_cast<const u32x4 *>(p) : u32x4{0, 0, 0, 0};
+  b.raw = ok ? *reinterpret_cast<const u32x4 *>(p + 4) : u32x4{0, 0, 0, 0};
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     f[e] = a.e[e];

@@ -14,30 +14,45 @@
 //   S       <- g^r S + sum_{s<r} b g^(r-1-s) k'_s^T v_s   (r valid rows)
 //   z       <- g^r z + sum_{s<r} b g^(r-1-s) k'_s
 //
-// Unrolling eqs 10-11 from a state S gives mu_{t} = g^(t+1) S + sum_{s<=t}
-// b g^(t-s) k'_s^T v_s, which is what the first three lines read out, and the
-// state after the chunk, which is the last two.  With no decay every weight
-// is 1 (eqs 7-8).
+// Unrolling eqs 10-11 from a state S gives mu_t = g^(t+1) S + sum_{s<=t}
+// b g^(t-s) k'_s^T v_s, which the first three lines read out, and the state
+// after the chunk, the last two.  Without decay every weight is 1 (eqs 7-8).
+// The normaliser z is eq 8 = eq 7 with v = 1: V is extended by a block of 16
+// columns holding (1, 0, ..., 0), so the state tiles of that block carry z in
+// their first column and the matrix cores update and read it with S.
 //
-// Sequence parallelism: each (batch, head) unit's sequence is cut into
-// segments of whole chunks.  Kernel `agg` computes every segment's aggregate
-// (its end state starting from zero); kernel `scan` turns the aggregates into
-// exclusive prefixes in place (state entering segment s = g^len * previous +
-// aggregate) and appends the total; kernel `fwd` then runs the chunk loop of
-// every segment from its prefix.  Non-causal attention (eq 9 with mu_n, nu_n)
-// reads the total in every segment.
+// One fused kernel, one 512-thread workgroup (8 waves) per sequence segment:
+//   phase 1 (several segments per (batch, head) unit only): the segment's
+//     aggregate, i.e. its end state from a zero state, from K and V alone,
+//     written to the workspace;
+//   exchange: grid barrier; each workgroup turns a slice of its unit's
+//     aggregates into exclusive prefixes (state entering segment s+1 = g^len
+//     times the state entering s plus A_s) and the total; grid barrier; each
+//     workgroup reads the state entering its segment (non-causal: the
+//     total).  The launch is cooperative, so every workgroup is resident and
+//     the barriers (a counter in the workspace, bounded wait) cannot deadlock;
+//   phase 2: the chunk loop from that state.
+// Both loops keep several chunks of loads in flight in a register ring.  All
+// global loads are unconditional (tail rows clamp to a valid row; the loop
+// runs whole ring revolutions, padding with empty chunks) so the compiler's
+// wait before each chunk only covers that chunk's loads.
 //
-// Work split inside a 256-thread workgroup (4 waves):
-//   - staging: all threads load the chunk's Q, K, V with 16-byte coalesced
-//     loads (prefetched one chunk ahead in registers), apply phi in fp32 and
-//     write the operand tiles to LDS: Q' and K' row-major, (w . K')^T and V^T
-//     transposed (w_s = b g^(r-1-s), the state-update weights);
-//   - readout: wave w owns 16-row output strips; it forms its strip of P^T on
-//     the matrix cores, feeds the accumulator straight back as the B operand
-//     of V^T P^T ("split" k-assignment), and adds S^T Q'^T from a bf16 copy of
-//     S^T kept in LDS;
-//   - state: the fp32 state S lives in registers as 16x16 accumulator tiles
-//     spread over the waves; each chunk adds (w.K')^T V on the matrix cores.
+// LDS tiles are all row-major ([position][feature]), written with 16-byte
+// stores; operands whose contraction index runs along rows are read with the
+// transposing LDS read (see la_device.h).  Row strides are 16 mod 32 bf16
+// elements, which makes those reads bank-conflict free.
+//
+// Work split per chunk (phase 2):
+//   - staging: every thread takes 16-byte pieces of Q, K, V; phi in fp32 for
+//     Q and K; K' rows past the end are zeroed (they feed the state; Q and V
+//     tails only reach outputs that are never stored);
+//   - readout: output strip tb (16 rows) belongs to waves tb and tb + STRIPS,
+//     which split its 16-column blocks; each forms the strip's P^T on the
+//     matrix cores and feeds the accumulator straight back as the B operand
+//     of V^T P^T ("split" k-assignment); S^T Q'^T comes from a T copy of S^T
+//     in LDS, and its extra block gives q'_t . z;
+//   - state: fp32 16x16 accumulator tiles spread over the waves, each chunk
+//     adding (w.K')^T [V | 1] on the matrix cores.
 #pragma once
 
 #include "la_device.h"
@@ -45,35 +60,89 @@
 
 namespace la {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;
 constexpr size_t kMaxLds = 160 * 1024;
 
-template <typename T, int D, int DF>
+// Registers holding one [C][W] slab of a [n][W] row-major matrix as 16-byte
+// pieces; consecutive threads take consecutive pieces (coalesced).
+template <typename T, int W, int C>
+struct Slab {
+  static constexpr int VEC = 16 / sizeof(T);
+  static constexpr int PPR = W / VEC;                 // pieces per row
+  static constexpr int PIECES = C * PPR;
+  static constexpr int PER = (PIECES + kThreads - 1) / kThreads;
+  static constexpr bool EXACT = PIECES % kThreads == 0;
+  u32x4 v[PER];
+
+  // Rows >= rows re-read row rows-1 (always valid).
+  __device__ __forceinline__ void load(const T *base, int64_t row0, int rows,
+                                       int tid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int p = tid + kThreads * i;
+      const int row = p / PPR, col = (p % PPR) * VEC;
+      const int rr = row < rows ? row : rows - 1;
+      if (EXACT || p < PIECES)
+        v[i] = *reinterpret_cast<const u32x4 *>(base + (row0 + rr) * W + col);
+    }
+  }
+};
+
+// Row stride (elements) for a row of w elements: 16 mod 32 for bf16 (the
+// transposing reads of 8 rows then hit disjoint banks), +4 for fp32.
+template <typename T>
+constexpr int lds_stride(int w) {
+  return sizeof(T) == 2 ? (w % 32 == 16 ? w : w + 16) : w + 4;
+}
+
+template <typename T, int D, int DF, bool DECAY>
 struct FwdShape {
   // Chunk rows: 64 for bf16 operands; 32 where LDS would not hold 64.
   static constexpr int C =
       (sizeof(T) == 2 && !(DF == 256 && D == 128)) ? 64 : 32;
   static constexpr int DFP = DF < 32 ? 32 : DF;      // padded k-width of q', k'
-  static constexpr int PADE = 16 / sizeof(T);        // 16-byte row padding
-  static constexpr int LQ = DFP + PADE;              // sQ, sK row stride
-  static constexpr int LT = C + PADE;                // sKT, sVT row stride
-  static constexpr int LS = DFP + PADE;              // sST row stride
+  static constexpr int LQ = lds_stride<T>(DFP);      // sQ, sK, sKw, sST
+  static constexpr int LV = lds_stride<T>(D + 16);   // sV: V | ones block
   static constexpr int STRIPS = C / 16;
+  static constexpr int WPS = kWaves / STRIPS;        // waves per output strip
   static constexpr int NJ = D / 16, NF = DF / 16;
-  static constexpr int NTILE = NF * NJ;              // 16x16 state tiles
-  static constexpr int TPW = (NTILE + kWaves - 1) / kWaves;
-  static constexpr int SQ = C * LQ, SK = C * LQ, SKT = DF * LT, SVT = D * LT,
-                       SST = D * LS;
-  static constexpr size_t lds_fwd =
-      sizeof(T) * (SQ + SK + SKT + SVT + SST) + sizeof(float) * (DF + C + 1);
-  static constexpr size_t lds_agg =
-      sizeof(T) * (SKT + SVT) + sizeof(float) * (C + 1);
-  // fp32 state slot: NTILE tiles x 64 lanes x 4 (accumulator order), then z.
-  static constexpr int SLOT_USED = NTILE * 256 + DF;
-  static constexpr int SLOT = (SLOT_USED + 63) / 64 * 64;
-  static constexpr bool fits = lds_fwd <= kMaxLds;
+  static constexpr int NJA = NJ + 1;                 // with the ones block
+  static constexpr int NTILE = NF * NJA;             // 16x16 state tiles
+  // state tiles of a wave: see tile_fb / tile_jb
+  static constexpr int FPW = NF >= kWaves ? NF / kWaves : 1;
+  static constexpr int WPF = NF >= kWaves ? 1 : kWaves / NF;
+  static constexpr int JPW = (NJA + WPF - 1) / WPF;
+  static constexpr int SQ = C * LQ, SKW = DECAY ? C * LQ : 0, SV = C * LV,
+                       SST = (D + 16) * LQ;
+  static constexpr size_t lds_bytes =
+      sizeof(T) * (2 * SQ + SKW + SV + SST) + sizeof(float) * (C + 1);
+  // fp32 state slot: NTILE tiles x 64 lanes x 4 (accumulator order).
+  static constexpr int SLOT = NTILE * 256;
+  // Workgroups per compute unit the instance is built for: two for the small
+  // shapes (<= 128 VGPRs, 4 waves per SIMD), else one.
+  static constexpr int OCC = (D <= 64 && DF <= 64) ? 2 : 1;
+  static constexpr int WAVES_PER_SIMD = OCC * kWaves / 4;
+  // register-ring depths (chunks of loads in flight per workgroup)
+  static constexpr int RING = OCC == 2 ? 24 : 64;   // VGPRs for the ring
+  static constexpr int REG2 = 4 * (Slab<T, DF, C>::PER * 2 + Slab<T, D, C>::PER);
+  static constexpr int REG1 = 4 * (Slab<T, DF, C>::PER + Slab<T, D, C>::PER);
+  static constexpr int NB2 = REG2 >= RING ? 1 : (RING / REG2 > 4 ? 4 : RING / REG2);
+  static constexpr int NB1 = REG1 >= RING ? 1 : (RING / REG1 > 6 ? 6 : RING / REG1);
+  static constexpr bool fits = lds_bytes <= kMaxLds;
 };
+
+// State tile ownership: wave w holds tiles (fb, jb) with
+//   fb = w % NF (NF < 8) or w + 8 m (NF >= 8),
+//   jb = w / NF + WPF m' (NF < 8) or every jb (NF >= 8).
+template <typename F>
+__device__ __forceinline__ int tile_fb(int w, int m) {
+  return F::NF >= kWaves ? w + kWaves * m : w % F::NF;
+}
+template <typename F>
+__device__ __forceinline__ int tile_jb(int w, int m) {
+  return F::NF >= kWaves ? m : w / F::NF + F::WPF * m;
+}
 
 // Per-head decay: g = a, b = 1 - a (eqs 10-11); g = b = 1 without decay.
 struct Decay {
@@ -85,206 +154,211 @@ struct Decay {
   }
 };
 
-// Registers holding one [C][W] slab of a [n][W] row-major matrix, as 16-byte
-// pieces distributed over the 256 threads (consecutive threads, consecutive
-// pieces: fully coalesced).
-template <typename T, int W, int C>
-struct Slab {
-  static constexpr int VEC = 16 / sizeof(T);
-  static constexpr int PPR = W / VEC;                 // pieces per row
-  static constexpr int PIECES = C * PPR;
-  static constexpr int PER = (PIECES + kThreads - 1) / kThreads;
-  uint4 v[PER];
-
-  __device__ __forceinline__ void load(const T *base, int64_t row0, int rows,
-                                       int tid) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int p = tid + kThreads * i;
-      const int row = p / PPR, col = (p % PPR) * VEC;
-      v[i] = make_uint4(0, 0, 0, 0);
-      if (p < PIECES && row < rows)
-        v[i] = *reinterpret_cast<const uint4 *>(base + (row0 + row) * W + col);
-    }
-  }
-};
-
-// phi(x) on the fp32 value of a stored element.
-__device__ __forceinline__ float feat(float x, int elu1) {
-  return elu1 ? elu_plus_one(x) : x;
-}
-
-// Write phi(Q) rows into sQ (row-major, rows >= r zeroed).
+// phi(Q) rows -> sQ (row-major).  Rows past the end are staged unmasked: they
+// only reach outputs that are never stored.
 template <typename T, int W, int C, int L>
-__device__ __forceinline__ void stage_rowmajor(const Slab<T, W, C> &sl, T *dst,
-                                               int rows, int tid, int elu1) {
+__device__ __forceinline__ void stage_queries(const Slab<T, W, C> &sl, T *dst,
+                                              int tid, int elu1) {
   using S = Slab<T, W, C>;
 #pragma unroll
   for (int i = 0; i < S::PER; ++i) {
     const int p = tid + kThreads * i;
-    if (p < S::PIECES) {
+    if (S::EXACT || p < S::PIECES) {
       const int row = p / S::PPR, col = (p % S::PPR) * S::VEC;
       Vec16<T> x, y;
       x.raw = sl.v[i];
 #pragma unroll
       for (int e = 0; e < S::VEC; ++e) {
-        const float f = row < rows ? feat(to_f32(x.e[e]), elu1) : 0.f;
-        y.e[e] = from_f32<T>(f);
+        const float xv = to_f32(x.e[e]);
+        y.e[e] = from_f32<T>(elu1 ? elu_plus_one_fast(xv) : xv);
       }
-      *reinterpret_cast<uint4 *>(dst + row * L + col) = y.raw;
+      *reinterpret_cast<u32x4 *>(dst + row * L + col) = y.raw;
     }
   }
 }
 
-// Write phi(K) rows into sK (row-major, unweighted) and, weighted by
-// w_s = b g^(r-1-s), transposed into sKT.  Rows >= r are zero in both.
-template <typename T, int W, int C, int LQ, int LT, bool ROWMAJOR>
+// phi(K) rows -> sK (row-major, when PLAIN), zero past the end; the keys the
+// state update uses go to sKw: w_s phi(k_s) with w_s = b g^(rows-1-s) under
+// decay (sKw is then its own tile), else sKw aliases sK.
+template <typename T, int W, int C, int L, bool DECAY, bool PLAIN>
 __device__ __forceinline__ void stage_keys(const Slab<T, W, C> &sl, T *sK,
-                                           T *sKT, const float *gp, float b,
+                                           T *sKw, const float *gp, float b,
                                            int rows, int tid, int elu1) {
   using S = Slab<T, W, C>;
 #pragma unroll
   for (int i = 0; i < S::PER; ++i) {
     const int p = tid + kThreads * i;
-    if (p < S::PIECES) {
+    if (S::EXACT || p < S::PIECES) {
       const int row = p / S::PPR, col = (p % S::PPR) * S::VEC;
-      const float w = row < rows ? b * gp[rows - 1 - row] : 0.f;
-      Vec16<T> x, y;
+      const bool valid = row < rows;
+      const float w = DECAY ? b * gp[valid ? rows - 1 - row : 0] : 1.f;
+      Vec16<T> x, y, yw;
       x.raw = sl.v[i];
 #pragma unroll
       for (int e = 0; e < S::VEC; ++e) {
-        const float f = row < rows ? feat(to_f32(x.e[e]), elu1) : 0.f;
+        const float xv = to_f32(x.e[e]);
+        const float f = valid ? (elu1 ? elu_plus_one_fast(xv) : xv) : 0.f;
         y.e[e] = from_f32<T>(f);
-        sKT[(col + e) * LT + row] = from_f32<T>(f * w);
+        if (DECAY) yw.e[e] = from_f32<T>(f * w);
       }
-      if (ROWMAJOR) *reinterpret_cast<uint4 *>(sK + row * LQ + col) = y.raw;
+      if (DECAY) {
+        if (PLAIN) *reinterpret_cast<u32x4 *>(sK + row * L + col) = y.raw;
+        *reinterpret_cast<u32x4 *>(sKw + row * L + col) = yw.raw;
+      } else {
+        *reinterpret_cast<u32x4 *>(sK + row * L + col) = y.raw;
+      }
     }
   }
 }
 
-// Write V rows transposed into sVT (rows >= r zero).
-template <typename T, int W, int C, int LT>
-__device__ __forceinline__ void stage_values(const Slab<T, W, C> &sl, T *sVT,
-                                             int rows, int tid) {
+// V rows -> sV (row-major, raw copy: tail rows meet zero keys or dropped rows).
+template <typename T, int W, int C, int L>
+__device__ __forceinline__ void stage_values(const Slab<T, W, C> &sl, T *sV,
+                                             int tid) {
   using S = Slab<T, W, C>;
 #pragma unroll
   for (int i = 0; i < S::PER; ++i) {
     const int p = tid + kThreads * i;
-    if (p < S::PIECES) {
+    if (S::EXACT || p < S::PIECES) {
       const int row = p / S::PPR, col = (p % S::PPR) * S::VEC;
-      Vec16<T> x;
-      x.raw = sl.v[i];
-#pragma unroll
-      for (int e = 0; e < S::VEC; ++e)
-        sVT[(col + e) * LT + row] = row < rows ? x.e[e] : from_f32<T>(0.f);
+      *reinterpret_cast<u32x4 *>(sV + row * L + col) = sl.v[i];
     }
   }
 }
 
-// S tile (fb, jb) += (w.K')^T V over the chunk:  A = sKT rows f, B = sVT rows j,
-// contraction over the chunk positions s (contiguous k-assignment).
-template <typename T, int C, int LT>
-__device__ __forceinline__ f32x4 state_tile_update(f32x4 acc, const T *sKT,
-                                                   const T *sVT, int fb, int jb,
-                                                   int li, int g) {
+// S tiles of this wave += (w.K')^T [V | 1] over the chunk: A = rows of sKw
+// read transposed (features along lanes), B = rows of sV read transposed
+// (columns along lanes); contraction over the chunk positions.
+template <typename F, typename T>
+__device__ __forceinline__ void state_update(f32x4 *S, const T *sKw,
+                                             const T *sV, float gr, int w,
+                                             int g, int li) {
+  constexpr int C = F::C;
 #pragma unroll
-  for (int kb = 0; kb < C / 32; ++kb) {
-    Frag<T> a, bb;
-    load_frag8(a, sKT + (16 * fb + li) * LT + 32 * kb + 8 * g);
-    load_frag8(bb, sVT + (16 * jb + li) * LT + 32 * kb + 8 * g);
-    acc = mma(a, bb, acc);
+  for (int m = 0; m < F::FPW; ++m) {
+    const int fb = tile_fb<F>(w, m);
+    Frag<T> af[C / 32];
+#pragma unroll
+    for (int kb = 0; kb < C / 32; ++kb)
+      load_frag_tr8(af[kb], sKw, F::LQ, 32 * kb, 16 * fb, g, li);
+#pragma unroll
+    for (int mj = 0; mj < F::JPW; ++mj) {
+      const int jb = tile_jb<F>(w, mj);
+      if (jb < F::NJA) {
+        f32x4 acc = S[m * F::JPW + mj] * gr;
+#pragma unroll
+        for (int kb = 0; kb < C / 32; ++kb) {
+          Frag<T> bf;
+          load_frag_tr8(bf, sV, F::LV, 32 * kb, 16 * jb, g, li);
+          acc = mma(af[kb], bf, acc);
+        }
+        S[m * F::JPW + mj] = acc;
+      }
+    }
   }
-  return acc;
 }
 
-// ---------------------------------------------------------------------------
-// Kernel 1: segment aggregates (end state of each segment from zero).
-// ---------------------------------------------------------------------------
-template <typename T, int D, int DF>
-__global__ __launch_bounds__(kThreads) void la_agg_kernel(FwdArgs a) {
-  using F = FwdShape<T, D, DF>;
-  constexpr int C = F::C, LT = F::LT;
-  extern __shared__ __align__(16) unsigned char smem[];
-  T *sKT = reinterpret_cast<T *>(smem);
-  T *sVT = sKT + F::SKT;
-  float *gp = reinterpret_cast<float *>(sVT + F::SVT);
-
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int g = lane >> 4, li = lane & 15;
-  const int64_t unit = blockIdx.x / a.nseg;
-  const int seg = blockIdx.x % a.nseg;
-  const Decay dk(a.decay, static_cast<int>(unit % a.H));
-  for (int i = tid; i <= C; i += kThreads) gp[i] = pow_int(dk.g, dk.lg, i);
-
-  const T *kb = static_cast<const T *>(a.k) + unit * a.n * DF;
-  const T *vb = static_cast<const T *>(a.v) + unit * a.n * D;
-  const int64_t start = seg * a.seg_len;
-  const int64_t end = min(a.n, start + a.seg_len);
-
-  f32x4 S[F::TPW];
+// S^T copy for the readout: tile (fb, jb) -> rows 16 jb + li, columns
+// 16 fb + 4 g .. +3 of sST.
+template <typename F, typename T>
+__device__ __forceinline__ void publish_state(const f32x4 *S, T *sST, int w,
+                                              int g, int li) {
 #pragma unroll
-  for (int i = 0; i < F::TPW; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float z = 0.f;
-
-  Slab<T, DF, C> rk;
-  Slab<T, D, C> rv;
-  rk.load(kb, start, static_cast<int>(min<int64_t>(C, end - start)), tid);
-  rv.load(vb, start, static_cast<int>(min<int64_t>(C, end - start)), tid);
-  __syncthreads();  // gp ready
-  for (int64_t row0 = start; row0 < end; row0 += C) {
-    const int rows = static_cast<int>(min<int64_t>(C, end - row0));
-    stage_keys<T, DF, C, F::LQ, LT, false>(rk, nullptr, sKT, gp, dk.b, rows,
-                                           tid, a.elu1);
-    stage_values<T, D, C, LT>(rv, sVT, rows, tid);
-    __syncthreads();
-    if (row0 + C < end) {
-      const int r2 = static_cast<int>(min<int64_t>(C, end - row0 - C));
-      rk.load(kb, row0 + C, r2, tid);
-      rv.load(vb, row0 + C, r2, tid);
-    }
-    const float gr = gp[rows];
+  for (int m = 0; m < F::FPW; ++m) {
 #pragma unroll
-    for (int i = 0; i < F::TPW; ++i) {
-      const int idx = w + kWaves * i;
-      if (idx < F::NTILE)
-        S[i] = state_tile_update<T, C, LT>(S[i] * gr, sKT, sVT, idx / F::NJ,
-                                           idx % F::NJ, li, g);
+    for (int mj = 0; mj < F::JPW; ++mj) {
+      const int fb = tile_fb<F>(w, m), jb = tile_jb<F>(w, mj);
+      const f32x4 s = S[m * F::JPW + mj];
+      if (jb < F::NJA)
+        store4(sST + (16 * jb + li) * F::LQ + 16 * fb + 4 * g, s[0], s[1],
+               s[2], s[3]);
     }
-    if (tid < DF) {
-      float zs = 0.f;
-      for (int s = 0; s < C; ++s) zs += to_f32(sKT[tid * LT + s]);
-      z = gr * z + zs;
-    }
-    __syncthreads();
   }
-  float *slot = a.states + (unit * (a.nseg + 1) + seg) * F::SLOT;
-#pragma unroll
-  for (int i = 0; i < F::TPW; ++i) {
-    const int idx = w + kWaves * i;
-    if (idx < F::NTILE)
-      *reinterpret_cast<f32x4 *>(slot + (idx * 64 + lane) * 4) = S[i];
-  }
-  if (tid < DF) slot[F::NTILE * 256 + tid] = z;
 }
 
-// ---------------------------------------------------------------------------
-// Kernel 3: chunked forward of one segment from its entering state.
-// ---------------------------------------------------------------------------
-template <typename T, int D, int DF, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void la_fwd_kernel(FwdArgs a) {
-  using F = FwdShape<T, D, DF>;
-  constexpr int C = F::C, LQ = F::LQ, LT = F::LT, LS = F::LS, DFP = F::DFP;
-  constexpr int STRIPS = F::STRIPS, NJ = F::NJ;
+// Grid-wide barrier of a cooperative launch (every workgroup is resident).
+// Each barrier instance k of the kernel owns two words of the workspace:
+// bar[2k] counts arrivals and bar[2k+1] departures.  Both are zero between
+// launches because the last workgroup to depart resets them (every workgroup
+// has passed the wait by then, and the next use of the words is the next
+// launch).  One thread per workgroup releases the workgroup's writes, spins
+// with relaxed loads (no cache maintenance per probe), then acquires.  The
+// wait is bounded (about a second): should the words ever be corrupt the
+// barrier sets the flag word bar[kBarrierFlag] and lets the kernel finish
+// rather than hang.
+constexpr int kBarrierFlag = 8;
+
+__device__ __forceinline__ void grid_barrier(unsigned *bar, int k,
+                                             unsigned nblocks) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned *arrive = bar + 2 * k, *depart = bar + 2 * k + 1;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned spins = 0;
+    while (__hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+           nblocks) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins > (1u << 22)) {
+        __hip_atomic_fetch_or(bar + kBarrierFlag, 1u, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (__hip_atomic_fetch_add(depart, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT) == nblocks - 1) {
+      __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(depart, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+}
+
+// Exclusive prefix over the segments of one unit, in place, for the slice
+// [e0, e1) of the state elements; slot nseg receives the total.  The state
+// entering segment s+1 is g^len_s times the state entering s plus A_s (eqs
+// 7-8 / 10-11 applied segment by segment).
+template <bool DECAY>
+__device__ __forceinline__ void scan_slice(float *ub, int slot, int nseg,
+                                           int64_t n, int64_t seg_len, float g,
+                                           float lg, int e0, int e1) {
+  for (int e = e0 + static_cast<int>(threadIdx.x); e < e1; e += kThreads) {
+    float x[kMaxSegments];
+#pragma unroll
+    for (int sp = 0; sp < kMaxSegments; ++sp)
+      x[sp] = ub[static_cast<int64_t>(sp < nseg ? sp : 0) * slot + e];
+    float run = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < kMaxSegments; ++sp) {
+      if (sp < nseg) {
+        ub[static_cast<int64_t>(sp) * slot + e] = run;
+        const int64_t len = min(seg_len, n - sp * seg_len);
+        run = (DECAY ? pow_int(g, lg, len) : 1.f) * run + x[sp];
+      }
+    }
+    ub[static_cast<int64_t>(nseg) * slot + e] = run;
+  }
+}
+
+template <typename T, int D, int DF, bool CAUSAL, bool MULTI, bool DECAY>
+__global__ __launch_bounds__(kThreads,
+                             (FwdShape<T, D, DF, DECAY>::WAVES_PER_SIMD))
+void la_fwd_kernel(FwdArgs a) {
+  using F = FwdShape<T, D, DF, DECAY>;
+  constexpr int C = F::C, LQ = F::LQ, LV = F::LV, DFP = F::DFP;
+  constexpr int STRIPS = F::STRIPS, NJ = F::NJ, WPS = F::WPS;
+  constexpr int NB1 = F::NB1, NB2 = F::NB2, TW = F::FPW * F::JPW;
   extern __shared__ __align__(16) unsigned char smem[];
   T *sQ = reinterpret_cast<T *>(smem);
   T *sK = sQ + F::SQ;
-  T *sKT = sK + F::SK;
-  T *sVT = sKT + F::SKT;
-  T *sST = sVT + F::SVT;
-  float *sz = reinterpret_cast<float *>(sST + F::SST);
-  float *gp = sz + DF;
+  T *sKw = DECAY ? sK + F::SQ : sK;
+  T *sV = sK + F::SQ + F::SKW;
+  T *sST = sV + F::SV;
+  float *gp = reinterpret_cast<float *>(sST + F::SST);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int g = lane >> 4, li = lane & 15;
   const int64_t unit = blockIdx.x / a.nseg;
   const int seg = blockIdx.x % a.nseg;
@@ -297,72 +371,157 @@ __global__ __launch_bounds__(kThreads) void la_fwd_kernel(FwdArgs a) {
   T *ob = static_cast<T *>(a.out) + unit * a.n * D;
   const int64_t start = seg * a.seg_len;
   const int64_t end = min(a.n, start + a.seg_len);
+  const int nch = static_cast<int>((end - start + C - 1) / C);
 
-  // Zero the k-padding columns of q', k' and S^T once (DF < 32 only).
+  // Constant parts of the tiles: the ones block of sV (column D = 1, the
+  // other 15 columns 0, every row) and, for DF < 32, the zero k-padding
+  // columns of q', k' and S^T.
+  for (int i = tid; i < C * 16; i += kThreads)
+    sV[(i / 16) * LV + D + i % 16] = from_f32<T>(i % 16 == 0 ? 1.f : 0.f);
   if (DFP != DF) {
     for (int i = tid; i < C * (DFP - DF); i += kThreads) {
       const int row = i / (DFP - DF), col = DF + i % (DFP - DF);
       sQ[row * LQ + col] = from_f32<T>(0.f);
       sK[row * LQ + col] = from_f32<T>(0.f);
     }
-    for (int i = tid; i < D * (DFP - DF); i += kThreads)
-      sST[(i / (DFP - DF)) * LS + DF + i % (DFP - DF)] = from_f32<T>(0.f);
+    for (int i = tid; i < (D + 16) * (DFP - DF); i += kThreads)
+      sST[(i / (DFP - DF)) * LQ + DF + i % (DFP - DF)] = from_f32<T>(0.f);
   }
 
-  // Entering state: exclusive prefix (causal) or total (non-causal).
-  const float *st = nullptr;
-  if (a.states)
-    st = a.states + (unit * (a.nseg + 1) + (CAUSAL ? seg : a.nseg)) * F::SLOT;
-  f32x4 S[F::TPW];
+  f32x4 S[TW];
 #pragma unroll
-  for (int i = 0; i < F::TPW; ++i) {
-    const int idx = w + kWaves * i;
-    S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (idx < F::NTILE) {
-      if (st) S[i] = *reinterpret_cast<const f32x4 *>(st + (idx * 64 + lane) * 4);
-      const int fb = idx / NJ, jb = idx % NJ;
-      store4(sST + (16 * jb + li) * LS + 16 * fb + 4 * g, S[i][0], S[i][1],
-             S[i][2], S[i][3]);
-    }
-  }
-  for (int f = tid; f < DF; f += kThreads) sz[f] = st ? st[F::NTILE * 256 + f] : 0.f;
+  for (int i = 0; i < TW; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  Slab<T, DF, C> rq, rk;
-  Slab<T, D, C> rv;
-  {
-    const int r0 = static_cast<int>(min<int64_t>(C, end - start));
-    rq.load(qb, start, r0, tid);
-    if (CAUSAL) {
-      rk.load(kb, start, r0, tid);
-      rv.load(vb, start, r0, tid);
+  if constexpr (MULTI) {
+    // ---------------- phase 1: segment aggregate from K, V ----------------
+    Slab<T, DF, C> rk[NB1];
+    Slab<T, D, C> rv[NB1];
+#pragma unroll
+    for (int b = 0; b < NB1; ++b) {
+      const int cl = b < nch ? b : nch - 1;
+      const int64_t r0 = start + cl * C;
+      const int rows = static_cast<int>(min<int64_t>(C, end - r0));
+      rk[b].load(kb, r0, rows, tid);
+      rv[b].load(vb, r0, rows, tid);
     }
-  }
-  __syncthreads();  // gp, sST, sz ready
-
-  for (int64_t row0 = start; row0 < end; row0 += C) {
-    const int rows = static_cast<int>(min<int64_t>(C, end - row0));
-    const bool last = row0 + C >= end;
-    stage_rowmajor<T, DF, C, LQ>(rq, sQ, rows, tid, a.elu1);
-    if (CAUSAL) {
-      stage_keys<T, DF, C, LQ, LT, true>(rk, sK, sKT, gp, dk.b, rows, tid,
-                                         a.elu1);
-      stage_values<T, D, C, LT>(rv, sVT, rows, tid);
-    }
-    __syncthreads();  // operand tiles ready
-    if (!last) {
-      const int r2 = static_cast<int>(min<int64_t>(C, end - row0 - C));
-      rq.load(qb, row0 + C, r2, tid);
-      if (CAUSAL) {
-        rk.load(kb, row0 + C, r2, tid);
-        rv.load(vb, row0 + C, r2, tid);
+    __syncthreads();  // gp and the constant tile parts ready
+    const int nch1 = (nch + NB1 - 1) / NB1 * NB1;
+    for (int c0 = 0; c0 < nch1; c0 += NB1) {
+#pragma unroll
+      for (int b = 0; b < NB1; ++b) {
+        const int c = c0 + b;
+        const int64_t r0 = start + c * C;
+        const int rows =
+            c < nch ? static_cast<int>(min<int64_t>(C, end - r0)) : 0;
+        stage_keys<T, DF, C, LQ, DECAY, false>(rk[b], sK, sKw, gp, dk.b, rows,
+                                               tid, a.elu1);
+        stage_values<T, D, C, LV>(rv[b], sV, tid);
+        __syncthreads();
+        {
+          const int cn = c + NB1 < nch ? c + NB1 : nch - 1;
+          const int64_t r2 = start + cn * C;
+          const int rows2 = static_cast<int>(min<int64_t>(C, end - r2));
+          rk[b].load(kb, r2, rows2, tid);
+          rv[b].load(vb, r2, rows2, tid);
+        }
+        state_update<F>(S, sKw, sV, DECAY ? gp[rows] : 1.f, w, g, li);
+        __syncthreads();
       }
     }
+    // With one segment the aggregate is already the state every row needs
+    // (non-causal total); several segments exchange through the workspace:
+    // write the aggregate, barrier, scan a slice of every unit's slots,
+    // barrier, read the state entering this segment (or the total).
+    if (a.nseg > 1) {
+      float *ub = a.states + unit * (a.nseg + 1) * static_cast<int64_t>(F::SLOT);
+      float *mine = ub + static_cast<int64_t>(seg) * F::SLOT;
+#pragma unroll
+      for (int m = 0; m < F::FPW; ++m)
+#pragma unroll
+        for (int mj = 0; mj < F::JPW; ++mj) {
+          const int jb = tile_jb<F>(w, mj);
+          const int idx = tile_fb<F>(w, m) * F::NJA + jb;
+          if (jb < F::NJA)
+            *reinterpret_cast<f32x4 *>(mine + (idx * 64 + lane) * 4) =
+                S[m * F::JPW + mj];
+        }
+      // Every workgroup reaches both barriers exactly once; they run only
+      // under a cooperative launch (the launcher uses one whenever nseg > 1).
+      grid_barrier(a.barrier, 0, gridDim.x);
+      const int per = (F::SLOT + a.nseg - 1) / a.nseg;
+      scan_slice<DECAY>(ub, F::SLOT, a.nseg, a.n, a.seg_len, dk.g, dk.lg,
+                        seg * per, min(F::SLOT, (seg + 1) * per));
+      grid_barrier(a.barrier, 1, gridDim.x);
+      const float *in = ub + static_cast<int64_t>(CAUSAL ? seg : a.nseg) * F::SLOT;
+#pragma unroll
+      for (int m = 0; m < F::FPW; ++m)
+#pragma unroll
+        for (int mj = 0; mj < F::JPW; ++mj) {
+          const int jb = tile_jb<F>(w, mj);
+          const int idx = tile_fb<F>(w, m) * F::NJA + jb;
+          if (jb < F::NJA)
+            S[m * F::JPW + mj] =
+                *reinterpret_cast<const f32x4 *>(in + (idx * 64 + lane) * 4);
+        }
+    }
+  }
 
-    // ---- readout of this wave's strips ----
-    for (int tb = w; tb < STRIPS; tb += kWaves) {
-      const int t = 16 * tb + li;
+  // the entering state as a T copy of S^T for the readout
+  publish_state<F>(S, sST, w, g, li);
+
+  // ---------------- phase 2: chunk loop ----------------
+  Slab<T, DF, C> rq[NB2], rk2[NB2];
+  Slab<T, D, C> rv2[NB2];
+#pragma unroll
+  for (int b = 0; b < NB2; ++b) {
+    const int cl = b < nch ? b : nch - 1;
+    const int64_t r0 = start + cl * C;
+    const int rows = static_cast<int>(min<int64_t>(C, end - r0));
+    rq[b].load(qb, r0, rows, tid);
+    if (CAUSAL) {
+      rk2[b].load(kb, r0, rows, tid);
+      rv2[b].load(vb, r0, rows, tid);
+    }
+  }
+  __syncthreads();  // gp, sST and the constant tile parts ready
+
+  const int tb = w % STRIPS;    // this wave's output strip
+  const int jh = w / STRIPS;    // and its share of the column blocks
+  const int t = 16 * tb + li;   // the output row this lane normalises
+  const float gt = CAUSAL ? gp[t + 1] : 1.f;
+  const int nch2 = (nch + NB2 - 1) / NB2 * NB2;
+  for (int c0 = 0; c0 < nch2; c0 += NB2) {
+#pragma unroll
+    for (int b = 0; b < NB2; ++b) {
+      const int c = c0 + b;
+      const int64_t row0 = start + c * C;
+      const int rows =
+          c < nch ? static_cast<int>(min<int64_t>(C, end - row0)) : 0;
+      const bool last = c + 1 >= nch;
+      stage_queries<T, DF, C, LQ>(rq[b], sQ, tid, a.elu1);
+      if (CAUSAL) {
+        stage_keys<T, DF, C, LQ, DECAY, true>(rk2[b], sK, sKw, gp, dk.b, rows,
+                                              tid, a.elu1);
+        stage_values<T, D, C, LV>(rv2[b], sV, tid);
+      }
+      __syncthreads();  // operand tiles ready
+      {
+        const int cn = c + NB2 < nch ? c + NB2 : nch - 1;
+        const int64_t r2 = start + cn * C;
+        const int rows2 = static_cast<int>(min<int64_t>(C, end - r2));
+        rq[b].load(qb, r2, rows2, tid);
+        if (CAUSAL) {
+          rk2[b].load(kb, r2, rows2, tid);
+          rv2[b].load(vb, r2, rows2, tid);
+        }
+      }
+
+      // ---- readout of strip tb: q' fragments, reused by every product ----
+      Frag<T> qf[DFP / 32];
+#pragma unroll
+      for (int kq = 0; kq < DFP / 32; ++kq)
+        load_frag8(qf[kq], sQ + t * LQ + 32 * kq + 8 * g);
       f32x4 pt[STRIPS];
-      float den_i = 0.f;
 #pragma unroll
       for (int sb = 0; sb < STRIPS; ++sb) {
         pt[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -370,18 +529,16 @@ __global__ __launch_bounds__(kThreads) void la_fwd_kernel(FwdArgs a) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kq = 0; kq < DFP / 32; ++kq) {
-            Frag<T> fa, fb;
+            Frag<T> fa;
             load_frag8(fa, sK + (16 * sb + li) * LQ + 32 * kq + 8 * g);
-            load_frag8(fb, sQ + (16 * tb + li) * LQ + 32 * kq + 8 * g);
-            acc = mma(fa, fb, acc);
+            acc = mma(fa, qf[kq], acc);
           }
           // acc[rr] = q'_t . k'_s with s = 16 sb + 4 g + rr
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             const int s = 16 * sb + 4 * g + rr;
-            const float wgt = s <= t ? dk.b * gp[t - s] : 0.f;
-            acc[rr] = round_to<T>(acc[rr] * wgt);
-            den_i += acc[rr];
+            if (DECAY) acc[rr] = s <= t ? acc[rr] * (dk.b * gp[t - s]) : 0.f;
+            else if (sb == tb) acc[rr] = s <= t ? acc[rr] : 0.f;
           }
           pt[sb] = acc;
         }
@@ -393,74 +550,53 @@ __global__ __launch_bounds__(kThreads) void la_fwd_kernel(FwdArgs a) {
         frag_from_acc(pf[kp], pt[2 * kp],
                       2 * kp + 1 < STRIPS ? pt[2 * kp + 1]
                                           : f32x4{0.f, 0.f, 0.f, 0.f});
-      den_i = wave_sum_groups(den_i);
-      float dx = 0.f;
-#pragma unroll
-      for (int ff = 0; ff < DF / 4; ++ff) {
-        const int f = g * (DF / 4) + ff;
-        dx += to_f32(sQ[t * LQ + f]) * sz[f];
-      }
-      dx = wave_sum_groups(dx);
-      const float gt = CAUSAL ? gp[t + 1] : 1.f;
-      const float den = den_i + gt * dx;
-#pragma unroll
-      for (int jb = 0; jb < NJ; ++jb) {
+      // Column block jb of num^T = V^T P^T + g^(t+1) S^T Q'^T.  Block NJ is
+      // the ones block: its first row is the denominator, sum_s P[t][s] +
+      // g^(t+1) q'_t . z, from the same rounded P and the same S copy as the
+      // numerators.
+      auto block = [&](int jb) {
         f32x4 an = {0.f, 0.f, 0.f, 0.f}, ai = {0.f, 0.f, 0.f, 0.f};
         if (CAUSAL) {
 #pragma unroll
           for (int kp = 0; kp < NPK; ++kp) {
             if (2 * kp <= tb) {
               Frag<T> fa;
-              const T *row = sVT + (16 * jb + li) * LT + 32 * kp;
-              load_frag44(fa, row + 4 * g, row + 16 + 4 * g);
+              load_frag_tr44(fa, sV, LV, 32 * kp, 16 * jb, g, li);
               an = mma(fa, pf[kp], an);
             }
           }
         }
 #pragma unroll
         for (int kq = 0; kq < DFP / 32; ++kq) {
-          Frag<T> fa, fb;
-          load_frag8(fa, sST + (16 * jb + li) * LS + 32 * kq + 8 * g);
-          load_frag8(fb, sQ + (16 * tb + li) * LQ + 32 * kq + 8 * g);
-          ai = mma(fa, fb, ai);
+          Frag<T> fa;
+          load_frag8(fa, sST + (16 * jb + li) * LQ + 32 * kq + 8 * g);
+          ai = mma(fa, qf[kq], ai);
         }
-        // an[rr], ai[rr]: column j = 16 jb + 4 g + rr of output row t
-        if (t < rows)
-          store4(ob + (row0 + t) * D + 16 * jb + 4 * g,
-                 (an[0] + gt * ai[0]) / den, (an[1] + gt * ai[1]) / den,
-                 (an[2] + gt * ai[2]) / den, (an[3] + gt * ai[3]) / den);
+        return an + gt * ai;
+      };
+      // the denominator of row t sits in lane t of group 0
+      const float den = __shfl(block(NJ)[0], li);
+      const float rden = 1.f / den;
+#pragma unroll
+      for (int jj = 0; jj < (NJ + WPS - 1) / WPS; ++jj) {
+        const int jb = jh + WPS * jj;
+        if (jb < NJ) {
+          const f32x4 o = block(jb) * rden;
+          // o[rr]: column j = 16 jb + 4 g + rr of output row t
+          if (t < rows)
+            store4(ob + (row0 + t) * D + 16 * jb + 4 * g, o[0], o[1], o[2],
+                   o[3]);
+        }
       }
-    }
 
-    if (CAUSAL && !last) {
-      // ---- state update: S <- g^r S + (w.K')^T V, z <- g^r z + sum w k' ----
-      const float gr = gp[rows];
-#pragma unroll
-      for (int i = 0; i < F::TPW; ++i) {
-        const int idx = w + kWaves * i;
-        if (idx < F::NTILE)
-          S[i] = state_tile_update<T, C, LT>(S[i] * gr, sKT, sVT, idx / NJ,
-                                             idx % NJ, li, g);
+      if (CAUSAL && !last) {
+        // ---- state update: S <- g^r S + (w.K')^T [V | 1] ----
+        state_update<F>(S, sKw, sV, DECAY ? gp[rows] : 1.f, w, g, li);
+        __syncthreads();  // all waves done reading sST and the chunk tiles
+        publish_state<F>(S, sST, w, g, li);
+      } else {
+        __syncthreads();  // before the next chunk overwrites the tiles
       }
-      float znew = 0.f;
-      if (tid < DF) {
-        float zs = 0.f;
-        for (int s = 0; s < C; ++s) zs += to_f32(sKT[tid * LT + s]);
-        znew = gr * sz[tid] + zs;
-      }
-      __syncthreads();  // every wave has finished reading sST, sz, sQ, sK
-#pragma unroll
-      for (int i = 0; i < F::TPW; ++i) {
-        const int idx = w + kWaves * i;
-        if (idx < F::NTILE) {
-          const int fb = idx / NJ, jb = idx % NJ;
-          store4(sST + (16 * jb + li) * LS + 16 * fb + 4 * g, S[i][0], S[i][1],
-                 S[i][2], S[i][3]);
-        }
-      }
-      if (tid < DF) sz[tid] = znew;
-    } else {
-      __syncthreads();  // before the next chunk overwrites the tiles
     }
   }
 }

@@ -1,5 +1,5 @@
-// Launchers and the (d, d_feat) instance table of the chunked forward, for
-// one storage type LA_T (included once per type by la_forward_*.hip).
+// Launchers and the (d, d_feat) instance table of the fused forward, for one
+// storage type (included once per type by la_forward_*.hip).
 #pragma once
 
 #include "la_forward.h"
@@ -7,59 +7,110 @@
 
 namespace la {
 
-template <typename T, int D, int DF>
-struct FwdRunner {
-  using F = FwdShape<T, D, DF>;
+template <typename T, int D, int DF, bool DECAY>
+struct FwdVariant {
+  using F = FwdShape<T, D, DF, DECAY>;
 
+  static const void *kernel(bool causal, bool multi) {
+    if (causal)
+      return multi
+          ? reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, true, true, DECAY>)
+          : reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, true, false, DECAY>);
+    return reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, false, true, DECAY>);
+  }
+
+  // Raise the dynamic-LDS limit of every instance once (above 64 KiB).
   static hipError_t set_lds() {
-    // Raise the dynamic-LDS limit once per kernel instance (above 64 KiB).
     static const hipError_t once = [] {
-      hipError_t e = hipFuncSetAttribute(
-          reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, true>),
-          hipFuncAttributeMaxDynamicSharedMemorySize,
-          static_cast<int>(F::lds_fwd));
-      if (e == hipSuccess)
-        e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, false>),
-            hipFuncAttributeMaxDynamicSharedMemorySize,
-            static_cast<int>(F::lds_fwd));
-      if (e == hipSuccess)
-        e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&la_agg_kernel<T, D, DF>),
-            hipFuncAttributeMaxDynamicSharedMemorySize,
-            static_cast<int>(F::lds_agg));
-      return e;
+      for (const void *k : {kernel(true, true), kernel(true, false),
+                            kernel(false, true)}) {
+        const hipError_t e = hipFuncSetAttribute(
+            k, hipFuncAttributeMaxDynamicSharedMemorySize,
+            static_cast<int>(F::lds_bytes));
+        if (e != hipSuccess) return e;
+      }
+      return hipSuccess;
     }();
     return once;
   }
 
-  static hipError_t run(const FwdArgs &a, int64_t units, int causal,
+  // Workgroups of the multi-segment kernel that can be resident at once.
+  static hipError_t capacity(int64_t *cap) {
+    static int per_cu = -1;
+    static int cus = 0;
+    if (per_cu < 0) {
+      int dev = 0, n = 0;
+      hipError_t e = hipGetDevice(&dev);
+      if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, kernel(true, true), kThreads, F::lds_bytes);
+      if (e != hipSuccess) return e;
+      per_cu = n;
+    }
+    *cap = static_cast<int64_t>(per_cu) * cus;
+    return hipSuccess;
+  }
+
+  static hipError_t run(const FwdArgs &args, int64_t units, int causal,
                         hipStream_t s) {
     hipError_t e = set_lds();
     if (e != hipSuccess) return e;
-    const int64_t nblk = units * a.nseg;
-    if (a.states) {
-      hipLaunchKernelGGL((la_agg_kernel<T, D, DF>), dim3(nblk), dim3(kThreads),
-                         F::lds_agg, s, a);
-      const hipError_t es = launch_scan(a.states, a.decay, a.H, a.n, a.seg_len,
-                                        a.nseg, units, F::SLOT, F::SLOT_USED,
-                                        s);
-      if (es != hipSuccess) return es;
+    FwdArgs a = args;
+    if (a.nseg > 1) {
+      // The grid barrier needs every workgroup resident: shrink the split to
+      // what fits (the workspace was sized for the largest split).
+      int64_t cap = 0;
+      e = capacity(&cap);
+      if (e != hipSuccess) return e;
+      if (units * a.nseg > cap) {
+        int64_t nseg = cap / units;
+        if (nseg < 1) nseg = 1;
+        const int64_t nch = (a.n + F::C - 1) / F::C;
+        const int64_t cps = (nch + nseg - 1) / nseg;
+        a.seg_len = cps * F::C;
+        a.nseg = static_cast<int>((a.n + a.seg_len - 1) / a.seg_len);
+      }
     }
-    if (causal)
-      hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, true>), dim3(nblk),
-                         dim3(kThreads), F::lds_fwd, s, a);
-    else
-      hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, false>), dim3(nblk),
-                         dim3(kThreads), F::lds_fwd, s, a);
-    return hipGetLastError();
+    const dim3 grid(static_cast<unsigned>(units * a.nseg)), block(kThreads);
+    if (causal && a.nseg == 1) {
+      hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, true, false, DECAY>), grid,
+                         block, F::lds_bytes, s, a);
+      return hipGetLastError();
+    }
+    if (a.nseg == 1) {  // non-causal, one segment: no grid barrier executes
+      hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, false, true, DECAY>), grid,
+                         block, F::lds_bytes, s, a);
+      return hipGetLastError();
+    }
+    void *params[] = {&a};
+    return hipLaunchCooperativeKernel(kernel(causal != 0, true), grid, block,
+                                      params, F::lds_bytes, s);
+  }
+};
+
+template <typename T, int D, int DF>
+struct FwdRunner {
+  using P = FwdShape<T, D, DF, false>;
+  using Q = FwdShape<T, D, DF, true>;
+
+  static hipError_t run(const FwdArgs &a, int64_t units, int causal,
+                        hipStream_t s) {
+    if (a.decay) {
+      if constexpr (Q::fits)
+        return FwdVariant<T, D, DF, true>::run(a, units, causal, s);
+      else
+        return hipErrorInvalidValue;
+    }
+    return FwdVariant<T, D, DF, false>::run(a, units, causal, s);
   }
 
   static const FwdOps *ops() {
-    if constexpr (!F::fits) {
+    if constexpr (!P::fits) {
       return nullptr;
     } else {
-      static const FwdOps o = {F::C, F::SLOT, F::lds_fwd, F::lds_agg, &run};
+      static const FwdOps o = {P::C, P::SLOT, Q::fits, &run};
       return &o;
     }
   }

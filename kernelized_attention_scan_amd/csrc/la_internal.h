@@ -7,12 +7,16 @@
 
 namespace la {
 
+// At most this many sequence segments per (batch, head) unit.
+constexpr int kMaxSegments = 16;
+
 // Arguments of the chunked forward kernels.
 struct FwdArgs {
   const void *q, *k, *v;
   void *out;
   const float *decay;   // [H] or null
-  float *states;        // [units][nseg + 1][slot] or null
+  float *states;        // [units][nseg + 1][slot] segment states, or null
+  unsigned *barrier;    // grid barrier words (zero between launches)
   int H;
   int64_t n;
   int64_t seg_len;      // multiple of the chunk length
@@ -20,17 +24,12 @@ struct FwdArgs {
   int elu1;             // 1: phi = elu + 1 on q, k; 0: q, k are features
 };
 
-// Exclusive prefix of the segment aggregates, in place (slot nseg = total).
-hipError_t launch_scan(float *states, const float *decay, int H, int64_t n,
-                       int64_t seg_len, int nseg, int64_t units, int slot,
-                       int used, hipStream_t stream);
-
 // Launch set of one (storage type, d, d_feat) instance of the chunked forward.
 struct FwdOps {
   int C;              // chunk rows
   int slot_floats;    // floats per fp32 state slot
-  size_t lds_fwd, lds_agg;
-  // Enqueue: [agg + scan when args.states], then the forward kernel.
+  bool decay_ok;      // the decayed variant fits in LDS too
+  // Enqueue the fused forward (cooperative launch when nseg > 1).
   hipError_t (*run)(const FwdArgs &args, int64_t units, int causal,
                     hipStream_t stream);
 };

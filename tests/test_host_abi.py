@@ -73,7 +73,7 @@ def fwd(lib, B=1, H=1, n=64, d=64, df=64, mapk=1, omega=None, decay=None,
     (dict(mapk=2, df=256, omega=None), B.LA_ERR_INVALID_ARG),  # no omega
     (dict(ptr=None), B.LA_ERR_INVALID_ARG),
     (dict(B=8, n=4096, ws=None), B.LA_ERR_WORKSPACE),          # segments
-    (dict(causal=0, ws=None), B.LA_ERR_WORKSPACE),             # total state
+    (dict(causal=0, n=4096, ws=None), B.LA_ERR_WORKSPACE),     # segments
 ])
 def test_forward_rejects(lib, kw, status):
     assert fwd(lib, **kw) == status
@@ -92,17 +92,22 @@ def test_workspace_bytes(lib):
     # rejected arguments report 0
     assert K.forward_workspace_bytes(-1, 1, 64, 64, 64) == 0
     assert K.forward_workspace_bytes(1, 1, 64, 48, 48) == 0
-    # segmented: units * (nseg + 1) fp32 slots of d' x d + d' (rounded to 64)
+    # segmented: 256 barrier bytes + units * (nseg + 1) fp32 slots of
+    # d' x (d + 16) (mu and, in the extra 16-column block, nu)
     ws = K.forward_workspace_bytes(4, 8, 4096, 64, 64)
-    units, C = 32, 64
+    units = 32
     nseg = 16                                  # 512 target groups / 32 units
-    slot = (64 * 64 + 64 + 63) // 64 * 64
-    assert ws == (units * (nseg + 1) * slot * 4 + 255) // 256 * 256
+    slot = 64 * (64 + 16)
+    assert ws == 256 + (units * (nseg + 1) * slot * 4 + 255) // 256 * 256
+    # at most 16 segments per unit
+    one = K.forward_workspace_bytes(1, 1, 1 << 16, 64, 64)
+    assert one == 256 + (17 * slot * 4 + 255) // 256 * 256
     # Performer adds Q' and K' (bf16, d_feat = m wide)
     wp = K.forward_workspace_bytes(4, 8, 8192, 64, 256, "performer")
     assert wp >= 2 * 4 * 8 * 8192 * 256 * 2
-    # non-causal always needs the total state
-    assert K.forward_workspace_bytes(1, 1, 64, 64, 64, causal=False) > 0
+    # non-causal over one segment keeps its total on chip; several need one
+    assert K.forward_workspace_bytes(1, 1, 64, 64, 64, causal=False) == 0
+    assert K.forward_workspace_bytes(1, 1, 4096, 64, 64, causal=False) > 0
     # fp32 storage with d_feat 256 and d 128 does not fit in LDS
     assert K.forward_workspace_bytes(1, 1, 64, 128, 256, "identity",
                                      dtype=__import__("torch").float32) == 0
