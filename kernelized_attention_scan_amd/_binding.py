@@ -32,8 +32,9 @@ SYMBOLS = ("la_featmap", "la_forward_workspace_bytes", "la_forward",
 _lock = threading.Lock()
 _lib = None
 # Zero-initialised workspaces, one per (device, stream): the library keeps the
-# barrier words at their start zero between calls, so a workspace is zeroed
-# once when it is allocated and then reused by every call on that stream.
+# synchronisation area at their start zero between calls, so a workspace is
+# zeroed once when it is allocated and then reused by every call on that
+# stream.
 _workspaces = {}
 
 
@@ -136,8 +137,9 @@ def _workspace(need: int, device) -> torch.Tensor:
 def new_workspace(B: int, H: int, n: int, d: int, d_feat: int,
                   feature_map="elu1", dtype=torch.bfloat16, causal: bool = True,
                   device="cuda") -> torch.Tensor:
-    """A zero-initialised workspace for forward() with these sizes (the
-    first 256 bytes must be zero before the first call; calls keep them so)."""
+    """A zero-initialised workspace for forward() with these sizes (its
+    synchronisation area must be zero before the first call; calls keep it
+    so)."""
     need = forward_workspace_bytes(B, H, n, d, d_feat, feature_map, dtype,
                                    causal)
     return torch.zeros(max(need, 1), dtype=torch.uint8, device=device)

@@ -47,15 +47,14 @@ bool supported_feat(int f) {
 size_t elem_size(int t) { return t == LA_BF16 ? 2 : 4; }
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Sequence split of the fused forward: about kTargetGroups workgroups in
+// Sequence split of the fused forward: about la::kTargetGroups workgroups in
 // total (two 512-thread workgroups per compute unit of a 256-CU MI355X), at
-// most la::kMaxSegments segments of whole chunks per (batch, head) unit.  The
-// launcher shrinks the split when fewer workgroups fit on the device.
-constexpr int64_t kTargetGroups = 512;
+// most la::kMaxSegments segments of whole chunks per (batch, head) unit.  A
+// unit gets several segments only when there are fewer than kTargetGroups
+// units.  The launcher shrinks the split when fewer workgroups fit on the
+// device.
+constexpr int64_t kTargetGroups = la::kTargetGroups;
 constexpr int64_t kMaxSegments = la::kMaxSegments;
-// The workspace starts with the grid-barrier words of the multi-segment
-// kernel; they must be zero before first use and every call leaves them zero.
-constexpr size_t kBarrierBytes = 256;
 
 struct FwdPlan {
   const la::FwdOps *ops = nullptr;
@@ -63,7 +62,8 @@ struct FwdPlan {
   int nseg = 0;
   bool need_states = false;
   size_t feat_bytes = 0;    // one of Q', K' (PERFORMER only)
-  size_t state_bytes = 0;   // barrier words + segment states
+  size_t sync_bytes = 0;    // synchronisation area
+  size_t state_bytes = 0;   // synchronisation area + segment aggregates
   size_t total() const { return state_bytes + 2 * feat_bytes; }
 };
 
@@ -105,9 +105,13 @@ la_status plan_forward(int B, int H, int64_t n, int d, int d_feat, int map,
   if (units * p->nseg > (int64_t{1} << 31) - 1)
     return fail(LA_ERR_UNSUPPORTED, "too many workgroups");
   p->need_states = p->nseg > 1;
+  if (p->need_states && units >= kTargetGroups)
+    return fail(LA_ERR_HIP, "internal: segmented split for %lld units",
+                static_cast<long long>(units));
+  p->sync_bytes = p->need_states ? la::kSyncBytes : 0;
   p->state_bytes = p->need_states
-                       ? kBarrierBytes +
-                             align256(static_cast<size_t>(units) * (p->nseg + 1) *
+                       ? p->sync_bytes +
+                             align256(static_cast<size_t>(units) * p->nseg *
                                       p->ops->slot_floats * sizeof(float))
                        : 0;
   p->feat_bytes = map == LA_MAP_PERFORMER
@@ -221,8 +225,8 @@ la_status la_forward(const void *q, const void *k, const void *v, void *out,
     a.v = v;
     a.out = out;
     a.decay = decay;
-    a.barrier = p.need_states ? reinterpret_cast<unsigned *>(ws) : nullptr;
-    a.states = p.need_states ? reinterpret_cast<float *>(ws + kBarrierBytes)
+    a.sync = p.need_states ? reinterpret_cast<unsigned *>(ws) : nullptr;
+    a.states = p.need_states ? reinterpret_cast<float *>(ws + p.sync_bytes)
                              : nullptr;
     a.H = H;
     a.n = n;

@@ -25,12 +25,12 @@
 //   phase 1 (several segments per (batch, head) unit only): the segment's
 //     aggregate, i.e. its end state from a zero state, from K and V alone,
 //     written to the workspace;
-//   exchange: grid barrier; each workgroup turns a slice of its unit's
-//     aggregates into exclusive prefixes (state entering segment s+1 = g^len
-//     times the state entering s plus A_s) and the total; grid barrier; each
-//     workgroup reads the state entering its segment (non-causal: the
-//     total).  The launch is cooperative, so every workgroup is resident and
-//     the barriers (a counter in the workspace, bounded wait) cannot deadlock;
+//   exchange: each segment publishes its aggregate and a flag in its unit's
+//     line of the workspace, waits for the flags of the segments it needs
+//     (those before it; all of them when non-causal) and sums their
+//     aggregates, weighted by the decay over the gap, into the state entering
+//     it (non-causal: the total).  Only workgroups of one unit wait on each
+//     other; the launch is cooperative, so all of them are resident;
 //   phase 2: the chunk loop from that state.
 // Both loops keep several chunks of loads in flight in a register ring.  All
 // global loads are unconditional (tail rows clamp to a valid row; the loop
@@ -276,68 +276,66 @@ __device__ __forceinline__ void publish_state(const f32x4 *S, T *sST, int w,
   }
 }
 
-// Grid-wide barrier of a cooperative launch (every workgroup is resident).
-// Each barrier instance k of the kernel owns two words of the workspace:
-// bar[2k] counts arrivals and bar[2k+1] departures.  Both are zero between
-// launches because the last workgroup to depart resets them (every workgroup
-// has passed the wait by then, and the next use of the words is the next
-// launch).  One thread per workgroup releases the workgroup's writes, spins
-// with relaxed loads (no cache maintenance per probe), then acquires.  The
-// wait is bounded (about a second): should the words ever be corrupt the
-// barrier sets the flag word bar[kBarrierFlag] and lets the kernel finish
-// rather than hang.
-constexpr int kBarrierFlag = 8;
-
-__device__ __forceinline__ void grid_barrier(unsigned *bar, int k,
-                                             unsigned nblocks) {
+// Exchange of segment aggregates between the workgroups of one (batch, head)
+// unit, through that unit's line of the synchronisation area (see
+// la_internal.h).  Publishing: the aggregate is written, every wave waits for
+// its stores, the workgroup releases them, then flag s is set.  Waiting: one wave polls the flags
+// it needs with relaxed loads (16 lanes, one line) and acquires once all are
+// set.  The launch is cooperative, so every workgroup a wait depends on is
+// resident.  The wait is bounded (a few seconds): if the area were ever
+// corrupt it sets the timeout word and lets the kernel finish instead of
+// hanging.  Every workgroup then counts itself done; the last one clears the
+// unit's line, so the area is zero again for the next launch (no workgroup
+// reads a flag after counting itself done).
+__device__ __forceinline__ void publish_flag(unsigned *line, int seg) {
+  // Each wave waits until its own stores of the aggregate have completed: a
+  // workgroup barrier does not wait for them, and the release below (cache
+  // write-back, then a wait for the flag writer's own accesses) covers what
+  // has reached the cache.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
-    unsigned *arrive = bar + 2 * k, *depart = bar + 2 * k + 1;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(line + seg, 1u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Flags [0, need) of the line all set; call from every thread.
+__device__ __forceinline__ void wait_flags(unsigned *line, int need,
+                                           unsigned *timeout_word) {
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
     unsigned spins = 0;
-    while (__hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-           nblocks) {
+    for (;;) {
+      const unsigned f = lane < need
+                             ? __hip_atomic_load(line + lane, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT)
+                             : 1u;
+      if (__all(f != 0u)) break;
       __builtin_amdgcn_s_sleep(2);
       if (++spins > (1u << 22)) {
-        __hip_atomic_fetch_or(bar + kBarrierFlag, 1u, __ATOMIC_RELAXED,
-                              __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0)
+          __hip_atomic_store(timeout_word, 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    if (__hip_atomic_fetch_add(depart, 1u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT) == nblocks - 1) {
-      __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(depart, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
   }
   __syncthreads();
 }
 
-// Exclusive prefix over the segments of one unit, in place, for the slice
-// [e0, e1) of the state elements; slot nseg receives the total.  The state
-// entering segment s+1 is g^len_s times the state entering s plus A_s (eqs
-// 7-8 / 10-11 applied segment by segment).
-template <bool DECAY>
-__device__ __forceinline__ void scan_slice(float *ub, int slot, int nseg,
-                                           int64_t n, int64_t seg_len, float g,
-                                           float lg, int e0, int e1) {
-  for (int e = e0 + static_cast<int>(threadIdx.x); e < e1; e += kThreads) {
-    float x[kMaxSegments];
-#pragma unroll
-    for (int sp = 0; sp < kMaxSegments; ++sp)
-      x[sp] = ub[static_cast<int64_t>(sp < nseg ? sp : 0) * slot + e];
-    float run = 0.f;
-#pragma unroll
-    for (int sp = 0; sp < kMaxSegments; ++sp) {
-      if (sp < nseg) {
-        ub[static_cast<int64_t>(sp) * slot + e] = run;
-        const int64_t len = min(seg_len, n - sp * seg_len);
-        run = (DECAY ? pow_int(g, lg, len) : 1.f) * run + x[sp];
-      }
-    }
-    ub[static_cast<int64_t>(nseg) * slot + e] = run;
+__device__ __forceinline__ void count_done(unsigned *line, int nseg) {
+  if (threadIdx.x == 0 &&
+      __hip_atomic_fetch_add(line + kSyncDoneWord, 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT) ==
+          static_cast<unsigned>(nseg - 1)) {
+    for (int s = 0; s < nseg; ++s)
+      __hip_atomic_store(line + s, 0u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(line + kSyncDoneWord, 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -360,8 +358,14 @@ void la_fwd_kernel(FwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int g = lane >> 4, li = lane & 15;
-  const int64_t unit = blockIdx.x / a.nseg;
-  const int seg = blockIdx.x % a.nseg;
+  // Workgroups are dispatched to the 8 XCDs round-robin by block index; the
+  // segments of one unit are given blocks of one XCD (when the grid divides
+  // evenly) so their exchange stays within one L2.
+  int64_t blk = blockIdx.x;
+  if (MULTI && a.nseg > 1 && gridDim.x % 8 == 0)
+    blk = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
+  const int64_t unit = blk / a.nseg;
+  const int seg = static_cast<int>(blk % a.nseg);
   const Decay dk(a.decay, static_cast<int>(unit % a.H));
   for (int i = tid; i <= C; i += kThreads) gp[i] = pow_int(dk.g, dk.lg, i);
 
@@ -391,6 +395,24 @@ void la_fwd_kernel(FwdArgs a) {
   f32x4 S[TW];
 #pragma unroll
   for (int i = 0; i < TW; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Phase-2 register ring, first revolution; in the segmented kernel these
+  // loads are issued once the aggregate is published and overlap the wait.
+  Slab<T, DF, C> rq[NB2], rk2[NB2];
+  Slab<T, D, C> rv2[NB2];
+  auto ring2_first = [&]() {
+#pragma unroll
+    for (int b = 0; b < NB2; ++b) {
+      const int cl = b < nch ? b : nch - 1;
+      const int64_t r0 = start + cl * C;
+      const int rows = static_cast<int>(min<int64_t>(C, end - r0));
+      rq[b].load(qb, r0, rows, tid);
+      if (CAUSAL) {
+        rk2[b].load(kb, r0, rows, tid);
+        rv2[b].load(vb, r0, rows, tid);
+      }
+    }
+  };
 
   if constexpr (MULTI) {
     // ---------------- phase 1: segment aggregate from K, V ----------------
@@ -429,60 +451,61 @@ void la_fwd_kernel(FwdArgs a) {
       }
     }
     // With one segment the aggregate is already the state every row needs
-    // (non-causal total); several segments exchange through the workspace:
-    // write the aggregate, barrier, scan a slice of every unit's slots,
-    // barrier, read the state entering this segment (or the total).
+    // (non-causal total).  With several, segment s combines the aggregates
+    // A_j of the segments before it (causal) or of all segments
+    // (non-causal): the state at position E is sum_j g^(E - end_j) A_j,
+    // eqs 7-8 / 10-11 applied segment by segment, with E the segment start
+    // (causal) or n.
     if (a.nseg > 1) {
-      float *ub = a.states + unit * (a.nseg + 1) * static_cast<int64_t>(F::SLOT);
-      float *mine = ub + static_cast<int64_t>(seg) * F::SLOT;
+      float *ub = a.states + unit * a.nseg * static_cast<int64_t>(F::SLOT);
+      unsigned *line = a.sync + kSyncHeaderWords + unit * kSyncLineWords;
+      const int need = CAUSAL ? seg : a.nseg;
+      if (!CAUSAL || seg + 1 < a.nseg) {
+        float *mine = ub + static_cast<int64_t>(seg) * F::SLOT;
 #pragma unroll
-      for (int m = 0; m < F::FPW; ++m)
+        for (int m = 0; m < F::FPW; ++m)
 #pragma unroll
-        for (int mj = 0; mj < F::JPW; ++mj) {
-          const int jb = tile_jb<F>(w, mj);
-          const int idx = tile_fb<F>(w, m) * F::NJA + jb;
-          if (jb < F::NJA)
-            *reinterpret_cast<f32x4 *>(mine + (idx * 64 + lane) * 4) =
-                S[m * F::JPW + mj];
-        }
-      // Every workgroup reaches both barriers exactly once; they run only
-      // under a cooperative launch (the launcher uses one whenever nseg > 1).
-      grid_barrier(a.barrier, 0, gridDim.x);
-      const int per = (F::SLOT + a.nseg - 1) / a.nseg;
-      scan_slice<DECAY>(ub, F::SLOT, a.nseg, a.n, a.seg_len, dk.g, dk.lg,
-                        seg * per, min(F::SLOT, (seg + 1) * per));
-      grid_barrier(a.barrier, 1, gridDim.x);
-      const float *in = ub + static_cast<int64_t>(CAUSAL ? seg : a.nseg) * F::SLOT;
+          for (int mj = 0; mj < F::JPW; ++mj) {
+            const int jb = tile_jb<F>(w, mj);
+            const int idx = tile_fb<F>(w, m) * F::NJA + jb;
+            if (jb < F::NJA)
+              *reinterpret_cast<f32x4 *>(mine + (idx * 64 + lane) * 4) =
+                  S[m * F::JPW + mj];
+          }
+        publish_flag(line, seg);
+      }
+      ring2_first();
+      if (need > 0) wait_flags(line, need, a.sync + kSyncTimeoutWord);
+      count_done(line, a.nseg);
 #pragma unroll
-      for (int m = 0; m < F::FPW; ++m)
+      for (int i = 0; i < TW; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int64_t epos = CAUSAL ? start : a.n;
+#pragma unroll 4
+      for (int j = 0; j < need; ++j) {
+        const int64_t end_j = min(a.n, (j + 1) * a.seg_len);
+        const float wj = DECAY ? pow_int(dk.g, dk.lg, epos - end_j) : 1.f;
+        const float *sj = ub + static_cast<int64_t>(j) * F::SLOT;
 #pragma unroll
-        for (int mj = 0; mj < F::JPW; ++mj) {
-          const int jb = tile_jb<F>(w, mj);
-          const int idx = tile_fb<F>(w, m) * F::NJA + jb;
-          if (jb < F::NJA)
-            S[m * F::JPW + mj] =
-                *reinterpret_cast<const f32x4 *>(in + (idx * 64 + lane) * 4);
-        }
+        for (int m = 0; m < F::FPW; ++m)
+#pragma unroll
+          for (int mj = 0; mj < F::JPW; ++mj) {
+            const int jb = tile_jb<F>(w, mj);
+            const int idx = tile_fb<F>(w, m) * F::NJA + jb;
+            if (jb < F::NJA)
+              S[m * F::JPW + mj] +=
+                  wj * *reinterpret_cast<const f32x4 *>(sj + (idx * 64 + lane) * 4);
+          }
+      }
+    } else {
+      ring2_first();
     }
   }
 
+  if constexpr (!MULTI) ring2_first();
   // the entering state as a T copy of S^T for the readout
   publish_state<F>(S, sST, w, g, li);
 
   // ---------------- phase 2: chunk loop ----------------
-  Slab<T, DF, C> rq[NB2], rk2[NB2];
-  Slab<T, D, C> rv2[NB2];
-#pragma unroll
-  for (int b = 0; b < NB2; ++b) {
-    const int cl = b < nch ? b : nch - 1;
-    const int64_t r0 = start + cl * C;
-    const int rows = static_cast<int>(min<int64_t>(C, end - r0));
-    rq[b].load(qb, r0, rows, tid);
-    if (CAUSAL) {
-      rk2[b].load(kb, r0, rows, tid);
-      rv2[b].load(vb, r0, rows, tid);
-    }
-  }
   __syncthreads();  // gp, sST and the constant tile parts ready
 
   const int tb = w % STRIPS;    // this wave's output strip

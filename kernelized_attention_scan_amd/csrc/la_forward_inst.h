@@ -59,7 +59,7 @@ struct FwdVariant {
     if (e != hipSuccess) return e;
     FwdArgs a = args;
     if (a.nseg > 1) {
-      // The grid barrier needs every workgroup resident: shrink the split to
+      // The exchange needs every workgroup resident: shrink the split to
       // what fits (the workspace was sized for the largest split).
       int64_t cap = 0;
       e = capacity(&cap);
@@ -79,7 +79,7 @@ struct FwdVariant {
                          block, F::lds_bytes, s, a);
       return hipGetLastError();
     }
-    if (a.nseg == 1) {  // non-causal, one segment: no grid barrier executes
+    if (a.nseg == 1) {  // non-causal, one segment: no exchange executes
       hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, false, true, DECAY>), grid,
                          block, F::lds_bytes, s, a);
       return hipGetLastError();

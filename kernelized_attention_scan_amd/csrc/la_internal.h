@@ -10,13 +10,36 @@ namespace la {
 // At most this many sequence segments per (batch, head) unit.
 constexpr int kMaxSegments = 16;
 
+// A sequence is split into several segments only when there are fewer than
+// this many (batch, head) units (about this many workgroups in total).
+constexpr int kTargetGroups = 512;
+
+// Synchronisation area at the start of the workspace of a multi-segment
+// forward (32-bit words, zero between calls).  Its size is fixed, so that
+// whatever sizes the calls sharing a workspace have, no call's scratch ever
+// lands on another call's flags:
+//   words [0, kSyncHeaderWords): status; word kSyncTimeoutWord is set to 1 if
+//     a wait ever gave up (corrupt area), else never written;
+//   then one line of kSyncLineWords per (batch, head) unit, for up to
+//     kTargetGroups units: word s is the "aggregate of segment s published"
+//     flag, word kSyncDoneWord counts the segments done waiting (the last one
+//     clears the line).
+constexpr int kSyncHeaderWords = 64;
+constexpr int kSyncTimeoutWord = 8;
+constexpr int kSyncLineWords = 32;
+constexpr int kSyncDoneWord = kMaxSegments;
+constexpr size_t kSyncBytes =
+    sizeof(unsigned) * (kSyncHeaderWords + kTargetGroups * kSyncLineWords);
+static_assert(kSyncDoneWord < kSyncLineWords, "sync line too short");
+static_assert(kSyncBytes % 256 == 0, "sync area keeps the states aligned");
+
 // Arguments of the chunked forward kernels.
 struct FwdArgs {
   const void *q, *k, *v;
   void *out;
   const float *decay;   // [H] or null
-  float *states;        // [units][nseg + 1][slot] segment states, or null
-  unsigned *barrier;    // grid barrier words (zero between launches)
+  float *states;        // [units][nseg][slot] segment aggregates, or null
+  unsigned *sync;       // synchronisation area (zero between launches)
   int H;
   int64_t n;
   int64_t seg_len;      // multiple of the chunk length

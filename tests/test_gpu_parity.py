@@ -222,6 +222,25 @@ def test_segmentation_invariance():
     assert (a - b).abs().max().item() <= 1e-2 * b.abs().max().item()
 
 
+def test_workspace_shared_across_shapes():
+    """One workspace serves segmented calls of different shapes in turn: the
+    scratch one shape leaves behind never reads as another shape's flags."""
+    shapes = [(1, 2, 2048), (4, 8, 1024), (1, 1, 4096), (2, 4, 700)]
+    cfgs = [I.ELU1_CAUSAL.replace(B=b, H=h, n=n) for b, h, n in shapes]
+    need = max(K.forward_workspace_bytes(c.B, c.H, c.n, c.d, c.d_feat)
+               for c in cfgs)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        for i, cfg in enumerate(cfgs):
+            x = I.make_prefill(cfg, 20 + i)
+            out = K.forward(dev(x["q"]), dev(x["k"]), dev(x["v"]),
+                            workspace=ws)
+            torch.cuda.synchronize()
+            ref = oracle.forward(f64(x["q"]), f64(x["k"]), f64(x["v"]),
+                                 cfg.mapk, None, None, True)
+            assert rel(out, ref) <= TOL[torch.bfloat16], (rep, cfg)
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_constant_v_gives_constant_output(dtype):
     cfg = I.ELU1_CAUSAL.replace(B=1, H=4, n=3000, dtype=dtype,

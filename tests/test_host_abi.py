@@ -92,16 +92,21 @@ def test_workspace_bytes(lib):
     # rejected arguments report 0
     assert K.forward_workspace_bytes(-1, 1, 64, 64, 64) == 0
     assert K.forward_workspace_bytes(1, 1, 64, 48, 48) == 0
-    # segmented: 256 barrier bytes + units * (nseg + 1) fp32 slots of
+    # segmented: a fixed synchronisation area (256 bytes + 512 lines of 128
+    # bytes, one per unit a split can have) + units * nseg fp32 aggregates of
     # d' x (d + 16) (mu and, in the extra 16-column block, nu)
+    sync = 256 + 512 * 128
     ws = K.forward_workspace_bytes(4, 8, 4096, 64, 64)
     units = 32
     nseg = 16                                  # 512 target groups / 32 units
     slot = 64 * (64 + 16)
-    assert ws == 256 + (units * (nseg + 1) * slot * 4 + 255) // 256 * 256
+    a256 = lambda x: (x + 255) // 256 * 256
+    assert ws == sync + a256(units * nseg * slot * 4)
     # at most 16 segments per unit
     one = K.forward_workspace_bytes(1, 1, 1 << 16, 64, 64)
-    assert one == 256 + (17 * slot * 4 + 255) // 256 * 256
+    assert one == sync + a256(16 * slot * 4)
+    # 512 units or more: one segment each, no workspace
+    assert K.forward_workspace_bytes(8, 64, 1 << 16, 64, 64) == 0
     # Performer adds Q' and K' (bf16, d_feat = m wide)
     wp = K.forward_workspace_bytes(4, 8, 8192, 64, 256, "performer")
     assert wp >= 2 * 4 * 8 * 8192 * 256 * 2
