@@ -30,7 +30,9 @@
 //     (those before it; all of them when non-causal) and sums their
 //     aggregates, weighted by the decay over the gap, into the state entering
 //     it (non-causal: the total).  Only workgroups of one unit wait on each
-//     other; the launch is cooperative, so all of them are resident;
+//     other.  Causal segments are numbered in the order their workgroups
+//     start, so every wait is on a running workgroup; the non-causal launch
+//     is cooperative, so all of its workgroups are resident;
 //   phase 2: the chunk loop from that state.
 // Both loops keep several chunks of loads in flight in a register ring.  All
 // global loads are unconditional (tail rows clamp to a valid row; the loop
@@ -116,12 +118,12 @@ struct FwdShape {
   static constexpr int SQ = C * LQ, SKW = DECAY ? C * LQ : 0, SV = C * LV,
                        SST = (D + 16) * LQ;
   static constexpr size_t lds_bytes =
-      sizeof(T) * (2 * SQ + SKW + SV + SST) + sizeof(float) * (C + 1);
+      sizeof(T) * (2 * SQ + SKW + SV + SST) + sizeof(float) * (C + 2);
   // fp32 state slot: NTILE tiles x 64 lanes x 4 (accumulator order).
   static constexpr int SLOT = NTILE * 256;
   // Workgroups per compute unit the instance is built for: two for the small
-  // shapes (<= 128 VGPRs, 4 waves per SIMD), else one.
-  static constexpr int OCC = (D <= 64 && DF <= 64) ? 2 : 1;
+  // bf16 shapes (<= 128 VGPRs, 4 waves per SIMD), else one.
+  static constexpr int OCC = (sizeof(T) == 2 && D <= 64 && DF <= 64) ? 2 : 1;
   static constexpr int WAVES_PER_SIMD = OCC * kWaves / 4;
   // register-ring depths (chunks of loads in flight per workgroup)
   static constexpr int RING = OCC == 2 ? 24 : 64;   // VGPRs for the ring
@@ -279,14 +281,15 @@ __device__ __forceinline__ void publish_state(const f32x4 *S, T *sST, int w,
 // Exchange of segment aggregates between the workgroups of one (batch, head)
 // unit, through that unit's line of the synchronisation area (see
 // la_internal.h).  Publishing: the aggregate is written, every wave waits for
-// its stores, the workgroup releases them, then flag s is set.  Waiting: one wave polls the flags
-// it needs with relaxed loads (16 lanes, one line) and acquires once all are
-// set.  The launch is cooperative, so every workgroup a wait depends on is
-// resident.  The wait is bounded (a few seconds): if the area were ever
+// its stores, the workgroup releases them, then flag s is set.  Waiting: one
+// wave polls the flags it needs with relaxed loads (16 lanes, one line) and
+// acquires once all are set.  Every workgroup a wait depends on is running
+// (causal: segment indices follow start order; non-causal: cooperative
+// launch).  The wait is bounded (a few seconds): if the area were ever
 // corrupt it sets the timeout word and lets the kernel finish instead of
 // hanging.  Every workgroup then counts itself done; the last one clears the
-// unit's line, so the area is zero again for the next launch (no workgroup
-// reads a flag after counting itself done).
+// unit's line (flags, ticket, count), so the area is zero again for the next
+// launch (no workgroup touches the line after counting itself done).
 __device__ __forceinline__ void publish_flag(unsigned *line, int seg) {
   // Each wave waits until its own stores of the aggregate have completed: a
   // workgroup barrier does not wait for them, and the release below (cache
@@ -334,6 +337,8 @@ __device__ __forceinline__ void count_done(unsigned *line, int nseg) {
     for (int s = 0; s < nseg; ++s)
       __hip_atomic_store(line + s, 0u, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(line + kSyncTicketWord, 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(line + kSyncDoneWord, 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -365,7 +370,29 @@ void la_fwd_kernel(FwdArgs a) {
   if (MULTI && a.nseg > 1 && gridDim.x % 8 == 0)
     blk = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
   const int64_t unit = blk / a.nseg;
-  const int seg = static_cast<int>(blk % a.nseg);
+  unsigned *line = MULTI && a.nseg > 1
+                       ? a.sync + kSyncHeaderWords + unit * kSyncLineWords
+                       : nullptr;
+  int seg = static_cast<int>(blk % a.nseg);
+  if (MULTI && CAUSAL && a.nseg > 1) {
+    // Causal segments take their index from the unit's ticket counter, in
+    // the order they start: a segment then only ever waits for segments that
+    // are already running, so no co-residency is needed.
+    int *ticket = reinterpret_cast<int *>(gp + C + 1);
+    if (tid == 0) {
+      unsigned t = __hip_atomic_fetch_add(line + kSyncTicketWord, 1u,
+                                          __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+      if (t >= static_cast<unsigned>(a.nseg)) {  // corrupt area: stay in bounds
+        __hip_atomic_store(a.sync + kSyncTimeoutWord, 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        t %= static_cast<unsigned>(a.nseg);
+      }
+      *ticket = static_cast<int>(t);
+    }
+    __syncthreads();
+    seg = __builtin_amdgcn_readfirstlane(*ticket);
+  }
   const Decay dk(a.decay, static_cast<int>(unit % a.H));
   for (int i = tid; i <= C; i += kThreads) gp[i] = pow_int(dk.g, dk.lg, i);
 
@@ -458,7 +485,6 @@ void la_fwd_kernel(FwdArgs a) {
     // (causal) or n.
     if (a.nseg > 1) {
       float *ub = a.states + unit * a.nseg * static_cast<int64_t>(F::SLOT);
-      unsigned *line = a.sync + kSyncHeaderWords + unit * kSyncLineWords;
       const int need = CAUSAL ? seg : a.nseg;
       if (!CAUSAL || seg + 1 < a.nseg) {
         float *mine = ub + static_cast<int64_t>(seg) * F::SLOT;
@@ -480,21 +506,36 @@ void la_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int i = 0; i < TW; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int64_t epos = CAUSAL ? start : a.n;
-#pragma unroll 4
-      for (int j = 0; j < need; ++j) {
-        const int64_t end_j = min(a.n, (j + 1) * a.seg_len);
-        const float wj = DECAY ? pow_int(dk.g, dk.lg, epos - end_j) : 1.f;
-        const float *sj = ub + static_cast<int64_t>(j) * F::SLOT;
+      // Groups of GRP aggregates (about 12 tiles per lane); the loads of a
+      // group are unconditional (indices past the last clamp to it, with
+      // weight 0) so they are all in flight together.
+      constexpr int GRP = TW >= 8 ? 1 : (TW >= 4 ? 2 : 4);
+      for (int j0 = 0; j0 < need; j0 += GRP) {
+        f32x4 buf[GRP][TW];
 #pragma unroll
-        for (int m = 0; m < F::FPW; ++m)
+        for (int u = 0; u < GRP; ++u) {
+          const int j = min(j0 + u, need - 1);
+          const float *sj = ub + static_cast<int64_t>(j) * F::SLOT;
 #pragma unroll
-          for (int mj = 0; mj < F::JPW; ++mj) {
-            const int jb = tile_jb<F>(w, mj);
-            const int idx = tile_fb<F>(w, m) * F::NJA + jb;
-            if (jb < F::NJA)
-              S[m * F::JPW + mj] +=
-                  wj * *reinterpret_cast<const f32x4 *>(sj + (idx * 64 + lane) * 4);
-          }
+          for (int m = 0; m < F::FPW; ++m)
+#pragma unroll
+            for (int mj = 0; mj < F::JPW; ++mj) {
+              const int jb = tile_jb<F>(w, mj);
+              const int idx = tile_fb<F>(w, m) * F::NJA + min(jb, F::NJA - 1);
+              buf[u][m * F::JPW + mj] =
+                  *reinterpret_cast<const f32x4 *>(sj + (idx * 64 + lane) * 4);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < GRP; ++u) {
+          const int j = j0 + u;
+          const int64_t end_j = min(a.n, (j + 1) * a.seg_len);
+          const float wj = j >= need ? 0.f
+                           : DECAY  ? pow_int(dk.g, dk.lg, epos - end_j)
+                                    : 1.f;
+#pragma unroll
+          for (int i = 0; i < TW; ++i) S[i] += wj * buf[u][i];
+        }
       }
     } else {
       ring2_first();

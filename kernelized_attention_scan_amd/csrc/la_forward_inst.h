@@ -34,7 +34,7 @@ struct FwdVariant {
     return once;
   }
 
-  // Workgroups of the multi-segment kernel that can be resident at once.
+  // Workgroups of the non-causal multi-segment kernel resident at once.
   static hipError_t capacity(int64_t *cap) {
     static int per_cu = -1;
     static int cus = 0;
@@ -45,7 +45,7 @@ struct FwdVariant {
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
       if (e == hipSuccess)
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, kernel(true, true), kThreads, F::lds_bytes);
+            &n, kernel(false, true), kThreads, F::lds_bytes);
       if (e != hipSuccess) return e;
       per_cu = n;
     }
@@ -58,9 +58,10 @@ struct FwdVariant {
     hipError_t e = set_lds();
     if (e != hipSuccess) return e;
     FwdArgs a = args;
-    if (a.nseg > 1) {
-      // The exchange needs every workgroup resident: shrink the split to
-      // what fits (the workspace was sized for the largest split).
+    if (a.nseg > 1 && !causal) {
+      // The non-causal exchange waits on every segment, so every workgroup
+      // must be resident: shrink the split to what fits (the workspace was
+      // sized for the largest split) and launch cooperatively.
       int64_t cap = 0;
       e = capacity(&cap);
       if (e != hipSuccess) return e;
@@ -74,9 +75,15 @@ struct FwdVariant {
       }
     }
     const dim3 grid(static_cast<unsigned>(units * a.nseg)), block(kThreads);
-    if (causal && a.nseg == 1) {
-      hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, true, false, DECAY>), grid,
-                         block, F::lds_bytes, s, a);
+    if (causal) {
+      // One segment: no exchange.  Several: segments are numbered in start
+      // order, so a plain launch cannot deadlock.
+      if (a.nseg == 1)
+        hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, true, false, DECAY>), grid,
+                           block, F::lds_bytes, s, a);
+      else
+        hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, true, true, DECAY>), grid,
+                           block, F::lds_bytes, s, a);
       return hipGetLastError();
     }
     if (a.nseg == 1) {  // non-causal, one segment: no exchange executes
@@ -85,8 +92,8 @@ struct FwdVariant {
       return hipGetLastError();
     }
     void *params[] = {&a};
-    return hipLaunchCooperativeKernel(kernel(causal != 0, true), grid, block,
-                                      params, F::lds_bytes, s);
+    return hipLaunchCooperativeKernel(kernel(false, true), grid, block, params,
+                                      F::lds_bytes, s);
   }
 };
 

@@ -22,15 +22,17 @@ constexpr int kTargetGroups = 512;
 //     a wait ever gave up (corrupt area), else never written;
 //   then one line of kSyncLineWords per (batch, head) unit, for up to
 //     kTargetGroups units: word s is the "aggregate of segment s published"
-//     flag, word kSyncDoneWord counts the segments done waiting (the last one
-//     clears the line).
+//     flag, word kSyncTicketWord hands out causal segment indices in start
+//     order, word kSyncDoneWord counts the segments done waiting (the last
+//     one clears the line).
 constexpr int kSyncHeaderWords = 64;
 constexpr int kSyncTimeoutWord = 8;
 constexpr int kSyncLineWords = 32;
 constexpr int kSyncDoneWord = kMaxSegments;
+constexpr int kSyncTicketWord = kMaxSegments + 1;
 constexpr size_t kSyncBytes =
     sizeof(unsigned) * (kSyncHeaderWords + kTargetGroups * kSyncLineWords);
-static_assert(kSyncDoneWord < kSyncLineWords, "sync line too short");
+static_assert(kSyncTicketWord < kSyncLineWords, "sync line too short");
 static_assert(kSyncBytes % 256 == 0, "sync area keeps the states aligned");
 
 // Arguments of the chunked forward kernels.
