@@ -1,15 +1,19 @@
 #!/usr/bin/env python3
 """Throughput of causal kernelized linear attention on one MI355X.
 
-One step = one la_forward call over one batch of synthetic, HBM-resident
-input (all hot-path kernels).  Default workload: elu+1 causal, B=4, H=8,
-n=4096, d=d'=64, bf16 storage.  The inputs (67 MB per set) fit in the 256 MB
-MALL, so the timed loop rotates over enough distinct buffer sets (> 300 MB) that
-every step reads from HBM.
+One step = one pass of the whole hot path over one batch of synthetic,
+HBM-resident input:
+  prefill workloads: one la_forward call (Performer: the two feature-map
+    launches and the chunked forward it makes);
+  decode: one la_decode_step over every (sequence, head) unit.
+Default workload: elu+1 causal, B=4, H=8, n=4096, d=d'=64, bf16 storage.
+Its inputs (67 MB per set) fit in the 256 MB MALL, so the timed loop rotates
+over enough distinct buffer sets (> 300 MB) that every step reads from HBM.
 
-Prints one JSON line:  tokens/s (B*H*n per second), the roofline of the hot
-path (HBM bound: algorithmic bytes = read q, k, v and write out once), and
-the fp64 CPU oracle timed on the host on a bounded sample.
+Prints one JSON line: throughput (tokens/s = B*H*n per second; decode:
+(sequence, head) units per second), the roofline of the dominant kernel
+(HBM bound: algorithmic bytes per launch / its measured duration), and the
+fp64 CPU oracle timed on the host cores over a bounded sample.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -46,23 +50,39 @@ def kernel_source_hash() -> str:
 def workloads():
     from kernelized_attention_scan_amd import inputs as I
     return {"elu1": I.ELU1_CAUSAL, "decayed": I.DECAYED,
-            "performer": I.PERFORMER, "tiny": I.TINY_FP32}
+            "performer": I.PERFORMER, "tiny": I.TINY_FP32,
+            "decode": I.DECODE}
 
 
-def algorithmic(cfg):
-    """Bytes and flops the method itself must move / compute per step."""
-    esz = 2 if "bfloat16" in str(cfg.dtype) else 4
-    tokens = cfg.tokens
-    byts = tokens * 4 * cfg.d * esz                 # read q, k, v; write out
+def esize(dtype) -> int:
+    return 2 if "bfloat16" in str(dtype) else 4
+
+
+def prefill_algorithmic(cfg):
+    """Bytes and flops the method itself must move / compute per step: read
+    q, k, v and write out once; 4 d' d + 4 d' flops per token (state update
+    and readout), plus the Performer projection of q and k."""
+    byts = cfg.tokens * 4 * cfg.d * esize(cfg.dtype)
     df = cfg.d_feat
-    flops = tokens * (4 * df * cfg.d + 4 * df)      # state update + readout
+    flops = cfg.tokens * (4 * df * cfg.d + 4 * df)
     if cfg.mapk == 2:
-        flops += tokens * 2 * 2 * cfg.d * cfg.m     # phi projection, q and k
+        flops += cfg.tokens * 2 * 2 * cfg.d * cfg.m
+    return byts, flops
+
+
+def decode_algorithmic(cfg):
+    """Per step: read and write mu, nu (fp32) once; read q, k, v and write
+    out (storage dtype)."""
+    units = cfg.S * cfg.H
+    df, d = cfg.d_feat, cfg.d
+    byts = units * (2 * df * d * 4 + 2 * df * 4 + 4 * d * esize(cfg.dtype))
+    flops = units * (4 * df * d + 4 * df)
     return byts, flops
 
 
 def load_traffic(workload: str):
-    """Counter-measured HBM bytes per step, if taken on the current kernels."""
+    """Counter-measured HBM bytes per launch of the dominant kernel, if taken
+    on the current kernel sources."""
     p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(p):
         return None
@@ -73,43 +93,198 @@ def load_traffic(workload: str):
     return t.get("traffic_bytes")
 
 
-def cpu_baseline(cfg, seed: int, budget_s: float = 20.0):
-    """The fp64 oracle on the host cores over a bounded sample of units."""
-    import numpy as np
+def time_loop(torch, fn, steps: int, stream):
+    """Average ms per call of fn(i) over `steps` calls, HIP events recorded on
+    the stream the library launches on."""
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(steps):
+        fn(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps
+
+
+# --------------------------------------------------------------------------
+# CPU baselines: the fp64 oracle, as it stands, on a bounded sample
+# --------------------------------------------------------------------------
+
+def cpu_baseline_prefill(cfg, seed: int, budget_s: float = 20.0):
     import oracle
     from kernelized_attention_scan_amd import inputs as I
     x = I.make_prefill(cfg, seed)
     f64 = lambda t: None if t is None else t.double().numpy()
-    q, k, v = x["q"], x["k"], x["v"]
     units = cfg.B * cfg.H
-    # calibrate on one unit, then take as many units as fit the budget
-    t0 = time.perf_counter()
-    oracle.forward(f64(q[:1, :1]), f64(k[:1, :1]), f64(v[:1, :1]), cfg.mapk,
-                   f64(x["omega"]),
-                   None if x["decay"] is None else f64(x["decay"][:1]),
-                   cfg.causal)
-    one = time.perf_counter() - t0
+    flat = lambda t: t.reshape(1, units, cfg.n, t.shape[-1])
+    q, k, v = flat(x["q"]), flat(x["k"]), flat(x["v"])
+    dec = None if x["decay"] is None else x["decay"].repeat(cfg.B)
+    om = f64(x["omega"])
     threads = oracle.num_threads()
-    take = max(1, min(units, int(budget_s / max(one, 1e-9)) * threads // 1))
-    take = min(take, units)
-    flat = lambda t: t.reshape(units, 1, cfg.n, t.shape[-1])[:take]
-    dec = None
-    if x["decay"] is not None:
-        dec = x["decay"].repeat(cfg.B)[:take]
-    qs, ks, vs = flat(q), flat(k), flat(v)
+    # calibrate on one unit per thread, then take as many units as fit
+    probe = min(units, threads)
     t0 = time.perf_counter()
-    oracle.forward(f64(qs).reshape(1, take, cfg.n, -1),
-                   f64(ks).reshape(1, take, cfg.n, -1),
-                   f64(vs).reshape(1, take, cfg.n, -1), cfg.mapk,
-                   f64(x["omega"]), None if dec is None else f64(dec),
+    oracle.forward(f64(q[:, :probe]), f64(k[:, :probe]), f64(v[:, :probe]),
+                   cfg.mapk, om, None if dec is None else f64(dec[:probe]),
                    cfg.causal)
-    dt = time.perf_counter() - t0
-    tokens = take * cfg.n
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
+    per_round = time.perf_counter() - t0
+    take = int(budget_s / max(per_round, 1e-9)) * probe
+    take = max(probe, min(units, take))
+    args = (f64(q[:, :take]), f64(k[:, :take]), f64(v[:, :take]), cfg.mapk,
+            om, None if dec is None else f64(dec[:take]), cfg.causal)
+    reps, dt = 0, 0.0
+    while reps == 0 or dt < 2.0:      # repeat a short sample for a stable time
+        t0 = time.perf_counter()
+        oracle.forward(*args)
+        dt += time.perf_counter() - t0
+        reps += 1
+    return {"value": reps * take * cfg.n / dt, "unit": "tokens/s",
+            "cores": threads, "kind": "oracle",
             "sample": f"{take} of {units} (batch, head) units x n={cfg.n} of "
-                      f"workload {cfg.name}, fp64 literal recurrence, "
-                      f"{dt:.1f} s"}
+                      f"workload {cfg.name}, {reps} pass(es); fp64 literal "
+                      f"recurrence, {dt:.1f} s"}
+
+
+def cpu_baseline_decode(cfg, seed: int, budget_s: float = 10.0):
+    import oracle
+    from kernelized_attention_scan_amd import inputs as I
+    x = I.make_decode(cfg, seed)
+    f64 = lambda t: None if t is None else t.double().numpy()
+    threads = oracle.num_threads()
+    S = cfg.S
+    probe = max(1, min(S, threads))
+    t0 = time.perf_counter()
+    oracle.decode(f64(x["mu"][:probe]), f64(x["nu"][:probe]),
+                  f64(x["q"][:probe]), f64(x["k"][:probe]),
+                  f64(x["v"][:probe]), cfg.mapk, f64(x["omega"]),
+                  f64(x["decay"]))
+    per = time.perf_counter() - t0
+    take = max(probe, min(S, int(budget_s / max(per, 1e-9)) * probe))
+    t0 = time.perf_counter()
+    oracle.decode(f64(x["mu"][:take]), f64(x["nu"][:take]),
+                  f64(x["q"][:take]), f64(x["k"][:take]),
+                  f64(x["v"][:take]), cfg.mapk, f64(x["omega"]),
+                  f64(x["decay"]))
+    dt = time.perf_counter() - t0
+    return {"value": take * cfg.H / dt, "unit": "head-tokens/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"{take} of {S} sequences x H={cfg.H} of workload "
+                      f"{cfg.name}; fp64 decode step (input conversion "
+                      f"included), {dt:.2f} s"}
+
+
+# --------------------------------------------------------------------------
+# GPU legs
+# --------------------------------------------------------------------------
+
+def prefill_leg(torch, K, I, cfg, args, dev):
+    mapname = I.MAP_NAMES[cfg.mapk]
+    byts, flops = prefill_algorithmic(cfg)
+    set_bytes = byts + (cfg.d * cfg.m * 4 if cfg.mapk == 2 else 0)
+    nsets = max(1, min(8, math.ceil(1.2 * MALL_BYTES / set_bytes)))
+    sets = []
+    for i in range(nsets):
+        x = I.make_prefill(cfg, args.seed + i)
+        sets.append({k: (None if t is None else t.to(dev)) for k, t in x.items()})
+    outs = [torch.empty_like(s["v"]) for s in sets]
+    ws = K.new_workspace(cfg.B, cfg.H, cfg.n, cfg.d, cfg.d_feat, mapname,
+                         cfg.dtype, cfg.causal, device=dev)
+    stream = torch.cuda.current_stream(dev)   # the library launches here
+
+    def step(i):
+        s = sets[i % nsets]
+        K.forward(s["q"], s["k"], s["v"], feature_map=mapname,
+                  omega=s["omega"], decay=s["decay"], causal=cfg.causal,
+                  out=outs[i % nsets], workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    t_wall = time.perf_counter()
+    ms = time_loop(torch, step, args.steps, stream)
+    t_wall = time.perf_counter() - t_wall
+
+    esz = esize(cfg.dtype)
+    if cfg.mapk != 2:
+        # one kernel per step: the chunked forward
+        kern = {"kernel": "la_fwd_kernel (chunked causal forward)",
+                "ms": ms, "bytes": byts, "flops": flops}
+    else:
+        # Performer: the same two kinds of launch la_forward makes, timed
+        # apart -- the feature map (x -> phi(x), per call one of q, k) and the
+        # chunked forward over the features.
+        rows = cfg.tokens
+        feats = [torch.empty(cfg.B, cfg.H, cfg.n, cfg.m, dtype=cfg.dtype,
+                             device=dev) for _ in range(2)]
+        fws = K.new_workspace(cfg.B, cfg.H, cfg.n, cfg.d, cfg.m, "identity",
+                              cfg.dtype, cfg.causal, device=dev)
+
+        def fmap(i):
+            s = sets[i % nsets]
+            K.featmap(s["q"], "performer", omega=s["omega"], out=feats[0])
+
+        def fwd_feat(i):
+            s = sets[i % nsets]
+            K.forward(feats[0], feats[1], s["v"], feature_map="identity",
+                      causal=cfg.causal, out=outs[i % nsets], workspace=fws)
+
+        fmap(0)
+        K.featmap(sets[0]["k"], "performer", omega=sets[0]["omega"],
+                  out=feats[1])
+        for i in range(3):
+            fwd_feat(i)
+        ms_f = time_loop(torch, fmap, args.steps, stream)
+        ms_w = time_loop(torch, fwd_feat, args.steps, stream)
+        f_bytes = rows * (cfg.d + cfg.m) * esz
+        w_bytes = cfg.tokens * (2 * cfg.m + 2 * cfg.d) * esz
+        w_flops = cfg.tokens * (4 * cfg.m * cfg.d + 4 * cfg.m)
+        if ms_w >= ms_f:
+            kern = {"kernel": "la_fwd_kernel over Performer features "
+                              "(d_feat = m)",
+                    "ms": ms_w, "bytes": w_bytes, "flops": w_flops}
+        else:
+            kern = {"kernel": "la_featmap_performer (one of q, k)",
+                    "ms": ms_f, "bytes": f_bytes,
+                    "flops": rows * 2 * cfg.d * cfg.m}
+        kern["other_launches_ms"] = {"featmap_one_of_q_k": ms_f,
+                                     "forward_over_features": ms_w}
+    return {"ms": ms, "t_wall": t_wall, "items": cfg.tokens,
+            "unit": "tokens/s", "bytes": byts, "flops": flops,
+            "kern": kern, "nsets": nsets,
+            "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H,
+                       "n": cfg.n, "d": cfg.d, "d_feat": cfg.d_feat,
+                       "map": mapname, "decay": cfg.decay,
+                       "causal": cfg.causal, "buffer_sets": nsets,
+                       "seed": args.seed}}
+
+
+def decode_leg(torch, K, I, cfg, args, dev):
+    mapname = I.MAP_NAMES[cfg.mapk]
+    byts, flops = decode_algorithmic(cfg)
+    x = I.make_decode(cfg, args.seed)
+    s = {k: (None if t is None else t.to(dev)) for k, t in x.items()}
+    out = torch.empty_like(s["v"])
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        # mu, nu are updated in place: successive steps form a decode chain
+        K.decode_step(s["mu"], s["nu"], s["q"], s["k"], s["v"], mapname,
+                      omega=s["omega"], decay=s["decay"], out=out)
+
+    for i in range(args.warmup):
+        step(i)
+    t_wall = time.perf_counter()
+    ms = time_loop(torch, step, args.steps, stream)
+    t_wall = time.perf_counter() - t_wall
+    units = cfg.S * cfg.H
+    return {"ms": ms, "t_wall": t_wall, "items": units,
+            "unit": "head-tokens/s", "bytes": byts, "flops": flops,
+            "kern": {"kernel": "la_decode_kernel (state streamed once)",
+                     "ms": ms, "bytes": byts, "flops": flops},
+            "nsets": 1,
+            "config": {"workload": cfg.name, "S": cfg.S, "H": cfg.H,
+                       "d": cfg.d, "d_feat": cfg.d_feat, "map": mapname,
+                       "a": cfg.a, "seed": args.seed}}
 
 
 def main() -> int:
@@ -120,11 +295,16 @@ def main() -> int:
     ap.add_argument("--workload", default="elu1", choices=sorted(workloads()))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-MiB buffer three times (a kernel of "
+                         "known HBM traffic, to scale the profiler's byte "
+                         "counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not "
-              "supported (the method shards over (batch, head) units with no "
-              "exchange; see the design notes)", file=sys.stderr)
+              "supported: this build runs on a single GPU (units of (batch, "
+              "head) shard across GPUs with no exchange, see the design "
+              "notes)", file=sys.stderr)
         return 2
 
     import torch
@@ -134,52 +314,37 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         return 1
-    K.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": nbytes,
+                          "copy_calibration_bytes_written": nbytes,
+                          "launches": 3}), flush=True)
+        return 0
+    K.load_library()
     cfg = workloads()[args.workload]
-    mapname = I.MAP_NAMES[cfg.mapk]
-    byts, flops = algorithmic(cfg)
-
-    # distinct buffer sets, together larger than the MALL
-    set_bytes = byts + (cfg.d * cfg.m * 4 if cfg.mapk == 2 else 0)
-    nsets = max(1, min(8, math.ceil(1.2 * MALL_BYTES / set_bytes)))
-    sets = []
-    for i in range(nsets):
-        x = I.make_prefill(cfg, args.seed + i)
-        sets.append({k: (None if t is None else t.to(dev)) for k, t in x.items()})
-    outs = [torch.empty_like(s["v"]) for s in sets]
-    ws = K.new_workspace(cfg.B, cfg.H, cfg.n, cfg.d, cfg.d_feat, mapname,
-                         cfg.dtype, cfg.causal, device=dev)
-
-    def step(i):
-        s = sets[i % nsets]
-        K.forward(s["q"], s["k"], s["v"], feature_map=mapname,
-                  omega=s["omega"], decay=s["decay"], causal=cfg.causal,
-                  out=outs[i % nsets], workspace=ws)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)   # the library launches here
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms = ev0.elapsed_time(ev1) / args.steps
-
-    tokens_per_s = cfg.tokens / (ms * 1e-3)
-    achieved = byts / (ms * 1e-3) / 1e9
-    traffic = load_traffic(cfg.name)
+    is_decode = args.workload == "decode"
+    leg = (decode_leg if is_decode else prefill_leg)(torch, K, I, cfg, args,
+                                                     dev)
+    ms = leg["ms"]
+    kern = leg["kern"]
+    achieved = kern["bytes"] / (kern["ms"] * 1e-3) / 1e9
+    if is_decode or cfg.dtype != torch.bfloat16:
+        dtype = "f32"
+    else:
+        dtype = "bf16"
     line = {
-        "metric": METRIC,
-        "value": tokens_per_s,
-        "unit": "tokens/s",
+        "metric": METRIC if not is_decode else
+                  "linear-attn decode step head-tokens/s (S·H/s) + % of "
+                  "HBM roofline",
+        "value": leg["items"] / (ms * 1e-3),
+        "unit": leg["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -187,24 +352,28 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.dtype == torch.bfloat16 else "f32",
+        "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "n": cfg.n,
-                   "d": cfg.d, "d_feat": cfg.d_feat, "map": mapname,
-                   "decay": cfg.decay, "causal": cfg.causal,
-                   "buffer_sets": nsets, "seed": args.seed},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic,
-                     "kernel": "la_forward (one call: all hot-path kernels)",
-                     "algorithmic_bytes_per_launch": byts,
-                     "algorithmic_flops_per_launch": flops,
+        "config": leg["config"],
+        "roofline": {"bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": load_traffic(args.workload),
+                     "kernel": kern["kernel"],
+                     "kernel_ms_per_launch": kern["ms"],
+                     "algorithmic_bytes_per_launch": kern["bytes"],
+                     "algorithmic_flops_per_launch": kern["flops"],
                      "mfma_frac_algorithmic":
-                         flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
-        "wall_s_timed_region": t_wall,
+                         kern["flops"] / (kern["ms"] * 1e-3) / 1e12
+                         / BF16_PEAK_TFLOPS},
+        "step_algorithmic_GBs": leg["bytes"] / (ms * 1e-3) / 1e9,
+        "wall_s_timed_region": leg["t_wall"],
     }
+    if "other_launches_ms" in kern:
+        line["roofline"]["launches_ms"] = kern["other_launches_ms"]
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, args.seed)
+        line["cpu_baseline"] = (cpu_baseline_decode if is_decode
+                                else cpu_baseline_prefill)(cfg, args.seed)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -47,13 +47,12 @@ bool supported_feat(int f) {
 size_t elem_size(int t) { return t == LA_BF16 ? 2 : 4; }
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Sequence split of the fused forward: about la::kTargetGroups workgroups in
-// total (two 512-thread workgroups per compute unit of a 256-CU MI355X), at
-// most la::kMaxSegments segments of whole chunks per (batch, head) unit.  A
-// unit gets several segments only when there are fewer than kTargetGroups
-// units.  The launcher shrinks the split when fewer workgroups fit on the
-// device.
-constexpr int64_t kTargetGroups = la::kTargetGroups;
+// Sequence split of the fused forward: about occ * la::kCUs workgroups in
+// total (occ = workgroups per compute unit of the instance), at most
+// la::kMaxSegments segments of whole chunks per (batch, head) unit.  A unit
+// gets several segments only when there are fewer units than that.  Causal
+// splits may exceed what is resident at once; the non-causal launcher
+// shrinks its split to what fits.
 constexpr int64_t kMaxSegments = la::kMaxSegments;
 
 struct FwdPlan {
@@ -95,7 +94,8 @@ la_status plan_forward(int B, int H, int64_t n, int d, int d_feat, int map,
     return fail(LA_ERR_UNSUPPORTED, "sizes too large");
   const int64_t C = p->ops->C;
   const int64_t nchunks = (n + C - 1) / C;
-  int64_t per_unit = (kTargetGroups + units - 1) / units;
+  const int64_t target = static_cast<int64_t>(p->ops->occ) * la::kCUs;
+  int64_t per_unit = (target + units - 1) / units;
   if (per_unit > kMaxSegments) per_unit = kMaxSegments;
   if (per_unit < 1) per_unit = 1;
   if (per_unit > nchunks) per_unit = nchunks;
@@ -105,7 +105,7 @@ la_status plan_forward(int B, int H, int64_t n, int d, int d_feat, int map,
   if (units * p->nseg > (int64_t{1} << 31) - 1)
     return fail(LA_ERR_UNSUPPORTED, "too many workgroups");
   p->need_states = p->nseg > 1;
-  if (p->need_states && units >= kTargetGroups)
+  if (p->need_states && units >= la::kMaxTargetGroups)
     return fail(LA_ERR_HIP, "internal: segmented split for %lld units",
                 static_cast<long long>(units));
   p->sync_bytes = p->need_states ? la::kSyncBytes : 0;

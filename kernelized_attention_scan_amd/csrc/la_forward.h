@@ -124,6 +124,7 @@ struct FwdShape {
   // Workgroups per compute unit the instance is built for: two for the small
   // bf16 shapes (<= 128 VGPRs, 4 waves per SIMD), else one.
   static constexpr int OCC = (sizeof(T) == 2 && D <= 64 && DF <= 64) ? 2 : 1;
+  static_assert(OCC * kCUs <= kMaxTargetGroups, "sync area too small");
   static constexpr int WAVES_PER_SIMD = OCC * kWaves / 4;
   // register-ring depths (chunks of loads in flight per workgroup)
   static constexpr int RING = OCC == 2 ? 24 : 64;   // VGPRs for the ring

@@ -117,7 +117,8 @@ struct FwdRunner {
     if constexpr (!P::fits) {
       return nullptr;
     } else {
-      static const FwdOps o = {P::C, P::SLOT, Q::fits, &run};
+      static_assert(P::OCC == Q::OCC, "one split for both variants");
+      static const FwdOps o = {P::C, P::SLOT, Q::fits, P::OCC, &run};
       return &o;
     }
   }

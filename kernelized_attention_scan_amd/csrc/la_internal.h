@@ -10,9 +10,12 @@ namespace la {
 // At most this many sequence segments per (batch, head) unit.
 constexpr int kMaxSegments = 16;
 
-// A sequence is split into several segments only when there are fewer than
-// this many (batch, head) units (about this many workgroups in total).
-constexpr int kTargetGroups = 512;
+// Compute units of an MI355X.  A forward is split into about
+// kCUs * (workgroups per CU of its instance) workgroups; a sequence is split
+// into several segments only when there are fewer (batch, head) units than
+// that, never more than kMaxTargetGroups.
+constexpr int kCUs = 256;
+constexpr int kMaxTargetGroups = 512;
 
 // Synchronisation area at the start of the workspace of a multi-segment
 // forward (32-bit words, zero between calls).  Its size is fixed, so that
@@ -21,7 +24,7 @@ constexpr int kTargetGroups = 512;
 //   words [0, kSyncHeaderWords): status; word kSyncTimeoutWord is set to 1 if
 //     a wait ever gave up (corrupt area), else never written;
 //   then one line of kSyncLineWords per (batch, head) unit, for up to
-//     kTargetGroups units: word s is the "aggregate of segment s published"
+//     kMaxTargetGroups units: word s is the "aggregate of segment s published"
 //     flag, word kSyncTicketWord hands out causal segment indices in start
 //     order, word kSyncDoneWord counts the segments done waiting (the last
 //     one clears the line).
@@ -31,7 +34,7 @@ constexpr int kSyncLineWords = 32;
 constexpr int kSyncDoneWord = kMaxSegments;
 constexpr int kSyncTicketWord = kMaxSegments + 1;
 constexpr size_t kSyncBytes =
-    sizeof(unsigned) * (kSyncHeaderWords + kTargetGroups * kSyncLineWords);
+    sizeof(unsigned) * (kSyncHeaderWords + kMaxTargetGroups * kSyncLineWords);
 static_assert(kSyncTicketWord < kSyncLineWords, "sync line too short");
 static_assert(kSyncBytes % 256 == 0, "sync area keeps the states aligned");
 
@@ -54,7 +57,8 @@ struct FwdOps {
   int C;              // chunk rows
   int slot_floats;    // floats per fp32 state slot
   bool decay_ok;      // the decayed variant fits in LDS too
-  // Enqueue the fused forward (cooperative launch when nseg > 1).
+  int occ;            // workgroups per compute unit the kernels are built for
+  // Enqueue the fused forward.
   hipError_t (*run)(const FwdArgs &args, int64_t units, int causal,
                     hipStream_t stream);
 };
