@@ -127,11 +127,12 @@ struct FwdShape {
   static_assert(OCC * kCUs <= kMaxTargetGroups, "sync area too small");
   static constexpr int WAVES_PER_SIMD = OCC * kWaves / 4;
   // register-ring depths (chunks of loads in flight per workgroup)
-  static constexpr int RING = OCC == 2 ? 24 : 64;   // VGPRs for the ring
+  static constexpr int RING = OCC == 2 ? 24 : 64;   // VGPRs, phase-2 ring
+  static constexpr int RING1 = OCC == 2 ? 32 : 64;  // VGPRs, phase-1 ring
   static constexpr int REG2 = 4 * (Slab<T, DF, C>::PER * 2 + Slab<T, D, C>::PER);
   static constexpr int REG1 = 4 * (Slab<T, DF, C>::PER + Slab<T, D, C>::PER);
   static constexpr int NB2 = REG2 >= RING ? 1 : (RING / REG2 > 4 ? 4 : RING / REG2);
-  static constexpr int NB1 = REG1 >= RING ? 1 : (RING / REG1 > 6 ? 6 : RING / REG1);
+  static constexpr int NB1 = REG1 >= RING1 ? 1 : (RING1 / REG1 > 6 ? 6 : RING1 / REG1);
   static constexpr bool fits = lds_bytes <= kMaxLds;
 };
 
@@ -281,28 +282,47 @@ __device__ __forceinline__ void publish_state(const f32x4 *S, T *sST, int w,
 
 // Exchange of segment aggregates between the workgroups of one (batch, head)
 // unit, through that unit's line of the synchronisation area (see
-// la_internal.h).  Publishing: the aggregate is written, every wave waits for
-// its stores, the workgroup releases them, then flag s is set.  Waiting: one
-// wave polls the flags it needs with relaxed loads (16 lanes, one line) and
-// acquires once all are set.  Every workgroup a wait depends on is running
-// (causal: segment indices follow start order; non-causal: cooperative
-// launch).  The wait is bounded (a few seconds): if the area were ever
-// corrupt it sets the timeout word and lets the kernel finish instead of
-// hanging.  Every workgroup then counts itself done; the last one clears the
-// unit's line (flags, ticket, count), so the area is zero again for the next
-// launch (no workgroup touches the line after counting itself done).
+// la_internal.h).  Aggregates are written and read with agent-scope atomic
+// 64-bit accesses, which are coherent across the XCDs' L2 caches by
+// themselves, so the exchange needs no cache write-back or invalidation.
+// Publishing: every wave waits until its aggregate stores have completed,
+// then flag s is set.  Waiting: one wave polls the flags it needs (16 lanes,
+// one line); the aggregates are read after every flag was seen set.  Every
+// workgroup a wait depends on is running (causal: segment indices follow
+// start order; non-causal: cooperative launch).  The wait is bounded (a few
+// seconds): if the area were ever corrupt it sets the timeout word and lets
+// the kernel finish instead of hanging.  At its very end every workgroup
+// counts itself done; the last one clears the unit's line (flags, ticket,
+// count), so the area is zero again for the next launch.
+__device__ __forceinline__ void store_agent(float *p, const f32x4 &v) {
+  typedef unsigned long long u64;
+  __hip_atomic_store(reinterpret_cast<u64 *>(p),
+                     __builtin_bit_cast(u64, __builtin_shufflevector(v, v, 0, 1)),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(reinterpret_cast<u64 *>(p) + 1,
+                     __builtin_bit_cast(u64, __builtin_shufflevector(v, v, 2, 3)),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ f32x4 load_agent(const float *p) {
+  typedef unsigned long long u64;
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const u64 lo = __hip_atomic_load(reinterpret_cast<const u64 *>(p),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const u64 hi = __hip_atomic_load(reinterpret_cast<const u64 *>(p) + 1,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const f32x2 a = __builtin_bit_cast(f32x2, lo), b = __builtin_bit_cast(f32x2, hi);
+  return f32x4{a[0], a[1], b[0], b[1]};
+}
+
 __device__ __forceinline__ void publish_flag(unsigned *line, int seg) {
-  // Each wave waits until its own stores of the aggregate have completed: a
-  // workgroup barrier does not wait for them, and the release below (cache
-  // write-back, then a wait for the flag writer's own accesses) covers what
-  // has reached the cache.
+  // Each wave waits until its own aggregate stores have completed (a
+  // workgroup barrier does not wait for them); only then is the flag set.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  if (threadIdx.x == 0)
     __hip_atomic_store(line + seg, 1u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
-  }
 }
 
 // Flags [0, need) of the line all set; call from every thread.
@@ -325,7 +345,6 @@ __device__ __forceinline__ void wait_flags(unsigned *line, int need,
         break;
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
 }
@@ -444,6 +463,8 @@ void la_fwd_kernel(FwdArgs a) {
 
   if constexpr (MULTI) {
     // ---------------- phase 1: segment aggregate from K, V ----------------
+    // (not for the last causal segment: no other segment needs its aggregate)
+    if (!CAUSAL || seg + 1 < a.nseg) {
     Slab<T, DF, C> rk[NB1];
     Slab<T, D, C> rv[NB1];
 #pragma unroll
@@ -478,6 +499,7 @@ void la_fwd_kernel(FwdArgs a) {
         __syncthreads();
       }
     }
+    }
     // With one segment the aggregate is already the state every row needs
     // (non-causal total).  With several, segment s combines the aggregates
     // A_j of the segments before it (causal) or of all segments
@@ -496,14 +518,12 @@ void la_fwd_kernel(FwdArgs a) {
             const int jb = tile_jb<F>(w, mj);
             const int idx = tile_fb<F>(w, m) * F::NJA + jb;
             if (jb < F::NJA)
-              *reinterpret_cast<f32x4 *>(mine + (idx * 64 + lane) * 4) =
-                  S[m * F::JPW + mj];
+              store_agent(mine + (idx * 64 + lane) * 4, S[m * F::JPW + mj]);
           }
         publish_flag(line, seg);
       }
       ring2_first();
       if (need > 0) wait_flags(line, need, a.sync + kSyncTimeoutWord);
-      count_done(line, a.nseg);
 #pragma unroll
       for (int i = 0; i < TW; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int64_t epos = CAUSAL ? start : a.n;
@@ -523,8 +543,7 @@ void la_fwd_kernel(FwdArgs a) {
             for (int mj = 0; mj < F::JPW; ++mj) {
               const int jb = tile_jb<F>(w, mj);
               const int idx = tile_fb<F>(w, m) * F::NJA + min(jb, F::NJA - 1);
-              buf[u][m * F::JPW + mj] =
-                  *reinterpret_cast<const f32x4 *>(sj + (idx * 64 + lane) * 4);
+              buf[u][m * F::JPW + mj] = load_agent(sj + (idx * 64 + lane) * 4);
             }
         }
 #pragma unroll
@@ -664,6 +683,7 @@ void la_fwd_kernel(FwdArgs a) {
       }
     }
   }
+  if (MULTI && a.nseg > 1) count_done(line, a.nseg);
 }
 
 }  // namespace la
