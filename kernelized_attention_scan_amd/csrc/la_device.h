@@ -158,16 +158,51 @@ __device__ __forceinline__ void load_frag_tr44(Frag<T> &f, const T *base, int ld
   tr_rows4(f, 4, base, ld, k0 + 16 + 4 * g, n0, i);
 }
 
+// ---------------------------------------------------------------------------
+// Packed bf16 pairs: one 32-bit word holds elements 2i (low half) and 2i+1.
+// ---------------------------------------------------------------------------
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats rounded to nearest even and packed (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  const f32x2 f = {lo, hi};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
+}
+// The two bf16 halves of a packed word, widened exactly.
+__device__ __forceinline__ float bf16_lo(unsigned u) {
+  return __builtin_bit_cast(float, u << 16);
+}
+__device__ __forceinline__ float bf16_hi(unsigned u) {
+  return __builtin_bit_cast(float, u & 0xffff0000u);
+}
+
 // Split-assignment fragment from two stacked accumulator tiles (top: k = 0..15
 // of the block, bottom: k = 16..31), rounded to the operand type.
-template <typename T>
-__device__ __forceinline__ void frag_from_acc(Frag<T> &f, const f32x4 &top,
+__device__ __forceinline__ void frag_from_acc(Frag<bf16> &f, const f32x4 &top,
+                                              const f32x4 &bot) {
+  const u32x4 w = {pack_bf16x2(top[0], top[1]), pack_bf16x2(top[2], top[3]),
+                   pack_bf16x2(bot[0], bot[1]), pack_bf16x2(bot[2], bot[3])};
+  f.v = __builtin_bit_cast(bf16x8, w);
+}
+__device__ __forceinline__ void frag_from_acc(Frag<float> &f, const f32x4 &top,
                                               const f32x4 &bot) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    f.v[r] = from_f32<T>(top[r]);
-    f.v[4 + r] = from_f32<T>(bot[r]);
+    f.v[r] = top[r];
+    f.v[4 + r] = bot[r];
   }
+}
+
+// Zero the elements of a fragment whose bit pattern in m is clear: m holds,
+// per pair of elements (2i, 2i+1), 0xffff in the low and/or high half.
+__device__ __forceinline__ void frag_mask(Frag<bf16> &f, const u32x4 &m) {
+  f.v = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, f.v) & m);
+}
+__device__ __forceinline__ void frag_mask(Frag<float> &f, const u32x4 &m) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (((m[e / 2] >> (16 * (e % 2))) & 1u) == 0u) f.v[e] = 0.f;
 }
 
 // Store 4 consecutive values (one accumulator column slice) as type T.

@@ -158,36 +158,59 @@ struct Decay {
   }
 };
 
+// phi over one 16-byte piece of T values (elu + 1 in fp32 when ELU, else the
+// values themselves), times w when SCALE, rounded once to T.
+template <typename T, bool ELU, bool SCALE>
+__device__ __forceinline__ u32x4 phi_piece(const u32x4 &x, float w) {
+  if constexpr (!ELU && !SCALE) {
+    return x;
+  } else {
+    auto f = [&](float v) {
+      const float y = ELU ? elu_plus_one_fast(v) : v;
+      return SCALE ? y * w : y;
+    };
+    if constexpr (sizeof(T) == 2) {
+      u32x4 y;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        y[i] = pack_bf16x2(f(bf16_lo(x[i])), f(bf16_hi(x[i])));
+      return y;
+    } else {
+      // whole-vector reinterpretation (per-element bit casts of vector
+      // elements are not reliable with this compiler)
+      const f32x4 xf = __builtin_bit_cast(f32x4, x);
+      const f32x4 yf = {f(xf[0]), f(xf[1]), f(xf[2]), f(xf[3])};
+      return __builtin_bit_cast(u32x4, yf);
+    }
+  }
+}
+
 // phi(Q) rows -> sQ (row-major).  Rows past the end are staged unmasked: they
 // only reach outputs that are never stored.
-template <typename T, int W, int C, int L>
+template <typename T, int W, int C, int L, bool ELU>
 __device__ __forceinline__ void stage_queries(const Slab<T, W, C> &sl, T *dst,
-                                              int tid, int elu1) {
+                                              int tid) {
   using S = Slab<T, W, C>;
 #pragma unroll
   for (int i = 0; i < S::PER; ++i) {
     const int p = tid + kThreads * i;
     if (S::EXACT || p < S::PIECES) {
       const int row = p / S::PPR, col = (p % S::PPR) * S::VEC;
-      Vec16<T> x, y;
-      x.raw = sl.v[i];
-#pragma unroll
-      for (int e = 0; e < S::VEC; ++e) {
-        const float xv = to_f32(x.e[e]);
-        y.e[e] = from_f32<T>(elu1 ? elu_plus_one_fast(xv) : xv);
-      }
-      *reinterpret_cast<u32x4 *>(dst + row * L + col) = y.raw;
+      *reinterpret_cast<u32x4 *>(dst + row * L + col) =
+          phi_piece<T, ELU, false>(sl.v[i], 1.f);
     }
   }
 }
 
-// phi(K) rows -> sK (row-major, when PLAIN), zero past the end; the keys the
-// state update uses go to sKw: w_s phi(k_s) with w_s = b g^(rows-1-s) under
-// decay (sKw is then its own tile), else sKw aliases sK.
-template <typename T, int W, int C, int L, bool DECAY, bool PLAIN>
+// phi(K) rows -> sK (row-major, when PLAIN), zero past the end (a bit mask on
+// the packed result, no branch); the keys the state update uses go to sKw:
+// w_s phi(k_s) with w_s = b g^(rows-1-s) under decay (sKw is then its own
+// tile), else sKw aliases sK.  Tail rows hold a copy of a valid row, so every
+// masked value is finite.
+template <typename T, int W, int C, int L, bool DECAY, bool PLAIN, bool ELU>
 __device__ __forceinline__ void stage_keys(const Slab<T, W, C> &sl, T *sK,
                                            T *sKw, const float *gp, float b,
-                                           int rows, int tid, int elu1) {
+                                           int rows, int tid) {
   using S = Slab<T, W, C>;
 #pragma unroll
   for (int i = 0; i < S::PER; ++i) {
@@ -195,21 +218,18 @@ __device__ __forceinline__ void stage_keys(const Slab<T, W, C> &sl, T *sK,
     if (S::EXACT || p < S::PIECES) {
       const int row = p / S::PPR, col = (p % S::PPR) * S::VEC;
       const bool valid = row < rows;
-      const float w = DECAY ? b * gp[valid ? rows - 1 - row : 0] : 1.f;
-      Vec16<T> x, y, yw;
-      x.raw = sl.v[i];
-#pragma unroll
-      for (int e = 0; e < S::VEC; ++e) {
-        const float xv = to_f32(x.e[e]);
-        const float f = valid ? (elu1 ? elu_plus_one_fast(xv) : xv) : 0.f;
-        y.e[e] = from_f32<T>(f);
-        if (DECAY) yw.e[e] = from_f32<T>(f * w);
-      }
+      const unsigned m = valid ? ~0u : 0u;
+      const u32x4 mm = {m, m, m, m};
       if (DECAY) {
-        if (PLAIN) *reinterpret_cast<u32x4 *>(sK + row * L + col) = y.raw;
-        *reinterpret_cast<u32x4 *>(sKw + row * L + col) = yw.raw;
+        const float w = b * gp[valid ? rows - 1 - row : 0];
+        if (PLAIN)
+          *reinterpret_cast<u32x4 *>(sK + row * L + col) =
+              phi_piece<T, ELU, false>(sl.v[i], 1.f) & mm;
+        *reinterpret_cast<u32x4 *>(sKw + row * L + col) =
+            phi_piece<T, ELU, true>(sl.v[i], w) & mm;
       } else {
-        *reinterpret_cast<u32x4 *>(sK + row * L + col) = y.raw;
+        *reinterpret_cast<u32x4 *>(sK + row * L + col) =
+            phi_piece<T, ELU, false>(sl.v[i], 1.f) & mm;
       }
     }
   }
@@ -364,7 +384,8 @@ __device__ __forceinline__ void count_done(unsigned *line, int nseg) {
   }
 }
 
-template <typename T, int D, int DF, bool CAUSAL, bool MULTI, bool DECAY>
+template <typename T, int D, int DF, bool CAUSAL, bool MULTI, bool DECAY,
+          bool ELU>
 __global__ __launch_bounds__(kThreads,
                              (FwdShape<T, D, DF, DECAY>::WAVES_PER_SIMD))
 void la_fwd_kernel(FwdArgs a) {
@@ -484,8 +505,8 @@ void la_fwd_kernel(FwdArgs a) {
         const int64_t r0 = start + c * C;
         const int rows =
             c < nch ? static_cast<int>(min<int64_t>(C, end - r0)) : 0;
-        stage_keys<T, DF, C, LQ, DECAY, false>(rk[b], sK, sKw, gp, dk.b, rows,
-                                               tid, a.elu1);
+        stage_keys<T, DF, C, LQ, DECAY, false, ELU>(rk[b], sK, sKw, gp, dk.b,
+                                                    rows, tid);
         stage_values<T, D, C, LV>(rv[b], sV, tid);
         __syncthreads();
         {
@@ -573,6 +594,18 @@ void la_fwd_kernel(FwdArgs a) {
   const int jh = w / STRIPS;    // and its share of the column blocks
   const int t = 16 * tb + li;   // the output row this lane normalises
   const float gt = CAUSAL ? gp[t + 1] : 1.f;
+  // Causal mask of the P^T fragment pair that holds the diagonal strip
+  // (pair kd = tb / 2): element e is key s = 16 (2 kd + e / 4) + 4 g + e % 4,
+  // kept when s <= t.  Pairs below it need no mask, pairs above are never
+  // used.
+  u32x4 dmask = {0u, 0u, 0u, 0u};
+  if (CAUSAL && !DECAY) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int s = 16 * (2 * (tb >> 1) + e / 4) + 4 * g + e % 4;
+      if (s <= t) dmask[e / 2] |= 0xffffu << (16 * (e % 2));
+    }
+  }
   const int nch2 = (nch + NB2 - 1) / NB2 * NB2;
   for (int c0 = 0; c0 < nch2; c0 += NB2) {
 #pragma unroll
@@ -582,10 +615,10 @@ void la_fwd_kernel(FwdArgs a) {
       const int rows =
           c < nch ? static_cast<int>(min<int64_t>(C, end - row0)) : 0;
       const bool last = c + 1 >= nch;
-      stage_queries<T, DF, C, LQ>(rq[b], sQ, tid, a.elu1);
+      stage_queries<T, DF, C, LQ, ELU>(rq[b], sQ, tid);
       if (CAUSAL) {
-        stage_keys<T, DF, C, LQ, DECAY, true>(rk2[b], sK, sKw, gp, dk.b, rows,
-                                              tid, a.elu1);
+        stage_keys<T, DF, C, LQ, DECAY, true, ELU>(rk2[b], sK, sKw, gp, dk.b,
+                                                   rows, tid);
         stage_values<T, D, C, LV>(rv2[b], sV, tid);
       }
       __syncthreads();  // operand tiles ready
@@ -617,12 +650,15 @@ void la_fwd_kernel(FwdArgs a) {
             load_frag8(fa, sK + (16 * sb + li) * LQ + 32 * kq + 8 * g);
             acc = mma(fa, qf[kq], acc);
           }
-          // acc[rr] = q'_t . k'_s with s = 16 sb + 4 g + rr
+          // acc[rr] = q'_t . k'_s with s = 16 sb + 4 g + rr; with decay the
+          // weights b g^(t-s), zero above the diagonal, are applied here,
+          // without it the diagonal is masked on the packed fragment below
+          if (DECAY) {
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const int s = 16 * sb + 4 * g + rr;
-            if (DECAY) acc[rr] = s <= t ? acc[rr] * (dk.b * gp[t - s]) : 0.f;
-            else if (sb == tb) acc[rr] = s <= t ? acc[rr] : 0.f;
+            for (int rr = 0; rr < 4; ++rr) {
+              const int s = 16 * sb + 4 * g + rr;
+              acc[rr] = s <= t ? acc[rr] * (dk.b * gp[t - s]) : 0.f;
+            }
           }
           pt[sb] = acc;
         }
@@ -630,10 +666,12 @@ void la_fwd_kernel(FwdArgs a) {
       constexpr int NPK = (STRIPS + 1) / 2;
       Frag<T> pf[NPK];
 #pragma unroll
-      for (int kp = 0; kp < NPK; ++kp)
+      for (int kp = 0; kp < NPK; ++kp) {
         frag_from_acc(pf[kp], pt[2 * kp],
                       2 * kp + 1 < STRIPS ? pt[2 * kp + 1]
                                           : f32x4{0.f, 0.f, 0.f, 0.f});
+        if (CAUSAL && !DECAY && kp == (tb >> 1)) frag_mask(pf[kp], dmask);
+      }
       // Column block jb of num^T = V^T P^T + g^(t+1) S^T Q'^T.  Block NJ is
       // the ones block: its first row is the denominator, sum_s P[t][s] +
       // g^(t+1) q'_t . z, from the same rounded P and the same S copy as the

@@ -7,16 +7,18 @@
 
 namespace la {
 
-template <typename T, int D, int DF, bool DECAY>
+// One (storage type, d, d_feat, decay, map) instance: ELU applies elu + 1 to
+// q and k while staging them, else they are features already.
+template <typename T, int D, int DF, bool DECAY, bool ELU>
 struct FwdVariant {
   using F = FwdShape<T, D, DF, DECAY>;
 
   static const void *kernel(bool causal, bool multi) {
     if (causal)
       return multi
-          ? reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, true, true, DECAY>)
-          : reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, true, false, DECAY>);
-    return reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, false, true, DECAY>);
+          ? reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, true, true, DECAY, ELU>)
+          : reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, true, false, DECAY, ELU>);
+    return reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, false, true, DECAY, ELU>);
   }
 
   // Raise the dynamic-LDS limit of every instance once (above 64 KiB).
@@ -79,16 +81,16 @@ struct FwdVariant {
       // One segment: no exchange.  Several: segments are numbered in start
       // order, so a plain launch cannot deadlock.
       if (a.nseg == 1)
-        hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, true, false, DECAY>), grid,
-                           block, F::lds_bytes, s, a);
+        hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, true, false, DECAY, ELU>),
+                           grid, block, F::lds_bytes, s, a);
       else
-        hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, true, true, DECAY>), grid,
-                           block, F::lds_bytes, s, a);
+        hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, true, true, DECAY, ELU>),
+                           grid, block, F::lds_bytes, s, a);
       return hipGetLastError();
     }
     if (a.nseg == 1) {  // non-causal, one segment: no exchange executes
-      hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, false, true, DECAY>), grid,
-                         block, F::lds_bytes, s, a);
+      hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, false, true, DECAY, ELU>),
+                         grid, block, F::lds_bytes, s, a);
       return hipGetLastError();
     }
     void *params[] = {&a};
@@ -102,15 +104,28 @@ struct FwdRunner {
   using P = FwdShape<T, D, DF, false>;
   using Q = FwdShape<T, D, DF, true>;
 
-  static hipError_t run(const FwdArgs &a, int64_t units, int causal,
-                        hipStream_t s) {
+  template <bool ELU>
+  static hipError_t run_map(const FwdArgs &a, int64_t units, int causal,
+                            hipStream_t s) {
     if (a.decay) {
       if constexpr (Q::fits)
-        return FwdVariant<T, D, DF, true>::run(a, units, causal, s);
+        return FwdVariant<T, D, DF, true, ELU>::run(a, units, causal, s);
       else
         return hipErrorInvalidValue;
     }
-    return FwdVariant<T, D, DF, false>::run(a, units, causal, s);
+    return FwdVariant<T, D, DF, false, ELU>::run(a, units, causal, s);
+  }
+
+  // elu + 1 instances exist only for d_feat == d (the map keeps the width).
+  static hipError_t run(const FwdArgs &a, int64_t units, int causal,
+                        hipStream_t s) {
+    if (a.elu1) {
+      if constexpr (D == DF)
+        return run_map<true>(a, units, causal, s);
+      else
+        return hipErrorInvalidValue;
+    }
+    return run_map<false>(a, units, causal, s);
   }
 
   static const FwdOps *ops() {
