@@ -606,6 +606,20 @@ void la_fwd_kernel(FwdArgs a) {
       if (s <= t) dmask[e / 2] |= 0xffffu << (16 * (e % 2));
     }
   }
+  // Decay weights of this lane's P^T elements, b g^(t-s) for key
+  // s = 16 sb + 4 g + rr (zero above the diagonal), computed once where the
+  // registers allow (one workgroup per CU); else per chunk from the table.
+  constexpr bool PREW = DECAY && F::OCC == 1;
+  float dw[PREW ? 4 * STRIPS : 1];
+  if constexpr (PREW) {
+#pragma unroll
+    for (int sb = 0; sb < STRIPS; ++sb)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int s = 16 * sb + 4 * g + rr;
+        dw[4 * sb + rr] = s <= t ? dk.b * gp[t - s] : 0.f;
+      }
+  }
   const int nch2 = (nch + NB2 - 1) / NB2 * NB2;
   for (int c0 = 0; c0 < nch2; c0 += NB2) {
 #pragma unroll
@@ -657,7 +671,8 @@ void la_fwd_kernel(FwdArgs a) {
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
               const int s = 16 * sb + 4 * g + rr;
-              acc[rr] = s <= t ? acc[rr] * (dk.b * gp[t - s]) : 0.f;
+              if (PREW) acc[rr] *= dw[4 * sb + rr];
+              else acc[rr] = s <= t ? acc[rr] * (dk.b * gp[t - s]) : 0.f;
             }
           }
           pt[sb] = acc;
