@@ -205,9 +205,15 @@ def prefill_leg(torch, K, I, cfg, args, dev):
     t_wall = time.perf_counter() - t_wall
 
     esz = esize(cfg.dtype)
-    if cfg.mapk != 2:
-        # one kernel per step: the chunked forward
-        kern = {"kernel": "la_fwd_kernel (chunked causal forward)",
+    # the library fuses the Performer map into the forward when it can (then
+    # no q', k' features go through the workspace)
+    fused = cfg.mapk == 2 and K.forward_workspace_bytes(
+        cfg.B, cfg.H, cfg.n, cfg.d, cfg.m, "performer", cfg.dtype,
+        cfg.causal) < 2 * cfg.tokens * cfg.m * esz
+    if cfg.mapk != 2 or fused:
+        # one kernel per step: the chunked forward (Performer: map fused)
+        kern = {"kernel": "la_fwd_kernel (chunked causal forward"
+                          + (", Performer map fused)" if fused else ")"),
                 "ms": ms, "bytes": byts, "flops": flops}
     else:
         # Performer: the same two kinds of launch la_forward makes, timed

@@ -60,7 +60,8 @@ struct FwdPlan {
   int64_t seg_len = 0;
   int nseg = 0;
   bool need_states = false;
-  size_t feat_bytes = 0;    // one of Q', K' (PERFORMER only)
+  bool fused_performer = false;  // Performer map applied inside the forward
+  size_t feat_bytes = 0;    // one of Q', K' (unfused PERFORMER only)
   size_t sync_bytes = 0;    // synchronisation area
   size_t state_bytes = 0;   // synchronisation area + segment aggregates
   size_t total() const { return state_bytes + 2 * feat_bytes; }
@@ -82,7 +83,18 @@ la_status plan_forward(int B, int H, int64_t n, int d, int d_feat, int map,
     return fail(LA_ERR_INVALID_ARG, "ELU1 needs d_feat == d (got %d, %d)", d_feat, d);
   if (!supported_d(d) || !supported_feat(d_feat))
     return fail(LA_ERR_UNSUPPORTED, "unsupported d=%d d_feat=%d", d, d_feat);
-  p->ops = dtype == LA_BF16 ? la::fwd_ops_bf16(d, d_feat) : la::fwd_ops_f32(d, d_feat);
+  // The Performer map is fused into the forward where an instance is built
+  // for these sizes (with its decayed variant, so the workspace does not
+  // depend on decay); otherwise q', k' go through the workspace.
+  if (map == LA_MAP_PERFORMER && dtype == LA_BF16) {
+    const la::FwdOps *pf = la::fwd_ops_bf16_performer(d, d_feat);
+    if (pf && pf->decay_ok) {
+      p->ops = pf;
+      p->fused_performer = true;
+    }
+  }
+  if (!p->fused_performer)
+    p->ops = dtype == LA_BF16 ? la::fwd_ops_bf16(d, d_feat) : la::fwd_ops_f32(d, d_feat);
   if (!p->ops || (decay && !p->ops->decay_ok))
     return fail(LA_ERR_UNSUPPORTED, "no %s%s kernel for d=%d d_feat=%d (LDS)",
                 dtype == LA_BF16 ? "bf16" : "fp32", decay ? " decayed" : "", d,
@@ -114,7 +126,7 @@ la_status plan_forward(int B, int H, int64_t n, int d, int d_feat, int map,
                              align256(static_cast<size_t>(units) * p->nseg *
                                       p->ops->slot_floats * sizeof(float))
                        : 0;
-  p->feat_bytes = map == LA_MAP_PERFORMER
+  p->feat_bytes = map == LA_MAP_PERFORMER && !p->fused_performer
                       ? align256(static_cast<size_t>(units * n) * d_feat *
                                  elem_size(dtype))
                       : 0;
@@ -207,7 +219,7 @@ la_status la_forward(const void *q, const void *k, const void *v, void *out,
     hipStream_t s = static_cast<hipStream_t>(stream);
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     const void *qf = q, *kf = k;
-    if (map == LA_MAP_PERFORMER) {
+    if (map == LA_MAP_PERFORMER && !p.fused_performer) {
       // Q', K' into the workspace, then the identity-map forward over them.
       unsigned char *fq = ws + p.state_bytes, *fk = fq + p.feat_bytes;
       hipError_t e = la::launch_featmap_performer(q, fq, omega, units * n, d,
@@ -233,6 +245,7 @@ la_status la_forward(const void *q, const void *k, const void *v, void *out,
     a.seg_len = p.seg_len;
     a.nseg = p.nseg;
     a.elu1 = map == LA_MAP_ELU1;
+    a.omega = p.fused_performer ? omega : nullptr;
     const hipError_t e = p.ops->run(a, units, causal, s);
     if (e != hipSuccess) return hip_fail(e, "la_forward launch");
     return ok();

@@ -98,14 +98,38 @@ constexpr int lds_stride(int w) {
   return sizeof(T) == 2 ? (w % 32 == 16 ? w : w + 16) : w + 4;
 }
 
-template <typename T, int D, int DF, bool DECAY>
+// Feature map an instance applies to q and k while staging them.
+constexpr int kMapFeatures = 0;   // q, k are features already
+constexpr int kMapElu = 1;        // elu + 1 (d' = d)
+constexpr int kMapPerformer = 2;  // Performer random features, fused
+
+// LDS bytes of one instance with chunk length c (see FwdShape).
+template <typename T>
+constexpr size_t fwd_lds_bytes(int c, int d, int df, bool decay, bool pf) {
+  const int dfp = df < 32 ? 32 : df;
+  const size_t sq = static_cast<size_t>(c) * lds_stride<T>(dfp);
+  const size_t sv = static_cast<size_t>(c) * lds_stride<T>(d + 16);
+  const size_t sst = static_cast<size_t>(d + 16) * lds_stride<T>(dfp);
+  const size_t sx = pf ? static_cast<size_t>(c) * lds_stride<T>(d) : 0;
+  const size_t sw = pf ? static_cast<size_t>(df) * lds_stride<T>(d) : 0;
+  return sizeof(T) * (2 * sq + (decay ? sq : 0) + sv + sst + 2 * sx + sw) +
+         sizeof(float) * (c + 2);
+}
+
+template <typename T, int D, int DF, bool DECAY, int MAP = kMapFeatures>
 struct FwdShape {
+  static constexpr bool PF = MAP == kMapPerformer;
+  static constexpr int DV = D;                       // value width d
+  // width of the q, k rows in memory: d for the fused Performer map
+  static constexpr int QW = PF ? D : DF;
   // Chunk rows: 64 for bf16 operands; 32 where LDS would not hold 64.
   static constexpr int C =
-      (sizeof(T) == 2 && !(DF == 256 && D == 128)) ? 64 : 32;
+      PF ? (fwd_lds_bytes<T>(64, D, DF, DECAY, true) <= kMaxLds ? 64 : 32)
+         : ((sizeof(T) == 2 && !(DF == 256 && D == 128)) ? 64 : 32);
   static constexpr int DFP = DF < 32 ? 32 : DF;      // padded k-width of q', k'
   static constexpr int LQ = lds_stride<T>(DFP);      // sQ, sK, sKw, sST
   static constexpr int LV = lds_stride<T>(D + 16);   // sV: V | ones block
+  static constexpr int LX = lds_stride<T>(D);        // raw q, k; omega^T
   static constexpr int STRIPS = C / 16;
   static constexpr int WPS = kWaves / STRIPS;        // waves per output strip
   static constexpr int NJ = D / 16, NF = DF / 16;
@@ -116,24 +140,29 @@ struct FwdShape {
   static constexpr int WPF = NF >= kWaves ? 1 : kWaves / NF;
   static constexpr int JPW = (NJA + WPF - 1) / WPF;
   static constexpr int SQ = C * LQ, SKW = DECAY ? C * LQ : 0, SV = C * LV,
-                       SST = (D + 16) * LQ;
-  static constexpr size_t lds_bytes =
-      sizeof(T) * (2 * SQ + SKW + SV + SST) + sizeof(float) * (C + 2);
+                       SST = (D + 16) * LQ, SX = PF ? C * LX : 0,
+                       SW = PF ? DF * LX : 0;
+  static constexpr size_t lds_bytes = fwd_lds_bytes<T>(C, D, DF, DECAY, PF);
   // fp32 state slot: NTILE tiles x 64 lanes x 4 (accumulator order).
   static constexpr int SLOT = NTILE * 256;
   // Workgroups per compute unit the instance is built for: two for the small
   // bf16 shapes (<= 128 VGPRs, 4 waves per SIMD), else one.
-  static constexpr int OCC = (sizeof(T) == 2 && D <= 64 && DF <= 64) ? 2 : 1;
+  static constexpr int OCC =
+      (!PF && sizeof(T) == 2 && D <= 64 && DF <= 64) ? 2 : 1;
   static_assert(OCC * kCUs <= kMaxTargetGroups, "sync area too small");
   static constexpr int WAVES_PER_SIMD = OCC * kWaves / 4;
   // register-ring depths (chunks of loads in flight per workgroup)
   static constexpr int RING = OCC == 2 ? 24 : 64;   // VGPRs, phase-2 ring
   static constexpr int RING1 = OCC == 2 ? 32 : 64;  // VGPRs, phase-1 ring
-  static constexpr int REG2 = 4 * (Slab<T, DF, C>::PER * 2 + Slab<T, D, C>::PER);
-  static constexpr int REG1 = 4 * (Slab<T, DF, C>::PER + Slab<T, D, C>::PER);
+  static constexpr int REG2 = 4 * (Slab<T, QW, C>::PER * 2 + Slab<T, D, C>::PER);
+  static constexpr int REG1 = 4 * (Slab<T, QW, C>::PER + Slab<T, D, C>::PER);
   static constexpr int NB2 = REG2 >= RING ? 1 : (RING / REG2 > 4 ? 4 : RING / REG2);
   static constexpr int NB1 = REG1 >= RING1 ? 1 : (RING1 / REG1 > 6 ? 6 : RING1 / REG1);
-  static constexpr bool fits = lds_bytes <= kMaxLds;
+  // the fused Performer map needs bf16 operands, d a multiple of 32 (the
+  // projection's k-width) and at least 32 features
+  static constexpr bool fits =
+      lds_bytes <= kMaxLds &&
+      (!PF || (sizeof(T) == 2 && D % 32 == 0 && DF >= 32));
 };
 
 // State tile ownership: wave w holds tiles (fb, jb) with
@@ -246,6 +275,65 @@ __device__ __forceinline__ void stage_values(const Slab<T, W, C> &sl, T *sV,
     if (S::EXACT || p < S::PIECES) {
       const int row = p / S::PPR, col = (p % S::PPR) * S::VEC;
       *reinterpret_cast<u32x4 *>(sV + row * L + col) = sl.v[i];
+    }
+  }
+}
+
+// Performer features of the rows of one chunk, fused ("Linear attention
+// research 2026" page, Performer random features: phi(x) = exp(x omega -
+// |x|^2 / 2) / sqrt(m)).  u^T = omega^T X^T runs on the matrix cores: A =
+// rows of omega^T (bf16, LDS), B = the raw q or k rows (LDS), contraction
+// over d.  Wave w takes strip ts = w % STRIPS (16 rows) and the feature tiles
+// fb = w / STRIPS + WPS m; its accumulator then holds features
+// 16 fb + 4 g .. +3 of row 16 ts + li, so the map is applied in registers
+// (exp2 of u log2 e minus the row's |x|^2 log2 e / 2 and log2 sqrt(m)) and
+// stored as 4 consecutive values.  |x|^2 is summed in fp32 from the stored
+// inputs.  KEYS: rows >= rows are zero; under decay the weighted copy
+// w_s phi(k_s), w_s = b g^(rows-1-s), goes to dstw (and the plain one to dst
+// when PLAIN).
+template <typename F, typename T, bool KEYS, bool DECAY, bool PLAIN>
+__device__ __forceinline__ void performer_features(
+    const T *sX, const T *sW, T *dst, T *dstw, const float *gp, float b,
+    int rows, int w, int g, int li) {
+  constexpr int KB = F::DV / 32;  // k-blocks of the contraction over d
+  const int row = 16 * (w % F::STRIPS) + li;
+  Frag<T> xf[KB];
+  float nrm = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    load_frag8(xf[kb], sX + row * F::LX + 32 * kb + 8 * g);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = to_f32(xf[kb].v[e]);
+      nrm += v * v;
+    }
+  }
+  nrm = wave_sum_groups(nrm);
+  constexpr float kLog2e = 1.4426950408889634f;
+  // log2 of 1/sqrt(m) folded into the exponent
+  const float c0 = -0.5f * kLog2e * nrm - 0.5f * __builtin_log2f(F::NF * 16.f);
+  const bool valid = !KEYS || row < rows;
+  const float wr = (KEYS && DECAY) ? (valid ? b * gp[rows - 1 - row] : 0.f)
+                                   : 1.f;
+#pragma unroll
+  for (int m = 0; m < (F::NF + F::WPS - 1) / F::WPS; ++m) {
+    const int fb = w / F::STRIPS + F::WPS * m;
+    if (fb < F::NF) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        Frag<T> wf;
+        load_frag8(wf, sW + (16 * fb + li) * F::LX + 32 * kb + 8 * g);
+        acc = mma(wf, xf[kb], acc);
+      }
+      float ph[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        ph[r] = valid ? __builtin_amdgcn_exp2f(acc[r] * kLog2e + c0) : 0.f;
+      const int off = row * F::LQ + 16 * fb + 4 * g;
+      if (!(KEYS && DECAY) || PLAIN) store4(dst + off, ph[0], ph[1], ph[2], ph[3]);
+      if (KEYS && DECAY)
+        store4(dstw + off, ph[0] * wr, ph[1] * wr, ph[2] * wr, ph[3] * wr);
     }
   }
 }
@@ -385,11 +473,13 @@ __device__ __forceinline__ void count_done(unsigned *line, int nseg) {
 }
 
 template <typename T, int D, int DF, bool CAUSAL, bool MULTI, bool DECAY,
-          bool ELU>
+          int MAP>
 __global__ __launch_bounds__(kThreads,
-                             (FwdShape<T, D, DF, DECAY>::WAVES_PER_SIMD))
+                             (FwdShape<T, D, DF, DECAY, MAP>::WAVES_PER_SIMD))
 void la_fwd_kernel(FwdArgs a) {
-  using F = FwdShape<T, D, DF, DECAY>;
+  using F = FwdShape<T, D, DF, DECAY, MAP>;
+  constexpr bool ELU = MAP == kMapElu, PF = F::PF;
+  constexpr int QW = F::QW, LX = F::LX;
   constexpr int C = F::C, LQ = F::LQ, LV = F::LV, DFP = F::DFP;
   constexpr int STRIPS = F::STRIPS, NJ = F::NJ, WPS = F::WPS;
   constexpr int NB1 = F::NB1, NB2 = F::NB2, TW = F::FPW * F::JPW;
@@ -399,7 +489,10 @@ void la_fwd_kernel(FwdArgs a) {
   T *sKw = DECAY ? sK + F::SQ : sK;
   T *sV = sK + F::SQ + F::SKW;
   T *sST = sV + F::SV;
-  float *gp = reinterpret_cast<float *>(sST + F::SST);
+  T *sXq = sST + F::SST;          // raw q, k rows and omega^T (fused Performer)
+  T *sXk = sXq + F::SX;
+  T *sW = sXk + F::SX;
+  float *gp = reinterpret_cast<float *>(sW + F::SW);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -437,8 +530,8 @@ void la_fwd_kernel(FwdArgs a) {
   const Decay dk(a.decay, static_cast<int>(unit % a.H));
   for (int i = tid; i <= C; i += kThreads) gp[i] = pow_int(dk.g, dk.lg, i);
 
-  const T *qb = static_cast<const T *>(a.q) + unit * a.n * DF;
-  const T *kb = static_cast<const T *>(a.k) + unit * a.n * DF;
+  const T *qb = static_cast<const T *>(a.q) + unit * a.n * QW;
+  const T *kb = static_cast<const T *>(a.k) + unit * a.n * QW;
   const T *vb = static_cast<const T *>(a.v) + unit * a.n * D;
   T *ob = static_cast<T *>(a.out) + unit * a.n * D;
   const int64_t start = seg * a.seg_len;
@@ -450,6 +543,12 @@ void la_fwd_kernel(FwdArgs a) {
   // columns of q', k' and S^T.
   for (int i = tid; i < C * 16; i += kThreads)
     sV[(i / 16) * LV + D + i % 16] = from_f32<T>(i % 16 == 0 ? 1.f : 0.f);
+  // Fused Performer: omega^T [d_feat][d] rounded once to T (omega is read in
+  // its [d][d_feat] order, so consecutive threads read consecutive floats).
+  if constexpr (PF) {
+    for (int i = tid; i < DF * D; i += kThreads)
+      sW[(i % DF) * LX + i / DF] = from_f32<T>(a.omega[i]);
+  }
   if (DFP != DF) {
     for (int i = tid; i < C * (DFP - DF); i += kThreads) {
       const int row = i / (DFP - DF), col = DF + i % (DFP - DF);
@@ -466,7 +565,7 @@ void la_fwd_kernel(FwdArgs a) {
 
   // Phase-2 register ring, first revolution; in the segmented kernel these
   // loads are issued once the aggregate is published and overlap the wait.
-  Slab<T, DF, C> rq[NB2], rk2[NB2];
+  Slab<T, QW, C> rq[NB2], rk2[NB2];
   Slab<T, D, C> rv2[NB2];
   auto ring2_first = [&]() {
 #pragma unroll
@@ -486,7 +585,7 @@ void la_fwd_kernel(FwdArgs a) {
     // ---------------- phase 1: segment aggregate from K, V ----------------
     // (not for the last causal segment: no other segment needs its aggregate)
     if (!CAUSAL || seg + 1 < a.nseg) {
-    Slab<T, DF, C> rk[NB1];
+    Slab<T, QW, C> rk[NB1];
     Slab<T, D, C> rv[NB1];
 #pragma unroll
     for (int b = 0; b < NB1; ++b) {
@@ -505,8 +604,11 @@ void la_fwd_kernel(FwdArgs a) {
         const int64_t r0 = start + c * C;
         const int rows =
             c < nch ? static_cast<int>(min<int64_t>(C, end - r0)) : 0;
-        stage_keys<T, DF, C, LQ, DECAY, false, ELU>(rk[b], sK, sKw, gp, dk.b,
-                                                    rows, tid);
+        if constexpr (PF)
+          stage_values<T, D, C, LX>(rk[b], sXk, tid);
+        else
+          stage_keys<T, DF, C, LQ, DECAY, false, ELU>(rk[b], sK, sKw, gp, dk.b,
+                                                      rows, tid);
         stage_values<T, D, C, LV>(rv[b], sV, tid);
         __syncthreads();
         {
@@ -515,6 +617,11 @@ void la_fwd_kernel(FwdArgs a) {
           const int rows2 = static_cast<int>(min<int64_t>(C, end - r2));
           rk[b].load(kb, r2, rows2, tid);
           rv[b].load(vb, r2, rows2, tid);
+        }
+        if constexpr (PF) {
+          performer_features<F, T, true, DECAY, false>(sXk, sW, sK, sKw, gp,
+                                                       dk.b, rows, w, g, li);
+          __syncthreads();
         }
         state_update<F>(S, sKw, sV, DECAY ? gp[rows] : 1.f, w, g, li);
         __syncthreads();
@@ -629,13 +736,17 @@ void la_fwd_kernel(FwdArgs a) {
       const int rows =
           c < nch ? static_cast<int>(min<int64_t>(C, end - row0)) : 0;
       const bool last = c + 1 >= nch;
-      stage_queries<T, DF, C, LQ, ELU>(rq[b], sQ, tid);
-      if (CAUSAL) {
-        stage_keys<T, DF, C, LQ, DECAY, true, ELU>(rk2[b], sK, sKw, gp, dk.b,
-                                                   rows, tid);
-        stage_values<T, D, C, LV>(rv2[b], sV, tid);
+      if constexpr (PF) {
+        stage_values<T, D, C, LX>(rq[b], sXq, tid);
+        if (CAUSAL) stage_values<T, D, C, LX>(rk2[b], sXk, tid);
+      } else {
+        stage_queries<T, DF, C, LQ, ELU>(rq[b], sQ, tid);
+        if (CAUSAL)
+          stage_keys<T, DF, C, LQ, DECAY, true, ELU>(rk2[b], sK, sKw, gp, dk.b,
+                                                     rows, tid);
       }
-      __syncthreads();  // operand tiles ready
+      if (CAUSAL) stage_values<T, D, C, LV>(rv2[b], sV, tid);
+      __syncthreads();  // operand tiles (fused Performer: raw rows) ready
       {
         const int cn = c + NB2 < nch ? c + NB2 : nch - 1;
         const int64_t r2 = start + cn * C;
@@ -645,6 +756,14 @@ void la_fwd_kernel(FwdArgs a) {
           rk2[b].load(kb, r2, rows2, tid);
           rv2[b].load(vb, r2, rows2, tid);
         }
+      }
+      if constexpr (PF) {
+        performer_features<F, T, false, false, true>(sXq, sW, sQ, sQ, gp, dk.b,
+                                                     rows, w, g, li);
+        if (CAUSAL)
+          performer_features<F, T, true, DECAY, true>(sXk, sW, sK, sKw, gp,
+                                                      dk.b, rows, w, g, li);
+        __syncthreads();  // q', k' tiles ready
       }
 
       // ---- readout of strip tb: q' fragments, reused by every product ----

@@ -7,18 +7,18 @@
 
 namespace la {
 
-// One (storage type, d, d_feat, decay, map) instance: ELU applies elu + 1 to
-// q and k while staging them, else they are features already.
-template <typename T, int D, int DF, bool DECAY, bool ELU>
+// One (storage type, d, d_feat, decay, map) instance; MAP is the feature map
+// applied to q and k while staging them (kMapFeatures: none).
+template <typename T, int D, int DF, bool DECAY, int MAP>
 struct FwdVariant {
-  using F = FwdShape<T, D, DF, DECAY>;
+  using F = FwdShape<T, D, DF, DECAY, MAP>;
 
   static const void *kernel(bool causal, bool multi) {
     if (causal)
       return multi
-          ? reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, true, true, DECAY, ELU>)
-          : reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, true, false, DECAY, ELU>);
-    return reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, false, true, DECAY, ELU>);
+          ? reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, true, true, DECAY, MAP>)
+          : reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, true, false, DECAY, MAP>);
+    return reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, false, true, DECAY, MAP>);
   }
 
   // Raise the dynamic-LDS limit of every instance once (above 64 KiB).
@@ -81,15 +81,15 @@ struct FwdVariant {
       // One segment: no exchange.  Several: segments are numbered in start
       // order, so a plain launch cannot deadlock.
       if (a.nseg == 1)
-        hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, true, false, DECAY, ELU>),
+        hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, true, false, DECAY, MAP>),
                            grid, block, F::lds_bytes, s, a);
       else
-        hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, true, true, DECAY, ELU>),
+        hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, true, true, DECAY, MAP>),
                            grid, block, F::lds_bytes, s, a);
       return hipGetLastError();
     }
     if (a.nseg == 1) {  // non-causal, one segment: no exchange executes
-      hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, false, true, DECAY, ELU>),
+      hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, false, true, DECAY, MAP>),
                          grid, block, F::lds_bytes, s, a);
       return hipGetLastError();
     }
@@ -99,33 +99,40 @@ struct FwdVariant {
   }
 };
 
-template <typename T, int D, int DF>
+// Launch set of one (storage type, d, d_feat): PERF selects the instances
+// with the Performer map fused, else the ones for features or elu + 1.
+template <typename T, int D, int DF, bool PERF = false>
 struct FwdRunner {
-  using P = FwdShape<T, D, DF, false>;
-  using Q = FwdShape<T, D, DF, true>;
+  static constexpr int MAP0 = PERF ? kMapPerformer : kMapFeatures;
+  using P = FwdShape<T, D, DF, false, MAP0>;
+  using Q = FwdShape<T, D, DF, true, MAP0>;
 
-  template <bool ELU>
+  template <int MAP>
   static hipError_t run_map(const FwdArgs &a, int64_t units, int causal,
                             hipStream_t s) {
     if (a.decay) {
       if constexpr (Q::fits)
-        return FwdVariant<T, D, DF, true, ELU>::run(a, units, causal, s);
+        return FwdVariant<T, D, DF, true, MAP>::run(a, units, causal, s);
       else
         return hipErrorInvalidValue;
     }
-    return FwdVariant<T, D, DF, false, ELU>::run(a, units, causal, s);
+    return FwdVariant<T, D, DF, false, MAP>::run(a, units, causal, s);
   }
 
   // elu + 1 instances exist only for d_feat == d (the map keeps the width).
   static hipError_t run(const FwdArgs &a, int64_t units, int causal,
                         hipStream_t s) {
-    if (a.elu1) {
-      if constexpr (D == DF)
-        return run_map<true>(a, units, causal, s);
-      else
-        return hipErrorInvalidValue;
+    if constexpr (PERF) {
+      return run_map<kMapPerformer>(a, units, causal, s);
+    } else {
+      if (a.elu1) {
+        if constexpr (D == DF)
+          return run_map<kMapElu>(a, units, causal, s);
+        else
+          return hipErrorInvalidValue;
+      }
+      return run_map<kMapFeatures>(a, units, causal, s);
     }
-    return run_map<false>(a, units, causal, s);
   }
 
   static const FwdOps *ops() {
@@ -133,6 +140,9 @@ struct FwdRunner {
       return nullptr;
     } else {
       static_assert(P::OCC == Q::OCC, "one split for both variants");
+      // the split is planned with P's chunk length; segments must hold whole
+      // chunks of the decayed variant too
+      static_assert(!Q::fits || P::C % Q::C == 0, "chunk lengths compatible");
       static const FwdOps o = {P::C, P::SLOT, Q::fits, P::OCC, &run};
       return &o;
     }

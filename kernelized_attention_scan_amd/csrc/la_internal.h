@@ -50,6 +50,7 @@ struct FwdArgs {
   int64_t seg_len;      // multiple of the chunk length
   int nseg;
   int elu1;             // 1: phi = elu + 1 on q, k; 0: q, k are features
+  const float *omega;   // [d][d_feat] for the fused Performer map, else null
 };
 
 // Launch set of one (storage type, d, d_feat) instance of the chunked forward.
@@ -66,6 +67,10 @@ struct FwdOps {
 // nullptr when the combination is not built (unsupported size or LDS).
 const FwdOps *fwd_ops_bf16(int d, int d_feat);
 const FwdOps *fwd_ops_f32(int d, int d_feat);
+// The forward with the Performer map fused into it (q, k of width d are
+// mapped to d_feat random features on chip); bf16 storage only.  nullptr
+// when not built for these sizes.
+const FwdOps *fwd_ops_bf16_performer(int d, int d_feat);
 
 // Feature map launchers.  dtype codes: 0 fp32, 1 bf16.
 hipError_t launch_featmap_elementwise(const void *x, void *y, int64_t count,

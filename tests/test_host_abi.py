@@ -107,9 +107,15 @@ def test_workspace_bytes(lib):
     assert one == sync + a256(16 * slot * 4)
     # 512 units or more: one segment each, no workspace
     assert K.forward_workspace_bytes(8, 64, 1 << 16, 64, 64) == 0
-    # Performer adds Q' and K' (bf16, d_feat = m wide)
+    # bf16 Performer: the map is fused into the forward, so no q', k' in the
+    # workspace; one workgroup per CU -> 256 target groups / 32 units = 8
+    # segments, aggregates of d' x (d + 16) = 256 x 80
     wp = K.forward_workspace_bytes(4, 8, 8192, 64, 256, "performer")
-    assert wp >= 2 * 4 * 8 * 8192 * 256 * 2
+    assert wp == sync + a256(32 * 8 * 256 * 80 * 4)
+    # fp32 storage keeps the unfused map: Q', K' (fp32, m wide) in it
+    wf = K.forward_workspace_bytes(4, 8, 8192, 64, 256, "performer",
+                                   dtype=__import__("torch").float32)
+    assert wf >= 2 * 4 * 8 * 8192 * 256 * 4
     # non-causal over one segment keeps its total on chip; several need one
     assert K.forward_workspace_bytes(1, 1, 64, 64, 64, causal=False) == 0
     assert K.forward_workspace_bytes(1, 1, 4096, 64, 64, causal=False) > 0
