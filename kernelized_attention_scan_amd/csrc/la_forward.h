@@ -111,8 +111,7 @@ constexpr size_t fwd_lds_bytes(int c, int d, int df, bool decay, bool pf) {
   const size_t sv = static_cast<size_t>(c) * lds_stride<T>(d + 16);
   const size_t sst = static_cast<size_t>(d + 16) * lds_stride<T>(dfp);
   const size_t sx = pf ? static_cast<size_t>(c) * lds_stride<T>(d) : 0;
-  const size_t sw = pf ? static_cast<size_t>(df) * lds_stride<T>(d) : 0;
-  return sizeof(T) * (2 * sq + (decay ? sq : 0) + sv + sst + 2 * sx + sw) +
+  return sizeof(T) * (2 * sq + (decay ? sq : 0) + sv + sst + 2 * sx) +
          sizeof(float) * (c + 2);
 }
 
@@ -129,7 +128,7 @@ struct FwdShape {
   static constexpr int DFP = DF < 32 ? 32 : DF;      // padded k-width of q', k'
   static constexpr int LQ = lds_stride<T>(DFP);      // sQ, sK, sKw, sST
   static constexpr int LV = lds_stride<T>(D + 16);   // sV: V | ones block
-  static constexpr int LX = lds_stride<T>(D);        // raw q, k; omega^T
+  static constexpr int LX = lds_stride<T>(D);        // raw q, k rows
   static constexpr int STRIPS = C / 16;
   static constexpr int WPS = kWaves / STRIPS;        // waves per output strip
   static constexpr int NJ = D / 16, NF = DF / 16;
@@ -140,8 +139,14 @@ struct FwdShape {
   static constexpr int WPF = NF >= kWaves ? 1 : kWaves / NF;
   static constexpr int JPW = (NJA + WPF - 1) / WPF;
   static constexpr int SQ = C * LQ, SKW = DECAY ? C * LQ : 0, SV = C * LV,
-                       SST = (D + 16) * LQ, SX = PF ? C * LX : 0,
-                       SW = PF ? DF * LX : 0;
+                       SST = (D + 16) * LQ, SX = PF ? C * LX : 0;
+  // Fused Performer projection: omega^T tiles per wave (kept in registers
+  // for the whole kernel) and the strips each wave maps.  NF >= 8: wave w
+  // owns feature tiles w + 8 m for every strip; else tile w % NF for strips
+  // w / NF + WPT j (WPT waves per tile).
+  static constexpr int TPW = NF >= kWaves ? NF / kWaves : 1;
+  static constexpr int WPT = NF >= kWaves ? 1 : kWaves / NF;
+  static constexpr int SPW = (STRIPS + WPT - 1) / WPT;
   static constexpr size_t lds_bytes = fwd_lds_bytes<T>(C, D, DF, DECAY, PF);
   // fp32 state slot: NTILE tiles x 64 lanes x 4 (accumulator order).
   static constexpr int SLOT = NTILE * 256;
@@ -159,10 +164,11 @@ struct FwdShape {
   static constexpr int NB2 = REG2 >= RING ? 1 : (RING / REG2 > 4 ? 4 : RING / REG2);
   static constexpr int NB1 = REG1 >= RING1 ? 1 : (RING1 / REG1 > 6 ? 6 : RING1 / REG1);
   // the fused Performer map needs bf16 operands, d a multiple of 32 (the
-  // projection's k-width) and at least 32 features
+  // projection's k-width), at least 32 features, and d d' <= 128 * 128 (the
+  // register budget of one workgroup per CU; larger shapes spill)
   static constexpr bool fits =
       lds_bytes <= kMaxLds &&
-      (!PF || (sizeof(T) == 2 && D % 32 == 0 && DF >= 32));
+      (!PF || (sizeof(T) == 2 && D % 32 == 0 && DF >= 32 && D * DF <= 16384));
 };
 
 // State tile ownership: wave w holds tiles (fb, jb) with
@@ -282,58 +288,70 @@ __device__ __forceinline__ void stage_values(const Slab<T, W, C> &sl, T *sV,
 // Performer features of the rows of one chunk, fused ("Linear attention
 // research 2026" page, Performer random features: phi(x) = exp(x omega -
 // |x|^2 / 2) / sqrt(m)).  u^T = omega^T X^T runs on the matrix cores: A =
-// rows of omega^T (bf16, LDS), B = the raw q or k rows (LDS), contraction
-// over d.  Wave w takes strip ts = w % STRIPS (16 rows) and the feature tiles
-// fb = w / STRIPS + WPS m; its accumulator then holds features
-// 16 fb + 4 g .. +3 of row 16 ts + li, so the map is applied in registers
-// (exp2 of u log2 e minus the row's |x|^2 log2 e / 2 and log2 sqrt(m)) and
-// stored as 4 consecutive values.  |x|^2 is summed in fp32 from the stored
-// inputs.  KEYS: rows >= rows are zero; under decay the weighted copy
-// w_s phi(k_s), w_s = b g^(rows-1-s), goes to dstw (and the plain one to dst
-// when PLAIN).
-template <typename F, typename T, bool KEYS, bool DECAY, bool PLAIN>
+// this wave's omega^T tiles (registers, see FwdShape::TPW), B = the raw q or
+// k rows (LDS), contraction over d.  For each of its strips (16 rows) the
+// wave sums |x|^2 of the rows in fp32, then for each of its feature tiles fb
+// its accumulator holds features 16 fb + 4 g .. +3 of row 16 ts + li: the
+// map is applied in registers (exp2 of u log2 e minus |x|^2 log2 e / 2 and
+// log2 sqrt(m)) and stored as 4 consecutive values.  WQ maps the queries
+// into dq; WK maps the keys: rows >= rows are zero, and under decay the
+// weighted copy w_s phi(k_s), w_s = b g^(rows-1-s), goes to dkw (the plain
+// one to dk when PLAIN or without decay).
+template <typename F, typename T, bool WQ, bool WK, bool DECAY, bool PLAIN>
 __device__ __forceinline__ void performer_features(
-    const T *sX, const T *sW, T *dst, T *dstw, const float *gp, float b,
-    int rows, int w, int g, int li) {
+    const Frag<T> (&wf)[F::TPW][F::DV / 32], const T *sXq, const T *sXk,
+    T *dq, T *dk, T *dkw, const float *gp, float b, int rows, int w, int g,
+    int li) {
   constexpr int KB = F::DV / 32;  // k-blocks of the contraction over d
-  const int row = 16 * (w % F::STRIPS) + li;
-  Frag<T> xf[KB];
-  float nrm = 0.f;
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    load_frag8(xf[kb], sX + row * F::LX + 32 * kb + 8 * g);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float v = to_f32(xf[kb].v[e]);
-      nrm += v * v;
-    }
-  }
-  nrm = wave_sum_groups(nrm);
   constexpr float kLog2e = 1.4426950408889634f;
-  // log2 of 1/sqrt(m) folded into the exponent
-  const float c0 = -0.5f * kLog2e * nrm - 0.5f * __builtin_log2f(F::NF * 16.f);
-  const bool valid = !KEYS || row < rows;
-  const float wr = (KEYS && DECAY) ? (valid ? b * gp[rows - 1 - row] : 0.f)
-                                   : 1.f;
+  const float lsm = 0.5f * __builtin_log2f(F::NF * 16.f);  // log2 sqrt(m)
 #pragma unroll
-  for (int m = 0; m < (F::NF + F::WPS - 1) / F::WPS; ++m) {
-    const int fb = w / F::STRIPS + F::WPS * m;
-    if (fb < F::NF) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < F::SPW; ++j) {
+    const int ts = F::NF >= kWaves ? j : w / F::NF + F::WPT * j;
+    if (ts < F::STRIPS) {
+      const int row = 16 * ts + li;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        Frag<T> wf;
-        load_frag8(wf, sW + (16 * fb + li) * F::LX + 32 * kb + 8 * g);
-        acc = mma(wf, xf[kb], acc);
+      for (int mat = 0; mat < 2; ++mat) {
+        const bool keys = mat == 1;
+        if ((keys && WK) || (!keys && WQ)) {
+          Frag<T> xf[KB];
+          float nrm = 0.f;
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            load_frag8(xf[kb], (keys ? sXk : sXq) + row * F::LX + 32 * kb + 8 * g);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float v = to_f32(xf[kb].v[e]);
+              nrm += v * v;
+            }
+          }
+          nrm = wave_sum_groups(nrm);
+          const float c0 = -0.5f * kLog2e * nrm - lsm;
+          const bool valid = !keys || row < rows;
+          const float wr =
+              (keys && DECAY) ? (valid ? b * gp[rows - 1 - row] : 0.f) : 1.f;
+#pragma unroll
+          for (int m = 0; m < F::TPW; ++m) {
+            const int fb = F::NF >= kWaves ? w + kWaves * m : w % F::NF;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) acc = mma(wf[m][kb], xf[kb], acc);
+            float ph[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              ph[r] = valid ? __builtin_amdgcn_exp2f(acc[r] * kLog2e + c0) : 0.f;
+            const int off = row * F::LQ + 16 * fb + 4 * g;
+            if (!keys) {
+              store4(dq + off, ph[0], ph[1], ph[2], ph[3]);
+            } else {
+              if (!DECAY || PLAIN) store4(dk + off, ph[0], ph[1], ph[2], ph[3]);
+              if (DECAY)
+                store4(dkw + off, ph[0] * wr, ph[1] * wr, ph[2] * wr,
+                       ph[3] * wr);
+            }
+          }
+        }
       }
-      float ph[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        ph[r] = valid ? __builtin_amdgcn_exp2f(acc[r] * kLog2e + c0) : 0.f;
-      const int off = row * F::LQ + 16 * fb + 4 * g;
-      if (!(KEYS && DECAY) || PLAIN) store4(dst + off, ph[0], ph[1], ph[2], ph[3]);
-      if (KEYS && DECAY)
-        store4(dstw + off, ph[0] * wr, ph[1] * wr, ph[2] * wr, ph[3] * wr);
     }
   }
 }
@@ -489,10 +507,9 @@ void la_fwd_kernel(FwdArgs a) {
   T *sKw = DECAY ? sK + F::SQ : sK;
   T *sV = sK + F::SQ + F::SKW;
   T *sST = sV + F::SV;
-  T *sXq = sST + F::SST;          // raw q, k rows and omega^T (fused Performer)
+  T *sXq = sST + F::SST;          // raw q, k rows (fused Performer)
   T *sXk = sXq + F::SX;
-  T *sW = sXk + F::SX;
-  float *gp = reinterpret_cast<float *>(sW + F::SW);
+  float *gp = reinterpret_cast<float *>(sXk + F::SX);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -543,11 +560,22 @@ void la_fwd_kernel(FwdArgs a) {
   // columns of q', k' and S^T.
   for (int i = tid; i < C * 16; i += kThreads)
     sV[(i / 16) * LV + D + i % 16] = from_f32<T>(i % 16 == 0 ? 1.f : 0.f);
-  // Fused Performer: omega^T [d_feat][d] rounded once to T (omega is read in
-  // its [d][d_feat] order, so consecutive threads read consecutive floats).
+  // Fused Performer: this wave's omega^T tiles as A fragments, rounded once
+  // to T and kept in registers (lane: feature 16 fb + li, d values
+  // 32 kb + 8 g .. +7; for each d the 16 lanes read 16 consecutive floats of
+  // omega [d][d_feat]).
+  Frag<T> wf[PF ? F::TPW : 1][PF ? D / 32 : 1];
   if constexpr (PF) {
-    for (int i = tid; i < DF * D; i += kThreads)
-      sW[(i % DF) * LX + i / DF] = from_f32<T>(a.omega[i]);
+#pragma unroll
+    for (int m = 0; m < F::TPW; ++m) {
+      const int fb = F::NF >= kWaves ? w + kWaves * m : w % F::NF;
+#pragma unroll
+      for (int kb = 0; kb < D / 32; ++kb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          wf[m][kb].v[e] =
+              from_f32<T>(a.omega[(32 * kb + 8 * g + e) * DF + 16 * fb + li]);
+    }
   }
   if (DFP != DF) {
     for (int i = tid; i < C * (DFP - DF); i += kThreads) {
@@ -619,8 +647,8 @@ void la_fwd_kernel(FwdArgs a) {
           rv[b].load(vb, r2, rows2, tid);
         }
         if constexpr (PF) {
-          performer_features<F, T, true, DECAY, false>(sXk, sW, sK, sKw, gp,
-                                                       dk.b, rows, w, g, li);
+          performer_features<F, T, false, true, DECAY, false>(
+              wf, sXq, sXk, sQ, sK, sKw, gp, dk.b, rows, w, g, li);
           __syncthreads();
         }
         state_update<F>(S, sKw, sV, DECAY ? gp[rows] : 1.f, w, g, li);
@@ -758,11 +786,8 @@ void la_fwd_kernel(FwdArgs a) {
         }
       }
       if constexpr (PF) {
-        performer_features<F, T, false, false, true>(sXq, sW, sQ, sQ, gp, dk.b,
-                                                     rows, w, g, li);
-        if (CAUSAL)
-          performer_features<F, T, true, DECAY, true>(sXk, sW, sK, sKw, gp,
-                                                      dk.b, rows, w, g, li);
+        performer_features<F, T, true, CAUSAL, DECAY, true>(
+            wf, sXq, sXk, sQ, sK, sKw, gp, dk.b, rows, w, g, li);
         __syncthreads();  // q', k' tiles ready
       }
 
