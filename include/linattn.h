@@ -115,6 +115,26 @@ la_status la_forward(const void *q, const void *k, const void *v, void *out,
                      la_dtype dtype, void *workspace, void *stream);
 
 /*
+ * la_forward_state -- la_forward that also hands out the state after the
+ * last position of every unit, the sums the decode step continues from:
+ * mu_n = sum_j w_j k'_j^T v_j and nu_n = sum_j w_j k'_j ("2.2 Linear
+ * Attention" eqs 7-8, or eqs 10-11 with decay; "3.2 Reducing d", remark
+ * after eq 27: the two sums are kept and updated as tokens arrive).
+ *   All arguments as la_forward, plus:
+ *   mu_out : device fp32 [B][H][d_feat][d], written (the decode step's mu)
+ *   nu_out : device fp32 [B][H][d_feat], written (the decode step's nu)
+ *   Both required (LA_ERR_INVALID_ARG if either is NULL).  With n == 0 they
+ *   are set to zero.  The state is fp32 as accumulated by the kernel; with
+ *   causal = 0 it is the total every row was read against (the same mu_n).
+ */
+la_status la_forward_state(const void *q, const void *k, const void *v,
+                           void *out, int B, int H, int64_t n, int d,
+                           int d_feat, la_map map, const float *omega,
+                           const float *decay, int causal, la_dtype dtype,
+                           void *workspace, float *mu_out, float *nu_out,
+                           void *stream);
+
+/*
  * la_decode_step -- one autoregressive step per (sequence, head) unit: the
  * running sums are updated in place by the new (k, v) and the new token's
  * output is read out from the UPDATED sums (it attends to itself).

@@ -27,7 +27,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
 
 # Exported symbols, in the order include/linattn.h declares them.
 SYMBOLS = ("la_featmap", "la_forward_workspace_bytes", "la_forward",
-           "la_decode_step", "la_status_str", "la_last_error")
+           "la_forward_state", "la_decode_step", "la_status_str",
+           "la_last_error")
 
 _lock = threading.Lock()
 _lib = None
@@ -65,6 +66,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.la_forward.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32,
                                    i32, vp, vp, i32, i32, vp, vp]
         lib.la_forward.restype = i32
+        lib.la_forward_state.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32,
+                                         i32, i32, vp, vp, i32, i32, vp, vp,
+                                         vp, vp]
+        lib.la_forward_state.restype = i32
         lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                        i32, i32, vp, vp, i32, vp]
         lib.la_decode_step.restype = i32
@@ -179,11 +184,16 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             feature_map="elu1", omega: Optional[torch.Tensor] = None,
             decay: Optional[torch.Tensor] = None, causal: bool = True,
             out: Optional[torch.Tensor] = None,
-            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+            workspace: Optional[torch.Tensor] = None,
+            mu_out: Optional[torch.Tensor] = None,
+            nu_out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Kernelized linear attention over q, k [B,H,n,d_qk], v [B,H,n,d].
 
     workspace: optional uint8 device tensor from new_workspace(); by default a
-    cached zero-initialised one per (device, stream) is used."""
+    cached zero-initialised one per (device, stream) is used.
+    mu_out [B,H,d_feat,d], nu_out [B,H,d_feat] (fp32, both or neither):
+    receive the state after the last position (la_forward_state), the state
+    decode_step continues from."""
     lib = load_library()
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _dev(t, nm)
@@ -211,11 +221,26 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if need and workspace.numel() < need:
         raise ValueError(f"workspace of {workspace.numel()} bytes is smaller "
                          f"than the {need} bytes required")
-    st = lib.la_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, n, d,
-                        d_feat, mapk, _ptr(omega), _ptr(decay),
-                        int(bool(causal)), dt,
-                        _ptr(workspace) if need else None, _stream(v.device))
-    _check(st, "la_forward")
+    if (mu_out is None) != (nu_out is None):
+        raise ValueError("mu_out and nu_out go together")
+    if mu_out is None:
+        st = lib.la_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, n, d,
+                            d_feat, mapk, _ptr(omega), _ptr(decay),
+                            int(bool(causal)), dt,
+                            _ptr(workspace) if need else None,
+                            _stream(v.device))
+        _check(st, "la_forward")
+        return out
+    _f32(mu_out, "mu_out")
+    _f32(nu_out, "nu_out")
+    if mu_out.shape != (B, H, d_feat, d) or nu_out.shape != (B, H, d_feat):
+        raise ValueError("mu_out must be [B,H,d_feat,d] and nu_out [B,H,d_feat]")
+    st = lib.la_forward_state(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, n,
+                              d, d_feat, mapk, _ptr(omega), _ptr(decay),
+                              int(bool(causal)), dt,
+                              _ptr(workspace) if need else None, _ptr(mu_out),
+                              _ptr(nu_out), _stream(v.device))
+    _check(st, "la_forward_state")
     return out
 
 

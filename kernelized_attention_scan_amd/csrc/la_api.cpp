@@ -135,6 +135,76 @@ la_status plan_forward(int B, int H, int64_t n, int d, int d_feat, int map,
 
 }  // namespace
 
+// la_forward and la_forward_state; mu_out / nu_out (both or neither) receive
+// the state after the last position.
+static la_status forward_impl(const void *q, const void *k, const void *v, void *out,
+                       int B, int H, int64_t n, int d, int d_feat, int map,
+                       const float *omega, const float *decay, int causal,
+                       int dtype, void *workspace, float *mu_out, float *nu_out,
+                       void *stream) {
+  try {
+    FwdPlan p;
+    const la_status st = plan_forward(B, H, n, d, d_feat, map, dtype, causal,
+                                      decay != nullptr, &p);
+    if (st != LA_OK) return st;
+    const int64_t units = static_cast<int64_t>(B) * H;
+    if (units == 0) return ok();
+    if (n == 0) {  // no positions: the handed-out state is zero
+      if (!mu_out) return ok();
+      hipStream_t s = static_cast<hipStream_t>(stream);
+      hipError_t e = la::launch_fill_zero(mu_out, units * d_feat * d, s);
+      if (e == hipSuccess) e = la::launch_fill_zero(nu_out, units * d_feat, s);
+      if (e != hipSuccess) return hip_fail(e, "la_forward_state zero state");
+      return ok();
+    }
+    if (!q || !k || !v || !out)
+      return fail(LA_ERR_INVALID_ARG, "null q, k, v or out");
+    if (map == LA_MAP_PERFORMER && !omega)
+      return fail(LA_ERR_INVALID_ARG, "PERFORMER needs omega");
+    if ((mu_out == nullptr) != (nu_out == nullptr))
+      return fail(LA_ERR_INVALID_ARG, "mu_out and nu_out go together");
+    if (p.total() > 0 && !workspace)
+      return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes required", p.total());
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    const void *qf = q, *kf = k;
+    if (map == LA_MAP_PERFORMER && !p.fused_performer) {
+      // Q', K' into the workspace, then the identity-map forward over them.
+      unsigned char *fq = ws + p.state_bytes, *fk = fq + p.feat_bytes;
+      hipError_t e = la::launch_featmap_performer(q, fq, omega, units * n, d,
+                                                  d_feat, dtype, dtype, s);
+      if (e == hipSuccess)
+        e = la::launch_featmap_performer(k, fk, omega, units * n, d, d_feat,
+                                         dtype, dtype, s);
+      if (e != hipSuccess) return hip_fail(e, "la_forward feature map");
+      qf = fq;
+      kf = fk;
+    }
+    la::FwdArgs a;
+    a.q = qf;
+    a.k = kf;
+    a.v = v;
+    a.out = out;
+    a.decay = decay;
+    a.sync = p.need_states ? reinterpret_cast<unsigned *>(ws) : nullptr;
+    a.states = p.need_states ? reinterpret_cast<float *>(ws + p.sync_bytes)
+                             : nullptr;
+    a.H = H;
+    a.n = n;
+    a.seg_len = p.seg_len;
+    a.nseg = p.nseg;
+    a.elu1 = map == LA_MAP_ELU1;
+    a.omega = p.fused_performer ? omega : nullptr;
+    a.mu_out = mu_out;
+    a.nu_out = nu_out;
+    const hipError_t e = p.ops->run(a, units, causal, s);
+    if (e != hipSuccess) return hip_fail(e, "la_forward launch");
+    return ok();
+  } catch (...) {
+    return fail(LA_ERR_HIP, "unexpected exception in la_forward");
+  }
+}
+
 extern "C" {
 
 const char *la_status_str(la_status s) {
@@ -203,55 +273,20 @@ la_status la_forward(const void *q, const void *k, const void *v, void *out,
                      int B, int H, int64_t n, int d, int d_feat, la_map map,
                      const float *omega, const float *decay, int causal,
                      la_dtype dtype, void *workspace, void *stream) {
-  try {
-    FwdPlan p;
-    const la_status st = plan_forward(B, H, n, d, d_feat, map, dtype, causal,
-                                      decay != nullptr, &p);
-    if (st != LA_OK) return st;
-    const int64_t units = static_cast<int64_t>(B) * H;
-    if (units == 0 || n == 0) return ok();
-    if (!q || !k || !v || !out)
-      return fail(LA_ERR_INVALID_ARG, "null q, k, v or out");
-    if (map == LA_MAP_PERFORMER && !omega)
-      return fail(LA_ERR_INVALID_ARG, "PERFORMER needs omega");
-    if (p.total() > 0 && !workspace)
-      return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes required", p.total());
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    unsigned char *ws = static_cast<unsigned char *>(workspace);
-    const void *qf = q, *kf = k;
-    if (map == LA_MAP_PERFORMER && !p.fused_performer) {
-      // Q', K' into the workspace, then the identity-map forward over them.
-      unsigned char *fq = ws + p.state_bytes, *fk = fq + p.feat_bytes;
-      hipError_t e = la::launch_featmap_performer(q, fq, omega, units * n, d,
-                                                  d_feat, dtype, dtype, s);
-      if (e == hipSuccess)
-        e = la::launch_featmap_performer(k, fk, omega, units * n, d, d_feat,
-                                         dtype, dtype, s);
-      if (e != hipSuccess) return hip_fail(e, "la_forward feature map");
-      qf = fq;
-      kf = fk;
-    }
-    la::FwdArgs a;
-    a.q = qf;
-    a.k = kf;
-    a.v = v;
-    a.out = out;
-    a.decay = decay;
-    a.sync = p.need_states ? reinterpret_cast<unsigned *>(ws) : nullptr;
-    a.states = p.need_states ? reinterpret_cast<float *>(ws + p.sync_bytes)
-                             : nullptr;
-    a.H = H;
-    a.n = n;
-    a.seg_len = p.seg_len;
-    a.nseg = p.nseg;
-    a.elu1 = map == LA_MAP_ELU1;
-    a.omega = p.fused_performer ? omega : nullptr;
-    const hipError_t e = p.ops->run(a, units, causal, s);
-    if (e != hipSuccess) return hip_fail(e, "la_forward launch");
-    return ok();
-  } catch (...) {
-    return fail(LA_ERR_HIP, "unexpected exception in la_forward");
-  }
+  return forward_impl(q, k, v, out, B, H, n, d, d_feat, map, omega, decay,
+                      causal, dtype, workspace, nullptr, nullptr, stream);
+}
+
+la_status la_forward_state(const void *q, const void *k, const void *v,
+                           void *out, int B, int H, int64_t n, int d,
+                           int d_feat, la_map map, const float *omega,
+                           const float *decay, int causal, la_dtype dtype,
+                           void *workspace, float *mu_out, float *nu_out,
+                           void *stream) {
+  if (!mu_out || !nu_out)
+    return fail(LA_ERR_INVALID_ARG, "la_forward_state needs mu_out and nu_out");
+  return forward_impl(q, k, v, out, B, H, n, d, d_feat, map, omega, decay,
+                      causal, dtype, workspace, mu_out, nu_out, stream);
 }
 
 la_status la_decode_step(float *mu, float *nu, const void *q, const void *k,

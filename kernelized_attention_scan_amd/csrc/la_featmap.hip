@@ -196,4 +196,22 @@ hipError_t launch_featmap_performer(const void *x, void *y, const float *omega,
   return performer_by_d<float, float>(x, y, omega, rows, d, m, s);
 }
 
+namespace {
+__global__ __launch_bounds__(256) void la_fill_zero_kernel(float *p,
+                                                           int64_t count) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+       i < count; i += static_cast<int64_t>(gridDim.x) * 256)
+    p[i] = 0.f;
+}
+}  // namespace
+
+hipError_t launch_fill_zero(float *p, int64_t count, hipStream_t stream) {
+  if (count <= 0) return hipSuccess;
+  const int64_t blocks = (count + 255) / 256;
+  const unsigned grid = static_cast<unsigned>(blocks < 1024 ? blocks : 1024);
+  hipLaunchKernelGGL(la_fill_zero_kernel, dim3(grid), dim3(256), 0, stream, p,
+                     count);
+  return hipGetLastError();
+}
+
 }  // namespace la

@@ -408,12 +408,14 @@ __device__ __forceinline__ void publish_state(const f32x4 *S, T *sST, int w,
 
 // Exchange of segment aggregates between the workgroups of one (batch, head)
 // unit, through that unit's line of the synchronisation area (see
-// la_internal.h).  Aggregates are written and read with agent-scope atomic
-// 64-bit accesses, which are coherent across the XCDs' L2 caches by
-// themselves, so the exchange needs no cache write-back or invalidation.
-// Publishing: every wave waits until its aggregate stores have completed,
-// then flag s is set.  Waiting: one wave polls the flags it needs (16 lanes,
-// one line); the aggregates are read after every flag was seen set.  Every
+// la_internal.h).  Aggregates are written with agent-scope atomic 64-bit
+// stores, which write through to the device's coherence point, so the
+// exchange needs no write-back of the L2 caches.  Publishing: every wave
+// waits until its aggregate stores have completed, then flag s is set.
+// Waiting: one wave polls the flags it needs (16 lanes, one line) and, once
+// all are set, acquires (invalidating stale cached lines); the aggregates are
+// then read with plain loads, which hit the L2 where the writers ran on the
+// same XCD.  Every
 // workgroup a wait depends on is running (causal: segment indices follow
 // start order; non-causal: cooperative launch).  The wait is bounded (a few
 // seconds): if the area were ever corrupt it sets the timeout word and lets
@@ -428,17 +430,6 @@ __device__ __forceinline__ void store_agent(float *p, const f32x4 &v) {
   __hip_atomic_store(reinterpret_cast<u64 *>(p) + 1,
                      __builtin_bit_cast(u64, __builtin_shufflevector(v, v, 2, 3)),
                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ f32x4 load_agent(const float *p) {
-  typedef unsigned long long u64;
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  const u64 lo = __hip_atomic_load(reinterpret_cast<const u64 *>(p),
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const u64 hi = __hip_atomic_load(reinterpret_cast<const u64 *>(p) + 1,
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const f32x2 a = __builtin_bit_cast(f32x2, lo), b = __builtin_bit_cast(f32x2, hi);
-  return f32x4{a[0], a[1], b[0], b[1]};
 }
 
 __device__ __forceinline__ void publish_flag(unsigned *line, int seg) {
@@ -471,6 +462,7 @@ __device__ __forceinline__ void wait_flags(unsigned *line, int need,
         break;
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
 }
@@ -554,6 +546,8 @@ void la_fwd_kernel(FwdArgs a) {
   const int64_t start = seg * a.seg_len;
   const int64_t end = min(a.n, start + a.seg_len);
   const int nch = static_cast<int>((end - start + C - 1) / C);
+  // this workgroup writes the unit's final state (the last segment does)
+  const bool keep_state = a.mu_out != nullptr && seg + 1 == a.nseg;
 
   // Constant parts of the tiles: the ones block of sV (column D = 1, the
   // other 15 columns 0, every row) and, for DF < 32, the zero k-padding
@@ -699,7 +693,8 @@ void la_fwd_kernel(FwdArgs a) {
             for (int mj = 0; mj < F::JPW; ++mj) {
               const int jb = tile_jb<F>(w, mj);
               const int idx = tile_fb<F>(w, m) * F::NJA + min(jb, F::NJA - 1);
-              buf[u][m * F::JPW + mj] = load_agent(sj + (idx * 64 + lane) * 4);
+              buf[u][m * F::JPW + mj] =
+                  *reinterpret_cast<const f32x4 *>(sj + (idx * 64 + lane) * 4);
             }
         }
 #pragma unroll
@@ -870,15 +865,37 @@ void la_fwd_kernel(FwdArgs a) {
         }
       }
 
-      if (CAUSAL && !last) {
+      // the last chunk updates the state only when it is handed out
+      if (CAUSAL && (!last || (keep_state && c + 1 == nch))) {
         // ---- state update: S <- g^r S + (w.K')^T [V | 1] ----
         state_update<F>(S, sKw, sV, DECAY ? gp[rows] : 1.f, w, g, li);
         __syncthreads();  // all waves done reading sST and the chunk tiles
-        publish_state<F>(S, sST, w, g, li);
+        if (!last) publish_state<F>(S, sST, w, g, li);
       } else {
         __syncthreads();  // before the next chunk overwrites the tiles
       }
     }
+  }
+  // The state after the unit's last position (causal: after the last chunk's
+  // update; non-causal: the total every row read), mu [d'][d] and nu [d'] in
+  // fp32: tile (fb, jb) holds rows 16 fb + 4 g + r of columns 16 jb + li,
+  // and the ones block's column 0 is nu.
+  if (keep_state) {
+    float *mu = a.mu_out + unit * static_cast<int64_t>(DF) * D;
+    float *nu = a.nu_out + unit * static_cast<int64_t>(DF);
+#pragma unroll
+    for (int m = 0; m < F::FPW; ++m)
+#pragma unroll
+      for (int mj = 0; mj < F::JPW; ++mj) {
+        const int fb = tile_fb<F>(w, m), jb = tile_jb<F>(w, mj);
+        const f32x4 v = S[m * F::JPW + mj];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int f = 16 * fb + 4 * g + r;
+          if (jb < NJ) mu[static_cast<int64_t>(f) * D + 16 * jb + li] = v[r];
+          else if (jb == NJ && li == 0) nu[f] = v[r];
+        }
+      }
   }
   if (MULTI && a.nseg > 1) count_done(line, a.nseg);
 }

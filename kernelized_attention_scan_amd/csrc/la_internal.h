@@ -51,6 +51,8 @@ struct FwdArgs {
   int nseg;
   int elu1;             // 1: phi = elu + 1 on q, k; 0: q, k are features
   const float *omega;   // [d][d_feat] for the fused Performer map, else null
+  float *mu_out;        // [units][d_feat][d] final state, or null
+  float *nu_out;        // [units][d_feat] final normaliser (with mu_out)
 };
 
 // Launch set of one (storage type, d, d_feat) instance of the chunked forward.
@@ -80,6 +82,9 @@ hipError_t launch_featmap_elementwise(const void *x, void *y, int64_t count,
 hipError_t launch_featmap_performer(const void *x, void *y, const float *omega,
                                     int64_t rows, int d, int m, int in_dt,
                                     int out_dt, hipStream_t stream);
+
+// Zero count floats (a fill kernel, so it can be captured in a graph).
+hipError_t launch_fill_zero(float *p, int64_t count, hipStream_t stream);
 
 // Decode step launcher (map: 0 identity, 1 elu1, 2 performer).
 hipError_t launch_decode(float *mu, float *nu, const void *q, const void *k,

@@ -282,6 +282,90 @@ def run_decode(cfg: I.DecodeConfig, seed=0):
     return rel(out, ro), rel(mu, rmu), rel(nu, rnu)
 
 
+# --------------------------------------------------------------------------
+# Prefill -> decode hand-off: the state after the last position
+# --------------------------------------------------------------------------
+
+def _oracle_state(x, cfg):
+    """mu_n, nu_n by the oracle's decode step applied to every position from
+    a zero state (the literal eqs 7-8 / 10-11)."""
+    B, H, n, d = x["v"].shape
+    mu = np.zeros((B, H, cfg.d_feat, d))
+    nu = np.zeros((B, H, cfg.d_feat))
+    q, k, v = f64(x["q"]), f64(x["k"]), f64(x["v"])
+    for j in range(n):
+        _, mu, nu = oracle.decode(mu, nu, q[:, :, j], k[:, :, j], v[:, :, j],
+                                  cfg.mapk, f64(x["omega"]), f64(x["decay"]))
+    return mu, nu
+
+
+STATE_CASES = {
+    # several segments per unit (the last one hands the state out)
+    "elu1_segmented": I.ELU1_CAUSAL.replace(B=2, H=2, n=1000),
+    "elu1_decay_d128": I.DECAYED.replace(B=1, H=2, n=700),
+    "performer_fused": I.PERFORMER.replace(B=1, H=2, n=300, m=64),
+    "fp32_decay_d32": I.ELU1_CAUSAL.replace(B=2, H=1, n=333, d=32,
+                                            dtype=torch.float32,
+                                            decay=(-2.0, -1.0)),
+    "one_chunk": I.ELU1_CAUSAL.replace(B=1, H=3, n=40),
+    "noncausal": I.ELU1_CAUSAL.replace(B=1, H=2, n=500, causal=False),
+}
+
+
+@pytest.mark.parametrize("name", sorted(STATE_CASES))
+def test_forward_state_matches_oracle(name):
+    cfg = STATE_CASES[name]
+    x = I.make_prefill(cfg, 31)
+    mu = torch.empty(cfg.B, cfg.H, cfg.d_feat, cfg.d, device="cuda")
+    nu = torch.empty(cfg.B, cfg.H, cfg.d_feat, device="cuda")
+    out = K.forward(dev(x["q"]), dev(x["k"]), dev(x["v"]),
+                    I.MAP_NAMES[cfg.mapk], omega=dev(x["omega"]),
+                    decay=dev(x["decay"]), causal=cfg.causal, mu_out=mu,
+                    nu_out=nu)
+    torch.cuda.synchronize()
+    rmu, rnu = _oracle_state(x, cfg)
+    ref = oracle.forward(f64(x["q"]), f64(x["k"]), f64(x["v"]), cfg.mapk,
+                         f64(x["omega"]), f64(x["decay"]), cfg.causal)
+    # the state is fp32, accumulated from features rounded to the storage type
+    assert rel(out, ref) <= TOL[cfg.dtype]
+    assert rel(mu, rmu) <= TOL[cfg.dtype]
+    assert rel(nu, rnu) <= TOL[cfg.dtype]
+
+
+def test_forward_state_empty_sequence_is_zero():
+    mu = torch.full((2, 3, 64, 64), 7.0, device="cuda")
+    nu = torch.full((2, 3, 64), 7.0, device="cuda")
+    e = torch.empty(2, 3, 0, 64, dtype=torch.bfloat16, device="cuda")
+    K.forward(e, e, e, mu_out=mu, nu_out=nu)
+    torch.cuda.synchronize()
+    assert mu.abs().max().item() == 0.0 and nu.abs().max().item() == 0.0
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("decay", [False, True])
+def test_prefill_state_then_decode_continues(dtype, decay):
+    """Prefill the first n0 positions with the state handed out, then decode
+    the rest token by token: the outputs equal one forward over all n."""
+    n, n0 = 600, 536
+    cfg = I.ELU1_CAUSAL.replace(B=2, H=2, n=n, d=32, dtype=dtype,
+                                decay=(-2.0, -1.0) if decay else None)
+    x = I.make_prefill(cfg, 41)
+    q, k, v, dec = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["decay"])
+    full = K.forward(q, k, v, decay=dec)
+    mu = torch.empty(2, 2, 32, 32, device="cuda")
+    nu = torch.empty(2, 2, 32, device="cuda")
+    K.forward(q[:, :, :n0].contiguous(), k[:, :, :n0].contiguous(),
+              v[:, :, :n0].contiguous(), decay=dec, mu_out=mu, nu_out=nu)
+    outs = [K.decode_step(mu, nu, q[:, :, j].contiguous(),
+                          k[:, :, j].contiguous(), v[:, :, j].contiguous(),
+                          decay=dec) for j in range(n0, n)]
+    torch.cuda.synchronize()
+    chain = torch.stack(outs, dim=2).float()
+    tail = full[:, :, n0:].float()
+    err = (chain - tail).abs().max().item() / tail.abs().max().item()
+    assert err <= TOL[dtype]
+
+
 @pytest.mark.parametrize("cfg", [
     I.DECODE.replace(name="dec_small", S=4, H=3),
     I.DECODE.replace(name="dec_d64_nodecay", S=3, H=5, d=64, a=None),

@@ -156,6 +156,24 @@ def test_decode_rejects(lib):
              1, None) == B.LA_OK
 
 
+def test_forward_state_rejects(lib):
+    f = lib.la_forward_state
+    P = FAKE
+    # the state outputs are required
+    assert f(P, P, P, P, 1, 1, 64, 64, 64, 1, None, None, 1, 1, None, None, P,
+             None) == B.LA_ERR_INVALID_ARG
+    assert f(P, P, P, P, 1, 1, 64, 64, 64, 1, None, None, 1, 1, None, P, None,
+             None) == B.LA_ERR_INVALID_ARG
+    # the same validation as la_forward
+    assert f(P, P, P, P, -1, 1, 64, 64, 64, 1, None, None, 1, 1, None, P, P,
+             None) == B.LA_ERR_INVALID_ARG
+    assert f(P, P, P, P, 1, 1, 64, 48, 48, 1, None, None, 1, 1, None, P, P,
+             None) == B.LA_ERR_UNSUPPORTED
+    # no units: nothing to do
+    assert f(None, None, None, None, 0, 4, 64, 64, 64, 1, None, None, 1, 1,
+             None, P, P, None) == B.LA_OK
+
+
 def test_last_error_is_cleared_on_success(lib):
     assert fwd(lib, B=-1) == B.LA_ERR_INVALID_ARG
     assert lib.la_last_error().decode() != ""
