@@ -147,7 +147,15 @@ struct FwdShape {
   static constexpr int TPW = NF >= kWaves ? NF / kWaves : 1;
   static constexpr int WPT = NF >= kWaves ? 1 : kWaves / NF;
   static constexpr int SPW = (STRIPS + WPT - 1) / WPT;
-  static constexpr size_t lds_bytes = fwd_lds_bytes<T>(C, D, DF, DECAY, PF);
+  // Resident keys: with two workgroups per CU and no decay, phase 1 keeps
+  // phi(K) of each chunk of a short segment (at most KRES chunks, one ring
+  // revolution) in its own LDS slot and phase 2 reuses it instead of loading
+  // and mapping K again.
+  static constexpr int KRES_ =
+      (!PF && !DECAY && sizeof(T) == 2 && D <= 64 && DF <= 64) ? 4 : 0;
+  static constexpr int KSLOTS = KRES_ > 0 ? KRES_ : 1;
+  static constexpr size_t lds_bytes = fwd_lds_bytes<T>(C, D, DF, DECAY, PF) +
+                                      sizeof(T) * (KSLOTS - 1) * SQ;
   // fp32 state slot: NTILE tiles x 64 lanes x 4 (accumulator order).
   static constexpr int SLOT = NTILE * 256;
   // Workgroups per compute unit the instance is built for: two for the small
@@ -163,6 +171,8 @@ struct FwdShape {
   static constexpr int REG1 = 4 * (Slab<T, QW, C>::PER + Slab<T, D, C>::PER);
   static constexpr int NB2 = REG2 >= RING ? 1 : (RING / REG2 > 4 ? 4 : RING / REG2);
   static constexpr int NB1 = REG1 >= RING1 ? 1 : (RING1 / REG1 > 6 ? 6 : RING1 / REG1);
+  // resident keys need phase 1 to cover a resident segment in one revolution
+  static constexpr int KRES = KRES_ > 0 && NB1 == KRES_ ? KRES_ : 0;
   // the fused Performer map needs bf16 operands, d a multiple of 32 (the
   // projection's k-width), at least 32 features, and d d' <= 128 * 128 (the
   // register budget of one workgroup per CU; larger shapes spill)
@@ -495,9 +505,9 @@ void la_fwd_kernel(FwdArgs a) {
   constexpr int NB1 = F::NB1, NB2 = F::NB2, TW = F::FPW * F::JPW;
   extern __shared__ __align__(16) unsigned char smem[];
   T *sQ = reinterpret_cast<T *>(smem);
-  T *sK = sQ + F::SQ;
-  T *sKw = DECAY ? sK + F::SQ : sK;
-  T *sV = sK + F::SQ + F::SKW;
+  T *sK = sQ + F::SQ;             // KSLOTS slots (resident keys), else one
+  T *sKw = DECAY ? sK + F::SQ * F::KSLOTS : sK;
+  T *sV = sK + F::SQ * F::KSLOTS + F::SKW;
   T *sST = sV + F::SV;
   T *sXq = sST + F::SST;          // raw q, k rows (fused Performer)
   T *sXk = sXq + F::SX;
@@ -548,6 +558,9 @@ void la_fwd_kernel(FwdArgs a) {
   const int nch = static_cast<int>((end - start + C - 1) / C);
   // this workgroup writes the unit's final state (the last segment does)
   const bool keep_state = a.mu_out != nullptr && seg + 1 == a.nseg;
+  // phi(K) of the whole segment stays in LDS from phase 1 to phase 2
+  const bool resident = F::KRES > 0 && MULTI && CAUSAL && a.nseg > 1 &&
+                        seg + 1 < a.nseg && nch <= F::KRES;
 
   // Constant parts of the tiles: the ones block of sV (column D = 1, the
   // other 15 columns 0, every row) and, for DF < 32, the zero k-padding
@@ -597,7 +610,7 @@ void la_fwd_kernel(FwdArgs a) {
       const int rows = static_cast<int>(min<int64_t>(C, end - r0));
       rq[b].load(qb, r0, rows, tid);
       if (CAUSAL) {
-        rk2[b].load(kb, r0, rows, tid);
+        if (!resident) rk2[b].load(kb, r0, rows, tid);
         rv2[b].load(vb, r0, rows, tid);
       }
     }
@@ -626,11 +639,14 @@ void la_fwd_kernel(FwdArgs a) {
         const int64_t r0 = start + c * C;
         const int rows =
             c < nch ? static_cast<int>(min<int64_t>(C, end - r0)) : 0;
+        // resident keys: chunk c's phi(K) in slot c (c < KRES: one
+        // revolution covers a resident segment)
+        T *sKc = resident ? sK + c * F::SQ : sK;
         if constexpr (PF)
           stage_values<T, D, C, LX>(rk[b], sXk, tid);
         else
-          stage_keys<T, DF, C, LQ, DECAY, false, ELU>(rk[b], sK, sKw, gp, dk.b,
-                                                      rows, tid);
+          stage_keys<T, DF, C, LQ, DECAY, false, ELU>(
+              rk[b], sKc, DECAY ? sKw : sKc, gp, dk.b, rows, tid);
         stage_values<T, D, C, LV>(rv[b], sV, tid);
         __syncthreads();
         {
@@ -645,7 +661,8 @@ void la_fwd_kernel(FwdArgs a) {
               wf, sXq, sXk, sQ, sK, sKw, gp, dk.b, rows, w, g, li);
           __syncthreads();
         }
-        state_update<F>(S, sKw, sV, DECAY ? gp[rows] : 1.f, w, g, li);
+        state_update<F>(S, DECAY ? sKw : sKc, sV, DECAY ? gp[rows] : 1.f, w,
+                        g, li);
         __syncthreads();
       }
     }
@@ -750,6 +767,7 @@ void la_fwd_kernel(FwdArgs a) {
         dw[4 * sb + rr] = s <= t ? dk.b * gp[t - s] : 0.f;
       }
   }
+  // resident keys: no K loads, no K staging; chunk c reads slot c
   const int nch2 = (nch + NB2 - 1) / NB2 * NB2;
   for (int c0 = 0; c0 < nch2; c0 += NB2) {
 #pragma unroll
@@ -764,7 +782,7 @@ void la_fwd_kernel(FwdArgs a) {
         if (CAUSAL) stage_values<T, D, C, LX>(rk2[b], sXk, tid);
       } else {
         stage_queries<T, DF, C, LQ, ELU>(rq[b], sQ, tid);
-        if (CAUSAL)
+        if (CAUSAL && !resident)
           stage_keys<T, DF, C, LQ, DECAY, true, ELU>(rk2[b], sK, sKw, gp, dk.b,
                                                      rows, tid);
       }
@@ -776,10 +794,11 @@ void la_fwd_kernel(FwdArgs a) {
         const int rows2 = static_cast<int>(min<int64_t>(C, end - r2));
         rq[b].load(qb, r2, rows2, tid);
         if (CAUSAL) {
-          rk2[b].load(kb, r2, rows2, tid);
+          if (!resident) rk2[b].load(kb, r2, rows2, tid);
           rv2[b].load(vb, r2, rows2, tid);
         }
       }
+      T *sKc = resident ? sK + c * F::SQ : sK;  // this chunk's phi(K)
       if constexpr (PF) {
         performer_features<F, T, true, CAUSAL, DECAY, true>(
             wf, sXq, sXk, sQ, sK, sKw, gp, dk.b, rows, w, g, li);
@@ -800,7 +819,7 @@ void la_fwd_kernel(FwdArgs a) {
 #pragma unroll
           for (int kq = 0; kq < DFP / 32; ++kq) {
             Frag<T> fa;
-            load_frag8(fa, sK + (16 * sb + li) * LQ + 32 * kq + 8 * g);
+            load_frag8(fa, sKc + (16 * sb + li) * LQ + 32 * kq + 8 * g);
             acc = mma(fa, qf[kq], acc);
           }
           // acc[rr] = q'_t . k'_s with s = 16 sb + 4 g + rr; with decay the
@@ -868,7 +887,8 @@ void la_fwd_kernel(FwdArgs a) {
       // the last chunk updates the state only when it is handed out
       if (CAUSAL && (!last || (keep_state && c + 1 == nch))) {
         // ---- state update: S <- g^r S + (w.K')^T [V | 1] ----
-        state_update<F>(S, sKw, sV, DECAY ? gp[rows] : 1.f, w, g, li);
+        state_update<F>(S, DECAY ? sKw : sKc, sV, DECAY ? gp[rows] : 1.f, w,
+                        g, li);
         __syncthreads();  // all waves done reading sST and the chunk tiles
         if (!last) publish_state<F>(S, sST, w, g, li);
       } else {
@@ -876,6 +896,7 @@ void la_fwd_kernel(FwdArgs a) {
       }
     }
   }
+
   // The state after the unit's last position (causal: after the last chunk's
   // update; non-causal: the total every row read), mu [d'][d] and nu [d'] in
   // fp32: tile (fb, jb) holds rows 16 fb + 4 g + r of columns 16 jb + li,
