@@ -47,9 +47,8 @@ bool supported_feat(int f) {
 size_t elem_size(int t) { return t == LA_BF16 ? 2 : 4; }
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Sequence split of the fused forward: about occ * la::kCUs workgroups in
-// total (occ = workgroups per compute unit of the instance), at most
-// la::kMaxSegments segments of whole chunks per (batch, head) unit.  A unit
+// Sequence split of the fused forward: about la::kCUs workgroups in total,
+// at most la::kMaxSegments segments of whole chunks per (batch, head) unit.  A unit
 // gets several segments only when there are fewer units than that.  Causal
 // splits may exceed what is resident at once; the non-causal launcher
 // shrinks its split to what fits.
@@ -106,7 +105,10 @@ la_status plan_forward(int B, int H, int64_t n, int d, int d_feat, int map,
     return fail(LA_ERR_UNSUPPORTED, "sizes too large");
   const int64_t C = p->ops->C;
   const int64_t nchunks = (n + C - 1) / C;
-  const int64_t target = static_cast<int64_t>(p->ops->occ) * la::kCUs;
+  // about one workgroup per compute unit: measured faster than filling a
+  // second workgroup slot per CU with shorter segments (the chain phase 1 ->
+  // exchange -> phase 2 is shorter with fewer, longer segments)
+  const int64_t target = la::kCUs;
   int64_t per_unit = (target + units - 1) / units;
   if (per_unit > kMaxSegments) per_unit = kMaxSegments;
   if (per_unit < 1) per_unit = 1;

@@ -98,7 +98,7 @@ def test_workspace_bytes(lib):
     sync = 256 + 512 * 128
     ws = K.forward_workspace_bytes(4, 8, 4096, 64, 64)
     units = 32
-    nseg = 16                                  # 512 target groups / 32 units
+    nseg = 8                     # 256 target groups (one per CU) / 32 units
     slot = 64 * (64 + 16)
     a256 = lambda x: (x + 255) // 256 * 256
     assert ws == sync + a256(units * nseg * slot * 4)
