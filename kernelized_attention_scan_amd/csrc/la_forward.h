@@ -66,6 +66,11 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;
 constexpr size_t kMaxLds = 160 * 1024;
 
+// Destination of the stores of output rows past the end of a partial chunk:
+// selecting this address instead of branching around the store keeps the
+// chunk loop free of branches (nothing ever reads it).
+__device__ __align__(16) unsigned char la_discard[16];
+
 // Registers holding one [C][W] slab of a [n][W] row-major matrix as 16-byte
 // pieces; consecutive threads take consecutive pieces (coalesced).
 template <typename T, int W, int C>
@@ -103,16 +108,25 @@ constexpr int kMapFeatures = 0;   // q, k are features already
 constexpr int kMapElu = 1;        // elu + 1 (d' = d)
 constexpr int kMapPerformer = 2;  // Performer random features, fused
 
-// LDS bytes of one instance with chunk length c (see FwdShape).
+// LDS bytes of one instance with chunk length c (see FwdShape): nbuf sets of
+// the q', w.k', V and S^T tiles, kslots slots of k', and the raw q, k rows of
+// the fused Performer map.
 template <typename T>
-constexpr size_t fwd_lds_bytes(int c, int d, int df, bool decay, bool pf) {
+constexpr size_t fwd_lds_bytes(int c, int d, int df, bool decay, bool pf,
+                               int kslots = 1, int nbuf = 1) {
   const int dfp = df < 32 ? 32 : df;
   const size_t sq = static_cast<size_t>(c) * lds_stride<T>(dfp);
   const size_t sv = static_cast<size_t>(c) * lds_stride<T>(d + 16);
   const size_t sst = static_cast<size_t>(d + 16) * lds_stride<T>(dfp);
   const size_t sx = pf ? static_cast<size_t>(c) * lds_stride<T>(d) : 0;
-  return sizeof(T) * (2 * sq + (decay ? sq : 0) + sv + sst + 2 * sx) +
+  return sizeof(T) * (nbuf * (sq + (decay ? sq : 0) + sv + sst) +
+                      kslots * sq + 2 * sx) +
          sizeof(float) * (c + 2);
+}
+
+// Largest power of two <= x, at most 8 (1 for x < 2).
+constexpr int pow2_floor(int x) {
+  return x >= 8 ? 8 : x >= 4 ? 4 : x >= 2 ? 2 : 1;
 }
 
 template <typename T, int D, int DF, bool DECAY, int MAP = kMapFeatures>
@@ -147,21 +161,35 @@ struct FwdShape {
   static constexpr int TPW = NF >= kWaves ? NF / kWaves : 1;
   static constexpr int WPT = NF >= kWaves ? 1 : kWaves / NF;
   static constexpr int SPW = (STRIPS + WPT - 1) / WPT;
-  // Resident keys: with two workgroups per CU and no decay, phase 1 keeps
-  // phi(K) of each chunk of a short segment (at most KRES chunks, one ring
-  // revolution) in its own LDS slot and phase 2 reuses it instead of loading
-  // and mapping K again.
+  // Software pipelining (both loops): two sets of operand tiles and of the
+  // S^T copy, so that chunk c + 1 is mapped and staged while chunk c is
+  // multiplied, with one barrier per chunk; where LDS holds the second set.
+  // Resident keys (bf16, no decay, d, d' <= 64): phase 1 keeps phi(K) of each
+  // chunk of a short segment (at most KRES_ chunks) in its own slot of sK and
+  // phase 2 reuses it instead of loading and mapping K again.
+  static constexpr bool RES_OK =
+      !PF && !DECAY && sizeof(T) == 2 && D <= 64 && DF <= 64;
   static constexpr int KRES_ =
-      (!PF && !DECAY && sizeof(T) == 2 && D <= 64 && DF <= 64) ? 4 : 0;
-  static constexpr int KSLOTS = KRES_ > 0 ? KRES_ : 1;
-  static constexpr size_t lds_bytes = fwd_lds_bytes<T>(C, D, DF, DECAY, PF) +
-                                      sizeof(T) * (KSLOTS - 1) * SQ;
+      !RES_OK ? 0
+      : fwd_lds_bytes<T>(C, D, DF, DECAY, PF, 8, 2) <= kMaxLds ? 8
+      : fwd_lds_bytes<T>(C, D, DF, DECAY, PF, 4, 2) <= kMaxLds ? 4
+                                                                : 0;
+  static constexpr int KS2 = KRES_ > 2 ? KRES_ : 2;
+  static constexpr bool PIPE =
+      !PF && fwd_lds_bytes<T>(C, D, DF, DECAY, PF, KS2, 2) <= kMaxLds;
+  static constexpr int NBUF = PIPE ? 2 : 1;                 // sets of tiles
+  static constexpr int KS = PIPE ? KS2 : 1;                 // slots of sK
+  static constexpr size_t lds_bytes =
+      fwd_lds_bytes<T>(C, D, DF, DECAY, PF, KS, NBUF);
   // fp32 state slot: NTILE tiles x 64 lanes x 4 (accumulator order).
   static constexpr int SLOT = NTILE * 256;
-  // Workgroups per compute unit the instance is built for: two for the small
-  // bf16 shapes (<= 128 VGPRs, 4 waves per SIMD), else one.
-  static constexpr int OCC =
-      (!PF && sizeof(T) == 2 && D <= 64 && DF <= 64) ? 2 : 1;
+  // Workgroups per compute unit the instance is built for: two (<= 128
+  // VGPRs, 4 waves per SIMD) for the small bf16 shapes where LDS holds two,
+  // else one.
+  static constexpr int OCC = (!PF && sizeof(T) == 2 && D <= 64 && DF <= 64 &&
+                              2 * lds_bytes <= kMaxLds)
+                                 ? 2
+                                 : 1;
   static_assert(OCC * kCUs <= kMaxTargetGroups, "sync area too small");
   static constexpr int WAVES_PER_SIMD = OCC * kWaves / 4;
   // register-ring depths (chunks of loads in flight per workgroup)
@@ -169,10 +197,12 @@ struct FwdShape {
   static constexpr int RING1 = OCC == 2 ? 32 : 64;  // VGPRs, phase-1 ring
   static constexpr int REG2 = 4 * (Slab<T, QW, C>::PER * 2 + Slab<T, D, C>::PER);
   static constexpr int REG1 = 4 * (Slab<T, QW, C>::PER + Slab<T, D, C>::PER);
-  static constexpr int NB2 = REG2 >= RING ? 1 : (RING / REG2 > 4 ? 4 : RING / REG2);
-  static constexpr int NB1 = REG1 >= RING1 ? 1 : (RING1 / REG1 > 6 ? 6 : RING1 / REG1);
-  // resident keys need phase 1 to cover a resident segment in one revolution
-  static constexpr int KRES = KRES_ > 0 && NB1 == KRES_ ? KRES_ : 0;
+  // (powers of two up to 4: loops run whole ring revolutions, and segments
+  // of a power-of-two number of chunks then need no padding chunks; deeper
+  // phase-1 rings were measured slower, the first chunk arriving later)
+  static constexpr int NB2 = pow2_floor(RING / REG2 > 4 ? 4 : RING / REG2);
+  static constexpr int NB1 = pow2_floor(RING1 / REG1 > 4 ? 4 : RING1 / REG1);
+  static constexpr int KRES = PIPE ? KRES_ : 0;
   // the fused Performer map needs bf16 operands, d a multiple of 32 (the
   // projection's k-width), at least 32 features, and d d' <= 128 * 128 (the
   // register budget of one workgroup per CU; larger shapes spill)
@@ -184,13 +214,17 @@ struct FwdShape {
 // State tile ownership: wave w holds tiles (fb, jb) with
 //   fb = w % NF (NF < 8) or w + 8 m (NF >= 8),
 //   jb = w / NF + WPF m' (NF < 8) or every jb (NF >= 8).
+// Where that jb would be past the last block, the wave holds a copy of tile
+// (fb, NJA - 1) instead: every wave then runs the same instructions, and the
+// copy, computed from the same operands in the same order, is bitwise equal
+// to the original, so writing it out again is harmless.
 template <typename F>
 __device__ __forceinline__ int tile_fb(int w, int m) {
   return F::NF >= kWaves ? w + kWaves * m : w % F::NF;
 }
 template <typename F>
 __device__ __forceinline__ int tile_jb(int w, int m) {
-  return F::NF >= kWaves ? m : w / F::NF + F::WPF * m;
+  return F::NF >= kWaves ? m : min(w / F::NF + F::WPF * m, F::NJA - 1);
 }
 
 // Per-head decay: g = a, b = 1 - a (eqs 10-11); g = b = 1 without decay.
@@ -369,31 +403,33 @@ __device__ __forceinline__ void performer_features(
 // S tiles of this wave += (w.K')^T [V | 1] over the chunk: A = rows of sKw
 // read transposed (features along lanes), B = rows of sV read transposed
 // (columns along lanes); contraction over the chunk positions.
+// kmask = 0 drops the keys (the state is only scaled by gr).
 template <typename F, typename T>
 __device__ __forceinline__ void state_update(f32x4 *S, const T *sKw,
                                              const T *sV, float gr, int w,
-                                             int g, int li) {
+                                             int g, int li,
+                                             unsigned kmask = ~0u) {
   constexpr int C = F::C;
 #pragma unroll
   for (int m = 0; m < F::FPW; ++m) {
     const int fb = tile_fb<F>(w, m);
     Frag<T> af[C / 32];
 #pragma unroll
-    for (int kb = 0; kb < C / 32; ++kb)
+    for (int kb = 0; kb < C / 32; ++kb) {
       load_frag_tr8(af[kb], sKw, F::LQ, 32 * kb, 16 * fb, g, li);
+      frag_mask(af[kb], u32x4{kmask, kmask, kmask, kmask});
+    }
 #pragma unroll
     for (int mj = 0; mj < F::JPW; ++mj) {
       const int jb = tile_jb<F>(w, mj);
-      if (jb < F::NJA) {
-        f32x4 acc = S[m * F::JPW + mj] * gr;
+      f32x4 acc = S[m * F::JPW + mj] * gr;
 #pragma unroll
-        for (int kb = 0; kb < C / 32; ++kb) {
-          Frag<T> bf;
-          load_frag_tr8(bf, sV, F::LV, 32 * kb, 16 * jb, g, li);
-          acc = mma(af[kb], bf, acc);
-        }
-        S[m * F::JPW + mj] = acc;
+      for (int kb = 0; kb < C / 32; ++kb) {
+        Frag<T> bf;
+        load_frag_tr8(bf, sV, F::LV, 32 * kb, 16 * jb, g, li);
+        acc = mma(af[kb], bf, acc);
       }
+      S[m * F::JPW + mj] = acc;
     }
   }
 }
@@ -409,9 +445,8 @@ __device__ __forceinline__ void publish_state(const f32x4 *S, T *sST, int w,
     for (int mj = 0; mj < F::JPW; ++mj) {
       const int fb = tile_fb<F>(w, m), jb = tile_jb<F>(w, mj);
       const f32x4 s = S[m * F::JPW + mj];
-      if (jb < F::NJA)
-        store4(sST + (16 * jb + li) * F::LQ + 16 * fb + 4 * g, s[0], s[1],
-               s[2], s[3]);
+      store4(sST + (16 * jb + li) * F::LQ + 16 * fb + 4 * g, s[0], s[1], s[2],
+             s[3]);
     }
   }
 }
@@ -492,24 +527,30 @@ __device__ __forceinline__ void count_done(unsigned *line, int nseg) {
   }
 }
 
+// RES: resident keys (causal, several segments, each at most KRES chunks):
+// every segment, the last one included, runs phase 1 and keeps phi(K) of
+// chunk c in slot c of sK for phase 2.
 template <typename T, int D, int DF, bool CAUSAL, bool MULTI, bool DECAY,
-          int MAP>
+          int MAP, bool RES = false>
 __global__ __launch_bounds__(kThreads,
                              (FwdShape<T, D, DF, DECAY, MAP>::WAVES_PER_SIMD))
 void la_fwd_kernel(FwdArgs a) {
   using F = FwdShape<T, D, DF, DECAY, MAP>;
+  static_assert(!RES || (F::KRES > 0 && CAUSAL && MULTI), "resident keys");
   constexpr bool ELU = MAP == kMapElu, PF = F::PF;
   constexpr int QW = F::QW, LX = F::LX;
   constexpr int C = F::C, LQ = F::LQ, LV = F::LV, DFP = F::DFP;
   constexpr int STRIPS = F::STRIPS, NJ = F::NJ, WPS = F::WPS;
   constexpr int NB1 = F::NB1, NB2 = F::NB2, TW = F::FPW * F::JPW;
   extern __shared__ __align__(16) unsigned char smem[];
+  // NBUF sets of sQ, sKw, sV and sST; KS slots of sK (resident keys, or
+  // one per set)
   T *sQ = reinterpret_cast<T *>(smem);
-  T *sK = sQ + F::SQ;             // KSLOTS slots (resident keys), else one
-  T *sKw = DECAY ? sK + F::SQ * F::KSLOTS : sK;
-  T *sV = sK + F::SQ * F::KSLOTS + F::SKW;
-  T *sST = sV + F::SV;
-  T *sXq = sST + F::SST;          // raw q, k rows (fused Performer)
+  T *sK = sQ + F::NBUF * F::SQ;
+  T *sKw = DECAY ? sK + F::SQ * F::KS : sK;
+  T *sV = sK + F::SQ * F::KS + F::NBUF * F::SKW;
+  T *sST = sV + F::NBUF * F::SV;
+  T *sXq = sST + F::NBUF * F::SST;  // raw q, k rows (fused Performer)
   T *sXk = sXq + F::SX;
   float *gp = reinterpret_cast<float *>(sXk + F::SX);
 
@@ -558,15 +599,16 @@ void la_fwd_kernel(FwdArgs a) {
   const int nch = static_cast<int>((end - start + C - 1) / C);
   // this workgroup writes the unit's final state (the last segment does)
   const bool keep_state = a.mu_out != nullptr && seg + 1 == a.nseg;
-  // phi(K) of the whole segment stays in LDS from phase 1 to phase 2
-  const bool resident = F::KRES > 0 && MULTI && CAUSAL && a.nseg > 1 &&
-                        seg + 1 < a.nseg && nch <= F::KRES;
+  // phi(K) of the whole segment stays in LDS from phase 1 to phase 2 (the
+  // launch guarantees nch <= KRES)
+  constexpr bool resident = RES;
 
   // Constant parts of the tiles: the ones block of sV (column D = 1, the
   // other 15 columns 0, every row) and, for DF < 32, the zero k-padding
   // columns of q', k' and S^T.
-  for (int i = tid; i < C * 16; i += kThreads)
-    sV[(i / 16) * LV + D + i % 16] = from_f32<T>(i % 16 == 0 ? 1.f : 0.f);
+  for (int i = tid; i < F::NBUF * C * 16; i += kThreads)
+    sV[(i / (C * 16)) * F::SV + ((i / 16) % C) * LV + D + i % 16] =
+        from_f32<T>(i % 16 == 0 ? 1.f : 0.f);
   // Fused Performer: this wave's omega^T tiles as A fragments, rounded once
   // to T and kept in registers (lane: feature 16 fb + li, d values
   // 32 kb + 8 g .. +7; for each d the 16 lanes read 16 consecutive floats of
@@ -585,13 +627,15 @@ void la_fwd_kernel(FwdArgs a) {
     }
   }
   if (DFP != DF) {
-    for (int i = tid; i < C * (DFP - DF); i += kThreads) {
-      const int row = i / (DFP - DF), col = DF + i % (DFP - DF);
-      sQ[row * LQ + col] = from_f32<T>(0.f);
-      sK[row * LQ + col] = from_f32<T>(0.f);
+    // every slot of sQ, sK and sST (the padding is never written again)
+    constexpr int NP = DFP - DF;
+    for (int i = tid; i < (F::NBUF + F::KS) * C * NP; i += kThreads) {
+      const int slot = i / (C * NP), row = (i / NP) % C, col = DF + i % NP;
+      sQ[slot * F::SQ + row * LQ + col] = from_f32<T>(0.f);  // sK follows sQ
     }
-    for (int i = tid; i < (D + 16) * (DFP - DF); i += kThreads)
-      sST[(i / (DFP - DF)) * LQ + DF + i % (DFP - DF)] = from_f32<T>(0.f);
+    for (int i = tid; i < F::NBUF * (D + 16) * NP; i += kThreads)
+      sST[(i / ((D + 16) * NP)) * F::SST + ((i / NP) % (D + 16)) * LQ + DF +
+          i % NP] = from_f32<T>(0.f);
   }
 
   f32x4 S[TW];
@@ -618,8 +662,9 @@ void la_fwd_kernel(FwdArgs a) {
 
   if constexpr (MULTI) {
     // ---------------- phase 1: segment aggregate from K, V ----------------
-    // (not for the last causal segment: no other segment needs its aggregate)
-    if (!CAUSAL || seg + 1 < a.nseg) {
+    // (not for the last causal segment, whose aggregate no other segment
+    // needs, unless it keeps its keys resident)
+    if (!CAUSAL || seg + 1 < a.nseg || RES) {
     Slab<T, QW, C> rk[NB1];
     Slab<T, D, C> rv[NB1];
 #pragma unroll
@@ -632,6 +677,55 @@ void la_fwd_kernel(FwdArgs a) {
     }
     __syncthreads();  // gp and the constant tile parts ready
     const int nch1 = (nch + NB1 - 1) / NB1 * NB1;
+    if constexpr (F::PIPE) {
+      // Chunk c + 1 is staged into set (c + 1) % 2 while the state update of
+      // chunk c reads set c % 2: one barrier per chunk.  Resident keys go to
+      // slot c; padding chunks (past nch, zero keys) to the unused sQ.
+      auto keys1 = [&](int c) -> T * {
+        if (resident) return c < nch ? sK + c * F::SQ : sQ + (c & 1) * F::SQ;
+        return sK + (c & 1) * F::SQ;
+      };
+      stage_keys<T, DF, C, LQ, DECAY, false, ELU>(
+          rk[0], keys1(0), sKw, gp, dk.b,
+          static_cast<int>(min<int64_t>(C, end - start)), tid);
+      stage_values<T, D, C, LV>(rv[0], sV, tid);
+      {
+        const int cn = NB1 < nch ? NB1 : nch - 1;
+        const int64_t r2 = start + cn * C;
+        const int rows2 = static_cast<int>(min<int64_t>(C, end - r2));
+        rk[0].load(kb, r2, rows2, tid);
+        rv[0].load(vb, r2, rows2, tid);
+      }
+      __syncthreads();
+      for (int c0 = 0; c0 < nch1; c0 += NB1) {
+#pragma unroll
+        for (int b = 0; b < NB1; ++b) {
+          const int c = c0 + b;
+          const int cur = NB1 % 2 == 0 ? (b & 1) : (c & 1), nxt = cur ^ 1;
+          const int rows =
+              c < nch ? static_cast<int>(min<int64_t>(C, end - (start + c * C)))
+                      : 0;
+          state_update<F>(S, DECAY ? sKw + cur * F::SQ : keys1(c),
+                          sV + cur * F::SV, DECAY ? gp[rows] : 1.f, w, g, li);
+          const int cn = c + 1, bn = (b + 1) % NB1;
+          const int rows_n =
+              cn < nch
+                  ? static_cast<int>(min<int64_t>(C, end - (start + cn * C)))
+                  : 0;
+          stage_keys<T, DF, C, LQ, DECAY, false, ELU>(
+              rk[bn], keys1(cn), sKw + nxt * F::SQ, gp, dk.b, rows_n, tid);
+          stage_values<T, D, C, LV>(rv[bn], sV + nxt * F::SV, tid);
+          {
+            const int cr = cn + NB1 < nch ? cn + NB1 : nch - 1;
+            const int64_t r2 = start + cr * C;
+            const int rows2 = static_cast<int>(min<int64_t>(C, end - r2));
+            rk[bn].load(kb, r2, rows2, tid);
+            rv[bn].load(vb, r2, rows2, tid);
+          }
+          __syncthreads();
+        }
+      }
+    } else
     for (int c0 = 0; c0 < nch1; c0 += NB1) {
 #pragma unroll
       for (int b = 0; b < NB1; ++b) {
@@ -684,8 +778,7 @@ void la_fwd_kernel(FwdArgs a) {
           for (int mj = 0; mj < F::JPW; ++mj) {
             const int jb = tile_jb<F>(w, mj);
             const int idx = tile_fb<F>(w, m) * F::NJA + jb;
-            if (jb < F::NJA)
-              store_agent(mine + (idx * 64 + lane) * 4, S[m * F::JPW + mj]);
+            store_agent(mine + (idx * 64 + lane) * 4, S[m * F::JPW + mj]);
           }
         publish_flag(line, seg);
       }
@@ -709,7 +802,7 @@ void la_fwd_kernel(FwdArgs a) {
 #pragma unroll
             for (int mj = 0; mj < F::JPW; ++mj) {
               const int jb = tile_jb<F>(w, mj);
-              const int idx = tile_fb<F>(w, m) * F::NJA + min(jb, F::NJA - 1);
+              const int idx = tile_fb<F>(w, m) * F::NJA + jb;
               buf[u][m * F::JPW + mj] =
                   *reinterpret_cast<const f32x4 *>(sj + (idx * 64 + lane) * 4);
             }
@@ -731,6 +824,224 @@ void la_fwd_kernel(FwdArgs a) {
   }
 
   if constexpr (!MULTI) ring2_first();
+  if constexpr (F::PIPE) {
+    // ------------ phase 2: chunk loop, software-pipelined ------------
+    // Chunk c is read out from set c % 2 while chunk c + 1 is mapped and
+    // staged into the other set and the state after chunk c is published
+    // into the other S^T copy: one barrier per chunk.  Every wave runs the
+    // same instructions (masks instead of branches on its strip), so a chunk
+    // is one straight block that the compiler can interleave.
+    __syncthreads();  // gp and the constant tile parts ready, phase 1 done
+    publish_state<F>(S, sST, w, g, li);
+    stage_queries<T, DF, C, LQ, ELU>(rq[0], sQ, tid);
+    if (CAUSAL) {
+      if (!resident)
+        stage_keys<T, DF, C, LQ, DECAY, true, ELU>(
+            rk2[0], sK, sKw, gp, dk.b,
+            static_cast<int>(min<int64_t>(C, end - start)), tid);
+      stage_values<T, D, C, LV>(rv2[0], sV, tid);
+    }
+    {
+      const int cr = NB2 < nch ? NB2 : nch - 1;
+      const int64_t r2 = start + cr * C;
+      const int rows2 = static_cast<int>(min<int64_t>(C, end - r2));
+      rq[0].load(qb, r2, rows2, tid);
+      if (CAUSAL) {
+        if (!resident) rk2[0].load(kb, r2, rows2, tid);
+        rv2[0].load(vb, r2, rows2, tid);
+      }
+    }
+    __syncthreads();
+
+    const int tb = w % STRIPS;    // this wave's output strip
+    const int jh = w / STRIPS;    // and its share of the column blocks
+    const int t = 16 * tb + li;   // the output row this lane normalises
+    const float gt = CAUSAL ? gp[t + 1] : 1.f;
+    // Causal mask of each P^T fragment pair kp: element e is key
+    // s = 16 (2 kp + e / 4) + 4 g + e % 4, kept when s <= t.
+    constexpr int NPK = (STRIPS + 1) / 2;
+    u32x4 pm[NPK];
+#pragma unroll
+    for (int kp = 0; kp < NPK; ++kp) {
+      pm[kp] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int s = 16 * (2 * kp + e / 4) + 4 * g + e % 4;
+        if (s <= t) pm[kp][e / 2] |= 0xffffu << (16 * (e % 2));
+      }
+    }
+    // decay weights b g^(t-s) of this lane's P^T elements (zero for s > t)
+    constexpr bool PREW = DECAY && F::OCC == 1;
+    float dw[PREW ? 4 * STRIPS : 1];
+    if constexpr (PREW) {
+#pragma unroll
+      for (int sb = 0; sb < STRIPS; ++sb)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int s = 16 * sb + 4 * g + rr;
+          dw[4 * sb + rr] = s <= t ? dk.b * gp[t - s] : 0.f;
+        }
+    }
+    constexpr int NJW = (NJ + WPS - 1) / WPS;
+    const int nch2 = (nch + NB2 - 1) / NB2 * NB2;
+    for (int c0 = 0; c0 < nch2; c0 += NB2) {
+#pragma unroll
+      for (int b = 0; b < NB2; ++b) {
+        const int c = c0 + b;
+        const int cur = NB2 % 2 == 0 ? (b & 1) : (c & 1), nxt = cur ^ 1;
+        const int64_t row0 = start + c * C;
+        const int rows =
+            c < nch ? static_cast<int>(min<int64_t>(C, end - row0)) : 0;
+        const T *sQc = sQ + cur * F::SQ;
+        // resident keys: chunk c's phi(K) in slot c (padding chunks read a
+        // stale slot; their outputs are dropped)
+        const T *sKc = resident ? sK + min(c, F::KS - 1) * F::SQ
+                                : sK + cur * F::SQ;
+        const T *sKwc = sKw + cur * F::SQ;
+        const T *sVc = sV + cur * F::SV;
+        const T *sSTc = CAUSAL ? sST + cur * F::SST : sST;
+
+        // ---- readout of strip tb ----
+        Frag<T> qf[DFP / 32];
+#pragma unroll
+        for (int kq = 0; kq < DFP / 32; ++kq)
+          load_frag8(qf[kq], sQc + t * LQ + 32 * kq + 8 * g);
+        Frag<T> pf[NPK];
+        if constexpr (CAUSAL) {
+          f32x4 pt[STRIPS];
+#pragma unroll
+          for (int sb = 0; sb < STRIPS; ++sb) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kq = 0; kq < DFP / 32; ++kq) {
+              Frag<T> fa;
+              load_frag8(fa, sKc + (16 * sb + li) * LQ + 32 * kq + 8 * g);
+              acc = mma(fa, qf[kq], acc);
+            }
+            if (DECAY) {
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) {
+                const int s = 16 * sb + 4 * g + rr;
+                if (PREW) acc[rr] *= dw[4 * sb + rr];
+                else acc[rr] = s <= t ? acc[rr] * (dk.b * gp[s <= t ? t - s : 0])
+                                      : 0.f;
+              }
+            }
+            pt[sb] = acc;
+          }
+#pragma unroll
+          for (int kp = 0; kp < NPK; ++kp) {
+            frag_from_acc(pf[kp], pt[2 * kp],
+                          2 * kp + 1 < STRIPS ? pt[2 * kp + 1]
+                                              : f32x4{0.f, 0.f, 0.f, 0.f});
+            if (!DECAY) frag_mask(pf[kp], pm[kp]);
+          }
+        }
+        // This wave's column blocks: vblock(jj) = jh + WPS jj for jj < NJW,
+        // then the ones block NJ (index NJW); their V^T fragments (split
+        // assignment) are loaded once and, where the wave's state tiles are
+        // the same blocks (SHARE), also serve the state update.
+        auto vblock = [&](int jj) {
+          return jj < NJW ? min(jh + WPS * jj, NJ) : NJ;
+        };
+        Frag<T> vf[CAUSAL ? NJW + 1 : 1][NPK];
+        if constexpr (CAUSAL) {
+#pragma unroll
+          for (int jj = 0; jj <= NJW; ++jj)
+#pragma unroll
+            for (int kp = 0; kp < NPK; ++kp)
+              load_frag_tr44(vf[jj][kp], sVc, LV, 32 * kp, 16 * vblock(jj), g,
+                             li);
+        }
+        // column block vblock(jj) of num^T = V^T P^T + g^(t+1) S^T Q'^T (the
+        // ones block: its first row is the denominator)
+        auto block = [&](int jj) {
+          const int jb = vblock(jj);
+          f32x4 an = {0.f, 0.f, 0.f, 0.f}, ai = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (CAUSAL) {
+#pragma unroll
+            for (int kp = 0; kp < NPK; ++kp) an = mma(vf[jj][kp], pf[kp], an);
+          }
+#pragma unroll
+          for (int kq = 0; kq < DFP / 32; ++kq) {
+            Frag<T> fa;
+            load_frag8(fa, sSTc + (16 * jb + li) * LQ + 32 * kq + 8 * g);
+            ai = mma(fa, qf[kq], ai);
+          }
+          return an + gt * ai;
+        };
+        const float rden = 1.f / __shfl(block(NJW)[0], li);
+#pragma unroll
+        for (int jj = 0; jj < NJW; ++jj) {
+          const f32x4 o = block(jj) * rden;
+          // o[rr]: column j = 16 jb + 4 g + rr of output row t; rows past
+          // the end (and blocks past the last) go to the discard word
+          const int jb = jh + WPS * jj;
+          T *dst = (NJ % WPS == 0 || jb < NJ) && t < rows
+                       ? ob + (row0 + t) * D + 16 * jb + 4 * g
+                       : reinterpret_cast<T *>(la_discard);
+          store4(dst, o[0], o[1], o[2], o[3]);
+        }
+
+        if constexpr (CAUSAL) {
+          // ---- state update: S <- g^r S + (w.K')^T [V | 1] ----
+          // (also after the last chunk and on padding chunks, whose keys
+          // are zero: the state then only matters when it is handed out)
+          const T *sKu = DECAY ? sKwc : sKc;
+          const float gr = DECAY ? gp[rows] : 1.f;
+          // resident keys: a padding chunk reads a stale slot, so its keys
+          // are dropped (elsewhere they were staged as zeros)
+          const unsigned kmask = RES && c >= nch ? 0u : ~0u;
+          if constexpr (F::NF == STRIPS && F::NF < kWaves) {
+            // tile (w % NF, tile_jb(w, m)) uses column block vblock(m)
+            static_assert(F::FPW == 1 && F::JPW <= NJW + 1, "tile layout");
+            Frag<T> af[NPK];
+#pragma unroll
+            for (int kp = 0; kp < NPK; ++kp) {
+              load_frag_tr44(af[kp], sKu, LQ, 32 * kp, 16 * tile_fb<F>(w, 0), g,
+                             li);
+              if (RES) frag_mask(af[kp], u32x4{kmask, kmask, kmask, kmask});
+            }
+#pragma unroll
+            for (int m = 0; m < F::JPW; ++m) {
+              f32x4 acc = S[m] * gr;
+#pragma unroll
+              for (int kp = 0; kp < NPK; ++kp) acc = mma(af[kp], vf[m][kp], acc);
+              S[m] = acc;
+            }
+          } else {
+            state_update<F>(S, sKu, sVc, gr, w, g, li, kmask);
+          }
+        }
+        // ---- chunk c + 1 into the other set; its ring slot reloaded ----
+        {
+          const int cn = c + 1, bn = (b + 1) % NB2;
+          const int rows_n =
+              cn < nch
+                  ? static_cast<int>(min<int64_t>(C, end - (start + cn * C)))
+                  : 0;
+          stage_queries<T, DF, C, LQ, ELU>(rq[bn], sQ + nxt * F::SQ, tid);
+          if (CAUSAL) {
+            if (!resident)
+              stage_keys<T, DF, C, LQ, DECAY, true, ELU>(
+                  rk2[bn], sK + nxt * F::SQ, sKw + nxt * F::SQ, gp, dk.b,
+                  rows_n, tid);
+            stage_values<T, D, C, LV>(rv2[bn], sV + nxt * F::SV, tid);
+          }
+          const int cr = cn + NB2 < nch ? cn + NB2 : nch - 1;
+          const int64_t r2 = start + cr * C;
+          const int rows2 = static_cast<int>(min<int64_t>(C, end - r2));
+          rq[bn].load(qb, r2, rows2, tid);
+          if (CAUSAL) {
+            if (!resident) rk2[bn].load(kb, r2, rows2, tid);
+            rv2[bn].load(vb, r2, rows2, tid);
+          }
+        }
+        if (CAUSAL) publish_state<F>(S, sST + nxt * F::SST, w, g, li);
+        __syncthreads();
+      }
+    }
+  } else {
   // the entering state as a T copy of S^T for the readout
   publish_state<F>(S, sST, w, g, li);
 
@@ -895,6 +1206,7 @@ void la_fwd_kernel(FwdArgs a) {
         __syncthreads();  // before the next chunk overwrites the tiles
       }
     }
+  }
   }
 
   // The state after the unit's last position (causal: after the last chunk's

@@ -21,11 +21,19 @@ struct FwdVariant {
     return reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, false, true, DECAY, MAP>);
   }
 
+  // Resident-key instance (causal, several segments of at most KRES chunks).
+  static const void *kernel_res() {
+    if constexpr (F::KRES > 0)
+      return reinterpret_cast<const void *>(
+          &la_fwd_kernel<T, D, DF, true, true, DECAY, MAP, true>);
+    return kernel(true, true);
+  }
+
   // Raise the dynamic-LDS limit of every instance once (above 64 KiB).
   static hipError_t set_lds() {
     static const hipError_t once = [] {
       for (const void *k : {kernel(true, true), kernel(true, false),
-                            kernel(false, true)}) {
+                            kernel(false, true), kernel_res()}) {
         const hipError_t e = hipFuncSetAttribute(
             k, hipFuncAttributeMaxDynamicSharedMemorySize,
             static_cast<int>(F::lds_bytes));
@@ -80,12 +88,21 @@ struct FwdVariant {
     if (causal) {
       // One segment: no exchange.  Several: segments are numbered in start
       // order, so a plain launch cannot deadlock.
-      if (a.nseg == 1)
+      if (a.nseg == 1) {
         hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, true, false, DECAY, MAP>),
                            grid, block, F::lds_bytes, s, a);
-      else
-        hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, true, true, DECAY, MAP>),
-                           grid, block, F::lds_bytes, s, a);
+        return hipGetLastError();
+      }
+      if constexpr (F::KRES > 0) {
+        if (a.seg_len <= static_cast<int64_t>(F::KRES) * F::C) {
+          hipLaunchKernelGGL(
+              (la_fwd_kernel<T, D, DF, true, true, DECAY, MAP, true>), grid,
+              block, F::lds_bytes, s, a);
+          return hipGetLastError();
+        }
+      }
+      hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, true, true, DECAY, MAP>),
+                         grid, block, F::lds_bytes, s, a);
       return hipGetLastError();
     }
     if (a.nseg == 1) {  // non-causal, one segment: no exchange executes
@@ -139,11 +156,10 @@ struct FwdRunner {
     if constexpr (!P::fits) {
       return nullptr;
     } else {
-      static_assert(P::OCC == Q::OCC, "one split for both variants");
       // the split is planned with P's chunk length; segments must hold whole
       // chunks of the decayed variant too
       static_assert(!Q::fits || P::C % Q::C == 0, "chunk lengths compatible");
-      static const FwdOps o = {P::C, P::SLOT, Q::fits, P::OCC, &run};
+      static const FwdOps o = {P::C, P::SLOT, Q::fits, &run};
       return &o;
     }
   }

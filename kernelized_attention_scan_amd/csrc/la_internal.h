@@ -60,7 +60,6 @@ struct FwdOps {
   int C;              // chunk rows
   int slot_floats;    // floats per fp32 state slot
   bool decay_ok;      // the decayed variant fits in LDS too
-  int occ;            // workgroups per compute unit the kernels are built for
   // Enqueue the fused forward.
   hipError_t (*run)(const FwdArgs &args, int64_t units, int causal,
                     hipStream_t stream);
