@@ -642,124 +642,100 @@ void la_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int i = 0; i < TW; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Chunk helpers: valid rows of chunk c (0 past the end), the chunk a ring
+  // load fetches for chunk c (clamped to the last one), and the tile set
+  // chunk c uses (c % 2 with two sets).
+  auto rows_of = [&](int c) -> int {
+    return c < nch ? static_cast<int>(min<int64_t>(C, end - (start + c * C)))
+                   : 0;
+  };
+  auto clamp_chunk = [&](int c) -> int { return c < nch ? c : nch - 1; };
+  auto set_of = [&](int c) -> int { return F::NBUF == 2 ? (c & 1) : 0; };
+
   // Phase-2 register ring, first revolution; in the segmented kernel these
   // loads are issued once the aggregate is published and overlap the wait.
   Slab<T, QW, C> rq[NB2], rk2[NB2];
   Slab<T, D, C> rv2[NB2];
-  auto ring2_first = [&]() {
-#pragma unroll
-    for (int b = 0; b < NB2; ++b) {
-      const int cl = b < nch ? b : nch - 1;
-      const int64_t r0 = start + cl * C;
-      const int rows = static_cast<int>(min<int64_t>(C, end - r0));
-      rq[b].load(qb, r0, rows, tid);
-      if (CAUSAL) {
-        if (!resident) rk2[b].load(kb, r0, rows, tid);
-        rv2[b].load(vb, r0, rows, tid);
-      }
+  auto load2 = [&](int c, Slab<T, QW, C> &sq, Slab<T, QW, C> &sk,
+                   Slab<T, D, C> &sv) {
+    const int cl = clamp_chunk(c);
+    const int64_t r0 = start + cl * C;
+    const int rows = rows_of(cl);
+    sq.load(qb, r0, rows, tid);
+    if (CAUSAL) {
+      if (!resident) sk.load(kb, r0, rows, tid);
+      sv.load(vb, r0, rows, tid);
     }
   };
+  auto ring2_first = [&]() {
+#pragma unroll
+    for (int b = 0; b < NB2; ++b) load2(b, rq[b], rk2[b], rv2[b]);
+  };
 
+  // The loops below run whole revolutions of their register ring (padding
+  // chunks past nch have zero keys and store nothing) and stage chunk c + 1
+  // while chunk c is multiplied.  With two tile sets (NBUF == 2) they do so
+  // concurrently, with one barrier per chunk; with one set a barrier
+  // separates the two.  The fused Performer map adds a step between staging
+  // the raw rows and using the features.
   if constexpr (MULTI) {
     // ---------------- phase 1: segment aggregate from K, V ----------------
     // (not for the last causal segment, whose aggregate no other segment
     // needs, unless it keeps its keys resident)
     if (!CAUSAL || seg + 1 < a.nseg || RES) {
-    Slab<T, QW, C> rk[NB1];
-    Slab<T, D, C> rv[NB1];
-#pragma unroll
-    for (int b = 0; b < NB1; ++b) {
-      const int cl = b < nch ? b : nch - 1;
-      const int64_t r0 = start + cl * C;
-      const int rows = static_cast<int>(min<int64_t>(C, end - r0));
-      rk[b].load(kb, r0, rows, tid);
-      rv[b].load(vb, r0, rows, tid);
-    }
-    __syncthreads();  // gp and the constant tile parts ready
-    const int nch1 = (nch + NB1 - 1) / NB1 * NB1;
-    if constexpr (F::PIPE) {
-      // Chunk c + 1 is staged into set (c + 1) % 2 while the state update of
-      // chunk c reads set c % 2: one barrier per chunk.  Resident keys go to
-      // slot c; padding chunks (past nch, zero keys) to the unused sQ.
-      auto keys1 = [&](int c) -> T * {
-        if (resident) return c < nch ? sK + c * F::SQ : sQ + (c & 1) * F::SQ;
-        return sK + (c & 1) * F::SQ;
+      Slab<T, QW, C> rk[NB1];
+      Slab<T, D, C> rv[NB1];
+      auto load1 = [&](int c, Slab<T, QW, C> &sk, Slab<T, D, C> &sv) {
+        const int cl = clamp_chunk(c);
+        sk.load(kb, start + cl * C, rows_of(cl), tid);
+        sv.load(vb, start + cl * C, rows_of(cl), tid);
       };
-      stage_keys<T, DF, C, LQ, DECAY, false, ELU>(
-          rk[0], keys1(0), sKw, gp, dk.b,
-          static_cast<int>(min<int64_t>(C, end - start)), tid);
-      stage_values<T, D, C, LV>(rv[0], sV, tid);
-      {
-        const int cn = NB1 < nch ? NB1 : nch - 1;
-        const int64_t r2 = start + cn * C;
-        const int rows2 = static_cast<int>(min<int64_t>(C, end - r2));
-        rk[0].load(kb, r2, rows2, tid);
-        rv[0].load(vb, r2, rows2, tid);
-      }
-      __syncthreads();
-      for (int c0 = 0; c0 < nch1; c0 += NB1) {
 #pragma unroll
-        for (int b = 0; b < NB1; ++b) {
-          const int c = c0 + b;
-          const int cur = NB1 % 2 == 0 ? (b & 1) : (c & 1), nxt = cur ^ 1;
-          const int rows =
-              c < nch ? static_cast<int>(min<int64_t>(C, end - (start + c * C)))
-                      : 0;
-          state_update<F>(S, DECAY ? sKw + cur * F::SQ : keys1(c),
-                          sV + cur * F::SV, DECAY ? gp[rows] : 1.f, w, g, li);
-          const int cn = c + 1, bn = (b + 1) % NB1;
-          const int rows_n =
-              cn < nch
-                  ? static_cast<int>(min<int64_t>(C, end - (start + cn * C)))
-                  : 0;
-          stage_keys<T, DF, C, LQ, DECAY, false, ELU>(
-              rk[bn], keys1(cn), sKw + nxt * F::SQ, gp, dk.b, rows_n, tid);
-          stage_values<T, D, C, LV>(rv[bn], sV + nxt * F::SV, tid);
-          {
-            const int cr = cn + NB1 < nch ? cn + NB1 : nch - 1;
-            const int64_t r2 = start + cr * C;
-            const int rows2 = static_cast<int>(min<int64_t>(C, end - r2));
-            rk[bn].load(kb, r2, rows2, tid);
-            rv[bn].load(vb, r2, rows2, tid);
-          }
-          __syncthreads();
-        }
-      }
-    } else
-    for (int c0 = 0; c0 < nch1; c0 += NB1) {
-#pragma unroll
-      for (int b = 0; b < NB1; ++b) {
-        const int c = c0 + b;
-        const int64_t r0 = start + c * C;
-        const int rows =
-            c < nch ? static_cast<int>(min<int64_t>(C, end - r0)) : 0;
-        // resident keys: chunk c's phi(K) in slot c (c < KRES: one
-        // revolution covers a resident segment)
-        T *sKc = resident ? sK + c * F::SQ : sK;
+      for (int b = 0; b < NB1; ++b) load1(b, rk[b], rv[b]);
+      // phi(K) of chunk c: its resident slot (padding chunks: the unused
+      // sQ), else the sK slot of its set
+      auto keys1 = [&](int c) -> T * {
+        if (resident)
+          return c < nch ? sK + c * F::SQ : sQ + set_of(c) * F::SQ;
+        return sK + set_of(c) * F::SQ;
+      };
+      auto stage1 = [&](int c, const Slab<T, QW, C> &sk,
+                        const Slab<T, D, C> &sv) {
         if constexpr (PF)
-          stage_values<T, D, C, LX>(rk[b], sXk, tid);
+          stage_values<T, D, C, LX>(sk, sXk, tid);
         else
           stage_keys<T, DF, C, LQ, DECAY, false, ELU>(
-              rk[b], sKc, DECAY ? sKw : sKc, gp, dk.b, rows, tid);
-        stage_values<T, D, C, LV>(rv[b], sV, tid);
-        __syncthreads();
-        {
-          const int cn = c + NB1 < nch ? c + NB1 : nch - 1;
-          const int64_t r2 = start + cn * C;
-          const int rows2 = static_cast<int>(min<int64_t>(C, end - r2));
-          rk[b].load(kb, r2, rows2, tid);
-          rv[b].load(vb, r2, rows2, tid);
-        }
+              sk, keys1(c), sKw + set_of(c) * F::SQ, gp, dk.b, rows_of(c),
+              tid);
+        stage_values<T, D, C, LV>(sv, sV + set_of(c) * F::SV, tid);
+      };
+      auto features1 = [&](int c) {
         if constexpr (PF) {
           performer_features<F, T, false, true, DECAY, false>(
-              wf, sXq, sXk, sQ, sK, sKw, gp, dk.b, rows, w, g, li);
+              wf, sXq, sXk, sQ, sK, sKw, gp, dk.b, rows_of(c), w, g, li);
           __syncthreads();
         }
-        state_update<F>(S, DECAY ? sKw : sKc, sV, DECAY ? gp[rows] : 1.f, w,
-                        g, li);
-        __syncthreads();
+      };
+      __syncthreads();  // gp and the constant tile parts ready
+      stage1(0, rk[0], rv[0]);
+      load1(NB1, rk[0], rv[0]);
+      __syncthreads();
+      features1(0);
+      for (int c0 = 0; c0 < nch; c0 += NB1) {
+#pragma unroll
+        for (int b = 0; b < NB1; ++b) {
+          const int c = c0 + b, bn = (b + 1) % NB1;
+          const int sc = F::NBUF == 2 && NB1 % 2 == 0 ? (b & 1) : set_of(c);
+          state_update<F>(S, DECAY ? sKw + sc * F::SQ : keys1(c),
+                          sV + sc * F::SV, DECAY ? gp[rows_of(c)] : 1.f, w, g,
+                          li);
+          if (F::NBUF == 1) __syncthreads();
+          stage1(c + 1, rk[bn], rv[bn]);
+          load1(c + 1 + NB1, rk[bn], rv[bn]);
+          __syncthreads();
+          features1(c + 1);
+        }
       }
-    }
     }
     // With one segment the aggregate is already the state every row needs
     // (non-causal total).  With several, segment s combines the aggregates
@@ -821,252 +797,62 @@ void la_fwd_kernel(FwdArgs a) {
     } else {
       ring2_first();
     }
+  } else {
+    ring2_first();
   }
 
-  if constexpr (!MULTI) ring2_first();
-  if constexpr (F::PIPE) {
-    // ------------ phase 2: chunk loop, software-pipelined ------------
-    // Chunk c is read out from set c % 2 while chunk c + 1 is mapped and
-    // staged into the other set and the state after chunk c is published
-    // into the other S^T copy: one barrier per chunk.  Every wave runs the
-    // same instructions (masks instead of branches on its strip), so a chunk
-    // is one straight block that the compiler can interleave.
-    __syncthreads();  // gp and the constant tile parts ready, phase 1 done
-    publish_state<F>(S, sST, w, g, li);
-    stage_queries<T, DF, C, LQ, ELU>(rq[0], sQ, tid);
-    if (CAUSAL) {
-      if (!resident)
-        stage_keys<T, DF, C, LQ, DECAY, true, ELU>(
-            rk2[0], sK, sKw, gp, dk.b,
-            static_cast<int>(min<int64_t>(C, end - start)), tid);
-      stage_values<T, D, C, LV>(rv2[0], sV, tid);
-    }
-    {
-      const int cr = NB2 < nch ? NB2 : nch - 1;
-      const int64_t r2 = start + cr * C;
-      const int rows2 = static_cast<int>(min<int64_t>(C, end - r2));
-      rq[0].load(qb, r2, rows2, tid);
-      if (CAUSAL) {
-        if (!resident) rk2[0].load(kb, r2, rows2, tid);
-        rv2[0].load(vb, r2, rows2, tid);
-      }
-    }
-    __syncthreads();
-
-    const int tb = w % STRIPS;    // this wave's output strip
-    const int jh = w / STRIPS;    // and its share of the column blocks
-    const int t = 16 * tb + li;   // the output row this lane normalises
-    const float gt = CAUSAL ? gp[t + 1] : 1.f;
-    // Causal mask of each P^T fragment pair kp: element e is key
-    // s = 16 (2 kp + e / 4) + 4 g + e % 4, kept when s <= t.
-    constexpr int NPK = (STRIPS + 1) / 2;
-    u32x4 pm[NPK];
-#pragma unroll
-    for (int kp = 0; kp < NPK; ++kp) {
-      pm[kp] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int s = 16 * (2 * kp + e / 4) + 4 * g + e % 4;
-        if (s <= t) pm[kp][e / 2] |= 0xffffu << (16 * (e % 2));
-      }
-    }
-    // decay weights b g^(t-s) of this lane's P^T elements (zero for s > t)
-    constexpr bool PREW = DECAY && F::OCC == 1;
-    float dw[PREW ? 4 * STRIPS : 1];
-    if constexpr (PREW) {
-#pragma unroll
-      for (int sb = 0; sb < STRIPS; ++sb)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int s = 16 * sb + 4 * g + rr;
-          dw[4 * sb + rr] = s <= t ? dk.b * gp[t - s] : 0.f;
-        }
-    }
-    constexpr int NJW = (NJ + WPS - 1) / WPS;
-    const int nch2 = (nch + NB2 - 1) / NB2 * NB2;
-    for (int c0 = 0; c0 < nch2; c0 += NB2) {
-#pragma unroll
-      for (int b = 0; b < NB2; ++b) {
-        const int c = c0 + b;
-        const int cur = NB2 % 2 == 0 ? (b & 1) : (c & 1), nxt = cur ^ 1;
-        const int64_t row0 = start + c * C;
-        const int rows =
-            c < nch ? static_cast<int>(min<int64_t>(C, end - row0)) : 0;
-        const T *sQc = sQ + cur * F::SQ;
-        // resident keys: chunk c's phi(K) in slot c (padding chunks read a
-        // stale slot; their outputs are dropped)
-        const T *sKc = resident ? sK + min(c, F::KS - 1) * F::SQ
-                                : sK + cur * F::SQ;
-        const T *sKwc = sKw + cur * F::SQ;
-        const T *sVc = sV + cur * F::SV;
-        const T *sSTc = CAUSAL ? sST + cur * F::SST : sST;
-
-        // ---- readout of strip tb ----
-        Frag<T> qf[DFP / 32];
-#pragma unroll
-        for (int kq = 0; kq < DFP / 32; ++kq)
-          load_frag8(qf[kq], sQc + t * LQ + 32 * kq + 8 * g);
-        Frag<T> pf[NPK];
-        if constexpr (CAUSAL) {
-          f32x4 pt[STRIPS];
-#pragma unroll
-          for (int sb = 0; sb < STRIPS; ++sb) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kq = 0; kq < DFP / 32; ++kq) {
-              Frag<T> fa;
-              load_frag8(fa, sKc + (16 * sb + li) * LQ + 32 * kq + 8 * g);
-              acc = mma(fa, qf[kq], acc);
-            }
-            if (DECAY) {
-#pragma unroll
-              for (int rr = 0; rr < 4; ++rr) {
-                const int s = 16 * sb + 4 * g + rr;
-                if (PREW) acc[rr] *= dw[4 * sb + rr];
-                else acc[rr] = s <= t ? acc[rr] * (dk.b * gp[s <= t ? t - s : 0])
-                                      : 0.f;
-              }
-            }
-            pt[sb] = acc;
-          }
-#pragma unroll
-          for (int kp = 0; kp < NPK; ++kp) {
-            frag_from_acc(pf[kp], pt[2 * kp],
-                          2 * kp + 1 < STRIPS ? pt[2 * kp + 1]
-                                              : f32x4{0.f, 0.f, 0.f, 0.f});
-            if (!DECAY) frag_mask(pf[kp], pm[kp]);
-          }
-        }
-        // This wave's column blocks: vblock(jj) = jh + WPS jj for jj < NJW,
-        // then the ones block NJ (index NJW); their V^T fragments (split
-        // assignment) are loaded once and, where the wave's state tiles are
-        // the same blocks (SHARE), also serve the state update.
-        auto vblock = [&](int jj) {
-          return jj < NJW ? min(jh + WPS * jj, NJ) : NJ;
-        };
-        Frag<T> vf[CAUSAL ? NJW + 1 : 1][NPK];
-        if constexpr (CAUSAL) {
-#pragma unroll
-          for (int jj = 0; jj <= NJW; ++jj)
-#pragma unroll
-            for (int kp = 0; kp < NPK; ++kp)
-              load_frag_tr44(vf[jj][kp], sVc, LV, 32 * kp, 16 * vblock(jj), g,
-                             li);
-        }
-        // column block vblock(jj) of num^T = V^T P^T + g^(t+1) S^T Q'^T (the
-        // ones block: its first row is the denominator)
-        auto block = [&](int jj) {
-          const int jb = vblock(jj);
-          f32x4 an = {0.f, 0.f, 0.f, 0.f}, ai = {0.f, 0.f, 0.f, 0.f};
-          if constexpr (CAUSAL) {
-#pragma unroll
-            for (int kp = 0; kp < NPK; ++kp) an = mma(vf[jj][kp], pf[kp], an);
-          }
-#pragma unroll
-          for (int kq = 0; kq < DFP / 32; ++kq) {
-            Frag<T> fa;
-            load_frag8(fa, sSTc + (16 * jb + li) * LQ + 32 * kq + 8 * g);
-            ai = mma(fa, qf[kq], ai);
-          }
-          return an + gt * ai;
-        };
-        const float rden = 1.f / __shfl(block(NJW)[0], li);
-#pragma unroll
-        for (int jj = 0; jj < NJW; ++jj) {
-          const f32x4 o = block(jj) * rden;
-          // o[rr]: column j = 16 jb + 4 g + rr of output row t; rows past
-          // the end (and blocks past the last) go to the discard word
-          const int jb = jh + WPS * jj;
-          T *dst = (NJ % WPS == 0 || jb < NJ) && t < rows
-                       ? ob + (row0 + t) * D + 16 * jb + 4 * g
-                       : reinterpret_cast<T *>(la_discard);
-          store4(dst, o[0], o[1], o[2], o[3]);
-        }
-
-        if constexpr (CAUSAL) {
-          // ---- state update: S <- g^r S + (w.K')^T [V | 1] ----
-          // (also after the last chunk and on padding chunks, whose keys
-          // are zero: the state then only matters when it is handed out)
-          const T *sKu = DECAY ? sKwc : sKc;
-          const float gr = DECAY ? gp[rows] : 1.f;
-          // resident keys: a padding chunk reads a stale slot, so its keys
-          // are dropped (elsewhere they were staged as zeros)
-          const unsigned kmask = RES && c >= nch ? 0u : ~0u;
-          if constexpr (F::NF == STRIPS && F::NF < kWaves) {
-            // tile (w % NF, tile_jb(w, m)) uses column block vblock(m)
-            static_assert(F::FPW == 1 && F::JPW <= NJW + 1, "tile layout");
-            Frag<T> af[NPK];
-#pragma unroll
-            for (int kp = 0; kp < NPK; ++kp) {
-              load_frag_tr44(af[kp], sKu, LQ, 32 * kp, 16 * tile_fb<F>(w, 0), g,
-                             li);
-              if (RES) frag_mask(af[kp], u32x4{kmask, kmask, kmask, kmask});
-            }
-#pragma unroll
-            for (int m = 0; m < F::JPW; ++m) {
-              f32x4 acc = S[m] * gr;
-#pragma unroll
-              for (int kp = 0; kp < NPK; ++kp) acc = mma(af[kp], vf[m][kp], acc);
-              S[m] = acc;
-            }
-          } else {
-            state_update<F>(S, sKu, sVc, gr, w, g, li, kmask);
-          }
-        }
-        // ---- chunk c + 1 into the other set; its ring slot reloaded ----
-        {
-          const int cn = c + 1, bn = (b + 1) % NB2;
-          const int rows_n =
-              cn < nch
-                  ? static_cast<int>(min<int64_t>(C, end - (start + cn * C)))
-                  : 0;
-          stage_queries<T, DF, C, LQ, ELU>(rq[bn], sQ + nxt * F::SQ, tid);
-          if (CAUSAL) {
-            if (!resident)
-              stage_keys<T, DF, C, LQ, DECAY, true, ELU>(
-                  rk2[bn], sK + nxt * F::SQ, sKw + nxt * F::SQ, gp, dk.b,
-                  rows_n, tid);
-            stage_values<T, D, C, LV>(rv2[bn], sV + nxt * F::SV, tid);
-          }
-          const int cr = cn + NB2 < nch ? cn + NB2 : nch - 1;
-          const int64_t r2 = start + cr * C;
-          const int rows2 = static_cast<int>(min<int64_t>(C, end - r2));
-          rq[bn].load(qb, r2, rows2, tid);
-          if (CAUSAL) {
-            if (!resident) rk2[bn].load(kb, r2, rows2, tid);
-            rv2[bn].load(vb, r2, rows2, tid);
-          }
-        }
-        if (CAUSAL) publish_state<F>(S, sST + nxt * F::SST, w, g, li);
-        __syncthreads();
-      }
-    }
-  } else {
-  // the entering state as a T copy of S^T for the readout
-  publish_state<F>(S, sST, w, g, li);
-
   // ---------------- phase 2: chunk loop ----------------
-  __syncthreads();  // gp, sST and the constant tile parts ready
+  // Every wave runs the same instructions (masks instead of branches on its
+  // output strip), so a chunk is one straight block the compiler can
+  // interleave.
+  auto stage2 = [&](int c, const Slab<T, QW, C> &sq, const Slab<T, QW, C> &sk,
+                    const Slab<T, D, C> &sv) {
+    const int sc = set_of(c);
+    if constexpr (PF) {
+      stage_values<T, D, C, LX>(sq, sXq, tid);
+      if (CAUSAL) stage_values<T, D, C, LX>(sk, sXk, tid);
+    } else {
+      stage_queries<T, DF, C, LQ, ELU>(sq, sQ + sc * F::SQ, tid);
+      if (CAUSAL && !resident)
+        stage_keys<T, DF, C, LQ, DECAY, true, ELU>(
+            sk, sK + sc * F::SQ, sKw + sc * F::SQ, gp, dk.b, rows_of(c), tid);
+    }
+    if (CAUSAL) stage_values<T, D, C, LV>(sv, sV + sc * F::SV, tid);
+  };
+  auto features2 = [&](int c) {
+    if constexpr (PF) {
+      performer_features<F, T, true, CAUSAL, DECAY, true>(
+          wf, sXq, sXk, sQ, sK, sKw, gp, dk.b, rows_of(c), w, g, li);
+      __syncthreads();
+    }
+  };
+  __syncthreads();  // gp and the constant tile parts ready, phase 1 done
+  publish_state<F>(S, sST, w, g, li);  // the entering state, set 0
+  stage2(0, rq[0], rk2[0], rv2[0]);
+  load2(NB2, rq[0], rk2[0], rv2[0]);
+  __syncthreads();
+  features2(0);
 
   const int tb = w % STRIPS;    // this wave's output strip
   const int jh = w / STRIPS;    // and its share of the column blocks
   const int t = 16 * tb + li;   // the output row this lane normalises
   const float gt = CAUSAL ? gp[t + 1] : 1.f;
-  // Causal mask of the P^T fragment pair that holds the diagonal strip
-  // (pair kd = tb / 2): element e is key s = 16 (2 kd + e / 4) + 4 g + e % 4,
-  // kept when s <= t.  Pairs below it need no mask, pairs above are never
-  // used.
-  u32x4 dmask = {0u, 0u, 0u, 0u};
-  if (CAUSAL && !DECAY) {
+  // Causal mask of each P^T fragment pair kp: element e is key
+  // s = 16 (2 kp + e / 4) + 4 g + e % 4, kept when s <= t.
+  constexpr int NPK = (STRIPS + 1) / 2;
+  u32x4 pm[NPK];
+#pragma unroll
+  for (int kp = 0; kp < NPK; ++kp) {
+    pm[kp] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int s = 16 * (2 * (tb >> 1) + e / 4) + 4 * g + e % 4;
-      if (s <= t) dmask[e / 2] |= 0xffffu << (16 * (e % 2));
+      const int s = 16 * (2 * kp + e / 4) + 4 * g + e % 4;
+      if (s <= t) pm[kp][e / 2] |= 0xffffu << (16 * (e % 2));
     }
   }
-  // Decay weights of this lane's P^T elements, b g^(t-s) for key
-  // s = 16 sb + 4 g + rr (zero above the diagonal), computed once where the
-  // registers allow (one workgroup per CU); else per chunk from the table.
+  // Decay weights b g^(t-s) of this lane's P^T elements (zero for s > t),
+  // computed once where the registers allow (one workgroup per CU), else
+  // per chunk from the table.
   constexpr bool PREW = DECAY && F::OCC == 1;
   float dw[PREW ? 4 * STRIPS : 1];
   if constexpr (PREW) {
@@ -1078,96 +864,102 @@ void la_fwd_kernel(FwdArgs a) {
         dw[4 * sb + rr] = s <= t ? dk.b * gp[t - s] : 0.f;
       }
   }
-  // resident keys: no K loads, no K staging; chunk c reads slot c
-  const int nch2 = (nch + NB2 - 1) / NB2 * NB2;
-  for (int c0 = 0; c0 < nch2; c0 += NB2) {
+  constexpr int NJW = (NJ + WPS - 1) / WPS;
+  for (int c0 = 0; c0 < nch; c0 += NB2) {
 #pragma unroll
     for (int b = 0; b < NB2; ++b) {
-      const int c = c0 + b;
+      const int c = c0 + b, bn = (b + 1) % NB2;
+      const int sc = F::NBUF == 2 && NB2 % 2 == 0 ? (b & 1) : set_of(c);
+      const int sn = F::NBUF == 2 ? sc ^ 1 : 0;
       const int64_t row0 = start + c * C;
-      const int rows =
-          c < nch ? static_cast<int>(min<int64_t>(C, end - row0)) : 0;
-      const bool last = c + 1 >= nch;
-      if constexpr (PF) {
-        stage_values<T, D, C, LX>(rq[b], sXq, tid);
-        if (CAUSAL) stage_values<T, D, C, LX>(rk2[b], sXk, tid);
-      } else {
-        stage_queries<T, DF, C, LQ, ELU>(rq[b], sQ, tid);
-        if (CAUSAL && !resident)
-          stage_keys<T, DF, C, LQ, DECAY, true, ELU>(rk2[b], sK, sKw, gp, dk.b,
-                                                     rows, tid);
-      }
-      if (CAUSAL) stage_values<T, D, C, LV>(rv2[b], sV, tid);
-      __syncthreads();  // operand tiles (fused Performer: raw rows) ready
-      {
-        const int cn = c + NB2 < nch ? c + NB2 : nch - 1;
-        const int64_t r2 = start + cn * C;
-        const int rows2 = static_cast<int>(min<int64_t>(C, end - r2));
-        rq[b].load(qb, r2, rows2, tid);
-        if (CAUSAL) {
-          if (!resident) rk2[b].load(kb, r2, rows2, tid);
-          rv2[b].load(vb, r2, rows2, tid);
-        }
-      }
-      T *sKc = resident ? sK + c * F::SQ : sK;  // this chunk's phi(K)
-      if constexpr (PF) {
-        performer_features<F, T, true, CAUSAL, DECAY, true>(
-            wf, sXq, sXk, sQ, sK, sKw, gp, dk.b, rows, w, g, li);
-        __syncthreads();  // q', k' tiles ready
-      }
+      const int rows = rows_of(c);
+      const T *sQc = sQ + sc * F::SQ;
+      // resident keys: chunk c's phi(K) in slot c (padding chunks read a
+      // stale slot; their outputs are dropped and their keys masked below)
+      const T *sKc = resident ? sK + min(c, F::KS - 1) * F::SQ
+                              : sK + sc * F::SQ;
+      const T *sKwc = sKw + sc * F::SQ;
+      const T *sVc = sV + sc * F::SV;
+      const T *sSTc = CAUSAL ? sST + sc * F::SST : sST;
 
       // ---- readout of strip tb: q' fragments, reused by every product ----
       Frag<T> qf[DFP / 32];
 #pragma unroll
       for (int kq = 0; kq < DFP / 32; ++kq)
-        load_frag8(qf[kq], sQ + t * LQ + 32 * kq + 8 * g);
-      f32x4 pt[STRIPS];
+        load_frag8(qf[kq], sQc + t * LQ + 32 * kq + 8 * g);
+      Frag<T> pf[NPK];
+      if constexpr (CAUSAL) {
+        f32x4 pt[STRIPS];
+        // Key strips above the diagonal strip only hold masked products:
+        // with wide features (d' >= 128) they are skipped (a branch on the
+        // wave's strip), else computed and masked (no branch).
+        constexpr bool SKIP = DFP >= 128;
 #pragma unroll
-      for (int sb = 0; sb < STRIPS; ++sb) {
-        pt[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (CAUSAL && sb <= tb) {
+        for (int sb = 0; sb < STRIPS; ++sb) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          if (!SKIP || sb <= tb) {
 #pragma unroll
-          for (int kq = 0; kq < DFP / 32; ++kq) {
-            Frag<T> fa;
-            load_frag8(fa, sKc + (16 * sb + li) * LQ + 32 * kq + 8 * g);
-            acc = mma(fa, qf[kq], acc);
+            for (int kq = 0; kq < DFP / 32; ++kq) {
+              Frag<T> fa;
+              load_frag8(fa, sKc + (16 * sb + li) * LQ + 32 * kq + 8 * g);
+              acc = mma(fa, qf[kq], acc);
+            }
           }
           // acc[rr] = q'_t . k'_s with s = 16 sb + 4 g + rr; with decay the
           // weights b g^(t-s), zero above the diagonal, are applied here,
-          // without it the diagonal is masked on the packed fragment below
+          // without it the causal mask is applied to the packed pairs
           if (DECAY) {
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
               const int s = 16 * sb + 4 * g + rr;
               if (PREW) acc[rr] *= dw[4 * sb + rr];
-              else acc[rr] = s <= t ? acc[rr] * (dk.b * gp[t - s]) : 0.f;
+              else acc[rr] = s <= t ? acc[rr] * (dk.b * gp[s <= t ? t - s : 0])
+                                    : 0.f;
             }
           }
           pt[sb] = acc;
         }
-      }
-      constexpr int NPK = (STRIPS + 1) / 2;
-      Frag<T> pf[NPK];
 #pragma unroll
-      for (int kp = 0; kp < NPK; ++kp) {
-        frag_from_acc(pf[kp], pt[2 * kp],
-                      2 * kp + 1 < STRIPS ? pt[2 * kp + 1]
-                                          : f32x4{0.f, 0.f, 0.f, 0.f});
-        if (CAUSAL && !DECAY && kp == (tb >> 1)) frag_mask(pf[kp], dmask);
+        for (int kp = 0; kp < NPK; ++kp) {
+          frag_from_acc(pf[kp], pt[2 * kp],
+                        2 * kp + 1 < STRIPS ? pt[2 * kp + 1]
+                                            : f32x4{0.f, 0.f, 0.f, 0.f});
+          if (!DECAY) frag_mask(pf[kp], pm[kp]);
+        }
       }
-      // Column block jb of num^T = V^T P^T + g^(t+1) S^T Q'^T.  Block NJ is
-      // the ones block: its first row is the denominator, sum_s P[t][s] +
-      // g^(t+1) q'_t . z, from the same rounded P and the same S copy as the
-      // numerators.
-      auto block = [&](int jb) {
+      // This wave's column blocks: vblock(jj) = jh + WPS jj for jj < NJW,
+      // then the ones block NJ (index NJW); their V^T fragments (split
+      // assignment) are loaded once and, where the wave's state tiles are
+      // the same blocks (SHARE), also serve the state update.
+      auto vblock = [&](int jj) {
+        return jj < NJW ? min(jh + WPS * jj, NJ) : NJ;
+      };
+      constexpr bool SHARE = CAUSAL && F::NF == STRIPS && F::NF < kWaves;
+      Frag<T> vf[SHARE ? NJW + 1 : 1][NPK];
+      if constexpr (SHARE) {
+#pragma unroll
+        for (int jj = 0; jj <= NJW; ++jj)
+#pragma unroll
+          for (int kp = 0; kp < NPK; ++kp)
+            load_frag_tr44(vf[jj][kp], sVc, LV, 32 * kp, 16 * vblock(jj), g,
+                           li);
+      }
+      // column block vblock(jj) of num^T = V^T P^T + g^(t+1) S^T Q'^T (the
+      // ones block: its first row is the denominator, sum_s P[t][s] +
+      // g^(t+1) q'_t . z, from the same rounded P and S copy as the
+      // numerators)
+      auto block = [&](int jj) {
+        const int jb = vblock(jj);
         f32x4 an = {0.f, 0.f, 0.f, 0.f}, ai = {0.f, 0.f, 0.f, 0.f};
-        if (CAUSAL) {
+        if constexpr (SHARE) {
+#pragma unroll
+          for (int kp = 0; kp < NPK; ++kp) an = mma(vf[jj][kp], pf[kp], an);
+        } else if constexpr (CAUSAL) {
 #pragma unroll
           for (int kp = 0; kp < NPK; ++kp) {
-            if (2 * kp <= tb) {
+            if (DFP < 128 || 2 * kp <= tb) {  // pairs above it are zero
               Frag<T> fa;
-              load_frag_tr44(fa, sV, LV, 32 * kp, 16 * jb, g, li);
+              load_frag_tr44(fa, sVc, LV, 32 * kp, 16 * jb, g, li);
               an = mma(fa, pf[kp], an);
             }
           }
@@ -1175,38 +967,61 @@ void la_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int kq = 0; kq < DFP / 32; ++kq) {
           Frag<T> fa;
-          load_frag8(fa, sST + (16 * jb + li) * LQ + 32 * kq + 8 * g);
+          load_frag8(fa, sSTc + (16 * jb + li) * LQ + 32 * kq + 8 * g);
           ai = mma(fa, qf[kq], ai);
         }
         return an + gt * ai;
       };
       // the denominator of row t sits in lane t of group 0
-      const float den = __shfl(block(NJ)[0], li);
-      const float rden = 1.f / den;
+      const float rden = 1.f / __shfl(block(NJW)[0], li);
 #pragma unroll
-      for (int jj = 0; jj < (NJ + WPS - 1) / WPS; ++jj) {
+      for (int jj = 0; jj < NJW; ++jj) {
+        const f32x4 o = block(jj) * rden;
+        // o[rr]: column j = 16 jb + 4 g + rr of output row t; rows past
+        // the end (and blocks past the last) go to the discard word
         const int jb = jh + WPS * jj;
-        if (jb < NJ) {
-          const f32x4 o = block(jb) * rden;
-          // o[rr]: column j = 16 jb + 4 g + rr of output row t
-          if (t < rows)
-            store4(ob + (row0 + t) * D + 16 * jb + 4 * g, o[0], o[1], o[2],
-                   o[3]);
-        }
+        T *dst = (NJ % WPS == 0 || jb < NJ) && t < rows
+                     ? ob + (row0 + t) * D + 16 * jb + 4 * g
+                     : reinterpret_cast<T *>(la_discard);
+        store4(dst, o[0], o[1], o[2], o[3]);
       }
 
-      // the last chunk updates the state only when it is handed out
-      if (CAUSAL && (!last || (keep_state && c + 1 == nch))) {
+      if constexpr (CAUSAL) {
         // ---- state update: S <- g^r S + (w.K')^T [V | 1] ----
-        state_update<F>(S, DECAY ? sKw : sKc, sV, DECAY ? gp[rows] : 1.f, w,
-                        g, li);
-        __syncthreads();  // all waves done reading sST and the chunk tiles
-        if (!last) publish_state<F>(S, sST, w, g, li);
-      } else {
-        __syncthreads();  // before the next chunk overwrites the tiles
+        // (also after the last chunk, where the state only matters when it
+        // is handed out, and on padding chunks, whose keys are zero)
+        const T *sKu = DECAY ? sKwc : sKc;
+        const float gr = DECAY ? gp[rows] : 1.f;
+        const unsigned kmask = RES && c >= nch ? 0u : ~0u;
+        if constexpr (SHARE) {
+          // tile (w % NF, tile_jb(w, m)) uses column block vblock(m)
+          static_assert(F::FPW == 1 && F::JPW <= NJW + 1, "tile layout");
+          Frag<T> af[NPK];
+#pragma unroll
+          for (int kp = 0; kp < NPK; ++kp) {
+            load_frag_tr44(af[kp], sKu, LQ, 32 * kp, 16 * tile_fb<F>(w, 0), g,
+                           li);
+            if (RES) frag_mask(af[kp], u32x4{kmask, kmask, kmask, kmask});
+          }
+#pragma unroll
+          for (int m = 0; m < F::JPW; ++m) {
+            f32x4 acc = S[m] * gr;
+#pragma unroll
+            for (int kp = 0; kp < NPK; ++kp) acc = mma(af[kp], vf[m][kp], acc);
+            S[m] = acc;
+          }
+        } else {
+          state_update<F>(S, sKu, sVc, gr, w, g, li, kmask);
+        }
       }
+      if (F::NBUF == 1) __syncthreads();  // the one tile set is free again
+      // ---- chunk c + 1 into its set; its ring slot reloaded ----
+      stage2(c + 1, rq[bn], rk2[bn], rv2[bn]);
+      load2(c + 1 + NB2, rq[bn], rk2[bn], rv2[bn]);
+      if (CAUSAL) publish_state<F>(S, sST + sn * F::SST, w, g, li);
+      __syncthreads();
+      features2(c + 1);
     }
-  }
   }
 
   // The state after the unit's last position (causal: after the last chunk's
