@@ -121,7 +121,7 @@ constexpr size_t fwd_lds_bytes(int c, int d, int df, bool decay, bool pf,
   const size_t sx = pf ? static_cast<size_t>(c) * lds_stride<T>(d) : 0;
   return sizeof(T) * (nbuf * (sq + (decay ? sq : 0) + sv + sst) +
                       kslots * sq + 2 * sx) +
-         sizeof(float) * (c + 2);
+         sizeof(float) * (c + 4);
 }
 
 // Largest power of two <= x, at most 8 (1 for x < 2).
@@ -453,20 +453,28 @@ __device__ __forceinline__ void publish_state(const f32x4 *S, T *sST, int w,
 
 // Exchange of segment aggregates between the workgroups of one (batch, head)
 // unit, through that unit's line of the synchronisation area (see
-// la_internal.h).  Aggregates are written with agent-scope atomic 64-bit
-// stores, which write through to the device's coherence point, so the
-// exchange needs no write-back of the L2 caches.  Publishing: every wave
-// waits until its aggregate stores have completed, then flag s is set.
-// Waiting: one wave polls the flags it needs (16 lanes, one line) and, once
-// all are set, acquires (invalidating stale cached lines); the aggregates are
-// then read with plain loads, which hit the L2 where the writers ran on the
-// same XCD.  Every
-// workgroup a wait depends on is running (causal: segment indices follow
-// start order; non-causal: cooperative launch).  The wait is bounded (a few
-// seconds): if the area were ever corrupt it sets the timeout word and lets
-// the kernel finish instead of hanging.  At its very end every workgroup
-// counts itself done; the last one clears the unit's line (flags, ticket,
-// count), so the area is zero again for the next launch.
+// la_internal.h).  Every workgroup a wait depends on is running (causal:
+// segment indices follow start order; non-causal: cooperative launch).
+//
+// The XCDs of an MI355X do not share their L2 caches.  Each segment records
+// the XCD it runs on in its unit's line when it starts.  A writer that finds
+// every segment of its unit recorded on its own XCD stores its aggregate
+// with plain stores, which land in that XCD's L2 (the L1 caches write
+// through); otherwise with agent-scope stores, which write through to the
+// device's coherence point.  The flag always goes to the coherence point,
+// and its value says which: 2 for this XCD's L2, 1 for the coherence point.
+// A reader polls the flags it needs at agent scope; once all are set it
+// invalidates its L1, and also its L2 when any writer wrote through (so no
+// stale line of an earlier launch hides that data), then reads the
+// aggregates with plain loads.  A writer uses its L2 only when every
+// segment of its unit, so every reader of it, runs on its XCD.
+//
+// Publishing: every wave waits until its aggregate stores have completed,
+// then flag s is set.  The waits are bounded (a few seconds): if the area
+// were ever corrupt they set the timeout word and let the kernel finish
+// instead of hanging.  At its very end every workgroup counts itself done;
+// the last one clears the unit's line (flags, ticket, count, XCD records),
+// so the area is zero again for the next launch.
 __device__ __forceinline__ void store_agent(float *p, const f32x4 &v) {
   typedef unsigned long long u64;
   __hip_atomic_store(reinterpret_cast<u64 *>(p),
@@ -477,13 +485,32 @@ __device__ __forceinline__ void store_agent(float *p, const f32x4 &v) {
                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void publish_flag(unsigned *line, int seg) {
+// The XCD this workgroup runs on as a 4-bit record, 1 + its id (hardware
+// register XCC_ID, bits 0..3); 15 stands for "unknown" and never matches.
+__device__ __forceinline__ unsigned xcc_record() {
+  const unsigned x = __builtin_amdgcn_s_getreg(20 | (3 << 11)) & 0xfu;
+  return x < 14 ? x + 1 : 15;
+}
+
+// Nibbles [0, n) of the record pair (r0: segments 0..7, r1: 8..15) all
+// equal to v.
+__device__ __forceinline__ bool records_match(unsigned r0, unsigned r1, int n,
+                                              unsigned v) {
+  const int n0 = n < 8 ? n : 8, n1 = n > 8 ? n - 8 : 0;
+  const unsigned m0 = n0 == 8 ? ~0u : (1u << (4 * n0)) - 1u;
+  const unsigned m1 = n1 == 8 ? ~0u : (1u << (4 * n1)) - 1u;
+  const unsigned rep = v * 0x11111111u;
+  return ((r0 ^ rep) & m0) == 0u && ((r1 ^ rep) & m1) == 0u;
+}
+
+__device__ __forceinline__ void publish_flag(unsigned *line, int seg,
+                                             bool local) {
   // Each wave waits until its own aggregate stores have completed (a
   // workgroup barrier does not wait for them); only then is the flag set.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0)
-    __hip_atomic_store(line + seg, 1u, __ATOMIC_RELAXED,
+    __hip_atomic_store(line + seg, local ? 2u : 1u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -492,12 +519,11 @@ __device__ __forceinline__ void wait_flags(unsigned *line, int need,
                                            unsigned *timeout_word) {
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
-    unsigned spins = 0;
+    unsigned spins = 0, f = 1u;
     for (;;) {
-      const unsigned f = lane < need
-                             ? __hip_atomic_load(line + lane, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT)
-                             : 1u;
+      f = lane < need ? __hip_atomic_load(line + lane, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT)
+                      : 2u;
       if (__all(f != 0u)) break;
       __builtin_amdgcn_s_sleep(2);
       if (++spins > (1u << 22)) {
@@ -507,7 +533,10 @@ __device__ __forceinline__ void wait_flags(unsigned *line, int need,
         break;
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (__any(f != 2u))
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    else
+      asm volatile("buffer_inv sc0" ::: "memory");  // this CU's L1
   }
   __syncthreads();
 }
@@ -519,6 +548,9 @@ __device__ __forceinline__ void count_done(unsigned *line, int nseg) {
           static_cast<unsigned>(nseg - 1)) {
     for (int s = 0; s < nseg; ++s)
       __hip_atomic_store(line + s, 0u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = 0; i < 2; ++i)
+      __hip_atomic_store(line + kSyncXccWord + i, 0u, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(line + kSyncTicketWord, 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
@@ -587,6 +619,14 @@ void la_fwd_kernel(FwdArgs a) {
     __syncthreads();
     seg = __builtin_amdgcn_readfirstlane(*ticket);
   }
+  // this segment's XCD record (see the exchange above)
+  const unsigned me = xcc_record();
+  if (MULTI && a.nseg > 1 && tid == 0)
+    __hip_atomic_fetch_or(line + kSyncXccWord + seg / 8, me << (4 * (seg % 8)),
+                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // wave 0, lanes 0 and 1: the unit's XCD records, read once every segment
+  // has probably recorded (0 where not read)
+  unsigned recs = 0u;
   const Decay dk(a.decay, static_cast<int>(unit % a.H));
   for (int i = tid; i <= C; i += kThreads) gp[i] = pow_int(dk.g, dk.lg, i);
 
@@ -719,6 +759,9 @@ void la_fwd_kernel(FwdArgs a) {
       __syncthreads();  // gp and the constant tile parts ready
       stage1(0, rk[0], rv[0]);
       load1(NB1, rk[0], rv[0]);
+      if (w == 0 && a.nseg > 1)
+        recs = __hip_atomic_load(line + kSyncXccWord + (lane & 1),
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __syncthreads();
       features1(0);
       for (int c0 = 0; c0 < nch; c0 += NB1) {
@@ -746,7 +789,14 @@ void la_fwd_kernel(FwdArgs a) {
     if (a.nseg > 1) {
       float *ub = a.states + unit * a.nseg * static_cast<int64_t>(F::SLOT);
       const int need = CAUSAL ? seg : a.nseg;
+      // the records as wave 0 read them, for every wave
+      unsigned *srec = reinterpret_cast<unsigned *>(gp + C + 2);
+      if (tid < 2) srec[tid] = recs;
+      __syncthreads();
+      const unsigned r0 = srec[0], r1 = srec[1];
       if (!CAUSAL || seg + 1 < a.nseg) {
+        // through this XCD's L2 when every segment of the unit runs on it
+        const bool local = me < 15 && records_match(r0, r1, a.nseg, me);
         float *mine = ub + static_cast<int64_t>(seg) * F::SLOT;
 #pragma unroll
         for (int m = 0; m < F::FPW; ++m)
@@ -754,19 +804,25 @@ void la_fwd_kernel(FwdArgs a) {
           for (int mj = 0; mj < F::JPW; ++mj) {
             const int jb = tile_jb<F>(w, mj);
             const int idx = tile_fb<F>(w, m) * F::NJA + jb;
-            store_agent(mine + (idx * 64 + lane) * 4, S[m * F::JPW + mj]);
+            float *dst = mine + (idx * 64 + lane) * 4;
+            if (local)
+              *reinterpret_cast<f32x4 *>(dst) = S[m * F::JPW + mj];
+            else
+              store_agent(dst, S[m * F::JPW + mj]);
           }
-        publish_flag(line, seg);
+        publish_flag(line, seg, local);
       }
       ring2_first();
       if (need > 0) wait_flags(line, need, a.sync + kSyncTimeoutWord);
 #pragma unroll
       for (int i = 0; i < TW; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int64_t epos = CAUSAL ? start : a.n;
-      // Groups of GRP aggregates (about 12 tiles per lane); the loads of a
-      // group are unconditional (indices past the last clamp to it, with
-      // weight 0) so they are all in flight together.
-      constexpr int GRP = TW >= 8 ? 1 : (TW >= 4 ? 2 : 4);
+      // Groups of GRP aggregates (about 12 tiles per lane, 24 with one
+      // workgroup per CU); the loads of a group are unconditional (indices
+      // past the last clamp to it, with weight 0) so they are all in flight
+      // together.
+      constexpr int TILES = F::OCC == 1 ? 24 : 12;
+      constexpr int GRP = TW >= TILES ? 1 : pow2_floor(TILES / TW);
       for (int j0 = 0; j0 < need; j0 += GRP) {
         f32x4 buf[GRP][TW];
 #pragma unroll

@@ -27,15 +27,18 @@ constexpr int kMaxTargetGroups = 512;
 //     kMaxTargetGroups units: word s is the "aggregate of segment s published"
 //     flag, word kSyncTicketWord hands out causal segment indices in start
 //     order, word kSyncDoneWord counts the segments done waiting (the last
-//     one clears the line).
+//     one clears the line), and the two words from kSyncXccWord record, 4
+//     bits per segment, the XCD (1 + its id) each segment runs on.
 constexpr int kSyncHeaderWords = 64;
 constexpr int kSyncTimeoutWord = 8;
 constexpr int kSyncLineWords = 32;
 constexpr int kSyncDoneWord = kMaxSegments;
 constexpr int kSyncTicketWord = kMaxSegments + 1;
+constexpr int kSyncXccWord = kMaxSegments + 2;
 constexpr size_t kSyncBytes =
     sizeof(unsigned) * (kSyncHeaderWords + kMaxTargetGroups * kSyncLineWords);
-static_assert(kSyncTicketWord < kSyncLineWords, "sync line too short");
+static_assert(kSyncXccWord + 1 < kSyncLineWords, "sync line too short");
+static_assert(kMaxSegments <= 16, "4-bit XCD records: two words per line");
 static_assert(kSyncBytes % 256 == 0, "sync area keeps the states aligned");
 
 // Arguments of the chunked forward kernels.

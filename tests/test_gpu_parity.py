@@ -241,6 +241,41 @@ def test_workspace_shared_across_shapes():
             assert rel(out, ref) <= TOL[torch.bfloat16], (rep, cfg)
 
 
+# Bytes of the synchronisation area at the start of a segmented forward's
+# workspace: 64 header words, then one 32-word line per unit for up to 512.
+SYNC_BYTES = 4 * (64 + 512 * 32)
+TIMEOUT_WORD = 8
+
+
+@pytest.mark.parametrize("cfg", [
+    I.ELU1_CAUSAL,
+    I.ELU1_CAUSAL.replace(causal=False),
+    I.ELU1_CAUSAL.replace(B=1, H=2, n=4096, decay=(-3.0, -1.0)),
+    I.PERFORMER.replace(n=2048),
+], ids=["elu1", "noncausal", "decayed", "performer"])
+def test_exchange_never_times_out_and_leaves_area_zero(cfg):
+    """Segmented calls: every wait for another segment's aggregate ends
+    because the flag was seen (the timeout word stays 0), and the last
+    workgroup of each unit clears its line (the whole area reads 0)."""
+    name = I.MAP_NAMES[cfg.mapk]
+    need = K.forward_workspace_bytes(cfg.B, cfg.H, cfg.n, cfg.d, cfg.d_feat,
+                                     name, cfg.dtype, cfg.causal)
+    assert need > SYNC_BYTES, "the case must be split into segments"
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    x = I.make_prefill(cfg, 31)
+    args = [dev(x["q"]), dev(x["k"]), dev(x["v"]), name]
+    kw = dict(omega=dev(x["omega"]), decay=dev(x["decay"]),
+              causal=cfg.causal, workspace=ws)
+    first = K.forward(*args, **kw)
+    for _ in range(4):
+        again = K.forward(*args, **kw)
+    torch.cuda.synchronize()
+    sync = ws[:SYNC_BYTES].view(torch.int32).cpu()
+    assert sync[TIMEOUT_WORD].item() == 0, "a wait gave up"
+    assert torch.count_nonzero(sync).item() == 0
+    assert torch.equal(first, again)
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_constant_v_gives_constant_output(dtype):
     cfg = I.ELU1_CAUSAL.replace(B=1, H=4, n=3000, dtype=dtype,
