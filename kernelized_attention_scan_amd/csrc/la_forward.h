@@ -1006,7 +1006,9 @@ void la_fwd_kernel(FwdArgs a) {
       // numerators)
       auto block = [&](int jj) {
         const int jb = vblock(jj);
+        // without decay g^(t+1) = 1: both products share one accumulator
         f32x4 an = {0.f, 0.f, 0.f, 0.f}, ai = {0.f, 0.f, 0.f, 0.f};
+        f32x4 &acc_i = DECAY ? ai : an;
         if constexpr (SHARE) {
 #pragma unroll
           for (int kp = 0; kp < NPK; ++kp) an = mma(vf[jj][kp], pf[kp], an);
@@ -1024,12 +1026,13 @@ void la_fwd_kernel(FwdArgs a) {
         for (int kq = 0; kq < DFP / 32; ++kq) {
           Frag<T> fa;
           load_frag8(fa, sSTc + (16 * jb + li) * LQ + 32 * kq + 8 * g);
-          ai = mma(fa, qf[kq], ai);
+          acc_i = mma(fa, qf[kq], acc_i);
         }
-        return an + gt * ai;
+        return DECAY ? an + gt * ai : an;
       };
-      // the denominator of row t sits in lane t of group 0
-      const float rden = 1.f / __shfl(block(NJW)[0], li);
+      // the denominator of row t sits in lane t of group 0; its reciprocal
+      // (hardware, within 1 ulp) scales the numerators
+      const float rden = __builtin_amdgcn_rcpf(__shfl(block(NJW)[0], li));
 #pragma unroll
       for (int jj = 0; jj < NJW; ++jj) {
         const f32x4 o = block(jj) * rden;
