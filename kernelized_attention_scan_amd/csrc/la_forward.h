@@ -192,16 +192,14 @@ struct FwdShape {
                                  : 1;
   static_assert(OCC * kCUs <= kMaxTargetGroups, "sync area too small");
   static constexpr int WAVES_PER_SIMD = OCC * kWaves / 4;
-  // register-ring depths (chunks of loads in flight per workgroup)
-  static constexpr int RING = OCC == 2 ? 24 : 64;   // VGPRs, phase-2 ring
-  static constexpr int RING1 = OCC == 2 ? 32 : 64;  // VGPRs, phase-1 ring
+  // Register-ring depths: chunks of loads in flight per workgroup.  With
+  // every CU streaming, shallow rings measured fastest: more loads in flight
+  // only made each chunk's data arrive later.  Phase 1 (K, V) keeps the
+  // next chunk in flight; phase 2 (q, k, v) the next two where a chunk's
+  // loads take at most 12 VGPRs (d <= 64 bf16), else the next one.
   static constexpr int REG2 = 4 * (Slab<T, QW, C>::PER * 2 + Slab<T, D, C>::PER);
-  static constexpr int REG1 = 4 * (Slab<T, QW, C>::PER + Slab<T, D, C>::PER);
-  // (powers of two up to 4: loops run whole ring revolutions, and segments
-  // of a power-of-two number of chunks then need no padding chunks; deeper
-  // phase-1 rings were measured slower, the first chunk arriving later)
-  static constexpr int NB2 = pow2_floor(RING / REG2 > 4 ? 4 : RING / REG2);
-  static constexpr int NB1 = pow2_floor(RING1 / REG1 > 4 ? 4 : RING1 / REG1);
+  static constexpr int NB2 = REG2 <= 12 ? 2 : 1;
+  static constexpr int NB1 = 1;
   static constexpr int KRES = PIPE ? KRES_ : 0;
   // the fused Performer map needs bf16 operands, d a multiple of 32 (the
   // projection's k-width), at least 32 features, and d d' <= 128 * 128 (the
