@@ -252,7 +252,12 @@ TIMEOUT_WORD = 8
     I.ELU1_CAUSAL.replace(causal=False),
     I.ELU1_CAUSAL.replace(B=1, H=2, n=4096, decay=(-3.0, -1.0)),
     I.PERFORMER.replace(n=2048),
-], ids=["elu1", "noncausal", "decayed", "performer"])
+    # 5 segments in a grid of 5: the segments run on different XCDs, so the
+    # aggregates go through the coherence point
+    I.ELU1_CAUSAL.replace(B=1, H=1, n=300),
+    I.ELU1_CAUSAL.replace(B=1, H=1, n=300, causal=False),
+], ids=["elu1", "noncausal", "decayed", "performer", "cross_xcd",
+        "cross_xcd_noncausal"])
 def test_exchange_never_times_out_and_leaves_area_zero(cfg):
     """Segmented calls: every wait for another segment's aggregate ends
     because the flag was seen (the timeout word stays 0), and the last
