@@ -942,12 +942,12 @@ void la_fwd_kernel(FwdArgs a) {
       for (int kq = 0; kq < DFP / 32; ++kq)
         load_frag8(qf[kq], sQc + t * LQ + 32 * kq + 8 * g);
       Frag<T> pf[NPK];
+      // Key strips above the diagonal strip only hold masked products: from
+      // d' = 64 on they are skipped (a branch on the wave's strip), for
+      // narrower features computed and masked (no branch).
+      constexpr bool SKIP = DFP >= 64;
       if constexpr (CAUSAL) {
         f32x4 pt[STRIPS];
-        // Key strips above the diagonal strip only hold masked products:
-        // with wide features (d' >= 128) they are skipped (a branch on the
-        // wave's strip), else computed and masked (no branch).
-        constexpr bool SKIP = DFP >= 128;
 #pragma unroll
         for (int sb = 0; sb < STRIPS; ++sb) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -1013,7 +1013,7 @@ void la_fwd_kernel(FwdArgs a) {
         } else if constexpr (CAUSAL) {
 #pragma unroll
           for (int kp = 0; kp < NPK; ++kp) {
-            if (DFP < 128 || 2 * kp <= tb) {  // pairs above it are zero
+            if (!SKIP || 2 * kp <= tb) {  // pairs above it are zero
               Frag<T> fa;
               load_frag_tr44(fa, sVc, LV, 32 * kp, 16 * jb, g, li);
               an = mma(fa, pf[kp], an);
