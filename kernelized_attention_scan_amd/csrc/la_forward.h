@@ -887,7 +887,11 @@ void la_fwd_kernel(FwdArgs a) {
   __syncthreads();
   features2(0);
 
-  const int tb = w % STRIPS;    // this wave's output strip
+  // This wave's output strip: the order alternates between groups of
+  // STRIPS waves, so the two waves a SIMD usually holds (w, w + 4) take
+  // strips of unequal causal work (k and STRIPS - 1 - k).
+  const int tb =
+      (w / STRIPS) % 2 == 0 ? w % STRIPS : STRIPS - 1 - w % STRIPS;
   const int jh = w / STRIPS;    // and its share of the column blocks
   const int t = 16 * tb + li;   // the output row this lane normalises
   const float gt = CAUSAL ? gp[t + 1] : 1.f;
