@@ -228,12 +228,15 @@ __device__ __forceinline__ float elu_plus_one(float x) {
   return x > 0.f ? x + 1.f : expf(x);
 }
 
-// The same map with exp(x) as the hardware 2^(x log2 e): relative error a few
-// 1e-7 for the x <= 0 branch, far below the bf16 rounding that follows, and
-// computed with no branch (both sides evaluated, then selected).
+// The same map with exp(x) as the hardware 2^(x log2 e) (relative error a
+// few 1e-7, far below the bf16 rounding that follows), computed with no
+// branch and no select: exp(x) >= 1 + x for every x, so
+// elu(x) + 1 = max(x + 1, min(exp(x), 1)), and min(2^y, 1) is the exp
+// instruction's output clamp to [0, 1].
 __device__ __forceinline__ float elu_plus_one_fast(float x) {
-  const float e = __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
-  return x > 0.f ? x + 1.f : e;
+  const float e = __builtin_amdgcn_fmed3f(
+      __builtin_amdgcn_exp2f(x * 1.4426950408889634f), 0.f, 1.f);
+  return fmaxf(x + 1.f, e);
 }
 
 // g^k for an integer k >= 0, with g^0 = 1 exactly (also for g = 0).
