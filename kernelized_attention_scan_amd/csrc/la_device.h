@@ -221,6 +221,43 @@ __device__ __forceinline__ void store4(float *p, float a, float b, float c,
 }
 
 // ---------------------------------------------------------------------------
+// Raw buffer accesses.  A resource covers n bytes at p; an access at byte
+// offset voffset + soffset at or past n reads zero and writes nothing (the
+// hardware range check, soffset included), so chunk loads and stores need
+// no clamps, pointer arithmetic or discard addresses per lane.  Word 3
+// selects 32-bit data format, as untyped loads and stores require.
+// ---------------------------------------------------------------------------
+constexpr int kBufferWord3 = 0x00020000;
+// An offset past every resource this library builds (stores there are
+// dropped).
+constexpr unsigned kNoAccess = 0x7ffffff0u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p,
+                                                            unsigned n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0,
+                                           static_cast<int>(n), kBufferWord3);
+}
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r,
+                                               unsigned off) {
+  return __builtin_bit_cast(
+      u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r,
+                                              unsigned off, float a, float b,
+                                              float c, float d, bf16) {
+  const u32x2 v = {pack_bf16x2(a, b), pack_bf16x2(c, d)};
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r,
+                                              unsigned off, float a, float b,
+                                              float c, float d, float) {
+  const f32x4 v = {a, b, c, d};
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off,
+                                         0, 0);
+}
+
+// ---------------------------------------------------------------------------
 // Feature maps on fp32 values ("Linear attention research 2026" page).
 // ---------------------------------------------------------------------------
 // elu(x) + 1 with alpha = 1: x + 1 for x > 0, exp(x) otherwise.

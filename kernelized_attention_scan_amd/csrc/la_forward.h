@@ -66,11 +66,6 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;
 constexpr size_t kMaxLds = 160 * 1024;
 
-// Destination of the stores of output rows past the end of a partial chunk:
-// selecting this address instead of branching around the store keeps the
-// chunk loop free of branches (nothing ever reads it).
-__device__ __align__(16) unsigned char la_discard[16];
-
 // Registers holding one [C][W] slab of a [n][W] row-major matrix as 16-byte
 // pieces; consecutive threads take consecutive pieces (coalesced).
 template <typename T, int W, int C>
@@ -82,16 +77,17 @@ struct Slab {
   static constexpr bool EXACT = PIECES % kThreads == 0;
   u32x4 v[PER];
 
-  // Rows >= rows re-read row rows-1 (always valid).
+  // Rows row0 .. row0 + rows - 1 of base; pieces of later rows read zero
+  // (the resource ends after the last valid row, so those rows cost no
+  // memory traffic).  Piece p of the slab sits at byte 16 p.
   __device__ __forceinline__ void load(const T *base, int64_t row0, int rows,
                                        int tid) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(
+        base + row0 * W, static_cast<unsigned>(rows) * W * sizeof(T));
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int p = tid + kThreads * i;
-      const int row = p / PPR, col = (p % PPR) * VEC;
-      const int rr = row < rows ? row : rows - 1;
-      if (EXACT || p < PIECES)
-        v[i] = *reinterpret_cast<const u32x4 *>(base + (row0 + rr) * W + col);
+      if (EXACT || p < PIECES) v[i] = buffer_load16(r, 16u * p);
     }
   }
 };
@@ -709,9 +705,8 @@ void la_fwd_kernel(FwdArgs a) {
   Slab<T, D, C> rv2[NB2];
   auto load2 = [&](int c, Slab<T, QW, C> &sq, Slab<T, QW, C> &sk,
                    Slab<T, D, C> &sv) {
-    const int cl = clamp_chunk(c);
-    const int64_t r0 = start + cl * C;
-    const int rows = rows_of(cl);
+    const int64_t r0 = start + clamp_chunk(c) * C;
+    const int rows = rows_of(c);  // 0 for padding chunks: zeros, no traffic
     sq.load(qb, r0, rows, tid);
     if (CAUSAL) {
       if (!resident) sk.load(kb, r0, rows, tid);
@@ -737,9 +732,9 @@ void la_fwd_kernel(FwdArgs a) {
       Slab<T, QW, C> rk[NB1];
       Slab<T, D, C> rv[NB1];
       auto load1 = [&](int c, Slab<T, QW, C> &sk, Slab<T, D, C> &sv) {
-        const int cl = clamp_chunk(c);
-        sk.load(kb, start + cl * C, rows_of(cl), tid);
-        sv.load(vb, start + cl * C, rows_of(cl), tid);
+        const int64_t r0 = start + clamp_chunk(c) * C;
+        sk.load(kb, r0, rows_of(c), tid);
+        sv.load(vb, r0, rows_of(c), tid);
       };
 #pragma unroll
       for (int b = 0; b < NB1; ++b) load1(b, rk[b], rv[b]);
@@ -947,7 +942,6 @@ void la_fwd_kernel(FwdArgs a) {
       const int c = c0 + b, bn = (b + 1) % NB2;
       const int sc = F::NBUF == 2 && NB2 % 2 == 0 ? (b & 1) : set_of(c);
       const int sn = F::NBUF == 2 ? sc ^ 1 : 0;
-      const int64_t row0 = start + c * C;
       const int rows = rows_of(c);
       const T *sQc = sQ + sc * F::SQ;
       // resident keys: chunk c's phi(K) in slot c (padding chunks read a
@@ -1058,16 +1052,20 @@ void la_fwd_kernel(FwdArgs a) {
       // the denominator of row t sits in lane t of group 0; its reciprocal
       // (hardware, within 1 ulp) scales the numerators
       const float rden = __builtin_amdgcn_rcpf(__shfl(block(NJW)[0], li));
+      // the chunk's output rows (none for padding chunks); stores of rows
+      // past the end and of blocks past the last are dropped
+      const __amdgpu_buffer_rsrc_t ro =
+          make_rsrc(ob + (start + clamp_chunk(c) * C) * D,
+                    static_cast<unsigned>(rows) * D * sizeof(T));
 #pragma unroll
       for (int jj = 0; jj < NJW; ++jj) {
         const f32x4 o = block(jj) * rden;
-        // o[rr]: column j = 16 jb + 4 g + rr of output row t; rows past
-        // the end (and blocks past the last) go to the discard word
+        // o[rr]: column j = 16 jb + 4 g + rr of output row t
         const int jb = jh + WPS * jj;
-        T *dst = (NJ % WPS == 0 || jb < NJ) && t < rows
-                     ? ob + (row0 + t) * D + 16 * jb + 4 * g
-                     : reinterpret_cast<T *>(la_discard);
-        store4(dst, o[0], o[1], o[2], o[3]);
+        const unsigned off = NJ % WPS == 0 || jb < NJ
+                                 ? (t * D + 16 * jb + 4 * g) * sizeof(T)
+                                 : kNoAccess;
+        buffer_store4(ro, off, o[0], o[1], o[2], o[3], T{});
       }
 
       if constexpr (CAUSAL) {
