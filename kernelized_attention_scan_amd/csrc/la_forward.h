@@ -648,12 +648,15 @@ void la_fwd_kernel(FwdArgs a) {
   // launch guarantees nch <= KRES)
   constexpr bool resident = RES;
 
-  // Constant parts of the tiles: the ones block of sV (column D = 1, the
-  // other 15 columns 0, every row) and, for DF < 32, the zero k-padding
-  // columns of q', k' and S^T.
+  // Constant parts of the tiles: the ones block of sV (columns D, D + 4,
+  // D + 8 and D + 12 = 1, the other 12 columns 0, every row) and, for
+  // DF < 32, the zero k-padding columns of q', k' and S^T.  The four ones
+  // columns give the state four equal copies of z, and the readout a
+  // denominator in element 0 of every lane's accumulator (no cross-lane
+  // step); nu is read from column D.
   for (int i = tid; i < F::NBUF * C * 16; i += kThreads)
     sV[(i / (C * 16)) * F::SV + ((i / 16) % C) * LV + D + i % 16] =
-        from_f32<T>(i % 16 == 0 ? 1.f : 0.f);
+        from_f32<T>(i % 4 == 0 ? 1.f : 0.f);
   // Fused Performer: this wave's omega^T tiles as A fragments, rounded once
   // to T and kept in registers (lane: feature 16 fb + li, d values
   // 32 kb + 8 g .. +7; for each d the 16 lanes read 16 consecutive floats of
@@ -692,9 +695,10 @@ void la_fwd_kernel(FwdArgs a) {
   // Chunk helpers: valid rows of chunk c (0 past the end), the chunk a ring
   // load fetches for chunk c (clamped to the last one), and the tile set
   // chunk c uses (c % 2 with two sets).
+  const int last_rows =  // rows of the last chunk (1 .. C when nch > 0)
+      static_cast<int>(end - (start + static_cast<int64_t>(nch - 1) * C));
   auto rows_of = [&](int c) -> int {
-    return c < nch ? static_cast<int>(min<int64_t>(C, end - (start + c * C)))
-                   : 0;
+    return c < nch - 1 ? C : c == nch - 1 ? last_rows : 0;
   };
   auto clamp_chunk = [&](int c) -> int { return c < nch ? c : nch - 1; };
   auto set_of = [&](int c) -> int { return F::NBUF == 2 ? (c & 1) : 0; };
@@ -931,11 +935,12 @@ void la_fwd_kernel(FwdArgs a) {
       }
   }
   constexpr int NJW = (NJ + WPS - 1) / WPS;
-  // V^T fragment of the ones block (column D is 1 at every row, the other
-  // 15 columns 0): a constant, so it is never read from LDS
+  // V^T fragment of the ones block (columns D + 4 k are 1 at every row, the
+  // others 0): a constant, so it is never read from LDS
   Frag<T> onesf;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) onesf.v[e] = from_f32<T>(li == 0 ? 1.f : 0.f);
+  for (int e = 0; e < 8; ++e)
+    onesf.v[e] = from_f32<T>(li % 4 == 0 ? 1.f : 0.f);
   for (int c0 = 0; c0 < nch; c0 += NB2) {
 #pragma unroll
     for (int b = 0; b < NB2; ++b) {
@@ -1019,9 +1024,9 @@ void la_fwd_kernel(FwdArgs a) {
           }
       }
       // column block vblock(jj) of num^T = V^T P^T + g^(t+1) S^T Q'^T (the
-      // ones block: its first row is the denominator, sum_s P[t][s] +
-      // g^(t+1) q'_t . z, from the same rounded P and S copy as the
-      // numerators)
+      // ones block: its rows 0, 4, 8, 12 are the denominator,
+      // sum_s P[t][s] + g^(t+1) q'_t . z, from the same rounded P and S copy
+      // as the numerators)
       auto block = [&](int jj) {
         const int jb = vblock(jj);
         // without decay g^(t+1) = 1: both products share one accumulator
@@ -1049,9 +1054,10 @@ void la_fwd_kernel(FwdArgs a) {
         }
         return DECAY ? an + gt * ai : an;
       };
-      // the denominator of row t sits in lane t of group 0; its reciprocal
-      // (hardware, within 1 ulp) scales the numerators
-      const float rden = __builtin_amdgcn_rcpf(__shfl(block(NJW)[0], li));
+      // the denominator of row t is element 0 of this lane's ones-block
+      // accumulator (row 4 g of the tile); its reciprocal (hardware, within
+      // 1 ulp) scales the numerators
+      const float rden = __builtin_amdgcn_rcpf(block(NJW)[0]);
       // the chunk's output rows (none for padding chunks); stores of rows
       // past the end and of blocks past the last are dropped
       const __amdgpu_buffer_rsrc_t ro =
@@ -1067,6 +1073,10 @@ void la_fwd_kernel(FwdArgs a) {
                                  : kNoAccess;
         buffer_store4(ro, off, o[0], o[1], o[2], o[3], T{});
       }
+      // the output stores issue here, before any wait for the next chunk's
+      // loads that the staging below needs (measured faster except with
+      // the fused Performer map, whose loop is scheduled better without)
+      if constexpr (!PF) __builtin_amdgcn_sched_barrier(0);
 
       if constexpr (CAUSAL) {
         // ---- state update: S <- g^r S + (w.K')^T [V | 1] ----
