@@ -117,7 +117,7 @@ constexpr size_t fwd_lds_bytes(int c, int d, int df, bool decay, bool pf,
   const size_t sx = pf ? static_cast<size_t>(c) * lds_stride<T>(d) : 0;
   return sizeof(T) * (nbuf * (sq + (decay ? sq : 0) + sv + sst) +
                       kslots * sq + 2 * sx) +
-         sizeof(float) * (c + 4);
+         sizeof(float) * (c + 4 + (pf ? 2 * c : 0));
 }
 
 // Largest power of two <= x, at most 8 (1 for x < 2).
@@ -323,26 +323,77 @@ __device__ __forceinline__ void stage_values(const Slab<T, W, C> &sl, T *sV,
   }
 }
 
+// x moved from lane l ^ 1, l ^ 2 (quad permutations), or mirrored within
+// 8 or 16 lanes (DPP row_half_mirror, row_mirror).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf,
+                                      0xf, false));
+}
+// Sum over aligned groups of N = 4, 8 or 16 consecutive lanes.
+template <int N>
+__device__ __forceinline__ float sum_lane_groups(float x) {
+  static_assert(N == 4 || N == 8 || N == 16, "lane group");
+  x += dpp_f32<0xb1>(x);                    // quad_perm 1, 0, 3, 2
+  x += dpp_f32<0x4e>(x);                    // quad_perm 2, 3, 0, 1
+  if constexpr (N >= 8) x += dpp_f32<0x141>(x);   // row_half_mirror
+  if constexpr (N >= 16) x += dpp_f32<0x140>(x);  // row_mirror
+  return x;
+}
+
+// Raw q or k rows of one chunk for the fused Performer map -> sX
+// (row-major), and for each row the exponent offset of its features,
+// c0 = -|x|^2 log2(e) / 2 - log2 sqrt(m), to c0[row]: -inf for rows at or
+// past valid_rows, whose features are then exactly 0.  The PPR threads that
+// stage a row's pieces sum their squares in fp32 and combine them across
+// lanes, so every norm is computed once per chunk.
+template <typename T, int W, int C, int L>
+__device__ __forceinline__ void stage_rows_pf(const Slab<T, W, C> &sl, T *sX,
+                                              float *c0, float lsm,
+                                              int valid_rows, int tid) {
+  using S = Slab<T, W, C>;
+  constexpr float kLog2e = 1.4426950408889634f;
+  static_assert(sizeof(T) == 2, "bf16 rows");
+#pragma unroll
+  for (int i = 0; i < S::PER; ++i) {
+    const int p = tid + kThreads * i;
+    const bool mine = S::EXACT || p < S::PIECES;
+    const int row = p / S::PPR, col = (p % S::PPR) * S::VEC;
+    float n = 0.f;
+    if (mine) {
+      *reinterpret_cast<u32x4 *>(sX + row * L + col) = sl.v[i];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float lo = bf16_lo(sl.v[i][k]), hi = bf16_hi(sl.v[i][k]);
+        n += lo * lo + hi * hi;
+      }
+    }
+    n = sum_lane_groups<S::PPR>(n);
+    if (mine && p % S::PPR == 0)
+      c0[row] = row < valid_rows ? -0.5f * kLog2e * n - lsm : -__builtin_inff();
+  }
+}
+
 // Performer features of the rows of one chunk, fused ("Linear attention
 // research 2026" page, Performer random features: phi(x) = exp(x omega -
 // |x|^2 / 2) / sqrt(m)).  u^T = omega^T X^T runs on the matrix cores: A =
 // this wave's omega^T tiles (registers, see FwdShape::TPW), B = the raw q or
-// k rows (LDS), contraction over d.  For each of its strips (16 rows) the
-// wave sums |x|^2 of the rows in fp32, then for each of its feature tiles fb
-// its accumulator holds features 16 fb + 4 g .. +3 of row 16 ts + li: the
-// map is applied in registers (exp2 of u log2 e minus |x|^2 log2 e / 2 and
-// log2 sqrt(m)) and stored as 4 consecutive values.  WQ maps the queries
-// into dq; WK maps the keys: rows >= rows are zero, and under decay the
-// weighted copy w_s phi(k_s), w_s = b g^(rows-1-s), goes to dkw (the plain
-// one to dk when PLAIN or without decay).
+// k rows (LDS), contraction over d.  The omega tiles carry the factor
+// log2 e and each accumulator starts at its row's exponent offset c0 (see
+// stage_rows_pf; c0q for the queries, c0k for the keys), so for each feature
+// tile fb the accumulator of row 16 ts + li holds the base-2 exponents of
+// features 16 fb + 4 g .. +3: one exp2 per feature, stored as 4 consecutive
+// values.  WQ maps the queries into dq; WK maps the keys: rows >= rows are
+// zero (c0 = -inf), and under decay the weighted copy w_s phi(k_s),
+// w_s = b g^(rows-1-s), goes to dkw (the plain one to dk when PLAIN or
+// without decay).
 template <typename F, typename T, bool WQ, bool WK, bool DECAY, bool PLAIN>
 __device__ __forceinline__ void performer_features(
     const Frag<T> (&wf)[F::TPW][F::DV / 32], const T *sXq, const T *sXk,
-    T *dq, T *dk, T *dkw, const float *gp, float b, int rows, int w, int g,
-    int li) {
+    const float *c0q, const float *c0k, T *dq, T *dk, T *dkw,
+    const float *gp, float b, int rows, int w, int g, int li) {
   constexpr int KB = F::DV / 32;  // k-blocks of the contraction over d
-  constexpr float kLog2e = 1.4426950408889634f;
-  const float lsm = 0.5f * __builtin_log2f(F::NF * 16.f);  // log2 sqrt(m)
 #pragma unroll
   for (int j = 0; j < F::SPW; ++j) {
     const int ts = F::NF >= kWaves ? j : w / F::NF + F::WPT * j;
@@ -353,31 +404,23 @@ __device__ __forceinline__ void performer_features(
         const bool keys = mat == 1;
         if ((keys && WK) || (!keys && WQ)) {
           Frag<T> xf[KB];
-          float nrm = 0.f;
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
-            load_frag8(xf[kb], (keys ? sXk : sXq) + row * F::LX + 32 * kb + 8 * g);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float v = to_f32(xf[kb].v[e]);
-              nrm += v * v;
-            }
-          }
-          nrm = wave_sum_groups(nrm);
-          const float c0 = -0.5f * kLog2e * nrm - lsm;
-          const bool valid = !keys || row < rows;
-          const float wr =
-              (keys && DECAY) ? (valid ? b * gp[rows - 1 - row] : 0.f) : 1.f;
+          for (int kb = 0; kb < KB; ++kb)
+            load_frag8(xf[kb],
+                       (keys ? sXk : sXq) + row * F::LX + 32 * kb + 8 * g);
+          const float c0 = (keys ? c0k : c0q)[row];
+          const float wr = (keys && DECAY)
+                               ? (row < rows ? b * gp[rows - 1 - row] : 0.f)
+                               : 1.f;
 #pragma unroll
           for (int m = 0; m < F::TPW; ++m) {
             const int fb = F::NF >= kWaves ? w + kWaves * m : w % F::NF;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            f32x4 acc = {c0, c0, c0, c0};
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) acc = mma(wf[m][kb], xf[kb], acc);
             float ph[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              ph[r] = valid ? __builtin_amdgcn_exp2f(acc[r] * kLog2e + c0) : 0.f;
+            for (int r = 0; r < 4; ++r) ph[r] = __builtin_amdgcn_exp2f(acc[r]);
             const int off = row * F::LQ + 16 * fb + 4 * g;
             if (!keys) {
               store4(dq + off, ph[0], ph[1], ph[2], ph[3]);
@@ -590,6 +633,10 @@ void la_fwd_kernel(FwdArgs a) {
   T *sXq = sST + F::NBUF * F::SST;  // raw q, k rows (fused Performer)
   T *sXk = sXq + F::SX;
   float *gp = reinterpret_cast<float *>(sXk + F::SX);
+  // fused Performer: the exponent offsets of the chunk's q rows, then of its
+  // k rows (see stage_rows_pf), after the C + 4 words of gp
+  float *pc0 = gp + C + 4;
+  const float lsm = 0.5f * __builtin_log2f(static_cast<float>(DF));
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -657,10 +704,10 @@ void la_fwd_kernel(FwdArgs a) {
   for (int i = tid; i < F::NBUF * C * 16; i += kThreads)
     sV[(i / (C * 16)) * F::SV + ((i / 16) % C) * LV + D + i % 16] =
         from_f32<T>(i % 4 == 0 ? 1.f : 0.f);
-  // Fused Performer: this wave's omega^T tiles as A fragments, rounded once
-  // to T and kept in registers (lane: feature 16 fb + li, d values
-  // 32 kb + 8 g .. +7; for each d the 16 lanes read 16 consecutive floats of
-  // omega [d][d_feat]).
+  // Fused Performer: this wave's omega^T tiles times log2 e as A fragments,
+  // rounded once to T and kept in registers (lane: feature 16 fb + li, d
+  // values 32 kb + 8 g .. +7; for each d the 16 lanes read 16 consecutive
+  // floats of omega [d][d_feat]).
   Frag<T> wf[PF ? F::TPW : 1][PF ? D / 32 : 1];
   if constexpr (PF) {
 #pragma unroll
@@ -670,8 +717,9 @@ void la_fwd_kernel(FwdArgs a) {
       for (int kb = 0; kb < D / 32; ++kb)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          wf[m][kb].v[e] =
-              from_f32<T>(a.omega[(32 * kb + 8 * g + e) * DF + 16 * fb + li]);
+          wf[m][kb].v[e] = from_f32<T>(
+              a.omega[(32 * kb + 8 * g + e) * DF + 16 * fb + li] *
+              1.4426950408889634f);
     }
   }
   if (DFP != DF) {
@@ -752,7 +800,7 @@ void la_fwd_kernel(FwdArgs a) {
       auto stage1 = [&](int c, const Slab<T, QW, C> &sk,
                         const Slab<T, D, C> &sv) {
         if constexpr (PF)
-          stage_values<T, D, C, LX>(sk, sXk, tid);
+          stage_rows_pf<T, D, C, LX>(sk, sXk, pc0 + C, lsm, rows_of(c), tid);
         else
           stage_keys<T, DF, C, LQ, DECAY, false, ELU>(
               sk, keys1(c), sKw + set_of(c) * F::SQ, gp, dk.b, rows_of(c),
@@ -762,7 +810,8 @@ void la_fwd_kernel(FwdArgs a) {
       auto features1 = [&](int c) {
         if constexpr (PF) {
           performer_features<F, T, false, true, DECAY, false>(
-              wf, sXq, sXk, sQ, sK, sKw, gp, dk.b, rows_of(c), w, g, li);
+              wf, sXq, sXk, pc0, pc0 + C, sQ, sK, sKw, gp, dk.b, rows_of(c),
+              w, g, li);
           __syncthreads();
         }
       };
@@ -875,8 +924,9 @@ void la_fwd_kernel(FwdArgs a) {
                     const Slab<T, D, C> &sv) {
     const int sc = set_of(c);
     if constexpr (PF) {
-      stage_values<T, D, C, LX>(sq, sXq, tid);
-      if (CAUSAL) stage_values<T, D, C, LX>(sk, sXk, tid);
+      stage_rows_pf<T, D, C, LX>(sq, sXq, pc0, lsm, C, tid);
+      if (CAUSAL)
+        stage_rows_pf<T, D, C, LX>(sk, sXk, pc0 + C, lsm, rows_of(c), tid);
     } else {
       stage_queries<T, DF, C, LQ, ELU>(sq, sQ + sc * F::SQ, tid);
       if (CAUSAL && !resident)
@@ -888,7 +938,8 @@ void la_fwd_kernel(FwdArgs a) {
   auto features2 = [&](int c) {
     if constexpr (PF) {
       performer_features<F, T, true, CAUSAL, DECAY, true>(
-          wf, sXq, sXk, sQ, sK, sKw, gp, dk.b, rows_of(c), w, g, li);
+          wf, sXq, sXk, pc0, pc0 + C, sQ, sK, sKw, gp, dk.b, rows_of(c), w, g,
+          li);
       __syncthreads();
     }
   };

@@ -121,6 +121,8 @@ GRID = [
     ("performer_m256", 1, 2, 900, 64, "performer", 256, False, True),
     ("performer_m64_decay", 1, 2, 400, 32, "performer", 64, True, True),
     ("performer_noncausal", 1, 1, 300, 64, "performer", 128, False, False),
+    ("performer_d128_m128", 1, 2, 500, 128, "performer", 128, False, True),
+    ("performer_d32_m256_decay", 1, 1, 333, 32, "performer", 256, True, True),
 ]
 
 
