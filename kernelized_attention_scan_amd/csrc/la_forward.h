@@ -220,6 +220,21 @@ template <typename F>
 __device__ __forceinline__ int tile_jb(int w, int m) {
   return F::NF >= kWaves ? m : min(w / F::NF + F::WPF * m, F::NJA - 1);
 }
+// Whether a wave's state tile m is the ones block (or its copy) in every
+// wave, which the tile layout fixes at compile time.
+template <typename F>
+__device__ __forceinline__ constexpr bool ones_tile(int m) {
+  return F::NF >= kWaves ? m == F::NJ : F::WPF * m >= F::NJ;
+}
+// A V (or V^T) fragment of the ones block in any lane assignment: lane
+// (g, i) holds column D + i, which is 1 for i = 0, 4, 8, 12 at every row.
+template <typename T>
+__device__ __forceinline__ Frag<T> ones_frag(int li) {
+  Frag<T> f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = from_f32<T>(li % 4 == 0 ? 1.f : 0.f);
+  return f;
+}
 
 // Per-head decay: g = a, b = 1 - a (eqs 10-11); g = b = 1 without decay.
 struct Decay {
@@ -463,7 +478,10 @@ __device__ __forceinline__ void state_update(f32x4 *S, const T *sKw,
 #pragma unroll
       for (int kb = 0; kb < C / 32; ++kb) {
         Frag<T> bf;
-        load_frag_tr8(bf, sV, F::LV, 32 * kb, 16 * jb, g, li);
+        if (ones_tile<F>(mj))  // a constant, not read from LDS
+          bf = ones_frag<T>(li);
+        else
+          load_frag_tr8(bf, sV, F::LV, 32 * kb, 16 * jb, g, li);
         acc = mma(af[kb], bf, acc);
       }
       S[m * F::JPW + mj] = acc;
@@ -988,10 +1006,7 @@ void la_fwd_kernel(FwdArgs a) {
   constexpr int NJW = (NJ + WPS - 1) / WPS;
   // V^T fragment of the ones block (columns D + 4 k are 1 at every row, the
   // others 0): a constant, so it is never read from LDS
-  Frag<T> onesf;
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-    onesf.v[e] = from_f32<T>(li % 4 == 0 ? 1.f : 0.f);
+  const Frag<T> onesf = ones_frag<T>(li);
   for (int c0 = 0; c0 < nch; c0 += NB2) {
 #pragma unroll
     for (int b = 0; b < NB2; ++b) {
