@@ -889,7 +889,10 @@ void la_fwd_kernel(FwdArgs a) {
           }
         publish_flag(line, seg, local);
       }
-      ring2_first();
+      // the first chunk's phase-2 loads overlap the wait; the rest of the
+      // ring follows the aggregates' loads, which would otherwise complete
+      // only after them (loads complete in order)
+      load2(0, rq[0], rk2[0], rv2[0]);
       if (need > 0) wait_flags(line, need, a.sync + kSyncTimeoutWord);
 #pragma unroll
       for (int i = 0; i < TW; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -927,6 +930,8 @@ void la_fwd_kernel(FwdArgs a) {
           for (int i = 0; i < TW; ++i) S[i] += wj * buf[u][i];
         }
       }
+#pragma unroll
+      for (int b = 1; b < NB2; ++b) load2(b, rq[b], rk2[b], rv2[b]);
     } else {
       ring2_first();
     }
