@@ -670,49 +670,17 @@ void la_fwd_kernel(FwdArgs a) {
                        ? a.sync + kSyncHeaderWords + unit * kSyncLineWords
                        : nullptr;
   int seg = static_cast<int>(blk % a.nseg);
-  if (MULTI && CAUSAL && a.nseg > 1) {
-    // Causal segments take their index from the unit's ticket counter, in
-    // the order they start: a segment then only ever waits for segments that
-    // are already running, so no co-residency is needed.
-    int *ticket = reinterpret_cast<int *>(gp + C + 1);
-    if (tid == 0) {
-      unsigned t = __hip_atomic_fetch_add(line + kSyncTicketWord, 1u,
-                                          __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-      if (t >= static_cast<unsigned>(a.nseg)) {  // corrupt area: stay in bounds
-        __hip_atomic_store(a.sync + kSyncTimeoutWord, 1u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-        t %= static_cast<unsigned>(a.nseg);
-      }
-      *ticket = static_cast<int>(t);
-    }
-    __syncthreads();
-    seg = __builtin_amdgcn_readfirstlane(*ticket);
-  }
-  // this segment's XCD record (see the exchange above)
-  const unsigned me = xcc_record();
-  if (MULTI && a.nseg > 1 && tid == 0)
-    __hip_atomic_fetch_or(line + kSyncXccWord + seg / 8, me << (4 * (seg % 8)),
-                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  // wave 0, lanes 0 and 1: the unit's XCD records, read once every segment
-  // has probably recorded (0 where not read)
-  unsigned recs = 0u;
+  // Causal segments take their index from the unit's ticket counter, in the
+  // order they start: a segment then only ever waits for segments that are
+  // already running, so no co-residency is needed.  The table of decay
+  // powers and the constant tile parts are set up while the ticket is in
+  // flight.
+  unsigned tk = 0u;
+  if (MULTI && CAUSAL && a.nseg > 1 && tid == 0)
+    tk = __hip_atomic_fetch_add(line + kSyncTicketWord, 1u, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
   const Decay dk(a.decay, static_cast<int>(unit % a.H));
   for (int i = tid; i <= C; i += kThreads) gp[i] = pow_int(dk.g, dk.lg, i);
-
-  const T *qb = static_cast<const T *>(a.q) + unit * a.n * QW;
-  const T *kb = static_cast<const T *>(a.k) + unit * a.n * QW;
-  const T *vb = static_cast<const T *>(a.v) + unit * a.n * D;
-  T *ob = static_cast<T *>(a.out) + unit * a.n * D;
-  const int64_t start = seg * a.seg_len;
-  const int64_t end = min(a.n, start + a.seg_len);
-  const int nch = static_cast<int>((end - start + C - 1) / C);
-  // this workgroup writes the unit's final state (the last segment does)
-  const bool keep_state = a.mu_out != nullptr && seg + 1 == a.nseg;
-  // phi(K) of the whole segment stays in LDS from phase 1 to phase 2 (the
-  // launch guarantees nch <= KRES)
-  constexpr bool resident = RES;
-
   // Constant parts of the tiles: the ones block of sV (columns D, D + 4,
   // D + 8 and D + 12 = 1, the other 12 columns 0, every row) and, for
   // DF < 32, the zero k-padding columns of q', k' and S^T.  The four ones
@@ -753,6 +721,41 @@ void la_fwd_kernel(FwdArgs a) {
           sst_col<T>(row, DF + i % NP)] = from_f32<T>(0.f);
     }
   }
+
+  if (MULTI && CAUSAL && a.nseg > 1) {
+    int *ticket = reinterpret_cast<int *>(gp + C + 1);
+    if (tid == 0) {
+      if (tk >= static_cast<unsigned>(a.nseg)) {  // corrupt area: in bounds
+        __hip_atomic_store(a.sync + kSyncTimeoutWord, 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        tk %= static_cast<unsigned>(a.nseg);
+      }
+      *ticket = static_cast<int>(tk);
+    }
+    __syncthreads();
+    seg = __builtin_amdgcn_readfirstlane(*ticket);
+  }
+  // this segment's XCD record (see the exchange above)
+  const unsigned me = xcc_record();
+  if (MULTI && a.nseg > 1 && tid == 0)
+    __hip_atomic_fetch_or(line + kSyncXccWord + seg / 8, me << (4 * (seg % 8)),
+                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // wave 0, lanes 0 and 1: the unit's XCD records, read once every segment
+  // has probably recorded (0 where not read)
+  unsigned recs = 0u;
+
+  const T *qb = static_cast<const T *>(a.q) + unit * a.n * QW;
+  const T *kb = static_cast<const T *>(a.k) + unit * a.n * QW;
+  const T *vb = static_cast<const T *>(a.v) + unit * a.n * D;
+  T *ob = static_cast<T *>(a.out) + unit * a.n * D;
+  const int64_t start = seg * a.seg_len;
+  const int64_t end = min(a.n, start + a.seg_len);
+  const int nch = static_cast<int>((end - start + C - 1) / C);
+  // this workgroup writes the unit's final state (the last segment does)
+  const bool keep_state = a.mu_out != nullptr && seg + 1 == a.nseg;
+  // phi(K) of the whole segment stays in LDS from phase 1 to phase 2 (the
+  // launch guarantees nch <= KRES)
+  constexpr bool resident = RES;
 
   f32x4 S[TW];
 #pragma unroll
@@ -1111,7 +1114,8 @@ void la_fwd_kernel(FwdArgs a) {
           for (int kp = 0; kp < NPK; ++kp) {
             if (!SKIP || 2 * kp <= tb) {  // pairs above it are zero
               Frag<T> fa = onesf;
-              if (jj < NJW) load_frag_tr44(fa, sVc, LV, 32 * kp, 16 * jb, g, li);
+              if (jj < NJW)
+                load_frag_tr44(fa, sVc, LV, 32 * kp, 16 * jb, g, li);
               an = mma(fa, pf[kp], an);
             }
           }
