@@ -790,6 +790,22 @@ void la_fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int b = 0; b < NB2; ++b) load2(b, rq[b], rk2[b], rv2[b]);
   };
+  // Phase-2 staging of chunk c into its tile set (see the chunk loop).
+  auto stage2 = [&](int c, const Slab<T, QW, C> &sq, const Slab<T, QW, C> &sk,
+                    const Slab<T, D, C> &sv) {
+    const int sc = set_of(c);
+    if constexpr (PF) {
+      stage_rows_pf<T, D, C, LX>(sq, sXq, pc0, lsm, C, tid);
+      if (CAUSAL)
+        stage_rows_pf<T, D, C, LX>(sk, sXk, pc0 + C, lsm, rows_of(c), tid);
+    } else {
+      stage_queries<T, DF, C, LQ, ELU>(sq, sQ + sc * F::SQ, tid);
+      if (CAUSAL && !resident)
+        stage_keys<T, DF, C, LQ, DECAY, true, ELU>(
+            sk, sK + sc * F::SQ, sKw + sc * F::SQ, gp, dk.b, rows_of(c), tid);
+    }
+    if (CAUSAL) stage_values<T, D, C, LV>(sv, sV + sc * F::SV, tid);
+  };
 
   // The loops below run whole revolutions of their register ring (padding
   // chunks past nch have zero keys and store nothing) and stage chunk c + 1
@@ -896,6 +912,9 @@ void la_fwd_kernel(FwdArgs a) {
       // ring follows the aggregates' loads, which would otherwise complete
       // only after them (loads complete in order)
       load2(0, rq[0], rk2[0], rv2[0]);
+      // chunk 0 is staged while the predecessors finish (its tiles are free:
+      // phase 1 ended with a workgroup barrier after its last use of them)
+      stage2(0, rq[0], rk2[0], rv2[0]);
       if (need > 0) wait_flags(line, need, a.sync + kSyncTimeoutWord);
 #pragma unroll
       for (int i = 0; i < TW; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -935,6 +954,7 @@ void la_fwd_kernel(FwdArgs a) {
       }
 #pragma unroll
       for (int b = 1; b < NB2; ++b) load2(b, rq[b], rk2[b], rv2[b]);
+      load2(NB2, rq[0], rk2[0], rv2[0]);
     } else {
       ring2_first();
     }
@@ -946,21 +966,6 @@ void la_fwd_kernel(FwdArgs a) {
   // Every wave runs the same instructions (masks instead of branches on its
   // output strip), so a chunk is one straight block the compiler can
   // interleave.
-  auto stage2 = [&](int c, const Slab<T, QW, C> &sq, const Slab<T, QW, C> &sk,
-                    const Slab<T, D, C> &sv) {
-    const int sc = set_of(c);
-    if constexpr (PF) {
-      stage_rows_pf<T, D, C, LX>(sq, sXq, pc0, lsm, C, tid);
-      if (CAUSAL)
-        stage_rows_pf<T, D, C, LX>(sk, sXk, pc0 + C, lsm, rows_of(c), tid);
-    } else {
-      stage_queries<T, DF, C, LQ, ELU>(sq, sQ + sc * F::SQ, tid);
-      if (CAUSAL && !resident)
-        stage_keys<T, DF, C, LQ, DECAY, true, ELU>(
-            sk, sK + sc * F::SQ, sKw + sc * F::SQ, gp, dk.b, rows_of(c), tid);
-    }
-    if (CAUSAL) stage_values<T, D, C, LV>(sv, sV + sc * F::SV, tid);
-  };
   auto features2 = [&](int c) {
     if constexpr (PF) {
       performer_features<F, T, true, CAUSAL, DECAY, true>(
@@ -971,8 +976,10 @@ void la_fwd_kernel(FwdArgs a) {
   };
   __syncthreads();  // gp and the constant tile parts ready, phase 1 done
   publish_state<F>(S, sST, w, g, li);  // the entering state, set 0
-  stage2(0, rq[0], rk2[0], rv2[0]);
-  load2(NB2, rq[0], rk2[0], rv2[0]);
+  if (!(MULTI && a.nseg > 1)) {  // else staged during the exchange
+    stage2(0, rq[0], rk2[0], rv2[0]);
+    load2(NB2, rq[0], rk2[0], rv2[0]);
+  }
   __syncthreads();
   features2(0);
 
