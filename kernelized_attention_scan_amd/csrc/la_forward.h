@@ -964,8 +964,9 @@ void la_fwd_kernel(FwdArgs a) {
 
   // ---------------- phase 2: chunk loop ----------------
   // Every wave runs the same instructions (masks instead of branches on its
-  // output strip), so a chunk is one straight block the compiler can
-  // interleave.
+  // output strip, apart from skipping whole key strips), so a chunk is one
+  // straight block the compiler can interleave.  The fused Performer map
+  // adds a feature step after each staging.
   auto features2 = [&](int c) {
     if constexpr (PF) {
       performer_features<F, T, true, CAUSAL, DECAY, true>(
