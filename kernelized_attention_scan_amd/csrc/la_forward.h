@@ -675,6 +675,26 @@ void la_fwd_kernel(FwdArgs a) {
   // already running, so no co-residency is needed.  The table of decay
   // powers and the constant tile parts are set up while the ticket is in
   // flight.
+  const T *qb = static_cast<const T *>(a.q) + unit * a.n * QW;
+  const T *kb = static_cast<const T *>(a.k) + unit * a.n * QW;
+  const T *vb = static_cast<const T *>(a.v) + unit * a.n * D;
+  T *ob = static_cast<T *>(a.out) + unit * a.n * D;
+  // Before the ticket returns, each workgroup loads the first phase-1 chunk
+  // of the segment its block would take in block order (guess).  The
+  // segments of a unit share an XCD, so together they bring every
+  // segment's first chunk into that L2: a workgroup whose ticket differs
+  // reloads from there.
+  constexpr bool GUESS = MULTI && CAUSAL && F::NB1 == 1;
+  const int guess = static_cast<int>(blk % a.nseg);
+  Slab<T, QW, C> gk;
+  Slab<T, D, C> gv;
+  if (GUESS && a.nseg > 1) {
+    const int64_t g0 = guess * a.seg_len;
+    const int grows =
+        static_cast<int>(max<int64_t>(0, min<int64_t>(C, a.n - g0)));
+    gk.load(kb, g0 < a.n ? g0 : 0, grows, tid);
+    gv.load(vb, g0 < a.n ? g0 : 0, grows, tid);
+  }
   unsigned tk = 0u;
   if (MULTI && CAUSAL && a.nseg > 1 && tid == 0)
     tk = __hip_atomic_fetch_add(line + kSyncTicketWord, 1u, __ATOMIC_RELAXED,
@@ -744,10 +764,6 @@ void la_fwd_kernel(FwdArgs a) {
   // has probably recorded (0 where not read)
   unsigned recs = 0u;
 
-  const T *qb = static_cast<const T *>(a.q) + unit * a.n * QW;
-  const T *kb = static_cast<const T *>(a.k) + unit * a.n * QW;
-  const T *vb = static_cast<const T *>(a.v) + unit * a.n * D;
-  T *ob = static_cast<T *>(a.out) + unit * a.n * D;
   const int64_t start = seg * a.seg_len;
   const int64_t end = min(a.n, start + a.seg_len);
   const int nch = static_cast<int>((end - start + C - 1) / C);
@@ -826,7 +842,14 @@ void la_fwd_kernel(FwdArgs a) {
         sv.load(vb, r0, rows_of(c), tid);
       };
 #pragma unroll
-      for (int b = 0; b < NB1; ++b) load1(b, rk[b], rv[b]);
+      for (int b = 0; b < NB1; ++b) {
+        if (GUESS && b == 0 && a.nseg > 1 && seg == guess) {
+          rk[0] = gk;  // the guess was right
+          rv[0] = gv;
+        } else {
+          load1(b, rk[b], rv[b]);
+        }
+      }
       // phi(K) of chunk c: its resident slot (padding chunks: the unused
       // sQ), else the sK slot of its set
       auto keys1 = [&](int c) -> T * {
