@@ -943,16 +943,16 @@ void la_fwd_kernel(FwdArgs a) {
       for (int i = 0; i < TW; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int64_t epos = CAUSAL ? start : a.n;
       // Groups of GRP aggregates (about 12 tiles per lane, 24 with one
-      // workgroup per CU); the loads of a group are unconditional (indices
-      // past the last clamp to it, with weight 0) so they are all in flight
-      // together.
+      // workgroup per CU), all loads of a group in flight together; members
+      // past the last aggregate load nothing (a wave-uniform condition) and
+      // add with weight 0.
       constexpr int TILES = F::OCC == 1 ? 24 : 12;
       constexpr int GRP = TW >= TILES ? 1 : pow2_floor(TILES / TW);
       for (int j0 = 0; j0 < need; j0 += GRP) {
         f32x4 buf[GRP][TW];
 #pragma unroll
         for (int u = 0; u < GRP; ++u) {
-          const int j = min(j0 + u, need - 1);
+          const int j = j0 + u;
           const float *sj = ub + static_cast<int64_t>(j) * F::SLOT;
 #pragma unroll
           for (int m = 0; m < F::FPW; ++m)
@@ -961,7 +961,9 @@ void la_fwd_kernel(FwdArgs a) {
               const int jb = tile_jb<F>(w, mj);
               const int idx = tile_fb<F>(w, m) * F::NJA + jb;
               buf[u][m * F::JPW + mj] =
-                  *reinterpret_cast<const f32x4 *>(sj + (idx * 64 + lane) * 4);
+                  j < need ? *reinterpret_cast<const f32x4 *>(
+                                 sj + (idx * 64 + lane) * 4)
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
 #pragma unroll
