@@ -777,15 +777,18 @@ void la_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int i = 0; i < TW; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Chunk helpers: valid rows of chunk c (0 past the end), the chunk a ring
-  // load fetches for chunk c (clamped to the last one), and the tile set
-  // chunk c uses (c % 2 with two sets).
+  // Chunk helpers: valid rows of chunk c (0 past the end), the chunk whose
+  // start a buffer resource for chunk c takes as its base (clamped to the
+  // last one, so the base stays inside the array; padding chunks cover no
+  // rows), and the tile set chunk c uses (c % 2 with two sets).
   const int last_rows =  // rows of the last chunk (1 .. C when nch > 0)
       static_cast<int>(end - (start + static_cast<int64_t>(nch - 1) * C));
   auto rows_of = [&](int c) -> int {
     return c < nch - 1 ? C : c == nch - 1 ? last_rows : 0;
   };
-  auto clamp_chunk = [&](int c) -> int { return c < nch ? c : nch - 1; };
+  auto clamp_chunk = [&](int c) -> int {
+    return c < nch ? c : max(nch - 1, 0);
+  };
   auto set_of = [&](int c) -> int { return F::NBUF == 2 ? (c & 1) : 0; };
 
   // Phase-2 register ring, first revolution; in the segmented kernel these
