@@ -1073,10 +1073,12 @@ void la_fwd_kernel(FwdArgs a) {
       for (int kq = 0; kq < DFP / 32; ++kq)
         load_frag8(qf[kq], sQc + t * LQ + 32 * kq + 8 * g);
       Frag<T> pf[NPK];
-      // Key strips above the diagonal strip only hold masked products: from
-      // d' = 64 on they are skipped (a branch on the wave's strip), for
-      // narrower features computed and masked (no branch).
-      constexpr bool SKIP = DFP >= 64;
+      // Key strips above the diagonal strip only hold masked products: they
+      // are skipped (a branch on the wave's strip) from d' = 128 on, and at
+      // d' = 64 unless the keys are resident; otherwise computed and masked
+      // (no branch).  Measured: with resident keys, whose chunk loop has the
+      // least other work, the branch costs more than the products it saves.
+      constexpr bool SKIP = DFP >= 128 || (DFP >= 64 && !RES);
       if constexpr (CAUSAL) {
         f32x4 pt[STRIPS];
 #pragma unroll
