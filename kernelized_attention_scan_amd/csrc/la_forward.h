@@ -220,6 +220,16 @@ template <typename F>
 __device__ __forceinline__ int tile_jb(int w, int m) {
   return F::NF >= kWaves ? m : min(w / F::NF + F::WPF * m, F::NJA - 1);
 }
+// Whether state tile m of wave w is a copy of another wave's ones-block
+// tile (dup), or the ones-block tile whose copies other waves hold (owner).
+template <typename F>
+__device__ __forceinline__ bool dup_tile(int w, int m) {
+  return F::NF < kWaves && w / F::NF + F::WPF * m > F::NJA - 1;
+}
+template <typename F>
+__device__ __forceinline__ bool owns_ones_tile(int w, int m) {
+  return F::NF < kWaves && w / F::NF + F::WPF * m == F::NJA - 1;
+}
 // Whether a wave's state tile m is the ones block (or its copy) in every
 // wave, which the tile layout fixes at compile time.
 template <typename F>
@@ -949,6 +959,10 @@ void la_fwd_kernel(FwdArgs a) {
       // workgroup per CU), all loads of a group in flight together; members
       // past the last aggregate load nothing (a wave-uniform condition) and
       // add with weight 0.
+      // With two tile sets, copies of the ones-block tile are not loaded:
+      // their owners pass the sum on through tile set 1 of sQ (free until
+      // chunk 1 is staged), read back after the next barrier.
+      constexpr bool DEDUP = F::NBUF == 2 && F::NF < kWaves;
       constexpr int TILES = F::OCC == 1 ? 24 : 12;
       constexpr int GRP = TW >= TILES ? 1 : pow2_floor(TILES / TW);
       for (int j0 = 0; j0 < need; j0 += GRP) {
@@ -964,9 +978,10 @@ void la_fwd_kernel(FwdArgs a) {
               const int jb = tile_jb<F>(w, mj);
               const int idx = tile_fb<F>(w, m) * F::NJA + jb;
               buf[u][m * F::JPW + mj] =
-                  j < need ? *reinterpret_cast<const f32x4 *>(
-                                 sj + (idx * 64 + lane) * 4)
-                           : f32x4{0.f, 0.f, 0.f, 0.f};
+                  j < need && !(DEDUP && dup_tile<F>(w, mj))
+                      ? *reinterpret_cast<const f32x4 *>(
+                            sj + (idx * 64 + lane) * 4)
+                      : f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
 #pragma unroll
@@ -979,6 +994,13 @@ void la_fwd_kernel(FwdArgs a) {
 #pragma unroll
           for (int i = 0; i < TW; ++i) S[i] += wj * buf[u][i];
         }
+      }
+      if constexpr (DEDUP) {
+        f32x4 *xs = reinterpret_cast<f32x4 *>(sQ + F::SQ);
+#pragma unroll
+        for (int mj = 0; mj < F::JPW; ++mj)
+          if (owns_ones_tile<F>(w, mj))
+            xs[tile_fb<F>(w, 0) * 64 + lane] = S[mj];
       }
 #pragma unroll
       for (int b = 1; b < NB2; ++b) load2(b, rq[b], rk2[b], rv2[b]);
@@ -1004,6 +1026,14 @@ void la_fwd_kernel(FwdArgs a) {
     }
   };
   __syncthreads();  // gp and the constant tile parts ready, phase 1 done
+  if constexpr (MULTI && F::NBUF == 2 && F::NF < kWaves) {
+    if (a.nseg > 1) {  // copies of the ones-block tile from their owners
+      const f32x4 *xs = reinterpret_cast<const f32x4 *>(sQ + F::SQ);
+#pragma unroll
+      for (int mj = 0; mj < F::JPW; ++mj)
+        if (dup_tile<F>(w, mj)) S[mj] = xs[tile_fb<F>(w, 0) * 64 + lane];
+    }
+  }
   publish_state<F>(S, sST, w, g, li);  // the entering state, set 0
   if (!(MULTI && a.nseg > 1)) {  // else staged during the exchange
     stage2(0, rq[0], rk2[0], rv2[0]);
