@@ -98,13 +98,15 @@ size_t la_forward_workspace_bytes(int B, int H, int64_t n, int d, int d_feat,
  *   omega    : device fp32 [d][d_feat] for PERFORMER, else ignored
  *   decay    : device fp32 [H], one a per head, or NULL for eqs 7-8
  *   workspace: device, at least la_forward_workspace_bytes(...) bytes; NULL
- *              allowed only when that is 0.  When the sequence is split into
- *              segments (B * H < 512) it starts with a synchronisation area
- *              of 65792 bytes: that area must be zero before the first call
- *              that uses the workspace (zero the whole workspace once at
- *              allocation) and every call leaves it zero.  The rest is
- *              scratch.  Calls that may run concurrently (different streams)
- *              must not share a workspace.
+ *              allowed only when that is 0.  Whenever a call uses a
+ *              workspace, its first 65792 bytes are a synchronisation area:
+ *              calls whose sequence is split into segments (B * H < 512)
+ *              use it, and no call writes anything else there.  It must be
+ *              zero before the first call that uses the workspace (zero the
+ *              whole workspace once at allocation) and every call leaves it
+ *              zero, so one workspace can serve calls of any sizes.  The
+ *              rest is scratch.  Calls that may run concurrently (different
+ *              streams) must not share a workspace.
  *   Supported: d in {16, 32, 64, 128}; d_feat in {16, 32, 64, 128, 256}.
  *   No epsilon is added to the denominator: with IDENTITY features whose
  *   q'.nu is zero the output is inf/nan (IEEE).

@@ -63,7 +63,16 @@ struct FwdPlan {
   size_t feat_bytes = 0;    // one of Q', K' (unfused PERFORMER only)
   size_t sync_bytes = 0;    // synchronisation area
   size_t state_bytes = 0;   // synchronisation area + segment aggregates
-  size_t total() const { return state_bytes + 2 * feat_bytes; }
+  // Q', K' start after the aggregates, and never below the fixed
+  // synchronisation area even when this call has no segments: a workspace
+  // shared with segmented calls keeps that area zero between calls, so no
+  // other data may ever be written there.
+  size_t feat_offset() const {
+    return state_bytes > 0 ? state_bytes : la::kSyncBytes;
+  }
+  size_t total() const {
+    return feat_bytes > 0 ? feat_offset() + 2 * feat_bytes : state_bytes;
+  }
 };
 
 // Validates la_forward's sizes and enums (not pointers) and fills the plan.
@@ -172,7 +181,7 @@ static la_status forward_impl(const void *q, const void *k, const void *v, void 
     const void *qf = q, *kf = k;
     if (map == LA_MAP_PERFORMER && !p.fused_performer) {
       // Q', K' into the workspace, then the identity-map forward over them.
-      unsigned char *fq = ws + p.state_bytes, *fk = fq + p.feat_bytes;
+      unsigned char *fq = ws + p.feat_offset(), *fk = fq + p.feat_bytes;
       hipError_t e = la::launch_featmap_performer(q, fq, omega, units * n, d,
                                                   d_feat, dtype, dtype, s);
       if (e == hipSuccess)

@@ -285,6 +285,34 @@ def test_exchange_never_times_out_and_leaves_area_zero(cfg):
     assert torch.count_nonzero(sync).item() == 0
 
 
+def test_shared_workspace_after_unfused_performer():
+    """One workspace serves calls of different sizes: an unfused Performer
+    call without segments (fp32 storage) writes its q', k' features into the
+    workspace, and a segmented call after it must still find the
+    synchronisation area zero."""
+    pf = I.PrefillConfig("pf_f32", B=1, H=2, n=17, d=32, dtype=torch.float32,
+                         mapk=I.MAP_PERFORMER, m=128, decay=(-3.0, -1.0),
+                         qk_std=0.5)
+    seg = I.PrefillConfig("seg_bf16", B=2, H=2, n=65, d=32)
+    need = max(K.forward_workspace_bytes(c.B, c.H, c.n, c.d, c.d_feat,
+                                         I.MAP_NAMES[c.mapk], c.dtype, c.causal)
+               for c in (pf, seg))
+    assert need > SYNC_BYTES
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    x = I.make_prefill(pf, 11)
+    K.forward(dev(x["q"]), dev(x["k"]), dev(x["v"]), "performer",
+              omega=dev(x["omega"]), decay=dev(x["decay"]), workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(ws[:SYNC_BYTES]).item() == 0
+    y = I.make_prefill(seg, 12)
+    out = K.forward(dev(y["q"]), dev(y["k"]), dev(y["v"]), "elu1",
+                    workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle.forward(f64(y["q"]), f64(y["k"]), f64(y["v"]), oracle.MAP_ELU1,
+                         None, None, True)
+    assert rel(out, ref) <= TOL[torch.bfloat16]
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_constant_v_gives_constant_output(dtype):
     cfg = I.ELU1_CAUSAL.replace(B=1, H=4, n=3000, dtype=dtype,

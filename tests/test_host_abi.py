@@ -119,6 +119,12 @@ def test_workspace_bytes(lib):
     # non-causal over one segment keeps its total on chip; several need one
     assert K.forward_workspace_bytes(1, 1, 64, 64, 64, causal=False) == 0
     assert K.forward_workspace_bytes(1, 1, 4096, 64, 64, causal=False) > 0
+    # unfused Performer without segments: Q', K' still start after the
+    # synchronisation area, which a shared workspace keeps zero for
+    # segmented calls
+    f32 = __import__("torch").float32
+    assert K.forward_workspace_bytes(1, 2, 17, 32, 128, "performer",
+                                     dtype=f32) == sync + 2 * a256(2 * 17 * 128 * 4)
     # fp32 storage with d_feat 256 and d 128 does not fit in LDS
     assert K.forward_workspace_bytes(1, 1, 64, 128, 256, "identity",
                                      dtype=__import__("torch").float32) == 0
