@@ -961,8 +961,10 @@ void la_fwd_kernel(FwdArgs a) {
       // add with weight 0.
       // With two tile sets, copies of the ones-block tile are not loaded:
       // their owners pass the sum on through tile set 1 of sQ (free until
-      // chunk 1 is staged), read back after the next barrier.
-      constexpr bool DEDUP = F::NBUF == 2 && F::NF < kWaves;
+      // chunk 1 is staged), read back after the next barrier.  Not with
+      // padded features (d' < 32): the padding columns of sQ are zeroed
+      // once per kernel and must stay zero.
+      constexpr bool DEDUP = F::NBUF == 2 && F::NF < kWaves && DFP == DF;
       constexpr int TILES = F::OCC == 1 ? 24 : 12;
       constexpr int GRP = TW >= TILES ? 1 : pow2_floor(TILES / TW);
       for (int j0 = 0; j0 < need; j0 += GRP) {
@@ -1026,7 +1028,7 @@ void la_fwd_kernel(FwdArgs a) {
     }
   };
   __syncthreads();  // gp and the constant tile parts ready, phase 1 done
-  if constexpr (MULTI && F::NBUF == 2 && F::NF < kWaves) {
+  if constexpr (MULTI && F::NBUF == 2 && F::NF < kWaves && DFP == DF) {
     if (a.nseg > 1) {  // copies of the ones-block tile from their owners
       const f32x4 *xs = reinterpret_cast<const f32x4 *>(sQ + F::SQ);
 #pragma unroll

@@ -313,6 +313,23 @@ def test_shared_workspace_after_unfused_performer():
     assert rel(out, ref) <= TOL[torch.bfloat16]
 
 
+def test_padded_features_many_segments():
+    """d' = 16 features (padded to 32 columns in LDS) over many segmented
+    units: the padding columns of every tile set must stay zero for the
+    whole kernel (scratch written there once turned outputs into NaN)."""
+    cfg = I.PrefillConfig("pad16", B=16, H=2, n=5000, d=128, m=16,
+                          mapk=I.MAP_IDENTITY)
+    q, k, v, dec = _identity_inputs(cfg, 4)
+    out = K.forward(q.cuda(), k.cuda(), v.cuda(), "identity", causal=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    for b, h in [(0, 0), (cfg.B - 1, cfg.H - 1)]:
+        ref = oracle.forward(f64(q[b:b + 1, h:h + 1]), f64(k[b:b + 1, h:h + 1]),
+                             f64(v[b:b + 1, h:h + 1]), oracle.MAP_IDENTITY,
+                             None, None, True)
+        assert rel(out[b:b + 1, h:h + 1], ref) <= TOL[torch.bfloat16]
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_constant_v_gives_constant_output(dtype):
     cfg = I.ELU1_CAUSAL.replace(B=1, H=4, n=3000, dtype=dtype,
