@@ -330,6 +330,59 @@ def test_padded_features_many_segments():
         assert rel(out[b:b + 1, h:h + 1], ref) <= TOL[torch.bfloat16]
 
 
+def test_random_shapes_share_one_workspace():
+    """32 random shapes (maps, d, d', n with ragged tails, B, H, decay,
+    causal, storage type; seed fixed) in one sequence, all through the
+    binding's cached workspace, so each call also runs after calls of other
+    sizes on the same memory.  Sampled units against the oracle."""
+    import random
+    rng = random.Random(777)
+    fails = []
+    for it in range(32):
+        mapk = rng.choice([I.MAP_ELU1, I.MAP_ELU1, I.MAP_PERFORMER,
+                           I.MAP_IDENTITY])
+        d = (rng.choice([16, 32, 64, 64, 128]) if mapk != I.MAP_PERFORMER
+             else rng.choice([32, 64]))
+        m = (rng.choice([32, 64, 128, 256]) if mapk == I.MAP_PERFORMER else
+             rng.choice([16, 32, 64, 128, 256]) if mapk == I.MAP_IDENTITY
+             else 0)
+        dtype = rng.choice([torch.bfloat16, torch.bfloat16, torch.float32])
+        B, H = rng.choice([1, 2, 3, 4, 16]), rng.choice([1, 2, 5, 8, 16])
+        n = rng.choice([1, 17, 63, 64, 65, 500, 1000, 2049, 4096, 5000])
+        decay = rng.choice([None, (-3.0, -1.0)])
+        causal = rng.random() < 0.8
+        cfg = I.PrefillConfig(f"rand{it}", B=B, H=H, n=n, d=d, dtype=dtype,
+                              mapk=mapk, m=m, decay=decay, causal=causal,
+                              qk_std=0.5 if mapk == I.MAP_PERFORMER else 1.0)
+        units = [(0, 0), (B - 1, H - 1)]
+        try:
+            if mapk == I.MAP_IDENTITY:
+                q, k, v, dec = _identity_inputs(cfg, it)
+                out = K.forward(q.cuda(), k.cuda(), v.cuda(), "identity",
+                                decay=dev(dec), causal=causal)
+                torch.cuda.synchronize()
+                err = 0.0
+                for b, h in units:
+                    dd = None if dec is None else f64(dec[h:h + 1])
+                    ref = oracle.forward(
+                        f64(q[b:b + 1, h:h + 1]), f64(k[b:b + 1, h:h + 1]),
+                        f64(v[b:b + 1, h:h + 1]), oracle.MAP_IDENTITY, None,
+                        dd, causal)
+                    err = max(err, rel(out[b:b + 1, h:h + 1], ref))
+            else:
+                err = run_forward(cfg, seed=it, units=units)
+        except K.LinAttnError as e:
+            if e.status == K._binding.LA_ERR_UNSUPPORTED:
+                continue  # a combination not built (LDS limit)
+            raise
+        except AssertionError as e:
+            fails.append((cfg, str(e)))
+            continue
+        if err > TOL[dtype]:
+            fails.append((cfg, err))
+    assert not fails, fails
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_constant_v_gives_constant_output(dtype):
     cfg = I.ELU1_CAUSAL.replace(B=1, H=4, n=3000, dtype=dtype,
