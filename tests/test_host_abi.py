@@ -130,6 +130,22 @@ def test_workspace_bytes(lib):
                                      dtype=__import__("torch").float32) == 0
 
 
+@pytest.mark.parametrize("B,H,n", [(1, 1, 1), (1, 2, 17), (2, 3, 64),
+                                   (4, 8, 999), (16, 40, 64), (1, 1, 5000)])
+@pytest.mark.parametrize("d,m", [(32, 64), (64, 256), (128, 128)])
+def test_unfused_performer_features_never_overlap_sync_area(B, H, n, d, m):
+    # fp32 storage takes the unfused Performer path: q', k' go through the
+    # workspace, and they always start after the synchronisation area
+    # (which a workspace shared with segmented calls keeps zero), whether
+    # or not this call has segments
+    import torch
+    need = K.forward_workspace_bytes(B, H, n, d, m, "performer",
+                                     dtype=torch.float32)
+    sync = 256 + 512 * 128
+    feat = (B * H * n * m * 4 + 255) // 256 * 256
+    assert need >= sync + 2 * feat
+
+
 def test_featmap_rejects(lib):
     f = lib.la_featmap
     assert f(FAKE, FAKE, None, -1, 64, 0, 1, 1, 1, None) == B.LA_ERR_INVALID_ARG
