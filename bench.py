@@ -6,9 +6,11 @@ HBM-resident input:
   prefill workloads: one la_forward call (Performer: the two feature-map
     launches and the chunked forward it makes);
   decode: one la_decode_step over every (sequence, head) unit.
-Default workload: elu+1 causal, B=4, H=8, n=4096, d=d'=64, bf16 storage.
-Its inputs (67 MB per set) fit in the 256 MB MALL, so the timed loop rotates
-over enough distinct buffer sets (> 300 MB) that every step reads from HBM.
+Default workload: the decayed recurrence (eqs 10-11), elu+1 causal, B=2,
+H=16, n=65536, d=d'=128, bf16 storage, one decay value per head.  Its inputs
+(2.1 GB) do not fit in the 256 MB MALL; workloads whose inputs do fit (elu1,
+performer) rotate over enough distinct buffer sets (> 300 MB) that every step
+reads from HBM.
 
 Prints one JSON line: throughput (tokens/s = B*H*n per second; decode:
 (sequence, head) units per second), the roofline of the dominant kernel
@@ -51,7 +53,7 @@ def workloads():
     from kernelized_attention_scan_amd import inputs as I
     return {"elu1": I.ELU1_CAUSAL, "decayed": I.DECAYED,
             "performer": I.PERFORMER, "tiny": I.TINY_FP32,
-            "decode": I.DECODE}
+            "decode": I.DECODE, "noncausal": I.ELU1_NONCAUSAL}
 
 
 def esize(dtype) -> int:
@@ -212,7 +214,9 @@ def prefill_leg(torch, K, I, cfg, args, dev):
         cfg.causal) < 2 * cfg.tokens * cfg.m * esz
     if cfg.mapk != 2 or fused:
         # one kernel per step: the chunked forward (Performer: map fused)
-        kern = {"kernel": "la_fwd_kernel (chunked causal forward"
+        kern = {"kernel": "la_fwd_kernel (chunked "
+                          + ("causal" if cfg.causal else
+                             "non-causal: aggregates, then readout") + " forward"
                           + (", Performer map fused)" if fused else ")"),
                 "ms": ms, "bytes": byts, "flops": flops}
     else:
@@ -298,7 +302,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="elu1", choices=sorted(workloads()))
+    ap.add_argument("--workload", default="decayed",
+                    choices=sorted(workloads()))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",

@@ -52,7 +52,8 @@ typedef enum la_status {
   LA_ERR_INVALID_ARG = 1, /* null pointer, negative size, inconsistent sizes */
   LA_ERR_UNSUPPORTED = 2, /* valid request outside the built kernel set      */
   LA_ERR_WORKSPACE = 3,   /* workspace NULL but required                     */
-  LA_ERR_HIP = 4          /* a HIP launch or runtime call failed             */
+  LA_ERR_HIP = 4,         /* a HIP launch or runtime call failed             */
+  LA_ERR_EXCHANGE = 5     /* la_workspace_check: a segment exchange failed   */
 } la_status;
 
 typedef enum la_map {
@@ -107,6 +108,17 @@ size_t la_forward_workspace_bytes(int B, int H, int64_t n, int d, int d_feat,
  *              zero, so one workspace can serve calls of any sizes.  The
  *              rest is scratch.  Calls that may run concurrently (different
  *              streams) must not share a workspace.
+ *              What a violation does: causal segments of a unit exchange
+ *              their partial sums through flags in that area.  A flag left
+ *              set (area not zeroed, or a concurrent call on another stream)
+ *              lets a segment read a partial sum before it is written: its
+ *              outputs are then wrong.  A ticket found out of range marks
+ *              the workspace's status word "corrupt"; a wait that never sees
+ *              its flag gives up after a bounded number of polls (about a
+ *              second or more by default), marks the status word "timeout"
+ *              and writes NaN to every output that depended on the missing
+ *              sum.  The kernel always finishes.  la_workspace_check reports
+ *              and clears that status word.
  *   Supported: d in {16, 32, 64, 128}; d_feat in {16, 32, 64, 128, 256}.
  *   No epsilon is added to the denominator: with IDENTITY features whose
  *   q'.nu is zero the output is inf/nan (IEEE).
@@ -155,6 +167,26 @@ la_status la_decode_step(float *mu, float *nu, const void *q, const void *k,
                          const void *v, void *out, int S, int H, int d,
                          int d_feat, la_map map, const float *omega,
                          const float *decay, la_dtype dtype, void *stream);
+
+/*
+ * la_workspace_check -- whether any call that used this workspace since the
+ * last check had a segment exchange fail (see la_forward's workspace notes):
+ * LA_OK if none, LA_ERR_EXCHANGE otherwise (la_last_error says which kind;
+ * the status is then cleared).  It waits for the work enqueued on `stream`,
+ * then reads 4 bytes of the workspace: a synchronising diagnostic, not for a
+ * hot loop.  workspace: device, a la_forward workspace (at least 65792
+ * bytes); LA_ERR_INVALID_ARG if NULL.
+ */
+la_status la_workspace_check(void *workspace, void *stream);
+
+/*
+ * la_set_exchange_spin_limit -- diagnostics: polls a segment's wait for
+ * another segment's partial sum makes before giving up (0 restores the
+ * default, about 2^22 polls).  Process-wide; applies to calls enqueued
+ * afterwards.  A small limit lets a test force the failure path of
+ * la_workspace_check while every kernel still ends normally.
+ */
+void la_set_exchange_spin_limit(unsigned spins);
 
 /* Static description of a status code (never NULL). */
 const char *la_status_str(la_status status);

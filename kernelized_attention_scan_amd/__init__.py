@@ -6,11 +6,13 @@ The computation runs in hand-written HIP kernels behind the C ABI of
 ``inputs``.  Build the library with ``python -m kernelized_attention_scan_amd.build``.
 """
 from ._binding import (LA_BF16, LA_F32, LIB_PATH, MAP_ELU1, MAP_IDENTITY,
-                       MAP_PERFORMER, SYMBOLS, LinAttnError, decode_step,
-                       featmap, forward, forward_workspace_bytes, load_library,
-                       new_workspace)
+                       MAP_PERFORMER, SYMBOLS, LinAttnError, cached_workspace,
+                       decode_step, featmap, forward, forward_workspace_bytes,
+                       load_library, new_workspace, set_exchange_spin_limit,
+                       workspace_check)
 
 __all__ = ["forward", "decode_step", "featmap", "forward_workspace_bytes",
-           "new_workspace",
+           "new_workspace", "workspace_check", "cached_workspace",
+           "set_exchange_spin_limit",
            "load_library", "LinAttnError", "LIB_PATH", "SYMBOLS", "MAP_IDENTITY",
            "MAP_ELU1", "MAP_PERFORMER", "LA_F32", "LA_BF16"]

@@ -14,8 +14,8 @@ from typing import Optional
 
 import torch
 
-LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP = \
-    range(5)
+(LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP,
+ LA_ERR_EXCHANGE) = range(6)
 MAP_IDENTITY, MAP_ELU1, MAP_PERFORMER = 0, 1, 2
 LA_F32, LA_BF16 = 0, 1
 
@@ -27,8 +27,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
 
 # Exported symbols, in the order include/linattn.h declares them.
 SYMBOLS = ("la_featmap", "la_forward_workspace_bytes", "la_forward",
-           "la_forward_state", "la_decode_step", "la_status_str",
-           "la_last_error")
+           "la_forward_state", "la_decode_step", "la_workspace_check",
+           "la_set_exchange_spin_limit", "la_status_str", "la_last_error")
 
 _lock = threading.Lock()
 _lib = None
@@ -73,6 +73,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                        i32, i32, vp, vp, i32, vp]
         lib.la_decode_step.restype = i32
+        lib.la_workspace_check.argtypes = [vp, vp]
+        lib.la_workspace_check.restype = i32
+        lib.la_set_exchange_spin_limit.argtypes = [ctypes.c_uint]
+        lib.la_set_exchange_spin_limit.restype = None
         lib.la_status_str.argtypes = [i32]
         lib.la_status_str.restype = ctypes.c_char_p
         lib.la_last_error.argtypes = []
@@ -117,13 +121,47 @@ def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
     return t
 
 
-def _f32(t: Optional[torch.Tensor], name: str) -> Optional[torch.Tensor]:
-    if t is None:
-        return None
-    _dev(t, name)
-    if t.dtype != torch.float32:
-        raise TypeError(f"{name} must be float32")
-    return t
+def _check_out(out: torch.Tensor, shape, dtype) -> None:
+    """A caller-supplied out must have the expected shape and dtype (one of
+    another size would be written past its end)."""
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected "
+                         f"{tuple(shape)}")
+    if out.dtype != dtype:
+        raise TypeError(f"out has dtype {out.dtype}, expected {dtype}")
+
+
+def _check_omega(omega: Optional[torch.Tensor], mapk: int, d: int) -> int:
+    """omega must be fp32 [d, m] for the Performer map; returns m (0 when
+    the map needs no omega)."""
+    if mapk != MAP_PERFORMER:
+        return 0
+    if omega is None:
+        raise ValueError("the performer map needs omega [d, m]")
+    if omega.dtype != torch.float32:
+        raise TypeError("omega must be float32")
+    if omega.dim() != 2 or omega.shape[0] != d:
+        raise ValueError(f"omega must be [d={d}, m], got {tuple(omega.shape)}")
+    return int(omega.shape[1])
+
+
+def _check_decay(decay: Optional[torch.Tensor], H: int) -> None:
+    if decay is None:
+        return
+    if decay.dtype != torch.float32:
+        raise TypeError("decay must be float32")
+    if decay.dim() != 1 or decay.shape[0] != H:
+        raise ValueError(f"decay must be [H={H}], got {tuple(decay.shape)}")
+
+
+def _on_gpu(ref: torch.Tensor, *named) -> None:
+    """Every given tensor is a contiguous GPU tensor on ref's device."""
+    for t, name in named:
+        if t is None:
+            continue
+        _dev(t, name)
+        if t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
 
 
 def _stream(device) -> ctypes.c_void_p:
@@ -164,15 +202,18 @@ def featmap(x: torch.Tensor, feature_map="elu1", omega=None,
             out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """phi row by row over the last axis: [..., d] -> [..., d_feat]."""
     lib = load_library()
-    _dev(x, "x")
     mapk = _map_code(feature_map)
     d = x.shape[-1]
-    m = omega.shape[1] if mapk == MAP_PERFORMER else d
+    m = _check_omega(omega, mapk, d) or d
     out_dtype = out_dtype or x.dtype
+    _dtype_code(x.dtype)
+    _dtype_code(out_dtype)
+    if out is not None:
+        _check_out(out, x.shape[:-1] + (m,), out.dtype)
+        _dtype_code(out.dtype)
+    _on_gpu(x, (x, "x"), (out, "out"), (omega, "omega"))
     if out is None:
         out = torch.empty(x.shape[:-1] + (m,), dtype=out_dtype, device=x.device)
-    _dev(out, "out")
-    _f32(omega, "omega")
     st = lib.la_featmap(_ptr(x), _ptr(out), _ptr(omega), x.numel() // d, d, m,
                         mapk, _dtype_code(x.dtype), _dtype_code(out.dtype),
                         _stream(x.device))
@@ -195,8 +236,6 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     receive the state after the last position (la_forward_state), the state
     decode_step continues from."""
     lib = load_library()
-    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
-        _dev(t, nm)
     if q.dim() != 4 or v.dim() != 4 or q.shape != k.shape:
         raise ValueError("q, k must be [B,H,n,d_qk] and v [B,H,n,d]")
     B, H, n, d = v.shape
@@ -204,15 +243,29 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         raise ValueError("q, k, v disagree on B, H, n")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share one dtype")
+    _dtype_code(v.dtype)
     mapk = _map_code(feature_map)
-    d_feat = omega.shape[1] if mapk == MAP_PERFORMER else q.shape[-1]
     if mapk != MAP_IDENTITY and q.shape[-1] != d:
         raise ValueError("q, k must have width d for elu1 and performer")
-    _f32(omega, "omega")
-    _f32(decay, "decay")
+    d_feat = _check_omega(omega, mapk, d) or q.shape[-1]
+    _check_decay(decay, H)
+    if out is not None:
+        _check_out(out, v.shape, v.dtype)
+    if (mu_out is None) != (nu_out is None):
+        raise ValueError("mu_out and nu_out go together")
+    if mu_out is not None:
+        if mu_out.dtype != torch.float32 or nu_out.dtype != torch.float32:
+            raise TypeError("mu_out and nu_out must be float32")
+        if mu_out.shape != (B, H, d_feat, d) or nu_out.shape != (B, H, d_feat):
+            raise ValueError("mu_out must be [B,H,d_feat,d] and nu_out "
+                             "[B,H,d_feat]")
+    if workspace is not None and workspace.dtype != torch.uint8:
+        raise TypeError("workspace must be a uint8 tensor")
+    _on_gpu(v, (q, "q"), (k, "k"), (v, "v"), (out, "out"), (omega, "omega"),
+            (decay, "decay"), (workspace, "workspace"), (mu_out, "mu_out"),
+            (nu_out, "nu_out"))
     if out is None:
         out = torch.empty_like(v)
-    _dev(out, "out")
     dt = _dtype_code(v.dtype)
     need = lib.la_forward_workspace_bytes(B, H, n, d, d_feat, mapk, dt,
                                           int(bool(causal)))
@@ -221,8 +274,6 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if need and workspace.numel() < need:
         raise ValueError(f"workspace of {workspace.numel()} bytes is smaller "
                          f"than the {need} bytes required")
-    if (mu_out is None) != (nu_out is None):
-        raise ValueError("mu_out and nu_out go together")
     if mu_out is None:
         st = lib.la_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, n, d,
                             d_feat, mapk, _ptr(omega), _ptr(decay),
@@ -231,10 +282,6 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                             _stream(v.device))
         _check(st, "la_forward")
         return out
-    _f32(mu_out, "mu_out")
-    _f32(nu_out, "nu_out")
-    if mu_out.shape != (B, H, d_feat, d) or nu_out.shape != (B, H, d_feat):
-        raise ValueError("mu_out must be [B,H,d_feat,d] and nu_out [B,H,d_feat]")
     st = lib.la_forward_state(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, n,
                               d, d_feat, mapk, _ptr(omega), _ptr(decay),
                               int(bool(causal)), dt,
@@ -252,22 +299,63 @@ def decode_step(mu: torch.Tensor, nu: torch.Tensor, q: torch.Tensor,
     """One decode step; mu [S,H,d_feat,d] and nu [S,H,d_feat] are updated in
     place.  Returns out [S,H,d]."""
     lib = load_library()
-    _f32(mu, "mu")
-    _f32(nu, "nu")
-    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
-        _dev(t, nm)
+    if v.dim() != 3 or mu.dim() != 4:
+        raise ValueError("v must be [S,H,d] and mu [S,H,d_feat,d]")
+    if mu.dtype != torch.float32 or nu.dtype != torch.float32:
+        raise TypeError("mu and nu must be float32")
     S, H, d = v.shape
     d_feat = mu.shape[2]
     if mu.shape != (S, H, d_feat, d) or nu.shape != (S, H, d_feat):
         raise ValueError("mu must be [S,H,d_feat,d] and nu [S,H,d_feat]")
-    _f32(omega, "omega")
-    _f32(decay, "decay")
+    mapk = _map_code(feature_map)
+    m = _check_omega(omega, mapk, d)
+    if mapk == MAP_PERFORMER and m != d_feat:
+        raise ValueError(f"omega has {m} features, mu has d_feat={d_feat}")
+    if mapk == MAP_ELU1 and d_feat != d:
+        raise ValueError("elu1 keeps the width: mu must be [S,H,d,d]")
+    dqk = d_feat if mapk == MAP_IDENTITY else d
+    if q.shape != (S, H, dqk) or k.shape != (S, H, dqk):
+        raise ValueError(f"q, k must be [S={S}, H={H}, {dqk}], got "
+                         f"{tuple(q.shape)}, {tuple(k.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    _dtype_code(v.dtype)
+    _check_decay(decay, H)
+    if out is not None:
+        _check_out(out, v.shape, v.dtype)
+    _on_gpu(v, (mu, "mu"), (nu, "nu"), (q, "q"), (k, "k"), (v, "v"),
+            (out, "out"), (omega, "omega"), (decay, "decay"))
     if out is None:
         out = torch.empty_like(v)
-    _dev(out, "out")
     st = lib.la_decode_step(_ptr(mu), _ptr(nu), _ptr(q), _ptr(k), _ptr(v),
-                            _ptr(out), S, H, d, d_feat, _map_code(feature_map),
+                            _ptr(out), S, H, d, d_feat, mapk,
                             _ptr(omega), _ptr(decay), _dtype_code(v.dtype),
                             _stream(v.device))
     _check(st, "la_decode_step")
     return out
+
+
+def workspace_check(workspace: torch.Tensor) -> None:
+    """Raise LinAttnError(LA_ERR_EXCHANGE) if a segment exchange failed in a
+    call that used this workspace since the last check (and clear that
+    status).  Synchronises with the current stream."""
+    lib = load_library()
+    _on_gpu(workspace, (workspace, "workspace"))
+    _check(lib.la_workspace_check(_ptr(workspace), _stream(workspace.device)),
+           "la_workspace_check")
+
+
+def cached_workspace(device="cuda") -> Optional[torch.Tensor]:
+    """The workspace forward() uses on the current stream of `device` when no
+    workspace is passed (None until a call needed one)."""
+    device = torch.device(device)
+    if device.index is None:
+        device = torch.device(device.type, torch.cuda.current_device())
+    return _workspaces.get((device.index,
+                            torch.cuda.current_stream(device).cuda_stream))
+
+
+def set_exchange_spin_limit(spins: int) -> None:
+    """Diagnostics: polls an exchange wait makes before giving up (0 restores
+    the default)."""
+    load_library().la_set_exchange_spin_limit(int(spins))

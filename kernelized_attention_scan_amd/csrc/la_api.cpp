@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -16,6 +17,9 @@
 namespace {
 
 thread_local std::string g_last_error;
+
+// Polls of an exchange wait before it gives up (la_set_exchange_spin_limit).
+std::atomic<unsigned> g_spin_limit{la::kDefaultSpinLimit};
 
 la_status fail(la_status st, const char *fmt, ...)
     __attribute__((format(printf, 2, 3)));
@@ -49,9 +53,9 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Sequence split of the fused forward: about la::kCUs workgroups in total,
 // at most la::kMaxSegments segments of whole chunks per (batch, head) unit.  A unit
-// gets several segments only when there are fewer units than that.  Causal
-// splits may exceed what is resident at once; the non-causal launcher
-// shrinks its split to what fits.
+// gets several segments only when there are fewer units than that.  No
+// split needs its workgroups to be resident at once: causal segments are
+// numbered in start order, non-causal ones run as two launches.
 constexpr int64_t kMaxSegments = la::kMaxSegments;
 
 struct FwdPlan {
@@ -208,6 +212,7 @@ static la_status forward_impl(const void *q, const void *k, const void *v, void 
     a.omega = p.fused_performer ? omega : nullptr;
     a.mu_out = mu_out;
     a.nu_out = nu_out;
+    a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
     const hipError_t e = p.ops->run(a, units, causal, s);
     if (e != hipSuccess) return hip_fail(e, "la_forward launch");
     return ok();
@@ -225,6 +230,7 @@ const char *la_status_str(la_status s) {
     case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED";
     case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE";
     case LA_ERR_HIP: return "LA_ERR_HIP";
+    case LA_ERR_EXCHANGE: return "LA_ERR_EXCHANGE";
   }
   return "LA_ERR_UNKNOWN";
 }
@@ -298,6 +304,39 @@ la_status la_forward_state(const void *q, const void *k, const void *v,
     return fail(LA_ERR_INVALID_ARG, "la_forward_state needs mu_out and nu_out");
   return forward_impl(q, k, v, out, B, H, n, d, d_feat, map, omega, decay,
                       causal, dtype, workspace, mu_out, nu_out, stream);
+}
+
+la_status la_workspace_check(void *workspace, void *stream) {
+  try {
+    if (!workspace) return fail(LA_ERR_INVALID_ARG, "null workspace");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    unsigned *word = static_cast<unsigned *>(workspace) + la::kSyncStatusWord;
+    unsigned status = 0;
+    hipError_t e = hipMemcpyAsync(&status, word, sizeof(status),
+                                  hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "la_workspace_check read");
+    if (status == 0) return ok();
+    const unsigned zero = 0;
+    e = hipMemcpyAsync(word, &zero, sizeof(zero), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "la_workspace_check clear");
+    return fail(LA_ERR_EXCHANGE, "segment exchange failed since the last "
+                "check:%s%s",
+                (status & la::kSyncStatusTimeout)
+                    ? " a wait for another segment's aggregate gave up "
+                      "(those outputs are NaN);" : "",
+                (status & la::kSyncStatusCorrupt)
+                    ? " the synchronisation area was not zero at the start "
+                      "of a call (outputs of that call are unreliable);" : "");
+  } catch (...) {
+    return fail(LA_ERR_HIP, "unexpected exception in la_workspace_check");
+  }
+}
+
+void la_set_exchange_spin_limit(unsigned spins) {
+  g_spin_limit.store(spins ? spins : la::kDefaultSpinLimit,
+                     std::memory_order_relaxed);
 }
 
 la_status la_decode_step(float *mu, float *nu, const void *q, const void *k,

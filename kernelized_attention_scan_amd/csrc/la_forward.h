@@ -29,10 +29,11 @@
 //     line of the workspace, waits for the flags of the segments it needs
 //     (those before it; all of them when non-causal) and sums their
 //     aggregates, weighted by the decay over the gap, into the state entering
-//     it (non-causal: the total).  Only workgroups of one unit wait on each
-//     other.  Causal segments are numbered in the order their workgroups
-//     start, so every wait is on a running workgroup; the non-causal launch
-//     is cooperative, so all of its workgroups are resident;
+//     it.  Only workgroups of one unit wait on each other.  Causal segments
+//     are numbered in the order their workgroups start, so every wait is on
+//     a running workgroup.  Non-causal segments need every aggregate: they
+//     run as two launches instead (aggregates, then readout), so nothing
+//     waits inside a kernel;
 //   phase 2: the chunk loop from that state.
 // Both loops keep several chunks of loads in flight in a register ring.  All
 // global loads are unconditional (tail rows clamp to a valid row; the loop
@@ -117,7 +118,7 @@ constexpr size_t fwd_lds_bytes(int c, int d, int df, bool decay, bool pf,
   const size_t sx = pf ? static_cast<size_t>(c) * lds_stride<T>(d) : 0;
   return sizeof(T) * (nbuf * (sq + (decay ? sq : 0) + sv + sst) +
                       kslots * sq + 2 * sx) +
-         sizeof(float) * (c + 4 + (pf ? 2 * c : 0));
+         sizeof(float) * (c + 8 + (pf ? 2 * c : 0));
 }
 
 // Largest power of two <= x, at most 8 (1 for x < 2).
@@ -529,8 +530,9 @@ __device__ __forceinline__ void publish_state(const f32x4 *S, T *sST, int w,
 
 // Exchange of segment aggregates between the workgroups of one (batch, head)
 // unit, through that unit's line of the synchronisation area (see
-// la_internal.h).  Every workgroup a wait depends on is running (causal:
-// segment indices follow start order; non-causal: cooperative launch).
+// la_internal.h).  Only causal launches exchange inside the kernel, and
+// every workgroup a wait depends on is running: segment indices follow
+// start order.
 //
 // The XCDs of an MI355X do not share their L2 caches.  Each segment records
 // the XCD it runs on in its unit's line when it starts.  A writer that finds
@@ -546,8 +548,9 @@ __device__ __forceinline__ void publish_state(const f32x4 *S, T *sST, int w,
 // segment of its unit, so every reader of it, runs on its XCD.
 //
 // Publishing: every wave waits until its aggregate stores have completed,
-// then flag s is set.  The waits are bounded (a few seconds): if the area
-// were ever corrupt they set the timeout word and let the kernel finish
+// then flag s is set.  The waits are bounded (a few seconds by default): if
+// the area were ever corrupt they set the status word, poison the outputs
+// that depend on the missing aggregates with NaN, and let the kernel finish
 // instead of hanging.  At its very end every workgroup counts itself done;
 // the last one clears the unit's line (flags, ticket, count, XCD records),
 // so the area is zero again for the next launch.
@@ -590,31 +593,39 @@ __device__ __forceinline__ void publish_flag(unsigned *line, int seg,
                        __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Flags [0, need) of the line all set; call from every thread.
-__device__ __forceinline__ void wait_flags(unsigned *line, int need,
-                                           unsigned *timeout_word) {
+// Flags [0, need) of the line all set; call from every thread.  The wait
+// polls at most spin_limit times; if it gives up, the status word gets
+// kSyncStatusTimeout and the function returns true in every thread (the
+// caller then poisons the outputs that depend on the missing aggregates).
+__device__ __forceinline__ bool wait_flags(unsigned *line, int need,
+                                           unsigned *status_word,
+                                           unsigned spin_limit, int *sflag) {
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
     unsigned spins = 0, f = 1u;
+    bool gave_up = false;
     for (;;) {
       f = lane < need ? __hip_atomic_load(line + lane, __ATOMIC_RELAXED,
                                           __HIP_MEMORY_SCOPE_AGENT)
                       : 2u;
       if (__all(f != 0u)) break;
-      __builtin_amdgcn_s_sleep(2);
-      if (++spins > (1u << 22)) {
+      if (++spins > spin_limit) {
+        gave_up = true;
         if (lane == 0)
-          __hip_atomic_store(timeout_word, 1u, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_fetch_or(status_word, kSyncStatusTimeout,
+                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
+      __builtin_amdgcn_s_sleep(2);
     }
     if (__any(f != 2u))
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     else
       asm volatile("buffer_inv sc0" ::: "memory");  // this CU's L1
+    if (lane == 0) *sflag = gave_up ? 1 : 0;
   }
   __syncthreads();
+  return __builtin_amdgcn_readfirstlane(*sflag) != 0;
 }
 
 __device__ __forceinline__ void count_done(unsigned *line, int nseg) {
@@ -638,13 +649,21 @@ __device__ __forceinline__ void count_done(unsigned *line, int nseg) {
 // RES: resident keys (causal, several segments, each at most KRES chunks):
 // every segment, the last one included, runs phase 1 and keeps phi(K) of
 // chunk c in slot c of sK for phase 2.
+// SPLIT (non-causal, several segments): 0 = one launch with the exchange
+// above; 1 = phase 1 only, the aggregate stored to its slot; 2 = phase 2
+// only, reading every aggregate a launch with SPLIT = 1 stored before it on
+// the same stream (the launch boundary orders them: no flags, no waits, no
+// co-residency).
 template <typename T, int D, int DF, bool CAUSAL, bool MULTI, bool DECAY,
-          int MAP, bool RES = false>
+          int MAP, bool RES = false, int SPLIT = 0>
 __global__ __launch_bounds__(kThreads,
                              (FwdShape<T, D, DF, DECAY, MAP>::WAVES_PER_SIMD))
 void la_fwd_kernel(FwdArgs a) {
   using F = FwdShape<T, D, DF, DECAY, MAP>;
   static_assert(!RES || (F::KRES > 0 && CAUSAL && MULTI), "resident keys");
+  static_assert(SPLIT == 0 || (MULTI && !CAUSAL && !RES), "split launches");
+  // the in-kernel exchange through the synchronisation area
+  constexpr bool EXCH = MULTI && SPLIT == 0;
   constexpr bool ELU = MAP == kMapElu, PF = F::PF;
   constexpr int QW = F::QW, LX = F::LX;
   constexpr int C = F::C, LQ = F::LQ, LV = F::LV, DFP = F::DFP;
@@ -662,8 +681,10 @@ void la_fwd_kernel(FwdArgs a) {
   T *sXk = sXq + F::SX;
   float *gp = reinterpret_cast<float *>(sXk + F::SX);
   // fused Performer: the exponent offsets of the chunk's q rows, then of its
-  // k rows (see stage_rows_pf), after the C + 4 words of gp
-  float *pc0 = gp + C + 4;
+  // k rows (see stage_rows_pf), after the C + 8 words of gp: the powers
+  // g^0 .. g^C, then the segment ticket, the two XCD record words and the
+  // exchange's give-up flag
+  float *pc0 = gp + C + 8;
   const float lsm = 0.5f * __builtin_log2f(static_cast<float>(DF));
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -676,7 +697,7 @@ void la_fwd_kernel(FwdArgs a) {
   if (MULTI && a.nseg > 1 && gridDim.x % 8 == 0)
     blk = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
   const int64_t unit = blk / a.nseg;
-  unsigned *line = MULTI && a.nseg > 1
+  unsigned *line = EXCH && a.nseg > 1
                        ? a.sync + kSyncHeaderWords + unit * kSyncLineWords
                        : nullptr;
   int seg = static_cast<int>(blk % a.nseg);
@@ -694,7 +715,7 @@ void la_fwd_kernel(FwdArgs a) {
   // segments of a unit share an XCD, so together they bring every
   // segment's first chunk into that L2: a workgroup whose ticket differs
   // reloads from there.
-  constexpr bool GUESS = MULTI && CAUSAL && F::NB1 == 1;
+  constexpr bool GUESS = EXCH && CAUSAL && F::NB1 == 1;
   const int guess = static_cast<int>(blk % a.nseg);
   Slab<T, QW, C> gk;
   Slab<T, D, C> gv;
@@ -706,7 +727,7 @@ void la_fwd_kernel(FwdArgs a) {
     gv.load(vb, g0 < a.n ? g0 : 0, grows, tid);
   }
   unsigned tk = 0u;
-  if (MULTI && CAUSAL && a.nseg > 1 && tid == 0)
+  if (EXCH && CAUSAL && a.nseg > 1 && tid == 0)
     tk = __hip_atomic_fetch_add(line + kSyncTicketWord, 1u, __ATOMIC_RELAXED,
                                 __HIP_MEMORY_SCOPE_AGENT);
   const Decay dk(a.decay, static_cast<int>(unit % a.H));
@@ -752,12 +773,12 @@ void la_fwd_kernel(FwdArgs a) {
     }
   }
 
-  if (MULTI && CAUSAL && a.nseg > 1) {
+  if (EXCH && CAUSAL && a.nseg > 1) {
     int *ticket = reinterpret_cast<int *>(gp + C + 1);
     if (tid == 0) {
       if (tk >= static_cast<unsigned>(a.nseg)) {  // corrupt area: in bounds
-        __hip_atomic_store(a.sync + kSyncTimeoutWord, 1u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_or(a.sync + kSyncStatusWord, kSyncStatusCorrupt,
+                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         tk %= static_cast<unsigned>(a.nseg);
       }
       *ticket = static_cast<int>(tk);
@@ -767,7 +788,7 @@ void la_fwd_kernel(FwdArgs a) {
   }
   // this segment's XCD record (see the exchange above)
   const unsigned me = xcc_record();
-  if (MULTI && a.nseg > 1 && tid == 0)
+  if (EXCH && a.nseg > 1 && tid == 0)
     __hip_atomic_fetch_or(line + kSyncXccWord + seg / 8, me << (4 * (seg % 8)),
                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // wave 0, lanes 0 and 1: the unit's XCD records, read once every segment
@@ -846,7 +867,7 @@ void la_fwd_kernel(FwdArgs a) {
     // ---------------- phase 1: segment aggregate from K, V ----------------
     // (not for the last causal segment, whose aggregate no other segment
     // needs, unless it keeps its keys resident)
-    if (!CAUSAL || seg + 1 < a.nseg || RES) {
+    if (SPLIT != 2 && (!CAUSAL || seg + 1 < a.nseg || RES)) {
       Slab<T, QW, C> rk[NB1];
       Slab<T, D, C> rv[NB1];
       auto load1 = [&](int c, Slab<T, QW, C> &sk, Slab<T, D, C> &sv) {
@@ -891,7 +912,7 @@ void la_fwd_kernel(FwdArgs a) {
       __syncthreads();  // gp and the constant tile parts ready
       stage1(0, rk[0], rv[0]);
       load1(NB1, rk[0], rv[0]);
-      if (w == 0 && a.nseg > 1)
+      if (EXCH && w == 0 && a.nseg > 1)
         recs = __hip_atomic_load(line + kSyncXccWord + (lane & 1),
                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __syncthreads();
@@ -926,7 +947,21 @@ void la_fwd_kernel(FwdArgs a) {
       if (tid < 2) srec[tid] = recs;
       __syncthreads();
       const unsigned r0 = srec[0], r1 = srec[1];
-      if (!CAUSAL || seg + 1 < a.nseg) {
+      if (SPLIT == 1) {
+        // aggregate-only launch: plain stores; the launch boundary makes
+        // them visible to the readout launch that follows
+        float *mine = ub + static_cast<int64_t>(seg) * F::SLOT;
+#pragma unroll
+        for (int m = 0; m < F::FPW; ++m)
+#pragma unroll
+          for (int mj = 0; mj < F::JPW; ++mj) {
+            const int idx = tile_fb<F>(w, m) * F::NJA + tile_jb<F>(w, mj);
+            *reinterpret_cast<f32x4 *>(mine + (idx * 64 + lane) * 4) =
+                S[m * F::JPW + mj];
+          }
+        return;
+      }
+      if (EXCH && (!CAUSAL || seg + 1 < a.nseg)) {
         // through this XCD's L2 when every segment of the unit runs on it
         const bool local = me < 15 && records_match(r0, r1, a.nseg, me);
         float *mine = ub + static_cast<int64_t>(seg) * F::SLOT;
@@ -951,7 +986,10 @@ void la_fwd_kernel(FwdArgs a) {
       // chunk 0 is staged while the predecessors finish (its tiles are free:
       // phase 1 ended with a workgroup barrier after its last use of them)
       stage2(0, rq[0], rk2[0], rv2[0]);
-      if (need > 0) wait_flags(line, need, a.sync + kSyncTimeoutWord);
+      bool gave_up = false;
+      if (EXCH && need > 0)
+        gave_up = wait_flags(line, need, a.sync + kSyncStatusWord,
+                             a.spin_limit, reinterpret_cast<int *>(gp + C + 4));
 #pragma unroll
       for (int i = 0; i < TW; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int64_t epos = CAUSAL ? start : a.n;
@@ -995,6 +1033,15 @@ void la_fwd_kernel(FwdArgs a) {
                                     : 1.f;
 #pragma unroll
           for (int i = 0; i < TW; ++i) S[i] += wj * buf[u][i];
+        }
+      }
+      if (gave_up) {
+        // a predecessor's aggregate never arrived: every output that
+        // depends on it becomes NaN rather than silently wrong
+#pragma unroll
+        for (int i = 0; i < TW; ++i) {
+          const float nan = __builtin_nanf("");
+          S[i] = f32x4{nan, nan, nan, nan};
         }
       }
       if constexpr (DEDUP) {
@@ -1282,7 +1329,7 @@ void la_fwd_kernel(FwdArgs a) {
         }
       }
   }
-  if (MULTI && a.nseg > 1) count_done(line, a.nseg);
+  if (EXCH && a.nseg > 1) count_done(line, a.nseg);
 }
 
 }  // namespace la

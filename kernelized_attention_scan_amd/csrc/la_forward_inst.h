@@ -21,6 +21,16 @@ struct FwdVariant {
     return reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, false, true, DECAY, MAP>);
   }
 
+  // Non-causal segmented forward as two launches: the aggregates, then the
+  // readout against their total.
+  static const void *kernel_split(int split) {
+    return split == 1
+        ? reinterpret_cast<const void *>(
+              &la_fwd_kernel<T, D, DF, false, true, DECAY, MAP, false, 1>)
+        : reinterpret_cast<const void *>(
+              &la_fwd_kernel<T, D, DF, false, true, DECAY, MAP, false, 2>);
+  }
+
   // Resident-key instance (causal, several segments of at most KRES chunks).
   static const void *kernel_res() {
     if constexpr (F::KRES > 0)
@@ -29,11 +39,14 @@ struct FwdVariant {
     return kernel(true, true);
   }
 
-  // Raise the dynamic-LDS limit of every instance once (above 64 KiB).
+  // Raise the dynamic-LDS limit of every instance once (above 64 KiB); a
+  // function-local static, so the first call does it under C++'s
+  // thread-safe initialisation.
   static hipError_t set_lds() {
     static const hipError_t once = [] {
       for (const void *k : {kernel(true, true), kernel(true, false),
-                            kernel(false, true), kernel_res()}) {
+                            kernel(false, true), kernel_res(),
+                            kernel_split(1), kernel_split(2)}) {
         const hipError_t e = hipFuncSetAttribute(
             k, hipFuncAttributeMaxDynamicSharedMemorySize,
             static_cast<int>(F::lds_bytes));
@@ -44,46 +57,10 @@ struct FwdVariant {
     return once;
   }
 
-  // Workgroups of the non-causal multi-segment kernel resident at once.
-  static hipError_t capacity(int64_t *cap) {
-    static int per_cu = -1;
-    static int cus = 0;
-    if (per_cu < 0) {
-      int dev = 0, n = 0;
-      hipError_t e = hipGetDevice(&dev);
-      if (e == hipSuccess)
-        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-      if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, kernel(false, true), kThreads, F::lds_bytes);
-      if (e != hipSuccess) return e;
-      per_cu = n;
-    }
-    *cap = static_cast<int64_t>(per_cu) * cus;
-    return hipSuccess;
-  }
-
-  static hipError_t run(const FwdArgs &args, int64_t units, int causal,
+  static hipError_t run(const FwdArgs &a, int64_t units, int causal,
                         hipStream_t s) {
     hipError_t e = set_lds();
     if (e != hipSuccess) return e;
-    FwdArgs a = args;
-    if (a.nseg > 1 && !causal) {
-      // The non-causal exchange waits on every segment, so every workgroup
-      // must be resident: shrink the split to what fits (the workspace was
-      // sized for the largest split) and launch cooperatively.
-      int64_t cap = 0;
-      e = capacity(&cap);
-      if (e != hipSuccess) return e;
-      if (units * a.nseg > cap) {
-        int64_t nseg = cap / units;
-        if (nseg < 1) nseg = 1;
-        const int64_t nch = (a.n + F::C - 1) / F::C;
-        const int64_t cps = (nch + nseg - 1) / nseg;
-        a.seg_len = cps * F::C;
-        a.nseg = static_cast<int>((a.n + a.seg_len - 1) / a.seg_len);
-      }
-    }
     const dim3 grid(static_cast<unsigned>(units * a.nseg)), block(kThreads);
     if (causal) {
       // One segment: no exchange.  Several: segments are numbered in start
@@ -110,9 +87,19 @@ struct FwdVariant {
                          grid, block, F::lds_bytes, s, a);
       return hipGetLastError();
     }
-    void *params[] = {&a};
-    return hipLaunchCooperativeKernel(kernel(false, true), grid, block, params,
-                                      F::lds_bytes, s);
+    // Non-causal, several segments: every readout needs every segment's
+    // aggregate, so the aggregates come from a launch of their own and the
+    // readout launch after it on the same stream reads them; no workgroup
+    // ever waits for another.
+    hipLaunchKernelGGL(
+        (la_fwd_kernel<T, D, DF, false, true, DECAY, MAP, false, 1>), grid,
+        block, F::lds_bytes, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(
+        (la_fwd_kernel<T, D, DF, false, true, DECAY, MAP, false, 2>), grid,
+        block, F::lds_bytes, s, a);
+    return hipGetLastError();
   }
 };
 

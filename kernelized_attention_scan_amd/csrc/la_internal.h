@@ -21,8 +21,12 @@ constexpr int kMaxTargetGroups = 512;
 // forward (32-bit words, zero between calls).  Its size is fixed, so that
 // whatever sizes the calls sharing a workspace have, no call's scratch ever
 // lands on another call's flags:
-//   words [0, kSyncHeaderWords): status; word kSyncTimeoutWord is set to 1 if
-//     a wait ever gave up (corrupt area), else never written;
+//   words [0, kSyncHeaderWords): header; word kSyncStatusWord collects
+//     kSyncStatusTimeout (a wait for another segment's aggregate gave up;
+//     the outputs of that segment are NaN) and kSyncStatusCorrupt (a
+//     segment ticket was out of range: the area was not zero at the start);
+//     kernels only ever set bits there, la_workspace_check reads and clears
+//     it;
 //   then one line of kSyncLineWords per (batch, head) unit, for up to
 //     kMaxTargetGroups units: word s is the "aggregate of segment s published"
 //     flag, word kSyncTicketWord hands out causal segment indices in start
@@ -30,7 +34,12 @@ constexpr int kMaxTargetGroups = 512;
 //     one clears the line), and the two words from kSyncXccWord record, 4
 //     bits per segment, the XCD (1 + its id) each segment runs on.
 constexpr int kSyncHeaderWords = 64;
-constexpr int kSyncTimeoutWord = 8;
+constexpr int kSyncStatusWord = 8;
+constexpr unsigned kSyncStatusTimeout = 1u;
+constexpr unsigned kSyncStatusCorrupt = 2u;
+// Polls of an exchange wait before it gives up, by default (about a second
+// or more; la_set_exchange_spin_limit changes it for diagnostics).
+constexpr unsigned kDefaultSpinLimit = 1u << 22;
 constexpr int kSyncLineWords = 32;
 constexpr int kSyncDoneWord = kMaxSegments;
 constexpr int kSyncTicketWord = kMaxSegments + 1;
@@ -56,6 +65,7 @@ struct FwdArgs {
   const float *omega;   // [d][d_feat] for the fused Performer map, else null
   float *mu_out;        // [units][d_feat][d] final state, or null
   float *nu_out;        // [units][d_feat] final normaliser (with mu_out)
+  unsigned spin_limit;  // polls of an exchange wait before it gives up
 };
 
 // Launch set of one (storage type, d, d_feat) instance of the chunked forward.

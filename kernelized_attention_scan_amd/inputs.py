@@ -80,14 +80,16 @@ class DecodeConfig:
 TINY_FP32 = PrefillConfig("tiny_fp32_elu1_B1H1n256d16", B=1, H=1, n=256, d=16,
                           dtype=torch.float32)
 ELU1_CAUSAL = PrefillConfig("elu1_causal_B4H8n4096d64", B=4, H=8, n=4096, d=64)
+ELU1_NONCAUSAL = PrefillConfig("elu1_noncausal_B4H8n4096d64", B=4, H=8,
+                               n=4096, d=64, causal=False)
 DECAYED = PrefillConfig("decayed_elu1_B2H16n65536d128", B=2, H=16, n=65536,
                         d=128, decay=(-3.0, -1.0))
 PERFORMER = PrefillConfig("performer_B4H8n8192d64m256", B=4, H=8, n=8192, d=64,
                           mapk=MAP_PERFORMER, m=256, qk_std=0.5)
 DECODE = DecodeConfig("decode_S256H32d128_a0.99", S=256, H=32, d=128)
 
-PREFILL_CONFIGS = {c.name: c for c in (TINY_FP32, ELU1_CAUSAL, DECAYED,
-                                       PERFORMER)}
+PREFILL_CONFIGS = {c.name: c for c in (TINY_FP32, ELU1_CAUSAL, ELU1_NONCAUSAL,
+                                       DECAYED, PERFORMER)}
 
 
 def _round(x: torch.Tensor, dtype: torch.dtype) -> torch.Tensor:

@@ -186,14 +186,46 @@ def test_forward_empty_inputs_are_noops():
 
 # --------------------------------------------------------------------------
 # Forward at the full workload sizes, in the benchmark's launch configuration,
-# against the oracle on sampled (batch, head) units.
+# against the oracle on every (batch, head) unit.
 # --------------------------------------------------------------------------
+
+def full_size_errors(cfg, seed=0):
+    """GPU forward on the whole config; the oracle on every unit, one batch
+    index at a time (its OpenMP loop runs over that batch's heads).  Returns
+    the per-unit relative errors, [B][H]."""
+    x = I.make_prefill(cfg, seed)
+    name = I.MAP_NAMES[cfg.mapk]
+    out = K.forward(dev(x["q"]), dev(x["k"]), dev(x["v"]), feature_map=name,
+                    omega=dev(x["omega"]), decay=dev(x["decay"]),
+                    causal=cfg.causal)
+    torch.cuda.synchronize()
+    out = out.cpu()
+    errs = np.zeros((cfg.B, cfg.H))
+    for b in range(cfg.B):
+        sl = slice(b, b + 1)
+        ref = oracle.forward(f64(x["q"][sl]), f64(x["k"][sl]),
+                             f64(x["v"][sl]), cfg.mapk, f64(x["omega"]),
+                             f64(x["decay"]), cfg.causal)
+        got = out[sl].double().numpy()
+        assert np.all(np.isfinite(got)), f"non-finite output, batch {b}"
+        for h in range(cfg.H):
+            r = ref[0, h]
+            errs[b, h] = np.max(np.abs(got[0, h] - r)) / np.max(np.abs(r))
+        del ref, got
+    return errs
+
 
 @pytest.mark.parametrize("cfg", [I.ELU1_CAUSAL, I.PERFORMER, I.DECAYED],
                          ids=lambda c: c.name)
-def test_forward_full_size_sampled_units(cfg):
-    units = [(0, 0), (cfg.B - 1, cfg.H - 1)]
-    assert run_forward(cfg, seed=0, units=units) <= 1e-2
+def test_forward_full_size_every_unit(cfg):
+    """Every one of the B*H units at the full workload size, element by
+    element: the block-to-unit mapping, the per-unit synchronisation lines
+    and the per-head decay all depend on the unit."""
+    errs = full_size_errors(cfg, seed=0)
+    worst = np.unravel_index(np.argmax(errs), errs.shape)
+    print(f"{cfg.name}: max per-unit rel err {errs.max():.3e} at "
+          f"(b, h) = {worst}", flush=True)
+    assert errs.max() <= 1e-2
 
 
 # --------------------------------------------------------------------------
@@ -283,6 +315,42 @@ def test_exchange_never_times_out_and_leaves_area_zero(cfg):
     sync = ws[:SYNC_BYTES].view(torch.int32).cpu()
     assert sync[TIMEOUT_WORD].item() == 0, "a wait gave up"
     assert torch.count_nonzero(sync).item() == 0
+    K.workspace_check(ws)             # the library reports no failure either
+
+
+def test_exchange_give_up_is_reported_and_poisons_outputs():
+    """A wait that gives up is reported by la_workspace_check and turns the
+    outputs that depend on the missing partial sums into NaN.  The host
+    forces it with a spin limit of one poll: the last causal segment skips
+    phase 1 and waits at once for fifteen segments that each still have 64
+    chunks of phase 1 to go.  Every kernel still ends normally, the
+    synchronisation area is zero again afterwards, and with the default
+    limit restored the same call matches the oracle."""
+    cfg = I.ELU1_CAUSAL.replace(B=1, H=1, n=65536)
+    need = K.forward_workspace_bytes(cfg.B, cfg.H, cfg.n, cfg.d, cfg.d_feat)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    x = I.make_prefill(cfg, 5)
+    args = [dev(x["q"]), dev(x["k"]), dev(x["v"])]
+    seg_len = 4096                  # 16 segments of 64 chunks
+    try:
+        K.set_exchange_spin_limit(1)
+        out = K.forward(*args, workspace=ws)
+        torch.cuda.synchronize()
+    finally:
+        K.set_exchange_spin_limit(0)
+    with pytest.raises(K.LinAttnError) as err:
+        K.workspace_check(ws)
+    assert err.value.status == K._binding.LA_ERR_EXCHANGE
+    assert "gave up" in str(err.value)
+    assert torch.isnan(out[0, 0, cfg.n - seg_len:].float()).all()
+    assert torch.count_nonzero(ws[:SYNC_BYTES]).item() == 0
+    K.workspace_check(ws)           # the status was cleared by the check
+    out = K.forward(*args, workspace=ws)
+    torch.cuda.synchronize()
+    K.workspace_check(ws)
+    ref = oracle.forward(f64(x["q"]), f64(x["k"]), f64(x["v"]), cfg.mapk,
+                         None, None, True)
+    assert rel(out, ref) <= TOL[torch.bfloat16]
 
 
 def test_shared_workspace_after_unfused_performer():

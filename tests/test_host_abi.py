@@ -42,9 +42,9 @@ def test_library_exports_every_header_symbol(lib):
 
 
 def test_status_strings(lib):
-    names = [lib.la_status_str(i).decode() for i in range(5)]
+    names = [lib.la_status_str(i).decode() for i in range(6)]
     assert names == ["LA_OK", "LA_ERR_INVALID_ARG", "LA_ERR_UNSUPPORTED",
-                     "LA_ERR_WORKSPACE", "LA_ERR_HIP"]
+                     "LA_ERR_WORKSPACE", "LA_ERR_HIP", "LA_ERR_EXCHANGE"]
     assert lib.la_status_str(99).decode() == "LA_ERR_UNKNOWN"
 
 
@@ -196,6 +196,11 @@ def test_forward_state_rejects(lib):
              None, P, P, None) == B.LA_OK
 
 
+def test_workspace_check_rejects_null(lib):
+    assert lib.la_workspace_check(None, None) == B.LA_ERR_INVALID_ARG
+    assert lib.la_last_error().decode() != ""
+
+
 def test_last_error_is_cleared_on_success(lib):
     assert fwd(lib, B=-1) == B.LA_ERR_INVALID_ARG
     assert lib.la_last_error().decode() != ""
@@ -208,3 +213,79 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(1, 1, 4, 16)
     with pytest.raises(ValueError):
         K.forward(x, x, x)
+
+
+# --------------------------------------------------------------------------
+# Binding: shapes and dtypes are checked on the host before any pointer is
+# taken (a mismatch would otherwise become an out-of-bounds device access)
+# --------------------------------------------------------------------------
+
+def _t(*shape, dtype=None):
+    import torch
+    return torch.zeros(*shape, dtype=dtype or torch.bfloat16)
+
+
+@pytest.mark.parametrize("kw,exc", [
+    (dict(out=_t(1, 2, 16, 32)), ValueError),                 # out too small
+    (dict(out=_t(1, 2, 16, 64, dtype=__import__("torch").float32)), TypeError),
+    (dict(decay=_t(3, dtype=__import__("torch").float32)), ValueError),  # != H
+    (dict(decay=_t(2)), TypeError),                           # not fp32
+    (dict(feature_map="performer"), ValueError),              # no omega
+    (dict(feature_map="performer",
+          omega=_t(32, 128, dtype=__import__("torch").float32)), ValueError),
+    (dict(feature_map="performer", omega=_t(64, 128)), TypeError),
+    (dict(mu_out=_t(1, 2, 64, 64, dtype=__import__("torch").float32)),
+     ValueError),                                             # nu_out missing
+    (dict(mu_out=_t(1, 2, 64, 32, dtype=__import__("torch").float32),
+          nu_out=_t(1, 2, 64, dtype=__import__("torch").float32)), ValueError),
+    (dict(workspace=_t(100, dtype=__import__("torch").float32)), TypeError),
+])
+def test_binding_forward_rejects_bad_shapes(kw, exc):
+    q = _t(1, 2, 16, 64)
+    with pytest.raises(exc):
+        K.forward(q, q, q, **kw)
+
+
+def test_binding_forward_rejects_mismatched_qkv():
+    with pytest.raises(ValueError):
+        K.forward(_t(1, 2, 16, 64), _t(1, 2, 16, 32), _t(1, 2, 16, 64))
+    with pytest.raises(ValueError):      # elu1 keeps the width
+        K.forward(_t(1, 2, 16, 32), _t(1, 2, 16, 32), _t(1, 2, 16, 64))
+    with pytest.raises(TypeError):
+        import torch
+        K.forward(_t(1, 2, 16, 64), _t(1, 2, 16, 64),
+                  _t(1, 2, 16, 64, dtype=torch.float32))
+
+
+@pytest.mark.parametrize("kw,exc", [
+    (dict(q=_t(2, 3, 32)), ValueError),                      # q width != d
+    (dict(k=_t(2, 4, 64)), ValueError),                      # k heads
+    (dict(out=_t(2, 3, 16)), ValueError),
+    (dict(decay=_t(4, dtype=__import__("torch").float32)), ValueError),
+    (dict(feature_map="performer",
+          omega=_t(64, 32, dtype=__import__("torch").float32)), ValueError),
+    (dict(feature_map="identity"), ValueError),              # q must be d_feat
+    (dict(nu=_t(2, 3, 32, dtype=__import__("torch").float32)), ValueError),
+])
+def test_binding_decode_rejects_bad_shapes(kw, exc):
+    import torch
+    args = dict(mu=_t(2, 3, 64, 64, dtype=torch.float32),
+                nu=_t(2, 3, 64, dtype=torch.float32), q=_t(2, 3, 64),
+                k=_t(2, 3, 64), v=_t(2, 3, 64))
+    if kw.get("feature_map") == "identity":
+        args["mu"] = _t(2, 3, 16, 64, dtype=torch.float32)
+        args["nu"] = _t(2, 3, 16, dtype=torch.float32)
+    extra = {k: v for k, v in kw.items() if k not in args}
+    args.update({k: v for k, v in kw.items() if k in args})
+    with pytest.raises(exc):
+        K.decode_step(args["mu"], args["nu"], args["q"], args["k"],
+                      args["v"], **extra)
+
+
+def test_binding_featmap_rejects_bad_shapes():
+    import torch
+    x = _t(10, 64)
+    with pytest.raises(ValueError):
+        K.featmap(x, "performer", omega=_t(32, 64, dtype=torch.float32))
+    with pytest.raises(ValueError):
+        K.featmap(x, "elu1", out=_t(10, 32))
