@@ -149,6 +149,31 @@ la_status la_forward_state(const void *q, const void *k, const void *v,
                            void *stream);
 
 /*
+ * la_forward_noalloc -- la_forward that allocates nothing and takes no
+ * workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ * Its scratch is a static device array of the library, 32 MiB, one copy per
+ * GPU, held until the process ends; the first call on a device looks it up
+ * and clears its synchronisation area with a fill kernel on `stream`.
+ *   Arguments, layouts, support and errors as la_forward, without
+ *   `workspace`.  The stream must belong to the current device.  When a
+ *   call's segment partial sums would not fit in the scratch, it splits the
+ *   sequence into fewer segments (results within the same tolerance).  The
+ *   Performer map with fp32 storage (or sizes the fused map is not built
+ *   for), which needs n-sized feature buffers, is rejected with
+ *   LA_ERR_UNSUPPORTED.
+ *   Every call on one GPU shares that GPU's scratch: calls that may overlap
+ *   on one GPU (different streams, or different threads) race and must be
+ *   serialised by the caller.  Exchange failures show as NaN outputs (there
+ *   is no workspace to check).
+ */
+la_status la_forward_noalloc(const void *q, const void *k, const void *v,
+                             void *out, int B, int H, int64_t n, int d,
+                             int d_feat, la_map map, const float *omega,
+                             const float *decay, int causal, la_dtype dtype,
+                             void *stream);
+
+/*
  * la_decode_step -- one autoregressive step per (sequence, head) unit: the
  * running sums are updated in place by the new (k, v) and the new token's
  * output is read out from the UPDATED sums (it attends to itself).

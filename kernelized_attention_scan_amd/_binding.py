@@ -27,7 +27,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
 
 # Exported symbols, in the order include/linattn.h declares them.
 SYMBOLS = ("la_featmap", "la_forward_workspace_bytes", "la_forward",
-           "la_forward_state", "la_decode_step", "la_workspace_check",
+           "la_forward_state", "la_forward_noalloc", "la_decode_step",
+           "la_workspace_check",
            "la_set_exchange_spin_limit", "la_status_str", "la_last_error")
 
 _lock = threading.Lock()
@@ -70,6 +71,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                          i32, i32, vp, vp, i32, i32, vp, vp,
                                          vp, vp]
         lib.la_forward_state.restype = i32
+        lib.la_forward_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32,
+                                           i32, i32, vp, vp, i32, i32, vp]
+        lib.la_forward_noalloc.restype = i32
         lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                        i32, i32, vp, vp, i32, vp]
         lib.la_decode_step.restype = i32
@@ -359,3 +363,37 @@ def set_exchange_spin_limit(spins: int) -> None:
     """Diagnostics: polls an exchange wait makes before giving up (0 restores
     the default)."""
     load_library().la_set_exchange_spin_limit(int(spins))
+
+
+def forward_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    feature_map="elu1", omega: Optional[torch.Tensor] = None,
+                    decay: Optional[torch.Tensor] = None, causal: bool = True,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """forward() through la_forward_noalloc: no workspace, the library's
+    static per-GPU scratch instead (calls overlapping on one GPU race).
+    `out` must be given by a caller that cannot allocate."""
+    lib = load_library()
+    if q.dim() != 4 or v.dim() != 4 or q.shape != k.shape:
+        raise ValueError("q, k must be [B,H,n,d_qk] and v [B,H,n,d]")
+    B, H, n, d = v.shape
+    if q.shape[:3] != v.shape[:3]:
+        raise ValueError("q, k, v disagree on B, H, n")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    dt = _dtype_code(v.dtype)
+    mapk = _map_code(feature_map)
+    if mapk != MAP_IDENTITY and q.shape[-1] != d:
+        raise ValueError("q, k must have width d for elu1 and performer")
+    d_feat = _check_omega(omega, mapk, d) or q.shape[-1]
+    _check_decay(decay, H)
+    if out is not None:
+        _check_out(out, v.shape, v.dtype)
+    _on_gpu(v, (q, "q"), (k, "k"), (v, "v"), (out, "out"), (omega, "omega"),
+            (decay, "decay"))
+    if out is None:
+        out = torch.empty_like(v)
+    st = lib.la_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, n,
+                                d, d_feat, mapk, _ptr(omega), _ptr(decay),
+                                int(bool(causal)), dt, _stream(v.device))
+    _check(st, "la_forward_noalloc")
+    return out

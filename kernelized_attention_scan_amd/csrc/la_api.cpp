@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "la_internal.h"
@@ -80,8 +81,11 @@ struct FwdPlan {
 };
 
 // Validates la_forward's sizes and enums (not pointers) and fills the plan.
+// A non-zero state_cap bounds the synchronisation area plus the segment
+// aggregates: the split then takes fewer segments per unit until they fit.
 la_status plan_forward(int B, int H, int64_t n, int d, int d_feat, int map,
-                       int dtype, int causal, bool decay, FwdPlan *p) {
+                       int dtype, int causal, bool decay, FwdPlan *p,
+                       size_t state_cap = 0) {
   if (B < 0 || H < 0 || n < 0)
     return fail(LA_ERR_INVALID_ARG, "negative size: B=%d H=%d n=%lld", B, H,
                 static_cast<long long>(n));
@@ -126,6 +130,13 @@ la_status plan_forward(int B, int H, int64_t n, int d, int d_feat, int map,
   if (per_unit > kMaxSegments) per_unit = kMaxSegments;
   if (per_unit < 1) per_unit = 1;
   if (per_unit > nchunks) per_unit = nchunks;
+  if (state_cap > 0) {
+    const size_t slot = static_cast<size_t>(p->ops->slot_floats) * sizeof(float);
+    while (per_unit > 1 &&
+           la::kSyncBytes + align256(static_cast<size_t>(units) * per_unit * slot) >
+               state_cap)
+      --per_unit;
+  }
   const int64_t cps = (nchunks + per_unit - 1) / per_unit;
   p->seg_len = cps * C;
   p->nseg = static_cast<int>((n + p->seg_len - 1) / p->seg_len);
@@ -152,16 +163,22 @@ la_status plan_forward(int B, int H, int64_t n, int d, int d_feat, int map,
 
 // la_forward and la_forward_state; mu_out / nu_out (both or neither) receive
 // the state after the last position.
+// workspace_cap != 0: the workspace holds only that many bytes (the
+// allocation-free entry point), so the plan fits its split into it and
+// rejects the unfused Performer map, whose features need n-sized buffers.
 static la_status forward_impl(const void *q, const void *k, const void *v, void *out,
                        int B, int H, int64_t n, int d, int d_feat, int map,
                        const float *omega, const float *decay, int causal,
                        int dtype, void *workspace, float *mu_out, float *nu_out,
-                       void *stream) {
+                       void *stream, size_t workspace_cap = 0) {
   try {
     FwdPlan p;
     const la_status st = plan_forward(B, H, n, d, d_feat, map, dtype, causal,
-                                      decay != nullptr, &p);
+                                      decay != nullptr, &p, workspace_cap);
     if (st != LA_OK) return st;
+    if (workspace_cap > 0 && p.total() > workspace_cap)
+      return fail(LA_ERR_UNSUPPORTED, "workspace of %zu bytes needed, %zu held",
+                  p.total(), workspace_cap);
     const int64_t units = static_cast<int64_t>(B) * H;
     if (units == 0) return ok();
     if (n == 0) {  // no positions: the handed-out state is zero
@@ -220,6 +237,49 @@ static la_status forward_impl(const void *q, const void *k, const void *v, void 
     return fail(LA_ERR_HIP, "unexpected exception in la_forward");
   }
 }
+
+// ---------------------------------------------------------------------------
+// Allocation-free forward: its workspace is this file-scope device array,
+// one copy per GPU, held until the process ends.  In host code `scratch` is
+// only a stand-in for the symbol; its device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t{32} << 20;
+static_assert(kScratchBytes > la::kSyncBytes, "scratch holds the sync area");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxScratchDevices] = {};
+
+// This device's copy of `scratch`.  The first call on a device looks the
+// address up and zeroes the synchronisation area at its start with a fill
+// kernel on the caller's stream (every forward leaves that area zero
+// again); later calls reuse the address.
+la_status device_scratch(hipStream_t s, void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "la_forward_noalloc device");
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(LA_ERR_UNSUPPORTED, "la_forward_noalloc: device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                      "la_forward_noalloc scratch address");
+    e = la::launch_fill_zero(static_cast<float *>(ptr),
+                             static_cast<int64_t>(la::kSyncBytes / sizeof(float)),
+                             s);
+    if (e != hipSuccess) return hip_fail(e, "la_forward_noalloc scratch clear");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return LA_OK;
+}
+}  // namespace
 
 extern "C" {
 
@@ -304,6 +364,42 @@ la_status la_forward_state(const void *q, const void *k, const void *v,
     return fail(LA_ERR_INVALID_ARG, "la_forward_state needs mu_out and nu_out");
   return forward_impl(q, k, v, out, B, H, n, d, d_feat, map, omega, decay,
                       causal, dtype, workspace, mu_out, nu_out, stream);
+}
+
+la_status la_forward_noalloc(const void *q, const void *k, const void *v,
+                             void *out, int B, int H, int64_t n, int d,
+                             int d_feat, la_map map, const float *omega,
+                             const float *decay, int causal, la_dtype dtype,
+                             void *stream) {
+  try {
+    // validate first, so invalid requests touch no device
+    FwdPlan p;
+    la_status st = plan_forward(B, H, n, d, d_feat, map, dtype, causal,
+                                decay != nullptr, &p, kScratchBytes);
+    if (st != LA_OK) return st;
+    if (static_cast<int64_t>(B) * H == 0 || n == 0) return ok();
+    if (!q || !k || !v || !out)
+      return fail(LA_ERR_INVALID_ARG, "null q, k, v or out");
+    if (map == LA_MAP_PERFORMER && !omega)
+      return fail(LA_ERR_INVALID_ARG, "PERFORMER needs omega");
+    if (p.total() > kScratchBytes)
+      return fail(LA_ERR_UNSUPPORTED,
+                  "la_forward_noalloc: this call needs a %zu-byte workspace "
+                  "(the Performer map with fp32 storage, or sizes the fused "
+                  "map is not built for, keep q', k' in it); the static "
+                  "scratch holds %zu bytes: use la_forward with a workspace",
+                  p.total(), kScratchBytes);
+    void *ws = nullptr;
+    if (p.total() > 0) {
+      st = device_scratch(static_cast<hipStream_t>(stream), &ws);
+      if (st != LA_OK) return st;
+    }
+    return forward_impl(q, k, v, out, B, H, n, d, d_feat, map, omega, decay,
+                        causal, dtype, ws, nullptr, nullptr, stream,
+                        kScratchBytes);
+  } catch (...) {
+    return fail(LA_ERR_HIP, "unexpected exception in la_forward_noalloc");
+  }
 }
 
 la_status la_workspace_check(void *workspace, void *stream) {
