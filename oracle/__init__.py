@@ -59,6 +59,10 @@ def _load():
                                        i32, i32, P, P, i32]
         lib.oracle_decode.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32,
                                       i32, i32, P, P]
+        lib.oracle_forward_gated.argtypes = [P, P, P, P, i32, i32, i64, i32,
+                                             i32, i32, i32, P, P, i32, i32]
+        lib.oracle_decode_gated.argtypes = [P, P, P, P, P, P, i32, i32, i32,
+                                            i32, i32, i32, P, P, i32]
         lib.oracle_num_threads.restype = i32
         _lib = lib
     return _lib
@@ -114,6 +118,55 @@ def forward(q, k, v, mapk: int = MAP_ELU1, omega=None, decay=None,
                            dqk, df, mapk, _ptr(om), _ptr(dec),
                            int(bool(causal)))
     return out
+
+
+# Layouts of the log decay of the gated recurrence (see linattn_oracle.c).
+LD_CHANNEL, LD_POSITION, LD_BOTH = 0, 1, 2
+
+
+def forward_gated(q, k, v, mapk: int, omega, log_decay, mode: int,
+                  causal: bool = True) -> np.ndarray:
+    """The recurrence with decay gamma = exp(log_decay) per state row
+    (LD_CHANNEL: [H, d_feat]), per position (LD_POSITION: [B, H, n]) or per
+    both (LD_BOTH: [B, H, n, d_feat]); input weight 1 - gamma (eqs 10-11
+    per row, "2.3 State-Space Models" eqs 14 and 21-25; Mamba's selective
+    decay)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, n, d = v.shape
+    dqk = q.shape[-1]
+    assert q.shape == k.shape == (B, H, n, dqk)
+    om = _f64(omega) if mapk == MAP_PERFORMER else None
+    df = feat_dim(dqk, mapk, om)
+    lam = _f64(log_decay)
+    want = {LD_CHANNEL: (H, df), LD_POSITION: (B, H, n),
+            LD_BOTH: (B, H, n, df)}[mode]
+    assert lam.shape == want, (lam.shape, want)
+    out = np.empty((B, H, n, d), dtype=np.float64)
+    _load().oracle_forward_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H,
+                                 n, d, dqk, df, mapk, _ptr(om), _ptr(lam),
+                                 mode, int(bool(causal)))
+    return out
+
+
+def decode_gated(mu, nu, q, k, v, mapk: int, omega, log_decay, mode: int):
+    """One decode step of the gated recurrence; log_decay is [H, d_feat]
+    (LD_CHANNEL), [S, H] (LD_POSITION) or [S, H, d_feat] (LD_BOTH).
+    Returns (out, mu_new, nu_new); the inputs are not modified."""
+    mu, nu = _f64(mu).copy(), _f64(nu).copy()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    S, H, d = v.shape
+    dqk = q.shape[-1]
+    om = _f64(omega) if mapk == MAP_PERFORMER else None
+    df = mu.shape[2]
+    assert df == feat_dim(dqk, mapk, om)
+    lam = _f64(log_decay)
+    want = {LD_CHANNEL: (H, df), LD_POSITION: (S, H), LD_BOTH: (S, H, df)}[mode]
+    assert lam.shape == want, (lam.shape, want)
+    out = np.empty((S, H, d), dtype=np.float64)
+    _load().oracle_decode_gated(_ptr(mu), _ptr(nu), _ptr(q), _ptr(k), _ptr(v),
+                                _ptr(out), S, H, d, dqk, df, mapk, _ptr(om),
+                                _ptr(lam), mode)
+    return out, mu, nu
 
 
 def decode(mu, nu, q, k, v, mapk: int = MAP_ELU1, omega=None, decay=None):

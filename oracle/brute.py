@@ -87,3 +87,42 @@ def attention(q, k, v, mapk: int = MAP_ELU1, omega=None, decay=None,
     """Brute-force kernelized attention straight from the raw q, k, v."""
     return masked_quadratic(features(q, mapk, omega), features(k, mapk, omega),
                             v, decay, causal)
+
+
+def gated_weights(lam_full, causal: bool = True) -> np.ndarray:
+    """[n, n, d_feat] weights of the gated recurrence, by explicit products.
+
+    lam_full: [n, d_feat] log decay of every state row at every position.
+    Entry (i, j, f) is the weight of key j in row i on feature f: the input
+    weight 1 - gamma_{j,f} times the product of gamma_{l,f} over the
+    positions l after j up to i (causal), or up to the last position
+    (non-causal: every row reads the final state).  "2.2 Linear Attention"
+    eqs 10-11 per state row, "2.3 State-Space Models" eqs 16-17 (powers of
+    the diagonal A) with the selective, per-position decay."""
+    g = np.exp(np.asarray(lam_full, dtype=np.float64))
+    n, df = g.shape
+    W = np.zeros((n, n, df))
+    for i in range(n):
+        for j in range(n):
+            if causal and j > i:
+                continue
+            last = i if causal else n - 1
+            W[i, j] = (1.0 - g[j]) * np.prod(g[j + 1:last + 1], axis=0)
+    return W
+
+
+def gated_quadratic(qf, kf, v, lam_full, causal: bool = True) -> np.ndarray:
+    """Att_i = sum_j sum_f q'_if k'_jf W_ijf v_j / sum_j sum_f q'_if k'_jf W_ijf
+    per (batch, head); lam_full is [B, H, n, d_feat] (broadcast the per-
+    channel or per-position layouts to it first)."""
+    qf = np.asarray(qf, dtype=np.float64)
+    kf = np.asarray(kf, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, n, d = v.shape
+    out = np.empty((B, H, n, d))
+    for b in range(B):
+        for h in range(H):
+            W = gated_weights(lam_full[b, h], causal)
+            A = np.einsum("if,jf,ijf->ij", qf[b, h], kf[b, h], W)
+            out[b, h] = (A @ v[b, h]) / A.sum(axis=1, keepdims=True)
+    return out

@@ -176,6 +176,109 @@ void oracle_decode(double *mu, double *nu, const double *q, const double *k,
   }
 }
 
+/* ------------------------------------------------------------------------
+ * Diagonal and input-dependent decay.
+ *
+ * [SSM]  "2.3 State-Space Models" (efficient2 page): the discretised state
+ *        update z_t = z_{t-1} A + s_t B (eq 14), unrolled with powers of A
+ *        (eqs 16-17), and A diagonalised to Lambda (eqs 21-25), so every
+ *        state channel decays by its own factor.
+ * [MB]   "Linear attention research 2026" page, Mamba's selective
+ *        mechanism: the decay is input-dependent, dA = exp(A delta_t).
+ *
+ * Reading (listed in the design notes): the log decay lam = log(gamma) is
+ * given per state row f (feature channel) and/or per position j; the
+ * update is eqs 10-11 with a replaced by gamma_{j,f} = exp(lam_{j,f}) on
+ * row f, and the input weight is 1 - gamma_{j,f}, the (1 - a) of eqs
+ * 10-11 (the zero-order-hold input weight of eq 14 up to a constant that
+ * cancels in the ratio):
+ *   mu_j[f][e] = gamma mu_{j-1}[f][e] + (1 - gamma) k'_{j,f} v_{j,e}
+ *   nu_j[f]    = gamma nu_{j-1}[f]    + (1 - gamma) k'_{j,f}
+ * The readout is eq 9 (causal form), unchanged.
+ * Layouts of lam (fp64 here), by mode:
+ *   ORC_LD_CHANNEL  : [H][dfeat], the same at every position (eqs 21-25)
+ *   ORC_LD_POSITION : [B][H][n] (decode: [S][H]), the same for every row
+ *   ORC_LD_BOTH     : [B][H][n][dfeat] (decode: [S][H][dfeat])
+ * ------------------------------------------------------------------------ */
+enum { ORC_LD_CHANNEL = 0, ORC_LD_POSITION = 1, ORC_LD_BOTH = 2 };
+
+/* log decay of row f at position j of unit u (head h) */
+static double lam_at(const double *lam, int mode, int64_t u, int h,
+                     int64_t j, int64_t n, int f, int dfeat) {
+  if (mode == ORC_LD_CHANNEL) return lam[(int64_t)h * dfeat + f];
+  if (mode == ORC_LD_POSITION) return lam[u * n + j];
+  return lam[(u * n + j) * dfeat + f];
+}
+
+/* One gated update of every state row (the recurrence above). */
+static void gated_update(double *mu, double *nu, const double *kf,
+                         const double *v, int d, int dfeat, const double *lam,
+                         int mode, int64_t u, int h, int64_t j, int64_t n) {
+  for (int f = 0; f < dfeat; ++f) {
+    const double g = exp(lam_at(lam, mode, u, h, j, n, f, dfeat));
+    const double b = 1.0 - g;
+    for (int e = 0; e < d; ++e)
+      mu[f * d + e] = g * mu[f * d + e] + b * kf[f] * v[e];
+    nu[f] = g * nu[f] + b * kf[f];
+  }
+}
+
+/* Forward with the gated recurrence, over B*H units from a zero state;
+ * arguments as oracle_forward, with lam and its mode in place of decay. */
+void oracle_forward_gated(const double *q, const double *k, const double *v,
+                          double *out, int B, int H, int64_t n, int d,
+                          int dqk, int dfeat, int map, const double *omega,
+                          const double *lam, int mode, int causal) {
+  const int64_t units = (int64_t)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t u = 0; u < units; ++u) {
+    const int h = (int)(u % H);
+    const double *qu = q + u * n * dqk, *ku = k + u * n * dqk;
+    const double *vu = v + u * n * d;
+    double *ou = out + u * n * d;
+    double *mu = (double *)calloc((size_t)dfeat * d, sizeof(double));
+    double *nu = (double *)calloc((size_t)dfeat, sizeof(double));
+    double *qf = (double *)malloc(sizeof(double) * dfeat);
+    double *kf = (double *)malloc(sizeof(double) * dfeat);
+    for (int64_t j = 0; j < n; ++j) {
+      feature_row(ku + j * dqk, kf, dqk, dfeat, map, omega);
+      gated_update(mu, nu, kf, vu + j * d, d, dfeat, lam, mode, u, h, j, n);
+      if (causal) {
+        feature_row(qu + j * dqk, qf, dqk, dfeat, map, omega);
+        readout(mu, nu, qf, ou + j * d, d, dfeat);
+      }
+    }
+    /* non-causal: every row reads the final sums (eq 9) */
+    for (int64_t j = 0; !causal && j < n; ++j) {
+      feature_row(qu + j * dqk, qf, dqk, dfeat, map, omega);
+      readout(mu, nu, qf, ou + j * d, d, dfeat);
+    }
+    free(mu); free(nu); free(qf); free(kf);
+  }
+}
+
+/* One decode step with the gated update; lam is [H][dfeat] (CHANNEL),
+ * [S][H] (POSITION: one value per unit) or [S][H][dfeat] (BOTH). */
+void oracle_decode_gated(double *mu, double *nu, const double *q,
+                         const double *k, const double *v, double *out, int S,
+                         int H, int d, int dqk, int dfeat, int map,
+                         const double *omega, const double *lam, int mode) {
+  const int64_t units = (int64_t)S * H;
+#pragma omp parallel for schedule(static)
+  for (int64_t u = 0; u < units; ++u) {
+    const int h = (int)(u % H);
+    double *qf = (double *)malloc(sizeof(double) * dfeat);
+    double *kf = (double *)malloc(sizeof(double) * dfeat);
+    double *muu = mu + u * (int64_t)dfeat * d, *nuu = nu + u * (int64_t)dfeat;
+    feature_row(k + u * dqk, kf, dqk, dfeat, map, omega);
+    /* a decode step is position 0 of a one-position sequence */
+    gated_update(muu, nuu, kf, v + u * d, d, dfeat, lam, mode, u, h, 0, 1);
+    feature_row(q + u * dqk, qf, dqk, dfeat, map, omega);
+    readout(muu, nuu, qf, out + u * d, d, dfeat);
+    free(qf); free(kf);
+  }
+}
+
 /* Number of OpenMP threads a parallel region here would use (1 without
  * OpenMP); reported beside the oracle's timing. */
 #ifdef _OPENMP

@@ -60,6 +60,26 @@ MUTANTS = {
         "    if (!causal) {\n      for (int64_t j = 0; j < n; ++j) {",
         "    if (!causal) {\n      memset(mu, 0, sizeof(double) * dfeat * d);\n"
         "      for (int64_t j = 0; j < n; ++j) {"),
+    # planted mistakes in the gated (diagonal / input-dependent) recurrence
+    "gated_factors_swapped": ("g * mu[f * d + e] + b * kf[f] * v[e]",
+                              "b * mu[f * d + e] + g * kf[f] * v[e]"),
+    "gated_nu_no_input_weight": ("nu[f] = g * nu[f] + b * kf[f];",
+                                 "nu[f] = g * nu[f] + kf[f];"),
+    "gated_channel_ignored": (
+        "if (mode == ORC_LD_CHANNEL) return lam[(int64_t)h * dfeat + f];",
+        "if (mode == ORC_LD_CHANNEL) return lam[(int64_t)h * dfeat];"),
+    "gated_previous_position": (
+        "if (mode == ORC_LD_POSITION) return lam[u * n + j];",
+        "if (mode == ORC_LD_POSITION) return lam[u * n + (j > 0 ? j - 1 : 0)];"),
+    "gated_both_transposed": ("return lam[(u * n + j) * dfeat + f];",
+                              "return lam[(u * dfeat + f) * n + j];"),
+    "gated_decode_readout_before_update": (
+        "    gated_update(muu, nuu, kf, v + u * d, d, dfeat, lam, mode, u, h, 0, 1);\n"
+        "    feature_row(q + u * dqk, qf, dqk, dfeat, map, omega);\n"
+        "    readout(muu, nuu, qf, out + u * d, d, dfeat);\n",
+        "    feature_row(q + u * dqk, qf, dqk, dfeat, map, omega);\n"
+        "    readout(muu, nuu, qf, out + u * d, d, dfeat);\n"
+        "    gated_update(muu, nuu, kf, v + u * d, d, dfeat, lam, mode, u, h, 0, 1);\n"),
 }
 
 
@@ -77,6 +97,10 @@ def _compile(src_text, tmp_path, tag):
                                    i32, P, P, i32]
     lib.oracle_decode.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32,
                                   i32, P, P]
+    lib.oracle_forward_gated.argtypes = [P, P, P, P, i32, i32, i64, i32, i32,
+                                         i32, i32, P, P, i32, i32]
+    lib.oracle_decode_gated.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32,
+                                        i32, i32, P, P, i32]
     lib.oracle_num_threads.restype = i32
     return lib
 
@@ -160,8 +184,55 @@ def chk_constant_v():
     return True
 
 
+def chk_gated_bruteforce():
+    rng = np.random.default_rng(7)
+    B, H, n, d = 1, 2, 17, 4
+    for mode in (oracle.LD_CHANNEL, oracle.LD_POSITION, oracle.LD_BOTH):
+        for causal in (True, False):
+            q = rng.standard_normal((B, H, n, d))
+            k = rng.standard_normal((B, H, n, d))
+            v = rng.standard_normal((B, H, n, d))
+            shape = {oracle.LD_CHANNEL: (H, d), oracle.LD_POSITION: (B, H, n),
+                     oracle.LD_BOTH: (B, H, n, d)}[mode]
+            lam = rng.uniform(-2.0, -0.05, size=shape)
+            full = {oracle.LD_CHANNEL: lambda l: np.broadcast_to(
+                        l[None, :, None, :], (B, H, n, d)),
+                    oracle.LD_POSITION: lambda l: np.broadcast_to(
+                        l[..., None], (B, H, n, d)),
+                    oracle.LD_BOTH: lambda l: l}[mode](lam)
+            got = oracle.forward_gated(q, k, v, oracle.MAP_ELU1, None, lam,
+                                       mode, causal)
+            want = brute.gated_quadratic(brute.features(q, oracle.MAP_ELU1),
+                                         brute.features(k, oracle.MAP_ELU1),
+                                         v, full, causal)
+            if not _close(got, want, 1e-12):
+                return False
+    return True
+
+
+def chk_gated_decode():
+    # one step from mu = [2], nu = [1] with gamma = 0.5: mu' = 0.5 * 2 +
+    # 0.5 * 1 * 4 = 3, nu' = 1, out = 3 (every layout)
+    for mode, lam in ((oracle.LD_CHANNEL, np.log([[0.5]])),
+                      (oracle.LD_POSITION, np.log([[0.5]])),
+                      (oracle.LD_BOTH, np.log([[[0.5]]]))):
+        out, mu, nu = oracle.decode_gated(
+            np.full((1, 1, 1, 1), 2.0), np.ones((1, 1, 1)), np.ones((1, 1, 1)),
+            np.ones((1, 1, 1)), np.full((1, 1, 1), 4.0), oracle.MAP_IDENTITY,
+            None, lam, mode)
+        if not (out.item() == 3.0 and mu.item() == 3.0 and nu.item() == 1.0):
+            return False
+    # out is read after the update: a new token with a different value
+    # moves the output (readout-before-update would return mu / nu = 2)
+    out, _, _ = oracle.decode_gated(
+        np.full((1, 1, 1, 1), 2.0), np.ones((1, 1, 1)), np.ones((1, 1, 1)),
+        np.ones((1, 1, 1)), np.full((1, 1, 1), 10.0), oracle.MAP_IDENTITY,
+        None, np.log([[0.5]]), oracle.LD_CHANNEL)
+    return out.item() == 6.0
+
+
 CHECKS = [chk_bruteforce, chk_hand_examples, chk_featmaps, chk_decode,
-          chk_constant_v]
+          chk_constant_v, chk_gated_bruteforce, chk_gated_decode]
 
 
 def _run_checks(lib, monkeypatch):
