@@ -53,7 +53,8 @@ def workloads():
     from kernelized_attention_scan_amd import inputs as I
     return {"elu1": I.ELU1_CAUSAL, "decayed": I.DECAYED,
             "performer": I.PERFORMER, "tiny": I.TINY_FP32,
-            "decode": I.DECODE, "noncausal": I.ELU1_NONCAUSAL}
+            "decode": I.DECODE, "noncausal": I.ELU1_NONCAUSAL,
+            "gated": I.GATED}
 
 
 def esize(dtype) -> int:
@@ -122,23 +123,33 @@ def cpu_baseline_prefill(cfg, seed: int, budget_s: float = 20.0):
     flat = lambda t: t.reshape(1, units, cfg.n, t.shape[-1])
     q, k, v = flat(x["q"]), flat(x["k"]), flat(x["v"])
     dec = None if x["decay"] is None else x["decay"].repeat(cfg.B)
+    lam = (None if x["log_decay"] is None
+           else x["log_decay"].reshape(1, units, cfg.n))
     om = f64(x["omega"])
     threads = oracle.num_threads()
+
+    def run(take):
+        sl = slice(0, take)
+        if lam is not None:    # the gated recurrence, per-position decay
+            return oracle.forward_gated(
+                f64(q[:, sl]), f64(k[:, sl]), f64(v[:, sl]), cfg.mapk, om,
+                f64(lam[:, sl]), oracle.LD_POSITION, cfg.causal)
+        return oracle.forward(f64(q[:, sl]), f64(k[:, sl]), f64(v[:, sl]),
+                              cfg.mapk, om,
+                              None if dec is None else f64(dec[sl]),
+                              cfg.causal)
+
     # calibrate on one unit per thread, then take as many units as fit
     probe = min(units, threads)
     t0 = time.perf_counter()
-    oracle.forward(f64(q[:, :probe]), f64(k[:, :probe]), f64(v[:, :probe]),
-                   cfg.mapk, om, None if dec is None else f64(dec[:probe]),
-                   cfg.causal)
+    run(probe)
     per_round = time.perf_counter() - t0
     take = int(budget_s / max(per_round, 1e-9)) * probe
     take = max(probe, min(units, take))
-    args = (f64(q[:, :take]), f64(k[:, :take]), f64(v[:, :take]), cfg.mapk,
-            om, None if dec is None else f64(dec[:take]), cfg.causal)
     reps, dt = 0, 0.0
     while reps == 0 or dt < 2.0:      # repeat a short sample for a stable time
         t0 = time.perf_counter()
-        oracle.forward(*args)
+        run(take)
         dt += time.perf_counter() - t0
         reps += 1
     return {"value": reps * take * cfg.n / dt, "unit": "tokens/s",
@@ -196,6 +207,12 @@ def prefill_leg(torch, K, I, cfg, args, dev):
 
     def step(i):
         s = sets[i % nsets]
+        if s["log_decay"] is not None:   # per-position decay
+            K.forward_gated(s["q"], s["k"], s["v"], s["log_decay"],
+                            "position", feature_map=mapname, omega=s["omega"],
+                            causal=cfg.causal, out=outs[i % nsets],
+                            workspace=ws)
+            return
         K.forward(s["q"], s["k"], s["v"], feature_map=mapname,
                   omega=s["omega"], decay=s["decay"], causal=cfg.causal,
                   out=outs[i % nsets], workspace=ws)
@@ -263,7 +280,7 @@ def prefill_leg(torch, K, I, cfg, args, dev):
             "kern": kern, "nsets": nsets,
             "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H,
                        "n": cfg.n, "d": cfg.d, "d_feat": cfg.d_feat,
-                       "map": mapname, "decay": cfg.decay,
+                       "map": mapname, "decay": cfg.decay, "gate": cfg.gate,
                        "causal": cfg.causal, "buffer_sets": nsets,
                        "seed": args.seed}}
 

@@ -64,6 +64,14 @@ typedef enum la_map {
 
 typedef enum la_dtype { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
 
+/* Layout of the log decay lam = log(gamma) of the gated recurrence (see
+ * la_forward_gated).  Values are fp32, device memory. */
+typedef enum la_decay_layout {
+  LA_LD_CHANNEL = 0,   /* [H][d_feat]: one decay per state row and head     */
+  LA_LD_POSITION = 1,  /* [B][H][n] (decode: [S][H]): one per position      */
+  LA_LD_BOTH = 2       /* [B][H][n][d_feat] (decode: [S][H][d_feat])        */
+} la_decay_layout;
+
 /*
  * la_featmap -- phi applied row by row: x [rows][d] -> x_feat [rows][d_feat].
  *   "Linear attention research 2026" page, Performer and Linear Transformer
@@ -172,6 +180,52 @@ la_status la_forward_noalloc(const void *q, const void *k, const void *v,
                              int d_feat, la_map map, const float *omega,
                              const float *decay, int causal, la_dtype dtype,
                              void *stream);
+
+/*
+ * la_forward_gated -- la_forward / la_forward_state with a decay that
+ * varies by position: gamma_j = exp(lam_j) replaces a in eqs 10-11 at
+ * position j,
+ *   mu_j = gamma_j mu_{j-1} + (1 - gamma_j) k'_j^T v_j,
+ *   nu_j = gamma_j nu_{j-1} + (1 - gamma_j) k'_j,
+ * read out as in la_forward.  This is the input-dependent decay of Mamba's
+ * selective step, dA = exp(A delta_t) ("Linear attention research 2026"
+ * page), applied to the state of "2.2 Linear Attention" eqs 10-11; 1 -
+ * gamma is the zero-order-hold input weight of the discretised update of
+ * "2.3 State-Space Models" eq 14, up to a constant that cancels in the
+ * ratio.
+ *   All arguments as la_forward, with
+ *   log_decay: device fp32 lam = log(gamma) in `layout`; values <= 0
+ *              (decays in (0, 1]) are expected and not checked; -inf gives
+ *              gamma = 0 (the state restarts at that position).
+ *   layout   : LA_LD_POSITION ([B][H][n]) is built.  LA_LD_CHANNEL and
+ *              LA_LD_BOTH (a decay per state row) return LA_ERR_UNSUPPORTED
+ *              for the chunked forward: la_decode_step_gated takes them.
+ *   mu_out, nu_out: optional (both or neither), as la_forward_state.
+ *   The workspace is la_forward_workspace_bytes(...) of the same sizes.
+ */
+la_status la_forward_gated(const void *q, const void *k, const void *v,
+                           void *out, int B, int H, int64_t n, int d,
+                           int d_feat, la_map map, const float *omega,
+                           const float *log_decay, la_decay_layout layout,
+                           int causal, la_dtype dtype, void *workspace,
+                           float *mu_out, float *nu_out, void *stream);
+
+/*
+ * la_decode_step_gated -- la_decode_step with a decay per state row and/or
+ * per unit: row f of unit u decays by gamma = exp(lam) with input weight
+ * 1 - gamma (the diagonal A of "2.3 State-Space Models" eqs 21-25, and
+ * Mamba's input-dependent decay).
+ *   All arguments as la_decode_step, with
+ *   log_decay: device fp32 lam, [H][d_feat] (LA_LD_CHANNEL), [S][H]
+ *              (LA_LD_POSITION: this step's decay per unit) or
+ *              [S][H][d_feat] (LA_LD_BOTH); LA_ERR_INVALID_ARG if NULL.
+ */
+la_status la_decode_step_gated(float *mu, float *nu, const void *q,
+                               const void *k, const void *v, void *out, int S,
+                               int H, int d, int d_feat, la_map map,
+                               const float *omega, const float *log_decay,
+                               la_decay_layout layout, la_dtype dtype,
+                               void *stream);
 
 /*
  * la_decode_step -- one autoregressive step per (sequence, head) unit: the

@@ -18,6 +18,8 @@ import torch
  LA_ERR_EXCHANGE) = range(6)
 MAP_IDENTITY, MAP_ELU1, MAP_PERFORMER = 0, 1, 2
 LA_F32, LA_BF16 = 0, 1
+LD_CHANNEL, LD_POSITION, LD_BOTH = 0, 1, 2
+_LAYOUTS = {"channel": LD_CHANNEL, "position": LD_POSITION, "both": LD_BOTH}
 
 _MAPS = {"identity": MAP_IDENTITY, "elu1": MAP_ELU1, "performer": MAP_PERFORMER}
 _DTYPES = {torch.float32: LA_F32, torch.bfloat16: LA_BF16}
@@ -27,8 +29,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
 
 # Exported symbols, in the order include/linattn.h declares them.
 SYMBOLS = ("la_featmap", "la_forward_workspace_bytes", "la_forward",
-           "la_forward_state", "la_forward_noalloc", "la_decode_step",
-           "la_workspace_check",
+           "la_forward_state", "la_forward_gated", "la_forward_noalloc",
+           "la_decode_step", "la_decode_step_gated", "la_workspace_check",
            "la_set_exchange_spin_limit", "la_status_str", "la_last_error")
 
 _lock = threading.Lock()
@@ -71,6 +73,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                          i32, i32, vp, vp, i32, i32, vp, vp,
                                          vp, vp]
         lib.la_forward_state.restype = i32
+        lib.la_forward_gated.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32,
+                                         i32, i32, vp, vp, i32, i32, i32, vp,
+                                         vp, vp, vp]
+        lib.la_forward_gated.restype = i32
+        lib.la_decode_step_gated.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32,
+                                             i32, i32, i32, vp, vp, i32, i32,
+                                             vp]
+        lib.la_decode_step_gated.restype = i32
         lib.la_forward_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32,
                                            i32, i32, vp, vp, i32, i32, vp]
         lib.la_forward_noalloc.restype = i32
@@ -396,4 +406,127 @@ def forward_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                 d, d_feat, mapk, _ptr(omega), _ptr(decay),
                                 int(bool(causal)), dt, _stream(v.device))
     _check(st, "la_forward_noalloc")
+    return out
+
+
+def _layout_code(layout) -> int:
+    if isinstance(layout, int):
+        return layout
+    try:
+        return _LAYOUTS[layout]
+    except KeyError:
+        raise ValueError(f"unknown decay layout {layout!r}") from None
+
+
+def forward_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  log_decay: torch.Tensor, layout="position",
+                  feature_map="elu1", omega: Optional[torch.Tensor] = None,
+                  causal: bool = True, out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None,
+                  mu_out: Optional[torch.Tensor] = None,
+                  nu_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """forward() with a decay exp(log_decay) per position (la_forward_gated):
+    log_decay is fp32 [B, H, n] for layout "position"."""
+    lib = load_library()
+    if q.dim() != 4 or v.dim() != 4 or q.shape != k.shape:
+        raise ValueError("q, k must be [B,H,n,d_qk] and v [B,H,n,d]")
+    B, H, n, d = v.shape
+    if q.shape[:3] != v.shape[:3]:
+        raise ValueError("q, k, v disagree on B, H, n")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    dt = _dtype_code(v.dtype)
+    mapk = _map_code(feature_map)
+    if mapk != MAP_IDENTITY and q.shape[-1] != d:
+        raise ValueError("q, k must have width d for elu1 and performer")
+    d_feat = _check_omega(omega, mapk, d) or q.shape[-1]
+    lay = _layout_code(layout)
+    want = {LD_CHANNEL: (H, d_feat), LD_POSITION: (B, H, n),
+            LD_BOTH: (B, H, n, d_feat)}[lay]
+    if log_decay.dtype != torch.float32:
+        raise TypeError("log_decay must be float32")
+    if tuple(log_decay.shape) != want:
+        raise ValueError(f"log_decay must be {want}, got "
+                         f"{tuple(log_decay.shape)}")
+    if out is not None:
+        _check_out(out, v.shape, v.dtype)
+    if (mu_out is None) != (nu_out is None):
+        raise ValueError("mu_out and nu_out go together")
+    if mu_out is not None:
+        if mu_out.dtype != torch.float32 or nu_out.dtype != torch.float32:
+            raise TypeError("mu_out and nu_out must be float32")
+        if mu_out.shape != (B, H, d_feat, d) or nu_out.shape != (B, H, d_feat):
+            raise ValueError("mu_out must be [B,H,d_feat,d] and nu_out "
+                             "[B,H,d_feat]")
+    if workspace is not None and workspace.dtype != torch.uint8:
+        raise TypeError("workspace must be a uint8 tensor")
+    _on_gpu(v, (q, "q"), (k, "k"), (v, "v"), (out, "out"), (omega, "omega"),
+            (log_decay, "log_decay"), (workspace, "workspace"),
+            (mu_out, "mu_out"), (nu_out, "nu_out"))
+    if out is None:
+        out = torch.empty_like(v)
+    need = lib.la_forward_workspace_bytes(B, H, n, d, d_feat, mapk, dt,
+                                          int(bool(causal)))
+    if need and workspace is None:
+        workspace = _workspace(need, v.device)
+    if need and workspace.numel() < need:
+        raise ValueError(f"workspace of {workspace.numel()} bytes is smaller "
+                         f"than the {need} bytes required")
+    st = lib.la_forward_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, n,
+                              d, d_feat, mapk, _ptr(omega), _ptr(log_decay),
+                              lay, int(bool(causal)), dt,
+                              _ptr(workspace) if need else None, _ptr(mu_out),
+                              _ptr(nu_out), _stream(v.device))
+    _check(st, "la_forward_gated")
+    return out
+
+
+def decode_step_gated(mu: torch.Tensor, nu: torch.Tensor, q: torch.Tensor,
+                      k: torch.Tensor, v: torch.Tensor,
+                      log_decay: torch.Tensor, layout="channel",
+                      feature_map="elu1", omega: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """decode_step() with a decay exp(log_decay) per state row and/or per
+    unit: log_decay [H, d_feat] ("channel"), [S, H] ("position") or
+    [S, H, d_feat] ("both")."""
+    lib = load_library()
+    if v.dim() != 3 or mu.dim() != 4:
+        raise ValueError("v must be [S,H,d] and mu [S,H,d_feat,d]")
+    if mu.dtype != torch.float32 or nu.dtype != torch.float32:
+        raise TypeError("mu and nu must be float32")
+    S, H, d = v.shape
+    d_feat = mu.shape[2]
+    if mu.shape != (S, H, d_feat, d) or nu.shape != (S, H, d_feat):
+        raise ValueError("mu must be [S,H,d_feat,d] and nu [S,H,d_feat]")
+    mapk = _map_code(feature_map)
+    m = _check_omega(omega, mapk, d)
+    if mapk == MAP_PERFORMER and m != d_feat:
+        raise ValueError(f"omega has {m} features, mu has d_feat={d_feat}")
+    if mapk == MAP_ELU1 and d_feat != d:
+        raise ValueError("elu1 keeps the width: mu must be [S,H,d,d]")
+    dqk = d_feat if mapk == MAP_IDENTITY else d
+    if q.shape != (S, H, dqk) or k.shape != (S, H, dqk):
+        raise ValueError(f"q, k must be [S={S}, H={H}, {dqk}]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    _dtype_code(v.dtype)
+    lay = _layout_code(layout)
+    want = {LD_CHANNEL: (H, d_feat), LD_POSITION: (S, H),
+            LD_BOTH: (S, H, d_feat)}[lay]
+    if log_decay.dtype != torch.float32:
+        raise TypeError("log_decay must be float32")
+    if tuple(log_decay.shape) != want:
+        raise ValueError(f"log_decay must be {want}, got "
+                         f"{tuple(log_decay.shape)}")
+    if out is not None:
+        _check_out(out, v.shape, v.dtype)
+    _on_gpu(v, (mu, "mu"), (nu, "nu"), (q, "q"), (k, "k"), (v, "v"),
+            (out, "out"), (omega, "omega"), (log_decay, "log_decay"))
+    if out is None:
+        out = torch.empty_like(v)
+    st = lib.la_decode_step_gated(_ptr(mu), _ptr(nu), _ptr(q), _ptr(k),
+                                  _ptr(v), _ptr(out), S, H, d, d_feat, mapk,
+                                  _ptr(omega), _ptr(log_decay), lay,
+                                  _dtype_code(v.dtype), _stream(v.device))
+    _check(st, "la_decode_step_gated")
     return out

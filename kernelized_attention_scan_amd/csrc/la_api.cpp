@@ -67,7 +67,11 @@ struct FwdPlan {
   bool fused_performer = false;  // Performer map applied inside the forward
   size_t feat_bytes = 0;    // one of Q', K' (unfused PERFORMER only)
   size_t sync_bytes = 0;    // synchronisation area
-  size_t state_bytes = 0;   // synchronisation area + segment aggregates
+  size_t agg_bytes = 0;     // segment aggregates
+  // synchronisation area + segment aggregates + each segment's sum of log2
+  // decay (used with per-position decay; reserved always, so a workspace's
+  // size does not depend on the kind of decay)
+  size_t state_bytes = 0;
   // Q', K' start after the aggregates, and never below the fixed
   // synchronisation area even when this call has no segments: a workspace
   // shared with segmented calls keeps that area zero between calls, so no
@@ -83,8 +87,9 @@ struct FwdPlan {
 // Validates la_forward's sizes and enums (not pointers) and fills the plan.
 // A non-zero state_cap bounds the synchronisation area plus the segment
 // aggregates: the split then takes fewer segments per unit until they fit.
+// decay: 0 none, 1 one value per head, 2 one per position.
 la_status plan_forward(int B, int H, int64_t n, int d, int d_feat, int map,
-                       int dtype, int causal, bool decay, FwdPlan *p,
+                       int dtype, int causal, int decay, FwdPlan *p,
                        size_t state_cap = 0) {
   if (B < 0 || H < 0 || n < 0)
     return fail(LA_ERR_INVALID_ARG, "negative size: B=%d H=%d n=%lld", B, H,
@@ -104,16 +109,18 @@ la_status plan_forward(int B, int H, int64_t n, int d, int d_feat, int map,
   // depend on decay); otherwise q', k' go through the workspace.
   if (map == LA_MAP_PERFORMER && dtype == LA_BF16) {
     const la::FwdOps *pf = la::fwd_ops_bf16_performer(d, d_feat);
-    if (pf && pf->decay_ok) {
+    if (pf && pf->decay_ok && pf->sel_ok) {
       p->ops = pf;
       p->fused_performer = true;
     }
   }
   if (!p->fused_performer)
     p->ops = dtype == LA_BF16 ? la::fwd_ops_bf16(d, d_feat) : la::fwd_ops_f32(d, d_feat);
-  if (!p->ops || (decay && !p->ops->decay_ok))
+  if (!p->ops || (decay == 1 && !p->ops->decay_ok) ||
+      (decay == 2 && !p->ops->sel_ok))
     return fail(LA_ERR_UNSUPPORTED, "no %s%s kernel for d=%d d_feat=%d (LDS)",
-                dtype == LA_BF16 ? "bf16" : "fp32", decay ? " decayed" : "", d,
+                dtype == LA_BF16 ? "bf16" : "fp32",
+                decay == 1 ? " decayed" : decay == 2 ? " gated" : "", d,
                 d_feat);
   const int64_t units = static_cast<int64_t>(B) * H;
   if (units == 0 || n == 0) return LA_OK;
@@ -132,10 +139,11 @@ la_status plan_forward(int B, int H, int64_t n, int d, int d_feat, int map,
   if (per_unit > nchunks) per_unit = nchunks;
   if (state_cap > 0) {
     const size_t slot = static_cast<size_t>(p->ops->slot_floats) * sizeof(float);
-    while (per_unit > 1 &&
-           la::kSyncBytes + align256(static_cast<size_t>(units) * per_unit * slot) >
-               state_cap)
-      --per_unit;
+    auto need = [&](int64_t k) {
+      return la::kSyncBytes + align256(static_cast<size_t>(units) * k * slot) +
+             align256(static_cast<size_t>(units) * k * sizeof(float));
+    };
+    while (per_unit > 1 && need(per_unit) > state_cap) --per_unit;
   }
   const int64_t cps = (nchunks + per_unit - 1) / per_unit;
   p->seg_len = cps * C;
@@ -147,11 +155,15 @@ la_status plan_forward(int B, int H, int64_t n, int d, int d_feat, int map,
     return fail(LA_ERR_HIP, "internal: segmented split for %lld units",
                 static_cast<long long>(units));
   p->sync_bytes = p->need_states ? la::kSyncBytes : 0;
-  p->state_bytes = p->need_states
-                       ? p->sync_bytes +
-                             align256(static_cast<size_t>(units) * p->nseg *
-                                      p->ops->slot_floats * sizeof(float))
-                       : 0;
+  p->agg_bytes = p->need_states
+                     ? align256(static_cast<size_t>(units) * p->nseg *
+                                p->ops->slot_floats * sizeof(float))
+                     : 0;
+  p->state_bytes =
+      p->need_states
+          ? p->sync_bytes + p->agg_bytes +
+                align256(static_cast<size_t>(units) * p->nseg * sizeof(float))
+          : 0;
   p->feat_bytes = map == LA_MAP_PERFORMER && !p->fused_performer
                       ? align256(static_cast<size_t>(units * n) * d_feat *
                                  elem_size(dtype))
@@ -166,15 +178,18 @@ la_status plan_forward(int B, int H, int64_t n, int d, int d_feat, int map,
 // workspace_cap != 0: the workspace holds only that many bytes (the
 // allocation-free entry point), so the plan fits its split into it and
 // rejects the unfused Performer map, whose features need n-sized buffers.
+// log_decay (per-position decay, [B][H][n]) replaces decay when given.
 static la_status forward_impl(const void *q, const void *k, const void *v, void *out,
                        int B, int H, int64_t n, int d, int d_feat, int map,
                        const float *omega, const float *decay, int causal,
                        int dtype, void *workspace, float *mu_out, float *nu_out,
-                       void *stream, size_t workspace_cap = 0) {
+                       void *stream, size_t workspace_cap = 0,
+                       const float *log_decay = nullptr) {
   try {
     FwdPlan p;
+    const int dkind = log_decay ? 2 : decay ? 1 : 0;
     const la_status st = plan_forward(B, H, n, d, d_feat, map, dtype, causal,
-                                      decay != nullptr, &p, workspace_cap);
+                                      dkind, &p, workspace_cap);
     if (st != LA_OK) return st;
     if (workspace_cap > 0 && p.total() > workspace_cap)
       return fail(LA_ERR_UNSUPPORTED, "workspace of %zu bytes needed, %zu held",
@@ -221,6 +236,10 @@ static la_status forward_impl(const void *q, const void *k, const void *v, void 
     a.sync = p.need_states ? reinterpret_cast<unsigned *>(ws) : nullptr;
     a.states = p.need_states ? reinterpret_cast<float *>(ws + p.sync_bytes)
                              : nullptr;
+    a.seg_log = p.need_states ? reinterpret_cast<float *>(
+                                    ws + p.sync_bytes + p.agg_bytes)
+                              : nullptr;
+    a.log_decay = log_decay;
     a.H = H;
     a.n = n;
     a.seg_len = p.seg_len;
@@ -337,7 +356,7 @@ size_t la_forward_workspace_bytes(int B, int H, int64_t n, int d, int d_feat,
     FwdPlan p;
     // The workspace does not depend on decay; size it for the plain variant.
     const la_status st =
-        plan_forward(B, H, n, d, d_feat, map, dtype, causal, false, &p);
+        plan_forward(B, H, n, d, d_feat, map, dtype, causal, 0, &p);
     g_last_error = saved;
     if (st != LA_OK) return 0;
     return p.total();
@@ -375,7 +394,7 @@ la_status la_forward_noalloc(const void *q, const void *k, const void *v,
     // validate first, so invalid requests touch no device
     FwdPlan p;
     la_status st = plan_forward(B, H, n, d, d_feat, map, dtype, causal,
-                                decay != nullptr, &p, kScratchBytes);
+                                decay != nullptr ? 1 : 0, &p, kScratchBytes);
     if (st != LA_OK) return st;
     if (static_cast<int64_t>(B) * H == 0 || n == 0) return ok();
     if (!q || !k || !v || !out)
@@ -435,10 +454,37 @@ void la_set_exchange_spin_limit(unsigned spins) {
                      std::memory_order_relaxed);
 }
 
-la_status la_decode_step(float *mu, float *nu, const void *q, const void *k,
-                         const void *v, void *out, int S, int H, int d,
-                         int d_feat, la_map map, const float *omega,
-                         const float *decay, la_dtype dtype, void *stream) {
+la_status la_forward_gated(const void *q, const void *k, const void *v,
+                           void *out, int B, int H, int64_t n, int d,
+                           int d_feat, la_map map, const float *omega,
+                           const float *log_decay, la_decay_layout layout,
+                           int causal, la_dtype dtype, void *workspace,
+                           float *mu_out, float *nu_out, void *stream) {
+  if (layout != LA_LD_CHANNEL && layout != LA_LD_POSITION &&
+      layout != LA_LD_BOTH)
+    return fail(LA_ERR_INVALID_ARG, "unknown decay layout %d", layout);
+  if (layout != LA_LD_POSITION)
+    return fail(LA_ERR_UNSUPPORTED,
+                "la_forward_gated: only the per-position layout is built for "
+                "the chunked forward (per-row decays need decay weights "
+                "inside the feature contraction); the decode step takes "
+                "every layout");
+  if ((mu_out == nullptr) != (nu_out == nullptr))
+    return fail(LA_ERR_INVALID_ARG, "mu_out and nu_out go together");
+  if (!log_decay && static_cast<int64_t>(B) * H > 0 && n > 0)
+    return fail(LA_ERR_INVALID_ARG, "null log_decay");
+  return forward_impl(q, k, v, out, B, H, n, d, d_feat, map, omega, nullptr,
+                      causal, dtype, workspace, mu_out, nu_out, stream, 0,
+                      log_decay ? log_decay : nullptr);
+}
+
+// la_decode_step and la_decode_step_gated: ld_layout < 0 for the former
+// (decay [H] or NULL), else the layout of log_decay.
+static la_status decode_impl(float *mu, float *nu, const void *q, const void *k,
+                             const void *v, void *out, int S, int H, int d,
+                             int d_feat, int map, const float *omega,
+                             const float *decay, int dtype, void *stream,
+                             int ld_layout) {
   try {
     if (S < 0 || H < 0) return fail(LA_ERR_INVALID_ARG, "negative size");
     if (!valid_map(map)) return fail(LA_ERR_INVALID_ARG, "unknown map %d", map);
@@ -457,14 +503,37 @@ la_status la_decode_step(float *mu, float *nu, const void *q, const void *k,
       return fail(LA_ERR_INVALID_ARG, "null pointer argument");
     if (map == LA_MAP_PERFORMER && !omega)
       return fail(LA_ERR_INVALID_ARG, "PERFORMER needs omega");
-    const hipError_t e =
-        la::launch_decode(mu, nu, q, k, v, out, units, H, d, d_feat, map, omega,
-                          decay, dtype, static_cast<hipStream_t>(stream));
+    if (ld_layout >= 0 && !decay)
+      return fail(LA_ERR_INVALID_ARG, "null log_decay");
+    const hipError_t e = la::launch_decode(
+        mu, nu, q, k, v, out, units, H, d, d_feat, map, omega, decay, dtype,
+        static_cast<hipStream_t>(stream), ld_layout);
     if (e != hipSuccess) return hip_fail(e, "la_decode_step launch");
     return ok();
   } catch (...) {
     return fail(LA_ERR_HIP, "unexpected exception in la_decode_step");
   }
+}
+
+la_status la_decode_step(float *mu, float *nu, const void *q, const void *k,
+                         const void *v, void *out, int S, int H, int d,
+                         int d_feat, la_map map, const float *omega,
+                         const float *decay, la_dtype dtype, void *stream) {
+  return decode_impl(mu, nu, q, k, v, out, S, H, d, d_feat, map, omega, decay,
+                     dtype, stream, -1);
+}
+
+la_status la_decode_step_gated(float *mu, float *nu, const void *q,
+                               const void *k, const void *v, void *out, int S,
+                               int H, int d, int d_feat, la_map map,
+                               const float *omega, const float *log_decay,
+                               la_decay_layout layout, la_dtype dtype,
+                               void *stream) {
+  if (layout != LA_LD_CHANNEL && layout != LA_LD_POSITION &&
+      layout != LA_LD_BOTH)
+    return fail(LA_ERR_INVALID_ARG, "unknown decay layout %d", layout);
+  return decode_impl(mu, nu, q, k, v, out, S, H, d, d_feat, map, omega,
+                     log_decay, dtype, stream, static_cast<int>(layout));
 }
 
 }  // extern "C"

@@ -14,6 +14,12 @@
 // in flight), then it updates, stores, and accumulates q'_f mu'[f][j..j+3].
 // The column partials are reduced through LDS in a fixed order (bitwise
 // deterministic), and q'.nu' by a fixed-order wave/LDS tree.
+//
+// Gated form (ROWS): every state row f decays by its own gamma_f =
+// exp(lam_f) with input weight 1 - gamma_f, lam given per row and head
+// (the diagonal A of "2.3 State-Space Models" eqs 21-25), per unit (the
+// input-dependent decay of Mamba's selective step, "Linear attention
+// research 2026" page), or per unit and row.
 #include "la_device.h"
 #include "la_internal.h"
 
@@ -40,24 +46,39 @@ __device__ __forceinline__ float block_sum(float x, float *red) {
   return s;
 }
 
-template <typename T, int D, int DF>
+// Layouts of the gated decode's log decay (la_decay_layout).
+constexpr int kLdChannel = 0, kLdPosition = 1, kLdBoth = 2;
+
+template <typename T, int D, int DF, bool ROWS>
 __global__ __launch_bounds__(kDecThreads) void la_decode_kernel(
     float *__restrict__ mu, float *__restrict__ nu, const T *__restrict__ q,
     const T *__restrict__ k, const T *__restrict__ v, T *__restrict__ out,
     int H, int map, const float *__restrict__ omega,
-    const float *__restrict__ decay) {
+    const float *__restrict__ decay, int ld_layout) {
   constexpr int TPR = D / 4;                 // threads per mu row (float4)
   constexpr int RPP = kDecThreads / TPR;     // rows per pass
   constexpr int ITER = (DF + RPP - 1) / RPP;
   __shared__ float qf[DF], kf[DF], vv[D], xq[D], xk[D];
   __shared__ float red[RPP][D];
   __shared__ float red4[kDecThreads / kWave];
+  // gated form: decay and input weight of every row
+  __shared__ float grow[ROWS ? DF : 1], brow[ROWS ? DF : 1];
 
   const int tid = threadIdx.x;
   const int64_t u = blockIdx.x;
   const int h = static_cast<int>(u % H);
-  const float g = decay ? decay[h] : 1.f;
-  const float b = decay ? 1.f - g : 1.f;
+  const float g = !ROWS && decay ? decay[h] : 1.f;
+  const float b = !ROWS && decay ? 1.f - g : 1.f;
+  if constexpr (ROWS) {
+    // decay holds log gamma in the given layout
+    for (int f = tid; f < DF; f += kDecThreads) {
+      const float lam = ld_layout == kLdChannel ? decay[h * DF + f]
+                        : ld_layout == kLdPosition ? decay[u]
+                                                   : decay[u * DF + f];
+      grow[f] = expf(lam);
+      brow[f] = -expm1f(lam);  // 1 - gamma, accurate for gamma near 1
+    }
+  }
 
   // ---- features of the new token ----
   if (map == 2) {
@@ -98,7 +119,8 @@ __global__ __launch_bounds__(kDecThreads) void la_decode_kernel(
   // ---- nu' = g nu + b k' and the denominator q' . nu' ----
   float part = 0.f;
   for (int f = tid; f < DF; f += kDecThreads) {
-    const float nn = g * nu[u * DF + f] + b * kf[f];
+    const float gf = ROWS ? grow[f] : g, bf = ROWS ? brow[f] : b;
+    const float nn = gf * nu[u * DF + f] + bf * kf[f];
     nu[u * DF + f] = nn;
     part += qf[f] * nn;
   }
@@ -120,7 +142,8 @@ __global__ __launch_bounds__(kDecThreads) void la_decode_kernel(
   for (int i = 0; i < ITER; ++i) {
     const int f = f0 + RPP * i;
     if (f < DF) {
-      const f32x4 nm = g * m[i] + (b * kf[f]) * v4;
+      const float gf = ROWS ? grow[f] : g, bf = ROWS ? brow[f] : b;
+      const f32x4 nm = gf * m[i] + (bf * kf[f]) * v4;
       __builtin_nontemporal_store(nm, reinterpret_cast<f32x4 *>(mub + f * D));
       acc += qf[f] * nm;
     }
@@ -138,21 +161,32 @@ __global__ __launch_bounds__(kDecThreads) void la_decode_kernel(
   }
 }
 
+// ld_layout < 0: decay is [H] (or null); else decay holds log gamma in that
+// layout (the gated form).
 template <typename T, int D, int DF>
 hipError_t run_decode(float *mu, float *nu, const void *q, const void *k,
                       const void *v, void *out, int64_t units, int H, int map,
-                      const float *omega, const float *decay, hipStream_t s) {
-  hipLaunchKernelGGL((la_decode_kernel<T, D, DF>), dim3(units),
-                     dim3(kDecThreads), 0, s, mu, nu,
-                     static_cast<const T *>(q), static_cast<const T *>(k),
-                     static_cast<const T *>(v), static_cast<T *>(out), H, map,
-                     omega, decay);
+                      const float *omega, const float *decay, int ld_layout,
+                      hipStream_t s) {
+  if (ld_layout >= 0)
+    hipLaunchKernelGGL((la_decode_kernel<T, D, DF, true>), dim3(units),
+                       dim3(kDecThreads), 0, s, mu, nu,
+                       static_cast<const T *>(q), static_cast<const T *>(k),
+                       static_cast<const T *>(v), static_cast<T *>(out), H,
+                       map, omega, decay, ld_layout);
+  else
+    hipLaunchKernelGGL((la_decode_kernel<T, D, DF, false>), dim3(units),
+                       dim3(kDecThreads), 0, s, mu, nu,
+                       static_cast<const T *>(q), static_cast<const T *>(k),
+                       static_cast<const T *>(v), static_cast<T *>(out), H,
+                       map, omega, decay, ld_layout);
   return hipGetLastError();
 }
 
 using DecodeFn = hipError_t (*)(float *, float *, const void *, const void *,
                                 const void *, void *, int64_t, int, int,
-                                const float *, const float *, hipStream_t);
+                                const float *, const float *, int,
+                                hipStream_t);
 
 template <typename T, int D>
 DecodeFn decode_by_feat(int df) {
@@ -186,11 +220,12 @@ bool decode_supported(int d, int d_feat) {
 hipError_t launch_decode(float *mu, float *nu, const void *q, const void *k,
                          const void *v, void *out, int64_t units, int H, int d,
                          int d_feat, int map, const float *omega,
-                         const float *decay, int dtype, hipStream_t s) {
+                         const float *decay, int dtype, hipStream_t s,
+                         int ld_layout) {
   DecodeFn fn = dtype == 1 ? decode_fn<bf16>(d, d_feat)
                            : decode_fn<float>(d, d_feat);
   if (!fn) return hipErrorInvalidValue;
-  return fn(mu, nu, q, k, v, out, units, H, map, omega, decay, s);
+  return fn(mu, nu, q, k, v, out, units, H, map, omega, decay, ld_layout, s);
 }
 
 }  // namespace la

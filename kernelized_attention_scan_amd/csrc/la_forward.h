@@ -106,19 +106,21 @@ constexpr int kMapElu = 1;        // elu + 1 (d' = d)
 constexpr int kMapPerformer = 2;  // Performer random features, fused
 
 // LDS bytes of one instance with chunk length c (see FwdShape): nbuf sets of
-// the q', w.k', V and S^T tiles, kslots slots of k', and the raw q, k rows of
-// the fused Performer map.
+// the q', w.k' (wkeys), V and S^T tiles, kslots slots of k', the raw q, k
+// rows of the fused Performer map, and with per-position decay (sel) one
+// table of the chunk's decay weights per set.
 template <typename T>
-constexpr size_t fwd_lds_bytes(int c, int d, int df, bool decay, bool pf,
-                               int kslots = 1, int nbuf = 1) {
+constexpr size_t fwd_lds_bytes(int c, int d, int df, bool wkeys, bool pf,
+                               int kslots = 1, int nbuf = 1, bool sel = false) {
   const int dfp = df < 32 ? 32 : df;
   const size_t sq = static_cast<size_t>(c) * lds_stride<T>(dfp);
   const size_t sv = static_cast<size_t>(c) * lds_stride<T>(d + 16);
   const size_t sst = static_cast<size_t>(d + 16) * lds_stride<T>(dfp);
   const size_t sx = pf ? static_cast<size_t>(c) * lds_stride<T>(d) : 0;
-  return sizeof(T) * (nbuf * (sq + (decay ? sq : 0) + sv + sst) +
+  return sizeof(T) * (nbuf * (sq + (wkeys ? sq : 0) + sv + sst) +
                       kslots * sq + 2 * sx) +
-         sizeof(float) * (c + 8 + (pf ? 2 * c : 0));
+         sizeof(float) * (c + 8 + kMaxSegments + (pf ? 2 * c : 0) +
+                          (sel ? nbuf * (3 * c + 4) : 0));
 }
 
 // Largest power of two <= x, at most 8 (1 for x < 2).
@@ -126,15 +128,22 @@ constexpr int pow2_floor(int x) {
   return x >= 8 ? 8 : x >= 4 ? 4 : x >= 2 ? 2 : 1;
 }
 
-template <typename T, int D, int DF, bool DECAY, int MAP = kMapFeatures>
+// DK: 0 no decay (eqs 7-8); 1 one decay a per head (eqs 10-11); 2 a decay
+// per position, given as its natural log (the input-dependent decay).
+template <typename T, int D, int DF, int DK, int MAP = kMapFeatures>
 struct FwdShape {
+  static constexpr bool DECAY = DK != 0;
+  static constexpr bool SEL = DK == 2;    // per-position decay
+  static constexpr bool WKEYS = DK == 1;  // a staged tile of weighted keys
   static constexpr bool PF = MAP == kMapPerformer;
   static constexpr int DV = D;                       // value width d
   // width of the q, k rows in memory: d for the fused Performer map
   static constexpr int QW = PF ? D : DF;
   // Chunk rows: 64 for bf16 operands; 32 where LDS would not hold 64.
   static constexpr int C =
-      PF ? (fwd_lds_bytes<T>(64, D, DF, DECAY, true) <= kMaxLds ? 64 : 32)
+      PF ? (fwd_lds_bytes<T>(64, D, DF, WKEYS, true, 1, 1, SEL) <= kMaxLds
+                ? 64
+                : 32)
          : ((sizeof(T) == 2 && !(DF == 256 && D == 128)) ? 64 : 32);
   static constexpr int DFP = DF < 32 ? 32 : DF;      // padded k-width of q', k'
   static constexpr int LQ = lds_stride<T>(DFP);      // sQ, sK, sKw, sST
@@ -149,7 +158,7 @@ struct FwdShape {
   static constexpr int FPW = NF >= kWaves ? NF / kWaves : 1;
   static constexpr int WPF = NF >= kWaves ? 1 : kWaves / NF;
   static constexpr int JPW = (NJA + WPF - 1) / WPF;
-  static constexpr int SQ = C * LQ, SKW = DECAY ? C * LQ : 0, SV = C * LV,
+  static constexpr int SQ = C * LQ, SKW = WKEYS ? C * LQ : 0, SV = C * LV,
                        SST = (D + 16) * LQ, SX = PF ? C * LX : 0;
   // Fused Performer projection: omega^T tiles per wave (kept in registers
   // for the whole kernel) and the strips each wave maps.  NF >= 8: wave w
@@ -168,16 +177,18 @@ struct FwdShape {
       !PF && !DECAY && sizeof(T) == 2 && D <= 64 && DF <= 64;
   static constexpr int KRES_ =
       !RES_OK ? 0
-      : fwd_lds_bytes<T>(C, D, DF, DECAY, PF, 8, 2) <= kMaxLds ? 8
-      : fwd_lds_bytes<T>(C, D, DF, DECAY, PF, 4, 2) <= kMaxLds ? 4
+      : fwd_lds_bytes<T>(C, D, DF, WKEYS, PF, 8, 2, SEL) <= kMaxLds ? 8
+      : fwd_lds_bytes<T>(C, D, DF, WKEYS, PF, 4, 2, SEL) <= kMaxLds ? 4
                                                                 : 0;
   static constexpr int KS2 = KRES_ > 2 ? KRES_ : 2;
   static constexpr bool PIPE =
-      !PF && fwd_lds_bytes<T>(C, D, DF, DECAY, PF, KS2, 2) <= kMaxLds;
+      !PF && fwd_lds_bytes<T>(C, D, DF, WKEYS, PF, KS2, 2, SEL) <= kMaxLds;
   static constexpr int NBUF = PIPE ? 2 : 1;                 // sets of tiles
   static constexpr int KS = PIPE ? KS2 : 1;                 // slots of sK
   static constexpr size_t lds_bytes =
-      fwd_lds_bytes<T>(C, D, DF, DECAY, PF, KS, NBUF);
+      fwd_lds_bytes<T>(C, D, DF, WKEYS, PF, KS, NBUF, SEL);
+  // per-position decay: floats of one set's table (see sel_table)
+  static constexpr int TAB = SEL ? 3 * C + 4 : 0;
   // fp32 state slot: NTILE tiles x 64 lanes x 4 (accumulator order).
   static constexpr int SLOT = NTILE * 256;
   // Workgroups per compute unit the instance is built for: two (<= 128
@@ -245,6 +256,86 @@ __device__ __forceinline__ Frag<T> ones_frag(int li) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) f.v[e] = from_f32<T>(li % 4 == 0 ? 1.f : 0.f);
   return f;
+}
+
+// ---------------------------------------------------------------------------
+// Per-position decay (the input-dependent decay of the Mamba section of the
+// "Linear attention research 2026" page, applied as eqs 10-11 with a per
+// position: gamma_t = exp(lam_t), input weight 1 - gamma_t).  With L_t the
+// sum of log2 gamma over the chunk's rows 0..t, the chunk formulas weight
+//   P[t][s] by (1 - gamma_s) 2^(L_t - L_s)   (s <= t),
+//   the entering state's readout by 2^(L_t),
+//   key s in the state update by (1 - gamma_s) 2^(L_last - L_s),
+//   the state itself by 2^(L_last),
+// where L_last is the sum over the whole chunk (rows past the end have
+// lam = 0).
+// ---------------------------------------------------------------------------
+
+// The chunk's log decays, one per row, in the first C threads (one dword
+// each, so a partly valid 16-byte piece can never be dropped whole by the
+// range check); 0 past the valid rows and in the other threads.
+template <int C>
+struct LamSlab {
+  float v;
+  __device__ __forceinline__ void load(const float *base, int64_t row0,
+                                       int rows, int tid) {
+    v = 0.f;
+    if (tid < C) {
+      const __amdgpu_buffer_rsrc_t r =
+          make_rsrc(base + row0, static_cast<unsigned>(rows) * 4u);
+      v = __builtin_bit_cast(float,
+                             __builtin_amdgcn_raw_buffer_load_b32(r, 4u * tid, 0, 0));
+    }
+  }
+};
+
+// The chunk's table, computed by the threads of wave 0 from their LamSlab
+// (C <= 64, lane t holds row t): tab[t] = L_t, tab[C + t] = 1 - gamma_t,
+// tab[2C + t] = state-update weight of key t, tab[3C] = 2^(L_last).  Returns
+// L_last (every lane).
+template <int C>
+__device__ __forceinline__ float sel_table(float lam, float *tab, int lane) {
+  static_assert(C <= kWave, "one row per lane of one wave");
+  constexpr float kLog2e = 1.4426950408889634f;
+  // Below -104, exp(lam) is 0 in fp32 (under the smallest subnormal), so
+  // the floor changes no decay; it keeps the sums finite when lam = -inf
+  // (a full reset), whose differences would otherwise be -inf - -inf.
+  lam = fmaxf(lam, -104.f);
+  float L = lane < C ? lam * kLog2e : 0.f;
+#pragma unroll
+  for (int o = 1; o < C; o <<= 1) {  // inclusive scan over the chunk's rows
+    const float y = __shfl_up(L, o);
+    if (lane >= o) L += y;
+  }
+  const float last = __shfl(L, C - 1);
+  if (lane < C) {
+    const float beta = -expm1f(lam);  // 1 - gamma, accurate for gamma near 1
+    tab[lane] = L;
+    tab[C + lane] = beta;
+    tab[2 * C + lane] = beta * __builtin_amdgcn_exp2f(last - L);
+    if (lane == 0) tab[3 * C] = __builtin_amdgcn_exp2f(last);
+  }
+  return last;
+}
+
+// Element e of f times the weight of its position: w0 for elements 0..3,
+// w1 for 4..7 (rounded back to the operand type).
+__device__ __forceinline__ void frag_scale(Frag<bf16> &f, const f32x4 &w0,
+                                           const f32x4 &w1) {
+  const u32x4 u = __builtin_bit_cast(u32x4, f.v);
+  const u32x4 r = {pack_bf16x2(bf16_lo(u[0]) * w0[0], bf16_hi(u[0]) * w0[1]),
+                   pack_bf16x2(bf16_lo(u[1]) * w0[2], bf16_hi(u[1]) * w0[3]),
+                   pack_bf16x2(bf16_lo(u[2]) * w1[0], bf16_hi(u[2]) * w1[1]),
+                   pack_bf16x2(bf16_lo(u[3]) * w1[2], bf16_hi(u[3]) * w1[3])};
+  f.v = __builtin_bit_cast(bf16x8, r);
+}
+__device__ __forceinline__ void frag_scale(Frag<float> &f, const f32x4 &w0,
+                                           const f32x4 &w1) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f.v[e] *= w0[e];
+    f.v[4 + e] *= w1[e];
+  }
 }
 
 // Per-head decay: g = a, b = 1 - a (eqs 10-11); g = b = 1 without decay.
@@ -466,12 +557,15 @@ __device__ __forceinline__ void performer_features(
 // S tiles of this wave += (w.K')^T [V | 1] over the chunk: A = rows of sKw
 // read transposed (features along lanes), B = rows of sV read transposed
 // (columns along lanes); contraction over the chunk positions.
-// kmask = 0 drops the keys (the state is only scaled by gr).
+// kmask = 0 drops the keys (the state is only scaled by gr).  With wk (per-
+// position decay) the keys of sKw are plain and position s is weighted by
+// wk[s] in registers.
 template <typename F, typename T>
 __device__ __forceinline__ void state_update(f32x4 *S, const T *sKw,
                                              const T *sV, float gr, int w,
                                              int g, int li,
-                                             unsigned kmask = ~0u) {
+                                             unsigned kmask = ~0u,
+                                             const float *wk = nullptr) {
   constexpr int C = F::C;
 #pragma unroll
   for (int m = 0; m < F::FPW; ++m) {
@@ -481,6 +575,10 @@ __device__ __forceinline__ void state_update(f32x4 *S, const T *sKw,
     for (int kb = 0; kb < C / 32; ++kb) {
       load_frag_tr8(af[kb], sKw, F::LQ, 32 * kb, 16 * fb, g, li);
       frag_mask(af[kb], u32x4{kmask, kmask, kmask, kmask});
+      if constexpr (F::SEL) {  // positions 32 kb + 8 g + e
+        const f32x4 *wp = reinterpret_cast<const f32x4 *>(wk + 32 * kb + 8 * g);
+        frag_scale(af[kb], wp[0], wp[1]);
+      }
     }
 #pragma unroll
     for (int mj = 0; mj < F::JPW; ++mj) {
@@ -654,12 +752,14 @@ __device__ __forceinline__ void count_done(unsigned *line, int nseg) {
 // only, reading every aggregate a launch with SPLIT = 1 stored before it on
 // the same stream (the launch boundary orders them: no flags, no waits, no
 // co-residency).
-template <typename T, int D, int DF, bool CAUSAL, bool MULTI, bool DECAY,
+// DK: the decay mode of FwdShape (0 none, 1 per head, 2 per position).
+template <typename T, int D, int DF, bool CAUSAL, bool MULTI, int DK,
           int MAP, bool RES = false, int SPLIT = 0>
 __global__ __launch_bounds__(kThreads,
-                             (FwdShape<T, D, DF, DECAY, MAP>::WAVES_PER_SIMD))
+                             (FwdShape<T, D, DF, DK, MAP>::WAVES_PER_SIMD))
 void la_fwd_kernel(FwdArgs a) {
-  using F = FwdShape<T, D, DF, DECAY, MAP>;
+  using F = FwdShape<T, D, DF, DK, MAP>;
+  constexpr bool DECAY = F::DECAY, SEL = F::SEL, WKEYS = F::WKEYS;
   static_assert(!RES || (F::KRES > 0 && CAUSAL && MULTI), "resident keys");
   static_assert(SPLIT == 0 || (MULTI && !CAUSAL && !RES), "split launches");
   // the in-kernel exchange through the synchronisation area
@@ -674,17 +774,21 @@ void la_fwd_kernel(FwdArgs a) {
   // one per set)
   T *sQ = reinterpret_cast<T *>(smem);
   T *sK = sQ + F::NBUF * F::SQ;
-  T *sKw = DECAY ? sK + F::SQ * F::KS : sK;
+  T *sKw = WKEYS ? sK + F::SQ * F::KS : sK;
   T *sV = sK + F::SQ * F::KS + F::NBUF * F::SKW;
   T *sST = sV + F::NBUF * F::SV;
   T *sXq = sST + F::NBUF * F::SST;  // raw q, k rows (fused Performer)
   T *sXk = sXq + F::SX;
   float *gp = reinterpret_cast<float *>(sXk + F::SX);
   // fused Performer: the exponent offsets of the chunk's q rows, then of its
-  // k rows (see stage_rows_pf), after the C + 8 words of gp: the powers
-  // g^0 .. g^C, then the segment ticket, the two XCD record words and the
-  // exchange's give-up flag
-  float *pc0 = gp + C + 8;
+  // k rows (see stage_rows_pf), after the C + 8 + kMaxSegments words of gp:
+  // the powers g^0 .. g^C, then the segment ticket, the two XCD record
+  // words, the exchange's give-up flag and (per-position decay) the weights
+  // of the segment aggregates
+  float *pc0 = gp + C + 8 + kMaxSegments;
+  float *sw = gp + C + 8;
+  // per-position decay: the chunk tables, one per tile set (see sel_table)
+  float *stab = pc0 + (PF ? 2 * C : 0);
   const float lsm = 0.5f * __builtin_log2f(static_cast<float>(DF));
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -709,6 +813,8 @@ void la_fwd_kernel(FwdArgs a) {
   const T *qb = static_cast<const T *>(a.q) + unit * a.n * QW;
   const T *kb = static_cast<const T *>(a.k) + unit * a.n * QW;
   const T *vb = static_cast<const T *>(a.v) + unit * a.n * D;
+  // per-position decay: the unit's log decays [n]
+  const float *lb = SEL ? a.log_decay + unit * a.n : nullptr;
   T *ob = static_cast<T *>(a.out) + unit * a.n * D;
   // Before the ticket returns, each workgroup loads the first phase-1 chunk
   // of the segment its block would take in block order (guess).  The
@@ -805,6 +911,8 @@ void la_fwd_kernel(FwdArgs a) {
   constexpr bool resident = RES;
 
   f32x4 S[TW];
+  // per-position decay: sum of log2 gamma over this segment (phase 1)
+  float seg_log2 = 0.f;
 #pragma unroll
   for (int i = 0; i < TW; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -826,23 +934,25 @@ void la_fwd_kernel(FwdArgs a) {
   // loads are issued once the aggregate is published and overlap the wait.
   Slab<T, QW, C> rq[NB2], rk2[NB2];
   Slab<T, D, C> rv2[NB2];
+  LamSlab<C> rl2[NB2];
   auto load2 = [&](int c, Slab<T, QW, C> &sq, Slab<T, QW, C> &sk,
-                   Slab<T, D, C> &sv) {
+                   Slab<T, D, C> &sv, LamSlab<C> &sl) {
     const int64_t r0 = start + clamp_chunk(c) * C;
     const int rows = rows_of(c);  // 0 for padding chunks: zeros, no traffic
     sq.load(qb, r0, rows, tid);
     if (CAUSAL) {
       if (!resident) sk.load(kb, r0, rows, tid);
       sv.load(vb, r0, rows, tid);
+      if constexpr (SEL) sl.load(lb, r0, rows, tid);
     }
   };
   auto ring2_first = [&]() {
 #pragma unroll
-    for (int b = 0; b < NB2; ++b) load2(b, rq[b], rk2[b], rv2[b]);
+    for (int b = 0; b < NB2; ++b) load2(b, rq[b], rk2[b], rv2[b], rl2[b]);
   };
   // Phase-2 staging of chunk c into its tile set (see the chunk loop).
   auto stage2 = [&](int c, const Slab<T, QW, C> &sq, const Slab<T, QW, C> &sk,
-                    const Slab<T, D, C> &sv) {
+                    const Slab<T, D, C> &sv, const LamSlab<C> &sl) {
     const int sc = set_of(c);
     if constexpr (PF) {
       stage_rows_pf<T, D, C, LX>(sq, sXq, pc0, lsm, C, tid);
@@ -851,10 +961,12 @@ void la_fwd_kernel(FwdArgs a) {
     } else {
       stage_queries<T, DF, C, LQ, ELU>(sq, sQ + sc * F::SQ, tid);
       if (CAUSAL && !resident)
-        stage_keys<T, DF, C, LQ, DECAY, true, ELU>(
+        stage_keys<T, DF, C, LQ, WKEYS, true, ELU>(
             sk, sK + sc * F::SQ, sKw + sc * F::SQ, gp, dk.b, rows_of(c), tid);
     }
     if (CAUSAL) stage_values<T, D, C, LV>(sv, sV + sc * F::SV, tid);
+    if constexpr (SEL)
+      if (CAUSAL && w == 0) sel_table<C>(sl.v, stab + sc * F::TAB, lane);
   };
 
   // The loops below run whole revolutions of their register ring (padding
@@ -870,18 +982,22 @@ void la_fwd_kernel(FwdArgs a) {
     if (SPLIT != 2 && (!CAUSAL || seg + 1 < a.nseg || RES)) {
       Slab<T, QW, C> rk[NB1];
       Slab<T, D, C> rv[NB1];
-      auto load1 = [&](int c, Slab<T, QW, C> &sk, Slab<T, D, C> &sv) {
+      LamSlab<C> rl[NB1];
+      auto load1 = [&](int c, Slab<T, QW, C> &sk, Slab<T, D, C> &sv,
+                       LamSlab<C> &sl) {
         const int64_t r0 = start + clamp_chunk(c) * C;
         sk.load(kb, r0, rows_of(c), tid);
         sv.load(vb, r0, rows_of(c), tid);
+        if constexpr (SEL) sl.load(lb, r0, rows_of(c), tid);
       };
 #pragma unroll
       for (int b = 0; b < NB1; ++b) {
         if (GUESS && b == 0 && a.nseg > 1 && seg == guess) {
           rk[0] = gk;  // the guess was right
           rv[0] = gv;
+          if constexpr (SEL) rl[0].load(lb, start, rows_of(0), tid);
         } else {
-          load1(b, rk[b], rv[b]);
+          load1(b, rk[b], rv[b], rl[b]);
         }
       }
       // phi(K) of chunk c: its resident slot (padding chunks: the unused
@@ -892,26 +1008,28 @@ void la_fwd_kernel(FwdArgs a) {
         return sK + set_of(c) * F::SQ;
       };
       auto stage1 = [&](int c, const Slab<T, QW, C> &sk,
-                        const Slab<T, D, C> &sv) {
+                        const Slab<T, D, C> &sv, const LamSlab<C> &sl) {
         if constexpr (PF)
           stage_rows_pf<T, D, C, LX>(sk, sXk, pc0 + C, lsm, rows_of(c), tid);
         else
-          stage_keys<T, DF, C, LQ, DECAY, false, ELU>(
+          stage_keys<T, DF, C, LQ, WKEYS, false, ELU>(
               sk, keys1(c), sKw + set_of(c) * F::SQ, gp, dk.b, rows_of(c),
               tid);
         stage_values<T, D, C, LV>(sv, sV + set_of(c) * F::SV, tid);
+        if constexpr (SEL)
+          if (w == 0) sel_table<C>(sl.v, stab + set_of(c) * F::TAB, lane);
       };
       auto features1 = [&](int c) {
         if constexpr (PF) {
-          performer_features<F, T, false, true, DECAY, false>(
+          performer_features<F, T, false, true, WKEYS, false>(
               wf, sXq, sXk, pc0, pc0 + C, sQ, sK, sKw, gp, dk.b, rows_of(c),
               w, g, li);
           __syncthreads();
         }
       };
       __syncthreads();  // gp and the constant tile parts ready
-      stage1(0, rk[0], rv[0]);
-      load1(NB1, rk[0], rv[0]);
+      stage1(0, rk[0], rv[0], rl[0]);
+      load1(NB1, rk[0], rv[0], rl[0]);
       if (EXCH && w == 0 && a.nseg > 1)
         recs = __hip_atomic_load(line + kSyncXccWord + (lane & 1),
                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -922,12 +1040,15 @@ void la_fwd_kernel(FwdArgs a) {
         for (int b = 0; b < NB1; ++b) {
           const int c = c0 + b, bn = (b + 1) % NB1;
           const int sc = F::NBUF == 2 && NB1 % 2 == 0 ? (b & 1) : set_of(c);
-          state_update<F>(S, DECAY ? sKw + sc * F::SQ : keys1(c),
-                          sV + sc * F::SV, DECAY ? gp[rows_of(c)] : 1.f, w, g,
-                          li);
+          const float *tabc = stab + sc * F::TAB;
+          state_update<F>(S, WKEYS ? sKw + sc * F::SQ : keys1(c),
+                          sV + sc * F::SV,
+                          WKEYS ? gp[rows_of(c)] : SEL ? tabc[3 * C] : 1.f, w,
+                          g, li, ~0u, tabc + 2 * C);
+          if constexpr (SEL) seg_log2 += tabc[C - 1];
           if (F::NBUF == 1) __syncthreads();
-          stage1(c + 1, rk[bn], rv[bn]);
-          load1(c + 1 + NB1, rk[bn], rv[bn]);
+          stage1(c + 1, rk[bn], rv[bn], rl[bn]);
+          load1(c + 1 + NB1, rk[bn], rv[bn], rl[bn]);
           __syncthreads();
           features1(c + 1);
         }
@@ -959,6 +1080,7 @@ void la_fwd_kernel(FwdArgs a) {
             *reinterpret_cast<f32x4 *>(mine + (idx * 64 + lane) * 4) =
                 S[m * F::JPW + mj];
           }
+        if (SEL && tid == 0) a.seg_log[unit * a.nseg + seg] = seg_log2;
         return;
       }
       if (EXCH && (!CAUSAL || seg + 1 < a.nseg)) {
@@ -977,19 +1099,45 @@ void la_fwd_kernel(FwdArgs a) {
             else
               store_agent(dst, S[m * F::JPW + mj]);
           }
+        if (SEL && tid == 0) {  // the segment's sum of log2 gamma, likewise
+          float *dst = a.seg_log + unit * a.nseg + seg;
+          if (local)
+            *dst = seg_log2;
+          else
+            __hip_atomic_store(dst, seg_log2, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
         publish_flag(line, seg, local);
       }
       // the first chunk's phase-2 loads overlap the wait; the rest of the
       // ring follows the aggregates' loads, which would otherwise complete
       // only after them (loads complete in order)
-      load2(0, rq[0], rk2[0], rv2[0]);
+      load2(0, rq[0], rk2[0], rv2[0], rl2[0]);
       // chunk 0 is staged while the predecessors finish (its tiles are free:
       // phase 1 ended with a workgroup barrier after its last use of them)
-      stage2(0, rq[0], rk2[0], rv2[0]);
+      stage2(0, rq[0], rk2[0], rv2[0], rl2[0]);
       bool gave_up = false;
       if (EXCH && need > 0)
         gave_up = wait_flags(line, need, a.sync + kSyncStatusWord,
                              a.spin_limit, reinterpret_cast<int *>(gp + C + 4));
+      if constexpr (SEL) {
+        // weight of aggregate j: the decay over the segments after it up
+        // to this one, 2^(sum of their log2 gamma); wave 0 lane j takes
+        // segment j and sums the totals after it
+        static_assert(kMaxSegments <= kWave, "one segment per lane");
+        if (w == 0) {
+          const float tj =
+              lane < need ? a.seg_log[unit * a.nseg + lane] : 0.f;
+          float suf = tj;  // inclusive suffix sum over lanes j .. need - 1
+#pragma unroll
+          for (int o = 1; o < kMaxSegments; o <<= 1) {
+            const float y = __shfl_down(suf, o);
+            if (lane + o < kMaxSegments) suf += y;
+          }
+          if (lane < need) sw[lane] = __builtin_amdgcn_exp2f(suf - tj);
+        }
+        __syncthreads();
+      }
 #pragma unroll
       for (int i = 0; i < TW; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int64_t epos = CAUSAL ? start : a.n;
@@ -1029,6 +1177,7 @@ void la_fwd_kernel(FwdArgs a) {
           const int j = j0 + u;
           const int64_t end_j = min(a.n, (j + 1) * a.seg_len);
           const float wj = j >= need ? 0.f
+                           : SEL    ? sw[j]
                            : DECAY  ? pow_int(dk.g, dk.lg, epos - end_j)
                                     : 1.f;
 #pragma unroll
@@ -1052,8 +1201,8 @@ void la_fwd_kernel(FwdArgs a) {
             xs[tile_fb<F>(w, 0) * 64 + lane] = S[mj];
       }
 #pragma unroll
-      for (int b = 1; b < NB2; ++b) load2(b, rq[b], rk2[b], rv2[b]);
-      load2(NB2, rq[0], rk2[0], rv2[0]);
+      for (int b = 1; b < NB2; ++b) load2(b, rq[b], rk2[b], rv2[b], rl2[b]);
+      load2(NB2, rq[0], rk2[0], rv2[0], rl2[0]);
     } else {
       ring2_first();
     }
@@ -1068,7 +1217,7 @@ void la_fwd_kernel(FwdArgs a) {
   // adds a feature step after each staging.
   auto features2 = [&](int c) {
     if constexpr (PF) {
-      performer_features<F, T, true, CAUSAL, DECAY, true>(
+      performer_features<F, T, true, CAUSAL, WKEYS, true>(
           wf, sXq, sXk, pc0, pc0 + C, sQ, sK, sKw, gp, dk.b, rows_of(c), w, g,
           li);
       __syncthreads();
@@ -1085,8 +1234,8 @@ void la_fwd_kernel(FwdArgs a) {
   }
   publish_state<F>(S, sST, w, g, li);  // the entering state, set 0
   if (!(MULTI && a.nseg > 1)) {  // else staged during the exchange
-    stage2(0, rq[0], rk2[0], rv2[0]);
-    load2(NB2, rq[0], rk2[0], rv2[0]);
+    stage2(0, rq[0], rk2[0], rv2[0], rl2[0]);
+    load2(NB2, rq[0], rk2[0], rv2[0], rl2[0]);
   }
   __syncthreads();
   features2(0);
@@ -1098,7 +1247,8 @@ void la_fwd_kernel(FwdArgs a) {
       (w / STRIPS) % 2 == 0 ? w % STRIPS : STRIPS - 1 - w % STRIPS;
   const int jh = w / STRIPS;    // and its share of the column blocks
   const int t = 16 * tb + li;   // the output row this lane normalises
-  const float gt = CAUSAL ? gp[t + 1] : 1.f;
+  // the entering state's weight in row t (per-position decay: per chunk)
+  float gt = CAUSAL && !SEL ? gp[t + 1] : 1.f;
   // Causal mask of each P^T fragment pair kp: element e is key
   // s = 16 (2 kp + e / 4) + 4 g + e % 4, kept when s <= t.
   constexpr int NPK = (STRIPS + 1) / 2;
@@ -1115,7 +1265,7 @@ void la_fwd_kernel(FwdArgs a) {
   // Decay weights b g^(t-s) of this lane's P^T elements (zero for s > t),
   // computed once where the registers allow (one workgroup per CU), else
   // per chunk from the table.
-  constexpr bool PREW = DECAY && F::OCC == 1;
+  constexpr bool PREW = WKEYS && F::OCC == 1;
   float dw[PREW ? 4 * STRIPS : 1];
   if constexpr (PREW) {
 #pragma unroll
@@ -1145,6 +1295,15 @@ void la_fwd_kernel(FwdArgs a) {
       const T *sKwc = sKw + sc * F::SQ;
       const T *sVc = sV + sc * F::SV;
       const T *sSTc = CAUSAL ? sST + sc * F::SST : sST;
+      // per-position decay: this chunk's table, and row t's log2 decay
+      const float *tabc = stab + sc * F::TAB;
+      float Lt = 0.f;
+      if constexpr (SEL) {
+        if (CAUSAL) {
+          Lt = tabc[t];
+          gt = __builtin_amdgcn_exp2f(Lt);
+        }
+      }
 
       // ---- readout of strip tb: q' fragments, reused by every product ----
       Frag<T> qf[DFP / 32];
@@ -1174,7 +1333,21 @@ void la_fwd_kernel(FwdArgs a) {
           // acc[rr] = q'_t . k'_s with s = 16 sb + 4 g + rr; with decay the
           // weights b g^(t-s), zero above the diagonal, are applied here,
           // without it the causal mask is applied to the packed pairs
-          if (DECAY) {
+          if constexpr (SEL) {
+            // (1 - gamma_s) 2^(L_t - L_s) from this chunk's table
+            const f32x4 ls =
+                *reinterpret_cast<const f32x4 *>(tabc + 16 * sb + 4 * g);
+            const f32x4 bs =
+                *reinterpret_cast<const f32x4 *>(tabc + C + 16 * sb + 4 * g);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const int s = 16 * sb + 4 * g + rr;
+              // (above the diagonal the weight may overflow; the select
+              // drops it)
+              const float wgt = bs[rr] * __builtin_amdgcn_exp2f(Lt - ls[rr]);
+              acc[rr] = s <= t ? acc[rr] * wgt : 0.f;
+            }
+          } else if (DECAY) {
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
               const int s = 16 * sb + 4 * g + rr;
@@ -1274,8 +1447,8 @@ void la_fwd_kernel(FwdArgs a) {
         // ---- state update: S <- g^r S + (w.K')^T [V | 1] ----
         // (also after the last chunk, where the state only matters when it
         // is handed out, and on padding chunks, whose keys are zero)
-        const T *sKu = DECAY ? sKwc : sKc;
-        const float gr = DECAY ? gp[rows] : 1.f;
+        const T *sKu = WKEYS ? sKwc : sKc;
+        const float gr = WKEYS ? gp[rows] : SEL ? tabc[3 * C] : 1.f;
         const unsigned kmask = RES && c >= nch ? 0u : ~0u;
         if constexpr (SHARE) {
           // tile (w % NF, tile_jb(w, m)) uses column block vblock(m)
@@ -1286,6 +1459,12 @@ void la_fwd_kernel(FwdArgs a) {
             load_frag_tr44(af[kp], sKu, LQ, 32 * kp, 16 * tile_fb<F>(w, 0), g,
                            li);
             if (RES) frag_mask(af[kp], u32x4{kmask, kmask, kmask, kmask});
+            if constexpr (SEL)  // positions 32 kp + 4 g + e, then + 16
+              frag_scale(af[kp],
+                         *reinterpret_cast<const f32x4 *>(tabc + 2 * C +
+                                                          32 * kp + 4 * g),
+                         *reinterpret_cast<const f32x4 *>(
+                             tabc + 2 * C + 32 * kp + 16 + 4 * g));
           }
 #pragma unroll
           for (int m = 0; m < F::JPW; ++m) {
@@ -1295,13 +1474,13 @@ void la_fwd_kernel(FwdArgs a) {
             S[m] = acc;
           }
         } else {
-          state_update<F>(S, sKu, sVc, gr, w, g, li, kmask);
+          state_update<F>(S, sKu, sVc, gr, w, g, li, kmask, tabc + 2 * C);
         }
       }
       if (F::NBUF == 1) __syncthreads();  // the one tile set is free again
       // ---- chunk c + 1 into its set; its ring slot reloaded ----
-      stage2(c + 1, rq[bn], rk2[bn], rv2[bn]);
-      load2(c + 1 + NB2, rq[bn], rk2[bn], rv2[bn]);
+      stage2(c + 1, rq[bn], rk2[bn], rv2[bn], rl2[bn]);
+      load2(c + 1 + NB2, rq[bn], rk2[bn], rv2[bn], rl2[bn]);
       if (CAUSAL) publish_state<F>(S, sST + sn * F::SST, w, g, li);
       __syncthreads();
       features2(c + 1);

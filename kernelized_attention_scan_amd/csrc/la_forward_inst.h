@@ -7,18 +7,19 @@
 
 namespace la {
 
-// One (storage type, d, d_feat, decay, map) instance; MAP is the feature map
-// applied to q and k while staging them (kMapFeatures: none).
-template <typename T, int D, int DF, bool DECAY, int MAP>
+// One (storage type, d, d_feat, decay mode, map) instance; DK is the decay
+// mode of FwdShape, MAP the feature map applied to q and k while staging
+// them (kMapFeatures: none).
+template <typename T, int D, int DF, int DK, int MAP>
 struct FwdVariant {
-  using F = FwdShape<T, D, DF, DECAY, MAP>;
+  using F = FwdShape<T, D, DF, DK, MAP>;
 
   static const void *kernel(bool causal, bool multi) {
     if (causal)
       return multi
-          ? reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, true, true, DECAY, MAP>)
-          : reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, true, false, DECAY, MAP>);
-    return reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, false, true, DECAY, MAP>);
+          ? reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, true, true, DK, MAP>)
+          : reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, true, false, DK, MAP>);
+    return reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, false, true, DK, MAP>);
   }
 
   // Non-causal segmented forward as two launches: the aggregates, then the
@@ -26,16 +27,16 @@ struct FwdVariant {
   static const void *kernel_split(int split) {
     return split == 1
         ? reinterpret_cast<const void *>(
-              &la_fwd_kernel<T, D, DF, false, true, DECAY, MAP, false, 1>)
+              &la_fwd_kernel<T, D, DF, false, true, DK, MAP, false, 1>)
         : reinterpret_cast<const void *>(
-              &la_fwd_kernel<T, D, DF, false, true, DECAY, MAP, false, 2>);
+              &la_fwd_kernel<T, D, DF, false, true, DK, MAP, false, 2>);
   }
 
   // Resident-key instance (causal, several segments of at most KRES chunks).
   static const void *kernel_res() {
     if constexpr (F::KRES > 0)
       return reinterpret_cast<const void *>(
-          &la_fwd_kernel<T, D, DF, true, true, DECAY, MAP, true>);
+          &la_fwd_kernel<T, D, DF, true, true, DK, MAP, true>);
     return kernel(true, true);
   }
 
@@ -66,24 +67,24 @@ struct FwdVariant {
       // One segment: no exchange.  Several: segments are numbered in start
       // order, so a plain launch cannot deadlock.
       if (a.nseg == 1) {
-        hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, true, false, DECAY, MAP>),
+        hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, true, false, DK, MAP>),
                            grid, block, F::lds_bytes, s, a);
         return hipGetLastError();
       }
       if constexpr (F::KRES > 0) {
         if (a.seg_len <= static_cast<int64_t>(F::KRES) * F::C) {
           hipLaunchKernelGGL(
-              (la_fwd_kernel<T, D, DF, true, true, DECAY, MAP, true>), grid,
+              (la_fwd_kernel<T, D, DF, true, true, DK, MAP, true>), grid,
               block, F::lds_bytes, s, a);
           return hipGetLastError();
         }
       }
-      hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, true, true, DECAY, MAP>),
+      hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, true, true, DK, MAP>),
                          grid, block, F::lds_bytes, s, a);
       return hipGetLastError();
     }
     if (a.nseg == 1) {  // non-causal, one segment: no exchange executes
-      hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, false, true, DECAY, MAP>),
+      hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, false, true, DK, MAP>),
                          grid, block, F::lds_bytes, s, a);
       return hipGetLastError();
     }
@@ -92,12 +93,12 @@ struct FwdVariant {
     // readout launch after it on the same stream reads them; no workgroup
     // ever waits for another.
     hipLaunchKernelGGL(
-        (la_fwd_kernel<T, D, DF, false, true, DECAY, MAP, false, 1>), grid,
+        (la_fwd_kernel<T, D, DF, false, true, DK, MAP, false, 1>), grid,
         block, F::lds_bytes, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(
-        (la_fwd_kernel<T, D, DF, false, true, DECAY, MAP, false, 2>), grid,
+        (la_fwd_kernel<T, D, DF, false, true, DK, MAP, false, 2>), grid,
         block, F::lds_bytes, s, a);
     return hipGetLastError();
   }
@@ -108,19 +109,26 @@ struct FwdVariant {
 template <typename T, int D, int DF, bool PERF = false>
 struct FwdRunner {
   static constexpr int MAP0 = PERF ? kMapPerformer : kMapFeatures;
-  using P = FwdShape<T, D, DF, false, MAP0>;
-  using Q = FwdShape<T, D, DF, true, MAP0>;
+  using P = FwdShape<T, D, DF, 0, MAP0>;  // no decay
+  using Q = FwdShape<T, D, DF, 1, MAP0>;  // one decay per head
+  using R = FwdShape<T, D, DF, 2, MAP0>;  // a decay per position
 
   template <int MAP>
   static hipError_t run_map(const FwdArgs &a, int64_t units, int causal,
                             hipStream_t s) {
-    if (a.decay) {
-      if constexpr (Q::fits)
-        return FwdVariant<T, D, DF, true, MAP>::run(a, units, causal, s);
+    if (a.log_decay) {
+      if constexpr (R::fits)
+        return FwdVariant<T, D, DF, 2, MAP>::run(a, units, causal, s);
       else
         return hipErrorInvalidValue;
     }
-    return FwdVariant<T, D, DF, false, MAP>::run(a, units, causal, s);
+    if (a.decay) {
+      if constexpr (Q::fits)
+        return FwdVariant<T, D, DF, 1, MAP>::run(a, units, causal, s);
+      else
+        return hipErrorInvalidValue;
+    }
+    return FwdVariant<T, D, DF, 0, MAP>::run(a, units, causal, s);
   }
 
   // elu + 1 instances exist only for d_feat == d (the map keeps the width).
@@ -144,9 +152,10 @@ struct FwdRunner {
       return nullptr;
     } else {
       // the split is planned with P's chunk length; segments must hold whole
-      // chunks of the decayed variant too
+      // chunks of the decayed variants too
       static_assert(!Q::fits || P::C % Q::C == 0, "chunk lengths compatible");
-      static const FwdOps o = {P::C, P::SLOT, Q::fits, &run};
+      static_assert(!R::fits || P::C % R::C == 0, "chunk lengths compatible");
+      static const FwdOps o = {P::C, P::SLOT, Q::fits, R::fits, &run};
       return &o;
     }
   }

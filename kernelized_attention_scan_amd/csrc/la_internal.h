@@ -66,6 +66,11 @@ struct FwdArgs {
   float *mu_out;        // [units][d_feat][d] final state, or null
   float *nu_out;        // [units][d_feat] final normaliser (with mu_out)
   unsigned spin_limit;  // polls of an exchange wait before it gives up
+  // per-position decay: log gamma [units][n], or null; and (several
+  // segments) each segment's sum of log2 gamma [units][nseg] in the
+  // workspace
+  const float *log_decay;
+  float *seg_log;
 };
 
 // Launch set of one (storage type, d, d_feat) instance of the chunked forward.
@@ -73,6 +78,7 @@ struct FwdOps {
   int C;              // chunk rows
   int slot_floats;    // floats per fp32 state slot
   bool decay_ok;      // the decayed variant fits in LDS too
+  bool sel_ok;        // the per-position decay variant fits in LDS too
   // Enqueue the fused forward.
   hipError_t (*run)(const FwdArgs &args, int64_t units, int causal,
                     hipStream_t stream);
@@ -98,11 +104,14 @@ hipError_t launch_featmap_performer(const void *x, void *y, const float *omega,
 // Zero count floats (a fill kernel, so it can be captured in a graph).
 hipError_t launch_fill_zero(float *p, int64_t count, hipStream_t stream);
 
-// Decode step launcher (map: 0 identity, 1 elu1, 2 performer).
+// Decode step launcher (map: 0 identity, 1 elu1, 2 performer).  With
+// ld_layout < 0, decay is [H] or null; else it holds log gamma in that
+// la_decay_layout (the gated form).
 hipError_t launch_decode(float *mu, float *nu, const void *q, const void *k,
                          const void *v, void *out, int64_t units, int H, int d,
                          int d_feat, int map, const float *omega,
-                         const float *decay, int dtype, hipStream_t stream);
+                         const float *decay, int dtype, hipStream_t stream,
+                         int ld_layout = -1);
 bool decode_supported(int d, int d_feat);
 
 }  // namespace la

@@ -11,7 +11,11 @@ and fp32 ``randn`` / ``rand``:
 
 * prefill: Q, K, V (each [B, H, n, d], scaled by ``qk_std`` / ``v_std``),
   then omega [d, m] = randn / sqrt(d) (Performer only), then u [H] ~ U(0, 1)
-  with the per-head decay a = 1 - 10^(lo + (hi - lo) u) (decayed only);
+  with the per-head decay a = 1 - 10^(lo + (hi - lo) u) (decayed only), then
+  (gated only) u [H] ~ U(0, 1) with A_h = -10^(lo + (hi - lo) u) and z
+  [B, H, n] ~ N(0, 1) with step delta = softplus(z): the per-position log
+  decay is A_h * delta, the selective step of the Mamba section (a rate per
+  head times an input-dependent step);
 * decode: mu = |randn| * ctx, nu = |randn| * ctx, then q, k, v, then omega.
 
 Tensors with bf16 storage are rounded once, fp32 -> bf16 round-to-nearest-even,
@@ -43,6 +47,7 @@ class PrefillConfig:
     v_std: float = 1.0
     decay: Optional[tuple] = None    # (lo, hi): 1 - a = 10^U(lo, hi)
     causal: bool = True
+    gate: Optional[tuple] = None     # (lo, hi): log decay -10^U(lo,hi) * delta
 
     @property
     def d_feat(self) -> int:
@@ -86,10 +91,13 @@ DECAYED = PrefillConfig("decayed_elu1_B2H16n65536d128", B=2, H=16, n=65536,
                         d=128, decay=(-3.0, -1.0))
 PERFORMER = PrefillConfig("performer_B4H8n8192d64m256", B=4, H=8, n=8192, d=64,
                           mapk=MAP_PERFORMER, m=256, qk_std=0.5)
+# Input-dependent (per-position) decay at the decayed workload's sizes.
+GATED = PrefillConfig("gated_elu1_B2H16n65536d128", B=2, H=16, n=65536,
+                      d=128, gate=(-3.0, -1.0))
 DECODE = DecodeConfig("decode_S256H32d128_a0.99", S=256, H=32, d=128)
 
 PREFILL_CONFIGS = {c.name: c for c in (TINY_FP32, ELU1_CAUSAL, ELU1_NONCAUSAL,
-                                       DECAYED, PERFORMER)}
+                                       DECAYED, PERFORMER, GATED)}
 
 
 def _round(x: torch.Tensor, dtype: torch.dtype) -> torch.Tensor:
@@ -98,7 +106,7 @@ def _round(x: torch.Tensor, dtype: torch.dtype) -> torch.Tensor:
 
 def make_prefill(cfg: PrefillConfig, seed: int = 0) -> dict:
     """CPU tensors q, k, v (storage dtype), omega (fp32 or None),
-    decay (fp32 [H] or None)."""
+    decay (fp32 [H] or None), log_decay (fp32 [B, H, n] or None)."""
     g = torch.Generator("cpu").manual_seed(seed)
     shape = (cfg.B, cfg.H, cfg.n, cfg.d)
     q = torch.randn(shape, generator=g) * cfg.qk_std
@@ -112,8 +120,17 @@ def make_prefill(cfg: PrefillConfig, seed: int = 0) -> dict:
         lo, hi = cfg.decay
         u = torch.rand((cfg.H,), generator=g)
         decay = (1.0 - torch.pow(10.0, lo + (hi - lo) * u)).to(torch.float32)
+    log_decay = None
+    if cfg.gate is not None:
+        lo, hi = cfg.gate
+        u = torch.rand((cfg.H,), generator=g)
+        rate = -torch.pow(10.0, lo + (hi - lo) * u)
+        z = torch.randn((cfg.B, cfg.H, cfg.n), generator=g)
+        step = torch.nn.functional.softplus(z)
+        log_decay = (rate[None, :, None] * step).to(torch.float32).contiguous()
     return {"q": _round(q, cfg.dtype), "k": _round(k, cfg.dtype),
-            "v": _round(v, cfg.dtype), "omega": omega, "decay": decay}
+            "v": _round(v, cfg.dtype), "omega": omega, "decay": decay,
+            "log_decay": log_decay}
 
 
 def make_decode(cfg: DecodeConfig, seed: int = 0) -> dict:

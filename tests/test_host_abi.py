@@ -94,24 +94,25 @@ def test_workspace_bytes(lib):
     assert K.forward_workspace_bytes(1, 1, 64, 48, 48) == 0
     # segmented: a fixed synchronisation area (256 bytes + 512 lines of 128
     # bytes, one per unit a split can have) + units * nseg fp32 aggregates of
-    # d' x (d + 16) (mu and, in the extra 16-column block, nu)
+    # d' x (d + 16) (mu and, in the extra 16-column block, nu) + units * nseg
+    # floats (each segment's sum of log decay, for per-position decay)
     sync = 256 + 512 * 128
     ws = K.forward_workspace_bytes(4, 8, 4096, 64, 64)
     units = 32
     nseg = 8                     # 256 target groups (one per CU) / 32 units
     slot = 64 * (64 + 16)
     a256 = lambda x: (x + 255) // 256 * 256
-    assert ws == sync + a256(units * nseg * slot * 4)
+    assert ws == sync + a256(units * nseg * slot * 4) + a256(units * nseg * 4)
     # at most 16 segments per unit
     one = K.forward_workspace_bytes(1, 1, 1 << 16, 64, 64)
-    assert one == sync + a256(16 * slot * 4)
+    assert one == sync + a256(16 * slot * 4) + a256(16 * 4)
     # 512 units or more: one segment each, no workspace
     assert K.forward_workspace_bytes(8, 64, 1 << 16, 64, 64) == 0
     # bf16 Performer: the map is fused into the forward, so no q', k' in the
     # workspace; one workgroup per CU -> 256 target groups / 32 units = 8
     # segments, aggregates of d' x (d + 16) = 256 x 80
     wp = K.forward_workspace_bytes(4, 8, 8192, 64, 256, "performer")
-    assert wp == sync + a256(32 * 8 * 256 * 80 * 4)
+    assert wp == sync + a256(32 * 8 * 256 * 80 * 4) + a256(32 * 8 * 4)
     # fp32 storage keeps the unfused map: Q', K' (fp32, m wide) in it
     wf = K.forward_workspace_bytes(4, 8, 8192, 64, 256, "performer",
                                    dtype=__import__("torch").float32)
