@@ -96,6 +96,23 @@ def load_traffic(workload: str):
     return t.get("traffic_bytes")
 
 
+def settle(torch, fn, ms: float):
+    """Run fn(i) untimed until about `ms` milliseconds of GPU work have
+    passed, so the timed steps run at the clocks a sustained load holds
+    (the first tens of milliseconds of a fresh load run slower)."""
+    if ms <= 0:
+        return 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    i = 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+    return i
+
+
 def time_loop(torch, fn, steps: int, stream):
     """Average ms per call of fn(i) over `steps` calls, HIP events recorded on
     the stream the library launches on."""
@@ -217,6 +234,7 @@ def prefill_leg(torch, K, I, cfg, args, dev):
                   omega=s["omega"], decay=s["decay"], causal=cfg.causal,
                   out=outs[i % nsets], workspace=ws)
 
+    settled = settle(torch, step, args.settle_ms)
     for i in range(args.warmup):
         step(i)
     t_wall = time.perf_counter()
@@ -277,7 +295,7 @@ def prefill_leg(torch, K, I, cfg, args, dev):
                                      "forward_over_features": ms_w}
     return {"ms": ms, "t_wall": t_wall, "items": cfg.tokens,
             "unit": "tokens/s", "bytes": byts, "flops": flops,
-            "kern": kern, "nsets": nsets,
+            "kern": kern, "nsets": nsets, "settle_steps": settled,
             "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H,
                        "n": cfg.n, "d": cfg.d, "d_feat": cfg.d_feat,
                        "map": mapname, "decay": cfg.decay, "gate": cfg.gate,
@@ -298,6 +316,7 @@ def decode_leg(torch, K, I, cfg, args, dev):
         K.decode_step(s["mu"], s["nu"], s["q"], s["k"], s["v"], mapname,
                       omega=s["omega"], decay=s["decay"], out=out)
 
+    settled = settle(torch, step, args.settle_ms)
     for i in range(args.warmup):
         step(i)
     t_wall = time.perf_counter()
@@ -308,7 +327,7 @@ def decode_leg(torch, K, I, cfg, args, dev):
             "unit": "head-tokens/s", "bytes": byts, "flops": flops,
             "kern": {"kernel": "la_decode_kernel (state streamed once)",
                      "ms": ms, "bytes": byts, "flops": flops},
-            "nsets": 1,
+            "nsets": 1, "settle_steps": settled,
             "config": {"workload": cfg.name, "S": cfg.S, "H": cfg.H,
                        "d": cfg.d, "d_feat": cfg.d_feat, "map": mapname,
                        "a": cfg.a, "seed": args.seed}}
@@ -322,6 +341,9 @@ def main() -> int:
     ap.add_argument("--workload", default="decayed",
                     choices=sorted(workloads()))
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed steps for this long before the warmup "
+                         "steps, so clocks reach their sustained level")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB buffer three times (a kernel of "
@@ -395,6 +417,7 @@ def main() -> int:
                          kern["flops"] / (kern["ms"] * 1e-3) / 1e12
                          / BF16_PEAK_TFLOPS},
         "step_algorithmic_GBs": leg["bytes"] / (ms * 1e-3) / 1e9,
+        "settle": {"ms": args.settle_ms, "untimed_steps": leg["settle_steps"]},
         "wall_s_timed_region": leg["t_wall"],
     }
     if "other_launches_ms" in kern:

@@ -63,6 +63,8 @@ def _load():
                                              i32, i32, i32, P, P, i32, i32]
         lib.oracle_decode_gated.argtypes = [P, P, P, P, P, P, i32, i32, i32,
                                             i32, i32, i32, P, P, i32]
+        lib.oracle_backward.argtypes = [P, P, P, P, P, P, P, i32, i32, i64,
+                                        i32, i32, i32, i32, P, P]
         lib.oracle_num_threads.restype = i32
         _lib = lib
     return _lib
@@ -118,6 +120,28 @@ def forward(q, k, v, mapk: int = MAP_ELU1, omega=None, decay=None,
                            dqk, df, mapk, _ptr(om), _ptr(dec),
                            int(bool(causal)))
     return out
+
+
+def backward(q, k, v, dout, mapk: int = MAP_ELU1, omega=None, decay=None):
+    """Gradients (dq, dk, dv) of sum(out * dout) for the causal forward:
+    the adjoint of the literal recurrence, position by position (see
+    linattn_oracle.c)."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, n, d = v.shape
+    dqk = q.shape[-1]
+    assert q.shape == k.shape == (B, H, n, dqk) and dout.shape == v.shape
+    om = _f64(omega) if mapk == MAP_PERFORMER else None
+    df = feat_dim(dqk, mapk, om)
+    if mapk == MAP_ELU1:
+        assert dqk == d
+    dec = None if decay is None else _f64(decay).reshape(H)
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    _load().oracle_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq),
+                            _ptr(dk), _ptr(dv), B, H, n, d, dqk, df, mapk,
+                            _ptr(om), _ptr(dec))
+    return dq, dk, dv
 
 
 # Layouts of the log decay of the gated recurrence (see linattn_oracle.c).

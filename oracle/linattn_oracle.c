@@ -279,6 +279,130 @@ void oracle_decode_gated(double *mu, double *nu, const double *q,
   }
 }
 
+/* ------------------------------------------------------------------------
+ * Gradients (backward pass) of the causal forward.
+ *
+ * The pages give the forward only; training through it ("Linear attention
+ * research 2026" page, its closing section on parallel training of the
+ * recurrent forms) needs the derivatives of out with respect to q, k, v.
+ * They are written here as the adjoint of the literal recurrence above,
+ * step by step (reverse-mode differentiation through the positions), in
+ * two sweeps so that no state has to be stored per position:
+ *
+ *   forward sweep, j = 1 .. n (the recurrence of eqs 7-8 / 10-11):
+ *     num_j = q'_j mu_j,  den_j = q'_j . nu_j,  out_j = num_j / den_j
+ *     dnum_j = dout_j / den_j,  dden_j = -(dout_j . num_j) / den_j^2
+ *     dq'_j  = mu_j dnum_j + nu_j dden_j        (mu_j row f: sum over e)
+ *   backward sweep, j = n .. 1, adjoint states M (d' x d) and Z (d'):
+ *     M += q'_j dnum_j^T,  Z += q'_j dden_j     (the readout at j)
+ *     dk'_j = b (M v_j + Z),  dv_j = b M^T k'_j (the update at j)
+ *     M <- g M,  Z <- g Z                       (mu_j = g mu_{j-1} + ...)
+ *   with g = b = 1 (eqs 7-8) or g = a, b = 1 - a (eqs 10-11); then the
+ *   chain rule through the feature map, per element:
+ *     ELU1: dx = dx' (x > 0) or dx' e^x (x <= 0);  IDENTITY: dx = dx';
+ *     PERFORMER: dx_c = sum_r dx'_r phi_r (omega[c][r] - x_c).
+ * Layouts as oracle_forward; dout, dq, dk, dv have the shapes of out, q,
+ * k, v.  Causal only.
+ * ------------------------------------------------------------------------ */
+
+/* d phi(x) / d x applied to the feature gradient gf (d' values) of the row
+ * x (d values): gx[c] = sum_r gf[r] d phi_r / d x_c. */
+static void feature_row_grad(const double *x, const double *gf, double *gx,
+                             int d, int dfeat, int map, const double *omega) {
+  if (map == ORC_MAP_IDENTITY) {
+    for (int c = 0; c < d; ++c) gx[c] = gf[c];
+  } else if (map == ORC_MAP_ELU1) {
+    for (int c = 0; c < d; ++c) gx[c] = x[c] > 0.0 ? gf[c] : gf[c] * exp(x[c]);
+  } else {
+    double *phi = (double *)malloc(sizeof(double) * dfeat);
+    feature_row(x, phi, d, dfeat, map, omega);
+    double s = 0.0;   /* sum_r gf_r phi_r */
+    for (int r = 0; r < dfeat; ++r) s += gf[r] * phi[r];
+    for (int c = 0; c < d; ++c) {
+      double acc = 0.0;
+      for (int r = 0; r < dfeat; ++r)
+        acc += gf[r] * phi[r] * omega[c * (int64_t)dfeat + r];
+      gx[c] = acc - x[c] * s;
+    }
+    free(phi);
+  }
+}
+
+void oracle_backward(const double *q, const double *k, const double *v,
+                     const double *dout, double *dq, double *dk, double *dv,
+                     int B, int H, int64_t n, int d, int dqk, int dfeat,
+                     int map, const double *omega, const double *decay) {
+  const int64_t units = (int64_t)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t u = 0; u < units; ++u) {
+    const int h = (int)(u % H);
+    const double a = decay ? decay[h] : 1.0, b = decay ? 1.0 - a : 1.0;
+    const double *qu = q + u * n * dqk, *ku = k + u * n * dqk;
+    const double *vu = v + u * n * d, *gu = dout + u * n * d;
+    double *dqu = dq + u * n * dqk, *dku = dk + u * n * dqk;
+    double *dvu = dv + u * n * d;
+    double *mu = (double *)calloc((size_t)dfeat * d, sizeof(double));
+    double *nu = (double *)calloc((size_t)dfeat, sizeof(double));
+    double *qf = (double *)malloc(sizeof(double) * dfeat);
+    double *kf = (double *)malloc(sizeof(double) * dfeat);
+    double *gf = (double *)malloc(sizeof(double) * dfeat);
+    /* per position: dnum (d) and dden (1), kept for the backward sweep */
+    double *dnum = (double *)malloc(sizeof(double) * (size_t)n * d);
+    double *dden = (double *)malloc(sizeof(double) * (size_t)n);
+    /* forward sweep */
+    for (int64_t j = 0; j < n; ++j) {
+      feature_row(ku + j * dqk, kf, dqk, dfeat, map, omega);
+      state_update(mu, nu, kf, vu + j * d, d, dfeat, decay != NULL, a);
+      feature_row(qu + j * dqk, qf, dqk, dfeat, map, omega);
+      double den = 0.0;
+      for (int f = 0; f < dfeat; ++f) den += qf[f] * nu[f];
+      double dn = 0.0;   /* dout_j . num_j */
+      for (int e = 0; e < d; ++e) {
+        double num = 0.0;
+        for (int f = 0; f < dfeat; ++f) num += mu[f * d + e] * qf[f];
+        dnum[j * d + e] = gu[j * d + e] / den;
+        dn += gu[j * d + e] * num;
+      }
+      dden[j] = -dn / (den * den);
+      for (int f = 0; f < dfeat; ++f) {
+        double acc = nu[f] * dden[j];
+        for (int e = 0; e < d; ++e) acc += mu[f * d + e] * dnum[j * d + e];
+        gf[f] = acc;
+      }
+      feature_row_grad(qu + j * dqk, gf, dqu + j * dqk, dqk, dfeat, map,
+                       omega);
+    }
+    /* backward sweep: adjoint states M (reusing mu) and Z (reusing nu) */
+    memset(mu, 0, sizeof(double) * (size_t)dfeat * d);
+    memset(nu, 0, sizeof(double) * (size_t)dfeat);
+    for (int64_t j = n - 1; j >= 0; --j) {
+      feature_row(qu + j * dqk, qf, dqk, dfeat, map, omega);
+      for (int f = 0; f < dfeat; ++f) {
+        for (int e = 0; e < d; ++e) mu[f * d + e] += qf[f] * dnum[j * d + e];
+        nu[f] += qf[f] * dden[j];
+      }
+      feature_row(ku + j * dqk, kf, dqk, dfeat, map, omega);
+      for (int f = 0; f < dfeat; ++f) {
+        double acc = nu[f];
+        for (int e = 0; e < d; ++e) acc += mu[f * d + e] * vu[j * d + e];
+        gf[f] = b * acc;
+      }
+      feature_row_grad(ku + j * dqk, gf, dku + j * dqk, dqk, dfeat, map,
+                       omega);
+      for (int e = 0; e < d; ++e) {
+        double acc = 0.0;
+        for (int f = 0; f < dfeat; ++f) acc += mu[f * d + e] * kf[f];
+        dvu[j * d + e] = b * acc;
+      }
+      for (int f = 0; f < dfeat; ++f) {
+        for (int e = 0; e < d; ++e) mu[f * d + e] *= a;
+        nu[f] *= a;
+      }
+    }
+    free(mu); free(nu); free(qf); free(kf); free(gf); free(dnum); free(dden);
+  }
+}
+
 /* Number of OpenMP threads a parallel region here would use (1 without
  * OpenMP); reported beside the oracle's timing. */
 #ifdef _OPENMP

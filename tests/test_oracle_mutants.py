@@ -80,6 +80,19 @@ MUTANTS = {
         "    feature_row(q + u * dqk, qf, dqk, dfeat, map, omega);\n"
         "    readout(muu, nuu, qf, out + u * d, d, dfeat);\n"
         "    gated_update(muu, nuu, kf, v + u * d, d, dfeat, lam, mode, u, h, 0, 1);\n"),
+    # planted mistakes in the backward pass
+    "bwd_dden_sign": ("dden[j] = -dn / (den * den);",
+                      "dden[j] = dn / (den * den);"),
+    "bwd_dk_missing_input_weight": ("gf[f] = b * acc;", "gf[f] = acc;"),
+    "bwd_elu_chain_rule_dropped": (
+        "gx[c] = x[c] > 0.0 ? gf[c] : gf[c] * exp(x[c]);", "gx[c] = gf[c];"),
+    "bwd_adjoint_not_decayed": ("for (int e = 0; e < d; ++e) mu[f * d + e] *= a;",
+                                ";"),
+    "bwd_dv_state_transposed": (
+        "for (int f = 0; f < dfeat; ++f) acc += mu[f * d + e] * kf[f];",
+        "for (int f = 0; f < dfeat; ++f) acc += mu[e * dfeat + f] * kf[f];"),
+    "bwd_performer_norm_term_dropped": ("gx[c] = acc - x[c] * s;",
+                                        "gx[c] = acc;"),
 }
 
 
@@ -101,6 +114,8 @@ def _compile(src_text, tmp_path, tag):
                                          i32, i32, P, P, i32, i32]
     lib.oracle_decode_gated.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32,
                                         i32, i32, P, P, i32]
+    lib.oracle_backward.argtypes = [P, P, P, P, P, P, P, i32, i32, i64, i32,
+                                    i32, i32, i32, P, P]
     lib.oracle_num_threads.restype = i32
     return lib
 
@@ -231,8 +246,46 @@ def chk_gated_decode():
     return out.item() == 6.0
 
 
+def chk_backward():
+    import torch
+    rng = np.random.default_rng(9)
+    B, H, n, d, m = 1, 2, 21, 4, 5   # d != m: a transposed state is caught
+    for mapk in (oracle.MAP_ELU1, oracle.MAP_PERFORMER):
+        for dec in (None, np.array([0.8, 0.6])):
+            q = rng.standard_normal((B, H, n, d)) * 0.7
+            k = rng.standard_normal((B, H, n, d)) * 0.7
+            v = rng.standard_normal((B, H, n, d))
+            g = rng.standard_normal((B, H, n, d))
+            om = rng.standard_normal((d, m)) / math.sqrt(d)
+            tq, tk, tv = (torch.tensor(x, requires_grad=True)
+                          for x in (q, k, v))
+            if mapk == oracle.MAP_ELU1:
+                qf = torch.nn.functional.elu(tq) + 1.0
+                kf = torch.nn.functional.elu(tk) + 1.0
+            else:
+                tom = torch.tensor(om)
+                qf = torch.exp(tq @ tom - 0.5 * (tq * tq).sum(-1, keepdim=True))
+                kf = torch.exp(tk @ tom - 0.5 * (tk * tk).sum(-1, keepdim=True))
+                qf, kf = qf / math.sqrt(m), kf / math.sqrt(m)
+            i = torch.arange(n)[:, None]
+            j = torch.arange(n)[None, :]
+            W = (j <= i).double()
+            if dec is not None:
+                a = torch.tensor(dec)[:, None, None]
+                W = W * (1 - a) * a ** (i - j).clamp(min=0).double()
+            A = (qf @ kf.transpose(-1, -2)) * W
+            out = (A @ tv) / A.sum(-1, keepdim=True)
+            (out * torch.tensor(g)).sum().backward()
+            got = oracle.backward(q, k, v, g, mapk, om, dec)
+            for x, t in zip(got, (tq, tk, tv)):
+                if not _close(x, t.grad.numpy(), 1e-10):
+                    return False
+    return True
+
+
 CHECKS = [chk_bruteforce, chk_hand_examples, chk_featmaps, chk_decode,
-          chk_constant_v, chk_gated_bruteforce, chk_gated_decode]
+          chk_constant_v, chk_gated_bruteforce, chk_gated_decode,
+          chk_backward]
 
 
 def _run_checks(lib, monkeypatch):
