@@ -182,6 +182,44 @@ la_status la_forward_noalloc(const void *q, const void *k, const void *v,
                              void *stream);
 
 /*
+ * la_forward_train -- the causal la_forward that also writes each row's
+ * denominator den_j = q'_j . nu_j, as the backward pass needs it ("2.2
+ * Linear Attention" eq 9, causal form: out_j = q'_j mu_j / den_j).
+ *   All arguments as la_forward (causal), plus
+ *   den : device fp32 [B][H][n], written; LA_ERR_INVALID_ARG if NULL.
+ */
+la_status la_forward_train(const void *q, const void *k, const void *v,
+                           void *out, float *den, int B, int H, int64_t n,
+                           int d, int d_feat, la_map map, const float *omega,
+                           const float *decay, la_dtype dtype, void *workspace,
+                           void *stream);
+
+/*
+ * la_backward -- gradients of sum(out * dout) with respect to q, k and v for
+ * the causal forward (eqs 7-11 with the feature map), for training through
+ * it ("Linear attention research 2026" page, closing section: parallel
+ * training of the recurrent forms).  With G_j = [dout_j / den_j |
+ * -(dout_j . out_j) / den_j] and w_ij the weights of eqs 7-8 / 10-11:
+ *   dq'_i = sum_{j<=i} w_ij (G_i . [v_j|1]) k'_j,
+ *   dk'_j = sum_{i>=j} w_ij (G_i . [v_j|1]) q'_i,
+ *   dv_j  = sum_{i>=j} w_ij (q'_i . k'_j) dout_i / den_i,
+ * then through the feature map (elu + 1: times 1 for x > 0, e^x else).
+ *   q, k, v, out, dout: device, dtype, [B][H][n][d] (out and den as
+ *                       la_forward_train wrote them for these q, k, v)
+ *   den   : device fp32 [B][H][n]
+ *   dq, dk, dv: device, dtype, [B][H][n][d], written (may not alias inputs)
+ *   map   : LA_MAP_ELU1 or LA_MAP_IDENTITY (LA_MAP_PERFORMER:
+ *           LA_ERR_UNSUPPORTED); omega is ignored
+ *   decay : device fp32 [H] or NULL, as la_forward
+ *   Supported: d == d_feat in {16, 32, 64, 128}.  No workspace.
+ */
+la_status la_backward(const void *q, const void *k, const void *v,
+                      const void *out, const float *den, const void *dout,
+                      void *dq, void *dk, void *dv, int B, int H, int64_t n,
+                      int d, int d_feat, la_map map, const float *omega,
+                      const float *decay, la_dtype dtype, void *stream);
+
+/*
  * la_forward_gated -- la_forward / la_forward_state with a decay that
  * varies by position: gamma_j = exp(lam_j) replaces a in eqs 10-11 at
  * position j,

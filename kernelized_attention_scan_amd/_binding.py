@@ -29,7 +29,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
 
 # Exported symbols, in the order include/linattn.h declares them.
 SYMBOLS = ("la_featmap", "la_forward_workspace_bytes", "la_forward",
-           "la_forward_state", "la_forward_gated", "la_forward_noalloc",
+           "la_forward_state", "la_forward_train", "la_backward",
+           "la_forward_gated", "la_forward_noalloc",
            "la_decode_step", "la_decode_step_gated", "la_workspace_check",
            "la_set_exchange_spin_limit", "la_status_str", "la_last_error")
 
@@ -73,6 +74,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                          i32, i32, vp, vp, i32, i32, vp, vp,
                                          vp, vp]
         lib.la_forward_state.restype = i32
+        lib.la_forward_train.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64,
+                                         i32, i32, i32, vp, vp, i32, vp, vp]
+        lib.la_forward_train.restype = i32
+        lib.la_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32,
+                                    i32, i64, i32, i32, i32, vp, vp, i32, vp]
+        lib.la_backward.restype = i32
         lib.la_forward_gated.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32,
                                          i32, i32, vp, vp, i32, i32, i32, vp,
                                          vp, vp, vp]
@@ -530,3 +537,91 @@ def decode_step_gated(mu: torch.Tensor, nu: torch.Tensor, q: torch.Tensor,
                                   _dtype_code(v.dtype), _stream(v.device))
     _check(st, "la_decode_step_gated")
     return out
+
+
+def forward_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  feature_map="elu1", decay: Optional[torch.Tensor] = None,
+                  out: Optional[torch.Tensor] = None,
+                  den: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None):
+    """The causal forward for training (la_forward_train): returns (out,
+    den), den [B,H,n] fp32 being each row's denominator, which backward()
+    takes."""
+    lib = load_library()
+    if q.dim() != 4 or v.dim() != 4 or q.shape != k.shape:
+        raise ValueError("q, k must be [B,H,n,d_qk] and v [B,H,n,d]")
+    B, H, n, d = v.shape
+    if q.shape[:3] != v.shape[:3]:
+        raise ValueError("q, k, v disagree on B, H, n")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    dt = _dtype_code(v.dtype)
+    mapk = _map_code(feature_map)
+    if mapk == MAP_PERFORMER:
+        raise ValueError("forward_train: elu1 or identity features")
+    if mapk != MAP_IDENTITY and q.shape[-1] != d:
+        raise ValueError("q, k must have width d for elu1")
+    d_feat = q.shape[-1]
+    _check_decay(decay, H)
+    if out is not None:
+        _check_out(out, v.shape, v.dtype)
+    if den is not None and (den.dtype != torch.float32 or
+                            tuple(den.shape) != (B, H, n)):
+        raise ValueError("den must be float32 [B, H, n]")
+    _on_gpu(v, (q, "q"), (k, "k"), (v, "v"), (out, "out"), (den, "den"),
+            (decay, "decay"), (workspace, "workspace"))
+    if out is None:
+        out = torch.empty_like(v)
+    if den is None:
+        den = torch.empty((B, H, n), dtype=torch.float32, device=v.device)
+    need = lib.la_forward_workspace_bytes(B, H, n, d, d_feat, mapk, dt, 1)
+    if need and workspace is None:
+        workspace = _workspace(need, v.device)
+    if need and workspace.numel() < need:
+        raise ValueError("workspace too small")
+    st = lib.la_forward_train(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(den),
+                              B, H, n, d, d_feat, mapk, None, _ptr(decay), dt,
+                              _ptr(workspace) if need else None,
+                              _stream(v.device))
+    _check(st, "la_forward_train")
+    return out, den
+
+
+def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+             out: torch.Tensor, den: torch.Tensor, dout: torch.Tensor,
+             feature_map="elu1", decay: Optional[torch.Tensor] = None,
+             dq: Optional[torch.Tensor] = None,
+             dk: Optional[torch.Tensor] = None,
+             dv: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv) of sum(out * dout) for the causal forward
+    (la_backward); out and den as forward_train() returned them."""
+    lib = load_library()
+    if q.dim() != 4 or v.dim() != 4 or q.shape != k.shape:
+        raise ValueError("q, k must be [B,H,n,d] and v [B,H,n,d]")
+    B, H, n, d = v.shape
+    if q.shape != v.shape:
+        raise ValueError("la_backward needs q, k, v of one shape (d' = d)")
+    for t, nm in ((out, "out"), (dout, "dout")):
+        if t.shape != v.shape or t.dtype != v.dtype:
+            raise ValueError(f"{nm} must match v in shape and dtype")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    if den.dtype != torch.float32 or tuple(den.shape) != (B, H, n):
+        raise ValueError("den must be float32 [B, H, n]")
+    dt = _dtype_code(v.dtype)
+    mapk = _map_code(feature_map)
+    _check_decay(decay, H)
+    for t, nm in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        if t is not None:
+            _check_out(t, v.shape, v.dtype)
+    _on_gpu(v, (q, "q"), (k, "k"), (v, "v"), (out, "out"), (den, "den"),
+            (dout, "dout"), (decay, "decay"), (dq, "dq"), (dk, "dk"),
+            (dv, "dv"))
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    st = lib.la_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(den),
+                         _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, H, n, d,
+                         d, mapk, None, _ptr(decay), dt, _stream(v.device))
+    _check(st, "la_backward")
+    return dq, dk, dv

@@ -184,7 +184,8 @@ static la_status forward_impl(const void *q, const void *k, const void *v, void 
                        const float *omega, const float *decay, int causal,
                        int dtype, void *workspace, float *mu_out, float *nu_out,
                        void *stream, size_t workspace_cap = 0,
-                       const float *log_decay = nullptr) {
+                       const float *log_decay = nullptr,
+                       float *den_out = nullptr) {
   try {
     FwdPlan p;
     const int dkind = log_decay ? 2 : decay ? 1 : 0;
@@ -240,6 +241,7 @@ static la_status forward_impl(const void *q, const void *k, const void *v, void 
                                     ws + p.sync_bytes + p.agg_bytes)
                               : nullptr;
     a.log_decay = log_decay;
+    a.den_out = den_out;
     a.H = H;
     a.n = n;
     a.seg_len = p.seg_len;
@@ -452,6 +454,64 @@ la_status la_workspace_check(void *workspace, void *stream) {
 void la_set_exchange_spin_limit(unsigned spins) {
   g_spin_limit.store(spins ? spins : la::kDefaultSpinLimit,
                      std::memory_order_relaxed);
+}
+
+la_status la_forward_train(const void *q, const void *k, const void *v,
+                           void *out, float *den, int B, int H, int64_t n,
+                           int d, int d_feat, la_map map, const float *omega,
+                           const float *decay, la_dtype dtype, void *workspace,
+                           void *stream) {
+  if (!den && static_cast<int64_t>(B) * H > 0 && n > 0)
+    return fail(LA_ERR_INVALID_ARG, "null den");
+  return forward_impl(q, k, v, out, B, H, n, d, d_feat, map, omega, decay, 1,
+                      dtype, workspace, nullptr, nullptr, stream, 0, nullptr,
+                      den);
+}
+
+la_status la_backward(const void *q, const void *k, const void *v,
+                      const void *out, const float *den, const void *dout,
+                      void *dq, void *dk, void *dv, int B, int H, int64_t n,
+                      int d, int d_feat, la_map map, const float *omega,
+                      const float *decay, la_dtype dtype, void *stream) {
+  try {
+    (void)omega;
+    if (B < 0 || H < 0 || n < 0)
+      return fail(LA_ERR_INVALID_ARG, "negative size");
+    if (!valid_map(map)) return fail(LA_ERR_INVALID_ARG, "unknown map %d", map);
+    if (!valid_dtype(dtype))
+      return fail(LA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    if (d <= 0 || d_feat <= 0)
+      return fail(LA_ERR_INVALID_ARG, "non-positive d=%d d_feat=%d", d, d_feat);
+    if (map == LA_MAP_ELU1 && d_feat != d)
+      return fail(LA_ERR_INVALID_ARG, "ELU1 needs d_feat == d");
+    if (map == LA_MAP_PERFORMER)
+      return fail(LA_ERR_UNSUPPORTED,
+                  "la_backward: the Performer map's gradient is not built");
+    if (!la::backward_supported(d, d_feat))
+      return fail(LA_ERR_UNSUPPORTED,
+                  "la_backward: d = d_feat in {16, 32, 64, 128} is built "
+                  "(got d=%d d_feat=%d)", d, d_feat);
+    const int64_t units = static_cast<int64_t>(B) * H;
+    if (units == 0 || n == 0) return ok();
+    if (units * n > (int64_t{1} << 46) || units > (int64_t{1} << 26))
+      return fail(LA_ERR_UNSUPPORTED, "sizes too large");
+    if (!q || !k || !v || !out || !den || !dout || !dq || !dk || !dv)
+      return fail(LA_ERR_INVALID_ARG, "null pointer argument");
+    la::BwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.den = den;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    a.decay = decay;
+    a.H = H;
+    a.n = n;
+    a.dqk = d;
+    a.elu1 = map == LA_MAP_ELU1;
+    const hipError_t e = la::launch_backward(a, units, d, dtype,
+                                             static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "la_backward launch");
+    return ok();
+  } catch (...) {
+    return fail(LA_ERR_HIP, "unexpected exception in la_backward");
+  }
 }
 
 la_status la_forward_gated(const void *q, const void *k, const void *v,

@@ -1,0 +1,539 @@
+// Gradients of the causal forward (training), on gfx950 matrix cores.
+//
+// The forward reads out out_t = num_t / den_t with num_t = q'_t mu_t and
+// den_t = q'_t . nu_t ("2.2 Linear Attention" eqs 7-11).  For a gradient
+// dout of the outputs, let
+//   G_t  = [dout_t / den_t | -(dout_t . out_t) / den_t]   (d + 1 values)
+//   V+_s = [v_s | 1],   w_ts = b g^(t-s) for s <= t  (g = b = 1 without decay)
+// (G's last value is carried as a bf16 pair hi + lo, matched by two ones in
+// V+, and formed from the rounded dout / den, so that G_t . V+_s cancels
+// to fp32 precision where the exact sum does: for one position, out = v and
+// the gradients of q and k are exactly zero.)
+// Differentiating the recurrence (the oracle's adjoint, regrouped) gives
+// three unnormalised causal linear attentions:
+//   dq'_t = sum_{s<=t} w_ts (G_t . V+_s) k'_s    query G,  key V+, value K'
+//   dk'_s = sum_{t>=s} w_ts (G_t . V+_s) q'_t    query V+, key G,  value Q'
+//   dv_s  = sum_{t>=s} w_ts (q'_t . k'_s) G_t    query K', key Q', value G
+// the last two running backwards through the sequence; then dq = phi'(q)
+// dq' and dk = phi'(k) dk' (elu + 1: 1 for x > 0, e^x else).
+//
+// Each of these is computed chunk by chunk exactly like the forward's
+// numerator (C = 64 rows, local t, s, state S before the chunk):
+//   out_t = sum_{s<=t} b g^(t-s) (X_t . Y_s) Z_s + g^(t+1) X_t S
+//   S    <- g^r S + sum_s b g^(r-1-s) Y_s^T Z_s            (r valid rows)
+// with (X, Y, Z) the (query, key, value) above; the reverse-order roles
+// take the chunks from the last to the first and the rows of each chunk
+// in reverse, so the same formulas read the sequence backwards.
+//
+// Parallelism: one 256-thread workgroup (4 waves) per (unit, role, block
+// of 16 output columns), each walking its unit's whole sequence.  The
+// roles and blocks of a unit are independent, so no segment exchange is
+// needed: B H (2 d'/16 + d/16) workgroups (768 at B H = 32, d = 128).
+// Every workgroup recomputes the scores of its role (the price of
+// independence); the raw rows it shares with the unit's other workgroups
+// come mostly from L2.
+#include "la_device.h"
+#include "la_internal.h"
+
+namespace la {
+
+namespace {
+
+constexpr int kBThreads = 256;
+constexpr int kBWaves = kBThreads / kWave;  // one 16-row output strip each
+constexpr int kBC = 64;                     // chunk rows
+constexpr int kRoleDQ = 0, kRoleDK = 1, kRoleDV = 2;
+
+// LDS row stride (elements) for w elements: 16 mod 32 for bf16 (conflict-
+// free transposing reads), +4 for fp32.
+template <typename T>
+constexpr int bstride(int w) {
+  return sizeof(T) == 2 ? (w % 32 == 16 ? w : w + 16) : w + 4;
+}
+
+template <typename T, int D, int ROLE, bool DECAY>
+struct BShape {
+  // X and Y are G and V+ (d + 2 wide: the last value of G as a pair,
+  // padded to a multiple of 32) for the dq and dk roles, and K', Q' (d
+  // wide, at least 32) for dv
+  static constexpr bool GV = ROLE != kRoleDV;
+  static constexpr int KX = GV ? (D + 2 + 31) / 32 * 32 : (D < 32 ? 32 : D);
+  static constexpr int LX = bstride<T>(KX);
+  static constexpr int LZ = bstride<T>(16);
+  static constexpr int NT = KX / 16;                 // 16 x 16 state tiles
+  static constexpr int TPW = (NT + kBWaves - 1) / kBWaves;
+  static constexpr int SX = kBC * LX, SZ = kBC * LZ, SST = 16 * LX;
+  static constexpr size_t lds_bytes =
+      sizeof(T) * (SX * (DECAY ? 3 : 2) + SZ * 2 + SST) +
+      sizeof(float) * (kBC + 4);
+};
+
+// 16-byte pieces of a [C][W] row-major slab (consecutive threads take
+// consecutive pieces) of rows row0 .. row0 + rows - 1 of a matrix whose
+// rows are LD elements long, starting at column col0; rows past `rows`
+// read zero (the buffer resource ends there).
+template <typename T, int W, int LD>
+struct BSlab {
+  static constexpr int VEC = 16 / sizeof(T);
+  static constexpr int PPR = W / VEC;
+  static constexpr int PIECES = kBC * PPR;
+  static constexpr int PER = (PIECES + kBThreads - 1) / kBThreads;
+  static constexpr bool EXACT = PIECES % kBThreads == 0;
+  u32x4 v[PER];
+  __device__ __forceinline__ void load(const T *base, int64_t row0, int rows,
+                                       int col0, int tid) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(
+        base + row0 * LD, static_cast<unsigned>(rows) * LD * sizeof(T));
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int p = tid + kBThreads * i;
+      if (EXACT || p < PIECES)
+        v[i] = buffer_load16(
+            r, static_cast<unsigned>(((p / PPR) * LD + col0 +
+                                      (p % PPR) * VEC) * sizeof(T)));
+    }
+  }
+};
+
+// The chunk's denominators, one per row: lane l of every wave holds row
+// l's (each wave reads them through a lane shuffle).
+struct BDen {
+  float v;
+  __device__ __forceinline__ void load(const float *base, int64_t row0,
+                                       int rows, int lane) {
+    static_assert(kBC == kWave, "one row per lane");
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc(base + row0, static_cast<unsigned>(rows) * 4u);
+    v = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(r, 4u * lane, 0, 0));
+  }
+};
+
+// Sum over aligned groups of N consecutive lanes (N a power of two <= 64).
+template <int N>
+__device__ __forceinline__ float sum_group(float x) {
+#pragma unroll
+  for (int o = 1; o < N; o <<= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// The values of one 16-byte piece as floats (8 bf16 or 4 fp32).
+template <typename T>
+__device__ __forceinline__ void piece_to_f32(const u32x4 &x,
+                                             float (&f)[16 / sizeof(T)]) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_lo(x[i]);
+      f[2 * i + 1] = bf16_hi(x[i]);
+    }
+  } else {
+    const f32x4 y = __builtin_bit_cast(f32x4, x);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = y[i];
+  }
+}
+template <typename T>
+__device__ __forceinline__ u32x4 f32_to_piece(const float (&f)[16 / sizeof(T)]) {
+  if constexpr (sizeof(T) == 2) {
+    return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                 pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
+  } else {
+    const f32x4 y = {f[0], f[1], f[2], f[3]};
+    return __builtin_bit_cast(u32x4, y);
+  }
+}
+
+__device__ __forceinline__ float phi(float x, bool elu) {
+  return elu ? elu_plus_one(x) : x;
+}
+__device__ __forceinline__ float dphi(float x, bool elu) {  // d phi / d x
+  return elu ? (x > 0.f ? 1.f : expf(x)) : 1.f;
+}
+
+template <typename T, int D, int ROLE, bool DECAY, bool ELU>
+__global__ __launch_bounds__(kBThreads) void la_bwd_kernel(BwdArgs a) {
+  using F = BShape<T, D, ROLE, DECAY>;
+  constexpr int C = kBC, KX = F::KX, LX = F::LX, LZ = F::LZ;
+  constexpr bool GV = F::GV, REV = ROLE != kRoleDQ;
+  constexpr int VEC = 16 / sizeof(T);
+  extern __shared__ __align__(16) unsigned char smem[];
+  T *sX = reinterpret_cast<T *>(smem);           // queries X
+  T *sY = sX + F::SX;                            // keys Y
+  T *sYw = DECAY ? sY + F::SX : sY;              // w_s Y_s (state update)
+  T *sZ = sY + F::SX * (DECAY ? 2 : 1);          // values Z (16 columns)
+  T *sP = sZ + F::SZ;                            // raw x for phi' (16 cols)
+  T *sST = sP + F::SZ;                           // S^T copy
+  float *gp = reinterpret_cast<float *>(sST + F::SST);  // g^0 .. g^C
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, li = lane & 15;
+  const int nblk = ROLE == kRoleDV ? D / 16 : a.dqk / 16;
+  // Workgroups are dispatched to the 8 XCDs round-robin by block index; the
+  // blocks of one unit are given indices of one XCD (when the grid divides
+  // evenly), so the rows they all read come from that XCD's L2.
+  int64_t bid = blockIdx.x;
+  if (gridDim.x % 8 == 0)
+    bid = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
+  const int64_t unit = bid / nblk;
+  const int blk = static_cast<int>(bid % nblk);
+  const int col0 = 16 * blk;
+  const int h = static_cast<int>(unit % a.H);
+  const float gdec = DECAY ? a.decay[h] : 1.f, bdec = DECAY ? 1.f - gdec : 1.f;
+  const float lg = log2f(gdec);
+  for (int i = tid; i <= C; i += kBThreads) gp[i] = pow_int(gdec, lg, i);
+
+  const int64_t n = a.n;
+  const T *qb = static_cast<const T *>(a.q) + unit * n * D;
+  const T *kb = static_cast<const T *>(a.k) + unit * n * D;
+  const T *vb = static_cast<const T *>(a.v) + unit * n * D;
+  const T *ob = static_cast<const T *>(a.out) + unit * n * D;
+  const T *gb = static_cast<const T *>(a.dout) + unit * n * D;
+  const float *db = a.den + unit * n;
+  T *res = static_cast<T *>(ROLE == kRoleDQ ? a.dq
+                            : ROLE == kRoleDK ? a.dk
+                                              : a.dv) +
+           unit * n * D;
+
+  // Constant parts: the padding columns of X and Y past the data (zero for
+  // every row; the V+ column d is written per chunk).
+  constexpr int XW = GV ? D + 2 : D;  // written columns of X, Y
+  for (int i = tid; i < C * (KX - XW); i += kBThreads) {
+    const int row = i / (KX - XW), col = XW + i % (KX - XW);
+    sX[row * LX + col] = from_f32<T>(0.f);
+    sY[row * LX + col] = from_f32<T>(0.f);
+    if (DECAY) sYw[row * LX + col] = from_f32<T>(0.f);
+  }
+
+  const int nch = static_cast<int>((n + C - 1) / C);
+  // Physical chunk of processing step c, its first row and valid rows.
+  auto chunk_of = [&](int c) { return REV ? nch - 1 - c : c; };
+  auto rows_of = [&](int c) -> int {
+    if (c >= nch) return 0;
+    const int64_t r0 = static_cast<int64_t>(chunk_of(c)) * C;
+    return static_cast<int>(min<int64_t>(C, n - r0));
+  };
+  auto row0_of = [&](int c) -> int64_t {
+    return c >= nch ? 0 : static_cast<int64_t>(chunk_of(c)) * C;
+  };
+
+  // Register ring (one chunk ahead).  GV roles: dout, out, v full rows;
+  // q and k blocks.  dv: k, q full rows; the dout block.
+  BSlab<T, D, D> r1, r2, r3;   // GV: dout, out, v   dv: k, q, (unused)
+  BSlab<T, 16, D> rb1, rb2;    // GV: q block, k block   dv: dout block
+  BDen rd;
+  auto load = [&](int c) {
+    const int64_t r0 = row0_of(c);
+    const int rows = rows_of(c);
+    if constexpr (GV) {
+      r1.load(gb, r0, rows, 0, tid);
+      r2.load(ob, r0, rows, 0, tid);
+      r3.load(vb, r0, rows, 0, tid);
+      rb1.load(qb, r0, rows, col0, tid);
+      rb2.load(kb, r0, rows, col0, tid);
+    } else {
+      r1.load(kb, r0, rows, 0, tid);
+      r2.load(qb, r0, rows, 0, tid);
+      rb1.load(gb, r0, rows, col0, tid);
+    }
+    rd.load(db, r0, rows, lane);
+  };
+
+  // Staging of processing step c (rows in processing order: raw row r of a
+  // reversed chunk goes to tile row rows - 1 - r; rows past the end are 0).
+  auto stage = [&](int c) {
+    const int rows = rows_of(c);
+    auto trow = [&](int r) { return REV && r < rows ? rows - 1 - r : r; };
+    if constexpr (GV) {
+      // G = [dout / den | -(dout . out) / den]; V+ = [v | 1]
+      T *sG = ROLE == kRoleDQ ? sX : sY;
+      T *sV = ROLE == kRoleDQ ? sY : sX;
+      using S = BSlab<T, D, D>;
+#pragma unroll
+      for (int i = 0; i < S::PER; ++i) {
+        const int p = tid + kBThreads * i;
+        const bool mine = S::EXACT || p < S::PIECES;
+        const int r = p / S::PPR, cc = (p % S::PPR) * VEC;
+        const float den = __shfl(rd.v, r & 63);  // row r's den, from lane r
+        const bool valid = r < rows;
+        const float rden = valid ? 1.f / den : 0.f;
+        float go[VEC], oo[VEC], vv[VEC];
+        piece_to_f32<T>(r1.v[i], go);
+        piece_to_f32<T>(r2.v[i], oo);
+        piece_to_f32<T>(r3.v[i], vv);
+        float dot = 0.f;   // g . out with g as the operand holds it
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          go[e] = round_to<T>(go[e] * rden);
+          dot += go[e] * oo[e];
+          if (!valid) vv[e] = 0.f;
+        }
+        dot = sum_group<S::PPR>(dot);
+        if (mine) {
+          const int t = trow(r);
+          *reinterpret_cast<u32x4 *>(sG + t * LX + cc) = f32_to_piece<T>(go);
+          const u32x4 pv = f32_to_piece<T>(vv);
+          *reinterpret_cast<u32x4 *>(sV + t * LX + cc) = pv;
+          if (DECAY && ROLE == kRoleDQ) {  // Y = V+: weighted copy
+            float wv[VEC];
+            const float ws = valid ? bdec * gp[rows - 1 - t] : 0.f;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) wv[e] = vv[e] * ws;
+            *reinterpret_cast<u32x4 *>(sYw + t * LX + cc) = f32_to_piece<T>(wv);
+          }
+          if (cc == 0) {
+            // h = -g . out as hi + lo (columns d, d + 1); V+ has 1 in both
+            const float hh = -dot;
+            const float hi = round_to<T>(hh), lo = hh - hi;
+            const float one = valid ? 1.f : 0.f;
+            sG[t * LX + D] = from_f32<T>(hi);
+            sG[t * LX + D + 1] = from_f32<T>(lo);
+            sV[t * LX + D] = from_f32<T>(one);
+            sV[t * LX + D + 1] = from_f32<T>(one);
+            if (DECAY) {
+              const float ws = valid ? bdec * gp[rows - 1 - t] : 0.f;
+              sYw[t * LX + D] = from_f32<T>(ROLE == kRoleDQ ? ws : hi * ws);
+              sYw[t * LX + D + 1] = from_f32<T>(ROLE == kRoleDQ ? ws : lo * ws);
+            }
+          }
+          if (DECAY && ROLE == kRoleDK) {  // Y = G: weighted copy
+            float wg[VEC];
+            const float ws = valid ? bdec * gp[rows - 1 - t] : 0.f;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) wg[e] = go[e] * ws;
+            *reinterpret_cast<u32x4 *>(sYw + t * LX + cc) = f32_to_piece<T>(wg);
+          }
+        }
+      }
+      // Z (the value block) and the raw block for phi'
+      using SB = BSlab<T, 16, D>;
+#pragma unroll
+      for (int i = 0; i < SB::PER; ++i) {
+        const int p = tid + kBThreads * i;
+        if (SB::EXACT || p < SB::PIECES) {
+          const int r = p / SB::PPR, cc = (p % SB::PPR) * VEC;
+          const int t = trow(r);
+          const bool valid = r < rows;
+          // dq: value K' (k block), phi' of the q block; dk: the reverse
+          const u32x4 &zraw = ROLE == kRoleDQ ? rb2.v[i] : rb1.v[i];
+          const u32x4 &praw = ROLE == kRoleDQ ? rb1.v[i] : rb2.v[i];
+          float z[VEC];
+          piece_to_f32<T>(zraw, z);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) z[e] = valid ? phi(z[e], ELU) : 0.f;
+          *reinterpret_cast<u32x4 *>(sZ + t * LZ + cc) = f32_to_piece<T>(z);
+          *reinterpret_cast<u32x4 *>(sP + t * LZ + cc) = praw;
+        }
+      }
+    } else {
+      // dv: X = K', Y = Q' (full rows), Z = the G block (dout / den)
+      using S = BSlab<T, D, D>;
+#pragma unroll
+      for (int i = 0; i < S::PER; ++i) {
+        const int p = tid + kBThreads * i;
+        if (S::EXACT || p < S::PIECES) {
+          const int r = p / S::PPR, cc = (p % S::PPR) * VEC;
+          const int t = trow(r);
+          const bool valid = r < rows;
+          float kx[VEC], qx[VEC];
+          piece_to_f32<T>(r1.v[i], kx);
+          piece_to_f32<T>(r2.v[i], qx);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            kx[e] = valid ? phi(kx[e], ELU) : 0.f;
+            qx[e] = valid ? phi(qx[e], ELU) : 0.f;
+          }
+          *reinterpret_cast<u32x4 *>(sX + t * LX + cc) = f32_to_piece<T>(kx);
+          *reinterpret_cast<u32x4 *>(sY + t * LX + cc) = f32_to_piece<T>(qx);
+          if (DECAY) {
+            const float ws = valid ? bdec * gp[rows - 1 - t] : 0.f;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) qx[e] *= ws;
+            *reinterpret_cast<u32x4 *>(sYw + t * LX + cc) = f32_to_piece<T>(qx);
+          }
+        }
+      }
+      using SB = BSlab<T, 16, D>;
+#pragma unroll
+      for (int i = 0; i < SB::PER; ++i) {
+        const int p = tid + kBThreads * i;
+        const int r = p / SB::PPR, cc = (p % SB::PPR) * VEC;
+        const float den = __shfl(rd.v, r & 63);
+        if (SB::EXACT || p < SB::PIECES) {
+          const int t = trow(r);
+          const float rden = r < rows ? 1.f / den : 0.f;
+          float z[VEC];
+          piece_to_f32<T>(rb1.v[i], z);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) z[e] *= rden;
+          *reinterpret_cast<u32x4 *>(sZ + t * LZ + cc) = f32_to_piece<T>(z);
+        }
+      }
+    }
+  };
+
+  // State tiles of this wave: S (features 16 fb .. +16, the 16 value
+  // columns), fb = w + kBWaves m; past NT: unused (kept zero).
+  f32x4 S[F::TPW];
+#pragma unroll
+  for (int m = 0; m < F::TPW; ++m) S[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto publish = [&]() {  // S^T copy: row = value column, columns = features
+#pragma unroll
+    for (int m = 0; m < F::TPW; ++m) {
+      const int fb = w + kBWaves * m;
+      if (fb < F::NT)
+        store4(sST + li * LX + 16 * fb + 4 * g, S[m][0], S[m][1], S[m][2],
+               S[m][3]);
+    }
+  };
+
+  const int tb = w;                 // this wave's output strip
+  const int t = 16 * tb + li;       // the query row this lane reads out
+  load(0);
+  __syncthreads();                  // gp and the constant parts ready
+  stage(0);
+  load(1);
+  publish();
+  __syncthreads();
+
+  for (int c = 0; c < nch; ++c) {
+    const int rows = rows_of(c);
+    const float gt = gp[t + 1];
+    // ---- readout of strip tb ----
+    Frag<T> xf[KX / 32];
+#pragma unroll
+    for (int kq = 0; kq < KX / 32; ++kq)
+      load_frag8(xf[kq], sX + t * LX + 32 * kq + 8 * g);
+    f32x4 pt[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (sb <= tb) {
+#pragma unroll
+        for (int kq = 0; kq < KX / 32; ++kq) {
+          Frag<T> fa;
+          load_frag8(fa, sY + (16 * sb + li) * LX + 32 * kq + 8 * g);
+          acc = mma(fa, xf[kq], acc);
+        }
+      }
+      // acc[rr]: key s = 16 sb + 4 g + rr, query t; causal weights
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int s = 16 * sb + 4 * g + rr;
+        acc[rr] = s <= t ? acc[rr] * (DECAY ? bdec * gp[s <= t ? t - s : 0]
+                                            : 1.f)
+                         : 0.f;
+      }
+      pt[sb] = acc;
+    }
+    f32x4 an = {0.f, 0.f, 0.f, 0.f}, ai = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+      if (2 * kp <= tb) {
+        Frag<T> pf, zf;
+        frag_from_acc(pf, pt[2 * kp], pt[2 * kp + 1]);
+        load_frag_tr44(zf, sZ, LZ, 32 * kp, 0, g, li);
+        an = mma(zf, pf, an);
+      }
+    }
+#pragma unroll
+    for (int kq = 0; kq < KX / 32; ++kq) {
+      Frag<T> fa;
+      load_frag8(fa, sST + li * LX + 32 * kq + 8 * g);
+      ai = mma(fa, xf[kq], ai);
+    }
+    const f32x4 o = an + gt * ai;
+    // o[r]: value column 4 g + r of query row t; times phi' for dq, dk
+    if (t < rows) {
+      const int64_t row = row0_of(c) + (REV ? rows - 1 - t : t);
+      float x[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float dp = 1.f;
+        if constexpr (GV) dp = dphi(to_f32(sP[t * LZ + 4 * g + r]), ELU);
+        x[r] = o[r] * dp;
+      }
+      store4(res + row * D + col0 + 4 * g, x[0], x[1], x[2], x[3]);
+    }
+    // ---- state update: S <- g^r S + (w Y)^T Z ----
+    const float gr = gp[rows];
+#pragma unroll
+    for (int m = 0; m < F::TPW; ++m) {
+      const int fb = w + kBWaves * m;
+      if (fb < F::NT) {
+        f32x4 acc = S[m] * gr;
+#pragma unroll
+        for (int kb2 = 0; kb2 < C / 32; ++kb2) {
+          Frag<T> af, bf;
+          load_frag_tr8(af, sYw, LX, 32 * kb2, 16 * fb, g, li);
+          load_frag_tr8(bf, sZ, LZ, 32 * kb2, 0, g, li);
+          acc = mma(af, bf, acc);
+        }
+        S[m] = acc;
+      }
+    }
+    __syncthreads();   // the tile set is free again
+    stage(c + 1);
+    load(c + 2);
+    publish();
+    __syncthreads();
+  }
+}
+
+template <typename T, int D, int ROLE, bool DECAY, bool ELU>
+hipError_t launch_role(const BwdArgs &a, int64_t units, hipStream_t s) {
+  using F = BShape<T, D, ROLE, DECAY>;
+  static const hipError_t once = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(&la_bwd_kernel<T, D, ROLE, DECAY, ELU>),
+      hipFuncAttributeMaxDynamicSharedMemorySize,
+      static_cast<int>(F::lds_bytes));
+  if (once != hipSuccess) return once;
+  const int nblk = ROLE == kRoleDV ? D / 16 : a.dqk / 16;
+  hipLaunchKernelGGL((la_bwd_kernel<T, D, ROLE, DECAY, ELU>),
+                     dim3(static_cast<unsigned>(units * nblk)),
+                     dim3(kBThreads), F::lds_bytes, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D, bool DECAY, bool ELU>
+hipError_t launch_all(const BwdArgs &a, int64_t units, hipStream_t s) {
+  hipError_t e = launch_role<T, D, kRoleDQ, DECAY, ELU>(a, units, s);
+  if (e == hipSuccess) e = launch_role<T, D, kRoleDK, DECAY, ELU>(a, units, s);
+  if (e == hipSuccess) e = launch_role<T, D, kRoleDV, DECAY, ELU>(a, units, s);
+  return e;
+}
+
+template <typename T, int D>
+hipError_t launch_d(const BwdArgs &a, int64_t units, hipStream_t s) {
+  if (a.decay)
+    return a.elu1 ? launch_all<T, D, true, true>(a, units, s)
+                  : launch_all<T, D, true, false>(a, units, s);
+  return a.elu1 ? launch_all<T, D, false, true>(a, units, s)
+                : launch_all<T, D, false, false>(a, units, s);
+}
+
+template <typename T>
+hipError_t launch_t(const BwdArgs &a, int64_t units, int d, hipStream_t s) {
+  switch (d) {
+    case 16: return launch_d<T, 16>(a, units, s);
+    case 32: return launch_d<T, 32>(a, units, s);
+    case 64: return launch_d<T, 64>(a, units, s);
+    case 128: return launch_d<T, 128>(a, units, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool backward_supported(int d, int d_feat) {
+  return d == d_feat && (d == 16 || d == 32 || d == 64 || d == 128);
+}
+
+hipError_t launch_backward(const BwdArgs &a, int64_t units, int d, int dtype,
+                           hipStream_t s) {
+  return dtype == 1 ? launch_t<bf16>(a, units, d, s)
+                    : launch_t<float>(a, units, d, s);
+}
+
+}  // namespace la

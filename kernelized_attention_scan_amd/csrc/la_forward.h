@@ -1422,7 +1422,12 @@ void la_fwd_kernel(FwdArgs a) {
       // the denominator of row t is element 0 of this lane's ones-block
       // accumulator (row 4 g of the tile); its reciprocal (hardware, within
       // 1 ulp) scales the numerators
-      const float rden = __builtin_amdgcn_rcpf(block(NJW)[0]);
+      const float den = block(NJW)[0];
+      const float rden = __builtin_amdgcn_rcpf(den);
+      // training forward: each row's denominator, for the backward pass
+      // (the waves with jh == 0 hold every row of their strip once)
+      if (a.den_out && jh == 0 && g == 0 && t < rows)
+        a.den_out[unit * a.n + start + clamp_chunk(c) * C + t] = den;
       // the chunk's output rows (none for padding chunks); stores of rows
       // past the end and of blocks past the last are dropped
       const __amdgpu_buffer_rsrc_t ro =

@@ -71,6 +71,8 @@ struct FwdArgs {
   // workspace
   const float *log_decay;
   float *seg_log;
+  // training forward: q'_j . nu_j of every row [units][n] (causal), or null
+  float *den_out;
 };
 
 // Launch set of one (storage type, d, d_feat) instance of the chunked forward.
@@ -113,5 +115,21 @@ hipError_t launch_decode(float *mu, float *nu, const void *q, const void *k,
                          const float *decay, int dtype, hipStream_t stream,
                          int ld_layout = -1);
 bool decode_supported(int d, int d_feat);
+
+// Arguments of the backward kernels (gradients of the causal forward).
+struct BwdArgs {
+  const void *q, *k, *v, *out, *dout;  // [units][n][d] storage type
+  const float *den;                    // [units][n], from la_forward_train
+  void *dq, *dk, *dv;                  // [units][n][d] storage type
+  const float *decay;                  // [H] or null
+  int H;
+  int64_t n;
+  int dqk;    // width of q, k (== d)
+  int elu1;   // 1: phi = elu + 1; 0: identity
+};
+bool backward_supported(int d, int d_feat);
+// Enqueue the three role kernels (dq, dk, dv); dtype 0 fp32, 1 bf16.
+hipError_t launch_backward(const BwdArgs &a, int64_t units, int d, int dtype,
+                           hipStream_t stream);
 
 }  // namespace la
