@@ -39,12 +39,30 @@ BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 MALL_BYTES = 256 << 20
 
 
-def kernel_source_hash() -> str:
+# The sources each timed kernel is built from (device code and the host
+# code that picks its launch shape); a change to any of them voids the
+# counter-measured traffic taken on the old build.
+KERNEL_SOURCES = {
+    "forward": ["la_device.h", "la_internal.h", "la_forward.h",
+                "la_forward_inst.h", "la_forward_bf16.hip",
+                "la_forward_bf16_pf.hip", "la_forward_f32.hip",
+                "la_api.cpp"],
+    "decode": ["la_device.h", "la_internal.h", "la_decode.hip", "la_api.cpp"],
+    "backward": ["la_device.h", "la_internal.h", "la_backward.hip",
+                 "la_api.cpp"],
+}
+
+
+def kernel_kind(workload: str) -> str:
+    return workload if workload in ("decode", "backward") else "forward"
+
+
+def kernel_source_hash(kind: str) -> str:
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "kernelized_attention_scan_amd",
-                                           "csrc", "*"))):
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode())
+    for name in sorted(KERNEL_SOURCES[kind]):
+        with open(os.path.join(ROOT, "kernelized_attention_scan_amd", "csrc",
+                               name), "rb") as f:
+            h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -54,7 +72,7 @@ def workloads():
     return {"elu1": I.ELU1_CAUSAL, "decayed": I.DECAYED,
             "performer": I.PERFORMER, "tiny": I.TINY_FP32,
             "decode": I.DECODE, "noncausal": I.ELU1_NONCAUSAL,
-            "gated": I.GATED}
+            "gated": I.GATED, "backward": I.DECAYED}
 
 
 def esize(dtype) -> int:
@@ -91,7 +109,7 @@ def load_traffic(workload: str):
         return None
     with open(p) as f:
         t = json.load(f)
-    if t.get("kernel_src_sha") != kernel_source_hash():
+    if t.get("kernel_src_sha") != kernel_source_hash(kernel_kind(workload)):
         return None
     return t.get("traffic_bytes")
 
@@ -303,6 +321,88 @@ def prefill_leg(torch, K, I, cfg, args, dev):
                        "seed": args.seed}}
 
 
+def backward_algorithmic(cfg):
+    """Per step of the backward: read q, k, v, out, dout and den once, write
+    dq, dk, dv once; flops of the three unnormalised linear attentions it
+    is made of (dq' and dk': widths d + 1 and d'; dv: d' and d), 4 x width
+    x width per token each."""
+    d, df = cfg.d, cfg.d_feat
+    byts = cfg.tokens * (8 * d * esize(cfg.dtype) + 4)
+    flops = cfg.tokens * (2 * 4 * (d + 1) * df + 4 * df * d)
+    return byts, flops
+
+
+def backward_leg(torch, K, I, cfg, args, dev):
+    """One step = la_backward over the whole workload (the training forward
+    that produces out and den runs once, before the timed region)."""
+    mapname = I.MAP_NAMES[cfg.mapk]
+    byts, flops = backward_algorithmic(cfg)
+    x = I.make_prefill(cfg, args.seed)
+    s = {k: (None if t is None else t.to(dev)) for k, t in x.items()}
+    g = torch.Generator("cpu").manual_seed(args.seed + 7)
+    dout = torch.randn(cfg.B, cfg.H, cfg.n, cfg.d, generator=g).to(
+        cfg.dtype).to(dev)
+    out, den = K.forward_train(s["q"], s["k"], s["v"], mapname,
+                               decay=s["decay"])
+    grads = [torch.empty_like(s["q"]) for _ in range(3)]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        K.backward(s["q"], s["k"], s["v"], out, den, dout, mapname,
+                   decay=s["decay"], dq=grads[0], dk=grads[1], dv=grads[2])
+
+    settled = settle(torch, step, args.settle_ms)
+    for i in range(args.warmup):
+        step(i)
+    t_wall = time.perf_counter()
+    ms = time_loop(torch, step, args.steps, stream)
+    t_wall = time.perf_counter() - t_wall
+    return {"ms": ms, "t_wall": t_wall, "items": cfg.tokens,
+            "unit": "tokens/s", "bytes": byts, "flops": flops,
+            "kern": {"kernel": "la_bwd_kernel (dq, dk and dv roles in one "
+                               "launch)",
+                     "ms": ms, "bytes": byts, "flops": flops},
+            "nsets": 1, "settle_steps": settled,
+            "config": {"workload": "backward_" + cfg.name, "B": cfg.B,
+                       "H": cfg.H, "n": cfg.n, "d": cfg.d,
+                       "d_feat": cfg.d_feat, "map": mapname,
+                       "decay": cfg.decay, "causal": True, "seed": args.seed}}
+
+
+def cpu_baseline_backward(cfg, seed: int, budget_s: float = 15.0):
+    import oracle
+    from kernelized_attention_scan_amd import inputs as I
+    x = I.make_prefill(cfg, seed)
+    f64 = lambda t: None if t is None else t.double().numpy()
+    g = __import__("torch").Generator("cpu").manual_seed(seed + 7)
+    dout = __import__("torch").randn(cfg.B, cfg.H, cfg.n, cfg.d, generator=g)
+    units = cfg.B * cfg.H
+    flat = lambda t: t.reshape(1, units, cfg.n, t.shape[-1])
+    q, k, v, do = flat(x["q"]), flat(x["k"]), flat(x["v"]), flat(dout)
+    dec = None if x["decay"] is None else x["decay"].repeat(cfg.B)
+    threads = oracle.num_threads()
+
+    def run(take):
+        sl = slice(0, take)
+        return oracle.backward(f64(q[:, sl]), f64(k[:, sl]), f64(v[:, sl]),
+                               f64(do[:, sl]), cfg.mapk, None,
+                               None if dec is None else f64(dec[sl]))
+
+    probe = min(units, threads)
+    t0 = time.perf_counter()
+    run(probe)
+    per = time.perf_counter() - t0
+    take = max(probe, min(units, int(budget_s / max(per, 1e-9)) * probe))
+    t0 = time.perf_counter()
+    run(take)
+    dt = time.perf_counter() - t0
+    return {"value": take * cfg.n / dt, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{take} of {units} (batch, head) units x n={cfg.n} of "
+                      f"workload {cfg.name}; fp64 adjoint recurrence "
+                      f"(gradients), {dt:.1f} s"}
+
+
 def decode_leg(torch, K, I, cfg, args, dev):
     mapname = I.MAP_NAMES[cfg.mapk]
     byts, flops = decode_algorithmic(cfg)
@@ -380,8 +480,9 @@ def main() -> int:
     K.load_library()
     cfg = workloads()[args.workload]
     is_decode = args.workload == "decode"
-    leg = (decode_leg if is_decode else prefill_leg)(torch, K, I, cfg, args,
-                                                     dev)
+    is_bwd = args.workload == "backward"
+    leg = (decode_leg if is_decode else backward_leg if is_bwd
+           else prefill_leg)(torch, K, I, cfg, args, dev)
     ms = leg["ms"]
     kern = leg["kern"]
     achieved = kern["bytes"] / (kern["ms"] * 1e-3) / 1e9
@@ -390,8 +491,10 @@ def main() -> int:
     else:
         dtype = "bf16"
     line = {
-        "metric": METRIC if not is_decode else
+        "metric": METRIC if not (is_decode or is_bwd) else
                   "linear-attn decode step head-tokens/s (S·H/s) + % of "
+                  "HBM roofline" if is_decode else
+                  "causal linear-attn backward tokens/s (B·H·n/s) + % of "
                   "HBM roofline",
         "value": leg["items"] / (ms * 1e-3),
         "unit": leg["unit"],
@@ -424,6 +527,7 @@ def main() -> int:
         line["roofline"]["launches_ms"] = kern["other_launches_ms"]
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = (cpu_baseline_decode if is_decode
+                                else cpu_baseline_backward if is_bwd
                                 else cpu_baseline_prefill)(cfg, args.seed)
     print(json.dumps(line), flush=True)
     return 0

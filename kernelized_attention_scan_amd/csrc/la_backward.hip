@@ -26,12 +26,15 @@
 // in reverse, so the same formulas read the sequence backwards.
 //
 // Parallelism: one 256-thread workgroup (4 waves) per (unit, role, block
-// of 16 output columns), each walking its unit's whole sequence.  The
-// roles and blocks of a unit are independent, so no segment exchange is
-// needed: B H (2 d'/16 + d/16) workgroups (768 at B H = 32, d = 128).
+// of 16 output columns), each walking its unit's whole sequence, all in one
+// launch.  The roles and blocks of a unit are independent, so no segment
+// exchange is needed: B H (2 d'/16 + d/16) workgroups (768 at B H = 32,
+// d = 128), about 53 KB of LDS each, so three share a compute unit.
 // Every workgroup recomputes the scores of its role (the price of
 // independence); the raw rows it shares with the unit's other workgroups
 // come mostly from L2.
+#include <algorithm>
+
 #include "la_device.h"
 #include "la_internal.h"
 
@@ -64,8 +67,7 @@ struct BShape {
   static constexpr int TPW = (NT + kBWaves - 1) / kBWaves;
   static constexpr int SX = kBC * LX, SZ = kBC * LZ, SST = 16 * LX;
   static constexpr size_t lds_bytes =
-      sizeof(T) * (SX * (DECAY ? 3 : 2) + SZ * 2 + SST) +
-      sizeof(float) * (kBC + 4);
+      sizeof(T) * (SX * 2 + SZ + SST) + sizeof(float) * (kBC + 4);
 };
 
 // 16-byte pieces of a [C][W] row-major slab (consecutive threads take
@@ -151,33 +153,23 @@ __device__ __forceinline__ float dphi(float x, bool elu) {  // d phi / d x
   return elu ? (x > 0.f ? 1.f : expf(x)) : 1.f;
 }
 
+// One role's workgroup: output columns 16 blk .. 16 blk + 15 of unit.
 template <typename T, int D, int ROLE, bool DECAY, bool ELU>
-__global__ __launch_bounds__(kBThreads) void la_bwd_kernel(BwdArgs a) {
+__device__ __forceinline__ void bwd_role(const BwdArgs &a, int64_t unit,
+                                         int blk, unsigned char *smem) {
   using F = BShape<T, D, ROLE, DECAY>;
   constexpr int C = kBC, KX = F::KX, LX = F::LX, LZ = F::LZ;
   constexpr bool GV = F::GV, REV = ROLE != kRoleDQ;
   constexpr int VEC = 16 / sizeof(T);
-  extern __shared__ __align__(16) unsigned char smem[];
   T *sX = reinterpret_cast<T *>(smem);           // queries X
   T *sY = sX + F::SX;                            // keys Y
-  T *sYw = DECAY ? sY + F::SX : sY;              // w_s Y_s (state update)
-  T *sZ = sY + F::SX * (DECAY ? 2 : 1);          // values Z (16 columns)
-  T *sP = sZ + F::SZ;                            // raw x for phi' (16 cols)
-  T *sST = sP + F::SZ;                           // S^T copy
+  T *sZ = sY + F::SX;                            // values Z (16 columns)
+  T *sST = sZ + F::SZ;                           // S^T copy
   float *gp = reinterpret_cast<float *>(sST + F::SST);  // g^0 .. g^C
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, li = lane & 15;
-  const int nblk = ROLE == kRoleDV ? D / 16 : a.dqk / 16;
-  // Workgroups are dispatched to the 8 XCDs round-robin by block index; the
-  // blocks of one unit are given indices of one XCD (when the grid divides
-  // evenly), so the rows they all read come from that XCD's L2.
-  int64_t bid = blockIdx.x;
-  if (gridDim.x % 8 == 0)
-    bid = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
-  const int64_t unit = bid / nblk;
-  const int blk = static_cast<int>(bid % nblk);
   const int col0 = 16 * blk;
   const int h = static_cast<int>(unit % a.H);
   const float gdec = DECAY ? a.decay[h] : 1.f, bdec = DECAY ? 1.f - gdec : 1.f;
@@ -203,7 +195,6 @@ __global__ __launch_bounds__(kBThreads) void la_bwd_kernel(BwdArgs a) {
     const int row = i / (KX - XW), col = XW + i % (KX - XW);
     sX[row * LX + col] = from_f32<T>(0.f);
     sY[row * LX + col] = from_f32<T>(0.f);
-    if (DECAY) sYw[row * LX + col] = from_f32<T>(0.f);
   }
 
   const int nch = static_cast<int>((n + C - 1) / C);
@@ -219,9 +210,9 @@ __global__ __launch_bounds__(kBThreads) void la_bwd_kernel(BwdArgs a) {
   };
 
   // Register ring (one chunk ahead).  GV roles: dout, out, v full rows;
-  // q and k blocks.  dv: k, q full rows; the dout block.
+  // the k block (dq) or q block (dk).  dv: k, q full rows; the dout block.
   BSlab<T, D, D> r1, r2, r3;   // GV: dout, out, v   dv: k, q, (unused)
-  BSlab<T, 16, D> rb1, rb2;    // GV: q block, k block   dv: dout block
+  BSlab<T, 16, D> rb1;         // GV: k or q block   dv: dout block
   BDen rd;
   auto load = [&](int c) {
     const int64_t r0 = row0_of(c);
@@ -230,8 +221,7 @@ __global__ __launch_bounds__(kBThreads) void la_bwd_kernel(BwdArgs a) {
       r1.load(gb, r0, rows, 0, tid);
       r2.load(ob, r0, rows, 0, tid);
       r3.load(vb, r0, rows, 0, tid);
-      rb1.load(qb, r0, rows, col0, tid);
-      rb2.load(kb, r0, rows, col0, tid);
+      rb1.load(ROLE == kRoleDQ ? kb : qb, r0, rows, col0, tid);
     } else {
       r1.load(kb, r0, rows, 0, tid);
       r2.load(qb, r0, rows, 0, tid);
@@ -273,15 +263,7 @@ __global__ __launch_bounds__(kBThreads) void la_bwd_kernel(BwdArgs a) {
         if (mine) {
           const int t = trow(r);
           *reinterpret_cast<u32x4 *>(sG + t * LX + cc) = f32_to_piece<T>(go);
-          const u32x4 pv = f32_to_piece<T>(vv);
-          *reinterpret_cast<u32x4 *>(sV + t * LX + cc) = pv;
-          if (DECAY && ROLE == kRoleDQ) {  // Y = V+: weighted copy
-            float wv[VEC];
-            const float ws = valid ? bdec * gp[rows - 1 - t] : 0.f;
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) wv[e] = vv[e] * ws;
-            *reinterpret_cast<u32x4 *>(sYw + t * LX + cc) = f32_to_piece<T>(wv);
-          }
+          *reinterpret_cast<u32x4 *>(sV + t * LX + cc) = f32_to_piece<T>(vv);
           if (cc == 0) {
             // h = -g . out as hi + lo (columns d, d + 1); V+ has 1 in both
             const float hh = -dot;
@@ -291,22 +273,10 @@ __global__ __launch_bounds__(kBThreads) void la_bwd_kernel(BwdArgs a) {
             sG[t * LX + D + 1] = from_f32<T>(lo);
             sV[t * LX + D] = from_f32<T>(one);
             sV[t * LX + D + 1] = from_f32<T>(one);
-            if (DECAY) {
-              const float ws = valid ? bdec * gp[rows - 1 - t] : 0.f;
-              sYw[t * LX + D] = from_f32<T>(ROLE == kRoleDQ ? ws : hi * ws);
-              sYw[t * LX + D + 1] = from_f32<T>(ROLE == kRoleDQ ? ws : lo * ws);
-            }
-          }
-          if (DECAY && ROLE == kRoleDK) {  // Y = G: weighted copy
-            float wg[VEC];
-            const float ws = valid ? bdec * gp[rows - 1 - t] : 0.f;
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) wg[e] = go[e] * ws;
-            *reinterpret_cast<u32x4 *>(sYw + t * LX + cc) = f32_to_piece<T>(wg);
           }
         }
       }
-      // Z (the value block) and the raw block for phi'
+      // Z (the value block)
       using SB = BSlab<T, 16, D>;
 #pragma unroll
       for (int i = 0; i < SB::PER; ++i) {
@@ -315,15 +285,12 @@ __global__ __launch_bounds__(kBThreads) void la_bwd_kernel(BwdArgs a) {
           const int r = p / SB::PPR, cc = (p % SB::PPR) * VEC;
           const int t = trow(r);
           const bool valid = r < rows;
-          // dq: value K' (k block), phi' of the q block; dk: the reverse
-          const u32x4 &zraw = ROLE == kRoleDQ ? rb2.v[i] : rb1.v[i];
-          const u32x4 &praw = ROLE == kRoleDQ ? rb1.v[i] : rb2.v[i];
+          // dq: value K' (the k block); dk: Q' (the q block)
           float z[VEC];
-          piece_to_f32<T>(zraw, z);
+          piece_to_f32<T>(rb1.v[i], z);
 #pragma unroll
           for (int e = 0; e < VEC; ++e) z[e] = valid ? phi(z[e], ELU) : 0.f;
           *reinterpret_cast<u32x4 *>(sZ + t * LZ + cc) = f32_to_piece<T>(z);
-          *reinterpret_cast<u32x4 *>(sP + t * LZ + cc) = praw;
         }
       }
     } else {
@@ -346,12 +313,6 @@ __global__ __launch_bounds__(kBThreads) void la_bwd_kernel(BwdArgs a) {
           }
           *reinterpret_cast<u32x4 *>(sX + t * LX + cc) = f32_to_piece<T>(kx);
           *reinterpret_cast<u32x4 *>(sY + t * LX + cc) = f32_to_piece<T>(qx);
-          if (DECAY) {
-            const float ws = valid ? bdec * gp[rows - 1 - t] : 0.f;
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) qx[e] *= ws;
-            *reinterpret_cast<u32x4 *>(sYw + t * LX + cc) = f32_to_piece<T>(qx);
-          }
         }
       }
       using SB = BSlab<T, 16, D>;
@@ -447,17 +408,29 @@ __global__ __launch_bounds__(kBThreads) void la_bwd_kernel(BwdArgs a) {
     // o[r]: value column 4 g + r of query row t; times phi' for dq, dk
     if (t < rows) {
       const int64_t row = row0_of(c) + (REV ? rows - 1 - t : t);
+      // dq, dk: times phi'(x) of the same elements of q or k (read back,
+      // from L2: the rows were loaded a chunk ago)
+      const T *xp = (ROLE == kRoleDQ ? qb : kb) + row * D + col0 + 4 * g;
       float x[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float dp = 1.f;
-        if constexpr (GV) dp = dphi(to_f32(sP[t * LZ + 4 * g + r]), ELU);
-        x[r] = o[r] * dp;
-      }
+      for (int r = 0; r < 4; ++r)
+        x[r] = GV && ELU ? o[r] * dphi(to_f32(xp[r]), true) : o[r];
       store4(res + row * D + col0 + 4 * g, x[0], x[1], x[2], x[3]);
     }
-    // ---- state update: S <- g^r S + (w Y)^T Z ----
+    // ---- state update: S <- g^r S + (w Y)^T Z, the weights w_s =
+    // b g^(r-1-s) of positions 32 kb + 8 g + e applied in registers ----
     const float gr = gp[rows];
+    f32x4 wlo[C / 32], whi[C / 32];
+    if constexpr (DECAY) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < C / 32; ++kb2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int s0 = 32 * kb2 + 8 * g + e, s1 = s0 + 4;
+          wlo[kb2][e] = s0 < rows ? bdec * gp[rows - 1 - s0] : 0.f;
+          whi[kb2][e] = s1 < rows ? bdec * gp[rows - 1 - s1] : 0.f;
+        }
+    }
 #pragma unroll
     for (int m = 0; m < F::TPW; ++m) {
       const int fb = w + kBWaves * m;
@@ -466,7 +439,8 @@ __global__ __launch_bounds__(kBThreads) void la_bwd_kernel(BwdArgs a) {
 #pragma unroll
         for (int kb2 = 0; kb2 < C / 32; ++kb2) {
           Frag<T> af, bf;
-          load_frag_tr8(af, sYw, LX, 32 * kb2, 16 * fb, g, li);
+          load_frag_tr8(af, sY, LX, 32 * kb2, 16 * fb, g, li);
+          if constexpr (DECAY) frag_scale(af, wlo[kb2], whi[kb2]);
           load_frag_tr8(bf, sZ, LZ, 32 * kb2, 0, g, li);
           acc = mma(af, bf, acc);
         }
@@ -481,27 +455,48 @@ __global__ __launch_bounds__(kBThreads) void la_bwd_kernel(BwdArgs a) {
   }
 }
 
-template <typename T, int D, int ROLE, bool DECAY, bool ELU>
-hipError_t launch_role(const BwdArgs &a, int64_t units, hipStream_t s) {
-  using F = BShape<T, D, ROLE, DECAY>;
-  static const hipError_t once = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&la_bwd_kernel<T, D, ROLE, DECAY, ELU>),
-      hipFuncAttributeMaxDynamicSharedMemorySize,
-      static_cast<int>(F::lds_bytes));
-  if (once != hipSuccess) return once;
-  const int nblk = ROLE == kRoleDV ? D / 16 : a.dqk / 16;
-  hipLaunchKernelGGL((la_bwd_kernel<T, D, ROLE, DECAY, ELU>),
-                     dim3(static_cast<unsigned>(units * nblk)),
-                     dim3(kBThreads), F::lds_bytes, s, a);
-  return hipGetLastError();
+// All roles in one launch: blocks [0, units nq) take dq, the next units nq
+// dk, the last units nv dv (nq = d'/16, nv = d/16).  Within a role the
+// blocks of one unit get indices of one XCD (workgroups are dispatched to
+// the 8 XCDs round-robin), so the rows they all read come from its L2.
+template <typename T, int D, bool DECAY, bool ELU>
+__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 3 : 1)))
+void la_bwd_kernel(BwdArgs a,
+                                                           int64_t units) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int nq = a.dqk / 16, nv = D / 16;
+  const int64_t b = blockIdx.x;
+  const int64_t cq = units * nq;
+  const int role = b < cq ? kRoleDQ : b < 2 * cq ? kRoleDK : kRoleDV;
+  int64_t i = role == kRoleDQ ? b : role == kRoleDK ? b - cq : b - 2 * cq;
+  const int nblk = role == kRoleDV ? nv : nq;
+  const int64_t span = units * nblk;
+  if (span % 8 == 0) i = (i % 8) * (span / 8) + i / 8;
+  const int64_t unit = i / nblk;
+  const int blk = static_cast<int>(i % nblk);
+  if (role == kRoleDQ)
+    bwd_role<T, D, kRoleDQ, DECAY, ELU>(a, unit, blk, smem);
+  else if (role == kRoleDK)
+    bwd_role<T, D, kRoleDK, DECAY, ELU>(a, unit, blk, smem);
+  else
+    bwd_role<T, D, kRoleDV, DECAY, ELU>(a, unit, blk, smem);
 }
 
 template <typename T, int D, bool DECAY, bool ELU>
 hipError_t launch_all(const BwdArgs &a, int64_t units, hipStream_t s) {
-  hipError_t e = launch_role<T, D, kRoleDQ, DECAY, ELU>(a, units, s);
-  if (e == hipSuccess) e = launch_role<T, D, kRoleDK, DECAY, ELU>(a, units, s);
-  if (e == hipSuccess) e = launch_role<T, D, kRoleDV, DECAY, ELU>(a, units, s);
-  return e;
+  constexpr size_t lds =
+      std::max({BShape<T, D, kRoleDQ, DECAY>::lds_bytes,
+                BShape<T, D, kRoleDK, DECAY>::lds_bytes,
+                BShape<T, D, kRoleDV, DECAY>::lds_bytes});
+  static const hipError_t once = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(&la_bwd_kernel<T, D, DECAY, ELU>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (once != hipSuccess) return once;
+  const int64_t blocks = units * (2 * (a.dqk / 16) + D / 16);
+  hipLaunchKernelGGL((la_bwd_kernel<T, D, DECAY, ELU>),
+                     dim3(static_cast<unsigned>(blocks)), dim3(kBThreads), lds,
+                     s, a, units);
+  return hipGetLastError();
 }
 
 template <typename T, int D>

@@ -177,6 +177,26 @@ __device__ __forceinline__ float bf16_hi(unsigned u) {
   return __builtin_bit_cast(float, u & 0xffff0000u);
 }
 
+// Element e of f times the weight of its position: w0 for elements 0..3,
+// w1 for 4..7 (rounded back to the operand type).
+__device__ __forceinline__ void frag_scale(Frag<bf16> &f, const f32x4 &w0,
+                                           const f32x4 &w1) {
+  const u32x4 u = __builtin_bit_cast(u32x4, f.v);
+  const u32x4 r = {pack_bf16x2(bf16_lo(u[0]) * w0[0], bf16_hi(u[0]) * w0[1]),
+                   pack_bf16x2(bf16_lo(u[1]) * w0[2], bf16_hi(u[1]) * w0[3]),
+                   pack_bf16x2(bf16_lo(u[2]) * w1[0], bf16_hi(u[2]) * w1[1]),
+                   pack_bf16x2(bf16_lo(u[3]) * w1[2], bf16_hi(u[3]) * w1[3])};
+  f.v = __builtin_bit_cast(bf16x8, r);
+}
+__device__ __forceinline__ void frag_scale(Frag<float> &f, const f32x4 &w0,
+                                           const f32x4 &w1) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f.v[e] *= w0[e];
+    f.v[4 + e] *= w1[e];
+  }
+}
+
 // Split-assignment fragment from two stacked accumulator tiles (top: k = 0..15
 // of the block, bottom: k = 16..31), rounded to the operand type.
 __device__ __forceinline__ void frag_from_acc(Frag<bf16> &f, const f32x4 &top,
