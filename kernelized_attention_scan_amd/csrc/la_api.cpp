@@ -132,37 +132,39 @@ la_status plan_forward(int B, int H, int64_t n, int d, int d_feat, int map,
   // about one workgroup per compute unit: measured faster than filling a
   // second workgroup slot per CU with shorter segments (the chain phase 1 ->
   // exchange -> phase 2 is shorter with fewer, longer segments)
+  // (with a value split each unit is vsplit computations of its own)
+  const int64_t vunits = units * p->ops->vsplit;
   const int64_t target = la::kCUs;
-  int64_t per_unit = (target + units - 1) / units;
+  int64_t per_unit = (target + vunits - 1) / vunits;
   if (per_unit > kMaxSegments) per_unit = kMaxSegments;
   if (per_unit < 1) per_unit = 1;
   if (per_unit > nchunks) per_unit = nchunks;
   if (state_cap > 0) {
     const size_t slot = static_cast<size_t>(p->ops->slot_floats) * sizeof(float);
     auto need = [&](int64_t k) {
-      return la::kSyncBytes + align256(static_cast<size_t>(units) * k * slot) +
-             align256(static_cast<size_t>(units) * k * sizeof(float));
+      return la::kSyncBytes + align256(static_cast<size_t>(vunits) * k * slot) +
+             align256(static_cast<size_t>(vunits) * k * sizeof(float));
     };
     while (per_unit > 1 && need(per_unit) > state_cap) --per_unit;
   }
   const int64_t cps = (nchunks + per_unit - 1) / per_unit;
   p->seg_len = cps * C;
   p->nseg = static_cast<int>((n + p->seg_len - 1) / p->seg_len);
-  if (units * p->nseg > (int64_t{1} << 31) - 1)
+  if (vunits * p->nseg > (int64_t{1} << 31) - 1)
     return fail(LA_ERR_UNSUPPORTED, "too many workgroups");
   p->need_states = p->nseg > 1;
-  if (p->need_states && units >= la::kMaxTargetGroups)
+  if (p->need_states && vunits >= la::kMaxTargetGroups)
     return fail(LA_ERR_HIP, "internal: segmented split for %lld units",
-                static_cast<long long>(units));
+                static_cast<long long>(vunits));
   p->sync_bytes = p->need_states ? la::kSyncBytes : 0;
   p->agg_bytes = p->need_states
-                     ? align256(static_cast<size_t>(units) * p->nseg *
+                     ? align256(static_cast<size_t>(vunits) * p->nseg *
                                 p->ops->slot_floats * sizeof(float))
                      : 0;
   p->state_bytes =
       p->need_states
           ? p->sync_bytes + p->agg_bytes +
-                align256(static_cast<size_t>(units) * p->nseg * sizeof(float))
+                align256(static_cast<size_t>(vunits) * p->nseg * sizeof(float))
           : 0;
   p->feat_bytes = map == LA_MAP_PERFORMER && !p->fused_performer
                       ? align256(static_cast<size_t>(units * n) * d_feat *

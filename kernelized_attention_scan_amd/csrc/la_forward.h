@@ -91,6 +91,22 @@ struct Slab {
       if (EXACT || p < PIECES) v[i] = buffer_load16(r, 16u * p);
     }
   }
+  // The same W columns out of rows of ld >= W elements (a column part of a
+  // wider matrix); the resource ends after the last valid row's W columns.
+  __device__ __forceinline__ void load_ld(const T *base, int64_t row0,
+                                          int rows, int ld, int tid) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(
+        base + row0 * ld,
+        rows > 0 ? static_cast<unsigned>((rows - 1) * ld + W) * sizeof(T) : 0u);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int p = tid + kThreads * i;
+      if (EXACT || p < PIECES)
+        v[i] = buffer_load16(
+            r, static_cast<unsigned>((p / PPR) * ld + (p % PPR) * VEC) *
+                   sizeof(T));
+    }
+  }
 };
 
 // Row stride (elements) for a row of w elements: 16 mod 32 for bf16 (the
@@ -107,11 +123,11 @@ constexpr int kMapPerformer = 2;  // Performer random features, fused
 
 // LDS bytes of one instance with chunk length c (see FwdShape): nbuf sets of
 // the q', w.k' (wkeys), V and S^T tiles, kslots slots of k', the raw q, k
-// rows of the fused Performer map, and with per-position decay (sel) one
-// table of the chunk's decay weights per set.
+// rows of the fused Performer map, and per set a table of tab floats (the
+// chunk's decay weights, where the instance keeps one).
 template <typename T>
 constexpr size_t fwd_lds_bytes(int c, int d, int df, bool wkeys, bool pf,
-                               int kslots = 1, int nbuf = 1, bool sel = false) {
+                               int kslots = 1, int nbuf = 1, int tab = 0) {
   const int dfp = df < 32 ? 32 : df;
   const size_t sq = static_cast<size_t>(c) * lds_stride<T>(dfp);
   const size_t sv = static_cast<size_t>(c) * lds_stride<T>(d + 16);
@@ -119,8 +135,7 @@ constexpr size_t fwd_lds_bytes(int c, int d, int df, bool wkeys, bool pf,
   const size_t sx = pf ? static_cast<size_t>(c) * lds_stride<T>(d) : 0;
   return sizeof(T) * (nbuf * (sq + (wkeys ? sq : 0) + sv + sst) +
                       kslots * sq + 2 * sx) +
-         sizeof(float) * (c + 8 + kMaxSegments + (pf ? 2 * c : 0) +
-                          (sel ? nbuf * (3 * c + 4) : 0));
+         sizeof(float) * (c + 8 + kMaxSegments + (pf ? 2 * c : 0) + nbuf * tab);
 }
 
 // Largest power of two <= x, at most 8 (1 for x < 2).
@@ -134,17 +149,28 @@ template <typename T, int D, int DF, int DK, int MAP = kMapFeatures>
 struct FwdShape {
   static constexpr bool DECAY = DK != 0;
   static constexpr bool SEL = DK == 2;    // per-position decay
-  static constexpr bool WKEYS = DK == 1;  // a staged tile of weighted keys
   static constexpr bool PF = MAP == kMapPerformer;
   static constexpr int DV = D;                       // value width d
   // width of the q, k rows in memory: d for the fused Performer map
   static constexpr int QW = PF ? D : DF;
   // Chunk rows: 64 for bf16 operands; 32 where LDS would not hold 64.
   static constexpr int C =
-      PF ? (fwd_lds_bytes<T>(64, D, DF, WKEYS, true, 1, 1, SEL) <= kMaxLds
+      PF ? (fwd_lds_bytes<T>(64, D, DF, DK == 1, true, 1, 1,
+                             SEL ? 3 * 64 + 4 : 0) <= kMaxLds
                 ? 64
                 : 32)
          : ((sizeof(T) == 2 && !(DF == 256 && D == 128)) ? 64 : 32);
+  // One decay per head: the state update reads a staged tile of weighted
+  // keys (WKEYS) where LDS holds one; else (RW) it weights the key
+  // fragments in registers from a per-chunk table, as per-position decay
+  // does.
+  static constexpr bool WKEYS =
+      DK == 1 && (PF || fwd_lds_bytes<T>(C, D, DF, true, false) <= kMaxLds);
+  static constexpr bool RW = DK == 1 && !WKEYS;
+  // Floats of one tile set's table: per-position decay, see sel_table; RW,
+  // the state-update weight of each key.  WOFF: where those weights start.
+  static constexpr int TAB = SEL ? 3 * C + 4 : RW ? C : 0;
+  static constexpr int WOFF = SEL ? 2 * C : 0;
   static constexpr int DFP = DF < 32 ? 32 : DF;      // padded k-width of q', k'
   static constexpr int LQ = lds_stride<T>(DFP);      // sQ, sK, sKw, sST
   static constexpr int LV = lds_stride<T>(D + 16);   // sV: V | ones block
@@ -177,18 +203,16 @@ struct FwdShape {
       !PF && !DECAY && sizeof(T) == 2 && D <= 64 && DF <= 64;
   static constexpr int KRES_ =
       !RES_OK ? 0
-      : fwd_lds_bytes<T>(C, D, DF, WKEYS, PF, 8, 2, SEL) <= kMaxLds ? 8
-      : fwd_lds_bytes<T>(C, D, DF, WKEYS, PF, 4, 2, SEL) <= kMaxLds ? 4
+      : fwd_lds_bytes<T>(C, D, DF, WKEYS, PF, 8, 2, TAB) <= kMaxLds ? 8
+      : fwd_lds_bytes<T>(C, D, DF, WKEYS, PF, 4, 2, TAB) <= kMaxLds ? 4
                                                                 : 0;
   static constexpr int KS2 = KRES_ > 2 ? KRES_ : 2;
   static constexpr bool PIPE =
-      !PF && fwd_lds_bytes<T>(C, D, DF, WKEYS, PF, KS2, 2, SEL) <= kMaxLds;
+      !PF && fwd_lds_bytes<T>(C, D, DF, WKEYS, PF, KS2, 2, TAB) <= kMaxLds;
   static constexpr int NBUF = PIPE ? 2 : 1;                 // sets of tiles
   static constexpr int KS = PIPE ? KS2 : 1;                 // slots of sK
   static constexpr size_t lds_bytes =
-      fwd_lds_bytes<T>(C, D, DF, WKEYS, PF, KS, NBUF, SEL);
-  // per-position decay: floats of one set's table (see sel_table)
-  static constexpr int TAB = SEL ? 3 * C + 4 : 0;
+      fwd_lds_bytes<T>(C, D, DF, WKEYS, PF, KS, NBUF, TAB);
   // fp32 state slot: NTILE tiles x 64 lanes x 4 (accumulator order).
   static constexpr int SLOT = NTILE * 256;
   // Workgroups per compute unit the instance is built for: two (<= 128
@@ -316,6 +340,15 @@ __device__ __forceinline__ float sel_table(float lam, float *tab, int lane) {
     if (lane == 0) tab[3 * C] = __builtin_amdgcn_exp2f(last);
   }
   return last;
+}
+
+// One decay per head with the weights in registers (RW): the state-update
+// weight b g^(rows-1-s) of each key s of the chunk, 0 past the valid rows,
+// written by the first C lanes of one wave.
+template <int C>
+__device__ __forceinline__ void rw_table(float *tab, const float *gp, float b,
+                                         int rows, int lane) {
+  if (lane < C) tab[lane] = lane < rows ? b * gp[rows - 1 - lane] : 0.f;
 }
 
 // Per-head decay: g = a, b = 1 - a (eqs 10-11); g = b = 1 without decay.
@@ -555,7 +588,7 @@ __device__ __forceinline__ void state_update(f32x4 *S, const T *sKw,
     for (int kb = 0; kb < C / 32; ++kb) {
       load_frag_tr8(af[kb], sKw, F::LQ, 32 * kb, 16 * fb, g, li);
       frag_mask(af[kb], u32x4{kmask, kmask, kmask, kmask});
-      if constexpr (F::SEL) {  // positions 32 kb + 8 g + e
+      if constexpr (F::SEL || F::RW) {  // positions 32 kb + 8 g + e
         const f32x4 *wp = reinterpret_cast<const f32x4 *>(wk + 32 * kb + 8 * g);
         frag_scale(af[kb], wp[0], wp[1]);
       }
@@ -734,12 +767,13 @@ __device__ __forceinline__ void count_done(unsigned *line, int nseg) {
 // co-residency).
 // DK: the decay mode of FwdShape (0 none, 1 per head, 2 per position).
 template <typename T, int D, int DF, bool CAUSAL, bool MULTI, int DK,
-          int MAP, bool RES = false, int SPLIT = 0>
+          int MAP, bool RES = false, int SPLIT = 0, int VS = 1>
 __global__ __launch_bounds__(kThreads,
                              (FwdShape<T, D, DF, DK, MAP>::WAVES_PER_SIMD))
 void la_fwd_kernel(FwdArgs a) {
   using F = FwdShape<T, D, DF, DK, MAP>;
-  constexpr bool DECAY = F::DECAY, SEL = F::SEL, WKEYS = F::WKEYS;
+  constexpr bool DECAY = F::DECAY, SEL = F::SEL, WKEYS = F::WKEYS,
+                 RW = F::RW;
   static_assert(!RES || (F::KRES > 0 && CAUSAL && MULTI), "resident keys");
   static_assert(SPLIT == 0 || (MULTI && !CAUSAL && !RES), "split launches");
   // the in-kernel exchange through the synchronisation area
@@ -780,9 +814,15 @@ void la_fwd_kernel(FwdArgs a) {
   int64_t blk = blockIdx.x;
   if (MULTI && a.nseg > 1 && gridDim.x % 8 == 0)
     blk = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
-  const int64_t unit = blk / a.nseg;
+  // With a value split (VS > 1) each (batch, head) unit is VS independent
+  // computations over D of its VS D value columns: vunit numbers them (sync
+  // line, aggregates), unit is the (batch, head) unit and part the columns.
+  const int64_t vunit = blk / a.nseg;
+  const int64_t unit = vunit / VS;
+  const int part = static_cast<int>(vunit % VS);
+  constexpr int LDV = D * VS;  // elements per row of v and out
   unsigned *line = EXCH && a.nseg > 1
-                       ? a.sync + kSyncHeaderWords + unit * kSyncLineWords
+                       ? a.sync + kSyncHeaderWords + vunit * kSyncLineWords
                        : nullptr;
   int seg = static_cast<int>(blk % a.nseg);
   // Causal segments take their index from the unit's ticket counter, in the
@@ -792,10 +832,16 @@ void la_fwd_kernel(FwdArgs a) {
   // flight.
   const T *qb = static_cast<const T *>(a.q) + unit * a.n * QW;
   const T *kb = static_cast<const T *>(a.k) + unit * a.n * QW;
-  const T *vb = static_cast<const T *>(a.v) + unit * a.n * D;
+  const T *vb = static_cast<const T *>(a.v) + unit * a.n * LDV + part * D;
   // per-position decay: the unit's log decays [n]
   const float *lb = SEL ? a.log_decay + unit * a.n : nullptr;
-  T *ob = static_cast<T *>(a.out) + unit * a.n * D;
+  T *ob = static_cast<T *>(a.out) + unit * a.n * LDV + part * D;
+  auto loadv = [&](Slab<T, D, C> &sv, int64_t r0, int rows) {
+    if constexpr (VS > 1)
+      sv.load_ld(vb, r0, rows, LDV, tid);
+    else
+      sv.load(vb, r0, rows, tid);
+  };
   // Before the ticket returns, each workgroup loads the first phase-1 chunk
   // of the segment its block would take in block order (guess).  The
   // segments of a unit share an XCD, so together they bring every
@@ -810,7 +856,7 @@ void la_fwd_kernel(FwdArgs a) {
     const int grows =
         static_cast<int>(max<int64_t>(0, min<int64_t>(C, a.n - g0)));
     gk.load(kb, g0 < a.n ? g0 : 0, grows, tid);
-    gv.load(vb, g0 < a.n ? g0 : 0, grows, tid);
+    loadv(gv, g0 < a.n ? g0 : 0, grows);
   }
   unsigned tk = 0u;
   if (EXCH && CAUSAL && a.nseg > 1 && tid == 0)
@@ -922,7 +968,7 @@ void la_fwd_kernel(FwdArgs a) {
     sq.load(qb, r0, rows, tid);
     if (CAUSAL) {
       if (!resident) sk.load(kb, r0, rows, tid);
-      sv.load(vb, r0, rows, tid);
+      loadv(sv, r0, rows);
       if constexpr (SEL) sl.load(lb, r0, rows, tid);
     }
   };
@@ -947,6 +993,9 @@ void la_fwd_kernel(FwdArgs a) {
     if (CAUSAL) stage_values<T, D, C, LV>(sv, sV + sc * F::SV, tid);
     if constexpr (SEL)
       if (CAUSAL && w == 0) sel_table<C>(sl.v, stab + sc * F::TAB, lane);
+    if constexpr (RW)
+      if (CAUSAL && w == 0)
+        rw_table<C>(stab + sc * F::TAB, gp, dk.b, rows_of(c), lane);
   };
 
   // The loops below run whole revolutions of their register ring (padding
@@ -967,7 +1016,7 @@ void la_fwd_kernel(FwdArgs a) {
                        LamSlab<C> &sl) {
         const int64_t r0 = start + clamp_chunk(c) * C;
         sk.load(kb, r0, rows_of(c), tid);
-        sv.load(vb, r0, rows_of(c), tid);
+        loadv(sv, r0, rows_of(c));
         if constexpr (SEL) sl.load(lb, r0, rows_of(c), tid);
       };
 #pragma unroll
@@ -998,6 +1047,9 @@ void la_fwd_kernel(FwdArgs a) {
         stage_values<T, D, C, LV>(sv, sV + set_of(c) * F::SV, tid);
         if constexpr (SEL)
           if (w == 0) sel_table<C>(sl.v, stab + set_of(c) * F::TAB, lane);
+        if constexpr (RW)
+          if (w == 0)
+            rw_table<C>(stab + set_of(c) * F::TAB, gp, dk.b, rows_of(c), lane);
       };
       auto features1 = [&](int c) {
         if constexpr (PF) {
@@ -1023,8 +1075,10 @@ void la_fwd_kernel(FwdArgs a) {
           const float *tabc = stab + sc * F::TAB;
           state_update<F>(S, WKEYS ? sKw + sc * F::SQ : keys1(c),
                           sV + sc * F::SV,
-                          WKEYS ? gp[rows_of(c)] : SEL ? tabc[3 * C] : 1.f, w,
-                          g, li, ~0u, tabc + 2 * C);
+                          WKEYS || RW ? gp[rows_of(c)]
+                          : SEL       ? tabc[3 * C]
+                                      : 1.f,
+                          w, g, li, ~0u, tabc + F::WOFF);
           if constexpr (SEL) seg_log2 += tabc[C - 1];
           if (F::NBUF == 1) __syncthreads();
           stage1(c + 1, rk[bn], rv[bn], rl[bn]);
@@ -1041,7 +1095,7 @@ void la_fwd_kernel(FwdArgs a) {
     // eqs 7-8 / 10-11 applied segment by segment, with E the segment start
     // (causal) or n.
     if (a.nseg > 1) {
-      float *ub = a.states + unit * a.nseg * static_cast<int64_t>(F::SLOT);
+      float *ub = a.states + vunit * a.nseg * static_cast<int64_t>(F::SLOT);
       const int need = CAUSAL ? seg : a.nseg;
       // the records as wave 0 read them, for every wave
       unsigned *srec = reinterpret_cast<unsigned *>(gp + C + 2);
@@ -1060,7 +1114,7 @@ void la_fwd_kernel(FwdArgs a) {
             *reinterpret_cast<f32x4 *>(mine + (idx * 64 + lane) * 4) =
                 S[m * F::JPW + mj];
           }
-        if (SEL && tid == 0) a.seg_log[unit * a.nseg + seg] = seg_log2;
+        if (SEL && tid == 0) a.seg_log[vunit * a.nseg + seg] = seg_log2;
         return;
       }
       if (EXCH && (!CAUSAL || seg + 1 < a.nseg)) {
@@ -1080,7 +1134,7 @@ void la_fwd_kernel(FwdArgs a) {
               store_agent(dst, S[m * F::JPW + mj]);
           }
         if (SEL && tid == 0) {  // the segment's sum of log2 gamma, likewise
-          float *dst = a.seg_log + unit * a.nseg + seg;
+          float *dst = a.seg_log + vunit * a.nseg + seg;
           if (local)
             *dst = seg_log2;
           else
@@ -1107,7 +1161,7 @@ void la_fwd_kernel(FwdArgs a) {
         static_assert(kMaxSegments <= kWave, "one segment per lane");
         if (w == 0) {
           const float tj =
-              lane < need ? a.seg_log[unit * a.nseg + lane] : 0.f;
+              lane < need ? a.seg_log[vunit * a.nseg + lane] : 0.f;
           float suf = tj;  // inclusive suffix sum over lanes j .. need - 1
 #pragma unroll
           for (int o = 1; o < kMaxSegments; o <<= 1) {
@@ -1245,7 +1299,7 @@ void la_fwd_kernel(FwdArgs a) {
   // Decay weights b g^(t-s) of this lane's P^T elements (zero for s > t),
   // computed once where the registers allow (one workgroup per CU), else
   // per chunk from the table.
-  constexpr bool PREW = WKEYS && F::OCC == 1;
+  constexpr bool PREW = (WKEYS || RW) && F::OCC == 1;
   float dw[PREW ? 4 * STRIPS : 1];
   if constexpr (PREW) {
 #pragma unroll
@@ -1406,20 +1460,22 @@ void la_fwd_kernel(FwdArgs a) {
       const float rden = __builtin_amdgcn_rcpf(den);
       // training forward: each row's denominator, for the backward pass
       // (the waves with jh == 0 hold every row of their strip once)
-      if (a.den_out && jh == 0 && g == 0 && t < rows)
+      if (a.den_out && part == 0 && jh == 0 && g == 0 && t < rows)
         a.den_out[unit * a.n + start + clamp_chunk(c) * C + t] = den;
       // the chunk's output rows (none for padding chunks); stores of rows
       // past the end and of blocks past the last are dropped
       const __amdgpu_buffer_rsrc_t ro =
-          make_rsrc(ob + (start + clamp_chunk(c) * C) * D,
-                    static_cast<unsigned>(rows) * D * sizeof(T));
+          make_rsrc(ob + (start + clamp_chunk(c) * C) * LDV,
+                    rows > 0 ? static_cast<unsigned>((rows - 1) * LDV + D) *
+                                   sizeof(T)
+                             : 0u);
 #pragma unroll
       for (int jj = 0; jj < NJW; ++jj) {
         const f32x4 o = block(jj) * rden;
         // o[rr]: column j = 16 jb + 4 g + rr of output row t
         const int jb = jh + WPS * jj;
         const unsigned off = NJ % WPS == 0 || jb < NJ
-                                 ? (t * D + 16 * jb + 4 * g) * sizeof(T)
+                                 ? (t * LDV + 16 * jb + 4 * g) * sizeof(T)
                                  : kNoAccess;
         buffer_store4(ro, off, o[0], o[1], o[2], o[3], T{});
       }
@@ -1433,7 +1489,7 @@ void la_fwd_kernel(FwdArgs a) {
         // (also after the last chunk, where the state only matters when it
         // is handed out, and on padding chunks, whose keys are zero)
         const T *sKu = WKEYS ? sKwc : sKc;
-        const float gr = WKEYS ? gp[rows] : SEL ? tabc[3 * C] : 1.f;
+        const float gr = WKEYS || RW ? gp[rows] : SEL ? tabc[3 * C] : 1.f;
         const unsigned kmask = RES && c >= nch ? 0u : ~0u;
         if constexpr (SHARE) {
           // tile (w % NF, tile_jb(w, m)) uses column block vblock(m)
@@ -1444,12 +1500,12 @@ void la_fwd_kernel(FwdArgs a) {
             load_frag_tr44(af[kp], sKu, LQ, 32 * kp, 16 * tile_fb<F>(w, 0), g,
                            li);
             if (RES) frag_mask(af[kp], u32x4{kmask, kmask, kmask, kmask});
-            if constexpr (SEL)  // positions 32 kp + 4 g + e, then + 16
+            if constexpr (SEL || RW)  // positions 32 kp + 4 g + e, then + 16
               frag_scale(af[kp],
-                         *reinterpret_cast<const f32x4 *>(tabc + 2 * C +
+                         *reinterpret_cast<const f32x4 *>(tabc + F::WOFF +
                                                           32 * kp + 4 * g),
                          *reinterpret_cast<const f32x4 *>(
-                             tabc + 2 * C + 32 * kp + 16 + 4 * g));
+                             tabc + F::WOFF + 32 * kp + 16 + 4 * g));
           }
 #pragma unroll
           for (int m = 0; m < F::JPW; ++m) {
@@ -1459,7 +1515,7 @@ void la_fwd_kernel(FwdArgs a) {
             S[m] = acc;
           }
         } else {
-          state_update<F>(S, sKu, sVc, gr, w, g, li, kmask, tabc + 2 * C);
+          state_update<F>(S, sKu, sVc, gr, w, g, li, kmask, tabc + F::WOFF);
         }
       }
       if (F::NBUF == 1) __syncthreads();  // the one tile set is free again
@@ -1477,7 +1533,7 @@ void la_fwd_kernel(FwdArgs a) {
   // fp32: tile (fb, jb) holds rows 16 fb + 4 g + r of columns 16 jb + li,
   // and the ones block's column 0 is nu.
   if (keep_state) {
-    float *mu = a.mu_out + unit * static_cast<int64_t>(DF) * D;
+    float *mu = a.mu_out + unit * static_cast<int64_t>(DF) * LDV + part * D;
     float *nu = a.nu_out + unit * static_cast<int64_t>(DF);
 #pragma unroll
     for (int m = 0; m < F::FPW; ++m)
@@ -1488,8 +1544,8 @@ void la_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int f = 16 * fb + 4 * g + r;
-          if (jb < NJ) mu[static_cast<int64_t>(f) * D + 16 * jb + li] = v[r];
-          else if (jb == NJ && li == 0) nu[f] = v[r];
+          if (jb < NJ) mu[static_cast<int64_t>(f) * LDV + 16 * jb + li] = v[r];
+          else if (jb == NJ && li == 0 && part == 0) nu[f] = v[r];
         }
       }
   }

@@ -9,17 +9,18 @@ namespace la {
 
 // One (storage type, d, d_feat, decay mode, map) instance; DK is the decay
 // mode of FwdShape, MAP the feature map applied to q and k while staging
-// them (kMapFeatures: none).
-template <typename T, int D, int DF, int DK, int MAP>
+// them (kMapFeatures: none).  VS > 1: the value columns are split into VS
+// parts of D columns, each its own set of workgroups.
+template <typename T, int D, int DF, int DK, int MAP, int VS = 1>
 struct FwdVariant {
   using F = FwdShape<T, D, DF, DK, MAP>;
 
   static const void *kernel(bool causal, bool multi) {
     if (causal)
       return multi
-          ? reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, true, true, DK, MAP>)
-          : reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, true, false, DK, MAP>);
-    return reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, false, true, DK, MAP>);
+          ? reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, true, true, DK, MAP, false, 0, VS>)
+          : reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, true, false, DK, MAP, false, 0, VS>);
+    return reinterpret_cast<const void *>(&la_fwd_kernel<T, D, DF, false, true, DK, MAP, false, 0, VS>);
   }
 
   // Non-causal segmented forward as two launches: the aggregates, then the
@@ -27,16 +28,16 @@ struct FwdVariant {
   static const void *kernel_split(int split) {
     return split == 1
         ? reinterpret_cast<const void *>(
-              &la_fwd_kernel<T, D, DF, false, true, DK, MAP, false, 1>)
+              &la_fwd_kernel<T, D, DF, false, true, DK, MAP, false, 1, VS>)
         : reinterpret_cast<const void *>(
-              &la_fwd_kernel<T, D, DF, false, true, DK, MAP, false, 2>);
+              &la_fwd_kernel<T, D, DF, false, true, DK, MAP, false, 2, VS>);
   }
 
   // Resident-key instance (causal, several segments of at most KRES chunks).
   static const void *kernel_res() {
     if constexpr (F::KRES > 0)
       return reinterpret_cast<const void *>(
-          &la_fwd_kernel<T, D, DF, true, true, DK, MAP, true>);
+          &la_fwd_kernel<T, D, DF, true, true, DK, MAP, true, 0, VS>);
     return kernel(true, true);
   }
 
@@ -62,29 +63,30 @@ struct FwdVariant {
                         hipStream_t s) {
     hipError_t e = set_lds();
     if (e != hipSuccess) return e;
-    const dim3 grid(static_cast<unsigned>(units * a.nseg)), block(kThreads);
+    const dim3 grid(static_cast<unsigned>(units * VS * a.nseg)),
+        block(kThreads);
     if (causal) {
       // One segment: no exchange.  Several: segments are numbered in start
       // order, so a plain launch cannot deadlock.
       if (a.nseg == 1) {
-        hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, true, false, DK, MAP>),
+        hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, true, false, DK, MAP, false, 0, VS>),
                            grid, block, F::lds_bytes, s, a);
         return hipGetLastError();
       }
       if constexpr (F::KRES > 0) {
         if (a.seg_len <= static_cast<int64_t>(F::KRES) * F::C) {
           hipLaunchKernelGGL(
-              (la_fwd_kernel<T, D, DF, true, true, DK, MAP, true>), grid,
+              (la_fwd_kernel<T, D, DF, true, true, DK, MAP, true, 0, VS>), grid,
               block, F::lds_bytes, s, a);
           return hipGetLastError();
         }
       }
-      hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, true, true, DK, MAP>),
+      hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, true, true, DK, MAP, false, 0, VS>),
                          grid, block, F::lds_bytes, s, a);
       return hipGetLastError();
     }
     if (a.nseg == 1) {  // non-causal, one segment: no exchange executes
-      hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, false, true, DK, MAP>),
+      hipLaunchKernelGGL((la_fwd_kernel<T, D, DF, false, true, DK, MAP, false, 0, VS>),
                          grid, block, F::lds_bytes, s, a);
       return hipGetLastError();
     }
@@ -93,12 +95,12 @@ struct FwdVariant {
     // readout launch after it on the same stream reads them; no workgroup
     // ever waits for another.
     hipLaunchKernelGGL(
-        (la_fwd_kernel<T, D, DF, false, true, DK, MAP, false, 1>), grid,
+        (la_fwd_kernel<T, D, DF, false, true, DK, MAP, false, 1, VS>), grid,
         block, F::lds_bytes, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(
-        (la_fwd_kernel<T, D, DF, false, true, DK, MAP, false, 2>), grid,
+        (la_fwd_kernel<T, D, DF, false, true, DK, MAP, false, 2, VS>), grid,
         block, F::lds_bytes, s, a);
     return hipGetLastError();
   }
@@ -106,29 +108,35 @@ struct FwdVariant {
 
 // Launch set of one (storage type, d, d_feat): PERF selects the instances
 // with the Performer map fused, else the ones for features or elu + 1.
+// Where no instance of the full value width fits LDS (fp32 storage, d = 128,
+// d' = 256: the fp32 S^T copy alone is 147 KiB) the value columns are split
+// in two halves (VS = 2), each its own computation over all of q', k'.
 template <typename T, int D, int DF, bool PERF = false>
 struct FwdRunner {
   static constexpr int MAP0 = PERF ? kMapPerformer : kMapFeatures;
-  using P = FwdShape<T, D, DF, 0, MAP0>;  // no decay
-  using Q = FwdShape<T, D, DF, 1, MAP0>;  // one decay per head
-  using R = FwdShape<T, D, DF, 2, MAP0>;  // a decay per position
+  static constexpr int VS =
+      !PERF && !FwdShape<T, D, DF, 0, MAP0>::fits && D >= 32 ? 2 : 1;
+  static constexpr int DP = D / VS;       // value columns per part
+  using P = FwdShape<T, DP, DF, 0, MAP0>;  // no decay
+  using Q = FwdShape<T, DP, DF, 1, MAP0>;  // one decay per head
+  using R = FwdShape<T, DP, DF, 2, MAP0>;  // a decay per position
 
   template <int MAP>
   static hipError_t run_map(const FwdArgs &a, int64_t units, int causal,
                             hipStream_t s) {
     if (a.log_decay) {
       if constexpr (R::fits)
-        return FwdVariant<T, D, DF, 2, MAP>::run(a, units, causal, s);
+        return FwdVariant<T, DP, DF, 2, MAP, VS>::run(a, units, causal, s);
       else
         return hipErrorInvalidValue;
     }
     if (a.decay) {
       if constexpr (Q::fits)
-        return FwdVariant<T, D, DF, 1, MAP>::run(a, units, causal, s);
+        return FwdVariant<T, DP, DF, 1, MAP, VS>::run(a, units, causal, s);
       else
         return hipErrorInvalidValue;
     }
-    return FwdVariant<T, D, DF, 0, MAP>::run(a, units, causal, s);
+    return FwdVariant<T, DP, DF, 0, MAP, VS>::run(a, units, causal, s);
   }
 
   // elu + 1 instances exist only for d_feat == d (the map keeps the width).
@@ -155,7 +163,7 @@ struct FwdRunner {
       // chunks of the decayed variants too
       static_assert(!Q::fits || P::C % Q::C == 0, "chunk lengths compatible");
       static_assert(!R::fits || P::C % R::C == 0, "chunk lengths compatible");
-      static const FwdOps o = {P::C, P::SLOT, Q::fits, R::fits, &run};
+      static const FwdOps o = {P::C, P::SLOT, Q::fits, R::fits, VS, &run};
       return &o;
     }
   }

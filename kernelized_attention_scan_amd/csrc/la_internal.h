@@ -81,6 +81,7 @@ struct FwdOps {
   int slot_floats;    // floats per fp32 state slot
   bool decay_ok;      // the decayed variant fits in LDS too
   bool sel_ok;        // the per-position decay variant fits in LDS too
+  int vsplit;         // computations per unit (value column parts), 1 or 2
   // Enqueue the fused forward.
   hipError_t (*run)(const FwdArgs &args, int64_t units, int causal,
                     hipStream_t stream);

@@ -82,6 +82,9 @@ GRID = [
     ("identity_df128_d64", 1, 2, 600, 64, "identity", 128, True, GATE),
     ("performer_m256", 1, 2, 900, 64, "performer", 256, True, GATE),
     ("performer_d32_m64", 1, 2, 400, 32, "performer", 64, True, GATE),
+    ("identity_df256_d128", 1, 2, 500, 128, "identity", 256, True, GATE),
+    ("identity_df256_d128_noncausal", 1, 1, 300, 128, "identity", 256, False,
+     GATE),
 ]
 
 

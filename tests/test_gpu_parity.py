@@ -118,6 +118,15 @@ GRID = [
     ("identity_df128_d64", 1, 2, 600, 64, "identity", 128, False, True),
     ("identity_df16_d128", 1, 1, 300, 128, "identity", 16, True, True),
     ("identity_df256_d128", 1, 1, 200, 128, "identity", 256, False, True),
+    # fp32 storage: value columns split in halves (d = 128, d' = 256), and
+    # the decay weights of the state update taken in registers (d' = 256)
+    ("identity_df256_d128_decay_segmented", 1, 2, 700, 128, "identity", 256,
+     True, True),
+    ("identity_df256_d128_noncausal", 1, 2, 300, 128, "identity", 256, True,
+     False),
+    ("identity_df256_d64_decay", 2, 2, 650, 64, "identity", 256, True, True),
+    ("performer_d128_m256_decay", 1, 1, 400, 128, "performer", 256, True,
+     True),
     ("performer_m256", 1, 2, 900, 64, "performer", 256, False, True),
     ("performer_m64_decay", 1, 2, 400, 32, "performer", 64, True, True),
     ("performer_noncausal", 1, 1, 300, 64, "performer", 128, False, False),
@@ -519,6 +528,11 @@ STATE_CASES = {
                                             decay=(-2.0, -1.0)),
     "one_chunk": I.ELU1_CAUSAL.replace(B=1, H=3, n=40),
     "noncausal": I.ELU1_CAUSAL.replace(B=1, H=2, n=500, causal=False),
+    # fp32, d = 128, d' = 256: two value halves each hand out their columns
+    "fp32_split_values_df256": I.PrefillConfig(
+        "fp32_split_values_df256", B=1, H=2, n=450, d=128,
+        dtype=torch.float32, mapk=I.MAP_PERFORMER, m=256, qk_std=0.5,
+        decay=(-2.0, -1.0)),
 }
 
 

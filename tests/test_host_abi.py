@@ -126,9 +126,12 @@ def test_workspace_bytes(lib):
     f32 = __import__("torch").float32
     assert K.forward_workspace_bytes(1, 2, 17, 32, 128, "performer",
                                      dtype=f32) == sync + 2 * a256(2 * 17 * 128 * 4)
-    # fp32 storage with d_feat 256 and d 128 does not fit in LDS
-    assert K.forward_workspace_bytes(1, 1, 64, 128, 256, "identity",
-                                     dtype=__import__("torch").float32) == 0
+    # fp32 storage with d_feat 256 and d 128 splits the value columns in two
+    # halves of 64, each its own computation with its own segments: 64 rows
+    # = 2 chunks of 32 -> 2 segments per half, aggregates of 256 x (64 + 16)
+    wv = K.forward_workspace_bytes(1, 1, 64, 128, 256, "identity",
+                                   dtype=__import__("torch").float32)
+    assert wv == sync + a256(2 * 2 * 256 * 80 * 4) + a256(2 * 2 * 4)
 
 
 @pytest.mark.parametrize("B,H,n", [(1, 1, 1), (1, 2, 17), (2, 3, 64),
