@@ -22,8 +22,8 @@ fp64 CPU oracle timed on the host cores over a bounded sample.
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
+import re
 import json
 import math
 import os
@@ -441,6 +441,9 @@ def main() -> int:
     ap.add_argument("--workload", default="decayed",
                     choices=sorted(workloads()))
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--n", type=int, default=0,
+                    help="sequence length other than the workload's own "
+                         "(prefill workloads; for length sweeps)")
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="untimed steps for this long before the warmup "
                          "steps, so clocks reach their sustained level")
@@ -479,6 +482,12 @@ def main() -> int:
         return 0
     K.load_library()
     cfg = workloads()[args.workload]
+    if args.n:
+        if args.workload == "decode":
+            print("--n applies to prefill workloads only", file=sys.stderr)
+            return 2
+        cfg = cfg.replace(n=args.n,
+                          name=re.sub(r"n\d+", f"n{args.n}", cfg.name, count=1))
     is_decode = args.workload == "decode"
     is_bwd = args.workload == "backward"
     leg = (decode_leg if is_decode else backward_leg if is_bwd
