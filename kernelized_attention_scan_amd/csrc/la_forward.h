@@ -122,19 +122,21 @@ constexpr int kMapElu = 1;        // elu + 1 (d' = d)
 constexpr int kMapPerformer = 2;  // Performer random features, fused
 
 // LDS bytes of one instance with chunk length c (see FwdShape): nbuf sets of
-// the q', w.k' (wkeys), V and S^T tiles, kslots slots of k', the raw q, k
-// rows of the fused Performer map, and per set a table of tab floats (the
-// chunk's decay weights, where the instance keeps one).
+// the q', w.k' (wkeys) and V tiles, nst S^T copies (0: one per set), kslots
+// slots of k', the raw q, k rows of the fused Performer map, and per set a
+// table of tab floats (the chunk's decay weights, where the instance keeps
+// one).
 template <typename T>
 constexpr size_t fwd_lds_bytes(int c, int d, int df, bool wkeys, bool pf,
-                               int kslots = 1, int nbuf = 1, int tab = 0) {
+                               int kslots = 1, int nbuf = 1, int tab = 0,
+                               int nst = 0) {
   const int dfp = df < 32 ? 32 : df;
   const size_t sq = static_cast<size_t>(c) * lds_stride<T>(dfp);
   const size_t sv = static_cast<size_t>(c) * lds_stride<T>(d + 16);
   const size_t sst = static_cast<size_t>(d + 16) * lds_stride<T>(dfp);
   const size_t sx = pf ? static_cast<size_t>(c) * lds_stride<T>(d) : 0;
-  return sizeof(T) * (nbuf * (sq + (wkeys ? sq : 0) + sv + sst) +
-                      kslots * sq + 2 * sx) +
+  return sizeof(T) * (nbuf * (sq + (wkeys ? sq : 0) + sv) +
+                      (nst > 0 ? nst : nbuf) * sst + kslots * sq + 2 * sx) +
          sizeof(float) * (c + 8 + kMaxSegments + (pf ? 2 * c : 0) + nbuf * tab);
 }
 
@@ -160,16 +162,11 @@ struct FwdShape {
                 ? 64
                 : 32)
          : ((sizeof(T) == 2 && !(DF == 256 && D == 128)) ? 64 : 32);
-  // One decay per head: the state update reads a staged tile of weighted
-  // keys (WKEYS) where LDS holds one; else (RW) it weights the key
-  // fragments in registers from a per-chunk table, as per-position decay
-  // does.
-  static constexpr bool WKEYS =
-      DK == 1 && (PF || fwd_lds_bytes<T>(C, D, DF, true, false) <= kMaxLds);
-  static constexpr bool RW = DK == 1 && !WKEYS;
-  // Floats of one tile set's table: per-position decay, see sel_table; RW,
-  // the state-update weight of each key.  WOFF: where those weights start.
-  static constexpr int TAB = SEL ? 3 * C + 4 : RW ? C : 0;
+  // Floats of one tile set's table: per-position decay, see sel_table; one
+  // decay per head with register weights (RW, below), the state-update
+  // weight of each key.  WOFF: where those weights start.
+  static constexpr int TABW = SEL ? 3 * C + 4 : 0;
+  static constexpr int TABR = SEL ? 3 * C + 4 : DK == 1 ? C : 0;
   static constexpr int WOFF = SEL ? 2 * C : 0;
   static constexpr int DFP = DF < 32 ? 32 : DF;      // padded k-width of q', k'
   static constexpr int LQ = lds_stride<T>(DFP);      // sQ, sK, sKw, sST
@@ -184,8 +181,8 @@ struct FwdShape {
   static constexpr int FPW = NF >= kWaves ? NF / kWaves : 1;
   static constexpr int WPF = NF >= kWaves ? 1 : kWaves / NF;
   static constexpr int JPW = (NJA + WPF - 1) / WPF;
-  static constexpr int SQ = C * LQ, SKW = WKEYS ? C * LQ : 0, SV = C * LV,
-                       SST = (D + 16) * LQ, SX = PF ? C * LX : 0;
+  static constexpr int SQ = C * LQ, SV = C * LV, SST = (D + 16) * LQ,
+                       SX = PF ? C * LX : 0;
   // Fused Performer projection: omega^T tiles per wave (kept in registers
   // for the whole kernel) and the strips each wave maps.  NF >= 8: wave w
   // owns feature tiles w + 8 m for every strip; else tile w % NF for strips
@@ -193,9 +190,12 @@ struct FwdShape {
   static constexpr int TPW = NF >= kWaves ? NF / kWaves : 1;
   static constexpr int WPT = NF >= kWaves ? 1 : kWaves / NF;
   static constexpr int SPW = (STRIPS + WPT - 1) / WPT;
-  // Software pipelining (both loops): two sets of operand tiles and of the
-  // S^T copy, so that chunk c + 1 is mapped and staged while chunk c is
-  // multiplied, with one barrier per chunk; where LDS holds the second set.
+  // Software pipelining (both loops): two sets of operand tiles, so that
+  // chunk c + 1 is mapped and staged while chunk c is multiplied; where LDS
+  // holds the second set.  With two S^T copies as well the chunk loop has
+  // one barrier; with one (NST = 1, where only that fits) the state is
+  // published between two barriers, and the staging still overlaps the
+  // matrix work.
   // Resident keys (bf16, no decay, d, d' <= 64): phase 1 keeps phi(K) of each
   // chunk of a short segment (at most KRES_ chunks) in its own slot of sK and
   // phase 2 reuses it instead of loading and mapping K again.
@@ -203,16 +203,40 @@ struct FwdShape {
       !PF && !DECAY && sizeof(T) == 2 && D <= 64 && DF <= 64;
   static constexpr int KRES_ =
       !RES_OK ? 0
-      : fwd_lds_bytes<T>(C, D, DF, WKEYS, PF, 8, 2, TAB) <= kMaxLds ? 8
-      : fwd_lds_bytes<T>(C, D, DF, WKEYS, PF, 4, 2, TAB) <= kMaxLds ? 4
-                                                                : 0;
+      : fwd_lds_bytes<T>(C, D, DF, false, PF, 8, 2) <= kMaxLds ? 8
+      : fwd_lds_bytes<T>(C, D, DF, false, PF, 4, 2) <= kMaxLds ? 4
+                                                           : 0;
   static constexpr int KS2 = KRES_ > 2 ? KRES_ : 2;
-  static constexpr bool PIPE =
-      !PF && fwd_lds_bytes<T>(C, D, DF, WKEYS, PF, KS2, 2, TAB) <= kMaxLds;
+  // candidate layouts: pipelined with a weighted key tile (one decay per
+  // head), pipelined without one, with one or two S^T copies
+  static constexpr bool PIPE_W =
+      !PF && DK == 1 &&
+      fwd_lds_bytes<T>(C, D, DF, true, PF, KS2, 2, TABW) <= kMaxLds;
+  static constexpr bool PIPE_R2 =
+      !PF && fwd_lds_bytes<T>(C, D, DF, false, PF, KS2, 2, TABR) <= kMaxLds;
+  // (not with per-position decay: its chunk loop measured 1 % slower so at
+  // d = d' = 128)
+  static constexpr bool PIPE_R1 =
+      !PF && !SEL &&
+      fwd_lds_bytes<T>(C, D, DF, false, PF, KS2, 2, TABR, 1) <= kMaxLds;
+  // One decay per head: the state update reads a staged tile of weighted
+  // keys (WKEYS) where that layout is pipelined, or where nothing is and
+  // LDS holds the tile; else (RW) it weights the key fragments in registers
+  // from a per-chunk table, as per-position decay does.
+  static constexpr bool WKEYS =
+      DK == 1 && (PF || PIPE_W ||
+                  (!PIPE_R2 && !PIPE_R1 &&
+                   fwd_lds_bytes<T>(C, D, DF, true, false, 1, 1, TABW) <=
+                       kMaxLds));
+  static constexpr bool RW = DK == 1 && !WKEYS;
+  static constexpr int SKW = WKEYS ? C * LQ : 0;
+  static constexpr int TAB = WKEYS ? TABW : TABR;
+  static constexpr bool PIPE = WKEYS ? PIPE_W : (PIPE_R2 || PIPE_R1);
   static constexpr int NBUF = PIPE ? 2 : 1;                 // sets of tiles
+  static constexpr int NST = PIPE && (WKEYS || PIPE_R2) ? 2 : 1;  // S^T copies
   static constexpr int KS = PIPE ? KS2 : 1;                 // slots of sK
   static constexpr size_t lds_bytes =
-      fwd_lds_bytes<T>(C, D, DF, WKEYS, PF, KS, NBUF, TAB);
+      fwd_lds_bytes<T>(C, D, DF, WKEYS, PF, KS, NBUF, TAB, NST);
   // fp32 state slot: NTILE tiles x 64 lanes x 4 (accumulator order).
   static constexpr int SLOT = NTILE * 256;
   // Workgroups per compute unit the instance is built for: two (<= 128
@@ -791,7 +815,7 @@ void la_fwd_kernel(FwdArgs a) {
   T *sKw = WKEYS ? sK + F::SQ * F::KS : sK;
   T *sV = sK + F::SQ * F::KS + F::NBUF * F::SKW;
   T *sST = sV + F::NBUF * F::SV;
-  T *sXq = sST + F::NBUF * F::SST;  // raw q, k rows (fused Performer)
+  T *sXq = sST + F::NST * F::SST;  // raw q, k rows (fused Performer)
   T *sXk = sXq + F::SX;
   float *gp = reinterpret_cast<float *>(sXk + F::SX);
   // fused Performer: the exponent offsets of the chunk's q rows, then of its
@@ -898,7 +922,7 @@ void la_fwd_kernel(FwdArgs a) {
       const int slot = i / (C * NP), row = (i / NP) % C, col = DF + i % NP;
       sQ[slot * F::SQ + row * LQ + col] = from_f32<T>(0.f);  // sK follows sQ
     }
-    for (int i = tid; i < F::NBUF * (D + 16) * NP; i += kThreads) {
+    for (int i = tid; i < F::NST * (D + 16) * NP; i += kThreads) {
       const int row = (i / NP) % (D + 16);
       sST[(i / ((D + 16) * NP)) * F::SST + row * LQ +
           sst_col<T>(row, DF + i % NP)] = from_f32<T>(0.f);
@@ -1328,7 +1352,7 @@ void la_fwd_kernel(FwdArgs a) {
                               : sK + sc * F::SQ;
       const T *sKwc = sKw + sc * F::SQ;
       const T *sVc = sV + sc * F::SV;
-      const T *sSTc = CAUSAL ? sST + sc * F::SST : sST;
+      const T *sSTc = CAUSAL && F::NST == 2 ? sST + sc * F::SST : sST;
       // per-position decay: this chunk's table, and row t's log2 decay
       const float *tabc = stab + sc * F::TAB;
       float Lt = 0.f;
@@ -1522,7 +1546,16 @@ void la_fwd_kernel(FwdArgs a) {
       // ---- chunk c + 1 into its set; its ring slot reloaded ----
       stage2(c + 1, rq[bn], rk2[bn], rv2[bn], rl2[bn]);
       load2(c + 1 + NB2, rq[bn], rk2[bn], rv2[bn], rl2[bn]);
-      if (CAUSAL) publish_state<F>(S, sST + sn * F::SST, w, g, li);
+      if constexpr (F::NBUF == 2 && F::NST == 1) {
+        // one S^T copy: every wave has read it for chunk c before the state
+        // after chunk c replaces it
+        if (CAUSAL) {
+          __syncthreads();
+          publish_state<F>(S, sST, w, g, li);
+        }
+      } else {
+        if (CAUSAL) publish_state<F>(S, sST + sn * F::SST, w, g, li);
+      }
       __syncthreads();
       features2(c + 1);
     }

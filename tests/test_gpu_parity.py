@@ -117,6 +117,12 @@ GRID = [
     ("noncausal_decay", 1, 3, 300, 32, "elu1", 0, True, False),
     ("identity_df128_d64", 1, 2, 600, 64, "identity", 128, False, True),
     ("identity_df16_d128", 1, 1, 300, 128, "identity", 16, True, True),
+    # layouts chosen by LDS: two tile sets with one S^T copy (d = 128,
+    # d' = 128 bf16; d = 64, d' = 128 fp32) and register-weighted keys
+    ("elu1_d128_nodecay", 1, 2, 1500, 128, "elu1", 0, False, True),
+    ("elu1_d128_noncausal_decay", 1, 2, 700, 128, "elu1", 0, True, False),
+    ("identity_df128_d64_decay", 1, 2, 600, 64, "identity", 128, True, True),
+    ("identity_df64_d128_decay", 1, 2, 500, 128, "identity", 64, True, True),
     ("identity_df256_d128", 1, 1, 200, 128, "identity", 256, False, True),
     # fp32 storage: value columns split in halves (d = 128, d' = 256), and
     # the decay weights of the state update taken in registers (d' = 256)
