@@ -211,13 +211,27 @@ la_status la_forward_train(const void *q, const void *k, const void *v,
  *   map   : LA_MAP_ELU1 or LA_MAP_IDENTITY (LA_MAP_PERFORMER:
  *           LA_ERR_UNSUPPORTED); omega is ignored
  *   decay : device fp32 [H] or NULL, as la_forward
- *   Supported: d == d_feat in {16, 32, 64, 128}.  No workspace.
+ *   workspace: device, at least la_backward_workspace_bytes(...) bytes, no
+ *           initial contents needed; LA_ERR_WORKSPACE if NULL.  Calls that
+ *           share one workspace must be ordered (one stream).
+ *   Supported: d == d_feat in {16, 32, 64, 128}.
  */
 la_status la_backward(const void *q, const void *k, const void *v,
                       const void *out, const float *den, const void *dout,
                       void *dq, void *dk, void *dv, int B, int H, int64_t n,
                       int d, int d_feat, la_map map, const float *omega,
-                      const float *decay, la_dtype dtype, void *stream);
+                      const float *decay, la_dtype dtype, void *workspace,
+                      void *stream);
+
+/*
+ * la_backward_workspace_bytes -- device workspace la_backward needs for
+ * these sizes: per row, the prepared G row (d + 2 values padded to a
+ * multiple of 32) and, for LA_MAP_ELU1, the features phi(k) and phi(q), all
+ * in dtype.  Pure host function; 0 for arguments la_backward would reject
+ * and for empty sizes.
+ */
+size_t la_backward_workspace_bytes(int B, int H, int64_t n, int d, int d_feat,
+                                   la_map map, la_dtype dtype);
 
 /*
  * la_forward_gated -- la_forward / la_forward_state with a decay that

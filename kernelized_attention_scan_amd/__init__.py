@@ -7,14 +7,16 @@ The computation runs in hand-written HIP kernels behind the C ABI of
 """
 from ._binding import (LA_BF16, LA_F32, LIB_PATH, MAP_ELU1, MAP_IDENTITY,
                        MAP_PERFORMER, SYMBOLS, LinAttnError, cached_workspace,
-                       backward, decode_step, decode_step_gated, featmap,
+                       backward, backward_workspace_bytes, decode_step,
+                       decode_step_gated, featmap,
                        forward, forward_train,
                        forward_gated, forward_noalloc,
                        forward_workspace_bytes,
                        load_library, new_workspace, set_exchange_spin_limit,
                        workspace_check)
 
-__all__ = ["forward", "forward_train", "backward", "forward_gated", "forward_noalloc", "decode_step",
+__all__ = ["forward", "forward_train", "backward", "backward_workspace_bytes",
+           "forward_gated", "forward_noalloc", "decode_step",
            "decode_step_gated", "featmap", "forward_workspace_bytes",
            "new_workspace", "workspace_check", "cached_workspace",
            "set_exchange_spin_limit",

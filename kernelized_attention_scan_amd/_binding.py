@@ -30,6 +30,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
 # Exported symbols, in the order include/linattn.h declares them.
 SYMBOLS = ("la_featmap", "la_forward_workspace_bytes", "la_forward",
            "la_forward_state", "la_forward_train", "la_backward",
+           "la_backward_workspace_bytes",
            "la_forward_gated", "la_forward_noalloc",
            "la_decode_step", "la_decode_step_gated", "la_workspace_check",
            "la_set_exchange_spin_limit", "la_status_str", "la_last_error")
@@ -78,8 +79,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                          i32, i32, i32, vp, vp, i32, vp, vp]
         lib.la_forward_train.restype = i32
         lib.la_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32,
-                                    i32, i64, i32, i32, i32, vp, vp, i32, vp]
+                                    i32, i64, i32, i32, i32, vp, vp, i32, vp,
+                                    vp]
         lib.la_backward.restype = i32
+        lib.la_backward_workspace_bytes.argtypes = [i32, i32, i64, i32, i32,
+                                                    i32, i32]
+        lib.la_backward_workspace_bytes.restype = sz
         lib.la_forward_gated.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32,
                                          i32, i32, vp, vp, i32, i32, i32, vp,
                                          vp, vp, vp]
@@ -587,14 +592,31 @@ def forward_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return out, den
 
 
+def backward_workspace_bytes(B: int, H: int, n: int, d: int,
+                             feature_map="elu1",
+                             dtype: torch.dtype = torch.bfloat16) -> int:
+    """Device workspace la_backward needs (la_backward_workspace_bytes)."""
+    return int(load_library().la_backward_workspace_bytes(
+        B, H, n, d, d, _map_code(feature_map), _dtype_code(dtype)))
+
+
+# backward()'s workspaces when none is passed: one per (device, stream),
+# grown as needed (no initial contents are needed)
+_bwd_workspaces = {}
+
+
 def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
              out: torch.Tensor, den: torch.Tensor, dout: torch.Tensor,
              feature_map="elu1", decay: Optional[torch.Tensor] = None,
              dq: Optional[torch.Tensor] = None,
              dk: Optional[torch.Tensor] = None,
-             dv: Optional[torch.Tensor] = None):
+             dv: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None):
     """Gradients (dq, dk, dv) of sum(out * dout) for the causal forward
-    (la_backward); out and den as forward_train() returned them."""
+    (la_backward); out and den as forward_train() returned them.
+    workspace: optional uint8 device tensor of at least
+    backward_workspace_bytes(...) bytes; by default one cached per (device,
+    stream) is used."""
     lib = load_library()
     if q.dim() != 4 or v.dim() != 4 or q.shape != k.shape:
         raise ValueError("q, k must be [B,H,n,d] and v [B,H,n,d]")
@@ -614,14 +636,27 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     for t, nm in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
         if t is not None:
             _check_out(t, v.shape, v.dtype)
+    need = int(lib.la_backward_workspace_bytes(B, H, n, d, d, mapk, dt))
+    if workspace is not None and (workspace.dtype != torch.uint8
+                                  or not workspace.is_contiguous()
+                                  or workspace.numel() < need):
+        raise ValueError(f"workspace must be a contiguous uint8 tensor of "
+                         f"at least {need} bytes")
     _on_gpu(v, (q, "q"), (k, "k"), (v, "v"), (out, "out"), (den, "den"),
             (dout, "dout"), (decay, "decay"), (dq, "dq"), (dk, "dk"),
-            (dv, "dv"))
+            (dv, "dv"), (workspace, "workspace"))
+    if workspace is None and need > 0:
+        key = (v.device.index, torch.cuda.current_stream(v.device).cuda_stream)
+        workspace = _bwd_workspaces.get(key)
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=v.device)
+            _bwd_workspaces[key] = workspace
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     st = lib.la_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(den),
                          _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, H, n, d,
-                         d, mapk, None, _ptr(decay), dt, _stream(v.device))
+                         d, mapk, None, _ptr(decay), dt, _ptr(workspace),
+                         _stream(v.device))
     _check(st, "la_backward")
     return dq, dk, dv

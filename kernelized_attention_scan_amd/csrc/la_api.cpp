@@ -470,11 +470,35 @@ la_status la_forward_train(const void *q, const void *k, const void *v,
                       den);
 }
 
+namespace {
+// Workspace of la_backward: G~ rows, then (elu + 1) K' and Q'.
+size_t backward_ws(int64_t units, int64_t n, int d, int map, int dtype,
+                   size_t *kf_off) {
+  const size_t es = elem_size(dtype);
+  const size_t g = align256(static_cast<size_t>(units * n) *
+                            la::backward_gwidth(d) * es);
+  const size_t f = align256(static_cast<size_t>(units * n) * d * es);
+  if (kf_off) *kf_off = g;
+  return g + (map == LA_MAP_ELU1 ? 2 * f : 0);
+}
+}  // namespace
+
+size_t la_backward_workspace_bytes(int B, int H, int64_t n, int d, int d_feat,
+                                   la_map map, la_dtype dtype) {
+  if (B <= 0 || H <= 0 || n <= 0 || !valid_dtype(dtype) || !valid_map(map) ||
+      map == LA_MAP_PERFORMER || !la::backward_supported(d, d_feat))
+    return 0;
+  const int64_t units = static_cast<int64_t>(B) * H;
+  if (units * n > (int64_t{1} << 46) || units > (int64_t{1} << 26)) return 0;
+  return backward_ws(units, n, d, map, dtype, nullptr);
+}
+
 la_status la_backward(const void *q, const void *k, const void *v,
                       const void *out, const float *den, const void *dout,
                       void *dq, void *dk, void *dv, int B, int H, int64_t n,
                       int d, int d_feat, la_map map, const float *omega,
-                      const float *decay, la_dtype dtype, void *stream) {
+                      const float *decay, la_dtype dtype, void *workspace,
+                      void *stream) {
   try {
     (void)omega;
     if (B < 0 || H < 0 || n < 0)
@@ -499,6 +523,13 @@ la_status la_backward(const void *q, const void *k, const void *v,
       return fail(LA_ERR_UNSUPPORTED, "sizes too large");
     if (!q || !k || !v || !out || !den || !dout || !dq || !dk || !dv)
       return fail(LA_ERR_INVALID_ARG, "null pointer argument");
+    if (!workspace)
+      return fail(LA_ERR_WORKSPACE, "la_backward: workspace of %zu bytes required",
+                  backward_ws(units, n, d, map, dtype, nullptr));
+    size_t kf_off = 0;
+    const size_t fbytes = align256(static_cast<size_t>(units * n) * d *
+                                   elem_size(dtype));
+    backward_ws(units, n, d, map, dtype, &kf_off);
     la::BwdArgs a;
     a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.den = den;
     a.dq = dq; a.dk = dk; a.dv = dv;
@@ -507,6 +538,10 @@ la_status la_backward(const void *q, const void *k, const void *v,
     a.n = n;
     a.dqk = d;
     a.elu1 = map == LA_MAP_ELU1;
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    a.gt = ws;
+    a.kf = a.elu1 ? ws + kf_off : const_cast<void *>(k);
+    a.qf = a.elu1 ? ws + kf_off + fbytes : const_cast<void *>(q);
     const hipError_t e = la::launch_backward(a, units, d, dtype,
                                              static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "la_backward launch");

@@ -25,15 +25,21 @@
 // take the chunks from the last to the first and the rows of each chunk
 // in reverse, so the same formulas read the sequence backwards.
 //
+// A preparation pass first writes, once per row, the operands every role
+// shares: G~ (G padded to a multiple of 32 columns, its last value as the
+// hi + lo pair), and for elu + 1 the features K' and Q'.  The role kernels
+// then only copy tiles.
+//
 // Parallelism: one 256-thread workgroup (4 waves) per (unit, role, block
 // of 16 output columns), each walking its unit's whole sequence, all in one
 // launch.  The roles and blocks of a unit are independent, so no segment
 // exchange is needed: B H (2 d'/16 + d/16) workgroups (768 at B H = 32,
 // d = 128), about 53 KB of LDS each, so three share a compute unit.
 // Every workgroup recomputes the scores of its role (the price of
-// independence); the raw rows it shares with the unit's other workgroups
-// come mostly from L2.
+// independence); the rows it shares with the unit's other workgroups come
+// mostly from L2.
 #include <algorithm>
+#include <type_traits>
 
 #include "la_device.h"
 #include "la_internal.h"
@@ -94,20 +100,6 @@ struct BSlab {
             r, static_cast<unsigned>(((p / PPR) * LD + col0 +
                                       (p % PPR) * VEC) * sizeof(T)));
     }
-  }
-};
-
-// The chunk's denominators, one per row: lane l of every wave holds row
-// l's (each wave reads them through a lane shuffle).
-struct BDen {
-  float v;
-  __device__ __forceinline__ void load(const float *base, int64_t row0,
-                                       int rows, int lane) {
-    static_assert(kBC == kWave, "one row per lane");
-    const __amdgpu_buffer_rsrc_t r =
-        make_rsrc(base + row0, static_cast<unsigned>(rows) * 4u);
-    v = __builtin_bit_cast(
-        float, __builtin_amdgcn_raw_buffer_load_b32(r, 4u * lane, 0, 0));
   }
 };
 
@@ -180,16 +172,18 @@ __device__ __forceinline__ void bwd_role(const BwdArgs &a, int64_t unit,
   const T *qb = static_cast<const T *>(a.q) + unit * n * D;
   const T *kb = static_cast<const T *>(a.k) + unit * n * D;
   const T *vb = static_cast<const T *>(a.v) + unit * n * D;
-  const T *ob = static_cast<const T *>(a.out) + unit * n * D;
-  const T *gb = static_cast<const T *>(a.dout) + unit * n * D;
-  const float *db = a.den + unit * n;
+  constexpr int KG = backward_gwidth(D);  // G~ row width
+  const T *gtb = static_cast<const T *>(a.gt) + unit * n * KG;
+  const T *kfb = static_cast<const T *>(a.kf) + unit * n * D;
+  const T *qfb = static_cast<const T *>(a.qf) + unit * n * D;
   T *res = static_cast<T *>(ROLE == kRoleDQ ? a.dq
                             : ROLE == kRoleDK ? a.dk
                                               : a.dv) +
            unit * n * D;
 
   // Constant parts: the padding columns of X and Y past the data (zero for
-  // every row; the V+ column d is written per chunk).
+  // every row; G~ rows are copied whole, the ones columns of V+ are written
+  // per chunk).
   constexpr int XW = GV ? D + 2 : D;  // written columns of X, Y
   for (int i = tid; i < C * (KX - XW); i += kBThreads) {
     const int row = i / (KX - XW), col = XW + i % (KX - XW);
@@ -209,25 +203,36 @@ __device__ __forceinline__ void bwd_role(const BwdArgs &a, int64_t unit,
     return c >= nch ? 0 : static_cast<int64_t>(chunk_of(c)) * C;
   };
 
-  // Register ring (one chunk ahead).  GV roles: dout, out, v full rows;
-  // the k block (dq) or q block (dk).  dv: k, q full rows; the dout block.
-  BSlab<T, D, D> r1, r2, r3;   // GV: dout, out, v   dv: k, q, (unused)
-  BSlab<T, 16, D> rb1;         // GV: k or q block   dv: dout block
-  BDen rd;
+  // Register ring (one chunk ahead).  GV roles: G~ and v full rows, the
+  // K' block (dq) or Q' block (dk).  dv: K', Q' full rows, the G~ block.
+  BSlab<T, KG, KG> rg;         // GV: G~
+  BSlab<T, D, D> r1, r2;       // GV: v (r1)   dv: K' (r1), Q' (r2)
+  BSlab<T, 16, D> rz;          // GV: K' or Q' block
+  BSlab<T, 16, KG> rzg;        // dv: G~ block
   auto load = [&](int c) {
     const int64_t r0 = row0_of(c);
     const int rows = rows_of(c);
     if constexpr (GV) {
-      r1.load(gb, r0, rows, 0, tid);
-      r2.load(ob, r0, rows, 0, tid);
-      r3.load(vb, r0, rows, 0, tid);
-      rb1.load(ROLE == kRoleDQ ? kb : qb, r0, rows, col0, tid);
+      rg.load(gtb, r0, rows, 0, tid);
+      r1.load(vb, r0, rows, 0, tid);
+      rz.load(ROLE == kRoleDQ ? kfb : qfb, r0, rows, col0, tid);
     } else {
-      r1.load(kb, r0, rows, 0, tid);
-      r2.load(qb, r0, rows, 0, tid);
-      rb1.load(gb, r0, rows, col0, tid);
+      r1.load(kfb, r0, rows, 0, tid);
+      r2.load(qfb, r0, rows, 0, tid);
+      rzg.load(gtb, r0, rows, col0, tid);
     }
-    rd.load(db, r0, rows, lane);
+  };
+  // Copy a slab's pieces into a tile of row stride L (rows in processing
+  // order; pieces of rows past the end are zero).
+  auto put = [&](const auto &sl, T *dst, int L, auto trow) {
+    using S = std::remove_cv_t<std::remove_reference_t<decltype(sl)>>;
+#pragma unroll
+    for (int i = 0; i < S::PER; ++i) {
+      const int p = tid + kBThreads * i;
+      if (S::EXACT || p < S::PIECES)
+        *reinterpret_cast<u32x4 *>(dst + trow(p / S::PPR) * L +
+                                   (p % S::PPR) * VEC) = sl.v[i];
+    }
   };
 
   // Staging of processing step c (rows in processing order: raw row r of a
@@ -236,102 +241,25 @@ __device__ __forceinline__ void bwd_role(const BwdArgs &a, int64_t unit,
     const int rows = rows_of(c);
     auto trow = [&](int r) { return REV && r < rows ? rows - 1 - r : r; };
     if constexpr (GV) {
-      // G = [dout / den | -(dout . out) / den]; V+ = [v | 1]
+      // G~ as it is; V+ = [v | 1 | 1] (0 past the end)
       T *sG = ROLE == kRoleDQ ? sX : sY;
       T *sV = ROLE == kRoleDQ ? sY : sX;
-      using S = BSlab<T, D, D>;
-#pragma unroll
-      for (int i = 0; i < S::PER; ++i) {
-        const int p = tid + kBThreads * i;
-        const bool mine = S::EXACT || p < S::PIECES;
-        const int r = p / S::PPR, cc = (p % S::PPR) * VEC;
-        const float den = __shfl(rd.v, r & 63);  // row r's den, from lane r
-        const bool valid = r < rows;
-        const float rden = valid ? 1.f / den : 0.f;
-        float go[VEC], oo[VEC], vv[VEC];
-        piece_to_f32<T>(r1.v[i], go);
-        piece_to_f32<T>(r2.v[i], oo);
-        piece_to_f32<T>(r3.v[i], vv);
-        float dot = 0.f;   // g . out with g as the operand holds it
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          go[e] = round_to<T>(go[e] * rden);
-          dot += go[e] * oo[e];
-          if (!valid) vv[e] = 0.f;
-        }
-        dot = sum_group<S::PPR>(dot);
-        if (mine) {
-          const int t = trow(r);
-          *reinterpret_cast<u32x4 *>(sG + t * LX + cc) = f32_to_piece<T>(go);
-          *reinterpret_cast<u32x4 *>(sV + t * LX + cc) = f32_to_piece<T>(vv);
-          if (cc == 0) {
-            // h = -g . out as hi + lo (columns d, d + 1); V+ has 1 in both
-            const float hh = -dot;
-            const float hi = round_to<T>(hh), lo = hh - hi;
-            const float one = valid ? 1.f : 0.f;
-            sG[t * LX + D] = from_f32<T>(hi);
-            sG[t * LX + D + 1] = from_f32<T>(lo);
-            sV[t * LX + D] = from_f32<T>(one);
-            sV[t * LX + D + 1] = from_f32<T>(one);
-          }
-        }
-      }
-      // Z (the value block)
-      using SB = BSlab<T, 16, D>;
-#pragma unroll
-      for (int i = 0; i < SB::PER; ++i) {
-        const int p = tid + kBThreads * i;
-        if (SB::EXACT || p < SB::PIECES) {
-          const int r = p / SB::PPR, cc = (p % SB::PPR) * VEC;
-          const int t = trow(r);
-          const bool valid = r < rows;
-          // dq: value K' (the k block); dk: Q' (the q block)
-          float z[VEC];
-          piece_to_f32<T>(rb1.v[i], z);
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) z[e] = valid ? phi(z[e], ELU) : 0.f;
-          *reinterpret_cast<u32x4 *>(sZ + t * LZ + cc) = f32_to_piece<T>(z);
-        }
+      put(rg, sG, LX, trow);
+      put(r1, sV, LX, trow);
+      if (tid < C) {
+        const int t = trow(tid);
+        const T one = from_f32<T>(tid < rows ? 1.f : 0.f);
+        sV[t * LX + D] = one;
+        sV[t * LX + D + 1] = one;
       }
     } else {
-      // dv: X = K', Y = Q' (full rows), Z = the G block (dout / den)
-      using S = BSlab<T, D, D>;
-#pragma unroll
-      for (int i = 0; i < S::PER; ++i) {
-        const int p = tid + kBThreads * i;
-        if (S::EXACT || p < S::PIECES) {
-          const int r = p / S::PPR, cc = (p % S::PPR) * VEC;
-          const int t = trow(r);
-          const bool valid = r < rows;
-          float kx[VEC], qx[VEC];
-          piece_to_f32<T>(r1.v[i], kx);
-          piece_to_f32<T>(r2.v[i], qx);
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            kx[e] = valid ? phi(kx[e], ELU) : 0.f;
-            qx[e] = valid ? phi(qx[e], ELU) : 0.f;
-          }
-          *reinterpret_cast<u32x4 *>(sX + t * LX + cc) = f32_to_piece<T>(kx);
-          *reinterpret_cast<u32x4 *>(sY + t * LX + cc) = f32_to_piece<T>(qx);
-        }
-      }
-      using SB = BSlab<T, 16, D>;
-#pragma unroll
-      for (int i = 0; i < SB::PER; ++i) {
-        const int p = tid + kBThreads * i;
-        const int r = p / SB::PPR, cc = (p % SB::PPR) * VEC;
-        const float den = __shfl(rd.v, r & 63);
-        if (SB::EXACT || p < SB::PIECES) {
-          const int t = trow(r);
-          const float rden = r < rows ? 1.f / den : 0.f;
-          float z[VEC];
-          piece_to_f32<T>(rb1.v[i], z);
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) z[e] *= rden;
-          *reinterpret_cast<u32x4 *>(sZ + t * LZ + cc) = f32_to_piece<T>(z);
-        }
-      }
+      put(r1, sX, LX, trow);
+      put(r2, sY, LX, trow);
     }
+    if constexpr (GV)
+      put(rz, sZ, LZ, trow);
+    else
+      put(rzg, sZ, LZ, trow);
   };
 
   // State tiles of this wave: S (features 16 fb .. +16, the 16 value
@@ -351,10 +279,37 @@ __device__ __forceinline__ void bwd_role(const BwdArgs &a, int64_t unit,
 
   const int tb = w;                 // this wave's output strip
   const int t = 16 * tb + li;       // the query row this lane reads out
+  // dq, dk (elu + 1): the raw q or k of this lane's four output elements
+  // (row t of the chunk, columns col0 + 4 g ..) for phi', loaded with the
+  // chunk's operands (pfn) and moved to pfc once that chunk is staged, so
+  // the load is never waited for at the output
+  constexpr bool PFI = GV && ELU;
+  using PV = std::conditional_t<sizeof(T) == 2, u32x2, u32x4>;
+  PV pfn{}, pfc{};
+  auto load_phi = [&](int c) {
+    if constexpr (PFI) {
+      const int rows = rows_of(c);
+      const __amdgpu_buffer_rsrc_t r =
+          make_rsrc((ROLE == kRoleDQ ? qb : kb) + row0_of(c) * D,
+                    static_cast<unsigned>(rows) * D * sizeof(T));
+      // rows at or past the end are out of the resource and read zero
+      const int rr = REV && t < rows ? rows - 1 - t : t;
+      const unsigned off =
+          static_cast<unsigned>(rr * D + col0 + 4 * g) * sizeof(T);
+      if constexpr (sizeof(T) == 2)
+        pfn = __builtin_bit_cast(
+            PV, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+      else
+        pfn = buffer_load16(r, off);
+    }
+  };
   load(0);
+  load_phi(0);
   __syncthreads();                  // gp and the constant parts ready
   stage(0);
+  pfc = pfn;
   load(1);
+  load_phi(1);
   publish();
   __syncthreads();
 
@@ -408,13 +363,24 @@ __device__ __forceinline__ void bwd_role(const BwdArgs &a, int64_t unit,
     // o[r]: value column 4 g + r of query row t; times phi' for dq, dk
     if (t < rows) {
       const int64_t row = row0_of(c) + (REV ? rows - 1 - t : t);
-      // dq, dk: times phi'(x) of the same elements of q or k (read back,
-      // from L2: the rows were loaded a chunk ago)
-      const T *xp = (ROLE == kRoleDQ ? qb : kb) + row * D + col0 + 4 * g;
+      // dq, dk: times phi'(x) of the same elements of q or k
+      float xin[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (PFI) {
+        if constexpr (sizeof(T) == 2) {
+          xin[0] = bf16_lo(pfc[0]);
+          xin[1] = bf16_hi(pfc[0]);
+          xin[2] = bf16_lo(pfc[1]);
+          xin[3] = bf16_hi(pfc[1]);
+        } else {
+          const f32x4 y = __builtin_bit_cast(f32x4, pfc);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) xin[r] = y[r];
+        }
+      }
       float x[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        x[r] = GV && ELU ? o[r] * dphi(to_f32(xp[r]), true) : o[r];
+        x[r] = PFI ? o[r] * dphi(xin[r], true) : o[r];
       store4(res + row * D + col0 + 4 * g, x[0], x[1], x[2], x[3]);
     }
     // ---- state update: S <- g^r S + (w Y)^T Z, the weights w_s =
@@ -449,9 +415,82 @@ __device__ __forceinline__ void bwd_role(const BwdArgs &a, int64_t unit,
     }
     __syncthreads();   // the tile set is free again
     stage(c + 1);
+    pfc = pfn;
     load(c + 2);
+    load_phi(c + 2);
     publish();
     __syncthreads();
+  }
+}
+
+// Preparation pass: per row of every unit, G~ = [g | h hi | h lo | 0 ..]
+// with g = dout / den rounded to the storage type and h = -(g . out) (the
+// dot product of the rounded g, in fp32; hi its rounding, lo the rest), and
+// for elu + 1 the features K' = phi(k), Q' = phi(q).  LPR consecutive
+// threads take one row, one 16-byte piece each; the row's dot product is
+// summed across them.  Grid-stride over groups of rows.
+template <typename T, int D, bool ELU>
+__global__ __launch_bounds__(kBThreads) void la_bwd_prep_kernel(
+    BwdArgs a, int64_t rows_total) {
+  constexpr int VEC = 16 / sizeof(T), LPR = D / VEC, KG = backward_gwidth(D);
+  constexpr int NPAD = (KG - D) / VEC;  // pieces of a G~ row past g
+  constexpr int RPB = kBThreads / LPR;  // rows per block and step
+  static_assert(NPAD <= LPR, "pad pieces");
+  const int tid = threadIdx.x, j = tid % LPR;
+  const int64_t nsteps = (rows_total + RPB - 1) / RPB;
+  for (int64_t st = blockIdx.x; st < nsteps; st += gridDim.x) {
+    const int64_t row = st * RPB + tid / LPR;
+    // a row's LPR threads are consecutive and aligned, so they stay or
+    // leave together and the sums below never read a departed lane
+    if (row >= rows_total) break;
+    const int64_t off = row * D + j * VEC;
+    const u32x4 dop =
+        *reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.dout) + off);
+    const u32x4 oup =
+        *reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.out) + off);
+    const float rden = 1.f / a.den[row];
+    float go[VEC], oo[VEC];
+    piece_to_f32<T>(dop, go);
+    piece_to_f32<T>(oup, oo);
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      go[e] = round_to<T>(go[e] * rden);
+      dot += go[e] * oo[e];
+    }
+    dot = sum_group<LPR>(dot);
+    T *gr = static_cast<T *>(a.gt) + row * KG;
+    *reinterpret_cast<u32x4 *>(gr + j * VEC) = f32_to_piece<T>(go);
+    if (j < NPAD) {
+      const float hh = -dot;
+      const float hi = round_to<T>(hh), lo = hh - hi;
+      float pad[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) pad[e] = 0.f;
+      if (j == 0) {
+        pad[0] = hi;
+        pad[1] = lo;
+      }
+      *reinterpret_cast<u32x4 *>(gr + D + j * VEC) = f32_to_piece<T>(pad);
+    }
+    if constexpr (ELU) {
+      const u32x4 qp =
+          *reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.q) + off);
+      const u32x4 kp =
+          *reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.k) + off);
+      float qx[VEC], kx[VEC];
+      piece_to_f32<T>(qp, qx);
+      piece_to_f32<T>(kp, kx);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        qx[e] = phi(qx[e], true);
+        kx[e] = phi(kx[e], true);
+      }
+      *reinterpret_cast<u32x4 *>(static_cast<T *>(a.qf) + off) =
+          f32_to_piece<T>(qx);
+      *reinterpret_cast<u32x4 *>(static_cast<T *>(a.kf) + off) =
+          f32_to_piece<T>(kx);
+    }
   }
 }
 
@@ -484,6 +523,16 @@ void la_bwd_kernel(BwdArgs a,
 
 template <typename T, int D, bool DECAY, bool ELU>
 hipError_t launch_all(const BwdArgs &a, int64_t units, hipStream_t s) {
+  {
+    constexpr int RPB = kBThreads / (D / (16 / static_cast<int>(sizeof(T))));
+    const int64_t steps = (units * a.n + RPB - 1) / RPB;
+    const unsigned grid =
+        static_cast<unsigned>(std::min<int64_t>(steps, int64_t{kCUs} * 16));
+    hipLaunchKernelGGL((la_bwd_prep_kernel<T, D, ELU>), dim3(grid),
+                       dim3(kBThreads), 0, s, a, units * a.n);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   constexpr size_t lds =
       std::max({BShape<T, D, kRoleDQ, DECAY>::lds_bytes,
                 BShape<T, D, kRoleDK, DECAY>::lds_bytes,

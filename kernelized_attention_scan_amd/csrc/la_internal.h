@@ -127,9 +127,17 @@ struct BwdArgs {
   int64_t n;
   int dqk;    // width of q, k (== d)
   int elu1;   // 1: phi = elu + 1; 0: identity
+  // Per-row operands, written by the preparation pass into the workspace:
+  // G~ = [dout / den | h hi | h lo | 0 ..] ([units][n][backward_gwidth(d)])
+  // and, for elu + 1, K' = phi(k), Q' = phi(q) ([units][n][d]; with the
+  // identity map they are k and q themselves).
+  void *gt, *kf, *qf;
 };
 bool backward_supported(int d, int d_feat);
-// Enqueue the three role kernels (dq, dk, dv); dtype 0 fp32, 1 bf16.
+// Width of a G~ row: d + 2 rounded up to a multiple of 32.
+constexpr int backward_gwidth(int d) { return (d + 2 + 31) / 32 * 32; }
+// Enqueue the preparation pass and the role kernels (dq, dk, dv); dtype 0
+// fp32, 1 bf16.
 hipError_t launch_backward(const BwdArgs &a, int64_t units, int d, int dtype,
                            hipStream_t stream);
 

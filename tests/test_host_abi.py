@@ -293,3 +293,38 @@ def test_binding_featmap_rejects_bad_shapes():
         K.featmap(x, "performer", omega=_t(32, 64, dtype=torch.float32))
     with pytest.raises(ValueError):
         K.featmap(x, "elu1", out=_t(10, 32))
+
+
+def test_backward_workspace_bytes(lib):
+    import torch
+    a256 = lambda x: (x + 255) // 256 * 256
+    # G~ rows of d + 2 values padded to a multiple of 32; elu + 1 adds the
+    # features phi(k) and phi(q), identity uses k and q themselves
+    rows = 2 * 3 * 100
+    assert K.backward_workspace_bytes(2, 3, 100, 128) == (
+        a256(rows * 160 * 2) + 2 * a256(rows * 128 * 2))
+    assert K.backward_workspace_bytes(2, 3, 100, 16, "identity") == a256(rows * 32 * 2)
+    assert K.backward_workspace_bytes(2, 3, 100, 64, dtype=torch.float32) == (
+        a256(rows * 96 * 4) + 2 * a256(rows * 64 * 4))
+    # rejected or empty: 0
+    assert K.backward_workspace_bytes(2, 3, 100, 48) == 0
+    assert K.backward_workspace_bytes(2, 3, 0, 64) == 0
+    assert K.backward_workspace_bytes(2, 3, 100, 64, "performer") == 0
+
+
+def test_backward_rejects_null_workspace(lib):
+    # host-side validation: nothing is enqueued, no device memory is touched
+    vp = ctypes.c_void_p(16)
+    st = lib.la_backward(vp, vp, vp, vp, vp, vp, vp, vp, vp, 1, 1, 64, 64, 64,
+                         B.MAP_ELU1, None, None, B.LA_BF16, None, None)
+    assert st == B.LA_ERR_WORKSPACE
+    assert "workspace" in lib.la_last_error().decode()
+
+
+def test_binding_backward_rejects_small_workspace():
+    import torch
+    x = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
+    den = torch.ones(1, 1, 64)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        K.backward(x, x, x, x, den, x, workspace=ws)
