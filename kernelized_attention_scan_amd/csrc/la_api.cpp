@@ -471,15 +471,21 @@ la_status la_forward_train(const void *q, const void *k, const void *v,
 }
 
 namespace {
-// Workspace of la_backward: G~ rows, then (elu + 1) K' and Q'.
+// Workspace of la_backward: G~ rows, then (elu + 1) K' and Q', then the
+// segment aggregates of the segmented roles.
 size_t backward_ws(int64_t units, int64_t n, int d, int map, int dtype,
-                   size_t *kf_off) {
+                   size_t *kf_off, size_t *agg_off = nullptr) {
   const size_t es = elem_size(dtype);
   const size_t g = align256(static_cast<size_t>(units * n) *
                             la::backward_gwidth(d) * es);
   const size_t f = align256(static_cast<size_t>(units * n) * d * es);
+  const size_t feats = map == LA_MAP_ELU1 ? 2 * f : 0;
+  const int nseg = la::backward_segments(units, n, d, dtype);
+  const size_t agg =
+      align256(la::backward_agg_floats(units, nseg) * sizeof(float));
   if (kf_off) *kf_off = g;
-  return g + (map == LA_MAP_ELU1 ? 2 * f : 0);
+  if (agg_off) *agg_off = g + feats;
+  return g + feats + agg;
 }
 }  // namespace
 
@@ -526,10 +532,10 @@ la_status la_backward(const void *q, const void *k, const void *v,
     if (!workspace)
       return fail(LA_ERR_WORKSPACE, "la_backward: workspace of %zu bytes required",
                   backward_ws(units, n, d, map, dtype, nullptr));
-    size_t kf_off = 0;
+    size_t kf_off = 0, agg_off = 0;
     const size_t fbytes = align256(static_cast<size_t>(units * n) * d *
                                    elem_size(dtype));
-    backward_ws(units, n, d, map, dtype, &kf_off);
+    backward_ws(units, n, d, map, dtype, &kf_off, &agg_off);
     la::BwdArgs a;
     a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.den = den;
     a.dq = dq; a.dk = dk; a.dv = dv;
@@ -542,6 +548,8 @@ la_status la_backward(const void *q, const void *k, const void *v,
     a.gt = ws;
     a.kf = a.elu1 ? ws + kf_off : const_cast<void *>(k);
     a.qf = a.elu1 ? ws + kf_off + fbytes : const_cast<void *>(q);
+    a.nseg = la::backward_segments(units, n, d, dtype);
+    a.agg = reinterpret_cast<float *>(ws + agg_off);
     const hipError_t e = la::launch_backward(a, units, d, dtype,
                                              static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "la_backward launch");

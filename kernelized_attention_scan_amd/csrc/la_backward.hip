@@ -80,13 +80,14 @@ struct BShape {
 // consecutive pieces) of rows row0 .. row0 + rows - 1 of a matrix whose
 // rows are LD elements long, starting at column col0; rows past `rows`
 // read zero (the buffer resource ends there).
-template <typename T, int W, int LD>
+template <typename T, int W, int LD, int NTH = kBThreads>
 struct BSlab {
   static constexpr int VEC = 16 / sizeof(T);
   static constexpr int PPR = W / VEC;
   static constexpr int PIECES = kBC * PPR;
-  static constexpr int PER = (PIECES + kBThreads - 1) / kBThreads;
-  static constexpr bool EXACT = PIECES % kBThreads == 0;
+  static constexpr int PER = (PIECES + NTH - 1) / NTH;
+  static constexpr bool EXACT = PIECES % NTH == 0;
+  static constexpr int THREADS = NTH;
   u32x4 v[PER];
   __device__ __forceinline__ void load(const T *base, int64_t row0, int rows,
                                        int col0, int tid) {
@@ -94,7 +95,7 @@ struct BSlab {
         base + row0 * LD, static_cast<unsigned>(rows) * LD * sizeof(T));
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int p = tid + kBThreads * i;
+      const int p = tid + NTH * i;
       if (EXACT || p < PIECES)
         v[i] = buffer_load16(
             r, static_cast<unsigned>(((p / PPR) * LD + col0 +
@@ -228,7 +229,7 @@ __device__ __forceinline__ void bwd_role(const BwdArgs &a, int64_t unit,
     using S = std::remove_cv_t<std::remove_reference_t<decltype(sl)>>;
 #pragma unroll
     for (int i = 0; i < S::PER; ++i) {
-      const int p = tid + kBThreads * i;
+      const int p = tid + S::THREADS * i;
       if (S::EXACT || p < S::PIECES)
         *reinterpret_cast<u32x4 *>(dst + trow(p / S::PPR) * L +
                                    (p % S::PPR) * VEC) = sl.v[i];
@@ -494,6 +495,390 @@ __global__ __launch_bounds__(kBThreads) void la_bwd_prep_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Segmented roles (bf16, d = 128).  One 512-thread workgroup (8 waves) per
+// (role, unit, segment of the role's processing order) owns all d output
+// columns, so a chunk's scores are formed once per 16-row strip instead of
+// once per 16-column block.  Two launches, like the forward's non-causal
+// split: PHASE 1 writes each segment's aggregate (its end state from a zero
+// state) to the workspace; PHASE 2 sums the aggregates of the segments
+// before it, each weighted by the decay over the rows between, and runs the
+// chunk loop from that state.  No workgroup waits for another.
+// Wave w = 4 jh + tb reads out strip tb for column blocks 4 jh .. 4 jh + 3
+// and owns the state of column block w (all its feature tiles).
+// ---------------------------------------------------------------------------
+constexpr int kSThreads = 512;
+constexpr int kSWaves = kSThreads / kWave;
+constexpr int kSegD = 128;                                   // d built
+constexpr int kSegTiles = backward_gwidth(kSegD) / 16;       // NT, at most
+constexpr int kSegSlot = kSWaves * kSegTiles * 256;          // floats
+
+template <typename T, int ROLE>
+struct SShape {
+  static constexpr int D = kSegD;
+  static constexpr bool GV = ROLE != kRoleDV;
+  static constexpr int KX = GV ? backward_gwidth(D) : D;
+  static constexpr int LX = bstride<T>(KX);
+  static constexpr int LZ = bstride<T>(D);
+  static constexpr int NT = KX / 16;
+  static constexpr int SX = kBC * LX, SZ = kBC * LZ, SST = D * LX;
+  static constexpr size_t lds_bytes =
+      sizeof(T) * (2 * SX + SZ + SST) + sizeof(float) * (kBC + 4);
+  static_assert(D / 16 == kSWaves, "one state column block per wave");
+};
+
+template <typename T, int ROLE, bool DECAY, bool ELU, int PHASE>
+__device__ __forceinline__ void seg_role(const BwdArgs &a, int64_t units,
+                                         int64_t unit, int seg,
+                                         unsigned char *smem) {
+  const int nseg = a.nseg;
+  float *agg = a.agg;
+  using F = SShape<T, ROLE>;
+  constexpr int D = F::D, C = kBC, KX = F::KX, LX = F::LX, LZ = F::LZ;
+  constexpr int NT = F::NT, KG = backward_gwidth(D);
+  constexpr bool GV = F::GV, REV = ROLE != kRoleDQ;
+  T *sX = reinterpret_cast<T *>(smem);           // queries X
+  T *sY = sX + F::SX;                            // keys Y
+  T *sZ = sY + F::SX;                            // values Z (all d columns)
+  T *sST = sZ + F::SZ;                           // S^T copy
+  float *gp = reinterpret_cast<float *>(sST + F::SST);  // g^0 .. g^C
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, li = lane & 15;
+  const int tb = w % 4, jh = w / 4;
+  const int h = static_cast<int>(unit % a.H);
+  const float gdec = DECAY ? a.decay[h] : 1.f, bdec = DECAY ? 1.f - gdec : 1.f;
+  const float lg = log2f(gdec);
+  for (int i = tid; i <= C; i += kSThreads) gp[i] = pow_int(gdec, lg, i);
+
+  const int64_t n = a.n;
+  const T *qb = static_cast<const T *>(a.q) + unit * n * D;
+  const T *kb = static_cast<const T *>(a.k) + unit * n * D;
+  const T *vb = static_cast<const T *>(a.v) + unit * n * D;
+  const T *gtb = static_cast<const T *>(a.gt) + unit * n * KG;
+  const T *kfb = static_cast<const T *>(a.kf) + unit * n * D;
+  const T *qfb = static_cast<const T *>(a.qf) + unit * n * D;
+  T *res = static_cast<T *>(ROLE == kRoleDQ ? a.dq
+                            : ROLE == kRoleDK ? a.dk
+                                              : a.dv) +
+           unit * n * D;
+
+  // the zero padding columns of X and Y (G~ rows are copied whole, the
+  // ones columns of V+ are written per chunk)
+  constexpr int XW = GV ? D + 2 : D;
+  for (int i = tid; i < C * (KX - XW); i += kSThreads) {
+    const int row = i / (KX - XW), col = XW + i % (KX - XW);
+    sX[row * LX + col] = from_f32<T>(0.f);
+    sY[row * LX + col] = from_f32<T>(0.f);
+  }
+
+  // processing steps of this segment (step c is physical chunk c, or
+  // nch - 1 - c for the reverse-order roles)
+  const int nch = static_cast<int>((n + C - 1) / C);
+  const int cps = (nch + nseg - 1) / nseg;
+  const int cb = seg * cps, ce = min(nch, cb + cps);
+  auto chunk_of = [&](int c) { return REV ? nch - 1 - c : c; };
+  auto rows_of = [&](int c) -> int {
+    if (c >= ce) return 0;
+    const int64_t r0 = static_cast<int64_t>(chunk_of(c)) * C;
+    return static_cast<int>(min<int64_t>(C, n - r0));
+  };
+  auto row0_of = [&](int c) -> int64_t {
+    return c >= ce ? 0 : static_cast<int64_t>(chunk_of(c)) * C;
+  };
+
+  // Register ring (one chunk ahead).  X is not needed in PHASE 1.
+  using SG = BSlab<T, KG, KG, kSThreads>;   // G~ rows
+  using SD = BSlab<T, D, D, kSThreads>;     // v, K' or Q' rows
+  using SZG = BSlab<T, D, KG, kSThreads>;   // the first d columns of G~
+  SG rg;
+  SD r1, r2;
+  SZG rzg;
+  // GV: rg = G~ (X of dq, Y of dk), r1 = v (V+), r2 = K' (dq) or Q' (dk)
+  // dv: r1 = K' (X), r2 = Q' (Y), rzg = G (Z)
+  constexpr bool NEED_G = GV ? (PHASE == 2 || ROLE == kRoleDK) : true;
+  constexpr bool NEED_R1 = GV ? (PHASE == 2 || ROLE == kRoleDQ) : PHASE == 2;
+  auto load = [&](int c) {
+    const int64_t r0 = row0_of(c);
+    const int rows = rows_of(c);
+    if constexpr (GV) {
+      if constexpr (NEED_G) rg.load(gtb, r0, rows, 0, tid);
+      if constexpr (NEED_R1) r1.load(vb, r0, rows, 0, tid);
+      r2.load(ROLE == kRoleDQ ? kfb : qfb, r0, rows, 0, tid);
+    } else {
+      if constexpr (NEED_R1) r1.load(kfb, r0, rows, 0, tid);
+      r2.load(qfb, r0, rows, 0, tid);
+      rzg.load(gtb, r0, rows, 0, tid);
+    }
+  };
+  auto put = [&](const auto &sl, T *dst, int L, auto trow) {
+    using S = std::remove_cv_t<std::remove_reference_t<decltype(sl)>>;
+#pragma unroll
+    for (int i = 0; i < S::PER; ++i) {
+      const int p = tid + S::THREADS * i;
+      if (S::EXACT || p < S::PIECES)
+        *reinterpret_cast<u32x4 *>(dst + trow(p / S::PPR) * L +
+                                   (p % S::PPR) * S::VEC) = sl.v[i];
+    }
+  };
+  auto stage = [&](int c) {
+    const int rows = rows_of(c);
+    auto trow = [&](int r) { return REV && r < rows ? rows - 1 - r : r; };
+    if constexpr (GV) {
+      T *sG = ROLE == kRoleDQ ? sX : sY;
+      T *sV = ROLE == kRoleDQ ? sY : sX;
+      if constexpr (NEED_G) put(rg, sG, LX, trow);
+      if constexpr (NEED_R1) {
+        put(r1, sV, LX, trow);
+        if (tid < C) {
+          const int t = trow(tid);
+          const T one = from_f32<T>(tid < rows ? 1.f : 0.f);
+          sV[t * LX + D] = one;
+          sV[t * LX + D + 1] = one;
+        }
+      }
+      put(r2, sZ, LZ, trow);
+    } else {
+      if constexpr (NEED_R1) put(r1, sX, LX, trow);
+      put(r2, sY, LX, trow);
+      put(rzg, sZ, LZ, trow);
+    }
+  };
+
+  // this wave's state: column block w, feature tiles 0 .. NT - 1
+  f32x4 S[NT];
+#pragma unroll
+  for (int fb = 0; fb < NT; ++fb) S[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto slot = [&](int sg) {
+    return agg + ((static_cast<int64_t>(ROLE) * units + unit) * nseg +
+                  sg) *
+                     kSegSlot +
+           (w * kSegTiles) * 256 + lane * 4;
+  };
+  if constexpr (PHASE == 2) {
+    // the entering state: the aggregates before this segment, each carried
+    // over the rows between it and this segment (whole chunks)
+    for (int sg = 0; sg < seg; ++sg) {
+      const float wgt =
+          DECAY ? pow_int(gdec, lg,
+                          static_cast<int64_t>(seg - sg - 1) * cps * C)
+                : 1.f;
+      const float *src = slot(sg);
+#pragma unroll
+      for (int fb = 0; fb < NT; ++fb)
+        S[fb] += wgt * *reinterpret_cast<const f32x4 *>(src + fb * 256);
+    }
+  }
+  auto publish = [&]() {  // S^T rows 16 w .. + 15 (this wave's columns)
+#pragma unroll
+    for (int fb = 0; fb < NT; ++fb)
+      store4(sST + (16 * w + li) * LX + 16 * fb + 4 * g, S[fb][0], S[fb][1],
+             S[fb][2], S[fb][3]);
+  };
+  auto state_update = [&](int c) {
+    const int rows = rows_of(c);
+    const float gr = gp[rows];
+    f32x4 wlo[C / 32], whi[C / 32];
+    if constexpr (DECAY) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < C / 32; ++kb2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int s0 = 32 * kb2 + 8 * g + e, s1 = s0 + 4;
+          wlo[kb2][e] = s0 < rows ? bdec * gp[rows - 1 - s0] : 0.f;
+          whi[kb2][e] = s1 < rows ? bdec * gp[rows - 1 - s1] : 0.f;
+        }
+    }
+    // the weights go on this wave's one Z block (positions along the
+    // contraction, as in the Y fragments), not on its NT Y fragments
+    Frag<T> bf[C / 32];
+#pragma unroll
+    for (int kb2 = 0; kb2 < C / 32; ++kb2) {
+      load_frag_tr8(bf[kb2], sZ, LZ, 32 * kb2, 16 * w, g, li);
+      if constexpr (DECAY) frag_scale(bf[kb2], wlo[kb2], whi[kb2]);
+    }
+#pragma unroll
+    for (int fb = 0; fb < NT; ++fb) {
+      f32x4 acc = S[fb] * gr;
+#pragma unroll
+      for (int kb2 = 0; kb2 < C / 32; ++kb2) {
+        Frag<T> af;
+        load_frag_tr8(af, sY, LX, 32 * kb2, 16 * fb, g, li);
+        acc = mma(af, bf[kb2], acc);
+      }
+      S[fb] = acc;
+    }
+  };
+
+  const int t = 16 * tb + li;  // the query row this lane reads out
+  // dq, dk (elu + 1): raw q or k of this lane's output elements (row t,
+  // columns 16 (4 jh + jj) + 4 g ..), loaded a chunk ahead
+  constexpr bool PFI = GV && ELU && PHASE == 2;
+  u32x2 pfn[4] = {}, pfc[4] = {};
+  auto load_phi = [&](int c) {
+    if constexpr (PFI) {
+      const int rows = rows_of(c);
+      const __amdgpu_buffer_rsrc_t r =
+          make_rsrc((ROLE == kRoleDQ ? qb : kb) + row0_of(c) * D,
+                    static_cast<unsigned>(rows) * D * sizeof(T));
+      const int rr = REV && t < rows ? rows - 1 - t : t;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        pfn[jj] = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                       r,
+                       static_cast<unsigned>(rr * D + 16 * (4 * jh + jj) +
+                                             4 * g) *
+                           sizeof(T),
+                       0, 0));
+    }
+  };
+
+  load(cb);
+  load_phi(cb);
+  __syncthreads();  // gp and the constant parts ready
+  stage(cb);
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) pfc[jj] = pfn[jj];
+  load(cb + 1);
+  load_phi(cb + 1);
+  if constexpr (PHASE == 2) publish();
+  __syncthreads();
+
+  for (int c = cb; c < ce; ++c) {
+    if constexpr (PHASE == 2) {
+      const int rows = rows_of(c);
+      const float gt = gp[t + 1];
+      Frag<T> xf[KX / 32];
+#pragma unroll
+      for (int kq = 0; kq < KX / 32; ++kq)
+        load_frag8(xf[kq], sX + t * LX + 32 * kq + 8 * g);
+      f32x4 pt[4];
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (sb <= tb) {
+#pragma unroll
+          for (int kq = 0; kq < KX / 32; ++kq) {
+            Frag<T> fa;
+            load_frag8(fa, sY + (16 * sb + li) * LX + 32 * kq + 8 * g);
+            acc = mma(fa, xf[kq], acc);
+          }
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int s_ = 16 * sb + 4 * g + rr;
+          acc[rr] = s_ <= t ? acc[rr] * (DECAY ? bdec * gp[s_ <= t ? t - s_ : 0]
+                                               : 1.f)
+                            : 0.f;
+        }
+        pt[sb] = acc;
+      }
+      Frag<T> pf[2];
+#pragma unroll
+      for (int kp = 0; kp < 2; ++kp)
+        frag_from_acc(pf[kp], pt[2 * kp], pt[2 * kp + 1]);
+      const int64_t row = row0_of(c) + (REV && t < rows ? rows - 1 - t : t);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int jb = 4 * jh + jj;
+        f32x4 an = {0.f, 0.f, 0.f, 0.f}, ai = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp) {
+          if (2 * kp <= tb) {
+            Frag<T> zf;
+            load_frag_tr44(zf, sZ, LZ, 32 * kp, 16 * jb, g, li);
+            an = mma(zf, pf[kp], an);
+          }
+        }
+#pragma unroll
+        for (int kq = 0; kq < KX / 32; ++kq) {
+          Frag<T> fa;
+          load_frag8(fa, sST + (16 * jb + li) * LX + 32 * kq + 8 * g);
+          ai = mma(fa, xf[kq], ai);
+        }
+        const f32x4 o = an + gt * ai;
+        if (t < rows) {
+          float x[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float xin = 0.f;
+            if constexpr (PFI)
+              xin = r % 2 == 0 ? bf16_lo(pfc[jj][r / 2]) : bf16_hi(pfc[jj][r / 2]);
+            x[r] = PFI ? o[r] * dphi(xin, true) : o[r];
+          }
+          store4(res + row * D + 16 * jb + 4 * g, x[0], x[1], x[2], x[3]);
+        }
+      }
+    }
+    state_update(c);
+    __syncthreads();  // the tile set is free again
+    stage(c + 1);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) pfc[jj] = pfn[jj];
+    load(c + 2);
+    load_phi(c + 2);
+    if constexpr (PHASE == 2) publish();
+    __syncthreads();
+  }
+  if constexpr (PHASE == 1) {
+    float *dst = slot(seg);
+#pragma unroll
+    for (int fb = 0; fb < NT; ++fb)
+      *reinterpret_cast<f32x4 *>(dst + fb * 256) = S[fb];
+  }
+}
+
+template <bool DECAY, bool ELU, int PHASE>
+__global__ __launch_bounds__(kSThreads) void la_bwd_seg_kernel(BwdArgs a,
+                                                               int64_t units) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int nseg = a.nseg;
+  const int64_t per_role = units * nseg;
+  const int role = static_cast<int>(blockIdx.x / per_role);
+  const int64_t rem = blockIdx.x % per_role;
+  const int64_t unit = rem / nseg;
+  const int seg = static_cast<int>(rem % nseg);
+  // the last segment's aggregate is never read
+  if (PHASE == 1 && seg == nseg - 1) return;
+  if (role == kRoleDQ)
+    seg_role<bf16, kRoleDQ, DECAY, ELU, PHASE>(a, units, unit, seg, smem);
+  else if (role == kRoleDK)
+    seg_role<bf16, kRoleDK, DECAY, ELU, PHASE>(a, units, unit, seg, smem);
+  else
+    seg_role<bf16, kRoleDV, DECAY, ELU, PHASE>(a, units, unit, seg, smem);
+}
+
+template <bool DECAY, bool ELU>
+hipError_t launch_seg(const BwdArgs &a, int64_t units, hipStream_t s) {
+  const int nseg = a.nseg;
+  constexpr size_t lds = std::max({SShape<bf16, kRoleDQ>::lds_bytes,
+                                   SShape<bf16, kRoleDK>::lds_bytes,
+                                   SShape<bf16, kRoleDV>::lds_bytes});
+  static const hipError_t once = [] {
+    for (const void *k :
+         {reinterpret_cast<const void *>(&la_bwd_seg_kernel<DECAY, ELU, 1>),
+          reinterpret_cast<const void *>(&la_bwd_seg_kernel<DECAY, ELU, 2>)}) {
+      const hipError_t e = hipFuncSetAttribute(
+          k, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }();
+  if (once != hipSuccess) return once;
+  const dim3 grid(static_cast<unsigned>(3 * units * nseg)), block(kSThreads);
+  if (nseg > 1) {
+    hipLaunchKernelGGL((la_bwd_seg_kernel<DECAY, ELU, 1>), grid, block, lds, s,
+                       a, units);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((la_bwd_seg_kernel<DECAY, ELU, 2>), grid, block, lds, s, a,
+                     units);
+  return hipGetLastError();
+}
+
 // All roles in one launch: blocks [0, units nq) take dq, the next units nq
 // dk, the last units nv dv (nq = d'/16, nv = d/16).  Within a role the
 // blocks of one unit get indices of one XCD (workgroups are dispatched to
@@ -521,17 +906,23 @@ void la_bwd_kernel(BwdArgs a,
     bwd_role<T, D, kRoleDV, DECAY, ELU>(a, unit, blk, smem);
 }
 
+template <typename T, int D, bool ELU>
+hipError_t launch_prep(const BwdArgs &a, int64_t units, hipStream_t s) {
+  constexpr int RPB = kBThreads / (D / (16 / static_cast<int>(sizeof(T))));
+  const int64_t steps = (units * a.n + RPB - 1) / RPB;
+  const unsigned grid =
+      static_cast<unsigned>(std::min<int64_t>(steps, int64_t{kCUs} * 16));
+  hipLaunchKernelGGL((la_bwd_prep_kernel<T, D, ELU>), dim3(grid),
+                     dim3(kBThreads), 0, s, a, units * a.n);
+  return hipGetLastError();
+}
+
 template <typename T, int D, bool DECAY, bool ELU>
 hipError_t launch_all(const BwdArgs &a, int64_t units, hipStream_t s) {
-  {
-    constexpr int RPB = kBThreads / (D / (16 / static_cast<int>(sizeof(T))));
-    const int64_t steps = (units * a.n + RPB - 1) / RPB;
-    const unsigned grid =
-        static_cast<unsigned>(std::min<int64_t>(steps, int64_t{kCUs} * 16));
-    hipLaunchKernelGGL((la_bwd_prep_kernel<T, D, ELU>), dim3(grid),
-                       dim3(kBThreads), 0, s, a, units * a.n);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  hipError_t e = launch_prep<T, D, ELU>(a, units, s);
+  if (e != hipSuccess) return e;
+  if constexpr (std::is_same_v<T, bf16> && D == kSegD) {
+    if (a.nseg > 0) return launch_seg<DECAY, ELU>(a, units, s);
   }
   constexpr size_t lds =
       std::max({BShape<T, D, kRoleDQ, DECAY>::lds_bytes,
@@ -572,6 +963,24 @@ hipError_t launch_t(const BwdArgs &a, int64_t units, int d, hipStream_t s) {
 
 bool backward_supported(int d, int d_feat) {
   return d == d_feat && (d == 16 || d == 32 || d == 64 || d == 128);
+}
+
+int backward_segments(int64_t units, int64_t n, int d, int dtype) {
+  if (dtype != 1 || d != kSegD || units <= 0 || n <= 0) return 0;
+  // three roles x units x segments workgroups of one per CU: about three
+  // rounds of the CUs, at most 16 segments, whole chunks each
+  const int64_t nch = (n + kBC - 1) / kBC;
+  int64_t k = (kCUs + units - 1) / units;
+  if (k > 16) k = 16;
+  if (k > nch) k = nch;
+  if (k < 1) k = 1;
+  // segments of whole chunks: the last non-empty one decides the count
+  const int64_t cps = (nch + k - 1) / k;
+  return static_cast<int>((nch + cps - 1) / cps);
+}
+
+size_t backward_agg_floats(int64_t units, int nseg) {
+  return nseg > 1 ? static_cast<size_t>(3 * units * nseg) * kSegSlot : 0;
 }
 
 hipError_t launch_backward(const BwdArgs &a, int64_t units, int d, int dtype,

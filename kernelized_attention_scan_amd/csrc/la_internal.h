@@ -132,10 +132,19 @@ struct BwdArgs {
   // and, for elu + 1, K' = phi(k), Q' = phi(q) ([units][n][d]; with the
   // identity map they are k and q themselves).
   void *gt, *kf, *qf;
+  // Segmented roles (backward_segments() > 0): segments per role and unit,
+  // and their aggregates in the workspace (backward_agg_floats() floats).
+  int nseg;
+  float *agg;
 };
 bool backward_supported(int d, int d_feat);
 // Width of a G~ row: d + 2 rounded up to a multiple of 32.
 constexpr int backward_gwidth(int d) { return (d + 2 + 31) / 32 * 32; }
+// Segments per (role, unit) of the segmented roles (bf16, d = 128), or 0
+// where the column-block kernel runs instead; and the floats of their
+// aggregates.
+int backward_segments(int64_t units, int64_t n, int d, int dtype);
+size_t backward_agg_floats(int64_t units, int nseg);
 // Enqueue the preparation pass and the role kernels (dq, dk, dv); dtype 0
 // fp32, 1 bf16.
 hipError_t launch_backward(const BwdArgs &a, int64_t units, int d, int dtype,

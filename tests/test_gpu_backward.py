@@ -82,6 +82,11 @@ GRID = [
     ("elu1_d16", 2, 2, 333, 16, "elu1", False),
     ("identity_d64", 1, 2, 500, 64, "identity", True),
     ("identity_d128_long", 1, 1, 3000, 128, "identity", False),
+    # d = 128 bf16 runs as segmented roles: a ragged tail, one chunk (one
+    # segment), and units enough for few segments each
+    ("elu1_d128_ragged", 2, 2, 1001, 128, "elu1", False),
+    ("elu1_d128_one_chunk", 1, 3, 40, 128, "elu1", True),
+    ("elu1_d128_many_units", 8, 8, 300, 128, "elu1", True),
 ]
 
 
