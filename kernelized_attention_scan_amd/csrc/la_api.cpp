@@ -471,16 +471,17 @@ la_status la_forward_train(const void *q, const void *k, const void *v,
 }
 
 namespace {
-// Workspace of la_backward: G~ rows, then (elu + 1) K' and Q', then the
-// segment aggregates of the segmented roles.
+// Workspace of la_backward: G~ rows, then (elu + 1, column-block kernel)
+// K' and Q', then the segment aggregates of the segmented roles.
 size_t backward_ws(int64_t units, int64_t n, int d, int map, int dtype,
                    size_t *kf_off, size_t *agg_off = nullptr) {
   const size_t es = elem_size(dtype);
   const size_t g = align256(static_cast<size_t>(units * n) *
                             la::backward_gwidth(d) * es);
   const size_t f = align256(static_cast<size_t>(units * n) * d * es);
-  const size_t feats = map == LA_MAP_ELU1 ? 2 * f : 0;
   const int nseg = la::backward_segments(units, n, d, dtype);
+  // the segmented roles map k, q themselves: no K', Q' rows
+  const size_t feats = map == LA_MAP_ELU1 && nseg == 0 ? 2 * f : 0;
   const size_t agg =
       align256(la::backward_agg_floats(units, nseg) * sizeof(float));
   if (kf_off) *kf_off = g;
@@ -546,9 +547,11 @@ la_status la_backward(const void *q, const void *k, const void *v,
     a.elu1 = map == LA_MAP_ELU1;
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     a.gt = ws;
-    a.kf = a.elu1 ? ws + kf_off : const_cast<void *>(k);
-    a.qf = a.elu1 ? ws + kf_off + fbytes : const_cast<void *>(q);
     a.nseg = la::backward_segments(units, n, d, dtype);
+    // K', Q' rows only where the column-block kernel reads them
+    const bool feats = a.elu1 && a.nseg == 0;
+    a.kf = feats ? ws + kf_off : const_cast<void *>(k);
+    a.qf = feats ? ws + kf_off + fbytes : const_cast<void *>(q);
     a.agg = reinterpret_cast<float *>(ws + agg_off);
     const hipError_t e = la::launch_backward(a, units, d, dtype,
                                              static_cast<hipStream_t>(stream));

@@ -557,8 +557,6 @@ __device__ __forceinline__ void seg_role(const BwdArgs &a, int64_t units,
   const T *kb = static_cast<const T *>(a.k) + unit * n * D;
   const T *vb = static_cast<const T *>(a.v) + unit * n * D;
   const T *gtb = static_cast<const T *>(a.gt) + unit * n * KG;
-  const T *kfb = static_cast<const T *>(a.kf) + unit * n * D;
-  const T *qfb = static_cast<const T *>(a.qf) + unit * n * D;
   T *res = static_cast<T *>(ROLE == kRoleDQ ? a.dq
                             : ROLE == kRoleDK ? a.dk
                                               : a.dv) +
@@ -588,9 +586,11 @@ __device__ __forceinline__ void seg_role(const BwdArgs &a, int64_t units,
     return c >= ce ? 0 : static_cast<int64_t>(chunk_of(c)) * C;
   };
 
-  // Register ring (one chunk ahead).  X is not needed in PHASE 1.
+  // Register ring (one chunk ahead).  X is not needed in PHASE 1.  K' and
+  // Q' are mapped from the raw k and q rows while staging (each workgroup
+  // stages a row once).
   using SG = BSlab<T, KG, KG, kSThreads>;   // G~ rows
-  using SD = BSlab<T, D, D, kSThreads>;     // v, K' or Q' rows
+  using SD = BSlab<T, D, D, kSThreads>;     // v, k or q rows
   using SZG = BSlab<T, D, KG, kSThreads>;   // the first d columns of G~
   SG rg;
   SD r1, r2;
@@ -605,11 +605,33 @@ __device__ __forceinline__ void seg_role(const BwdArgs &a, int64_t units,
     if constexpr (GV) {
       if constexpr (NEED_G) rg.load(gtb, r0, rows, 0, tid);
       if constexpr (NEED_R1) r1.load(vb, r0, rows, 0, tid);
-      r2.load(ROLE == kRoleDQ ? kfb : qfb, r0, rows, 0, tid);
+      r2.load(ROLE == kRoleDQ ? kb : qb, r0, rows, 0, tid);
     } else {
-      if constexpr (NEED_R1) r1.load(kfb, r0, rows, 0, tid);
-      r2.load(qfb, r0, rows, 0, tid);
+      if constexpr (NEED_R1) r1.load(kb, r0, rows, 0, tid);
+      r2.load(qb, r0, rows, 0, tid);
       rzg.load(gtb, r0, rows, 0, tid);
+    }
+  };
+  // the same with phi applied (elu + 1 in fp32, rounded once; rows past the
+  // end stay zero)
+  auto put_phi = [&](const SD &sl, T *dst, int L, auto trow, int rows) {
+#pragma unroll
+    for (int i = 0; i < SD::PER; ++i) {
+      const int p = tid + SD::THREADS * i;
+      if (SD::EXACT || p < SD::PIECES) {
+        const int r = p / SD::PPR;
+        u32x4 y = sl.v[i];
+        if constexpr (ELU) {
+          float f[SD::VEC];
+          piece_to_f32<T>(sl.v[i], f);
+#pragma unroll
+          for (int e = 0; e < SD::VEC; ++e)
+            f[e] = r < rows ? elu_plus_one_fast(f[e]) : 0.f;
+          y = f32_to_piece<T>(f);
+        }
+        *reinterpret_cast<u32x4 *>(dst + trow(r) * L + (p % SD::PPR) * SD::VEC) =
+            y;
+      }
     }
   };
   auto put = [&](const auto &sl, T *dst, int L, auto trow) {
@@ -638,10 +660,10 @@ __device__ __forceinline__ void seg_role(const BwdArgs &a, int64_t units,
           sV[t * LX + D + 1] = one;
         }
       }
-      put(r2, sZ, LZ, trow);
+      put_phi(r2, sZ, LZ, trow, rows);
     } else {
-      if constexpr (NEED_R1) put(r1, sX, LX, trow);
-      put(r2, sY, LX, trow);
+      if constexpr (NEED_R1) put_phi(r1, sX, LX, trow, rows);
+      put_phi(r2, sY, LX, trow, rows);
       put(rzg, sZ, LZ, trow);
     }
   };
@@ -919,11 +941,17 @@ hipError_t launch_prep(const BwdArgs &a, int64_t units, hipStream_t s) {
 
 template <typename T, int D, bool DECAY, bool ELU>
 hipError_t launch_all(const BwdArgs &a, int64_t units, hipStream_t s) {
+  if constexpr (std::is_same_v<T, bf16> && D == kSegD) {
+    if (a.nseg > 0) {
+      // segmented roles map k, q themselves: the preparation pass writes
+      // only G~
+      hipError_t e = launch_prep<T, D, false>(a, units, s);
+      if (e != hipSuccess) return e;
+      return launch_seg<DECAY, ELU>(a, units, s);
+    }
+  }
   hipError_t e = launch_prep<T, D, ELU>(a, units, s);
   if (e != hipSuccess) return e;
-  if constexpr (std::is_same_v<T, bf16> && D == kSegD) {
-    if (a.nseg > 0) return launch_seg<DECAY, ELU>(a, units, s);
-  }
   constexpr size_t lds =
       std::max({BShape<T, D, kRoleDQ, DECAY>::lds_bytes,
                 BShape<T, D, kRoleDK, DECAY>::lds_bytes,

@@ -301,15 +301,14 @@ def test_backward_workspace_bytes(lib):
     # G~ rows of d + 2 values padded to a multiple of 32; elu + 1 adds the
     # features phi(k) and phi(q), identity uses k and q themselves
     rows = 2 * 3 * 100
-    # bf16 at d = 128 adds the segment aggregates of the segmented roles:
-    # 6 units, 100 rows = 2 chunks -> 2 segments, 3 roles x 8 waves x 10
-    # feature tiles x 256 floats each
+    # bf16 at d = 128 runs the segmented roles, which map k, q themselves
+    # (no K', Q' rows) and keep segment aggregates: 6 units, 100 rows = 2
+    # chunks -> 2 segments, 3 roles x 8 waves x 10 feature tiles x 256
+    # floats each
     assert K.backward_workspace_bytes(2, 3, 100, 128) == (
-        a256(rows * 160 * 2) + 2 * a256(rows * 128 * 2) +
-        a256(3 * 6 * 2 * 8 * 10 * 256 * 4))
+        a256(rows * 160 * 2) + a256(3 * 6 * 2 * 8 * 10 * 256 * 4))
     # one chunk: one segment, no aggregates
-    assert K.backward_workspace_bytes(2, 3, 64, 128) == (
-        a256(384 * 160 * 2) + 2 * a256(384 * 128 * 2))
+    assert K.backward_workspace_bytes(2, 3, 64, 128) == a256(384 * 160 * 2)
     assert K.backward_workspace_bytes(2, 3, 100, 128, dtype=torch.float32) == (
         a256(rows * 160 * 4) + 2 * a256(rows * 128 * 4))
     assert K.backward_workspace_bytes(2, 3, 100, 16, "identity") == a256(rows * 32 * 2)
