@@ -359,8 +359,8 @@ def backward_leg(torch, K, I, cfg, args, dev):
     t_wall = time.perf_counter() - t_wall
     return {"ms": ms, "t_wall": t_wall, "items": cfg.tokens,
             "unit": "tokens/s", "bytes": byts, "flops": flops,
-            "kern": {"kernel": "la_bwd_kernel (dq, dk and dv roles in one "
-                               "launch)",
+            "kern": {"kernel": "la_bwd_prep_kernel + la_bwd_seg_kernel "
+                               "(aggregates, then readout) per step",
                      "ms": ms, "bytes": byts, "flops": flops},
             "nsets": 1, "settle_steps": settled,
             "config": {"workload": "backward_" + cfg.name, "B": cfg.B,

@@ -30,14 +30,15 @@
 // hi + lo pair), and for elu + 1 the features K' and Q'.  The role kernels
 // then only copy tiles.
 //
-// Parallelism: one 256-thread workgroup (4 waves) per (unit, role, block
-// of 16 output columns), each walking its unit's whole sequence, all in one
-// launch.  The roles and blocks of a unit are independent, so no segment
-// exchange is needed: B H (2 d'/16 + d/16) workgroups (768 at B H = 32,
-// d = 128), about 53 KB of LDS each, so three share a compute unit.
-// Every workgroup recomputes the scores of its role (the price of
-// independence); the rows it shares with the unit's other workgroups come
-// mostly from L2.
+// Two kernels run the roles.  bf16 at d = 128 takes the segmented roles
+// (see la_bwd_seg_kernel below): a workgroup per (role, unit, segment of the
+// sequence) owns all output columns, with the segments' aggregates combined
+// across two launches.  Other sizes and fp32 take the column-block kernel:
+// one 256-thread workgroup (4 waves) per (unit, role, block of 16 output
+// columns), each walking its unit's whole sequence, all in one launch; the
+// roles and blocks of a unit are independent, so no segment exchange is
+// needed, but every workgroup recomputes the scores of its role, and the
+// rows it shares with the unit's other workgroups come mostly from L2.
 #include <algorithm>
 #include <type_traits>
 
