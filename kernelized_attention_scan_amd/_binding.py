@@ -660,3 +660,33 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                          _stream(v.device))
     _check(st, "la_backward")
     return dq, dk, dv
+
+
+class _LinearAttention(torch.autograd.Function):
+    """forward_train() forward, backward() gradients (no arithmetic here)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, feature_map, decay):
+        out, den = forward_train(q.contiguous(), k.contiguous(),
+                                 v.contiguous(), feature_map, decay=decay)
+        ctx.save_for_backward(q, k, v, out, den)
+        ctx.feature_map = feature_map
+        ctx.decay = decay
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, out, den = ctx.saved_tensors
+        dq, dk, dv = backward(q.contiguous(), k.contiguous(), v.contiguous(),
+                              out, den, dout.contiguous(), ctx.feature_map,
+                              decay=ctx.decay)
+        return dq, dk, dv, None, None
+
+
+def linear_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                     feature_map="elu1",
+                     decay: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal kernelized linear attention as a differentiable torch op:
+    la_forward_train forward, la_backward gradients for q, k and v (decay is
+    not differentiated).  elu1 or identity features, d_feat == d."""
+    return _LinearAttention.apply(q, k, v, feature_map, decay)

@@ -178,3 +178,26 @@ def test_backward_rejects_performer():
     with pytest.raises(K.LinAttnError) as e:
         K.backward(x, x, x, x, den, x, "performer")
     assert e.value.status == K._binding.LA_ERR_UNSUPPORTED
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_autograd_op_matches_oracle(dtype):
+    """linear_attention() as a torch op: its autograd gradients are those of
+    la_backward, checked against the oracle's adjoint."""
+    cfg = I.DECAYED.replace(B=1, H=2, n=333, d=64, dtype=dtype)
+    x = I.make_prefill(cfg, 21)
+    g = torch.Generator("cpu").manual_seed(22)
+    dout = torch.randn(cfg.B, cfg.H, cfg.n, cfg.d, generator=g).to(dtype)
+    q, k, v = (dev(x[n]).requires_grad_(True) for n in ("q", "k", "v"))
+    out = K.linear_attention(q, k, v, "elu1", decay=dev(x["decay"]))
+    out.backward(dev(dout))
+    torch.cuda.synchronize()
+    refs = oracle.backward(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(dout),
+                           oracle.MAP_ELU1, None, f64(x["decay"]))
+    for t, r in zip((q, k, v), refs):
+        assert rel(t.grad, r) <= GTOL[dtype]
+    ref_out = oracle.forward(f64(x["q"]), f64(x["k"]), f64(x["v"]),
+                             oracle.MAP_ELU1, None, f64(x["decay"]))
+    assert rel(out.detach(), ref_out) <= (1e-4 if dtype == torch.float32
+                                          else 1e-2)
