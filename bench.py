@@ -54,7 +54,9 @@ KERNEL_SOURCES = {
 
 
 def kernel_kind(workload: str) -> str:
-    return workload if workload in ("decode", "backward") else "forward"
+    if workload.startswith("decode"):
+        return "decode"
+    return workload if workload == "backward" else "forward"
 
 
 def kernel_source_hash(kind: str) -> str:
@@ -72,7 +74,8 @@ def workloads():
     return {"elu1": I.ELU1_CAUSAL, "decayed": I.DECAYED,
             "performer": I.PERFORMER, "tiny": I.TINY_FP32,
             "decode": I.DECODE, "noncausal": I.ELU1_NONCAUSAL,
-            "gated": I.GATED, "backward": I.DECAYED}
+            "gated": I.GATED, "backward": I.DECAYED,
+            "decode_channel": I.DECODE_CHANNEL}
 
 
 def esize(dtype) -> int:
@@ -91,12 +94,15 @@ def prefill_algorithmic(cfg):
     return byts, flops
 
 
-def decode_algorithmic(cfg):
+def decode_algorithmic(cfg, channel: bool = False):
     """Per step: read and write mu, nu (fp32) once; read q, k, v and write
-    out (storage dtype)."""
+    out (storage dtype); with a decay per channel, read the [H, d_feat] log
+    decays once."""
     units = cfg.S * cfg.H
     df, d = cfg.d_feat, cfg.d
     byts = units * (2 * df * d * 4 + 2 * df * 4 + 4 * d * esize(cfg.dtype))
+    if channel:
+        byts += cfg.H * df * 4
     flops = units * (4 * df * d + 4 * df)
     return byts, flops
 
@@ -194,26 +200,32 @@ def cpu_baseline_prefill(cfg, seed: int, budget_s: float = 20.0):
                       f"recurrence, {dt:.1f} s"}
 
 
-def cpu_baseline_decode(cfg, seed: int, budget_s: float = 10.0):
+def cpu_baseline_decode(cfg, seed: int, budget_s: float = 10.0,
+                        channel: bool = False):
     import oracle
     from kernelized_attention_scan_amd import inputs as I
     x = I.make_decode(cfg, seed)
     f64 = lambda t: None if t is None else t.double().numpy()
+    lam = f64(I.decode_channel_log_decay(cfg, seed)) if channel else None
     threads = oracle.num_threads()
     S = cfg.S
+
+    def run(take):
+        a = (f64(x["mu"][:take]), f64(x["nu"][:take]), f64(x["q"][:take]),
+             f64(x["k"][:take]), f64(x["v"][:take]), cfg.mapk,
+             f64(x["omega"]))
+        if channel:
+            oracle.decode_gated(*a, lam, oracle.LD_CHANNEL)
+        else:
+            oracle.decode(*a, f64(x["decay"]))
+
     probe = max(1, min(S, threads))
     t0 = time.perf_counter()
-    oracle.decode(f64(x["mu"][:probe]), f64(x["nu"][:probe]),
-                  f64(x["q"][:probe]), f64(x["k"][:probe]),
-                  f64(x["v"][:probe]), cfg.mapk, f64(x["omega"]),
-                  f64(x["decay"]))
+    run(probe)
     per = time.perf_counter() - t0
     take = max(probe, min(S, int(budget_s / max(per, 1e-9)) * probe))
     t0 = time.perf_counter()
-    oracle.decode(f64(x["mu"][:take]), f64(x["nu"][:take]),
-                  f64(x["q"][:take]), f64(x["k"][:take]),
-                  f64(x["v"][:take]), cfg.mapk, f64(x["omega"]),
-                  f64(x["decay"]))
+    run(take)
     dt = time.perf_counter() - t0
     return {"value": take * cfg.H / dt, "unit": "head-tokens/s",
             "cores": threads, "kind": "oracle",
@@ -405,16 +417,24 @@ def cpu_baseline_backward(cfg, seed: int, budget_s: float = 15.0):
 
 def decode_leg(torch, K, I, cfg, args, dev):
     mapname = I.MAP_NAMES[cfg.mapk]
-    byts, flops = decode_algorithmic(cfg)
+    channel = args.workload == "decode_channel"
+    byts, flops = decode_algorithmic(cfg, channel)
     x = I.make_decode(cfg, args.seed)
     s = {k: (None if t is None else t.to(dev)) for k, t in x.items()}
+    lam = (I.decode_channel_log_decay(cfg, args.seed).to(dev) if channel
+           else None)
     out = torch.empty_like(s["v"])
     stream = torch.cuda.current_stream(dev)
 
     def step(i):
         # mu, nu are updated in place: successive steps form a decode chain
-        K.decode_step(s["mu"], s["nu"], s["q"], s["k"], s["v"], mapname,
-                      omega=s["omega"], decay=s["decay"], out=out)
+        if channel:
+            K.decode_step_gated(s["mu"], s["nu"], s["q"], s["k"], s["v"],
+                                lam, "channel", mapname, omega=s["omega"],
+                                out=out)
+        else:
+            K.decode_step(s["mu"], s["nu"], s["q"], s["k"], s["v"], mapname,
+                          omega=s["omega"], decay=s["decay"], out=out)
 
     settled = settle(torch, step, args.settle_ms)
     for i in range(args.warmup):
@@ -430,7 +450,10 @@ def decode_leg(torch, K, I, cfg, args, dev):
             "nsets": 1, "settle_steps": settled,
             "config": {"workload": cfg.name, "S": cfg.S, "H": cfg.H,
                        "d": cfg.d, "d_feat": cfg.d_feat, "map": mapname,
-                       "a": cfg.a, "seed": args.seed}}
+                       "a": cfg.a,
+                       "decay": ("per channel: log(1 - 10^U(-3,-1)) [H, "
+                                 "d_feat]" if channel else "per head"),
+                       "seed": args.seed}}
 
 
 def main() -> int:
@@ -483,12 +506,12 @@ def main() -> int:
     K.load_library()
     cfg = workloads()[args.workload]
     if args.n:
-        if args.workload == "decode":
+        if args.workload.startswith("decode"):
             print("--n applies to prefill workloads only", file=sys.stderr)
             return 2
         cfg = cfg.replace(n=args.n,
                           name=re.sub(r"n\d+", f"n{args.n}", cfg.name, count=1))
-    is_decode = args.workload == "decode"
+    is_decode = args.workload.startswith("decode")
     is_bwd = args.workload == "backward"
     leg = (decode_leg if is_decode else backward_leg if is_bwd
            else prefill_leg)(torch, K, I, cfg, args, dev)
@@ -535,9 +558,12 @@ def main() -> int:
     if "other_launches_ms" in kern:
         line["roofline"]["launches_ms"] = kern["other_launches_ms"]
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = (cpu_baseline_decode if is_decode
-                                else cpu_baseline_backward if is_bwd
-                                else cpu_baseline_prefill)(cfg, args.seed)
+        if is_decode:
+            line["cpu_baseline"] = cpu_baseline_decode(
+                cfg, args.seed, channel=args.workload == "decode_channel")
+        else:
+            line["cpu_baseline"] = (cpu_baseline_backward if is_bwd
+                                    else cpu_baseline_prefill)(cfg, args.seed)
     print(json.dumps(line), flush=True)
     return 0
 

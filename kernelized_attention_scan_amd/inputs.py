@@ -95,6 +95,9 @@ PERFORMER = PrefillConfig("performer_B4H8n8192d64m256", B=4, H=8, n=8192, d=64,
 GATED = PrefillConfig("gated_elu1_B2H16n65536d128", B=2, H=16, n=65536,
                       d=128, gate=(-3.0, -1.0))
 DECODE = DecodeConfig("decode_S256H32d128_a0.99", S=256, H=32, d=128)
+# the same step with a decay per state row (per channel, [H, d_feat])
+DECODE_CHANNEL = DecodeConfig("decode_channel_S256H32d128", S=256, H=32,
+                              d=128, a=None)
 
 PREFILL_CONFIGS = {c.name: c for c in (TINY_FP32, ELU1_CAUSAL, ELU1_NONCAUSAL,
                                        DECAYED, PERFORMER, GATED)}
@@ -152,3 +155,12 @@ def make_decode(cfg: DecodeConfig, seed: int = 0) -> dict:
     return {"mu": mu, "nu": nu, "q": _round(q, cfg.dtype),
             "k": _round(k, cfg.dtype), "v": _round(v, cfg.dtype),
             "omega": omega, "decay": decay}
+
+
+def decode_channel_log_decay(cfg: DecodeConfig, seed: int = 0) -> torch.Tensor:
+    """Per-channel log decays [H, d_feat] (fp32) for the decode step: log(1 -
+    10^U(-3, -1)), drawn from their own generator (seed + 101) so the other
+    decode inputs of the same seed are unchanged."""
+    g = torch.Generator("cpu").manual_seed(seed + 101)
+    u = torch.rand((cfg.H, cfg.d_feat), generator=g)
+    return torch.log1p(-(10.0 ** (-3.0 + 2.0 * u)))
