@@ -50,6 +50,10 @@ KERNEL_SOURCES = {
     "decode": ["la_device.h", "la_internal.h", "la_decode.hip", "la_api.cpp"],
     "backward": ["la_device.h", "la_internal.h", "la_backward.hip",
                  "la_api.cpp"],
+    "rows": ["la_device.h", "la_internal.h", "la_forward_rows.h",
+             "la_forward_rows_inst.h", "la_forward_rows.hip",
+             "la_forward_rows_bf16.hip", "la_forward_rows_f32.hip",
+             "la_api.cpp"],
 }
 
 

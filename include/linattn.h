@@ -234,26 +234,46 @@ size_t la_backward_workspace_bytes(int B, int H, int64_t n, int d, int d_feat,
                                    la_map map, la_dtype dtype);
 
 /*
+ * la_forward_gated_workspace_bytes -- device workspace la_forward_gated
+ * needs for these sizes and this decay layout (0 when none).  For
+ * LA_LD_POSITION it equals la_forward_workspace_bytes of the same sizes; for
+ * a decay per state row it covers the segment aggregates (and Q', K' for
+ * PERFORMER).  Pure host function, never fails: returns 0 for arguments
+ * la_forward_gated would reject.
+ */
+size_t la_forward_gated_workspace_bytes(int B, int H, int64_t n, int d,
+                                        int d_feat, la_map map,
+                                        la_decay_layout layout, la_dtype dtype,
+                                        int causal);
+
+/*
  * la_forward_gated -- la_forward / la_forward_state with a decay that
- * varies by position: gamma_j = exp(lam_j) replaces a in eqs 10-11 at
- * position j,
- *   mu_j = gamma_j mu_{j-1} + (1 - gamma_j) k'_j^T v_j,
- *   nu_j = gamma_j nu_{j-1} + (1 - gamma_j) k'_j,
- * read out as in la_forward.  This is the input-dependent decay of Mamba's
- * selective step, dA = exp(A delta_t) ("Linear attention research 2026"
- * page), applied to the state of "2.2 Linear Attention" eqs 10-11; 1 -
- * gamma is the zero-order-hold input weight of the discretised update of
- * "2.3 State-Space Models" eq 14, up to a constant that cancels in the
- * ratio.
+ * varies by position and/or state row: gamma = exp(lam) replaces a in
+ * eqs 10-11, row f of the state at position j decaying by gamma_j[f],
+ *   mu_j[f] = gamma_j[f] mu_{j-1}[f] + (1 - gamma_j[f]) k'_j[f] v_j,
+ *   nu_j[f] = gamma_j[f] nu_{j-1}[f] + (1 - gamma_j[f]) k'_j[f],
+ * read out as in la_forward.  One decay per row (LA_LD_CHANNEL) is the
+ * diagonal A of "2.3 State-Space Models" eqs 21-25; one per position
+ * (LA_LD_POSITION) is the input-dependent decay of Mamba's selective step,
+ * dA = exp(A delta_t) ("Linear attention research 2026" page), and
+ * LA_LD_BOTH is that decay per row.  1 - gamma is the zero-order-hold input
+ * weight of the discretised update of "2.3 State-Space Models" eq 14, up to
+ * a constant that cancels in the ratio.
  *   All arguments as la_forward, with
  *   log_decay: device fp32 lam = log(gamma) in `layout`; values <= 0
  *              (decays in (0, 1]) are expected and not checked; -inf gives
- *              gamma = 0 (the state restarts at that position).
- *   layout   : LA_LD_POSITION ([B][H][n]) is built.  LA_LD_CHANNEL and
- *              LA_LD_BOTH (a decay per state row) return LA_ERR_UNSUPPORTED
- *              for the chunked forward: la_decode_step_gated takes them.
+ *              gamma = 0 (the state row restarts at that position).
+ *   layout   : LA_LD_POSITION ([B][H][n]), LA_LD_CHANNEL ([H][d_feat]) or
+ *              LA_LD_BOTH ([B][H][n][d_feat]).  With a decay per row, the
+ *              products of queries and keys inside a 16-position chunk
+ *              floor each step's decay at 2^-15 (gamma >= 3.1e-5): a step
+ *              that decays more forgets what came before it inside its
+ *              chunk to within 3.1e-5 instead of fully; across chunks and
+ *              in the state the decay is exact.
  *   mu_out, nu_out: optional (both or neither), as la_forward_state.
- *   The workspace is la_forward_workspace_bytes(...) of the same sizes.
+ *   workspace: la_forward_gated_workspace_bytes(...) of the same sizes and
+ *              layout, with the synchronisation area of la_forward zero
+ *              (the per-row path never writes it).
  */
 la_status la_forward_gated(const void *q, const void *k, const void *v,
                            void *out, int B, int H, int64_t n, int d,

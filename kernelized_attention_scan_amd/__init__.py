@@ -11,7 +11,8 @@ from ._binding import (LA_BF16, LA_F32, LIB_PATH, MAP_ELU1, MAP_IDENTITY,
                        decode_step_gated, featmap,
                        forward, forward_train,
                        forward_gated, forward_noalloc,
-                       forward_workspace_bytes, linear_attention,
+                       forward_workspace_bytes, gated_workspace_bytes,
+                       linear_attention,
                        load_library, new_workspace, set_exchange_spin_limit,
                        workspace_check)
 
@@ -19,6 +20,7 @@ __all__ = ["forward", "forward_train", "backward", "backward_workspace_bytes",
            "linear_attention",
            "forward_gated", "forward_noalloc", "decode_step",
            "decode_step_gated", "featmap", "forward_workspace_bytes",
+           "gated_workspace_bytes",
            "new_workspace", "workspace_check", "cached_workspace",
            "set_exchange_spin_limit",
            "load_library", "LinAttnError", "LIB_PATH", "SYMBOLS", "MAP_IDENTITY",

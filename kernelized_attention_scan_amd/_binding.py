@@ -31,7 +31,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
 SYMBOLS = ("la_featmap", "la_forward_workspace_bytes", "la_forward",
            "la_forward_state", "la_forward_train", "la_backward",
            "la_backward_workspace_bytes",
-           "la_forward_gated", "la_forward_noalloc",
+           "la_forward_gated", "la_forward_gated_workspace_bytes",
+           "la_forward_noalloc",
            "la_decode_step", "la_decode_step_gated", "la_workspace_check",
            "la_set_exchange_spin_limit", "la_status_str", "la_last_error")
 
@@ -89,6 +90,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                          i32, i32, vp, vp, i32, i32, i32, vp,
                                          vp, vp, vp]
         lib.la_forward_gated.restype = i32
+        lib.la_forward_gated_workspace_bytes.argtypes = [
+            i32, i32, i64, i32, i32, i32, i32, i32, i32]
+        lib.la_forward_gated_workspace_bytes.restype = sz
         lib.la_decode_step_gated.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32,
                                              i32, i32, i32, vp, vp, i32, i32,
                                              vp]
@@ -221,6 +225,16 @@ def forward_workspace_bytes(B: int, H: int, n: int, d: int, d_feat: int,
     return int(load_library().la_forward_workspace_bytes(
         B, H, n, d, d_feat, _map_code(feature_map), _dtype_code(dtype),
         int(bool(causal))))
+
+
+def gated_workspace_bytes(B: int, H: int, n: int, d: int, d_feat: int,
+                          feature_map="elu1", layout="position",
+                          dtype=torch.bfloat16, causal: bool = True) -> int:
+    """Device workspace la_forward_gated needs for this decay layout (0 if
+    none or if rejected)."""
+    return int(load_library().la_forward_gated_workspace_bytes(
+        B, H, n, d, d_feat, _map_code(feature_map), _layout_code(layout),
+        _dtype_code(dtype), int(bool(causal))))
 
 
 def featmap(x: torch.Tensor, feature_map="elu1", omega=None,
@@ -437,8 +451,9 @@ def forward_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                   workspace: Optional[torch.Tensor] = None,
                   mu_out: Optional[torch.Tensor] = None,
                   nu_out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """forward() with a decay exp(log_decay) per position (la_forward_gated):
-    log_decay is fp32 [B, H, n] for layout "position"."""
+    """forward() with a decay exp(log_decay) per position and/or state row
+    (la_forward_gated): log_decay is fp32 [B, H, n] for layout "position",
+    [H, d_feat] for "channel" and [B, H, n, d_feat] for "both"."""
     lib = load_library()
     if q.dim() != 4 or v.dim() != 4 or q.shape != k.shape:
         raise ValueError("q, k must be [B,H,n,d_qk] and v [B,H,n,d]")
@@ -477,8 +492,8 @@ def forward_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             (mu_out, "mu_out"), (nu_out, "nu_out"))
     if out is None:
         out = torch.empty_like(v)
-    need = lib.la_forward_workspace_bytes(B, H, n, d, d_feat, mapk, dt,
-                                          int(bool(causal)))
+    need = lib.la_forward_gated_workspace_bytes(B, H, n, d, d_feat, mapk, lay,
+                                                dt, int(bool(causal)))
     if need and workspace is None:
         workspace = _workspace(need, v.device)
     if need and workspace.numel() < need:

@@ -173,6 +173,66 @@ la_status plan_forward(int B, int H, int64_t n, int d, int d_feat, int map,
   return LA_OK;
 }
 
+// Plan of the forward with a decay per state row: segments of whole
+// 16-row chunks, their aggregates after the synchronisation area (which it
+// never writes, so a workspace shared with la_forward keeps that area zero),
+// then Q', K' for the Performer map.
+struct RowPlan {
+  const la::RowOps *ops = nullptr;
+  int64_t seg_len = 0;
+  int nseg = 0;
+  size_t agg_bytes = 0;   // [units][nseg + 1] aggregate slots
+  size_t feat_bytes = 0;  // one of Q', K' (PERFORMER)
+  size_t feat_offset() const { return la::kSyncBytes + agg_bytes; }
+  size_t total() const {
+    return agg_bytes + feat_bytes > 0 ? feat_offset() + 2 * feat_bytes : 0;
+  }
+};
+
+la_status plan_rows(int B, int H, int64_t n, int d, int d_feat, int map,
+                    int dtype, int causal, RowPlan *p) {
+  if (B < 0 || H < 0 || n < 0)
+    return fail(LA_ERR_INVALID_ARG, "negative size: B=%d H=%d n=%lld", B, H,
+                static_cast<long long>(n));
+  if (!valid_map(map)) return fail(LA_ERR_INVALID_ARG, "unknown map %d", map);
+  if (!valid_dtype(dtype)) return fail(LA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (causal != 0 && causal != 1)
+    return fail(LA_ERR_INVALID_ARG, "causal must be 0 or 1, got %d", causal);
+  if (d <= 0 || d_feat <= 0)
+    return fail(LA_ERR_INVALID_ARG, "non-positive d=%d d_feat=%d", d, d_feat);
+  if (map == LA_MAP_ELU1 && d_feat != d)
+    return fail(LA_ERR_INVALID_ARG, "ELU1 needs d_feat == d (got %d, %d)", d_feat, d);
+  if (!supported_d(d) || !supported_feat(d_feat))
+    return fail(LA_ERR_UNSUPPORTED, "unsupported d=%d d_feat=%d", d, d_feat);
+  p->ops = la::row_ops(d, d_feat, dtype == LA_BF16 ? 1 : 0);
+  if (!p->ops)
+    return fail(LA_ERR_UNSUPPORTED, "no per-row decay kernel for d=%d d_feat=%d",
+                d, d_feat);
+  const int64_t units = static_cast<int64_t>(B) * H;
+  if (units == 0 || n == 0) return LA_OK;
+  if (units > (int64_t{1} << 30) || n > (int64_t{1} << 40) ||
+      units * n > (int64_t{1} << 46))
+    return fail(LA_ERR_UNSUPPORTED, "sizes too large");
+  const int64_t C = la::kRowChunk;
+  const int64_t nch = (n + C - 1) / C;
+  const int64_t k = la::row_segments(units, n);
+  const int64_t cps = (nch + k - 1) / k;
+  p->seg_len = cps * C;
+  p->nseg = static_cast<int>((n + p->seg_len - 1) / p->seg_len);
+  if (units * p->nseg > (int64_t{1} << 31) - 1 ||
+      units * ((p->ops->slot_floats + 255) / 256) > (int64_t{1} << 31) - 1)
+    return fail(LA_ERR_UNSUPPORTED, "too many workgroups");
+  p->agg_bytes = !causal || p->nseg > 1
+                     ? align256(static_cast<size_t>(units) * (p->nseg + 1) *
+                                p->ops->slot_floats * sizeof(float))
+                     : 0;
+  p->feat_bytes = map == LA_MAP_PERFORMER
+                      ? align256(static_cast<size_t>(units * n) * d_feat *
+                                 elem_size(dtype))
+                      : 0;
+  return LA_OK;
+}
+
 }  // namespace
 
 // la_forward and la_forward_state; mu_out / nu_out (both or neither) receive
@@ -258,6 +318,73 @@ static la_status forward_impl(const void *q, const void *k, const void *v, void 
     return ok();
   } catch (...) {
     return fail(LA_ERR_HIP, "unexpected exception in la_forward");
+  }
+}
+
+// la_forward_gated with a decay per state row (lam [H][d_feat], or
+// [B][H][n][d_feat] with per_position).
+static la_status forward_rows_impl(const void *q, const void *k, const void *v,
+                                   void *out, int B, int H, int64_t n, int d,
+                                   int d_feat, int map, const float *omega,
+                                   const float *log_decay, int per_position,
+                                   int causal, int dtype, void *workspace,
+                                   float *mu_out, float *nu_out, void *stream) {
+  try {
+    RowPlan p;
+    const la_status st =
+        plan_rows(B, H, n, d, d_feat, map, dtype, causal, &p);
+    if (st != LA_OK) return st;
+    const int64_t units = static_cast<int64_t>(B) * H;
+    if (units == 0) return ok();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (n == 0) {  // no positions: the handed-out state is zero
+      if (!mu_out) return ok();
+      hipError_t e = la::launch_fill_zero(mu_out, units * d_feat * d, s);
+      if (e == hipSuccess) e = la::launch_fill_zero(nu_out, units * d_feat, s);
+      if (e != hipSuccess) return hip_fail(e, "la_forward_gated zero state");
+      return ok();
+    }
+    if (!q || !k || !v || !out)
+      return fail(LA_ERR_INVALID_ARG, "null q, k, v or out");
+    if (map == LA_MAP_PERFORMER && !omega)
+      return fail(LA_ERR_INVALID_ARG, "PERFORMER needs omega");
+    if (p.total() > 0 && !workspace)
+      return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes required", p.total());
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    const void *qf = q, *kf = k;
+    if (map == LA_MAP_PERFORMER) {
+      unsigned char *fq = ws + p.feat_offset(), *fk = fq + p.feat_bytes;
+      hipError_t e = la::launch_featmap_performer(q, fq, omega, units * n, d,
+                                                  d_feat, dtype, dtype, s);
+      if (e == hipSuccess)
+        e = la::launch_featmap_performer(k, fk, omega, units * n, d, d_feat,
+                                         dtype, dtype, s);
+      if (e != hipSuccess) return hip_fail(e, "la_forward_gated feature map");
+      qf = fq;
+      kf = fk;
+    }
+    la::RowArgs a;
+    a.q = qf;
+    a.k = kf;
+    a.v = v;
+    a.out = out;
+    a.lam = log_decay;
+    a.per_position = per_position;
+    a.H = H;
+    a.n = n;
+    a.seg_len = p.seg_len;
+    a.nseg = p.nseg;
+    a.elu1 = map == LA_MAP_ELU1;
+    a.skip_last = 0;
+    a.agg = p.agg_bytes > 0 ? reinterpret_cast<float *>(ws + la::kSyncBytes)
+                            : nullptr;
+    a.mu_out = mu_out;
+    a.nu_out = nu_out;
+    const hipError_t e = p.ops->run(a, units, causal, s);
+    if (e != hipSuccess) return hip_fail(e, "la_forward_gated launch");
+    return ok();
+  } catch (...) {
+    return fail(LA_ERR_HIP, "unexpected exception in la_forward_gated");
   }
 }
 
@@ -361,6 +488,25 @@ size_t la_forward_workspace_bytes(int B, int H, int64_t n, int d, int d_feat,
     // The workspace does not depend on decay; size it for the plain variant.
     const la_status st =
         plan_forward(B, H, n, d, d_feat, map, dtype, causal, 0, &p);
+    g_last_error = saved;
+    if (st != LA_OK) return 0;
+    return p.total();
+  } catch (...) {
+    return 0;
+  }
+}
+
+size_t la_forward_gated_workspace_bytes(int B, int H, int64_t n, int d,
+                                        int d_feat, la_map map,
+                                        la_decay_layout layout, la_dtype dtype,
+                                        int causal) {
+  if (layout == LA_LD_POSITION)
+    return la_forward_workspace_bytes(B, H, n, d, d_feat, map, dtype, causal);
+  if (layout != LA_LD_CHANNEL && layout != LA_LD_BOTH) return 0;
+  try {
+    const std::string saved = g_last_error;
+    RowPlan p;
+    const la_status st = plan_rows(B, H, n, d, d_feat, map, dtype, causal, &p);
     g_last_error = saved;
     if (st != LA_OK) return 0;
     return p.total();
@@ -571,16 +717,14 @@ la_status la_forward_gated(const void *q, const void *k, const void *v,
   if (layout != LA_LD_CHANNEL && layout != LA_LD_POSITION &&
       layout != LA_LD_BOTH)
     return fail(LA_ERR_INVALID_ARG, "unknown decay layout %d", layout);
-  if (layout != LA_LD_POSITION)
-    return fail(LA_ERR_UNSUPPORTED,
-                "la_forward_gated: only the per-position layout is built for "
-                "the chunked forward (per-row decays need decay weights "
-                "inside the feature contraction); the decode step takes "
-                "every layout");
   if ((mu_out == nullptr) != (nu_out == nullptr))
     return fail(LA_ERR_INVALID_ARG, "mu_out and nu_out go together");
   if (!log_decay && static_cast<int64_t>(B) * H > 0 && n > 0)
     return fail(LA_ERR_INVALID_ARG, "null log_decay");
+  if (layout != LA_LD_POSITION)
+    return forward_rows_impl(q, k, v, out, B, H, n, d, d_feat, map, omega,
+                             log_decay, layout == LA_LD_BOTH ? 1 : 0, causal,
+                             dtype, workspace, mu_out, nu_out, stream);
   return forward_impl(q, k, v, out, B, H, n, d, d_feat, map, omega, nullptr,
                       causal, dtype, workspace, mu_out, nu_out, stream, 0,
                       log_decay ? log_decay : nullptr);

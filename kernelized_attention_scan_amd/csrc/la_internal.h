@@ -95,6 +95,39 @@ const FwdOps *fwd_ops_f32(int d, int d_feat);
 // when not built for these sizes.
 const FwdOps *fwd_ops_bf16_performer(int d, int d_feat);
 
+// Arguments of the chunked forward with a decay per state row (one value
+// per row and head, or one per position and row).
+struct RowArgs {
+  const void *q, *k, *v;  // [units][n][d_feat], [units][n][d_feat], [units][n][d]
+  void *out;              // [units][n][d]
+  const float *lam;       // log g: [H][d_feat] or [units][n][d_feat]
+  int per_position;       // 0: lam is [H][d_feat]; 1: [units][n][d_feat]
+  int H;
+  int64_t n;
+  int64_t seg_len;        // multiple of kRowChunk
+  int nseg;
+  int elu1;               // phi = elu + 1 on q, k (else they are features)
+  int skip_last;          // set by the launcher for the aggregate launch
+  float *agg;             // [units][nseg + 1][slot_floats] aggregates
+  float *mu_out, *nu_out; // final state (both or neither), or null
+};
+constexpr int kRowChunk = 16;
+
+// Launch set of one (storage type, d, d_feat) instance of that forward.
+struct RowOps {
+  int slot_floats;  // floats per aggregate slot
+  // Enqueue the aggregate, carry and readout launches (the first two only
+  // for several segments or the non-causal form).
+  hipError_t (*run)(const RowArgs &args, int64_t units, int causal,
+                    hipStream_t stream);
+};
+// nullptr for sizes that are not built; dtype 0 fp32, 1 bf16.
+const RowOps *row_ops(int d, int d_feat, int dtype);
+const RowOps *row_ops_bf16(int d, int d_feat);
+const RowOps *row_ops_f32(int d, int d_feat);
+// Segments per unit of that forward.
+int row_segments(int64_t units, int64_t n);
+
 // Feature map launchers.  dtype codes: 0 fp32, 1 bf16.
 hipError_t launch_featmap_elementwise(const void *x, void *y, int64_t count,
                                       int elu1, int in_dt, int out_dt,

@@ -94,13 +94,17 @@ PERFORMER = PrefillConfig("performer_B4H8n8192d64m256", B=4, H=8, n=8192, d=64,
 # Input-dependent (per-position) decay at the decayed workload's sizes.
 GATED = PrefillConfig("gated_elu1_B2H16n65536d128", B=2, H=16, n=65536,
                       d=128, gate=(-3.0, -1.0))
+# A decay per state row (per channel, [H, d_feat]) at the same sizes; its
+# log decays come from row_log_decay.
+CHANNEL = PrefillConfig("channel_elu1_B2H16n65536d128", B=2, H=16, n=65536,
+                        d=128)
 DECODE = DecodeConfig("decode_S256H32d128_a0.99", S=256, H=32, d=128)
 # the same step with a decay per state row (per channel, [H, d_feat])
 DECODE_CHANNEL = DecodeConfig("decode_channel_S256H32d128", S=256, H=32,
                               d=128, a=None)
 
 PREFILL_CONFIGS = {c.name: c for c in (TINY_FP32, ELU1_CAUSAL, ELU1_NONCAUSAL,
-                                       DECAYED, PERFORMER, GATED)}
+                                       DECAYED, PERFORMER, GATED, CHANNEL)}
 
 
 def _round(x: torch.Tensor, dtype: torch.dtype) -> torch.Tensor:
@@ -164,3 +168,26 @@ def decode_channel_log_decay(cfg: DecodeConfig, seed: int = 0) -> torch.Tensor:
     g = torch.Generator("cpu").manual_seed(seed + 101)
     u = torch.rand((cfg.H, cfg.d_feat), generator=g)
     return torch.log1p(-(10.0 ** (-3.0 + 2.0 * u)))
+
+
+def row_log_decay(cfg: PrefillConfig, seed: int = 0, layout: str = "channel",
+                  lo: float = -3.0, hi: float = -1.0,
+                  d_feat: Optional[int] = None) -> torch.Tensor:
+    """Log decays per state row (fp32), from their own generator (seed + 202)
+    so the other prefill inputs of the same seed are unchanged:
+    "channel": [H, d_feat] = log(1 - 10^U(lo, hi));
+    "both": [B, H, n, d_feat] = A * softplus(z) with a rate per head and row
+    A = -10^U(lo, hi) [H, d_feat] and z [B, H, n, d_feat] ~ N(0, 1), the
+    per-position recipe of make_prefill applied row by row.  d_feat
+    overrides the config's feature width (features given directly)."""
+    g = torch.Generator("cpu").manual_seed(seed + 202)
+    df = d_feat or cfg.d_feat
+    u = torch.rand((cfg.H, df), generator=g)
+    if layout == "channel":
+        return torch.log1p(-(10.0 ** (lo + (hi - lo) * u))).to(torch.float32)
+    if layout != "both":
+        raise ValueError(f"unknown layout {layout!r}")
+    rate = -torch.pow(10.0, lo + (hi - lo) * u)
+    z = torch.randn((cfg.B, cfg.H, cfg.n, df), generator=g)
+    step = torch.nn.functional.softplus(z)
+    return (rate[None, :, None, :] * step).to(torch.float32).contiguous()

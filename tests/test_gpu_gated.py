@@ -231,30 +231,3 @@ def test_decode_gated(layout, dtype, mapk):
                                        mapk, f64(x["omega"]), f64(lam), mode)
     assert rel(out, ro) <= TOL[dtype]
     assert rel(mu, rmu) <= 1e-4 and rel(nu, rnu) <= 1e-4
-
-
-def test_forward_gated_rejects_per_row_layouts():
-    x = torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16, device="cuda")
-    lam = torch.zeros(2, 64, device="cuda")
-    with pytest.raises(K.LinAttnError) as e:
-        K.forward_gated(x, x, x, lam, "channel")
-    assert e.value.status == K._binding.LA_ERR_UNSUPPORTED
-
-
-def test_decode_channel_full_workload():
-    """The decode workload with a decay per state row (S=256 x H=32, d = d'
-    = 128, log decays log(1 - 10^U(-3, -1)) per head and channel): every
-    unit checked."""
-    cfg = I.DECODE_CHANNEL
-    x = I.make_decode(cfg, 0)
-    lam = I.decode_channel_log_decay(cfg, 0)
-    mu, nu = dev(x["mu"]), dev(x["nu"])
-    out = K.decode_step_gated(mu, nu, dev(x["q"]), dev(x["k"]), dev(x["v"]),
-                              dev(lam), "channel", "elu1")
-    torch.cuda.synchronize()
-    ro, rmu, rnu = oracle.decode_gated(f64(x["mu"]), f64(x["nu"]),
-                                       f64(x["q"]), f64(x["k"]), f64(x["v"]),
-                                       cfg.mapk, None, f64(lam),
-                                       oracle.LD_CHANNEL)
-    assert rel(out, ro) <= 1e-2
-    assert rel(mu, rmu) <= 1e-4 and rel(nu, rnu) <= 1e-4

@@ -336,3 +336,66 @@ def test_binding_backward_rejects_small_workspace():
     ws = torch.zeros(16, dtype=torch.uint8)
     with pytest.raises(ValueError):
         K.backward(x, x, x, x, den, x, workspace=ws)
+
+
+def test_gated_workspace_bytes(lib):
+    import torch
+    a256 = lambda x: (x + 255) // 256 * 256
+    sync = 256 + 512 * 128
+    # the per-position layout shares la_forward's workspace
+    assert K.gated_workspace_bytes(4, 8, 4096, 64, 64, layout="position") == \
+        K.forward_workspace_bytes(4, 8, 4096, 64, 64)
+    # a decay per row: 16-row chunks, about 512 workgroups in all and at
+    # most 16 segments per unit; units * (nseg + 1) aggregate slots of
+    # d' x d state floats + d' (nu) + d' (summed log2 decay), after the
+    # synchronisation area of la_forward (never written by this path)
+    for layout in ("channel", "both"):
+        ws = K.gated_workspace_bytes(4, 8, 4096, 64, 64, layout=layout)
+        nseg = 16                # 512 / 32 units, 256 chunks
+        assert ws == sync + a256(32 * (nseg + 1) * (64 * 64 + 2 * 64) * 4)
+    # d' below 32 is padded to 32 in the slot (its state rows 16..31 stay 0)
+    ws = K.gated_workspace_bytes(1, 2, 100, 128, 16, "identity", "channel")
+    nseg = 7                     # 7 chunks of 16 rows, 256 target per unit
+    assert ws == sync + a256(2 * (nseg + 1) * (128 * 32 + 2 * 32) * 4)
+    # causal over one segment: no aggregates, no workspace
+    assert K.gated_workspace_bytes(1, 1, 16, 64, 64, layout="channel") == 0
+    assert K.gated_workspace_bytes(600, 1, 4096, 64, 64, layout="channel") == 0
+    # non-causal always takes the aggregate and carry launches
+    assert K.gated_workspace_bytes(1, 1, 16, 64, 64, layout="channel",
+                                   causal=False) == \
+        sync + a256(2 * (64 * 64 + 2 * 64) * 4)
+    # Performer: Q', K' (d' wide, storage type) after the aggregates
+    wp = K.gated_workspace_bytes(1, 1, 16, 64, 256, "performer", "both")
+    assert wp == sync + 2 * a256(16 * 256 * 2)
+    wf = K.gated_workspace_bytes(1, 1, 16, 64, 256, "performer", "both",
+                                 dtype=torch.float32)
+    assert wf == sync + 2 * a256(16 * 256 * 4)
+    # rejected arguments report 0
+    assert K.gated_workspace_bytes(1, 1, 64, 48, 48, layout="channel") == 0
+    assert K.gated_workspace_bytes(1, 1, 64, 64, 32, "elu1", "both") == 0
+    assert lib.la_forward_gated_workspace_bytes(1, 1, 64, 64, 64, 1, 7, 1,
+                                                1) == 0
+
+
+def test_gated_rows_rejects(lib):
+    f = lib.la_forward_gated
+    lam = FAKE
+    # ELU1 needs d_feat == d; unsupported sizes; bad causal; null pointers
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 32, 1, None, lam, 0, 1, 1,
+             FAKE, None, None, None) == B.LA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 48, 48, 1, None, lam, 2, 1, 1,
+             FAKE, None, None, None) == B.LA_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 64, 1, None, lam, 0, 2, 1,
+             FAKE, None, None, None) == B.LA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 64, 1, None, None, 0, 1, 1,
+             FAKE, None, None, None) == B.LA_ERR_INVALID_ARG
+    assert f(None, FAKE, FAKE, FAKE, 1, 1, 64, 64, 64, 1, None, lam, 2, 1, 1,
+             FAKE, None, None, None) == B.LA_ERR_INVALID_ARG
+    # Performer without omega; missing workspace where one is needed
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 128, 2, None, lam, 0, 1, 1,
+             FAKE, None, None, None) == B.LA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 64, 1, None, lam, 0, 0, 1,
+             None, None, None, None) == B.LA_ERR_WORKSPACE
+    # empty sizes are no-ops
+    assert f(FAKE, FAKE, FAKE, FAKE, 0, 1, 64, 64, 64, 1, None, lam, 0, 1, 1,
+             None, None, None, None) == B.LA_OK
