@@ -60,6 +60,8 @@ KERNEL_SOURCES = {
 def kernel_kind(workload: str) -> str:
     if workload.startswith("decode"):
         return "decode"
+    if workload == "channel":
+        return "rows"
     return workload if workload == "backward" else "forward"
 
 
@@ -78,7 +80,7 @@ def workloads():
     return {"elu1": I.ELU1_CAUSAL, "decayed": I.DECAYED,
             "performer": I.PERFORMER, "tiny": I.TINY_FP32,
             "decode": I.DECODE, "noncausal": I.ELU1_NONCAUSAL,
-            "gated": I.GATED, "backward": I.DECAYED,
+            "gated": I.GATED, "backward": I.DECAYED, "channel": I.CHANNEL,
             "decode_channel": I.DECODE_CHANNEL}
 
 
@@ -86,11 +88,14 @@ def esize(dtype) -> int:
     return 2 if "bfloat16" in str(dtype) else 4
 
 
-def prefill_algorithmic(cfg):
+def prefill_algorithmic(cfg, channel: bool = False):
     """Bytes and flops the method itself must move / compute per step: read
-    q, k, v and write out once; 4 d' d + 4 d' flops per token (state update
-    and readout), plus the Performer projection of q and k."""
+    q, k, v and write out once (with a decay per channel, read its [H,
+    d_feat] log decays once too); 4 d' d + 4 d' flops per token (state
+    update and readout), plus the Performer projection of q and k."""
     byts = cfg.tokens * 4 * cfg.d * esize(cfg.dtype)
+    if channel:
+        byts += cfg.H * cfg.d_feat * 4
     df = cfg.d_feat
     flops = cfg.tokens * (4 * df * cfg.d + 4 * df)
     if cfg.mapk == 2:
@@ -159,10 +164,15 @@ def time_loop(torch, fn, steps: int, stream):
 # CPU baselines: the fp64 oracle, as it stands, on a bounded sample
 # --------------------------------------------------------------------------
 
-def cpu_baseline_prefill(cfg, seed: int, budget_s: float = 20.0):
+def cpu_baseline_prefill(cfg, seed: int, budget_s: float = 20.0,
+                         channel: bool = False):
     import oracle
     from kernelized_attention_scan_amd import inputs as I
     x = I.make_prefill(cfg, seed)
+    # a decay per channel: [H, d_feat] per head, repeated for each batch row
+    # of the flattened units
+    chl = (I.row_log_decay(cfg, seed, "channel").repeat(cfg.B, 1)
+           if channel else None)
     f64 = lambda t: None if t is None else t.double().numpy()
     units = cfg.B * cfg.H
     flat = lambda t: t.reshape(1, units, cfg.n, t.shape[-1])
@@ -175,6 +185,10 @@ def cpu_baseline_prefill(cfg, seed: int, budget_s: float = 20.0):
 
     def run(take):
         sl = slice(0, take)
+        if chl is not None:    # the gated recurrence, a decay per channel
+            return oracle.forward_gated(
+                f64(q[:, sl]), f64(k[:, sl]), f64(v[:, sl]), cfg.mapk, om,
+                f64(chl[sl]), oracle.LD_CHANNEL, cfg.causal)
         if lam is not None:    # the gated recurrence, per-position decay
             return oracle.forward_gated(
                 f64(q[:, sl]), f64(k[:, sl]), f64(v[:, sl]), cfg.mapk, om,
@@ -244,20 +258,34 @@ def cpu_baseline_decode(cfg, seed: int, budget_s: float = 10.0,
 
 def prefill_leg(torch, K, I, cfg, args, dev):
     mapname = I.MAP_NAMES[cfg.mapk]
-    byts, flops = prefill_algorithmic(cfg)
+    channel = args.workload == "channel"
+    byts, flops = prefill_algorithmic(cfg, channel)
     set_bytes = byts + (cfg.d * cfg.m * 4 if cfg.mapk == 2 else 0)
     nsets = max(1, min(8, math.ceil(1.2 * MALL_BYTES / set_bytes)))
     sets = []
     for i in range(nsets):
         x = I.make_prefill(cfg, args.seed + i)
+        if channel:
+            x["row_log_decay"] = I.row_log_decay(cfg, args.seed + i, "channel")
         sets.append({k: (None if t is None else t.to(dev)) for k, t in x.items()})
     outs = [torch.empty_like(s["v"]) for s in sets]
-    ws = K.new_workspace(cfg.B, cfg.H, cfg.n, cfg.d, cfg.d_feat, mapname,
-                         cfg.dtype, cfg.causal, device=dev)
+    if channel:
+        ws = torch.zeros(max(1, K.gated_workspace_bytes(
+            cfg.B, cfg.H, cfg.n, cfg.d, cfg.d_feat, mapname, "channel",
+            cfg.dtype, cfg.causal)), dtype=torch.uint8, device=dev)
+    else:
+        ws = K.new_workspace(cfg.B, cfg.H, cfg.n, cfg.d, cfg.d_feat, mapname,
+                             cfg.dtype, cfg.causal, device=dev)
     stream = torch.cuda.current_stream(dev)   # the library launches here
 
     def step(i):
         s = sets[i % nsets]
+        if channel:                      # a decay per channel
+            K.forward_gated(s["q"], s["k"], s["v"], s["row_log_decay"],
+                            "channel", feature_map=mapname, omega=s["omega"],
+                            causal=cfg.causal, out=outs[i % nsets],
+                            workspace=ws)
+            return
         if s["log_decay"] is not None:   # per-position decay
             K.forward_gated(s["q"], s["k"], s["v"], s["log_decay"],
                             "position", feature_map=mapname, omega=s["omega"],
@@ -281,7 +309,14 @@ def prefill_leg(torch, K, I, cfg, args, dev):
     fused = cfg.mapk == 2 and K.forward_workspace_bytes(
         cfg.B, cfg.H, cfg.n, cfg.d, cfg.m, "performer", cfg.dtype,
         cfg.causal) < 2 * cfg.tokens * cfg.m * esz
-    if cfg.mapk != 2 or fused:
+    if channel:
+        # one call per step: three launches -- the segment aggregates, the
+        # carry scan and the readout -- timed together
+        kern = {"kernel": "la_fwd_rows_kernel (aggregates) + "
+                          "la_fwd_rows_carry_kernel + la_fwd_rows_kernel "
+                          "(readout) per step",
+                "ms": ms, "bytes": byts, "flops": flops}
+    elif cfg.mapk != 2 or fused:
         # one kernel per step: the chunked forward (Performer: map fused)
         kern = {"kernel": "la_fwd_kernel (chunked "
                           + ("causal" if cfg.causal else
@@ -333,6 +368,8 @@ def prefill_leg(torch, K, I, cfg, args, dev):
             "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H,
                        "n": cfg.n, "d": cfg.d, "d_feat": cfg.d_feat,
                        "map": mapname, "decay": cfg.decay, "gate": cfg.gate,
+                       "channel_decay": ("log(1 - 10^U(-3,-1)) [H, d_feat]"
+                                         if channel else None),
                        "causal": cfg.causal, "buffer_sets": nsets,
                        "seed": args.seed}}
 
@@ -566,8 +603,10 @@ def main() -> int:
             line["cpu_baseline"] = cpu_baseline_decode(
                 cfg, args.seed, channel=args.workload == "decode_channel")
         else:
-            line["cpu_baseline"] = (cpu_baseline_backward if is_bwd
-                                    else cpu_baseline_prefill)(cfg, args.seed)
+            line["cpu_baseline"] = (
+                cpu_baseline_backward(cfg, args.seed) if is_bwd else
+                cpu_baseline_prefill(cfg, args.seed,
+                                     channel=args.workload == "channel"))
     print(json.dumps(line), flush=True)
     return 0
 

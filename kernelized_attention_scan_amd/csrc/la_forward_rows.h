@@ -299,8 +299,12 @@ __device__ __forceinline__ void store8(float *p, float (&x)[8]) {
 // PHASE 0: causal readout; 1: segment aggregates; 2: non-causal readout.
 // PP: the decay is given per position and row (else per row only; the
 // non-causal readout reads no decay).
+// Two waves per SIMD where the state fits beside them (bf16 operands,
+// d' <= 128): the chunk loop is a chain of dependent steps, and a second
+// workgroup per CU hides their latency.
 template <typename T, int D, int DF, int PHASE, bool PP>
-__global__ __launch_bounds__(kRowThreads) void la_fwd_rows_kernel(RowArgs a) {
+__global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(
+    sizeof(T) == 2 && DF <= 128 ? 2 : 1))) void la_fwd_rows_kernel(RowArgs a) {
   using S = RowShape<T, D, DF>;
   constexpr int DFP = S::DFP, NFT = S::NFT, NKB = S::NKB, NEB = S::NEB,
                 EPW = S::EPW, NG = S::NG, NIT = S::NIT, LQ = S::LQ, LV = S::LV;
@@ -559,8 +563,11 @@ __global__ __launch_bounds__(kRowThreads) void la_fwd_rows_kernel(RowArgs a) {
         frag16_from_acc(pf, pt);
         den += wave_sum_groups(frag16_sum(pf));
       }
+      // reciprocal of each output row's denominator (hardware, within
+      // 1 ulp: far below the storage rounding that follows)
+      const float rden = __builtin_amdgcn_rcpf(den);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dr[r] = __shfl(den, 4 * g + r);
+      for (int r = 0; r < 4; ++r) dr[r] = __shfl(rden, 4 * g + r);
     }
 
 #pragma unroll
@@ -588,7 +595,7 @@ __global__ __launch_bounds__(kRowThreads) void la_fwd_rows_kernel(RowArgs a) {
         T *o = og + (r0 + 4 * g) * D + 16 * jb + i16;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (4 * g + r < rows) o[r * D] = from_f32<T>(acc[r] / dr[r]);
+          if (4 * g + r < rows) o[r * D] = from_f32<T>(acc[r] * dr[r]);
       }
       if (CARRY) {
 #pragma unroll
