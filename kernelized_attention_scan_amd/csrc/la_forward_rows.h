@@ -67,13 +67,20 @@ struct RowShape {
   static constexpr int EPW = (NEB + 3) / 4;      // column blocks per wave
   static constexpr int NG = DFP / 8;             // 8-feature groups per row
   static constexpr int NIT = (NG + 15) / 16;     // groups per scaling thread
+  // Row strides by how a tile is read.  Q~, Q^ and K^ give each lane a row
+  // (8-byte reads at column 4 (lane / 16)): a stride of 8 (mod 32) bf16
+  // elements spreads 16 rows x 2 column groups over all 64 banks.  K~ and V
+  // are read transposed (ds_read_b64_tr_b16: 4 rows x 4 column quads per
+  // 16 lanes), which wants 16 (mod 32).  fp32 tiles: 4 floats of padding.
   static constexpr int PAD = 16 / static_cast<int>(sizeof(T));
-  static constexpr int LQ = DFP + PAD;           // operand row stride
-  static constexpr int LV = D + PAD;             // value row stride
+  static constexpr int PADT = sizeof(T) == 2 ? 16 : 4;
+  static constexpr int LQ = DFP + PAD;           // Q~, Q^, K^ row stride
+  static constexpr int LT = DFP + PADT;          // K~ row stride
+  static constexpr int LV = D % 32 == 16 && sizeof(T) == 2 ? D : D + PADT;
   static constexpr int TILE = kRowC * LQ;        // elements per operand tile
   static constexpr int VE = 16 / static_cast<int>(sizeof(T));  // per 16 B
   static constexpr int NVG = kRowC * D / VE;     // 16-byte value groups
-  static constexpr int OFF_V = 4 * TILE * static_cast<int>(sizeof(T));
+  static constexpr int OFF_V = (3 * TILE + kRowC * LT) * static_cast<int>(sizeof(T));
   static constexpr int OFF_DEN = OFF_V + kRowC * LV * static_cast<int>(sizeof(T));
   static constexpr int OFF_DEC = OFF_DEN + 4 * kRowC * 4;
   static constexpr int BUF = OFF_DEC + DFP * 4;
@@ -307,7 +314,8 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(
     sizeof(T) == 2 && DF <= 128 ? 2 : 1))) void la_fwd_rows_kernel(RowArgs a) {
   using S = RowShape<T, D, DF>;
   constexpr int DFP = S::DFP, NFT = S::NFT, NKB = S::NKB, NEB = S::NEB,
-                EPW = S::EPW, NG = S::NG, NIT = S::NIT, LQ = S::LQ, LV = S::LV;
+                EPW = S::EPW, NG = S::NG, NIT = S::NIT, LQ = S::LQ, LT = S::LT,
+                LV = S::LV;
   constexpr bool READ = PHASE != 1;   // forms outputs
   constexpr bool CARRY = PHASE != 2;  // runs the recurrence through the chunk
   constexpr bool SCORE = PHASE == 0;  // intra-chunk scores
@@ -345,6 +353,8 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(
   };
   float nu[NIT][8];       // nu of this thread's features (same in all 16 rows)
   float dsum[NIT][8];     // summed log2 decay of the segment (per position)
+  float rr[NIT][8];       // aggregates: decay from the chunk's end to the
+                          // segment's end (chunks run last to first)
   RowFac fc[NIT];         // one decay per row: factors of a full chunk
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
@@ -353,6 +363,7 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(
     for (int e = 0; e < 8; ++e) {
       nu[it][e] = 0.f;
       dsum[it][e] = 0.f;
+      rr[it][e] = 1.f;
     }
     if (CARRY && !PP && j < NG) {
       float l[8], b[8];
@@ -497,15 +508,28 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(
           for (int e = 0; e < 8; ++e) x[e] = kv[e] * F.kh[e];
           store8(KH + t * LQ + f0, x);
         }
+        if constexpr (PHASE == 1) {
+          // aggregates run the chunks last to first: each chunk's carry
+          // operand takes the decay still to come in the segment, so the
+          // state and nu are plain sums (no per-chunk decay of the state)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = kv[e] * F.kt[e];
-        store8(KT + t * LQ + f0, x);
+          for (int e = 0; e < 8; ++e) x[e] = kv[e] * (F.kt[e] * rr[it][e]);
+          store8(KT + t * LT + f0, x);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          nu[it][e] = F.dec[e] * nu[it][e] + row_sum(x[e]);
-          if (PP) dsum[it][e] += F.tot[e];
+          for (int e = 0; e < 8; ++e) {
+            nu[it][e] += row_sum(x[e]);
+            rr[it][e] *= F.dec[e];
+            if (PP) dsum[it][e] += F.tot[e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = kv[e] * F.kt[e];
+          store8(KT + t * LT + f0, x);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            nu[it][e] = F.dec[e] * nu[it][e] + row_sum(x[e]);
         }
-        if (t == 0) {
+        if (PHASE == 0 && t == 0) {
           const f32x4 d0 = {F.dec[0], F.dec[1], F.dec[2], F.dec[3]};
           const f32x4 d1 = {F.dec[4], F.dec[5], F.dec[6], F.dec[7]};
           reinterpret_cast<f32x4 *>(DEC + f0)[0] = d0;
@@ -601,25 +625,31 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int i = 0; i < NFT; ++i) {
           Frag16<T> kf;
-          tr16(kf, KT, LQ, 4 * g, 16 * i, i16);
-          const f32x4 dc = *reinterpret_cast<const f32x4 *>(DEC + 16 * i + 4 * g);
-          f32x4 s0 = st[m][i];
+          tr16(kf, KT, LT, 4 * g, 16 * i, i16);
+          if constexpr (PHASE == 1) {
+            st[m][i] = mma16(kf, vf, st[m][i]);
+          } else {
+            const f32x4 dc = *reinterpret_cast<const f32x4 *>(DEC + 16 * i + 4 * g);
+            f32x4 s0 = st[m][i];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) s0[r] *= dc[r];
-          st[m][i] = mma16(kf, vf, s0);
+            for (int r = 0; r < 4; ++r) s0[r] *= dc[r];
+            st[m][i] = mma16(kf, vf, s0);
+          }
         }
       }
     }
   };
 
   // ---- chunk loop: one barrier per chunk ----------------------------------
-  issue(0);
-  scale(0, 0);
-  for (int c = 0; c < nch; ++c) {
+  // (step i handles chunk i; the aggregates take chunk nch - 1 - i)
+  auto chunk_at = [&](int i) { return PHASE == 1 ? nch - 1 - i : i; };
+  issue(chunk_at(0));
+  scale(chunk_at(0), 0);
+  for (int i = 0; i < nch; ++i) {
     __syncthreads();
-    if (c + 1 < nch) issue(c + 1);
-    matrix(c, c & 1);
-    if (c + 1 < nch) scale(c + 1, (c + 1) & 1);
+    if (i + 1 < nch) issue(chunk_at(i + 1));
+    matrix(chunk_at(i), i & 1);
+    if (i + 1 < nch) scale(chunk_at(i + 1), (i + 1) & 1);
   }
 
   // ---- results ------------------------------------------------------------
