@@ -266,10 +266,10 @@ size_t la_forward_gated_workspace_bytes(int B, int H, int64_t n, int d,
  *   layout   : LA_LD_POSITION ([B][H][n]), LA_LD_CHANNEL ([H][d_feat]) or
  *              LA_LD_BOTH ([B][H][n][d_feat]).  With a decay per row, the
  *              products of queries and keys inside a 16-position chunk
- *              floor each step's decay at 2^-15 (gamma >= 3.1e-5): a step
- *              that decays more forgets what came before it inside its
- *              chunk to within 3.1e-5 instead of fully; across chunks and
- *              in the state the decay is exact.
+ *              floor each step's decay at 2^-32: a step that decays more
+ *              forgets what came before it inside its chunk to within
+ *              2.3e-10 of its weight instead of fully; across chunks and in
+ *              the state the decay is exact.
  *   mu_out, nu_out: optional (both or neither), as la_forward_state.
  *   workspace: la_forward_gated_workspace_bytes(...) of the same sizes and
  *              layout, with the synchronisation area of la_forward zero

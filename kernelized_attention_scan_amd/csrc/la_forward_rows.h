@@ -19,27 +19,36 @@
 //                                   + sum_s (k'_s (1-g_s) 2^(L_15-L_s))^T v_s
 //   intra-chunk scores:   P[t][s] = sum_f q'_t[f] k'_s[f] (1-g_s[f])
 //                                   2^(L_t[f] - L_s[f]),  s <= t,
-// all factors at most 1 except the last, whose weight sits inside the sum
-// over f.  It is split about row 7 of the chunk:
-//   P = (q' * 2^(L_t - L_7)) (k' (1-g) 2^(L_7 - L_s))^T,
-// so each operand factor spans at most 8 steps of decay.  Inside this
-// product only, each step's log2 decay is floored at kRowFloor, which keeps
-// every factor within 2^(8 * 15) of one (finite and normal in bf16 and fp32);
-// a step whose decay is below 2^kRowFloor is one that forgets its past to
-// better than 3e-5 already.  Readout and carry factors use the exact decay.
+// the first two with factors at most 1; the last has its weight inside the
+// sum over f.  For s < t it is split about an anchor row a with s <= a < t:
+//   P[t][s] = (q'_t * 2^(L_t - L_a)) . (k'_s (1-g_s) 2^(L_a - L_s)),
+// both factors at most 1, so neither overflows, and one underflows only
+// where the weight itself is below 2^-126.  The anchor comes from the
+// highest bit b in which s and t differ (a binary hierarchy over the 16
+// rows): level b holds, in one tile, every row r as a key (bit b of r
+// clear) or as a query (bit b set) about a = r with bits 0..b-1 set and bit
+// b clear, so s (a key) and t (a query) of the same block meet at the same
+// a.  Four products (b = 3, 2, 1, 0), each tile both operands, and each
+// score taken from its level; the diagonal P[t][t] = sum_f q'_t k'_t
+// (1 - g_t) has no decay factor and is summed in fp32 by the scaling role.
+// Inside the scores only, a step's log2 decay is floored at kRowFloor (a
+// step that forgets more than all but 2^-32 of its past is taken to forget
+// exactly that), which keeps the sums finite for log decays of -inf.
 //
 // Work split of a workgroup (4 waves, one segment of one (batch, head) unit):
 //   * scaling role, every thread: row t = lane % 16 of the chunk and groups
 //     of 8 features j = lane / 16 + 4 wave (+ 16 per iteration); it loads
 //     q, k (and the decay) of its row and features, applies phi, forms the
-//     four scaled operands into LDS, the partial denominator q~ . nu, and
-//     keeps nu (replicated over the 16 row lanes) up to date;
+//     scaled operands into LDS, the partial denominator q~ . nu and
+//     diagonal score, and keeps nu (replicated over the 16 row lanes) up to
+//     date;
 //   * matrix role, wave w: value column blocks jb = w, w + 4, ...; it keeps
 //     those columns of the fp32 state in its accumulators (rows f = 16 i +
 //     4 (lane / 16) + r, column 16 jb + lane % 16), which feed the readout
 //     directly as operands ("split" k-assignment), and forms P^T itself.
 // One barrier per chunk: the scaling of chunk c + 1 fills the other LDS
-// buffer while the matrix role works on chunk c.
+// buffer while the matrix role works on chunk c (where two buffers do not
+// fit, one buffer and a second barrier).
 //
 // Segments of a unit run as separate workgroups in three launches: the
 // aggregates (each segment's state from zero, its nu and its summed log2
@@ -55,7 +64,7 @@ namespace la {
 
 constexpr int kRowC = kRowChunk;
 constexpr int kRowThreads = 256;
-constexpr float kRowFloor = -15.f;
+constexpr float kRowFloor = -32.f;
 constexpr float kLog2E = 1.4426950408889634f;
 
 template <typename T, int D, int DF>
@@ -67,7 +76,7 @@ struct RowShape {
   static constexpr int EPW = (NEB + 3) / 4;      // column blocks per wave
   static constexpr int NG = DFP / 8;             // 8-feature groups per row
   static constexpr int NIT = (NG + 15) / 16;     // groups per scaling thread
-  // Row strides by how a tile is read.  Q~, Q^ and K^ give each lane a row
+  // Row strides by how a tile is read.  Q~ and the score tiles give each lane a row
   // (8-byte reads at column 4 (lane / 16)): a stride of 8 (mod 32) bf16
   // elements spreads 16 rows x 2 column groups over all 64 banks.  K~ and V
   // are read transposed (ds_read_b64_tr_b16: 4 rows x 4 column quads per
@@ -80,11 +89,18 @@ struct RowShape {
   static constexpr int TILE = kRowC * LQ;        // elements per operand tile
   static constexpr int VE = 16 / static_cast<int>(sizeof(T));  // per 16 B
   static constexpr int NVG = kRowC * D / VE;     // 16-byte value groups
-  static constexpr int OFF_V = (3 * TILE + kRowC * LT) * static_cast<int>(sizeof(T));
+  // tiles: Q~, four score levels (row stride LQ), K~ (LT), V (LV), then the
+  // per-wave partial denominators and diagonal scores, the chunk's decay
+  static constexpr int OFF_V = (5 * TILE + kRowC * LT) * static_cast<int>(sizeof(T));
   static constexpr int OFF_DEN = OFF_V + kRowC * LV * static_cast<int>(sizeof(T));
-  static constexpr int OFF_DEC = OFF_DEN + 4 * kRowC * 4;
+  static constexpr int OFF_DIAG = OFF_DEN + 4 * kRowC * 4;
+  static constexpr int OFF_DEC = OFF_DIAG + 4 * kRowC * 4;
   static constexpr int BUF = OFF_DEC + DFP * 4;
-  static constexpr int lds_bytes = 2 * BUF;
+  // two LDS buffers (scaling of the next chunk overlaps the products of
+  // this one) where they fit, else one (fp32, d' = 256) and a second
+  // barrier per chunk
+  static constexpr int NB = 2 * BUF <= 160 * 1024 ? 2 : 1;
+  static constexpr int lds_bytes = NB * BUF;
   // aggregate slot: state in accumulator order, then nu, then sum log2 g
   static constexpr int NSTATE = NEB * NFT * 256;
   static constexpr int SLOT = NSTATE + 2 * DFP;
@@ -199,8 +215,9 @@ __device__ __forceinline__ float row_sum(float x) {
 // ---------------------------------------------------------------------------
 struct RowFac {
   float qt[8];   // readout operand:  2^L_t
-  float qh[8];   // score operand:    2^(Lf_t - Lf_7)
-  float kh[8];   // score operand:    (1 - g_t) 2^(Lf_7 - Lf_t)
+  float x[4][8]; // score operand of level b = 3 - i: as a key (bit b of t
+                 // clear) (1 - g_t) 2^(Lf_a - Lf_t), as a query 2^(Lf_t - Lf_a)
+  float b[8];    // 1 - g_t (diagonal score)
   float kt[8];   // carry operand:    (1 - g_t) 2^(L_15 - L_t)
   float tot[8];  // L_15 (log2 decay of the whole chunk)
   float dec[8];  // 2^L_15
@@ -218,15 +235,23 @@ __device__ __forceinline__ void channel_factors(RowFac &F, const float (&l)[8],
                                                 const float (&b)[8], int t,
                                                 int rows) {
   const int cnt = t + 1 < rows ? t + 1 : rows;
-  const int c7 = rows < 8 ? rows : 8;
   const bool live = t < rows;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float lf = fmaxf(l[e], kRowFloor);
-    const float eq = static_cast<float>(cnt - c7) * lf;
     F.qt[e] = __builtin_amdgcn_exp2f(steps_log2(cnt, l[e]));
-    F.qh[e] = __builtin_amdgcn_exp2f(eq);
-    F.kh[e] = live ? b[e] * __builtin_amdgcn_exp2f(-eq) : 0.f;
+    F.b[e] = live ? b[e] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int bit = 3 - i, lo = (1 << bit) - 1;
+      const int an = (t & ~(2 * lo + 1)) | lo;       // anchor row
+      const int ca = an + 1 < rows ? an + 1 : rows;  // live rows through it
+      const bool key = ((t >> bit) & 1) == 0;
+      // |live rows between the anchor and t| steps of decay, at most 1
+      const float ex = static_cast<float>(key ? ca - cnt : cnt - ca) * lf;
+      F.x[i][e] = key ? (live ? b[e] * __builtin_amdgcn_exp2f(ex) : 0.f)
+                      : __builtin_amdgcn_exp2f(ex);
+    }
     F.kt[e] = live ? b[e] * __builtin_amdgcn_exp2f(steps_log2(rows - cnt, l[e]))
                    : 0.f;
     F.tot[e] = steps_log2(rows, l[e]);
@@ -237,18 +262,26 @@ __device__ __forceinline__ void channel_factors(RowFac &F, const float (&l)[8],
 // One decay per position and row: scans over the 16 rows of the chunk (the
 // lanes of this thread's 16-lane row).  Padding rows carry l = 0, b = 0.
 __device__ __forceinline__ void position_factors(RowFac &F, const float (&l)[8],
-                                                 const float (&b)[8], int t) {
+                                                 const float (&b)[8], int t,
+                                                 int lane) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float p = row_prefix(l[e]);
     const float lf = fmaxf(l[e], kRowFloor);
     const float pf = row_prefix(lf);
-    const float pf7 = row_sum(t <= 7 ? lf : 0.f);
     const float sx = row_suffix_excl(l[e]);
     F.tot[e] = row_sum(l[e]);
     F.qt[e] = __builtin_amdgcn_exp2f(p);
-    F.qh[e] = __builtin_amdgcn_exp2f(pf - pf7);
-    F.kh[e] = b[e] * __builtin_amdgcn_exp2f(pf7 - pf);
+    F.b[e] = b[e];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int bit = 3 - i, lo = (1 << bit) - 1;
+      const int an = (t & ~(2 * lo + 1)) | lo;
+      const float pa = __shfl(pf, (lane & ~15) | an);  // prefix at the anchor
+      const bool key = ((t >> bit) & 1) == 0;
+      F.x[i][e] = key ? b[e] * __builtin_amdgcn_exp2f(pa - pf)
+                      : __builtin_amdgcn_exp2f(pf - pa);
+    }
     F.kt[e] = b[e] * __builtin_amdgcn_exp2f(sx);
     F.dec[e] = __builtin_amdgcn_exp2f(F.tot[e]);
   }
@@ -451,12 +484,13 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(
   auto scale = [&](int c, int b) {
     unsigned char *buf = smem + b * S::BUF;
     T *QT = reinterpret_cast<T *>(buf);
-    T *QH = QT + S::TILE, *KH = QT + 2 * S::TILE, *KT = QT + 3 * S::TILE;
+    T *XS = QT + S::TILE, *KT = QT + 5 * S::TILE;  // four score tiles
     T *VV = reinterpret_cast<T *>(buf + S::OFF_V);
     float *DENP = reinterpret_cast<float *>(buf + S::OFF_DEN);
+    float *DIAGP = reinterpret_cast<float *>(buf + S::OFF_DIAG);
     float *DEC = reinterpret_cast<float *>(buf + S::OFF_DEC);
     const int rows = rows_of(c);
-    float den = 0.f;
+    float den = 0.f, dg = 0.f;
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int j = g + 4 * w + 16 * it;
@@ -464,6 +498,7 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(
       const int f0 = 8 * j;
       const bool in = f0 < DF;
       RowFac F;
+      float qv[8];  // phi(q) of this row's features (also for the diagonal)
       if (CARRY) {
         if constexpr (PP) {
           float l[8], bb[8];
@@ -473,7 +508,7 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(
             bb[e] = -expm1f(l[e]);
             l[e] *= kLog2E;
           }
-          position_factors(F, l, bb, t);
+          position_factors(F, l, bb, t, lane);
         } else if (rows < kRowC) {
           float l[8], bb[8];
           channel_decay(j, l, bb);
@@ -483,7 +518,7 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(
         }
       }
       if (READ) {
-        float qv[8], x[8];
+        float x[8];
         raw8_float(rq[it], qv);
         if (a.elu1 && in)
           for (int e = 0; e < 8; ++e) qv[e] = elu_plus_one_fast(qv[e]);
@@ -493,9 +528,14 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int e = 0; e < 8; ++e) den += x[e] * nu[it][e];
         if (SCORE) {
+          // as a query at the levels where bit (3 - i) of t is set
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = qv[e] * F.qh[e];
-          store8(QH + t * LQ + f0, x);
+          for (int i = 0; i < 4; ++i)
+            if ((t >> (3 - i)) & 1) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) x[e] = qv[e] * F.x[i][e];
+              store8(XS + i * S::TILE + t * LQ + f0, x);
+            }
         }
       }
       if (CARRY) {
@@ -504,9 +544,16 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(
         if (a.elu1 && in)
           for (int e = 0; e < 8; ++e) kv[e] = elu_plus_one_fast(kv[e]);
         if (SCORE) {
+          // as a key at the others; and the diagonal score's part
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = kv[e] * F.kh[e];
-          store8(KH + t * LQ + f0, x);
+          for (int i = 0; i < 4; ++i)
+            if (((t >> (3 - i)) & 1) == 0) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) x[e] = kv[e] * F.x[i][e];
+              store8(XS + i * S::TILE + t * LQ + f0, x);
+            }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dg += qv[e] * kv[e] * F.b[e];
         }
         if constexpr (PHASE == 1) {
           // aggregates run the chunks last to first: each chunk's carry
@@ -540,6 +587,10 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(
     if (READ) {
       den = wave_sum_groups(den);
       if (g == 0) DENP[w * kRowC + t] = den;
+      if (SCORE) {
+        dg = wave_sum_groups(dg);
+        if (g == 0) DIAGP[w * kRowC + t] = dg;
+      }
     }
     if (CARRY) {
 #pragma unroll
@@ -558,9 +609,10 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(
     if (w >= NEB) return;
     const unsigned char *buf = smem + b * S::BUF;
     const T *QT = reinterpret_cast<const T *>(buf);
-    const T *QH = QT + S::TILE, *KH = QT + 2 * S::TILE, *KT = QT + 3 * S::TILE;
+    const T *XS = QT + S::TILE, *KT = QT + 5 * S::TILE;
     const T *VV = reinterpret_cast<const T *>(buf + S::OFF_V);
     const float *DENP = reinterpret_cast<const float *>(buf + S::OFF_DEN);
+    const float *DIAGP = reinterpret_cast<const float *>(buf + S::OFF_DIAG);
     const float *DEC = reinterpret_cast<const float *>(buf + S::OFF_DEC);
     const int rows = rows_of(c);
     const int64_t r0 = start + static_cast<int64_t>(c) * kRowC;
@@ -570,20 +622,36 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(
     if (READ) {
       float den = (DENP[t] + DENP[kRowC + t]) + (DENP[2 * kRowC + t] + DENP[3 * kRowC + t]);
       if (SCORE) {
-        // P^T: rows s = 4 g + r, column t = lane % 16; keep s <= t.
-        f32x4 pt = {0.f, 0.f, 0.f, 0.f};
+        // P^T: rows s = 4 g + r, column t = lane % 16; keep s <= t.  Level
+        // i's tile is both operands of its product (keys and queries in
+        // different rows); entry (t, s < t) comes from the level of the
+        // highest bit in which s and t differ, the diagonal from the
+        // scaling role's fp32 sums.
+        f32x4 pl[4];
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          Frag<T> fa, fb;
-          load_frag44(fa, KH + i16 * LQ + 32 * kb + 4 * g,
-                      KH + i16 * LQ + 32 * kb + 16 + 4 * g);
-          load_frag44(fb, QH + i16 * LQ + 32 * kb + 4 * g,
-                      QH + i16 * LQ + 32 * kb + 16 + 4 * g);
-          pt = mma(fa, fb, pt);
+        for (int i = 0; i < 4; ++i) pl[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) {
+            Frag<T> fx;
+            const T *xs = XS + i * S::TILE + i16 * LQ + 32 * kb;
+            load_frag44(fx, xs + 4 * g, xs + 16 + 4 * g);
+            pl[i] = mma(fx, fx, pl[i]);
+          }
         }
+        const float dg = (DIAGP[t] + DIAGP[kRowC + t]) +
+                         (DIAGP[2 * kRowC + t] + DIAGP[3 * kRowC + t]);
+        f32x4 pt;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (4 * g + r > i16) pt[r] = 0.f;
+        for (int r = 0; r < 4; ++r) {
+          const int sr = 4 * g + r, x = sr ^ i16;
+          pt[r] = sr > i16 ? 0.f
+                  : x == 0 ? dg
+                  : x >= 8 ? pl[0][r]
+                  : x >= 4 ? pl[1][r]
+                  : x >= 2 ? pl[2][r] : pl[3][r];
+        }
         frag16_from_acc(pf, pt);
         den += wave_sum_groups(frag16_sum(pf));
       }
@@ -643,13 +711,17 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(
   // ---- chunk loop: one barrier per chunk ----------------------------------
   // (step i handles chunk i; the aggregates take chunk nch - 1 - i)
   auto chunk_at = [&](int i) { return PHASE == 1 ? nch - 1 - i : i; };
+  constexpr int NB = S::NB;
   issue(chunk_at(0));
   scale(chunk_at(0), 0);
   for (int i = 0; i < nch; ++i) {
     __syncthreads();
     if (i + 1 < nch) issue(chunk_at(i + 1));
-    matrix(chunk_at(i), i & 1);
-    if (i + 1 < nch) scale(chunk_at(i + 1), (i + 1) & 1);
+    matrix(chunk_at(i), NB == 2 ? i & 1 : 0);
+    if (i + 1 < nch) {
+      if (NB == 1) __syncthreads();  // one buffer: its readers are done
+      scale(chunk_at(i + 1), NB == 2 ? (i + 1) & 1 : 0);
+    }
   }
 
   // ---- results ------------------------------------------------------------

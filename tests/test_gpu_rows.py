@@ -95,6 +95,8 @@ GRID = [
      GATE),
     ("performer_m256", 1, 2, 900, 64, "performer", 256, True, GATE),
     ("performer_d32_m64", 1, 2, 400, 32, "performer", 64, True, GATE),
+    ("performer_m256_strong_decay", 2, 1, 1000, 64, "performer", 256, True,
+     None),
 ]
 
 
@@ -269,3 +271,72 @@ def test_rows_full_size_every_unit():
     print(f"per-channel full size: max per-unit rel err {worst:.3e}",
           flush=True)
     assert worst <= 1e-2
+
+
+def test_rows_random_shapes():
+    """24 random configurations (layout, map, d, d', ragged n, B, H,
+    causality, storage type, mild or strong decays; seed fixed) in one
+    sequence through the binding's cached workspace; sampled units against
+    the oracle."""
+    import random
+    rng = random.Random(2027)
+    fails = []
+    for it in range(24):
+        layout = rng.choice(["channel", "both"])
+        mapk = rng.choice([I.MAP_ELU1, I.MAP_ELU1, I.MAP_PERFORMER,
+                           I.MAP_IDENTITY])
+        d = (rng.choice([16, 32, 64, 128]) if mapk != I.MAP_PERFORMER
+             else rng.choice([32, 64]))
+        m = (rng.choice([32, 64, 128, 256]) if mapk == I.MAP_PERFORMER else
+             rng.choice([16, 32, 64, 128, 256]) if mapk == I.MAP_IDENTITY
+             else 0)
+        dtype = rng.choice([torch.bfloat16, torch.bfloat16, torch.float32])
+        B, H = rng.choice([1, 2, 3]), rng.choice([1, 2, 5])
+        n = rng.choice([1, 15, 16, 17, 100, 513, 1000, 2049])
+        causal = rng.random() < 0.75
+        gate = GATE if rng.random() < 0.7 else STRONG[layout]
+        cfg = I.PrefillConfig(f"rows_rand{it}", B=B, H=H, n=n, d=d,
+                              dtype=dtype, mapk=mapk, m=m, causal=causal,
+                              qk_std=0.5 if mapk == I.MAP_PERFORMER else 1.0)
+        x = row_inputs(cfg, it, layout, gate)
+        out = K.forward_gated(dev(x["q"]), dev(x["k"]), dev(x["v"]),
+                              dev(x["lam"]), layout, I.MAP_NAMES[mapk],
+                              omega=dev(x["omega"]), causal=causal)
+        torch.cuda.synchronize()
+        err = 0.0
+        for b, h in [(0, 0), (B - 1, H - 1)]:
+            u = (slice(b, b + 1), slice(h, h + 1))
+            lam = x["lam"][h:h + 1] if layout == "channel" else x["lam"][u]
+            ref = oracle.forward_gated(f64(x["q"][u]), f64(x["k"][u]),
+                                       f64(x["v"][u]), mapk, f64(x["omega"]),
+                                       f64(lam), MODE[layout], causal)
+            err = max(err, rel(out[u], ref))
+        if err > TOL[dtype]:
+            fails.append((cfg, layout, gate, err))
+    assert not fails, fails
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_rows_small_features_strong_decay(dtype):
+    """Performer features (about 2^-16 here) with strong decays (log decay
+    down to about -95 per step): the same per-position decays given to every
+    row of the per-row forward match the oracle and the per-position kernel.
+    (An intra-chunk score split about one anchor row underflowed here.)"""
+    cfg = I.PrefillConfig("rows_small_strong", B=2, H=1, n=1000, d=64,
+                          dtype=dtype, mapk=I.MAP_PERFORMER, m=256,
+                          causal=True, qk_std=0.5)
+    x = I.make_prefill(cfg, 7)
+    lam = I.row_log_decay(cfg, 7, "both", *STRONG["both"], d_feat=256)
+    lp = lam[..., 0].contiguous()
+    args = [dev(x["q"]), dev(x["k"]), dev(x["v"])]
+    a = K.forward_gated(*args, dev(lp), "position", "performer",
+                        omega=dev(x["omega"]))
+    b = K.forward_gated(*args, dev(lp[..., None].expand(*lam.shape)
+                                   .contiguous()), "both", "performer",
+                        omega=dev(x["omega"]))
+    torch.cuda.synchronize()
+    ref = oracle.forward_gated(f64(x["q"]), f64(x["k"]), f64(x["v"]),
+                               I.MAP_PERFORMER, f64(x["omega"]), f64(lp),
+                               oracle.LD_POSITION, True)
+    assert rel(a, ref) <= TOL[dtype]
+    assert rel(b, ref) <= TOL[dtype]
