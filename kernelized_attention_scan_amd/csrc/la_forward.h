@@ -252,9 +252,10 @@ struct FwdShape {
   // every CU streaming, shallow rings measured fastest: more loads in flight
   // only made each chunk's data arrive later.  Phase 1 (K, V) keeps the
   // next chunk in flight; phase 2 (q, k, v) the next two where a chunk's
-  // loads take at most 12 VGPRs (d <= 64 bf16), else the next one.
+  // loads take at most 24 VGPRs (bf16 d <= 128: 1 % faster at d = 128 than
+  // one chunk), else the next one.
   static constexpr int REG2 = 4 * (Slab<T, QW, C>::PER * 2 + Slab<T, D, C>::PER);
-  static constexpr int NB2 = REG2 <= 12 ? 2 : 1;
+  static constexpr int NB2 = REG2 <= 24 ? 2 : 1;
   static constexpr int NB1 = 1;
   static constexpr int KRES = PIPE ? KRES_ : 0;
   // the fused Performer map needs bf16 operands, d a multiple of 32 (the
