@@ -516,6 +516,12 @@ def main() -> int:
                     help="only copy a MIB-MiB buffer three times (a kernel of "
                          "known HBM traffic, to scale the profiler's byte "
                          "counters) and exit")
+    ap.add_argument("--stream-rate", type=int, default=0, metavar="MIB",
+                    help="only time plain streaming kernels over MIB-MiB "
+                         "buffers (torch's elementwise add, which reads and "
+                         "writes each byte once, and a device copy), print "
+                         "their rates and exit: what a plain kernel reaches "
+                         "on this GPU, beside the 8 TB/s peak")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not "
@@ -543,6 +549,29 @@ def main() -> int:
         print(json.dumps({"copy_calibration_bytes_read": nbytes,
                           "copy_calibration_bytes_written": nbytes,
                           "launches": 3}), flush=True)
+        return 0
+    if args.stream_rate:
+        n = (args.stream_rate << 20) // 2
+        x = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        y = torch.empty_like(x)
+        rates = {}
+        for name, fn in (("add", lambda: torch.add(x, 1.0, out=y)),
+                         ("copy", lambda: y.copy_(x))):
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            sec = e0.elapsed_time(e1) * 1e-3 / args.steps
+            rates[f"{name}_TBps"] = round(2 * 2 * n / sec / 1e12, 3)
+        print(json.dumps({"stream_rate_bytes_read": 2 * n,
+                          "stream_rate_bytes_written": 2 * n,
+                          "launches": args.steps, **rates}), flush=True)
         return 0
     K.load_library()
     cfg = workloads()[args.workload]
