@@ -853,6 +853,339 @@ __device__ __forceinline__ void seg_role(const BwdArgs &a, int64_t units,
   }
 }
 
+// The dk and dv readouts fused (PHASE 2).  Both roles run backwards through
+// the sequence over the same weights and share every operand: dk takes
+// queries V+, keys G~, values Q'; dv queries K', keys Q', values G.  Their
+// states are transposes of each other: S_dv = (the first d rows of
+// S_dk)^T, both sums of w G~^T Q' over the rows already passed.  So one
+// workgroup stages V+, G~, Q', K' once per chunk, keeps S_dk (the dk role's
+// state and aggregates, whose PHASE 1 is unchanged) and reads both outputs
+// out of one S_dk^T copy: dk's inter-chunk term takes its rows, dv's its
+// columns through transposing reads.  Wave w = 4 jh + tb reads out strip tb
+// of both outputs for column blocks 4 jh .. 4 jh + 3.
+constexpr size_t kDkvLds =
+    sizeof(bf16) * (2 * SShape<bf16, kRoleDK>::SX + 2 * SShape<bf16, kRoleDK>::SZ +
+                    SShape<bf16, kRoleDK>::SST) +
+    sizeof(float) * (kBC + 4);
+
+template <bool DECAY, bool ELU>
+__device__ __forceinline__ void seg_dkv(const BwdArgs &a, int64_t units,
+                                        int64_t unit, int seg,
+                                        unsigned char *smem) {
+  using T = bf16;
+  using F = SShape<T, kRoleDK>;
+  const int nseg = a.nseg;
+  constexpr int D = F::D, C = kBC, KX = F::KX, LX = F::LX, LZ = F::LZ;
+  constexpr int NT = F::NT, KG = backward_gwidth(D);
+  T *sV = reinterpret_cast<T *>(smem);  // V+ rows: dk's queries
+  T *sG = sV + F::SX;                   // G~ rows: dk's keys, dv's values
+  T *sQ = sG + F::SX;                   // Q': dk's values, dv's keys
+  T *sK = sQ + F::SZ;                   // K': dv's queries
+  T *sST = sK + F::SZ;                  // S_dk^T: row f of Q', column c of G~
+  float *gp = reinterpret_cast<float *>(sST + F::SST);  // g^0 .. g^C
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, li = lane & 15;
+  const int tb = w % 4, jh = w / 4;
+  const int h = static_cast<int>(unit % a.H);
+  const float gdec = DECAY ? a.decay[h] : 1.f, bdec = DECAY ? 1.f - gdec : 1.f;
+  const float lg = log2f(gdec);
+  for (int i = tid; i <= C; i += kSThreads) gp[i] = pow_int(gdec, lg, i);
+
+  const int64_t n = a.n;
+  const T *qb = static_cast<const T *>(a.q) + unit * n * D;
+  const T *kb = static_cast<const T *>(a.k) + unit * n * D;
+  const T *vb = static_cast<const T *>(a.v) + unit * n * D;
+  const T *gtb = static_cast<const T *>(a.gt) + unit * n * KG;
+  T *dkb = static_cast<T *>(a.dk) + unit * n * D;
+  T *dvb = static_cast<T *>(a.dv) + unit * n * D;
+
+  // the zero padding columns of V+ (G~ rows are copied whole, V+'s ones
+  // columns are written per chunk)
+  for (int i = tid; i < C * (KX - D - 2); i += kSThreads) {
+    const int row = i / (KX - D - 2), col = D + 2 + i % (KX - D - 2);
+    sV[row * LX + col] = from_f32<T>(0.f);
+  }
+
+  // processing steps: step c is physical chunk nch - 1 - c, its rows reversed
+  const int nch = static_cast<int>((n + C - 1) / C);
+  const int cps = (nch + nseg - 1) / nseg;
+  const int cb = seg * cps, ce = min(nch, cb + cps);
+  auto rows_of = [&](int c) -> int {
+    if (c >= ce) return 0;
+    const int64_t r0 = static_cast<int64_t>(nch - 1 - c) * C;
+    return static_cast<int>(min<int64_t>(C, n - r0));
+  };
+  auto row0_of = [&](int c) -> int64_t {
+    return c >= ce ? 0 : static_cast<int64_t>(nch - 1 - c) * C;
+  };
+
+  // register ring, one chunk ahead: G~, v, and the raw q and k rows
+  using SG = BSlab<T, KG, KG, kSThreads>;
+  using SD = BSlab<T, D, D, kSThreads>;
+  SG rg;
+  SD rv, rq, rk;
+  auto load = [&](int c) {
+    const int64_t r0 = row0_of(c);
+    const int rows = rows_of(c);
+    rg.load(gtb, r0, rows, 0, tid);
+    rv.load(vb, r0, rows, 0, tid);
+    rq.load(qb, r0, rows, 0, tid);
+    rk.load(kb, r0, rows, 0, tid);
+  };
+  auto put_phi = [&](const SD &sl, T *dst, auto trow, int rows) {
+#pragma unroll
+    for (int i = 0; i < SD::PER; ++i) {
+      const int p = tid + SD::THREADS * i;
+      if (SD::EXACT || p < SD::PIECES) {
+        const int r = p / SD::PPR;
+        u32x4 y = sl.v[i];
+        if constexpr (ELU) {
+          float f[SD::VEC];
+          piece_to_f32<T>(sl.v[i], f);
+#pragma unroll
+          for (int e = 0; e < SD::VEC; ++e)
+            f[e] = r < rows ? elu_plus_one_fast(f[e]) : 0.f;
+          y = f32_to_piece<T>(f);
+        }
+        *reinterpret_cast<u32x4 *>(dst + trow(r) * LZ + (p % SD::PPR) * SD::VEC) =
+            y;
+      }
+    }
+  };
+  auto put = [&](const auto &sl, T *dst, auto trow) {
+    using S = std::remove_cv_t<std::remove_reference_t<decltype(sl)>>;
+#pragma unroll
+    for (int i = 0; i < S::PER; ++i) {
+      const int p = tid + S::THREADS * i;
+      if (S::EXACT || p < S::PIECES)
+        *reinterpret_cast<u32x4 *>(dst + trow(p / S::PPR) * LX +
+                                   (p % S::PPR) * S::VEC) = sl.v[i];
+    }
+  };
+  auto stage = [&](int c) {
+    const int rows = rows_of(c);
+    auto trow = [&](int r) { return r < rows ? rows - 1 - r : r; };
+    put(rg, sG, trow);
+    put(rv, sV, trow);
+    if (tid < C) {
+      const int t = trow(tid);
+      const T one = from_f32<T>(tid < rows ? 1.f : 0.f);
+      sV[t * LX + D] = one;
+      sV[t * LX + D + 1] = one;
+    }
+    put_phi(rq, sQ, trow, rows);
+    put_phi(rk, sK, trow, rows);
+  };
+
+  // this wave's part of S_dk: column block w of Q', all NT tiles of G~;
+  // the entering state sums the dk role's aggregates before this segment
+  f32x4 S[NT];
+#pragma unroll
+  for (int fb = 0; fb < NT; ++fb) S[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int sg = 0; sg < seg; ++sg) {
+    const float wgt =
+        DECAY ? pow_int(gdec, lg, static_cast<int64_t>(seg - sg - 1) * cps * C)
+              : 1.f;
+    const float *src = a.agg +
+                       ((static_cast<int64_t>(kRoleDK) * units + unit) * nseg +
+                        sg) * kSegSlot +
+                       (w * kSegTiles) * 256 + lane * 4;
+#pragma unroll
+    for (int fb = 0; fb < NT; ++fb)
+      S[fb] += wgt * *reinterpret_cast<const f32x4 *>(src + fb * 256);
+  }
+  auto publish = [&]() {  // S_dk^T rows 16 w .. + 15
+#pragma unroll
+    for (int fb = 0; fb < NT; ++fb)
+      store4(sST + (16 * w + li) * LX + 16 * fb + 4 * g, S[fb][0], S[fb][1],
+             S[fb][2], S[fb][3]);
+  };
+  auto state_update = [&](int c) {  // S_dk <- g^r S_dk + sum w G~^T Q'
+    const int rows = rows_of(c);
+    const float gr = gp[rows];
+    f32x4 wlo[C / 32], whi[C / 32];
+    if constexpr (DECAY) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < C / 32; ++kb2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int s0 = 32 * kb2 + 8 * g + e, s1 = s0 + 4;
+          wlo[kb2][e] = s0 < rows ? bdec * gp[rows - 1 - s0] : 0.f;
+          whi[kb2][e] = s1 < rows ? bdec * gp[rows - 1 - s1] : 0.f;
+        }
+    }
+    Frag<T> bf[C / 32];
+#pragma unroll
+    for (int kb2 = 0; kb2 < C / 32; ++kb2) {
+      load_frag_tr8(bf[kb2], sQ, LZ, 32 * kb2, 16 * w, g, li);
+      if constexpr (DECAY) frag_scale(bf[kb2], wlo[kb2], whi[kb2]);
+    }
+#pragma unroll
+    for (int fb = 0; fb < NT; ++fb) {
+      f32x4 acc = S[fb] * gr;
+#pragma unroll
+      for (int kb2 = 0; kb2 < C / 32; ++kb2) {
+        Frag<T> af;
+        load_frag_tr8(af, sG, LX, 32 * kb2, 16 * fb, g, li);
+        acc = mma(af, bf[kb2], acc);
+      }
+      S[fb] = acc;
+    }
+  };
+
+  const int t = 16 * tb + li;  // the query row this lane reads out
+  // phi'(k) inputs of dk: raw k of this lane's output elements (row t,
+  // columns 16 (4 jh + jj) + 4 g ..), loaded a chunk ahead
+  u32x2 pfn[4] = {}, pfc[4] = {};
+  auto load_phi = [&](int c) {
+    if constexpr (ELU) {
+      const int rows = rows_of(c);
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(
+          kb + row0_of(c) * D, static_cast<unsigned>(rows) * D * sizeof(T));
+      const int rr = t < rows ? rows - 1 - t : t;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        pfn[jj] = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                       r,
+                       static_cast<unsigned>(rr * D + 16 * (4 * jh + jj) +
+                                             4 * g) *
+                           sizeof(T),
+                       0, 0));
+    }
+  };
+  // masked, decay-weighted scores P^T (keys s = 16 sb + 4 g + r of the
+  // chunk, this lane's query t) from the key rows of sY against xf
+  auto scores = [&](Frag<T>(&pf)[2], const T *sY, int ly, const Frag<T> *xf,
+                    auto nk) {
+    constexpr int NK = decltype(nk)::value;
+    f32x4 pt[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (sb <= tb) {
+#pragma unroll
+        for (int kq = 0; kq < NK; ++kq) {
+          Frag<T> fa;
+          load_frag8(fa, sY + (16 * sb + li) * ly + 32 * kq + 8 * g);
+          acc = mma(fa, xf[kq], acc);
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int s_ = 16 * sb + 4 * g + rr;
+        acc[rr] = s_ <= t ? acc[rr] * (DECAY ? bdec * gp[s_ <= t ? t - s_ : 0]
+                                             : 1.f)
+                          : 0.f;
+      }
+      pt[sb] = acc;
+    }
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp)
+      frag_from_acc(pf[kp], pt[2 * kp], pt[2 * kp + 1]);
+  };
+
+  load(cb);
+  load_phi(cb);
+  __syncthreads();  // gp and the padding columns ready
+  stage(cb);
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) pfc[jj] = pfn[jj];
+  load(cb + 1);
+  load_phi(cb + 1);
+  publish();
+  __syncthreads();
+
+  for (int c = cb; c < ce; ++c) {
+    const int rows = rows_of(c);
+    const float gt = gp[t + 1];
+    const int64_t row = row0_of(c) + (t < rows ? rows - 1 - t : t);
+    // ---- dk: queries V+ (KX wide), keys G~, values Q'
+    {
+      Frag<T> xf[KX / 32];
+#pragma unroll
+      for (int kq = 0; kq < KX / 32; ++kq)
+        load_frag8(xf[kq], sV + t * LX + 32 * kq + 8 * g);
+      Frag<T> pf[2];
+      scores(pf, sG, LX, xf, std::integral_constant<int, KX / 32>{});
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int jb = 4 * jh + jj;
+        f32x4 an = {0.f, 0.f, 0.f, 0.f}, ai = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp) {
+          if (2 * kp <= tb) {
+            Frag<T> zf;
+            load_frag_tr44(zf, sQ, LZ, 32 * kp, 16 * jb, g, li);
+            an = mma(zf, pf[kp], an);
+          }
+        }
+#pragma unroll
+        for (int kq = 0; kq < KX / 32; ++kq) {
+          Frag<T> fa;
+          load_frag8(fa, sST + (16 * jb + li) * LX + 32 * kq + 8 * g);
+          ai = mma(fa, xf[kq], ai);
+        }
+        const f32x4 o = an + gt * ai;
+        if (t < rows) {
+          float x[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float xin = ELU ? (r % 2 == 0 ? bf16_lo(pfc[jj][r / 2])
+                                                : bf16_hi(pfc[jj][r / 2]))
+                                  : 0.f;
+            x[r] = ELU ? o[r] * dphi(xin, true) : o[r];
+          }
+          store4(dkb + row * D + 16 * jb + 4 * g, x[0], x[1], x[2], x[3]);
+        }
+      }
+    }
+    // ---- dv: queries K', keys Q', values G (the first d columns of G~);
+    // the state term reads S_dv = S_dk^T through transposing reads of sST
+    {
+      Frag<T> xf[D / 32];
+#pragma unroll
+      for (int kq = 0; kq < D / 32; ++kq)
+        load_frag8(xf[kq], sK + t * LZ + 32 * kq + 8 * g);
+      Frag<T> pf[2];
+      scores(pf, sQ, LZ, xf, std::integral_constant<int, D / 32>{});
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int jb = 4 * jh + jj;
+        f32x4 an = {0.f, 0.f, 0.f, 0.f}, ai = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp) {
+          if (2 * kp <= tb) {
+            Frag<T> zf;
+            load_frag_tr44(zf, sG, LX, 32 * kp, 16 * jb, g, li);
+            an = mma(zf, pf[kp], an);
+          }
+        }
+#pragma unroll
+        for (int kq = 0; kq < D / 32; ++kq) {
+          Frag<T> fa;
+          load_frag_tr8(fa, sST, LX, 32 * kq, 16 * jb, g, li);
+          ai = mma(fa, xf[kq], ai);
+        }
+        const f32x4 o = an + gt * ai;
+        if (t < rows)
+          store4(dvb + row * D + 16 * jb + 4 * g, o[0], o[1], o[2], o[3]);
+      }
+    }
+    state_update(c);
+    __syncthreads();  // the tile set is free again
+    stage(c + 1);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) pfc[jj] = pfn[jj];
+    load(c + 2);
+    load_phi(c + 2);
+    publish();
+    __syncthreads();
+  }
+}
+
 template <bool DECAY, bool ELU, int PHASE>
 __global__ __launch_bounds__(kSThreads) void la_bwd_seg_kernel(BwdArgs a,
                                                                int64_t units) {
@@ -865,12 +1198,13 @@ __global__ __launch_bounds__(kSThreads) void la_bwd_seg_kernel(BwdArgs a,
   const int seg = static_cast<int>(rem % nseg);
   // the last segment's aggregate is never read
   if (PHASE == 1 && seg == nseg - 1) return;
+  // role 0: dq; role 1: the dk aggregates (PHASE 1), dk and dv (PHASE 2)
   if (role == kRoleDQ)
     seg_role<bf16, kRoleDQ, DECAY, ELU, PHASE>(a, units, unit, seg, smem);
-  else if (role == kRoleDK)
+  else if (PHASE == 1)
     seg_role<bf16, kRoleDK, DECAY, ELU, PHASE>(a, units, unit, seg, smem);
   else
-    seg_role<bf16, kRoleDV, DECAY, ELU, PHASE>(a, units, unit, seg, smem);
+    seg_dkv<DECAY, ELU>(a, units, unit, seg, smem);
 }
 
 template <bool DECAY, bool ELU>
@@ -878,7 +1212,8 @@ hipError_t launch_seg(const BwdArgs &a, int64_t units, hipStream_t s) {
   const int nseg = a.nseg;
   constexpr size_t lds = std::max({SShape<bf16, kRoleDQ>::lds_bytes,
                                    SShape<bf16, kRoleDK>::lds_bytes,
-                                   SShape<bf16, kRoleDV>::lds_bytes});
+                                   kDkvLds});
+  static_assert(lds <= 160 * 1024, "LDS of one workgroup");
   static const hipError_t once = [] {
     for (const void *k :
          {reinterpret_cast<const void *>(&la_bwd_seg_kernel<DECAY, ELU, 1>),
@@ -890,7 +1225,7 @@ hipError_t launch_seg(const BwdArgs &a, int64_t units, hipStream_t s) {
     return hipSuccess;
   }();
   if (once != hipSuccess) return once;
-  const dim3 grid(static_cast<unsigned>(3 * units * nseg)), block(kSThreads);
+  const dim3 grid(static_cast<unsigned>(2 * units * nseg)), block(kSThreads);
   if (nseg > 1) {
     hipLaunchKernelGGL((la_bwd_seg_kernel<DECAY, ELU, 1>), grid, block, lds, s,
                        a, units);
@@ -996,8 +1331,8 @@ bool backward_supported(int d, int d_feat) {
 
 int backward_segments(int64_t units, int64_t n, int d, int dtype) {
   if (dtype != 1 || d != kSegD || units <= 0 || n <= 0) return 0;
-  // three roles x units x segments workgroups of one per CU: about three
-  // rounds of the CUs, at most 16 segments, whole chunks each
+  // two roles (dq; dk with dv) x units x segments workgroups of one per
+  // CU: about two rounds of the CUs, at most 16 segments, whole chunks each
   const int64_t nch = (n + kBC - 1) / kBC;
   int64_t k = (kCUs + units - 1) / units;
   if (k > 16) k = 16;
@@ -1009,7 +1344,9 @@ int backward_segments(int64_t units, int64_t n, int d, int dtype) {
 }
 
 size_t backward_agg_floats(int64_t units, int nseg) {
-  return nseg > 1 ? static_cast<size_t>(3 * units * nseg) * kSegSlot : 0;
+  // aggregates of the dq and dk roles (the fused dk and dv readout takes
+  // dk's)
+  return nseg > 1 ? static_cast<size_t>(2 * units * nseg) * kSegSlot : 0;
 }
 
 hipError_t launch_backward(const BwdArgs &a, int64_t units, int d, int dtype,

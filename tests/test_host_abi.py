@@ -303,10 +303,10 @@ def test_backward_workspace_bytes(lib):
     rows = 2 * 3 * 100
     # bf16 at d = 128 runs the segmented roles, which map k, q themselves
     # (no K', Q' rows) and keep segment aggregates: 6 units, 100 rows = 2
-    # chunks -> 2 segments, 3 roles x 8 waves x 10 feature tiles x 256
-    # floats each
+    # chunks -> 2 segments, 2 roles (dq; dk, whose state dv shares) x 8
+    # waves x 10 feature tiles x 256 floats each
     assert K.backward_workspace_bytes(2, 3, 100, 128) == (
-        a256(rows * 160 * 2) + a256(3 * 6 * 2 * 8 * 10 * 256 * 4))
+        a256(rows * 160 * 2) + a256(2 * 6 * 2 * 8 * 10 * 256 * 4))
     # one chunk: one segment, no aggregates
     assert K.backward_workspace_bytes(2, 3, 64, 128) == a256(384 * 160 * 2)
     assert K.backward_workspace_bytes(2, 3, 100, 128, dtype=torch.float32) == (
