@@ -858,13 +858,14 @@ __device__ __forceinline__ void seg_role(const BwdArgs &a, int64_t units,
 // queries V+, keys G~, values Q'; dv queries K', keys Q', values G.  Their
 // states are transposes of each other: S_dv = (the first d rows of
 // S_dk)^T, both sums of w G~^T Q' over the rows already passed.  So one
-// workgroup stages V+, G~, Q', K' once per chunk, keeps S_dk (the dk role's
-// state and aggregates, whose PHASE 1 is unchanged) and reads both outputs
-// out of one S_dk^T copy: dk's inter-chunk term takes its rows, dv's its
-// columns through transposing reads.  Wave w = 4 jh + tb reads out strip tb
-// of both outputs for column blocks 4 jh .. 4 jh + 3.
+// workgroup stages V+, G~, Q', K' and the raw k rows (whose phi'(k) scales
+// dk) once per chunk, keeps S_dk (the dk role's state and aggregates, whose
+// PHASE 1 is unchanged) and reads both outputs out of one S_dk^T copy: dk's
+// inter-chunk term takes its rows, dv's its columns through transposing
+// reads.  Wave w = 4 jh + tb reads out strip tb of both outputs for column
+// blocks 4 jh .. 4 jh + 3.
 constexpr size_t kDkvLds =
-    sizeof(bf16) * (2 * SShape<bf16, kRoleDK>::SX + 2 * SShape<bf16, kRoleDK>::SZ +
+    sizeof(bf16) * (2 * SShape<bf16, kRoleDK>::SX + 3 * SShape<bf16, kRoleDK>::SZ +
                     SShape<bf16, kRoleDK>::SST) +
     sizeof(float) * (kBC + 4);
 
@@ -881,7 +882,8 @@ __device__ __forceinline__ void seg_dkv(const BwdArgs &a, int64_t units,
   T *sG = sV + F::SX;                   // G~ rows: dk's keys, dv's values
   T *sQ = sG + F::SX;                   // Q': dk's values, dv's keys
   T *sK = sQ + F::SZ;                   // K': dv's queries
-  T *sST = sK + F::SZ;                  // S_dk^T: row f of Q', column c of G~
+  T *sKr = sK + F::SZ;                  // raw k: phi'(k) of dk's outputs
+  T *sST = sKr + F::SZ;                 // S_dk^T: row f of Q', column c of G~
   float *gp = reinterpret_cast<float *>(sST + F::SST);  // g^0 .. g^C
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -954,6 +956,15 @@ __device__ __forceinline__ void seg_dkv(const BwdArgs &a, int64_t units,
       }
     }
   };
+  auto put_raw = [&](const SD &sl, T *dst, auto trow) {
+#pragma unroll
+    for (int i = 0; i < SD::PER; ++i) {
+      const int p = tid + SD::THREADS * i;
+      if (SD::EXACT || p < SD::PIECES)
+        *reinterpret_cast<u32x4 *>(dst + trow(p / SD::PPR) * LZ +
+                                   (p % SD::PPR) * SD::VEC) = sl.v[i];
+    }
+  };
   auto put = [&](const auto &sl, T *dst, auto trow) {
     using S = std::remove_cv_t<std::remove_reference_t<decltype(sl)>>;
 #pragma unroll
@@ -977,6 +988,7 @@ __device__ __forceinline__ void seg_dkv(const BwdArgs &a, int64_t units,
     }
     put_phi(rq, sQ, trow, rows);
     put_phi(rk, sK, trow, rows);
+    if constexpr (ELU) put_raw(rk, sKr, trow);
   };
 
   // this wave's part of S_dk: column block w of Q', all NT tiles of G~;
@@ -1036,26 +1048,6 @@ __device__ __forceinline__ void seg_dkv(const BwdArgs &a, int64_t units,
   };
 
   const int t = 16 * tb + li;  // the query row this lane reads out
-  // phi'(k) inputs of dk: raw k of this lane's output elements (row t,
-  // columns 16 (4 jh + jj) + 4 g ..), loaded a chunk ahead
-  u32x2 pfn[4] = {}, pfc[4] = {};
-  auto load_phi = [&](int c) {
-    if constexpr (ELU) {
-      const int rows = rows_of(c);
-      const __amdgpu_buffer_rsrc_t r = make_rsrc(
-          kb + row0_of(c) * D, static_cast<unsigned>(rows) * D * sizeof(T));
-      const int rr = t < rows ? rows - 1 - t : t;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        pfn[jj] = __builtin_bit_cast(
-            u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                       r,
-                       static_cast<unsigned>(rr * D + 16 * (4 * jh + jj) +
-                                             4 * g) *
-                           sizeof(T),
-                       0, 0));
-    }
-  };
   // masked, decay-weighted scores P^T (keys s = 16 sb + 4 g + r of the
   // chunk, this lane's query t) from the key rows of sY against xf
   auto scores = [&](Frag<T>(&pf)[2], const T *sY, int ly, const Frag<T> *xf,
@@ -1088,13 +1080,9 @@ __device__ __forceinline__ void seg_dkv(const BwdArgs &a, int64_t units,
   };
 
   load(cb);
-  load_phi(cb);
   __syncthreads();  // gp and the padding columns ready
   stage(cb);
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj) pfc[jj] = pfn[jj];
   load(cb + 1);
-  load_phi(cb + 1);
   publish();
   __syncthreads();
 
@@ -1130,12 +1118,16 @@ __device__ __forceinline__ void seg_dkv(const BwdArgs &a, int64_t units,
         }
         const f32x4 o = an + gt * ai;
         if (t < rows) {
+          // phi'(k) from the raw k row staged with the chunk
+          const u32x2 kr =
+              ELU ? *reinterpret_cast<const u32x2 *>(sKr + t * LZ + 16 * jb + 4 * g)
+                  : u32x2{0u, 0u};
           float x[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float xin = ELU ? (r % 2 == 0 ? bf16_lo(pfc[jj][r / 2])
-                                                : bf16_hi(pfc[jj][r / 2]))
-                                  : 0.f;
+            const float xin =
+                ELU ? (r % 2 == 0 ? bf16_lo(kr[r / 2]) : bf16_hi(kr[r / 2]))
+                    : 0.f;
             x[r] = ELU ? o[r] * dphi(xin, true) : o[r];
           }
           store4(dkb + row * D + 16 * jb + 4 * g, x[0], x[1], x[2], x[3]);
@@ -1177,10 +1169,7 @@ __device__ __forceinline__ void seg_dkv(const BwdArgs &a, int64_t units,
     state_update(c);
     __syncthreads();  // the tile set is free again
     stage(c + 1);
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) pfc[jj] = pfn[jj];
     load(c + 2);
-    load_phi(c + 2);
     publish();
     __syncthreads();
   }
