@@ -506,7 +506,9 @@ __global__ __launch_bounds__(kBThreads) void la_bwd_prep_kernel(
 // before it, each weighted by the decay over the rows between, and runs the
 // chunk loop from that state.  No workgroup waits for another.
 // Wave w = 4 jh + tb reads out strip tb for column blocks 4 jh .. 4 jh + 3
-// and owns the state of column block w (all its feature tiles).
+// and owns the state of column block w (all its feature tiles).  seg_role
+// runs dq (both launches) and the dk aggregates; seg_dkv below reads out dk
+// and dv together, so the dv role has no workgroup of its own.
 // ---------------------------------------------------------------------------
 constexpr int kSThreads = 512;
 constexpr int kSWaves = kSThreads / kWave;
@@ -516,15 +518,18 @@ constexpr int kSegSlot = kSWaves * kSegTiles * 256;          // floats
 
 template <typename T, int ROLE>
 struct SShape {
+  static_assert(ROLE == kRoleDQ || ROLE == kRoleDK, "dq, dk layouts");
   static constexpr int D = kSegD;
-  static constexpr bool GV = ROLE != kRoleDV;
-  static constexpr int KX = GV ? backward_gwidth(D) : D;
+  // queries and keys G~ and V+: d + 2 values padded to a multiple of 32
+  static constexpr int KX = backward_gwidth(D);
   static constexpr int LX = bstride<T>(KX);
   static constexpr int LZ = bstride<T>(D);
   static constexpr int NT = KX / 16;
   static constexpr int SX = kBC * LX, SZ = kBC * LZ, SST = D * LX;
+  // dq also stages the raw q rows (phi'(q) of its outputs)
+  static constexpr int SP = ROLE == kRoleDQ ? SZ : 0;
   static constexpr size_t lds_bytes =
-      sizeof(T) * (2 * SX + SZ + SST) + sizeof(float) * (kBC + 4);
+      sizeof(T) * (2 * SX + SZ + SST + SP) + sizeof(float) * (kBC + 4);
   static_assert(D / 16 == kSWaves, "one state column block per wave");
 };
 
@@ -537,12 +542,15 @@ __device__ __forceinline__ void seg_role(const BwdArgs &a, int64_t units,
   using F = SShape<T, ROLE>;
   constexpr int D = F::D, C = kBC, KX = F::KX, LX = F::LX, LZ = F::LZ;
   constexpr int NT = F::NT, KG = backward_gwidth(D);
-  constexpr bool GV = F::GV, REV = ROLE != kRoleDQ;
+  static_assert(ROLE == kRoleDQ || (ROLE == kRoleDK && PHASE == 1),
+                "seg_dkv reads out dk");
+  constexpr bool REV = ROLE != kRoleDQ;
   T *sX = reinterpret_cast<T *>(smem);           // queries X
   T *sY = sX + F::SX;                            // keys Y
   T *sZ = sY + F::SX;                            // values Z (all d columns)
   T *sST = sZ + F::SZ;                           // S^T copy
-  float *gp = reinterpret_cast<float *>(sST + F::SST);  // g^0 .. g^C
+  T *sP = sST + F::SST;                          // raw q rows (dq)
+  float *gp = reinterpret_cast<float *>(sP + F::SP);  // g^0 .. g^C
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -558,14 +566,11 @@ __device__ __forceinline__ void seg_role(const BwdArgs &a, int64_t units,
   const T *kb = static_cast<const T *>(a.k) + unit * n * D;
   const T *vb = static_cast<const T *>(a.v) + unit * n * D;
   const T *gtb = static_cast<const T *>(a.gt) + unit * n * KG;
-  T *res = static_cast<T *>(ROLE == kRoleDQ ? a.dq
-                            : ROLE == kRoleDK ? a.dk
-                                              : a.dv) +
-           unit * n * D;
+  T *res = static_cast<T *>(a.dq) + unit * n * D;
 
   // the zero padding columns of X and Y (G~ rows are copied whole, the
   // ones columns of V+ are written per chunk)
-  constexpr int XW = GV ? D + 2 : D;
+  constexpr int XW = D + 2;
   for (int i = tid; i < C * (KX - XW); i += kSThreads) {
     const int row = i / (KX - XW), col = XW + i % (KX - XW);
     sX[row * LX + col] = from_f32<T>(0.f);
@@ -592,26 +597,20 @@ __device__ __forceinline__ void seg_role(const BwdArgs &a, int64_t units,
   // stages a row once).
   using SG = BSlab<T, KG, KG, kSThreads>;   // G~ rows
   using SD = BSlab<T, D, D, kSThreads>;     // v, k or q rows
-  using SZG = BSlab<T, D, KG, kSThreads>;   // the first d columns of G~
   SG rg;
-  SD r1, r2;
-  SZG rzg;
-  // GV: rg = G~ (X of dq, Y of dk), r1 = v (V+), r2 = K' (dq) or Q' (dk)
-  // dv: r1 = K' (X), r2 = Q' (Y), rzg = G (Z)
-  constexpr bool NEED_G = GV ? (PHASE == 2 || ROLE == kRoleDK) : true;
-  constexpr bool NEED_R1 = GV ? (PHASE == 2 || ROLE == kRoleDQ) : PHASE == 2;
+  SD r1, r2, r3;
+  // rg = G~ (X of dq, Y of dk), r1 = v (V+), r2 = K' (dq) or Q' (dk), r3 =
+  // the raw q rows (dq's phi'(q), staged to sP)
+  constexpr bool NEED_G = PHASE == 2 || ROLE == kRoleDK;
+  constexpr bool NEED_R1 = PHASE == 2 || ROLE == kRoleDQ;
+  constexpr bool PFI = ROLE == kRoleDQ && ELU && PHASE == 2;
   auto load = [&](int c) {
     const int64_t r0 = row0_of(c);
     const int rows = rows_of(c);
-    if constexpr (GV) {
-      if constexpr (NEED_G) rg.load(gtb, r0, rows, 0, tid);
-      if constexpr (NEED_R1) r1.load(vb, r0, rows, 0, tid);
-      r2.load(ROLE == kRoleDQ ? kb : qb, r0, rows, 0, tid);
-    } else {
-      if constexpr (NEED_R1) r1.load(kb, r0, rows, 0, tid);
-      r2.load(qb, r0, rows, 0, tid);
-      rzg.load(gtb, r0, rows, 0, tid);
-    }
+    if constexpr (NEED_G) rg.load(gtb, r0, rows, 0, tid);
+    if constexpr (NEED_R1) r1.load(vb, r0, rows, 0, tid);
+    r2.load(ROLE == kRoleDQ ? kb : qb, r0, rows, 0, tid);
+    if constexpr (PFI) r3.load(qb, r0, rows, 0, tid);
   };
   // the same with phi applied (elu + 1 in fp32, rounded once; rows past the
   // end stay zero)
@@ -648,25 +647,20 @@ __device__ __forceinline__ void seg_role(const BwdArgs &a, int64_t units,
   auto stage = [&](int c) {
     const int rows = rows_of(c);
     auto trow = [&](int r) { return REV && r < rows ? rows - 1 - r : r; };
-    if constexpr (GV) {
-      T *sG = ROLE == kRoleDQ ? sX : sY;
-      T *sV = ROLE == kRoleDQ ? sY : sX;
-      if constexpr (NEED_G) put(rg, sG, LX, trow);
-      if constexpr (NEED_R1) {
-        put(r1, sV, LX, trow);
-        if (tid < C) {
-          const int t = trow(tid);
-          const T one = from_f32<T>(tid < rows ? 1.f : 0.f);
-          sV[t * LX + D] = one;
-          sV[t * LX + D + 1] = one;
-        }
+    T *sG = ROLE == kRoleDQ ? sX : sY;
+    T *sV = ROLE == kRoleDQ ? sY : sX;
+    if constexpr (NEED_G) put(rg, sG, LX, trow);
+    if constexpr (NEED_R1) {
+      put(r1, sV, LX, trow);
+      if (tid < C) {
+        const int t = trow(tid);
+        const T one = from_f32<T>(tid < rows ? 1.f : 0.f);
+        sV[t * LX + D] = one;
+        sV[t * LX + D + 1] = one;
       }
-      put_phi(r2, sZ, LZ, trow, rows);
-    } else {
-      if constexpr (NEED_R1) put_phi(r1, sX, LX, trow, rows);
-      put_phi(r2, sY, LX, trow, rows);
-      put(rzg, sZ, LZ, trow);
     }
+    put_phi(r2, sZ, LZ, trow, rows);
+    if constexpr (PFI) put(r3, sP, LZ, trow);
   };
 
   // this wave's state: column block w, feature tiles 0 .. NT - 1
@@ -735,37 +729,11 @@ __device__ __forceinline__ void seg_role(const BwdArgs &a, int64_t units,
   };
 
   const int t = 16 * tb + li;  // the query row this lane reads out
-  // dq, dk (elu + 1): raw q or k of this lane's output elements (row t,
-  // columns 16 (4 jh + jj) + 4 g ..), loaded a chunk ahead
-  constexpr bool PFI = GV && ELU && PHASE == 2;
-  u32x2 pfn[4] = {}, pfc[4] = {};
-  auto load_phi = [&](int c) {
-    if constexpr (PFI) {
-      const int rows = rows_of(c);
-      const __amdgpu_buffer_rsrc_t r =
-          make_rsrc((ROLE == kRoleDQ ? qb : kb) + row0_of(c) * D,
-                    static_cast<unsigned>(rows) * D * sizeof(T));
-      const int rr = REV && t < rows ? rows - 1 - t : t;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        pfn[jj] = __builtin_bit_cast(
-            u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                       r,
-                       static_cast<unsigned>(rr * D + 16 * (4 * jh + jj) +
-                                             4 * g) *
-                           sizeof(T),
-                       0, 0));
-    }
-  };
 
   load(cb);
-  load_phi(cb);
   __syncthreads();  // gp and the constant parts ready
   stage(cb);
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj) pfc[jj] = pfn[jj];
   load(cb + 1);
-  load_phi(cb + 1);
   if constexpr (PHASE == 2) publish();
   __syncthreads();
 
@@ -823,12 +791,16 @@ __device__ __forceinline__ void seg_role(const BwdArgs &a, int64_t units,
         }
         const f32x4 o = an + gt * ai;
         if (t < rows) {
+          // dq (elu + 1): phi'(q) from the raw q row staged with the chunk
+          const u32x2 qr =
+              PFI ? *reinterpret_cast<const u32x2 *>(sP + t * LZ + 16 * jb + 4 * g)
+                  : u32x2{0u, 0u};
           float x[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            float xin = 0.f;
-            if constexpr (PFI)
-              xin = r % 2 == 0 ? bf16_lo(pfc[jj][r / 2]) : bf16_hi(pfc[jj][r / 2]);
+            const float xin =
+                PFI ? (r % 2 == 0 ? bf16_lo(qr[r / 2]) : bf16_hi(qr[r / 2]))
+                    : 0.f;
             x[r] = PFI ? o[r] * dphi(xin, true) : o[r];
           }
           store4(res + row * D + 16 * jb + 4 * g, x[0], x[1], x[2], x[3]);
@@ -838,10 +810,7 @@ __device__ __forceinline__ void seg_role(const BwdArgs &a, int64_t units,
     state_update(c);
     __syncthreads();  // the tile set is free again
     stage(c + 1);
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) pfc[jj] = pfn[jj];
     load(c + 2);
-    load_phi(c + 2);
     if constexpr (PHASE == 2) publish();
     __syncthreads();
   }
@@ -1188,12 +1157,14 @@ __global__ __launch_bounds__(kSThreads) void la_bwd_seg_kernel(BwdArgs a,
   // the last segment's aggregate is never read
   if (PHASE == 1 && seg == nseg - 1) return;
   // role 0: dq; role 1: the dk aggregates (PHASE 1), dk and dv (PHASE 2)
-  if (role == kRoleDQ)
+  if (role == kRoleDQ) {
     seg_role<bf16, kRoleDQ, DECAY, ELU, PHASE>(a, units, unit, seg, smem);
-  else if (PHASE == 1)
-    seg_role<bf16, kRoleDK, DECAY, ELU, PHASE>(a, units, unit, seg, smem);
-  else
-    seg_dkv<DECAY, ELU>(a, units, unit, seg, smem);
+  } else {
+    if constexpr (PHASE == 1)
+      seg_role<bf16, kRoleDK, DECAY, ELU, 1>(a, units, unit, seg, smem);
+    else
+      seg_dkv<DECAY, ELU>(a, units, unit, seg, smem);
+  }
 }
 
 template <bool DECAY, bool ELU>
