@@ -618,6 +618,8 @@ def main() -> int:
                      "kernel_ms_per_launch": kern["ms"],
                      "algorithmic_bytes_per_launch": kern["bytes"],
                      "algorithmic_flops_per_launch": kern["flops"],
+                     "algorithmic_TFLOPs":
+                         kern["flops"] / (kern["ms"] * 1e-3) / 1e12,
                      "mfma_frac_algorithmic":
                          kern["flops"] / (kern["ms"] * 1e-3) / 1e12
                          / BF16_PEAK_TFLOPS},
