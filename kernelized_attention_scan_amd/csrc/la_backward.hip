@@ -33,7 +33,8 @@
 // Two kernels run the roles.  bf16 at d = 128 takes the segmented roles
 // (see la_bwd_seg_kernel below): a workgroup per (role, unit, segment of the
 // sequence) owns all output columns, with the segments' aggregates combined
-// across two launches.  Other sizes and fp32 take the column-block kernel:
+// across two launches; dk and dv share one workgroup, since their states
+// are transposes of each other.  Other sizes and fp32 take the column-block kernel:
 // one 256-thread workgroup (4 waves) per (unit, role, block of 16 output
 // columns), each walking its unit's whole sequence, all in one launch; the
 // roles and blocks of a unit are independent, so no segment exchange is
