@@ -558,13 +558,15 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(
         if constexpr (PHASE == 1) {
           // aggregates run the chunks last to first: each chunk's carry
           // operand takes the decay still to come in the segment, so the
-          // state and nu are plain sums (no per-chunk decay of the state)
+          // state and nu are plain sums (no per-chunk decay of the state);
+          // each lane sums its own row's part of nu, and the rows are
+          // summed once, after the last chunk
 #pragma unroll
           for (int e = 0; e < 8; ++e) x[e] = kv[e] * (F.kt[e] * rr[it][e]);
           store8(KT + t * LT + f0, x);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            nu[it][e] += row_sum(x[e]);
+            nu[it][e] += x[e];
             rr[it][e] *= F.dec[e];
             if (PP) dsum[it][e] += F.tot[e];
           }
@@ -736,6 +738,10 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(
           reinterpret_cast<f32x4 *>(sl)[(jb * NFT + i) * 64 + lane] = st[m][i];
       }
     }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) nu[it][e] = row_sum(nu[it][e]);
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int j = g + 4 * w + 16 * it;
