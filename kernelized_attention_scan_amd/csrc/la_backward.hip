@@ -531,6 +531,9 @@ struct SShape {
   static constexpr int SP = ROLE == kRoleDQ ? SZ : 0;
   static constexpr size_t lds_bytes =
       sizeof(T) * (2 * SX + SZ + SST + SP) + sizeof(float) * (kBC + 4);
+  // the aggregates launch stages only Y and Z: two workgroups fit a CU
+  static constexpr size_t lds_bytes_agg =
+      sizeof(T) * (SX + SZ) + sizeof(float) * (kBC + 4);
   static_assert(D / 16 == kSWaves, "one state column block per wave");
 };
 
@@ -546,12 +549,14 @@ __device__ __forceinline__ void seg_role(const BwdArgs &a, int64_t units,
   static_assert(ROLE == kRoleDQ || (ROLE == kRoleDK && PHASE == 1),
                 "seg_dkv reads out dk");
   constexpr bool REV = ROLE != kRoleDQ;
+  // PHASE 2: X, Y, Z, S^T, raw q (dq) and the powers of g; PHASE 1 reads
+  // no queries and publishes no S^T: Y, Z and the powers only
   T *sX = reinterpret_cast<T *>(smem);           // queries X
-  T *sY = sX + F::SX;                            // keys Y
+  T *sY = PHASE == 1 ? sX : sX + F::SX;          // keys Y
   T *sZ = sY + F::SX;                            // values Z (all d columns)
   T *sST = sZ + F::SZ;                           // S^T copy
   T *sP = sST + F::SST;                          // raw q rows (dq)
-  float *gp = reinterpret_cast<float *>(sP + F::SP);  // g^0 .. g^C
+  float *gp = reinterpret_cast<float *>(PHASE == 1 ? sST : sP + F::SP);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -574,7 +579,7 @@ __device__ __forceinline__ void seg_role(const BwdArgs &a, int64_t units,
   constexpr int XW = D + 2;
   for (int i = tid; i < C * (KX - XW); i += kSThreads) {
     const int row = i / (KX - XW), col = XW + i % (KX - XW);
-    sX[row * LX + col] = from_f32<T>(0.f);
+    if (PHASE == 2) sX[row * LX + col] = from_f32<T>(0.f);
     sY[row * LX + col] = from_f32<T>(0.f);
   }
 
@@ -1145,9 +1150,11 @@ __device__ __forceinline__ void seg_dkv(const BwdArgs &a, int64_t units,
   }
 }
 
+// The aggregates launch (PHASE 1) runs two workgroups per CU (four waves
+// per SIMD: at most 128 VGPRs); the readout one.
 template <bool DECAY, bool ELU, int PHASE>
-__global__ __launch_bounds__(kSThreads) void la_bwd_seg_kernel(BwdArgs a,
-                                                               int64_t units) {
+__global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
+    PHASE == 1 ? 4 : 1))) void la_bwd_seg_kernel(BwdArgs a, int64_t units) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int nseg = a.nseg;
   const int64_t per_role = units * nseg;
@@ -1174,22 +1181,24 @@ hipError_t launch_seg(const BwdArgs &a, int64_t units, hipStream_t s) {
   constexpr size_t lds = std::max({SShape<bf16, kRoleDQ>::lds_bytes,
                                    SShape<bf16, kRoleDK>::lds_bytes,
                                    kDkvLds});
-  static_assert(lds <= 160 * 1024, "LDS of one workgroup");
+  constexpr size_t lds1 = std::max(SShape<bf16, kRoleDQ>::lds_bytes_agg,
+                                   SShape<bf16, kRoleDK>::lds_bytes_agg);
+  static_assert(lds <= 160 * 1024 && 2 * lds1 <= 160 * 1024,
+                "LDS of one workgroup (two for the aggregates)");
   static const hipError_t once = [] {
-    for (const void *k :
-         {reinterpret_cast<const void *>(&la_bwd_seg_kernel<DECAY, ELU, 1>),
-          reinterpret_cast<const void *>(&la_bwd_seg_kernel<DECAY, ELU, 2>)}) {
-      const hipError_t e = hipFuncSetAttribute(
-          k, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-      if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&la_bwd_seg_kernel<DECAY, ELU, 1>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds1));
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&la_bwd_seg_kernel<DECAY, ELU, 2>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   }();
   if (once != hipSuccess) return once;
   const dim3 grid(static_cast<unsigned>(2 * units * nseg)), block(kSThreads);
   if (nseg > 1) {
-    hipLaunchKernelGGL((la_bwd_seg_kernel<DECAY, ELU, 1>), grid, block, lds, s,
-                       a, units);
+    hipLaunchKernelGGL((la_bwd_seg_kernel<DECAY, ELU, 1>), grid, block, lds1,
+                       s, a, units);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
