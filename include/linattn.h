@@ -203,18 +203,25 @@ la_status la_forward_train(const void *q, const void *k, const void *v,
  *   dq'_i = sum_{j<=i} w_ij (G_i . [v_j|1]) k'_j,
  *   dk'_j = sum_{i>=j} w_ij (G_i . [v_j|1]) q'_i,
  *   dv_j  = sum_{i>=j} w_ij (q'_i . k'_j) dout_i / den_i,
- * then through the feature map (elu + 1: times 1 for x > 0, e^x else).
+ * then through the feature map (elu + 1: times 1 for x > 0, e^x else;
+ * Performer, "Linear attention research 2026" page, Performer section:
+ * d phi_r / d x = phi_r(x) (omega_r - x), so dx = (dx' * phi(x)) omega^T -
+ * x (dx' . phi(x)), where for the queries dq' . phi(q) = 0 exactly, each
+ * output being unchanged by a scaling of its q', and that term is dropped).
  *   q, k, v, out, dout: device, dtype, [B][H][n][d] (out and den as
  *                       la_forward_train wrote them for these q, k, v)
  *   den   : device fp32 [B][H][n]
  *   dq, dk, dv: device, dtype, [B][H][n][d], written (may not alias inputs)
- *   map   : LA_MAP_ELU1 or LA_MAP_IDENTITY (LA_MAP_PERFORMER:
- *           LA_ERR_UNSUPPORTED); omega is ignored
+ *   map   : LA_MAP_ELU1, LA_MAP_IDENTITY or LA_MAP_PERFORMER
+ *   omega : LA_MAP_PERFORMER: device fp32 [d][d_feat], the forward's;
+ *           LA_ERR_INVALID_ARG if NULL; not differentiated.  Else ignored.
  *   decay : device fp32 [H] or NULL, as la_forward
  *   workspace: device, at least la_backward_workspace_bytes(...) bytes, no
  *           initial contents needed; LA_ERR_WORKSPACE if NULL.  Calls that
  *           share one workspace must be ordered (one stream).
- *   Supported: d == d_feat in {16, 32, 64, 128}.
+ *   Supported: ELU1, IDENTITY: d == d_feat in {16, 32, 64, 128};
+ *              PERFORMER: d in {32, 64, 128}, d_feat in {32, 64, 128, 256},
+ *              d * d_feat <= 16384.  Other sizes: LA_ERR_UNSUPPORTED.
  */
 la_status la_backward(const void *q, const void *k, const void *v,
                       const void *out, const float *den, const void *dout,
@@ -227,8 +234,10 @@ la_status la_backward(const void *q, const void *k, const void *v,
  * la_backward_workspace_bytes -- device workspace la_backward needs for
  * these sizes: per row, the prepared G row (d + 2 values padded to a
  * multiple of 32) and, for LA_MAP_ELU1, the features phi(k) and phi(q), all
- * in dtype.  Pure host function; 0 for arguments la_backward would reject
- * and for empty sizes.
+ * in dtype; for LA_MAP_PERFORMER the features phi(k), phi(q) (d_feat values
+ * each, dtype) and the feature gradients dq', dk' (d_feat values each,
+ * fp32).  Pure host function; 0 for arguments la_backward would reject and
+ * for empty sizes.
  */
 size_t la_backward_workspace_bytes(int B, int H, int64_t n, int d, int d_feat,
                                    la_map map, la_dtype dtype);

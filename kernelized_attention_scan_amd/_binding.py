@@ -563,10 +563,11 @@ def forward_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                   feature_map="elu1", decay: Optional[torch.Tensor] = None,
                   out: Optional[torch.Tensor] = None,
                   den: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None):
+                  workspace: Optional[torch.Tensor] = None,
+                  omega: Optional[torch.Tensor] = None):
     """The causal forward for training (la_forward_train): returns (out,
     den), den [B,H,n] fp32 being each row's denominator, which backward()
-    takes."""
+    takes.  omega: fp32 [d, m] for the performer map."""
     lib = load_library()
     if q.dim() != 4 or v.dim() != 4 or q.shape != k.shape:
         raise ValueError("q, k must be [B,H,n,d_qk] and v [B,H,n,d]")
@@ -577,11 +578,9 @@ def forward_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         raise TypeError("q, k, v must share one dtype")
     dt = _dtype_code(v.dtype)
     mapk = _map_code(feature_map)
-    if mapk == MAP_PERFORMER:
-        raise ValueError("forward_train: elu1 or identity features")
     if mapk != MAP_IDENTITY and q.shape[-1] != d:
-        raise ValueError("q, k must have width d for elu1")
-    d_feat = q.shape[-1]
+        raise ValueError("q, k must have width d for elu1 and performer")
+    d_feat = _check_omega(omega, mapk, d) or q.shape[-1]
     _check_decay(decay, H)
     if out is not None:
         _check_out(out, v.shape, v.dtype)
@@ -589,7 +588,7 @@ def forward_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                             tuple(den.shape) != (B, H, n)):
         raise ValueError("den must be float32 [B, H, n]")
     _on_gpu(v, (q, "q"), (k, "k"), (v, "v"), (out, "out"), (den, "den"),
-            (decay, "decay"), (workspace, "workspace"))
+            (decay, "decay"), (workspace, "workspace"), (omega, "omega"))
     if out is None:
         out = torch.empty_like(v)
     if den is None:
@@ -600,7 +599,8 @@ def forward_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if need and workspace.numel() < need:
         raise ValueError("workspace too small")
     st = lib.la_forward_train(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(den),
-                              B, H, n, d, d_feat, mapk, None, _ptr(decay), dt,
+                              B, H, n, d, d_feat, mapk, _ptr(omega),
+                              _ptr(decay), dt,
                               _ptr(workspace) if need else None,
                               _stream(v.device))
     _check(st, "la_forward_train")
@@ -609,10 +609,13 @@ def forward_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
 
 def backward_workspace_bytes(B: int, H: int, n: int, d: int,
                              feature_map="elu1",
-                             dtype: torch.dtype = torch.bfloat16) -> int:
-    """Device workspace la_backward needs (la_backward_workspace_bytes)."""
+                             dtype: torch.dtype = torch.bfloat16,
+                             d_feat: Optional[int] = None) -> int:
+    """Device workspace la_backward needs (la_backward_workspace_bytes);
+    d_feat defaults to d (the performer map's m otherwise)."""
     return int(load_library().la_backward_workspace_bytes(
-        B, H, n, d, d, _map_code(feature_map), _dtype_code(dtype)))
+        B, H, n, d, d if d_feat is None else d_feat, _map_code(feature_map),
+        _dtype_code(dtype)))
 
 
 # backward()'s workspaces when none is passed: one per (device, stream),
@@ -626,9 +629,11 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
              dq: Optional[torch.Tensor] = None,
              dk: Optional[torch.Tensor] = None,
              dv: Optional[torch.Tensor] = None,
-             workspace: Optional[torch.Tensor] = None):
+             workspace: Optional[torch.Tensor] = None,
+             omega: Optional[torch.Tensor] = None):
     """Gradients (dq, dk, dv) of sum(out * dout) for the causal forward
-    (la_backward); out and den as forward_train() returned them.
+    (la_backward); out and den as forward_train() returned them.  omega:
+    fp32 [d, m] for the performer map (not differentiated).
     workspace: optional uint8 device tensor of at least
     backward_workspace_bytes(...) bytes; by default one cached per (device,
     stream) is used."""
@@ -637,7 +642,7 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         raise ValueError("q, k must be [B,H,n,d] and v [B,H,n,d]")
     B, H, n, d = v.shape
     if q.shape != v.shape:
-        raise ValueError("la_backward needs q, k, v of one shape (d' = d)")
+        raise ValueError("la_backward needs q, k, v of one shape")
     for t, nm in ((out, "out"), (dout, "dout")):
         if t.shape != v.shape or t.dtype != v.dtype:
             raise ValueError(f"{nm} must match v in shape and dtype")
@@ -647,11 +652,12 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         raise ValueError("den must be float32 [B, H, n]")
     dt = _dtype_code(v.dtype)
     mapk = _map_code(feature_map)
+    d_feat = _check_omega(omega, mapk, d) or d
     _check_decay(decay, H)
     for t, nm in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
         if t is not None:
             _check_out(t, v.shape, v.dtype)
-    need = int(lib.la_backward_workspace_bytes(B, H, n, d, d, mapk, dt))
+    need = int(lib.la_backward_workspace_bytes(B, H, n, d, d_feat, mapk, dt))
     if workspace is not None and (workspace.dtype != torch.uint8
                                   or not workspace.is_contiguous()
                                   or workspace.numel() < need):
@@ -659,7 +665,7 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                          f"at least {need} bytes")
     _on_gpu(v, (q, "q"), (k, "k"), (v, "v"), (out, "out"), (den, "den"),
             (dout, "dout"), (decay, "decay"), (dq, "dq"), (dk, "dk"),
-            (dv, "dv"), (workspace, "workspace"))
+            (dv, "dv"), (workspace, "workspace"), (omega, "omega"))
     if workspace is None and need > 0:
         key = (v.device.index, torch.cuda.current_stream(v.device).cuda_stream)
         workspace = _bwd_workspaces.get(key)
@@ -671,8 +677,8 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     dv = torch.empty_like(v) if dv is None else dv
     st = lib.la_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(den),
                          _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, H, n, d,
-                         d, mapk, None, _ptr(decay), dt, _ptr(workspace),
-                         _stream(v.device))
+                         d_feat, mapk, _ptr(omega), _ptr(decay), dt,
+                         _ptr(workspace), _stream(v.device))
     _check(st, "la_backward")
     return dq, dk, dv
 
@@ -681,12 +687,14 @@ class _LinearAttention(torch.autograd.Function):
     """forward_train() forward, backward() gradients (no arithmetic here)."""
 
     @staticmethod
-    def forward(ctx, q, k, v, feature_map, decay):
+    def forward(ctx, q, k, v, feature_map, decay, omega):
         out, den = forward_train(q.contiguous(), k.contiguous(),
-                                 v.contiguous(), feature_map, decay=decay)
+                                 v.contiguous(), feature_map, decay=decay,
+                                 omega=omega)
         ctx.save_for_backward(q, k, v, out, den)
         ctx.feature_map = feature_map
         ctx.decay = decay
+        ctx.omega = omega
         return out
 
     @staticmethod
@@ -694,14 +702,16 @@ class _LinearAttention(torch.autograd.Function):
         q, k, v, out, den = ctx.saved_tensors
         dq, dk, dv = backward(q.contiguous(), k.contiguous(), v.contiguous(),
                               out, den, dout.contiguous(), ctx.feature_map,
-                              decay=ctx.decay)
-        return dq, dk, dv, None, None
+                              decay=ctx.decay, omega=ctx.omega)
+        return dq, dk, dv, None, None, None
 
 
 def linear_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                      feature_map="elu1",
-                     decay: Optional[torch.Tensor] = None) -> torch.Tensor:
+                     decay: Optional[torch.Tensor] = None,
+                     omega: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Causal kernelized linear attention as a differentiable torch op:
-    la_forward_train forward, la_backward gradients for q, k and v (decay is
-    not differentiated).  elu1 or identity features, d_feat == d."""
-    return _LinearAttention.apply(q, k, v, feature_map, decay)
+    la_forward_train forward, la_backward gradients for q, k and v (decay
+    and omega are not differentiated).  elu1 or identity features with
+    d_feat == d, or the performer map with omega fp32 [d, m]."""
+    return _LinearAttention.apply(q, k, v, feature_map, decay, omega)

@@ -634,16 +634,94 @@ size_t backward_ws(int64_t units, int64_t n, int d, int map, int dtype,
   if (agg_off) *agg_off = g + feats;
   return g + feats + agg;
 }
+// Workspace of la_backward with the Performer map: G~ rows, then K', Q'
+// (dtype) and the feature gradients dq', dk' (fp32), d_feat values per row
+// each; *fbytes and *gbytes are the sizes of one feature and one feature
+// gradient buffer.
+size_t backward_ws_performer(int64_t units, int64_t n, int d, int d_feat,
+                             int dtype, size_t *fbytes, size_t *gbytes) {
+  const size_t es = elem_size(dtype);
+  const size_t g = align256(static_cast<size_t>(units * n) *
+                            la::backward_gwidth(d) * es);
+  const size_t f = align256(static_cast<size_t>(units * n) * d_feat * es);
+  const size_t fg = align256(static_cast<size_t>(units * n) * d_feat * 4);
+  if (fbytes) *fbytes = f;
+  if (gbytes) *gbytes = fg;
+  return g + 2 * f + 2 * fg;
+}
 }  // namespace
 
 size_t la_backward_workspace_bytes(int B, int H, int64_t n, int d, int d_feat,
                                    la_map map, la_dtype dtype) {
-  if (B <= 0 || H <= 0 || n <= 0 || !valid_dtype(dtype) || !valid_map(map) ||
-      map == LA_MAP_PERFORMER || !la::backward_supported(d, d_feat))
+  if (B <= 0 || H <= 0 || n <= 0 || !valid_dtype(dtype) || !valid_map(map))
+    return 0;
+  if (map == LA_MAP_PERFORMER ? !la::backward_performer_supported(d, d_feat)
+                              : !la::backward_supported(d, d_feat))
     return 0;
   const int64_t units = static_cast<int64_t>(B) * H;
   if (units * n > (int64_t{1} << 46) || units > (int64_t{1} << 26)) return 0;
+  if (map == LA_MAP_PERFORMER)
+    return backward_ws_performer(units, n, d, d_feat, dtype, nullptr, nullptr);
   return backward_ws(units, n, d, map, dtype, nullptr);
+}
+
+// la_backward with the Performer map: K' = phi(k), Q' = phi(q) into the
+// workspace, the three roles over them (dq', dk' to the workspace, dv to
+// its output), then dq, dk through the map.
+static la_status backward_performer(const void *q, const void *k,
+                                    const void *v, const void *out,
+                                    const float *den, const void *dout,
+                                    void *dq, void *dk, void *dv, int B, int H,
+                                    int64_t n, int d, int d_feat,
+                                    const float *omega, const float *decay,
+                                    la_dtype dtype, void *workspace,
+                                    void *stream) {
+  if (!la::backward_performer_supported(d, d_feat))
+    return fail(LA_ERR_UNSUPPORTED,
+                "la_backward PERFORMER: d in {32, 64, 128}, d_feat in {32, "
+                "64, 128, 256}, d * d_feat <= 16384 are built (got d=%d "
+                "d_feat=%d)", d, d_feat);
+  const int64_t units = static_cast<int64_t>(B) * H;
+  if (units == 0 || n == 0) return ok();
+  if (units * n > (int64_t{1} << 46) || units > (int64_t{1} << 26))
+    return fail(LA_ERR_UNSUPPORTED, "sizes too large");
+  if (!q || !k || !v || !out || !den || !dout || !dq || !dk || !dv)
+    return fail(LA_ERR_INVALID_ARG, "null pointer argument");
+  if (!omega) return fail(LA_ERR_INVALID_ARG, "PERFORMER needs omega");
+  size_t fb = 0, gb = 0;
+  const size_t total =
+      backward_ws_performer(units, n, d, d_feat, dtype, &fb, &gb);
+  if (!workspace)
+    return fail(LA_ERR_WORKSPACE, "la_backward: workspace of %zu bytes required",
+                total);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned char *ws = static_cast<unsigned char *>(workspace);
+  const size_t g = total - 2 * fb - 2 * gb;
+  la::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.den = den;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.decay = decay;
+  a.H = H;
+  a.n = n;
+  a.dqk = d;
+  a.elu1 = 0;
+  a.gt = ws;
+  a.kf = ws + g;
+  a.qf = ws + g + fb;
+  a.dqf = ws + g + 2 * fb;
+  a.dkf = ws + g + 2 * fb + gb;
+  a.omega = omega;
+  a.nseg = 0;
+  a.agg = nullptr;
+  hipError_t e = la::launch_featmap_performer(k, a.kf, omega, units * n, d,
+                                              d_feat, dtype, dtype, s);
+  if (e == hipSuccess)
+    e = la::launch_featmap_performer(q, a.qf, omega, units * n, d, d_feat,
+                                     dtype, dtype, s);
+  if (e != hipSuccess) return hip_fail(e, "la_backward feature map");
+  e = la::launch_backward_performer(a, units, d, d_feat, dtype == LA_BF16 ? 1 : 0, s);
+  if (e != hipSuccess) return hip_fail(e, "la_backward launch");
+  return ok();
 }
 
 la_status la_backward(const void *q, const void *k, const void *v,
@@ -653,7 +731,6 @@ la_status la_backward(const void *q, const void *k, const void *v,
                       const float *decay, la_dtype dtype, void *workspace,
                       void *stream) {
   try {
-    (void)omega;
     if (B < 0 || H < 0 || n < 0)
       return fail(LA_ERR_INVALID_ARG, "negative size");
     if (!valid_map(map)) return fail(LA_ERR_INVALID_ARG, "unknown map %d", map);
@@ -664,8 +741,9 @@ la_status la_backward(const void *q, const void *k, const void *v,
     if (map == LA_MAP_ELU1 && d_feat != d)
       return fail(LA_ERR_INVALID_ARG, "ELU1 needs d_feat == d");
     if (map == LA_MAP_PERFORMER)
-      return fail(LA_ERR_UNSUPPORTED,
-                  "la_backward: the Performer map's gradient is not built");
+      return backward_performer(q, k, v, out, den, dout, dq, dk, dv, B, H, n,
+                                d, d_feat, omega, decay, dtype, workspace,
+                                stream);
     if (!la::backward_supported(d, d_feat))
       return fail(LA_ERR_UNSUPPORTED,
                   "la_backward: d = d_feat in {16, 32, 64, 128} is built "

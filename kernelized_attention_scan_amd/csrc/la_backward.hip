@@ -62,13 +62,13 @@ constexpr int bstride(int w) {
   return sizeof(T) == 2 ? (w % 32 == 16 ? w : w + 16) : w + 4;
 }
 
-template <typename T, int D, int ROLE, bool DECAY>
+template <typename T, int D, int DF, int ROLE, bool DECAY>
 struct BShape {
   // X and Y are G and V+ (d + 2 wide: the last value of G as a pair,
-  // padded to a multiple of 32) for the dq and dk roles, and K', Q' (d
+  // padded to a multiple of 32) for the dq and dk roles, and K', Q' (d'
   // wide, at least 32) for dv
   static constexpr bool GV = ROLE != kRoleDV;
-  static constexpr int KX = GV ? (D + 2 + 31) / 32 * 32 : (D < 32 ? 32 : D);
+  static constexpr int KX = GV ? (D + 2 + 31) / 32 * 32 : (DF < 32 ? 32 : DF);
   static constexpr int LX = bstride<T>(KX);
   static constexpr int LZ = bstride<T>(16);
   static constexpr int NT = KX / 16;                 // 16 x 16 state tiles
@@ -148,11 +148,15 @@ __device__ __forceinline__ float dphi(float x, bool elu) {  // d phi / d x
   return elu ? (x > 0.f ? 1.f : expf(x)) : 1.f;
 }
 
-// One role's workgroup: output columns 16 blk .. 16 blk + 15 of unit.
-template <typename T, int D, int ROLE, bool DECAY, bool ELU>
+// One role's workgroup: output columns 16 blk .. 16 blk + 15 of unit.  The
+// dq and dk roles write feature gradients, d' wide (times phi' for elu + 1,
+// where d' = d); with FG (the Performer map) they go to the workspace in
+// fp32 (dqf, dkf) and a conversion pass takes them through the map.
+template <typename T, int D, int DF, int ROLE, bool DECAY, bool ELU,
+          bool FG = false>
 __device__ __forceinline__ void bwd_role(const BwdArgs &a, int64_t unit,
                                          int blk, unsigned char *smem) {
-  using F = BShape<T, D, ROLE, DECAY>;
+  using F = BShape<T, D, DF, ROLE, DECAY>;
   constexpr int C = kBC, KX = F::KX, LX = F::LX, LZ = F::LZ;
   constexpr bool GV = F::GV, REV = ROLE != kRoleDQ;
   constexpr int VEC = 16 / sizeof(T);
@@ -177,17 +181,20 @@ __device__ __forceinline__ void bwd_role(const BwdArgs &a, int64_t unit,
   const T *vb = static_cast<const T *>(a.v) + unit * n * D;
   constexpr int KG = backward_gwidth(D);  // G~ row width
   const T *gtb = static_cast<const T *>(a.gt) + unit * n * KG;
-  const T *kfb = static_cast<const T *>(a.kf) + unit * n * D;
-  const T *qfb = static_cast<const T *>(a.qf) + unit * n * D;
-  T *res = static_cast<T *>(ROLE == kRoleDQ ? a.dq
-                            : ROLE == kRoleDK ? a.dk
-                                              : a.dv) +
-           unit * n * D;
+  const T *kfb = static_cast<const T *>(a.kf) + unit * n * DF;
+  const T *qfb = static_cast<const T *>(a.qf) + unit * n * DF;
+  // output rows: d' feature gradients (dq, dk) or d values (dv)
+  constexpr int RW = ROLE == kRoleDV ? D : DF;
+  using RT = std::conditional_t<FG && ROLE != kRoleDV, float, T>;
+  void *rb = ROLE == kRoleDQ ? (FG ? a.dqf : a.dq)
+             : ROLE == kRoleDK ? (FG ? a.dkf : a.dk)
+                               : a.dv;
+  RT *res = static_cast<RT *>(rb) + unit * n * RW;
 
   // Constant parts: the padding columns of X and Y past the data (zero for
   // every row; G~ rows are copied whole, the ones columns of V+ are written
   // per chunk).
-  constexpr int XW = GV ? D + 2 : D;  // written columns of X, Y
+  constexpr int XW = GV ? D + 2 : DF;  // written columns of X, Y
   for (int i = tid; i < C * (KX - XW); i += kBThreads) {
     const int row = i / (KX - XW), col = XW + i % (KX - XW);
     sX[row * LX + col] = from_f32<T>(0.f);
@@ -209,8 +216,9 @@ __device__ __forceinline__ void bwd_role(const BwdArgs &a, int64_t unit,
   // Register ring (one chunk ahead).  GV roles: G~ and v full rows, the
   // K' block (dq) or Q' block (dk).  dv: K', Q' full rows, the G~ block.
   BSlab<T, KG, KG> rg;         // GV: G~
-  BSlab<T, D, D> r1, r2;       // GV: v (r1)   dv: K' (r1), Q' (r2)
-  BSlab<T, 16, D> rz;          // GV: K' or Q' block
+  BSlab<T, D, D> r1;           // GV: v
+  BSlab<T, DF, DF> r1f, r2f;   // dv: K' (r1f), Q' (r2f)
+  BSlab<T, 16, DF> rz;         // GV: K' or Q' block
   BSlab<T, 16, KG> rzg;        // dv: G~ block
   auto load = [&](int c) {
     const int64_t r0 = row0_of(c);
@@ -220,8 +228,8 @@ __device__ __forceinline__ void bwd_role(const BwdArgs &a, int64_t unit,
       r1.load(vb, r0, rows, 0, tid);
       rz.load(ROLE == kRoleDQ ? kfb : qfb, r0, rows, col0, tid);
     } else {
-      r1.load(kfb, r0, rows, 0, tid);
-      r2.load(qfb, r0, rows, 0, tid);
+      r1f.load(kfb, r0, rows, 0, tid);
+      r2f.load(qfb, r0, rows, 0, tid);
       rzg.load(gtb, r0, rows, col0, tid);
     }
   };
@@ -256,8 +264,8 @@ __device__ __forceinline__ void bwd_role(const BwdArgs &a, int64_t unit,
         sV[t * LX + D + 1] = one;
       }
     } else {
-      put(r1, sX, LX, trow);
-      put(r2, sY, LX, trow);
+      put(r1f, sX, LX, trow);
+      put(r2f, sY, LX, trow);
     }
     if constexpr (GV)
       put(rz, sZ, LZ, trow);
@@ -286,6 +294,7 @@ __device__ __forceinline__ void bwd_role(const BwdArgs &a, int64_t unit,
   // (row t of the chunk, columns col0 + 4 g ..) for phi', loaded with the
   // chunk's operands (pfn) and moved to pfc once that chunk is staged, so
   // the load is never waited for at the output
+  static_assert(!ELU || DF == D, "elu + 1 keeps d' = d");
   constexpr bool PFI = GV && ELU;
   using PV = std::conditional_t<sizeof(T) == 2, u32x2, u32x4>;
   PV pfn{}, pfc{};
@@ -384,7 +393,7 @@ __device__ __forceinline__ void bwd_role(const BwdArgs &a, int64_t unit,
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         x[r] = PFI ? o[r] * dphi(xin[r], true) : o[r];
-      store4(res + row * D + col0 + 4 * g, x[0], x[1], x[2], x[3]);
+      store4(res + row * RW + col0 + 4 * g, x[0], x[1], x[2], x[3]);
     }
     // ---- state update: S <- g^r S + (w Y)^T Z, the weights w_s =
     // b g^(r-1-s) of positions 32 kb + 8 g + e applied in registers ----
@@ -1211,12 +1220,13 @@ hipError_t launch_seg(const BwdArgs &a, int64_t units, hipStream_t s) {
 // dk, the last units nv dv (nq = d'/16, nv = d/16).  Within a role the
 // blocks of one unit get indices of one XCD (workgroups are dispatched to
 // the 8 XCDs round-robin), so the rows they all read come from its L2.
-template <typename T, int D, bool DECAY, bool ELU>
-__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 3 : 1)))
+template <typename T, int D, int DF, bool DECAY, bool ELU, bool FG = false>
+__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(
+    sizeof(T) == 2 ? (DF <= 128 ? 3 : 2) : 1)))
 void la_bwd_kernel(BwdArgs a,
                                                            int64_t units) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int nq = a.dqk / 16, nv = D / 16;
+  constexpr int nq = DF / 16, nv = D / 16;
   const int64_t b = blockIdx.x;
   const int64_t cq = units * nq;
   const int role = b < cq ? kRoleDQ : b < 2 * cq ? kRoleDK : kRoleDV;
@@ -1227,11 +1237,11 @@ void la_bwd_kernel(BwdArgs a,
   const int64_t unit = i / nblk;
   const int blk = static_cast<int>(i % nblk);
   if (role == kRoleDQ)
-    bwd_role<T, D, kRoleDQ, DECAY, ELU>(a, unit, blk, smem);
+    bwd_role<T, D, DF, kRoleDQ, DECAY, ELU, FG>(a, unit, blk, smem);
   else if (role == kRoleDK)
-    bwd_role<T, D, kRoleDK, DECAY, ELU>(a, unit, blk, smem);
+    bwd_role<T, D, DF, kRoleDK, DECAY, ELU, FG>(a, unit, blk, smem);
   else
-    bwd_role<T, D, kRoleDV, DECAY, ELU>(a, unit, blk, smem);
+    bwd_role<T, D, DF, kRoleDV, DECAY, ELU, FG>(a, unit, blk, smem);
 }
 
 template <typename T, int D, bool ELU>
@@ -1245,9 +1255,9 @@ hipError_t launch_prep(const BwdArgs &a, int64_t units, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T, int D, bool DECAY, bool ELU>
+template <typename T, int D, int DF, bool DECAY, bool ELU, bool FG = false>
 hipError_t launch_all(const BwdArgs &a, int64_t units, hipStream_t s) {
-  if constexpr (std::is_same_v<T, bf16> && D == kSegD) {
+  if constexpr (std::is_same_v<T, bf16> && D == kSegD && DF == D) {
     if (a.nseg > 0) {
       // segmented roles map k, q themselves: the preparation pass writes
       // only G~
@@ -1259,27 +1269,183 @@ hipError_t launch_all(const BwdArgs &a, int64_t units, hipStream_t s) {
   hipError_t e = launch_prep<T, D, ELU>(a, units, s);
   if (e != hipSuccess) return e;
   constexpr size_t lds =
-      std::max({BShape<T, D, kRoleDQ, DECAY>::lds_bytes,
-                BShape<T, D, kRoleDK, DECAY>::lds_bytes,
-                BShape<T, D, kRoleDV, DECAY>::lds_bytes});
+      std::max({BShape<T, D, DF, kRoleDQ, DECAY>::lds_bytes,
+                BShape<T, D, DF, kRoleDK, DECAY>::lds_bytes,
+                BShape<T, D, DF, kRoleDV, DECAY>::lds_bytes});
+  static_assert(lds <= 160 * 1024, "LDS of one workgroup");
   static const hipError_t once = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&la_bwd_kernel<T, D, DECAY, ELU>),
+      reinterpret_cast<const void *>(&la_bwd_kernel<T, D, DF, DECAY, ELU, FG>),
       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (once != hipSuccess) return once;
-  const int64_t blocks = units * (2 * (a.dqk / 16) + D / 16);
-  hipLaunchKernelGGL((la_bwd_kernel<T, D, DECAY, ELU>),
+  const int64_t blocks = units * (2 * (DF / 16) + D / 16);
+  hipLaunchKernelGGL((la_bwd_kernel<T, D, DF, DECAY, ELU, FG>),
                      dim3(static_cast<unsigned>(blocks)), dim3(kBThreads), lds,
                      s, a, units);
   return hipGetLastError();
 }
 
+// Performer map ("Linear attention research 2026" page, Performer random
+// features: phi_r(x) = exp(x . omega_r - |x|^2 / 2) / sqrt(m)), whose
+// derivative is d phi_r / d x = phi_r(x) (omega_r - x): a feature gradient
+// gx' becomes, per row,
+//   gx = (gx' * phi(x)) omega^T - x sum_r gx'_r phi_r(x).
+// For the queries the last sum is exactly zero: each output is unchanged
+// when q'_t is scaled (q'_t mu_t / q'_t . nu_t), so q'_t . dq'_t = 0.  It is
+// dropped there (with_sum = 0): computed from rounded operands it would
+// only add the noise of a cancelling sum of d' terms.
+// pf_rows<D>() rows per step: u = gx' * phi(x) goes to LDS transposed ([r][row]),
+// omega^T to LDS once ([r][c]); thread (row block rb, column block j) forms
+// rows 4 rb .. +3, columns 4 j .. +3 with 16 multiply-adds per r, both
+// operands 16-byte LDS reads.  fp32 throughout; rows past the end are
+// skipped.
+template <int D>
+constexpr int pf_rows() {  // 4 rows x 4 columns per thread, at most 64 rows
+  return 16 * kBThreads / D < 64 ? 16 * kBThreads / D : 64;
+}
+template <int D, int DF>
+constexpr size_t pf_grad_lds() {
+  return sizeof(float) * (static_cast<size_t>(DF) * D +
+                          static_cast<size_t>(DF) * (pf_rows<D>() + 4) +
+                          pf_rows<D>());
+}
+
+template <typename T, int D, int DF>
+__global__ __launch_bounds__(kBThreads) void la_bwd_pf_grad_kernel(
+    const T *__restrict__ xf, const float *__restrict__ gf,
+    const T *__restrict__ x, T *__restrict__ dx,
+    const float *__restrict__ omega, int64_t rows, int with_sum) {
+  constexpr int kPfRows = pf_rows<D>();
+  static_assert(D % 16 == 0 && (kPfRows / 4) * (D / 4) <= kBThreads,
+                "thread tiling");
+  constexpr int LU = kPfRows + 4;  // row stride of u (padding: banks)
+  constexpr int VEC = 16 / sizeof(T);
+  extern __shared__ __align__(16) unsigned char smem[];
+  float *om = reinterpret_cast<float *>(smem);  // [DF][D]: omega^T
+  float *u = om + DF * D;                       // [DF][LU]
+  float *su = u + DF * LU;                      // [kPfRows]
+  const int tid = threadIdx.x;
+  for (int i = tid; i < DF * D; i += kBThreads) {
+    const int r = i / D, c = i % D;
+    om[i] = omega[c * DF + r];
+  }
+  const int nj = D / 4;
+  const int rb = tid / nj, j = tid % nj;  // rows 4 rb .., columns 4 j ..
+  const bool active = rb < kPfRows / 4;
+  const int64_t nsteps = (rows + kPfRows - 1) / kPfRows;
+  for (int64_t st = blockIdx.x; st < nsteps; st += gridDim.x) {
+    const int64_t row0 = st * kPfRows;
+    __syncthreads();  // om ready; the previous step's u, su are read
+    // u = gx' * phi(x), transposed; pieces of VEC consecutive features
+    for (int p = tid; p < kPfRows * DF / VEC; p += kBThreads) {
+      const int rr = p / (DF / VEC), f0 = (p % (DF / VEC)) * VEC;
+      float a[VEC], b[VEC];
+      if (row0 + rr < rows) {
+        const int64_t off = (row0 + rr) * DF + f0;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) a[e] = gf[off + e];
+        piece_to_f32<T>(*reinterpret_cast<const u32x4 *>(xf + off), b);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) a[e] = b[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) u[(f0 + e) * LU + rr] = a[e] * b[e];
+    }
+    __syncthreads();
+    if (tid < kPfRows) {  // sum_r u_r of each row, in a fixed order
+      float acc = 0.f;
+      if (with_sum)
+        for (int r = 0; r < DF; ++r) acc += u[r * LU + tid];
+      su[tid] = acc;
+    }
+    __syncthreads();
+    if (active) {
+      f32x4 acc[4] = {};
+      for (int r = 0; r < DF; ++r) {
+        const f32x4 uu = *reinterpret_cast<const f32x4 *>(u + r * LU + 4 * rb);
+        const f32x4 ww = *reinterpret_cast<const f32x4 *>(om + r * D + 4 * j);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += uu[i] * ww;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t row = row0 + 4 * rb + i;
+        if (row < rows) {
+          const T *xr = x + row * D + 4 * j;
+          const float s = su[4 * rb + i];
+          store4(dx + row * D + 4 * j, acc[i][0] - to_f32(xr[0]) * s,
+                 acc[i][1] - to_f32(xr[1]) * s, acc[i][2] - to_f32(xr[2]) * s,
+                 acc[i][3] - to_f32(xr[3]) * s);
+        }
+      }
+    }
+  }
+}
+
+// Performer backward for one size: G~ (no features: K' and Q' are in the
+// workspace already), the three roles by column blocks (dq', dk' to the
+// workspace in fp32, dv to its output), then dq and dk through the map.
+template <typename T, int D, int DF>
+hipError_t launch_pf(const BwdArgs &a, int64_t units, hipStream_t s) {
+  hipError_t e = launch_prep<T, D, false>(a, units, s);
+  if (e != hipSuccess) return e;
+  e = a.decay ? launch_all<T, D, DF, true, false, true>(a, units, s)
+              : launch_all<T, D, DF, false, false, true>(a, units, s);
+  if (e != hipSuccess) return e;
+  constexpr size_t lds = pf_grad_lds<D, DF>();
+  static_assert(lds <= 160 * 1024, "LDS of the conversion pass");
+  static const hipError_t once = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(&la_bwd_pf_grad_kernel<T, D, DF>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (once != hipSuccess) return once;
+  const int64_t rows = units * a.n;
+  constexpr int PR = pf_rows<D>();
+  const unsigned grid = static_cast<unsigned>(
+      std::min<int64_t>((rows + PR - 1) / PR, int64_t{kCUs} * 4));
+  hipLaunchKernelGGL((la_bwd_pf_grad_kernel<T, D, DF>), dim3(grid),
+                     dim3(kBThreads), lds, s, static_cast<const T *>(a.qf),
+                     static_cast<const float *>(a.dqf), static_cast<const T *>(a.q),
+                     static_cast<T *>(a.dq), a.omega, rows, 0);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((la_bwd_pf_grad_kernel<T, D, DF>), dim3(grid),
+                     dim3(kBThreads), lds, s, static_cast<const T *>(a.kf),
+                     static_cast<const float *>(a.dkf), static_cast<const T *>(a.k),
+                     static_cast<T *>(a.dk), a.omega, rows, 1);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_pf_d(const BwdArgs &a, int64_t units, int df, hipStream_t s) {
+  switch (df) {
+    case 32: return launch_pf<T, D, 32>(a, units, s);
+    case 64: return launch_pf<T, D, 64>(a, units, s);
+    case 128: return launch_pf<T, D, 128>(a, units, s);
+    case 256:
+      if constexpr (D * 256 <= 16384) return launch_pf<T, D, 256>(a, units, s);
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+hipError_t launch_pf_t(const BwdArgs &a, int64_t units, int d, int df,
+                       hipStream_t s) {
+  switch (d) {
+    case 32: return launch_pf_d<T, 32>(a, units, df, s);
+    case 64: return launch_pf_d<T, 64>(a, units, df, s);
+    case 128: return launch_pf_d<T, 128>(a, units, df, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <typename T, int D>
 hipError_t launch_d(const BwdArgs &a, int64_t units, hipStream_t s) {
   if (a.decay)
-    return a.elu1 ? launch_all<T, D, true, true>(a, units, s)
-                  : launch_all<T, D, true, false>(a, units, s);
-  return a.elu1 ? launch_all<T, D, false, true>(a, units, s)
-                : launch_all<T, D, false, false>(a, units, s);
+    return a.elu1 ? launch_all<T, D, D, true, true>(a, units, s)
+                  : launch_all<T, D, D, true, false>(a, units, s);
+  return a.elu1 ? launch_all<T, D, D, false, true>(a, units, s)
+                : launch_all<T, D, D, false, false>(a, units, s);
 }
 
 template <typename T>
@@ -1297,6 +1463,19 @@ hipError_t launch_t(const BwdArgs &a, int64_t units, int d, hipStream_t s) {
 
 bool backward_supported(int d, int d_feat) {
   return d == d_feat && (d == 16 || d == 32 || d == 64 || d == 128);
+}
+
+bool backward_performer_supported(int d, int d_feat) {
+  return (d == 32 || d == 64 || d == 128) &&
+         (d_feat == 32 || d_feat == 64 || d_feat == 128 || d_feat == 256) &&
+         d * d_feat <= 16384;
+}
+
+hipError_t launch_backward_performer(const BwdArgs &a, int64_t units, int d,
+                                     int d_feat, int dtype, hipStream_t s) {
+  if (!backward_performer_supported(d, d_feat)) return hipErrorInvalidValue;
+  return dtype == 1 ? launch_pf_t<bf16>(a, units, d, d_feat, s)
+                    : launch_pf_t<float>(a, units, d, d_feat, s);
 }
 
 int backward_segments(int64_t units, int64_t n, int d, int dtype) {

@@ -169,8 +169,21 @@ struct BwdArgs {
   // and their aggregates in the workspace (backward_agg_floats() floats).
   int nseg;
   float *agg;
+  // Performer map (else null): K' and Q' are its features ([units][n]
+  // [d_feat], in kf, qf), the dq and dk roles write the feature gradients
+  // dq', dk' ([units][n][d_feat]) here, and a last pass takes them through
+  // the map with omega ([d][d_feat] fp32).
+  void *dqf = nullptr, *dkf = nullptr;
+  const float *omega = nullptr;
 };
 bool backward_supported(int d, int d_feat);
+// Sizes the Performer map's backward is built for.
+bool backward_performer_supported(int d, int d_feat);
+// Enqueue the Performer map's backward (preparation, roles, conversion);
+// kf, qf must hold the features already.
+hipError_t launch_backward_performer(const BwdArgs &a, int64_t units, int d,
+                                     int d_feat, int dtype,
+                                     hipStream_t stream);
 // Width of a G~ row: d + 2 rounded up to a multiple of 32.
 constexpr int backward_gwidth(int d) { return (d + 2 + 31) / 32 * 32; }
 // Segments per (role, unit) of the segmented roles (bf16, d = 128), or 0

@@ -172,11 +172,67 @@ def test_backward_full_size_every_unit():
     assert max(worst) <= GTOL[torch.bfloat16]
 
 
-def test_backward_rejects_performer():
-    x = torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16, device="cuda")
+PF_GRID = [
+    # (name, B, H, n, d, m, dtype, decayed): the Performer map's backward
+    # (features, column-block roles over d' = m, then the map's chain rule)
+    ("pf_d64_m256_bf16", 1, 2, 300, 64, 256, torch.bfloat16, False),
+    ("pf_d64_m256_bf16_decay", 1, 2, 333, 64, 256, torch.bfloat16, True),
+    ("pf_d32_m64_fp32", 2, 1, 200, 32, 64, torch.float32, False),
+    ("pf_d32_m64_fp32_decay", 1, 2, 129, 32, 64, torch.float32, True),
+    ("pf_d128_m128_bf16", 1, 1, 150, 128, 128, torch.bfloat16, True),
+    ("pf_d64_m32_fp32_one_chunk", 1, 3, 40, 64, 32, torch.float32, False),
+]
+
+
+@pytest.mark.parametrize("case", PF_GRID, ids=[c[0] for c in PF_GRID])
+def test_backward_performer_matches_oracle(case):
+    name, B, H, n, d, m, dtype, decayed = case
+    cfg = I.PERFORMER.replace(B=B, H=H, n=n, d=d, m=m, dtype=dtype,
+                              decay=I.DECAYED.decay if decayed else None)
+    x = make(cfg, 31)
+    q, k, v, om = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["omega"])
+    dec = dev(x["decay"])
+    out, den = K.forward_train(q, k, v, "performer", decay=dec, omega=om)
+    dq, dk, dv = K.backward(q, k, v, out, den, dev(x["dout"]), "performer",
+                            decay=dec, omega=om)
+    torch.cuda.synchronize()
+    ref_out = oracle.forward(f64(x["q"]), f64(x["k"]), f64(x["v"]),
+                             oracle.MAP_PERFORMER, f64(x["omega"]),
+                             f64(x["decay"]))
+    assert rel(out, ref_out) <= TOL[dtype]
+    refs = oracle.backward(f64(x["q"]), f64(x["k"]), f64(x["v"]),
+                           f64(x["dout"]), oracle.MAP_PERFORMER,
+                           f64(x["omega"]), f64(x["decay"]))
+    errs = [rel(t, r) for t, r in zip((dq, dk, dv), refs)]
+    print(f"{name}: rel err dq {errs[0]:.2e} dk {errs[1]:.2e} "
+          f"dv {errs[2]:.2e}", flush=True)
+    assert max(errs) <= GTOL[dtype]
+
+
+def test_autograd_op_performer_matches_oracle():
+    """linear_attention() with the performer map: forward_train through the
+    fused map, la_backward's gradients through the map's chain rule."""
+    cfg = I.PERFORMER.replace(B=1, H=2, n=257, d=64, m=128,
+                              dtype=torch.float32)
+    x = make(cfg, 41)
+    q, k, v = (dev(x[n]).requires_grad_(True) for n in ("q", "k", "v"))
+    om = dev(x["omega"])
+    out = K.linear_attention(q, k, v, "performer", omega=om)
+    out.backward(dev(x["dout"]))
+    torch.cuda.synchronize()
+    refs = oracle.backward(f64(x["q"]), f64(x["k"]), f64(x["v"]),
+                           f64(x["dout"]), oracle.MAP_PERFORMER,
+                           f64(x["omega"]), None)
+    for t, r in zip((q, k, v), refs):
+        assert rel(t.grad, r) <= GTOL[torch.float32]
+
+
+def test_backward_performer_rejects_unbuilt_sizes():
+    x = torch.zeros(1, 2, 64, 16, dtype=torch.bfloat16, device="cuda")
     den = torch.ones(1, 2, 64, device="cuda")
+    om = torch.zeros(16, 64, device="cuda")
     with pytest.raises(K.LinAttnError) as e:
-        K.backward(x, x, x, x, den, x, "performer")
+        K.backward(x, x, x, x, den, x, "performer", omega=om)
     assert e.value.status == K._binding.LA_ERR_UNSUPPORTED
 
 

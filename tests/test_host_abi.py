@@ -317,7 +317,19 @@ def test_backward_workspace_bytes(lib):
     # rejected or empty: 0
     assert K.backward_workspace_bytes(2, 3, 100, 48) == 0
     assert K.backward_workspace_bytes(2, 3, 0, 64) == 0
-    assert K.backward_workspace_bytes(2, 3, 100, 64, "performer") == 0
+    # the Performer map: G~ rows, then K', Q' (bf16) and dq', dk' (fp32),
+    # d_feat values each
+    assert K.backward_workspace_bytes(2, 3, 100, 64, "performer",
+                                      d_feat=256) == (
+        a256(rows * 96 * 2) + 2 * a256(rows * 256 * 2) +
+        2 * a256(rows * 256 * 4))
+    assert K.backward_workspace_bytes(2, 3, 100, 64, "performer") == (
+        a256(rows * 96 * 2) + 2 * a256(rows * 64 * 2) +
+        2 * a256(rows * 64 * 4))
+    # Performer sizes not built: d = 16, d * d_feat > 16384
+    assert K.backward_workspace_bytes(2, 3, 100, 16, "performer") == 0
+    assert K.backward_workspace_bytes(2, 3, 100, 128, "performer",
+                                      d_feat=256) == 0
 
 
 def test_backward_rejects_null_workspace(lib):
