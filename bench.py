@@ -49,7 +49,7 @@ KERNEL_SOURCES = {
                 "la_api.cpp"],
     "decode": ["la_device.h", "la_internal.h", "la_decode.hip", "la_api.cpp"],
     "backward": ["la_device.h", "la_internal.h", "la_backward.hip",
-                 "la_api.cpp"],
+                 "la_featmap.hip", "la_api.cpp"],
     "rows": ["la_device.h", "la_internal.h", "la_forward_rows.h",
              "la_forward_rows_inst.h", "la_forward_rows.hip",
              "la_forward_rows_bf16.hip", "la_forward_rows_f32.hip",
@@ -62,7 +62,7 @@ def kernel_kind(workload: str) -> str:
         return "decode"
     if workload == "channel":
         return "rows"
-    return workload if workload == "backward" else "forward"
+    return "backward" if workload.startswith("backward") else "forward"
 
 
 def kernel_source_hash(kind: str) -> str:
@@ -81,7 +81,8 @@ def workloads():
             "performer": I.PERFORMER, "tiny": I.TINY_FP32,
             "decode": I.DECODE, "noncausal": I.ELU1_NONCAUSAL,
             "gated": I.GATED, "backward": I.DECAYED, "channel": I.CHANNEL,
-            "decode_channel": I.DECODE_CHANNEL}
+            "decode_channel": I.DECODE_CHANNEL,
+            "backward_performer": I.PERFORMER}
 
 
 def esize(dtype) -> int:
@@ -396,13 +397,14 @@ def backward_leg(torch, K, I, cfg, args, dev):
     dout = torch.randn(cfg.B, cfg.H, cfg.n, cfg.d, generator=g).to(
         cfg.dtype).to(dev)
     out, den = K.forward_train(s["q"], s["k"], s["v"], mapname,
-                               decay=s["decay"])
+                               decay=s["decay"], omega=s["omega"])
     grads = [torch.empty_like(s["q"]) for _ in range(3)]
     stream = torch.cuda.current_stream(dev)
 
     def step(i):
         K.backward(s["q"], s["k"], s["v"], out, den, dout, mapname,
-                   decay=s["decay"], dq=grads[0], dk=grads[1], dv=grads[2])
+                   decay=s["decay"], dq=grads[0], dk=grads[1], dv=grads[2],
+                   omega=s["omega"])
 
     settled = settle(torch, step, args.settle_ms)
     for i in range(args.warmup):
@@ -412,7 +414,11 @@ def backward_leg(torch, K, I, cfg, args, dev):
     t_wall = time.perf_counter() - t_wall
     return {"ms": ms, "t_wall": t_wall, "items": cfg.tokens,
             "unit": "tokens/s", "bytes": byts, "flops": flops,
-            "kern": {"kernel": "la_bwd_prep_kernel + la_bwd_seg_kernel "
+            "kern": {"kernel": ("la_featmap_performer_kernel x2 + "
+                                "la_bwd_prep_kernel + la_bwd_kernel + "
+                                "la_bwd_pf_grad_kernel x2 per step")
+                               if cfg.mapk == I.MAP_PERFORMER else
+                               "la_bwd_prep_kernel + la_bwd_seg_kernel "
                                "(aggregates, then readout) per step",
                      "ms": ms, "bytes": byts, "flops": flops},
             "nsets": 1, "settle_steps": settled,
@@ -438,7 +444,7 @@ def cpu_baseline_backward(cfg, seed: int, budget_s: float = 15.0):
     def run(take):
         sl = slice(0, take)
         return oracle.backward(f64(q[:, sl]), f64(k[:, sl]), f64(v[:, sl]),
-                               f64(do[:, sl]), cfg.mapk, None,
+                               f64(do[:, sl]), cfg.mapk, f64(x["omega"]),
                                None if dec is None else f64(dec[sl]))
 
     probe = min(units, threads)
@@ -582,7 +588,7 @@ def main() -> int:
         cfg = cfg.replace(n=args.n,
                           name=re.sub(r"n\d+", f"n{args.n}", cfg.name, count=1))
     is_decode = args.workload.startswith("decode")
-    is_bwd = args.workload == "backward"
+    is_bwd = args.workload.startswith("backward")
     leg = (decode_leg if is_decode else backward_leg if is_bwd
            else prefill_leg)(torch, K, I, cfg, args, dev)
     ms = leg["ms"]

@@ -1293,20 +1293,14 @@ hipError_t launch_all(const BwdArgs &a, int64_t units, hipStream_t s) {
 // when q'_t is scaled (q'_t mu_t / q'_t . nu_t), so q'_t . dq'_t = 0.  It is
 // dropped there (with_sum = 0): computed from rounded operands it would
 // only add the noise of a cancelling sum of d' terms.
-// pf_rows<D>() rows per step: u = gx' * phi(x) goes to LDS transposed ([r][row]),
-// omega^T to LDS once ([r][c]); thread (row block rb, column block j) forms
-// rows 4 rb .. +3, columns 4 j .. +3 with 16 multiply-adds per r, both
-// operands 16-byte LDS reads.  fp32 throughout; rows past the end are
-// skipped.
-template <int D>
-constexpr int pf_rows() {  // 4 rows x 4 columns per thread, at most 64 rows
-  return 16 * kBThreads / D < 64 ? 16 * kBThreads / D : 64;
-}
+// 64 rows per step: u = gx' * phi(x) ([row][r]) and omega ([c][r], kept for
+// the whole kernel) in LDS, the product u omega^T on the matrix cores in
+// fp32 (v_mfma_f32_16x16x4_f32: exact products, fp32 sums); each wave takes
+// every fourth 16 x 16 output tile.  Rows past the end are skipped.
+constexpr int kPfRows = 64;
 template <int D, int DF>
 constexpr size_t pf_grad_lds() {
-  return sizeof(float) * (static_cast<size_t>(DF) * D +
-                          static_cast<size_t>(DF) * (pf_rows<D>() + 4) +
-                          pf_rows<D>());
+  return sizeof(float) * (static_cast<size_t>(D + kPfRows) * (DF + 4) + kPfRows);
 }
 
 template <typename T, int D, int DF>
@@ -1314,68 +1308,95 @@ __global__ __launch_bounds__(kBThreads) void la_bwd_pf_grad_kernel(
     const T *__restrict__ xf, const float *__restrict__ gf,
     const T *__restrict__ x, T *__restrict__ dx,
     const float *__restrict__ omega, int64_t rows, int with_sum) {
-  constexpr int kPfRows = pf_rows<D>();
-  static_assert(D % 16 == 0 && (kPfRows / 4) * (D / 4) <= kBThreads,
-                "thread tiling");
-  constexpr int LU = kPfRows + 4;  // row stride of u (padding: banks)
+  constexpr int PR = kPfRows, L = DF + 4;  // row stride of omega and u
   constexpr int VEC = 16 / sizeof(T);
+  constexpr int NT = (PR / 16) * (D / 16), TPW = (NT + kBWaves - 1) / kBWaves;
+  constexpr int TPR = DF / VEC;            // fill threads per row
+  static_assert(DF % 32 == 0 && D % 16 == 0 && kBThreads % TPR == 0 &&
+                    TPR <= kWave,
+                "tiling");
   extern __shared__ __align__(16) unsigned char smem[];
-  float *om = reinterpret_cast<float *>(smem);  // [DF][D]: omega^T
-  float *u = om + DF * D;                       // [DF][LU]
-  float *su = u + DF * LU;                      // [kPfRows]
-  const int tid = threadIdx.x;
-  for (int i = tid; i < DF * D; i += kBThreads) {
-    const int r = i / D, c = i % D;
-    om[i] = omega[c * DF + r];
-  }
-  const int nj = D / 4;
-  const int rb = tid / nj, j = tid % nj;  // rows 4 rb .., columns 4 j ..
-  const bool active = rb < kPfRows / 4;
-  const int64_t nsteps = (rows + kPfRows - 1) / kPfRows;
+  float *om = reinterpret_cast<float *>(smem);  // [D][L]: omega
+  float *u = om + D * L;                        // [PR][L]
+  float *su = u + PR * L;                       // [PR]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = tid >> 6, g = lane >> 4, li = lane & 15;
+  for (int i = tid; i < D * DF; i += kBThreads)
+    om[(i / DF) * L + i % DF] = omega[i];
+  const int64_t nsteps = (rows + PR - 1) / PR;
   for (int64_t st = blockIdx.x; st < nsteps; st += gridDim.x) {
-    const int64_t row0 = st * kPfRows;
+    const int64_t row0 = st * PR;
     __syncthreads();  // om ready; the previous step's u, su are read
-    // u = gx' * phi(x), transposed; pieces of VEC consecutive features
-    for (int p = tid; p < kPfRows * DF / VEC; p += kBThreads) {
-      const int rr = p / (DF / VEC), f0 = (p % (DF / VEC)) * VEC;
+    // fill: TPR consecutive threads take one row, VEC features each; all
+    // of a thread's loads are issued before any is used
+    constexpr int FI = PR * TPR / kBThreads;
+    static_assert(PR * TPR % kBThreads == 0, "whole fill rounds");
+    f32x4 gl[FI][VEC / 4];
+    u32x4 xl[FI];
+#pragma unroll
+    for (int it = 0; it < FI; ++it) {
+      const int p = tid + kBThreads * it;
+      const int rr = p / TPR, f0 = (p % TPR) * VEC;
+      const int64_t off = (row0 + rr) * DF + f0;
+      const bool in = row0 + rr < rows;
+#pragma unroll
+      for (int e = 0; e < VEC / 4; ++e)
+        gl[it][e] = in ? *reinterpret_cast<const f32x4 *>(gf + off + 4 * e)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
+      xl[it] = in ? *reinterpret_cast<const u32x4 *>(xf + off)
+                  : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int it = 0; it < FI; ++it) {
+      const int p = tid + kBThreads * it;
+      const int rr = p / TPR, f0 = (p % TPR) * VEC;
       float a[VEC], b[VEC];
-      if (row0 + rr < rows) {
-        const int64_t off = (row0 + rr) * DF + f0;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) a[e] = gf[off + e];
-        piece_to_f32<T>(*reinterpret_cast<const u32x4 *>(xf + off), b);
-      } else {
+      for (int e = 0; e < VEC; ++e) a[e] = gl[it][e / 4][e % 4];
+      piece_to_f32<T>(xl[it], b);
+      float part = 0.f;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) a[e] = b[e] = 0.f;
+      for (int e = 0; e < VEC; e += 4) {
+        const f32x4 ue = {a[e] * b[e], a[e + 1] * b[e + 1],
+                          a[e + 2] * b[e + 2], a[e + 3] * b[e + 3]};
+        *reinterpret_cast<f32x4 *>(u + rr * L + f0 + e) = ue;
+        part += (ue[0] + ue[1]) + (ue[2] + ue[3]);
       }
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) u[(f0 + e) * LU + rr] = a[e] * b[e];
+      // the row's TPR threads are consecutive and aligned: sum them
+      part = sum_group<TPR>(part);
+      if (p % TPR == 0) su[rr] = with_sum ? part : 0.f;
     }
     __syncthreads();
-    if (tid < kPfRows) {  // sum_r u_r of each row, in a fixed order
-      float acc = 0.f;
-      if (with_sum)
-        for (int r = 0; r < DF; ++r) acc += u[r * LU + tid];
-      su[tid] = acc;
-    }
-    __syncthreads();
-    if (active) {
-      f32x4 acc[4] = {};
-      for (int r = 0; r < DF; ++r) {
-        const f32x4 uu = *reinterpret_cast<const f32x4 *>(u + r * LU + 4 * rb);
-        const f32x4 ww = *reinterpret_cast<const f32x4 *>(om + r * D + 4 * j);
+    f32x4 acc[TPW];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] += uu[i] * ww;
+    for (int m = 0; m < TPW; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+    for (int kb = 0; kb < DF / 32; ++kb) {
+#pragma unroll
+      for (int m = 0; m < TPW; ++m) {
+        const int t = w + kBWaves * m;
+        if (t < NT) {
+          const int mt = t / (D / 16), nt = t % (D / 16);
+          Frag<float> fa, fb;
+          load_frag8(fa, u + (16 * mt + li) * L + 32 * kb + 8 * g);
+          load_frag8(fb, om + (16 * nt + li) * L + 32 * kb + 8 * g);
+          acc[m] = mma(fa, fb, acc[m]);
+        }
       }
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t row = row0 + 4 * rb + i;
-        if (row < rows) {
-          const T *xr = x + row * D + 4 * j;
-          const float s = su[4 * rb + i];
-          store4(dx + row * D + 4 * j, acc[i][0] - to_f32(xr[0]) * s,
-                 acc[i][1] - to_f32(xr[1]) * s, acc[i][2] - to_f32(xr[2]) * s,
-                 acc[i][3] - to_f32(xr[3]) * s);
+    for (int m = 0; m < TPW; ++m) {
+      const int t = w + kBWaves * m;
+      if (t < NT) {
+        const int mt = t / (D / 16), nt = t % (D / 16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int rl = 16 * mt + 4 * g + r;
+          const int64_t row = row0 + rl;
+          if (row < rows) {
+            const int64_t o = row * D + 16 * nt + li;
+            dx[o] = from_f32<T>(acc[m][r] - to_f32(x[o]) * su[rl]);
+          }
         }
       }
     }
@@ -1399,9 +1420,8 @@ hipError_t launch_pf(const BwdArgs &a, int64_t units, hipStream_t s) {
       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (once != hipSuccess) return once;
   const int64_t rows = units * a.n;
-  constexpr int PR = pf_rows<D>();
   const unsigned grid = static_cast<unsigned>(
-      std::min<int64_t>((rows + PR - 1) / PR, int64_t{kCUs} * 4));
+      std::min<int64_t>((rows + kPfRows - 1) / kPfRows, int64_t{kCUs} * 4));
   hipLaunchKernelGGL((la_bwd_pf_grad_kernel<T, D, DF>), dim3(grid),
                      dim3(kBThreads), lds, s, static_cast<const T *>(a.qf),
                      static_cast<const float *>(a.dqf), static_cast<const T *>(a.q),
