@@ -65,6 +65,9 @@ def _load():
                                             i32, i32, i32, P, P, i32]
         lib.oracle_backward.argtypes = [P, P, P, P, P, P, P, i32, i32, i64,
                                         i32, i32, i32, i32, P, P]
+        lib.oracle_backward_gated.argtypes = [P, P, P, P, P, P, P, i32, i32,
+                                              i64, i32, i32, i32, i32, P, P,
+                                              i32]
         lib.oracle_num_threads.restype = i32
         _lib = lib
     return _lib
@@ -170,6 +173,30 @@ def forward_gated(q, k, v, mapk: int, omega, log_decay, mode: int,
                                  n, d, dqk, df, mapk, _ptr(om), _ptr(lam),
                                  mode, int(bool(causal)))
     return out
+
+
+def backward_gated(q, k, v, dout, mapk: int, omega, log_decay, mode: int):
+    """Gradients (dq, dk, dv) of sum(out * dout) for the causal gated
+    forward (forward_gated's log_decay and mode): the adjoint with each
+    position's and row's decay in place of one per head (see
+    linattn_oracle.c).  The decay is not differentiated."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, n, d = v.shape
+    dqk = q.shape[-1]
+    assert q.shape == k.shape == (B, H, n, dqk) and dout.shape == v.shape
+    om = _f64(omega) if mapk == MAP_PERFORMER else None
+    df = feat_dim(dqk, mapk, om)
+    lam = _f64(log_decay)
+    want = {LD_CHANNEL: (H, df), LD_POSITION: (B, H, n),
+            LD_BOTH: (B, H, n, df)}[mode]
+    assert lam.shape == want, (lam.shape, want)
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    _load().oracle_backward_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                                  _ptr(dq), _ptr(dk), _ptr(dv), B, H, n, d,
+                                  dqk, df, mapk, _ptr(om), _ptr(lam), mode)
+    return dq, dk, dv
 
 
 def decode_gated(mu, nu, q, k, v, mapk: int, omega, log_decay, mode: int):

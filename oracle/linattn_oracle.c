@@ -403,6 +403,89 @@ void oracle_backward(const double *q, const double *k, const double *v,
   }
 }
 
+/* Gradients of the causal forward with the gated recurrence (lam and mode
+ * as oracle_forward_gated): the adjoint above with the decay g_j[f] =
+ * exp(lam) and the input weight 1 - g_j[f] of each position and state row in
+ * place of a and 1 - a.  Going backward, the adjoint states take row f of
+ * position j's weight for dk, dv at j, then decay by g_j[f] on their way to
+ * j - 1 (d mu_j / d mu_{j-1} = g_j).  The decay itself is not
+ * differentiated. */
+void oracle_backward_gated(const double *q, const double *k, const double *v,
+                           const double *dout, double *dq, double *dk,
+                           double *dv, int B, int H, int64_t n, int d,
+                           int dqk, int dfeat, int map, const double *omega,
+                           const double *lam, int mode) {
+  const int64_t units = (int64_t)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t u = 0; u < units; ++u) {
+    const int h = (int)(u % H);
+    const double *qu = q + u * n * dqk, *ku = k + u * n * dqk;
+    const double *vu = v + u * n * d, *gu = dout + u * n * d;
+    double *dqu = dq + u * n * dqk, *dku = dk + u * n * dqk;
+    double *dvu = dv + u * n * d;
+    double *mu = (double *)calloc((size_t)dfeat * d, sizeof(double));
+    double *nu = (double *)calloc((size_t)dfeat, sizeof(double));
+    double *qf = (double *)malloc(sizeof(double) * dfeat);
+    double *kf = (double *)malloc(sizeof(double) * dfeat);
+    double *gf = (double *)malloc(sizeof(double) * dfeat);
+    double *dnum = (double *)malloc(sizeof(double) * (size_t)n * d);
+    double *dden = (double *)malloc(sizeof(double) * (size_t)n);
+    /* forward sweep: the states, each row's dnum, dden and dq */
+    for (int64_t j = 0; j < n; ++j) {
+      feature_row(ku + j * dqk, kf, dqk, dfeat, map, omega);
+      gated_update(mu, nu, kf, vu + j * d, d, dfeat, lam, mode, u, h, j, n);
+      feature_row(qu + j * dqk, qf, dqk, dfeat, map, omega);
+      double den = 0.0;
+      for (int f = 0; f < dfeat; ++f) den += qf[f] * nu[f];
+      double dn = 0.0;
+      for (int e = 0; e < d; ++e) {
+        double num = 0.0;
+        for (int f = 0; f < dfeat; ++f) num += mu[f * d + e] * qf[f];
+        dnum[j * d + e] = gu[j * d + e] / den;
+        dn += gu[j * d + e] * num;
+      }
+      dden[j] = -dn / (den * den);
+      for (int f = 0; f < dfeat; ++f) {
+        double acc = nu[f] * dden[j];
+        for (int e = 0; e < d; ++e) acc += mu[f * d + e] * dnum[j * d + e];
+        gf[f] = acc;
+      }
+      feature_row_grad(qu + j * dqk, gf, dqu + j * dqk, dqk, dfeat, map,
+                       omega);
+    }
+    /* backward sweep: adjoint states M (reusing mu) and Z (reusing nu) */
+    memset(mu, 0, sizeof(double) * (size_t)dfeat * d);
+    memset(nu, 0, sizeof(double) * (size_t)dfeat);
+    for (int64_t j = n - 1; j >= 0; --j) {
+      feature_row(qu + j * dqk, qf, dqk, dfeat, map, omega);
+      for (int f = 0; f < dfeat; ++f) {
+        for (int e = 0; e < d; ++e) mu[f * d + e] += qf[f] * dnum[j * d + e];
+        nu[f] += qf[f] * dden[j];
+      }
+      feature_row(ku + j * dqk, kf, dqk, dfeat, map, omega);
+      for (int e = 0; e < d; ++e) dvu[j * d + e] = 0.0;
+      for (int f = 0; f < dfeat; ++f) {
+        const double g = exp(lam_at(lam, mode, u, h, j, n, f, dfeat));
+        const double b = 1.0 - g;
+        double acc = nu[f];
+        for (int e = 0; e < d; ++e) {
+          acc += mu[f * d + e] * vu[j * d + e];
+          dvu[j * d + e] += b * mu[f * d + e] * kf[f];
+        }
+        gf[f] = b * acc;
+      }
+      feature_row_grad(ku + j * dqk, gf, dku + j * dqk, dqk, dfeat, map,
+                       omega);
+      for (int f = 0; f < dfeat; ++f) {
+        const double g = exp(lam_at(lam, mode, u, h, j, n, f, dfeat));
+        for (int e = 0; e < d; ++e) mu[f * d + e] *= g;
+        nu[f] *= g;
+      }
+    }
+    free(mu); free(nu); free(qf); free(kf); free(gf); free(dnum); free(dden);
+  }
+}
+
 /* Number of OpenMP threads a parallel region here would use (1 without
  * OpenMP); reported beside the oracle's timing. */
 #ifdef _OPENMP
