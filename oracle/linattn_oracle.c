@@ -328,6 +328,90 @@ static void feature_row_grad(const double *x, const double *gf, double *gx,
   }
 }
 
+/* The adjoint for one unit.  Decay: per head (has_decay, a; none: a = 1,
+ * input weight 1) or, with lam, the gated decay g = exp(lam) and input
+ * weight 1 - g of each position and state row (lam and mode as
+ * oracle_forward_gated).  Going backward, the adjoint states take row f of
+ * position j's input weight for dk, dv at j, then decay by row f of
+ * position j's decay on their way to j - 1 (d mu_j / d mu_{j-1} = g_j).
+ * The decay itself is not differentiated. */
+static void backward_unit(const double *qu, const double *ku, const double *vu,
+                          const double *gu, double *dqu, double *dku,
+                          double *dvu, int64_t n, int d, int dqk, int dfeat,
+                          int map, const double *omega, int has_decay,
+                          double a, const double *lam, int mode, int64_t u,
+                          int h) {
+  double *mu = (double *)calloc((size_t)dfeat * d, sizeof(double));
+  double *nu = (double *)calloc((size_t)dfeat, sizeof(double));
+  double *qf = (double *)malloc(sizeof(double) * dfeat);
+  double *kf = (double *)malloc(sizeof(double) * dfeat);
+  double *gf = (double *)malloc(sizeof(double) * dfeat);
+  double *gw = (double *)malloc(sizeof(double) * dfeat);  /* decay of row f */
+  double *bw = (double *)malloc(sizeof(double) * dfeat);  /* input weight */
+  /* per position: dnum (d) and dden (1), kept for the backward sweep */
+  double *dnum = (double *)malloc(sizeof(double) * (size_t)n * d);
+  double *dden = (double *)malloc(sizeof(double) * (size_t)n);
+  /* forward sweep */
+  for (int64_t j = 0; j < n; ++j) {
+    feature_row(ku + j * dqk, kf, dqk, dfeat, map, omega);
+    if (lam)
+      gated_update(mu, nu, kf, vu + j * d, d, dfeat, lam, mode, u, h, j, n);
+    else
+      state_update(mu, nu, kf, vu + j * d, d, dfeat, has_decay, a);
+    feature_row(qu + j * dqk, qf, dqk, dfeat, map, omega);
+    double den = 0.0;
+    for (int f = 0; f < dfeat; ++f) den += qf[f] * nu[f];
+    double dn = 0.0;   /* dout_j . num_j */
+    for (int e = 0; e < d; ++e) {
+      double num = 0.0;
+      for (int f = 0; f < dfeat; ++f) num += mu[f * d + e] * qf[f];
+      dnum[j * d + e] = gu[j * d + e] / den;
+      dn += gu[j * d + e] * num;
+    }
+    dden[j] = -dn / (den * den);
+    for (int f = 0; f < dfeat; ++f) {
+      double acc = nu[f] * dden[j];
+      for (int e = 0; e < d; ++e) acc += mu[f * d + e] * dnum[j * d + e];
+      gf[f] = acc;
+    }
+    feature_row_grad(qu + j * dqk, gf, dqu + j * dqk, dqk, dfeat, map, omega);
+  }
+  /* backward sweep: adjoint states M (reusing mu) and Z (reusing nu) */
+  memset(mu, 0, sizeof(double) * (size_t)dfeat * d);
+  memset(nu, 0, sizeof(double) * (size_t)dfeat);
+  for (int64_t j = n - 1; j >= 0; --j) {
+    for (int f = 0; f < dfeat; ++f) {
+      gw[f] = lam ? exp(lam_at(lam, mode, u, h, j, n, f, dfeat))
+                  : has_decay ? a : 1.0;
+      bw[f] = lam || has_decay ? 1.0 - gw[f] : 1.0;
+    }
+    feature_row(qu + j * dqk, qf, dqk, dfeat, map, omega);
+    for (int f = 0; f < dfeat; ++f) {
+      for (int e = 0; e < d; ++e) mu[f * d + e] += qf[f] * dnum[j * d + e];
+      nu[f] += qf[f] * dden[j];
+    }
+    feature_row(ku + j * dqk, kf, dqk, dfeat, map, omega);
+    for (int f = 0; f < dfeat; ++f) {
+      const double b = bw[f];
+      double acc = nu[f];
+      for (int e = 0; e < d; ++e) acc += mu[f * d + e] * vu[j * d + e];
+      gf[f] = b * acc;
+    }
+    feature_row_grad(ku + j * dqk, gf, dku + j * dqk, dqk, dfeat, map, omega);
+    for (int e = 0; e < d; ++e) {
+      double acc = 0.0;
+      for (int f = 0; f < dfeat; ++f) acc += mu[f * d + e] * kf[f] * bw[f];
+      dvu[j * d + e] = acc;
+    }
+    for (int f = 0; f < dfeat; ++f) {
+      for (int e = 0; e < d; ++e) mu[f * d + e] *= gw[f];
+      nu[f] *= gw[f];
+    }
+  }
+  free(mu); free(nu); free(qf); free(kf); free(gf); free(gw); free(bw);
+  free(dnum); free(dden);
+}
+
 void oracle_backward(const double *q, const double *k, const double *v,
                      const double *dout, double *dq, double *dk, double *dv,
                      int B, int H, int64_t n, int d, int dqk, int dfeat,
@@ -336,80 +420,16 @@ void oracle_backward(const double *q, const double *k, const double *v,
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t u = 0; u < units; ++u) {
     const int h = (int)(u % H);
-    const double a = decay ? decay[h] : 1.0, b = decay ? 1.0 - a : 1.0;
-    const double *qu = q + u * n * dqk, *ku = k + u * n * dqk;
-    const double *vu = v + u * n * d, *gu = dout + u * n * d;
-    double *dqu = dq + u * n * dqk, *dku = dk + u * n * dqk;
-    double *dvu = dv + u * n * d;
-    double *mu = (double *)calloc((size_t)dfeat * d, sizeof(double));
-    double *nu = (double *)calloc((size_t)dfeat, sizeof(double));
-    double *qf = (double *)malloc(sizeof(double) * dfeat);
-    double *kf = (double *)malloc(sizeof(double) * dfeat);
-    double *gf = (double *)malloc(sizeof(double) * dfeat);
-    /* per position: dnum (d) and dden (1), kept for the backward sweep */
-    double *dnum = (double *)malloc(sizeof(double) * (size_t)n * d);
-    double *dden = (double *)malloc(sizeof(double) * (size_t)n);
-    /* forward sweep */
-    for (int64_t j = 0; j < n; ++j) {
-      feature_row(ku + j * dqk, kf, dqk, dfeat, map, omega);
-      state_update(mu, nu, kf, vu + j * d, d, dfeat, decay != NULL, a);
-      feature_row(qu + j * dqk, qf, dqk, dfeat, map, omega);
-      double den = 0.0;
-      for (int f = 0; f < dfeat; ++f) den += qf[f] * nu[f];
-      double dn = 0.0;   /* dout_j . num_j */
-      for (int e = 0; e < d; ++e) {
-        double num = 0.0;
-        for (int f = 0; f < dfeat; ++f) num += mu[f * d + e] * qf[f];
-        dnum[j * d + e] = gu[j * d + e] / den;
-        dn += gu[j * d + e] * num;
-      }
-      dden[j] = -dn / (den * den);
-      for (int f = 0; f < dfeat; ++f) {
-        double acc = nu[f] * dden[j];
-        for (int e = 0; e < d; ++e) acc += mu[f * d + e] * dnum[j * d + e];
-        gf[f] = acc;
-      }
-      feature_row_grad(qu + j * dqk, gf, dqu + j * dqk, dqk, dfeat, map,
-                       omega);
-    }
-    /* backward sweep: adjoint states M (reusing mu) and Z (reusing nu) */
-    memset(mu, 0, sizeof(double) * (size_t)dfeat * d);
-    memset(nu, 0, sizeof(double) * (size_t)dfeat);
-    for (int64_t j = n - 1; j >= 0; --j) {
-      feature_row(qu + j * dqk, qf, dqk, dfeat, map, omega);
-      for (int f = 0; f < dfeat; ++f) {
-        for (int e = 0; e < d; ++e) mu[f * d + e] += qf[f] * dnum[j * d + e];
-        nu[f] += qf[f] * dden[j];
-      }
-      feature_row(ku + j * dqk, kf, dqk, dfeat, map, omega);
-      for (int f = 0; f < dfeat; ++f) {
-        double acc = nu[f];
-        for (int e = 0; e < d; ++e) acc += mu[f * d + e] * vu[j * d + e];
-        gf[f] = b * acc;
-      }
-      feature_row_grad(ku + j * dqk, gf, dku + j * dqk, dqk, dfeat, map,
-                       omega);
-      for (int e = 0; e < d; ++e) {
-        double acc = 0.0;
-        for (int f = 0; f < dfeat; ++f) acc += mu[f * d + e] * kf[f];
-        dvu[j * d + e] = b * acc;
-      }
-      for (int f = 0; f < dfeat; ++f) {
-        for (int e = 0; e < d; ++e) mu[f * d + e] *= a;
-        nu[f] *= a;
-      }
-    }
-    free(mu); free(nu); free(qf); free(kf); free(gf); free(dnum); free(dden);
+    backward_unit(q + u * n * dqk, k + u * n * dqk, v + u * n * d,
+                  dout + u * n * d, dq + u * n * dqk, dk + u * n * dqk,
+                  dv + u * n * d, n, d, dqk, dfeat, map, omega, decay != NULL,
+                  decay ? decay[h] : 1.0, NULL, 0, u, h);
   }
 }
 
 /* Gradients of the causal forward with the gated recurrence (lam and mode
- * as oracle_forward_gated): the adjoint above with the decay g_j[f] =
- * exp(lam) and the input weight 1 - g_j[f] of each position and state row in
- * place of a and 1 - a.  Going backward, the adjoint states take row f of
- * position j's weight for dk, dv at j, then decay by g_j[f] on their way to
- * j - 1 (d mu_j / d mu_{j-1} = g_j).  The decay itself is not
- * differentiated. */
+ * as oracle_forward_gated): the adjoint above with each position's and
+ * state row's decay in place of one per head. */
 void oracle_backward_gated(const double *q, const double *k, const double *v,
                            const double *dout, double *dq, double *dk,
                            double *dv, int B, int H, int64_t n, int d,
@@ -419,70 +439,10 @@ void oracle_backward_gated(const double *q, const double *k, const double *v,
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t u = 0; u < units; ++u) {
     const int h = (int)(u % H);
-    const double *qu = q + u * n * dqk, *ku = k + u * n * dqk;
-    const double *vu = v + u * n * d, *gu = dout + u * n * d;
-    double *dqu = dq + u * n * dqk, *dku = dk + u * n * dqk;
-    double *dvu = dv + u * n * d;
-    double *mu = (double *)calloc((size_t)dfeat * d, sizeof(double));
-    double *nu = (double *)calloc((size_t)dfeat, sizeof(double));
-    double *qf = (double *)malloc(sizeof(double) * dfeat);
-    double *kf = (double *)malloc(sizeof(double) * dfeat);
-    double *gf = (double *)malloc(sizeof(double) * dfeat);
-    double *dnum = (double *)malloc(sizeof(double) * (size_t)n * d);
-    double *dden = (double *)malloc(sizeof(double) * (size_t)n);
-    /* forward sweep: the states, each row's dnum, dden and dq */
-    for (int64_t j = 0; j < n; ++j) {
-      feature_row(ku + j * dqk, kf, dqk, dfeat, map, omega);
-      gated_update(mu, nu, kf, vu + j * d, d, dfeat, lam, mode, u, h, j, n);
-      feature_row(qu + j * dqk, qf, dqk, dfeat, map, omega);
-      double den = 0.0;
-      for (int f = 0; f < dfeat; ++f) den += qf[f] * nu[f];
-      double dn = 0.0;
-      for (int e = 0; e < d; ++e) {
-        double num = 0.0;
-        for (int f = 0; f < dfeat; ++f) num += mu[f * d + e] * qf[f];
-        dnum[j * d + e] = gu[j * d + e] / den;
-        dn += gu[j * d + e] * num;
-      }
-      dden[j] = -dn / (den * den);
-      for (int f = 0; f < dfeat; ++f) {
-        double acc = nu[f] * dden[j];
-        for (int e = 0; e < d; ++e) acc += mu[f * d + e] * dnum[j * d + e];
-        gf[f] = acc;
-      }
-      feature_row_grad(qu + j * dqk, gf, dqu + j * dqk, dqk, dfeat, map,
-                       omega);
-    }
-    /* backward sweep: adjoint states M (reusing mu) and Z (reusing nu) */
-    memset(mu, 0, sizeof(double) * (size_t)dfeat * d);
-    memset(nu, 0, sizeof(double) * (size_t)dfeat);
-    for (int64_t j = n - 1; j >= 0; --j) {
-      feature_row(qu + j * dqk, qf, dqk, dfeat, map, omega);
-      for (int f = 0; f < dfeat; ++f) {
-        for (int e = 0; e < d; ++e) mu[f * d + e] += qf[f] * dnum[j * d + e];
-        nu[f] += qf[f] * dden[j];
-      }
-      feature_row(ku + j * dqk, kf, dqk, dfeat, map, omega);
-      for (int e = 0; e < d; ++e) dvu[j * d + e] = 0.0;
-      for (int f = 0; f < dfeat; ++f) {
-        const double g = exp(lam_at(lam, mode, u, h, j, n, f, dfeat));
-        const double b = 1.0 - g;
-        double acc = nu[f];
-        for (int e = 0; e < d; ++e) {
-          acc += mu[f * d + e] * vu[j * d + e];
-          dvu[j * d + e] += b * mu[f * d + e] * kf[f];
-        }
-        gf[f] = b * acc;
-      }
-      feature_row_grad(ku + j * dqk, gf, dku + j * dqk, dqk, dfeat, map,
-                       omega);
-      for (int f = 0; f < dfeat; ++f) {
-        const double g = exp(lam_at(lam, mode, u, h, j, n, f, dfeat));
-        for (int e = 0; e < d; ++e) mu[f * d + e] *= g;
-        nu[f] *= g;
-      }
-    }
-    free(mu); free(nu); free(qf); free(kf); free(gf); free(dnum); free(dden);
+    backward_unit(q + u * n * dqk, k + u * n * dqk, v + u * n * d,
+                  dout + u * n * d, dq + u * n * dqk, dk + u * n * dqk,
+                  dv + u * n * d, n, d, dqk, dfeat, map, omega, 0, 1.0, lam,
+                  mode, u, h);
   }
 }
 

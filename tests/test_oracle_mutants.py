@@ -86,11 +86,11 @@ MUTANTS = {
     "bwd_dk_missing_input_weight": ("gf[f] = b * acc;", "gf[f] = acc;"),
     "bwd_elu_chain_rule_dropped": (
         "gx[c] = x[c] > 0.0 ? gf[c] : gf[c] * exp(x[c]);", "gx[c] = gf[c];"),
-    "bwd_adjoint_not_decayed": ("for (int e = 0; e < d; ++e) mu[f * d + e] *= a;",
+    "bwd_adjoint_not_decayed": ("for (int e = 0; e < d; ++e) mu[f * d + e] *= gw[f];",
                                 ";"),
     "bwd_dv_state_transposed": (
-        "for (int f = 0; f < dfeat; ++f) acc += mu[f * d + e] * kf[f];",
-        "for (int f = 0; f < dfeat; ++f) acc += mu[e * dfeat + f] * kf[f];"),
+        "for (int f = 0; f < dfeat; ++f) acc += mu[f * d + e] * kf[f] * bw[f];",
+        "for (int f = 0; f < dfeat; ++f) acc += mu[e * dfeat + f] * kf[f] * bw[f];"),
     "bwd_performer_norm_term_dropped": ("gx[c] = acc - x[c] * s;",
                                         "gx[c] = acc;"),
 }
