@@ -82,7 +82,7 @@ def workloads():
             "decode": I.DECODE, "noncausal": I.ELU1_NONCAUSAL,
             "gated": I.GATED, "backward": I.DECAYED, "channel": I.CHANNEL,
             "decode_channel": I.DECODE_CHANNEL,
-            "backward_performer": I.PERFORMER}
+            "backward_performer": I.PERFORMER, "backward_gated": I.GATED}
 
 
 def esize(dtype) -> int:
@@ -391,20 +391,22 @@ def backward_leg(torch, K, I, cfg, args, dev):
     that produces out and den runs once, before the timed region)."""
     mapname = I.MAP_NAMES[cfg.mapk]
     byts, flops = backward_algorithmic(cfg)
+    byts += 4 * cfg.tokens if cfg.gate is not None else 0  # lam, fp32
     x = I.make_prefill(cfg, args.seed)
     s = {k: (None if t is None else t.to(dev)) for k, t in x.items()}
     g = torch.Generator("cpu").manual_seed(args.seed + 7)
     dout = torch.randn(cfg.B, cfg.H, cfg.n, cfg.d, generator=g).to(
         cfg.dtype).to(dev)
     out, den = K.forward_train(s["q"], s["k"], s["v"], mapname,
-                               decay=s["decay"], omega=s["omega"])
+                               decay=s["decay"], omega=s["omega"],
+                               log_decay=s["log_decay"])
     grads = [torch.empty_like(s["q"]) for _ in range(3)]
     stream = torch.cuda.current_stream(dev)
 
     def step(i):
         K.backward(s["q"], s["k"], s["v"], out, den, dout, mapname,
                    decay=s["decay"], dq=grads[0], dk=grads[1], dv=grads[2],
-                   omega=s["omega"])
+                   omega=s["omega"], log_decay=s["log_decay"])
 
     settled = settle(torch, step, args.settle_ms)
     for i in range(args.warmup):
@@ -418,6 +420,9 @@ def backward_leg(torch, K, I, cfg, args, dev):
                                 "la_bwd_prep_kernel + la_bwd_kernel + "
                                 "la_bwd_pf_grad_kernel x2 per step")
                                if cfg.mapk == I.MAP_PERFORMER else
+                               "la_bwd_prep_kernel + la_bwd_kernel "
+                               "(column-block roles) per step"
+                               if cfg.gate is not None else
                                "la_bwd_prep_kernel + la_bwd_seg_kernel "
                                "(aggregates, then readout) per step",
                      "ms": ms, "bytes": byts, "flops": flops},
@@ -425,7 +430,8 @@ def backward_leg(torch, K, I, cfg, args, dev):
             "config": {"workload": "backward_" + cfg.name, "B": cfg.B,
                        "H": cfg.H, "n": cfg.n, "d": cfg.d,
                        "d_feat": cfg.d_feat, "map": mapname,
-                       "decay": cfg.decay, "causal": True, "seed": args.seed}}
+                       "decay": cfg.decay, "gate": cfg.gate, "causal": True,
+                       "seed": args.seed}}
 
 
 def cpu_baseline_backward(cfg, seed: int, budget_s: float = 15.0):
@@ -439,10 +445,17 @@ def cpu_baseline_backward(cfg, seed: int, budget_s: float = 15.0):
     flat = lambda t: t.reshape(1, units, cfg.n, t.shape[-1])
     q, k, v, do = flat(x["q"]), flat(x["k"]), flat(x["v"]), flat(dout)
     dec = None if x["decay"] is None else x["decay"].repeat(cfg.B)
+    lam = (None if x["log_decay"] is None
+           else x["log_decay"].reshape(1, units, cfg.n))
     threads = oracle.num_threads()
 
     def run(take):
         sl = slice(0, take)
+        if lam is not None:
+            return oracle.backward_gated(
+                f64(q[:, sl]), f64(k[:, sl]), f64(v[:, sl]), f64(do[:, sl]),
+                cfg.mapk, f64(x["omega"]), f64(lam[:, sl]),
+                oracle.LD_POSITION)
         return oracle.backward(f64(q[:, sl]), f64(k[:, sl]), f64(v[:, sl]),
                                f64(do[:, sl]), cfg.mapk, f64(x["omega"]),
                                None if dec is None else f64(dec[sl]))

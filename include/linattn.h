@@ -292,6 +292,60 @@ la_status la_forward_gated(const void *q, const void *k, const void *v,
                            float *mu_out, float *nu_out, void *stream);
 
 /*
+ * la_forward_gated_train -- the causal la_forward_gated with one decay per
+ * position that also writes each row's denominator, for la_backward_gated
+ * (as la_forward_train does for la_backward).
+ *   All arguments as la_forward_gated (causal, no handed-out state), plus
+ *   den   : device fp32 [B][H][n], written; LA_ERR_INVALID_ARG if NULL.
+ *   layout: LA_LD_POSITION only; the other layouts return
+ *           LA_ERR_UNSUPPORTED.
+ *   workspace: la_forward_gated_workspace_bytes(...) with LA_LD_POSITION
+ *           and causal = 1, synchronisation area zero as for la_forward.
+ */
+la_status la_forward_gated_train(const void *q, const void *k, const void *v,
+                                 void *out, float *den, int B, int H,
+                                 int64_t n, int d, int d_feat, la_map map,
+                                 const float *omega, const float *log_decay,
+                                 la_decay_layout layout, la_dtype dtype,
+                                 void *workspace, void *stream);
+
+/*
+ * la_backward_gated -- la_backward for the causal forward with one decay
+ * per position (la_forward_gated, LA_LD_POSITION: the input-dependent decay
+ * of Mamba's selective step, "Linear attention research 2026" page; the
+ * recurrence of la_forward_gated).  The weights of la_backward become
+ *   w_ij = (1 - gamma_j) prod_{p=j+1..i} gamma_p   (j <= i),
+ * and the decay itself is an input that is not differentiated.
+ *   All arguments as la_backward, with out and den from
+ *   la_forward_gated_train, and
+ *   log_decay: device fp32 lam = log(gamma), [B][H][n], as the forward's;
+ *              LA_ERR_INVALID_ARG if NULL for non-empty sizes.  Values
+ *              below -104 act as -104 (gamma = 0 in fp32 either way).
+ *   layout   : LA_LD_POSITION; the other layouts return LA_ERR_UNSUPPORTED.
+ *   workspace: device, at least la_backward_gated_workspace_bytes(...).
+ *   Supported: ELU1, IDENTITY with d == d_feat in {16, 32, 64, 128};
+ *              PERFORMER returns LA_ERR_UNSUPPORTED.
+ */
+la_status la_backward_gated(const void *q, const void *k, const void *v,
+                            const void *out, const float *den,
+                            const void *dout, void *dq, void *dk, void *dv,
+                            int B, int H, int64_t n, int d, int d_feat,
+                            la_map map, const float *omega,
+                            const float *log_decay, la_decay_layout layout,
+                            la_dtype dtype, void *workspace, void *stream);
+
+/*
+ * la_backward_gated_workspace_bytes -- device workspace la_backward_gated
+ * needs: per row the prepared G row (d + 2 values padded to a multiple of
+ * 32) and, for LA_MAP_ELU1, the features phi(k) and phi(q), all in dtype.
+ * Pure host function; 0 for arguments la_backward_gated would reject and
+ * for empty sizes.
+ */
+size_t la_backward_gated_workspace_bytes(int B, int H, int64_t n, int d,
+                                         int d_feat, la_map map,
+                                         la_dtype dtype);
+
+/*
  * la_decode_step_gated -- la_decode_step with a decay per state row and/or
  * per unit: row f of unit u decays by gamma = exp(lam) with input weight
  * 1 - gamma (the diagonal A of "2.3 State-Space Models" eqs 21-25, and

@@ -31,7 +31,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
 SYMBOLS = ("la_featmap", "la_forward_workspace_bytes", "la_forward",
            "la_forward_state", "la_forward_train", "la_backward",
            "la_backward_workspace_bytes",
-           "la_forward_gated", "la_forward_gated_workspace_bytes",
+           "la_forward_gated", "la_forward_gated_train", "la_backward_gated",
+           "la_backward_gated_workspace_bytes",
+           "la_forward_gated_workspace_bytes",
            "la_forward_noalloc",
            "la_decode_step", "la_decode_step_gated", "la_workspace_check",
            "la_set_exchange_spin_limit", "la_status_str", "la_last_error")
@@ -90,6 +92,17 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                          i32, i32, vp, vp, i32, i32, i32, vp,
                                          vp, vp, vp]
         lib.la_forward_gated.restype = i32
+        lib.la_forward_gated_train.argtypes = [vp, vp, vp, vp, vp, i32, i32,
+                                               i64, i32, i32, i32, vp, vp,
+                                               i32, i32, vp, vp]
+        lib.la_forward_gated_train.restype = i32
+        lib.la_backward_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                          i32, i32, i64, i32, i32, i32, vp,
+                                          vp, i32, i32, vp, vp]
+        lib.la_backward_gated.restype = i32
+        lib.la_backward_gated_workspace_bytes.argtypes = [i32, i32, i64, i32,
+                                                          i32, i32, i32]
+        lib.la_backward_gated_workspace_bytes.restype = sz
         lib.la_forward_gated_workspace_bytes.argtypes = [
             i32, i32, i64, i32, i32, i32, i32, i32, i32]
         lib.la_forward_gated_workspace_bytes.restype = sz
@@ -564,10 +577,13 @@ def forward_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                   out: Optional[torch.Tensor] = None,
                   den: Optional[torch.Tensor] = None,
                   workspace: Optional[torch.Tensor] = None,
-                  omega: Optional[torch.Tensor] = None):
+                  omega: Optional[torch.Tensor] = None,
+                  log_decay: Optional[torch.Tensor] = None):
     """The causal forward for training (la_forward_train): returns (out,
     den), den [B,H,n] fp32 being each row's denominator, which backward()
-    takes.  omega: fp32 [d, m] for the performer map."""
+    takes.  omega: fp32 [d, m] for the performer map.  log_decay: fp32
+    [B, H, n], a decay exp(log_decay) per position in place of decay
+    (la_forward_gated_train)."""
     lib = load_library()
     if q.dim() != 4 or v.dim() != 4 or q.shape != k.shape:
         raise ValueError("q, k must be [B,H,n,d_qk] and v [B,H,n,d]")
@@ -582,13 +598,15 @@ def forward_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         raise ValueError("q, k must have width d for elu1 and performer")
     d_feat = _check_omega(omega, mapk, d) or q.shape[-1]
     _check_decay(decay, H)
+    _check_position_decay(log_decay, decay, B, H, n)
     if out is not None:
         _check_out(out, v.shape, v.dtype)
     if den is not None and (den.dtype != torch.float32 or
                             tuple(den.shape) != (B, H, n)):
         raise ValueError("den must be float32 [B, H, n]")
     _on_gpu(v, (q, "q"), (k, "k"), (v, "v"), (out, "out"), (den, "den"),
-            (decay, "decay"), (workspace, "workspace"), (omega, "omega"))
+            (decay, "decay"), (workspace, "workspace"), (omega, "omega"),
+            (log_decay, "log_decay"))
     if out is None:
         out = torch.empty_like(v)
     if den is None:
@@ -598,6 +616,13 @@ def forward_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         workspace = _workspace(need, v.device)
     if need and workspace.numel() < need:
         raise ValueError("workspace too small")
+    if log_decay is not None:
+        st = lib.la_forward_gated_train(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(den), B, H, n, d,
+            d_feat, mapk, _ptr(omega), _ptr(log_decay), LD_POSITION, dt,
+            _ptr(workspace) if need else None, _stream(v.device))
+        _check(st, "la_forward_gated_train")
+        return out, den
     st = lib.la_forward_train(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(den),
                               B, H, n, d, d_feat, mapk, _ptr(omega),
                               _ptr(decay), dt,
@@ -607,15 +632,32 @@ def forward_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return out, den
 
 
+def _check_position_decay(log_decay, decay, B, H, n):
+    """A decay per position: fp32 [B, H, n], not together with decay."""
+    if log_decay is None:
+        return
+    if decay is not None:
+        raise ValueError("pass decay or log_decay, not both")
+    if log_decay.dtype != torch.float32:
+        raise TypeError("log_decay must be float32")
+    if tuple(log_decay.shape) != (B, H, n) or not log_decay.is_contiguous():
+        raise ValueError(f"log_decay must be contiguous [B, H, n] = "
+                         f"{(B, H, n)}, got {tuple(log_decay.shape)}")
+
+
 def backward_workspace_bytes(B: int, H: int, n: int, d: int,
                              feature_map="elu1",
                              dtype: torch.dtype = torch.bfloat16,
-                             d_feat: Optional[int] = None) -> int:
-    """Device workspace la_backward needs (la_backward_workspace_bytes);
-    d_feat defaults to d (the performer map's m otherwise)."""
-    return int(load_library().la_backward_workspace_bytes(
-        B, H, n, d, d if d_feat is None else d_feat, _map_code(feature_map),
-        _dtype_code(dtype)))
+                             d_feat: Optional[int] = None,
+                             gated: bool = False) -> int:
+    """Device workspace la_backward needs (la_backward_workspace_bytes), or
+    with gated la_backward_gated (la_backward_gated_workspace_bytes); d_feat
+    defaults to d (the performer map's m otherwise)."""
+    lib = load_library()
+    fn = (lib.la_backward_gated_workspace_bytes if gated
+          else lib.la_backward_workspace_bytes)
+    return int(fn(B, H, n, d, d if d_feat is None else d_feat,
+                  _map_code(feature_map), _dtype_code(dtype)))
 
 
 # backward()'s workspaces when none is passed: one per (device, stream),
@@ -630,10 +672,13 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
              dk: Optional[torch.Tensor] = None,
              dv: Optional[torch.Tensor] = None,
              workspace: Optional[torch.Tensor] = None,
-             omega: Optional[torch.Tensor] = None):
+             omega: Optional[torch.Tensor] = None,
+             log_decay: Optional[torch.Tensor] = None):
     """Gradients (dq, dk, dv) of sum(out * dout) for the causal forward
     (la_backward); out and den as forward_train() returned them.  omega:
-    fp32 [d, m] for the performer map (not differentiated).
+    fp32 [d, m] for the performer map (not differentiated).  log_decay: fp32
+    [B, H, n], the forward's decay per position (la_backward_gated; not
+    differentiated).
     workspace: optional uint8 device tensor of at least
     backward_workspace_bytes(...) bytes; by default one cached per (device,
     stream) is used."""
@@ -654,10 +699,14 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     mapk = _map_code(feature_map)
     d_feat = _check_omega(omega, mapk, d) or d
     _check_decay(decay, H)
+    _check_position_decay(log_decay, decay, B, H, n)
     for t, nm in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
         if t is not None:
             _check_out(t, v.shape, v.dtype)
-    need = int(lib.la_backward_workspace_bytes(B, H, n, d, d_feat, mapk, dt))
+    gated = log_decay is not None
+    need = int((lib.la_backward_gated_workspace_bytes if gated
+                else lib.la_backward_workspace_bytes)(B, H, n, d, d_feat,
+                                                      mapk, dt))
     if workspace is not None and (workspace.dtype != torch.uint8
                                   or not workspace.is_contiguous()
                                   or workspace.numel() < need):
@@ -665,7 +714,8 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                          f"at least {need} bytes")
     _on_gpu(v, (q, "q"), (k, "k"), (v, "v"), (out, "out"), (den, "den"),
             (dout, "dout"), (decay, "decay"), (dq, "dq"), (dk, "dk"),
-            (dv, "dv"), (workspace, "workspace"), (omega, "omega"))
+            (dv, "dv"), (workspace, "workspace"), (omega, "omega"),
+            (log_decay, "log_decay"))
     if workspace is None and need > 0:
         key = (v.device.index, torch.cuda.current_stream(v.device).cuda_stream)
         workspace = _bwd_workspaces.get(key)
@@ -675,6 +725,14 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    if gated:
+        st = lib.la_backward_gated(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(den), _ptr(dout),
+            _ptr(dq), _ptr(dk), _ptr(dv), B, H, n, d, d_feat, mapk,
+            _ptr(omega), _ptr(log_decay), LD_POSITION, dt, _ptr(workspace),
+            _stream(v.device))
+        _check(st, "la_backward_gated")
+        return dq, dk, dv
     st = lib.la_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(den),
                          _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, H, n, d,
                          d_feat, mapk, _ptr(omega), _ptr(decay), dt,
@@ -687,14 +745,15 @@ class _LinearAttention(torch.autograd.Function):
     """forward_train() forward, backward() gradients (no arithmetic here)."""
 
     @staticmethod
-    def forward(ctx, q, k, v, feature_map, decay, omega):
+    def forward(ctx, q, k, v, feature_map, decay, omega, log_decay):
         out, den = forward_train(q.contiguous(), k.contiguous(),
                                  v.contiguous(), feature_map, decay=decay,
-                                 omega=omega)
+                                 omega=omega, log_decay=log_decay)
         ctx.save_for_backward(q, k, v, out, den)
         ctx.feature_map = feature_map
         ctx.decay = decay
         ctx.omega = omega
+        ctx.log_decay = log_decay
         return out
 
     @staticmethod
@@ -702,16 +761,21 @@ class _LinearAttention(torch.autograd.Function):
         q, k, v, out, den = ctx.saved_tensors
         dq, dk, dv = backward(q.contiguous(), k.contiguous(), v.contiguous(),
                               out, den, dout.contiguous(), ctx.feature_map,
-                              decay=ctx.decay, omega=ctx.omega)
-        return dq, dk, dv, None, None, None
+                              decay=ctx.decay, omega=ctx.omega,
+                              log_decay=ctx.log_decay)
+        return dq, dk, dv, None, None, None, None
 
 
 def linear_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                      feature_map="elu1",
                      decay: Optional[torch.Tensor] = None,
-                     omega: Optional[torch.Tensor] = None) -> torch.Tensor:
+                     omega: Optional[torch.Tensor] = None,
+                     log_decay: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Causal kernelized linear attention as a differentiable torch op:
-    la_forward_train forward, la_backward gradients for q, k and v (decay
-    and omega are not differentiated).  elu1 or identity features with
-    d_feat == d, or the performer map with omega fp32 [d, m]."""
-    return _LinearAttention.apply(q, k, v, feature_map, decay, omega)
+    la_forward_train forward, la_backward gradients for q, k and v (decay,
+    log_decay and omega are not differentiated).  elu1 or identity features
+    with d_feat == d, or the performer map with omega fp32 [d, m];
+    log_decay fp32 [B, H, n] (a decay per position: la_forward_gated_train
+    and la_backward_gated, elu1 or identity) in place of decay."""
+    return _LinearAttention.apply(q, k, v, feature_map, decay, omega,
+                                  log_decay)

@@ -618,14 +618,16 @@ la_status la_forward_train(const void *q, const void *k, const void *v,
 
 namespace {
 // Workspace of la_backward: G~ rows, then (elu + 1, column-block kernel)
-// K' and Q', then the segment aggregates of the segmented roles.
+// K' and Q', then the segment aggregates of the segmented roles.  With a
+// decay per position (gated) only the column-block kernel runs.
 size_t backward_ws(int64_t units, int64_t n, int d, int map, int dtype,
-                   size_t *kf_off, size_t *agg_off = nullptr) {
+                   size_t *kf_off, size_t *agg_off = nullptr,
+                   bool gated = false) {
   const size_t es = elem_size(dtype);
   const size_t g = align256(static_cast<size_t>(units * n) *
                             la::backward_gwidth(d) * es);
   const size_t f = align256(static_cast<size_t>(units * n) * d * es);
-  const int nseg = la::backward_segments(units, n, d, dtype);
+  const int nseg = gated ? 0 : la::backward_segments(units, n, d, dtype);
   // the segmented roles map k, q themselves: no K', Q' rows
   const size_t feats = map == LA_MAP_ELU1 && nseg == 0 ? 2 * f : 0;
   const size_t agg =
@@ -724,12 +726,26 @@ static la_status backward_performer(const void *q, const void *k,
   return ok();
 }
 
-la_status la_backward(const void *q, const void *k, const void *v,
-                      const void *out, const float *den, const void *dout,
-                      void *dq, void *dk, void *dv, int B, int H, int64_t n,
-                      int d, int d_feat, la_map map, const float *omega,
-                      const float *decay, la_dtype dtype, void *workspace,
-                      void *stream) {
+size_t la_backward_gated_workspace_bytes(int B, int H, int64_t n, int d,
+                                         int d_feat, la_map map,
+                                         la_dtype dtype) {
+  if (B <= 0 || H <= 0 || n <= 0 || !valid_dtype(dtype) || !valid_map(map))
+    return 0;
+  if (map == LA_MAP_PERFORMER || !la::backward_supported(d, d_feat)) return 0;
+  const int64_t units = static_cast<int64_t>(B) * H;
+  if (units * n > (int64_t{1} << 46) || units > (int64_t{1} << 26)) return 0;
+  return backward_ws(units, n, d, map, dtype, nullptr, nullptr, true);
+}
+
+// la_backward (decay [H] or null, lam null) and la_backward_gated (lam, a
+// decay per position, [B][H][n]).
+static la_status backward_impl(const void *q, const void *k, const void *v,
+                               const void *out, const float *den,
+                               const void *dout, void *dq, void *dk, void *dv,
+                               int B, int H, int64_t n, int d, int d_feat,
+                               la_map map, const float *omega,
+                               const float *decay, const float *lam,
+                               la_dtype dtype, void *workspace, void *stream) {
   try {
     if (B < 0 || H < 0 || n < 0)
       return fail(LA_ERR_INVALID_ARG, "negative size");
@@ -754,24 +770,26 @@ la_status la_backward(const void *q, const void *k, const void *v,
       return fail(LA_ERR_UNSUPPORTED, "sizes too large");
     if (!q || !k || !v || !out || !den || !dout || !dq || !dk || !dv)
       return fail(LA_ERR_INVALID_ARG, "null pointer argument");
+    const bool gated = lam != nullptr;
     if (!workspace)
       return fail(LA_ERR_WORKSPACE, "la_backward: workspace of %zu bytes required",
-                  backward_ws(units, n, d, map, dtype, nullptr));
+                  backward_ws(units, n, d, map, dtype, nullptr, nullptr, gated));
     size_t kf_off = 0, agg_off = 0;
     const size_t fbytes = align256(static_cast<size_t>(units * n) * d *
                                    elem_size(dtype));
-    backward_ws(units, n, d, map, dtype, &kf_off, &agg_off);
+    backward_ws(units, n, d, map, dtype, &kf_off, &agg_off, gated);
     la::BwdArgs a;
     a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.den = den;
     a.dq = dq; a.dk = dk; a.dv = dv;
-    a.decay = decay;
+    a.decay = gated ? nullptr : decay;
+    a.lam = lam;
     a.H = H;
     a.n = n;
     a.dqk = d;
     a.elu1 = map == LA_MAP_ELU1;
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     a.gt = ws;
-    a.nseg = la::backward_segments(units, n, d, dtype);
+    a.nseg = gated ? 0 : la::backward_segments(units, n, d, dtype);
     // K', Q' rows only where the column-block kernel reads them
     const bool feats = a.elu1 && a.nseg == 0;
     a.kf = feats ? ws + kf_off : const_cast<void *>(k);
@@ -784,6 +802,60 @@ la_status la_backward(const void *q, const void *k, const void *v,
   } catch (...) {
     return fail(LA_ERR_HIP, "unexpected exception in la_backward");
   }
+}
+
+la_status la_backward(const void *q, const void *k, const void *v,
+                      const void *out, const float *den, const void *dout,
+                      void *dq, void *dk, void *dv, int B, int H, int64_t n,
+                      int d, int d_feat, la_map map, const float *omega,
+                      const float *decay, la_dtype dtype, void *workspace,
+                      void *stream) {
+  return backward_impl(q, k, v, out, den, dout, dq, dk, dv, B, H, n, d,
+                       d_feat, map, omega, decay, nullptr, dtype, workspace,
+                       stream);
+}
+
+la_status la_backward_gated(const void *q, const void *k, const void *v,
+                            const void *out, const float *den,
+                            const void *dout, void *dq, void *dk, void *dv,
+                            int B, int H, int64_t n, int d, int d_feat,
+                            la_map map, const float *omega,
+                            const float *log_decay, la_decay_layout layout,
+                            la_dtype dtype, void *workspace, void *stream) {
+  if (layout != LA_LD_CHANNEL && layout != LA_LD_POSITION &&
+      layout != LA_LD_BOTH)
+    return fail(LA_ERR_INVALID_ARG, "unknown decay layout %d", layout);
+  if (layout != LA_LD_POSITION)
+    return fail(LA_ERR_UNSUPPORTED,
+                "la_backward_gated: only LA_LD_POSITION is built");
+  if (map == LA_MAP_PERFORMER)
+    return fail(LA_ERR_UNSUPPORTED,
+                "la_backward_gated: the PERFORMER map is not built");
+  if (!log_decay && static_cast<int64_t>(B) * H > 0 && n > 0)
+    return fail(LA_ERR_INVALID_ARG, "null log_decay");
+  return backward_impl(q, k, v, out, den, dout, dq, dk, dv, B, H, n, d,
+                       d_feat, map, omega, nullptr, log_decay, dtype,
+                       workspace, stream);
+}
+
+la_status la_forward_gated_train(const void *q, const void *k, const void *v,
+                                 void *out, float *den, int B, int H,
+                                 int64_t n, int d, int d_feat, la_map map,
+                                 const float *omega, const float *log_decay,
+                                 la_decay_layout layout, la_dtype dtype,
+                                 void *workspace, void *stream) {
+  if (layout != LA_LD_CHANNEL && layout != LA_LD_POSITION &&
+      layout != LA_LD_BOTH)
+    return fail(LA_ERR_INVALID_ARG, "unknown decay layout %d", layout);
+  if (layout != LA_LD_POSITION)
+    return fail(LA_ERR_UNSUPPORTED,
+                "la_forward_gated_train: only LA_LD_POSITION is built");
+  const bool empty = static_cast<int64_t>(B) * H <= 0 || n <= 0;
+  if (!den && !empty) return fail(LA_ERR_INVALID_ARG, "null den");
+  if (!log_decay && !empty) return fail(LA_ERR_INVALID_ARG, "null log_decay");
+  return forward_impl(q, k, v, out, B, H, n, d, d_feat, map, omega, nullptr, 1,
+                      dtype, workspace, nullptr, nullptr, stream, 0, log_decay,
+                      den);
 }
 
 la_status la_forward_gated(const void *q, const void *k, const void *v,

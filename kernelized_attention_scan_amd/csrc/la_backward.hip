@@ -62,7 +62,7 @@ constexpr int bstride(int w) {
   return sizeof(T) == 2 ? (w % 32 == 16 ? w : w + 16) : w + 4;
 }
 
-template <typename T, int D, int DF, int ROLE, bool DECAY>
+template <typename T, int D, int DF, int ROLE, bool DECAY, bool SEL = false>
 struct BShape {
   // X and Y are G and V+ (d + 2 wide: the last value of G as a pair,
   // padded to a multiple of 32) for the dq and dk roles, and K', Q' (d'
@@ -74,8 +74,10 @@ struct BShape {
   static constexpr int NT = KX / 16;                 // 16 x 16 state tiles
   static constexpr int TPW = (NT + kBWaves - 1) / kBWaves;
   static constexpr int SX = kBC * LX, SZ = kBC * LZ, SST = 16 * LX;
+  // g^0 .. g^C, or with a decay per position the chunk's table (3 C + 4)
+  static constexpr int TAB = SEL ? 3 * kBC + 4 : kBC + 4;
   static constexpr size_t lds_bytes =
-      sizeof(T) * (SX * 2 + SZ + SST) + sizeof(float) * (kBC + 4);
+      sizeof(T) * (SX * 2 + SZ + SST) + sizeof(float) * TAB;
 };
 
 // 16-byte pieces of a [C][W] row-major slab (consecutive threads take
@@ -148,15 +150,58 @@ __device__ __forceinline__ float dphi(float x, bool elu) {  // d phi / d x
   return elu ? (x > 0.f ? 1.f : expf(x)) : 1.f;
 }
 
+// A decay per position (lam = log gamma, Mamba's input-dependent step):
+// the chunk's table, computed by the 64 lanes of one wave, lane p holding
+// lam of the position at processing index p (0 past the valid rows, which
+// then keep the state: gamma = 1, 1 - gamma = 0).  With L the sums of
+// log2 gamma over processing indices:
+//   forward (dq): L_p inclusive (positions start .. p), so the entering
+//     state reads out with 2^(L_t), key s scores b_s 2^(L_t - L_s) and
+//     enters the state with b_s 2^(L_last - L_s);
+//   reverse (dk, dv): L_p exclusive (the positions after p's, up to the
+//     chunk's end), so the entering state reads out with b_t 2^(L_t), key
+//     s scores b_t 2^(L_t - L_s) and enters with 2^(L_all - L_s): in the
+//     adjoint the weight 1 - gamma belongs to the earlier position, which
+//     is the query there.
+// tab[p] = L_p, tab[C + p] = 1 - gamma_p, tab[2 C + p] = the state-update
+// weight of key p (0 past the valid rows), tab[3 C] = 2^(sum of the chunk).
+template <bool REV>
+__device__ __forceinline__ void gate_table(float lam, float *tab, int lane,
+                                           int rows) {
+  constexpr int C = kBC;
+  static_assert(C == kWave, "one row per lane");
+  constexpr float kLog2e = 1.4426950408889634f;
+  // below -104 exp(lam) is 0 in fp32; the floor keeps the sums finite for
+  // lam = -inf (a full reset)
+  lam = fmaxf(lam, -104.f);
+  const float l = lam * kLog2e;
+  float L = l;
+#pragma unroll
+  for (int o = 1; o < C; o <<= 1) {
+    const float y = __shfl_up(L, o);
+    if (lane >= o) L += y;
+  }
+  const float all = __shfl(L, C - 1);
+  if (REV) L -= l;
+  const float beta = -expm1f(lam);  // 1 - gamma, accurate near gamma = 1
+  tab[lane] = L;
+  tab[C + lane] = beta;
+  tab[2 * C + lane] =
+      lane < rows ? (REV ? 1.f : beta) * __builtin_amdgcn_exp2f(all - L) : 0.f;
+  if (lane == 0) tab[3 * C] = __builtin_amdgcn_exp2f(all);
+}
+
 // One role's workgroup: output columns 16 blk .. 16 blk + 15 of unit.  The
 // dq and dk roles write feature gradients, d' wide (times phi' for elu + 1,
 // where d' = d); with FG (the Performer map) they go to the workspace in
-// fp32 (dqf, dkf) and a conversion pass takes them through the map.
+// fp32 (dqf, dkf) and a conversion pass takes them through the map.  SEL:
+// a decay per position (a.lam) instead of one per head (DECAY is set too).
 template <typename T, int D, int DF, int ROLE, bool DECAY, bool ELU,
-          bool FG = false>
+          bool FG = false, bool SEL = false>
 __device__ __forceinline__ void bwd_role(const BwdArgs &a, int64_t unit,
                                          int blk, unsigned char *smem) {
-  using F = BShape<T, D, DF, ROLE, DECAY>;
+  static_assert(!SEL || DECAY, "a decay per position is a decay");
+  using F = BShape<T, D, DF, ROLE, DECAY, SEL>;
   constexpr int C = kBC, KX = F::KX, LX = F::LX, LZ = F::LZ;
   constexpr bool GV = F::GV, REV = ROLE != kRoleDQ;
   constexpr int VEC = 16 / sizeof(T);
@@ -165,15 +210,19 @@ __device__ __forceinline__ void bwd_role(const BwdArgs &a, int64_t unit,
   T *sZ = sY + F::SX;                            // values Z (16 columns)
   T *sST = sZ + F::SZ;                           // S^T copy
   float *gp = reinterpret_cast<float *>(sST + F::SST);  // g^0 .. g^C
+  float *tab = gp;  // SEL: the chunk's table (gate_table) instead
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, li = lane & 15;
   const int col0 = 16 * blk;
   const int h = static_cast<int>(unit % a.H);
-  const float gdec = DECAY ? a.decay[h] : 1.f, bdec = DECAY ? 1.f - gdec : 1.f;
+  constexpr bool HD = DECAY && !SEL;  // one decay per head
+  const float gdec = HD ? a.decay[h] : 1.f, bdec = HD ? 1.f - gdec : 1.f;
   const float lg = log2f(gdec);
-  for (int i = tid; i <= C; i += kBThreads) gp[i] = pow_int(gdec, lg, i);
+  if constexpr (!SEL)
+    for (int i = tid; i <= C; i += kBThreads) gp[i] = pow_int(gdec, lg, i);
+  const float *lb = SEL ? a.lam + unit * a.n : nullptr;
 
   const int64_t n = a.n;
   const T *qb = static_cast<const T *>(a.q) + unit * n * D;
@@ -220,9 +269,22 @@ __device__ __forceinline__ void bwd_role(const BwdArgs &a, int64_t unit,
   BSlab<T, DF, DF> r1f, r2f;   // dv: K' (r1f), Q' (r2f)
   BSlab<T, 16, DF> rz;         // GV: K' or Q' block
   BSlab<T, 16, KG> rzg;        // dv: G~ block
+  // SEL: lam of processing index `lane` of the chunk (wave 0; 0 past the
+  // valid rows, which are out of the buffer resource)
+  float laml = 0.f;
   auto load = [&](int c) {
     const int64_t r0 = row0_of(c);
     const int rows = rows_of(c);
+    if constexpr (SEL) {
+      if (w == 0) {
+        const __amdgpu_buffer_rsrc_t r =
+            make_rsrc(lb + r0, static_cast<unsigned>(rows) * sizeof(float));
+        const int rr = REV && lane < rows ? rows - 1 - lane : lane;
+        laml = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(
+                       r, static_cast<unsigned>(rr) * 4u, 0, 0));
+      }
+    }
     if constexpr (GV) {
       rg.load(gtb, r0, rows, 0, tid);
       r1.load(vb, r0, rows, 0, tid);
@@ -251,6 +313,8 @@ __device__ __forceinline__ void bwd_role(const BwdArgs &a, int64_t unit,
   auto stage = [&](int c) {
     const int rows = rows_of(c);
     auto trow = [&](int r) { return REV && r < rows ? rows - 1 - r : r; };
+    if constexpr (SEL)
+      if (w == 0) gate_table<REV>(laml, tab, lane, rows);
     if constexpr (GV) {
       // G~ as it is; V+ = [v | 1 | 1] (0 past the end)
       T *sG = ROLE == kRoleDQ ? sX : sY;
@@ -327,7 +391,10 @@ __device__ __forceinline__ void bwd_role(const BwdArgs &a, int64_t unit,
 
   for (int c = 0; c < nch; ++c) {
     const int rows = rows_of(c);
-    const float gt = gp[t + 1];
+    // the entering state's readout weight of query t
+    const float gt = !SEL ? gp[t + 1]
+                     : REV ? tab[C + t] * __builtin_amdgcn_exp2f(tab[t])
+                           : __builtin_amdgcn_exp2f(tab[t]);
     // ---- readout of strip tb ----
     Frag<T> xf[KX / 32];
 #pragma unroll
@@ -346,12 +413,28 @@ __device__ __forceinline__ void bwd_role(const BwdArgs &a, int64_t unit,
         }
       }
       // acc[rr]: key s = 16 sb + 4 g + rr, query t; causal weights
+      if constexpr (SEL) {
+        const f32x4 ls =
+            *reinterpret_cast<const f32x4 *>(tab + 16 * sb + 4 * g);
+        const f32x4 bs =
+            *reinterpret_cast<const f32x4 *>(tab + C + 16 * sb + 4 * g);
+        const float lt = tab[t], bt = tab[C + t];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int s = 16 * sb + 4 * g + rr;
-        acc[rr] = s <= t ? acc[rr] * (DECAY ? bdec * gp[s <= t ? t - s : 0]
-                                            : 1.f)
-                         : 0.f;
+        for (int rr = 0; rr < 4; ++rr) {
+          const int s = 16 * sb + 4 * g + rr;
+          // (above the diagonal the power may overflow: the select drops it)
+          const float wgt =
+              (REV ? bt : bs[rr]) * __builtin_amdgcn_exp2f(lt - ls[rr]);
+          acc[rr] = s <= t ? acc[rr] * wgt : 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int s = 16 * sb + 4 * g + rr;
+          acc[rr] = s <= t ? acc[rr] * (DECAY ? bdec * gp[s <= t ? t - s : 0]
+                                              : 1.f)
+                           : 0.f;
+        }
       }
       pt[sb] = acc;
     }
@@ -397,9 +480,17 @@ __device__ __forceinline__ void bwd_role(const BwdArgs &a, int64_t unit,
     }
     // ---- state update: S <- g^r S + (w Y)^T Z, the weights w_s =
     // b g^(r-1-s) of positions 32 kb + 8 g + e applied in registers ----
-    const float gr = gp[rows];
+    const float gr = SEL ? tab[3 * C] : gp[rows];
     f32x4 wlo[C / 32], whi[C / 32];
-    if constexpr (DECAY) {
+    if constexpr (SEL) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < C / 32; ++kb2) {
+        wlo[kb2] = *reinterpret_cast<const f32x4 *>(tab + 2 * C + 32 * kb2 +
+                                                    8 * g);
+        whi[kb2] = *reinterpret_cast<const f32x4 *>(tab + 2 * C + 32 * kb2 +
+                                                    8 * g + 4);
+      }
+    } else if constexpr (DECAY) {
 #pragma unroll
       for (int kb2 = 0; kb2 < C / 32; ++kb2)
 #pragma unroll
@@ -1220,11 +1311,11 @@ hipError_t launch_seg(const BwdArgs &a, int64_t units, hipStream_t s) {
 // dk, the last units nv dv (nq = d'/16, nv = d/16).  Within a role the
 // blocks of one unit get indices of one XCD (workgroups are dispatched to
 // the 8 XCDs round-robin), so the rows they all read come from its L2.
-template <typename T, int D, int DF, bool DECAY, bool ELU, bool FG = false>
+template <typename T, int D, int DF, bool DECAY, bool ELU, bool FG = false,
+          bool SEL = false>
 __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(
     sizeof(T) == 2 ? (DF <= 128 ? 3 : 2) : 1)))
-void la_bwd_kernel(BwdArgs a,
-                                                           int64_t units) {
+void la_bwd_kernel(BwdArgs a, int64_t units) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int nq = DF / 16, nv = D / 16;
   const int64_t b = blockIdx.x;
@@ -1237,11 +1328,11 @@ void la_bwd_kernel(BwdArgs a,
   const int64_t unit = i / nblk;
   const int blk = static_cast<int>(i % nblk);
   if (role == kRoleDQ)
-    bwd_role<T, D, DF, kRoleDQ, DECAY, ELU, FG>(a, unit, blk, smem);
+    bwd_role<T, D, DF, kRoleDQ, DECAY, ELU, FG, SEL>(a, unit, blk, smem);
   else if (role == kRoleDK)
-    bwd_role<T, D, DF, kRoleDK, DECAY, ELU, FG>(a, unit, blk, smem);
+    bwd_role<T, D, DF, kRoleDK, DECAY, ELU, FG, SEL>(a, unit, blk, smem);
   else
-    bwd_role<T, D, DF, kRoleDV, DECAY, ELU, FG>(a, unit, blk, smem);
+    bwd_role<T, D, DF, kRoleDV, DECAY, ELU, FG, SEL>(a, unit, blk, smem);
 }
 
 template <typename T, int D, bool ELU>
@@ -1255,9 +1346,10 @@ hipError_t launch_prep(const BwdArgs &a, int64_t units, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T, int D, int DF, bool DECAY, bool ELU, bool FG = false>
+template <typename T, int D, int DF, bool DECAY, bool ELU, bool FG = false,
+          bool SEL = false>
 hipError_t launch_all(const BwdArgs &a, int64_t units, hipStream_t s) {
-  if constexpr (std::is_same_v<T, bf16> && D == kSegD && DF == D) {
+  if constexpr (std::is_same_v<T, bf16> && D == kSegD && DF == D && !SEL) {
     if (a.nseg > 0) {
       // segmented roles map k, q themselves: the preparation pass writes
       // only G~
@@ -1269,16 +1361,17 @@ hipError_t launch_all(const BwdArgs &a, int64_t units, hipStream_t s) {
   hipError_t e = launch_prep<T, D, ELU>(a, units, s);
   if (e != hipSuccess) return e;
   constexpr size_t lds =
-      std::max({BShape<T, D, DF, kRoleDQ, DECAY>::lds_bytes,
-                BShape<T, D, DF, kRoleDK, DECAY>::lds_bytes,
-                BShape<T, D, DF, kRoleDV, DECAY>::lds_bytes});
+      std::max({BShape<T, D, DF, kRoleDQ, DECAY, SEL>::lds_bytes,
+                BShape<T, D, DF, kRoleDK, DECAY, SEL>::lds_bytes,
+                BShape<T, D, DF, kRoleDV, DECAY, SEL>::lds_bytes});
   static_assert(lds <= 160 * 1024, "LDS of one workgroup");
   static const hipError_t once = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&la_bwd_kernel<T, D, DF, DECAY, ELU, FG>),
+      reinterpret_cast<const void *>(
+          &la_bwd_kernel<T, D, DF, DECAY, ELU, FG, SEL>),
       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (once != hipSuccess) return once;
   const int64_t blocks = units * (2 * (DF / 16) + D / 16);
-  hipLaunchKernelGGL((la_bwd_kernel<T, D, DF, DECAY, ELU, FG>),
+  hipLaunchKernelGGL((la_bwd_kernel<T, D, DF, DECAY, ELU, FG, SEL>),
                      dim3(static_cast<unsigned>(blocks)), dim3(kBThreads), lds,
                      s, a, units);
   return hipGetLastError();
@@ -1461,6 +1554,9 @@ hipError_t launch_pf_t(const BwdArgs &a, int64_t units, int d, int df,
 
 template <typename T, int D>
 hipError_t launch_d(const BwdArgs &a, int64_t units, hipStream_t s) {
+  if (a.lam)
+    return a.elu1 ? launch_all<T, D, D, true, true, false, true>(a, units, s)
+                  : launch_all<T, D, D, true, false, false, true>(a, units, s);
   if (a.decay)
     return a.elu1 ? launch_all<T, D, D, true, true>(a, units, s)
                   : launch_all<T, D, D, true, false>(a, units, s);

@@ -175,6 +175,10 @@ struct BwdArgs {
   // the map with omega ([d][d_feat] fp32).
   void *dqf = nullptr, *dkf = nullptr;
   const float *omega = nullptr;
+  // Per-position decay (else null): lam = log(gamma) of every position
+  // ([units][n] fp32, the layout la_forward_gated takes); decay is null
+  // then and the column-block kernel runs (nseg = 0).
+  const float *lam = nullptr;
 };
 bool backward_supported(int d, int d_feat);
 // Sizes the Performer map's backward is built for.

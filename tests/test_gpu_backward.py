@@ -257,3 +257,123 @@ def test_autograd_op_matches_oracle(dtype):
                              oracle.MAP_ELU1, None, f64(x["decay"]))
     assert rel(out.detach(), ref_out) <= (1e-4 if dtype == torch.float32
                                           else 1e-2)
+
+
+# A decay per position (la_forward_gated_train, la_backward_gated): the
+# oracle's adjoint of the gated recurrence (oracle.backward_gated).  Gate
+# ranges are log10 of the per-head rate that scales softplus(z) (the input
+# recipe of the gated forward), from slow decay to about 3e-7 per step.
+GATED_GRID = [
+    # (name, B, H, n, d, map, gate)
+    ("ragged_d64", 2, 2, 1000, 64, "elu1", (-3.0, -1.0)),
+    ("d128", 1, 2, 700, 128, "elu1", (-2.0, -0.5)),
+    ("identity_d32_n17", 1, 2, 17, 32, "identity", (-2.0, -0.5)),
+    ("d16_fast", 2, 1, 333, 16, "elu1", (-1.0, 0.5)),
+    ("identity_d128_long", 1, 1, 3000, 128, "identity", (-3.0, -1.0)),
+    ("one_chunk", 1, 3, 40, 128, "elu1", (-2.0, -0.5)),
+]
+
+
+def run_gated(cfg, seed, lam=None):
+    x = make(cfg, seed)
+    if lam is not None:
+        x["log_decay"] = lam
+    name = I.MAP_NAMES[cfg.mapk]
+    q, k, v, ld = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["log_decay"])
+    out, den = K.forward_train(q, k, v, name, log_decay=ld)
+    grads = K.backward(q, k, v, out, den, dev(x["dout"]), name, log_decay=ld)
+    torch.cuda.synchronize()
+    ref = oracle.backward_gated(f64(x["q"]), f64(x["k"]), f64(x["v"]),
+                                f64(x["dout"]), cfg.mapk, None,
+                                f64(x["log_decay"]), oracle.LD_POSITION)
+    ref_out = oracle.forward_gated(f64(x["q"]), f64(x["k"]), f64(x["v"]),
+                                   cfg.mapk, None, f64(x["log_decay"]),
+                                   oracle.LD_POSITION, True)
+    return out, grads, ref_out, ref
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("case", GATED_GRID, ids=[c[0] for c in GATED_GRID])
+def test_backward_gated_grid(case, dtype):
+    name, B, H, n, d, mp, gate = case
+    mapk = I.MAP_ELU1 if mp == "elu1" else I.MAP_IDENTITY
+    cfg = I.PrefillConfig(f"bwd_gated_{name}", B=B, H=H, n=n, d=d,
+                          dtype=dtype, mapk=mapk, gate=gate)
+    print(f"gated backward {name} {dtype}", flush=True)
+    out, grads, ref_out, ref = run_gated(cfg, seed=9)
+    errs = [rel(gq, r) for gq, r in zip(grads, ref)]
+    print(f"  dq {errs[0]:.2e} dk {errs[1]:.2e} dv {errs[2]:.2e}", flush=True)
+    assert max(errs) <= GTOL[dtype], errs
+    assert rel(out, ref_out) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_backward_gated_resets(dtype):
+    """lam = -inf (gamma = 0: the state restarts) at scattered positions,
+    one of them a chunk's first row and one its last, and very negative
+    values elsewhere among ordinary ones: the kernel floors lam at -104,
+    where exp(lam) is 0 in fp32 as it is for -inf."""
+    cfg = I.PrefillConfig("bwd_gated_resets", B=1, H=2, n=300, d=64,
+                          dtype=dtype, mapk=I.MAP_ELU1, gate=(-2.0, -0.5))
+    lam = I.make_prefill(cfg, 11)["log_decay"].clone()
+    lam[0, 0, [0, 64, 127, 200]] = -float("inf")
+    lam[0, 1, [5, 130, 131]] = -500.0
+    out, grads, ref_out, ref = run_gated(cfg, seed=11, lam=lam)
+    errs = [rel(gq, r) for gq, r in zip(grads, ref)]
+    print(f"resets {dtype}: dq {errs[0]:.2e} dk {errs[1]:.2e} "
+          f"dv {errs[2]:.2e}", flush=True)
+    assert max(errs) <= GTOL[dtype], errs
+    assert rel(out, ref_out) <= TOL[dtype]
+
+
+def test_backward_gated_full_size_every_unit():
+    """The gated workload's sizes (B2 H16 n65536 d128, bf16, elu + 1, a
+    decay per position), every unit and every gradient against the
+    oracle's adjoint (one oracle call per batch row, its heads in
+    parallel)."""
+    cfg = I.PrefillConfig("bwd_gated_full", B=2, H=16, n=65536, d=128,
+                          dtype=torch.bfloat16, mapk=I.MAP_ELU1,
+                          gate=(-3.0, -1.0))
+    x = make(cfg, 0)
+    q, k, v, ld = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["log_decay"])
+    out, den = K.forward_train(q, k, v, "elu1", log_decay=ld)
+    grads = K.backward(q, k, v, out, den, dev(x["dout"]), "elu1",
+                       log_decay=ld)
+    torch.cuda.synchronize()
+    grads = [t.cpu() for t in grads]
+    worst = [0.0, 0.0, 0.0]
+    for b in range(cfg.B):
+        sl = slice(b, b + 1)
+        ref = oracle.backward_gated(f64(x["q"][sl]), f64(x["k"][sl]),
+                                    f64(x["v"][sl]), f64(x["dout"][sl]),
+                                    cfg.mapk, None, f64(x["log_decay"][sl]),
+                                    oracle.LD_POSITION)
+        for i in range(3):
+            got = grads[i][sl].double().numpy()
+            assert np.all(np.isfinite(got))
+            for h in range(cfg.H):
+                r = ref[i][0, h]
+                worst[i] = max(worst[i], np.max(np.abs(got[0, h] - r)) /
+                               np.max(np.abs(r)))
+        del ref
+    print(f"gated backward full size: max per-unit rel err dq {worst[0]:.2e} "
+          f"dk {worst[1]:.2e} dv {worst[2]:.2e}", flush=True)
+    assert max(worst) <= GTOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_autograd_op_gated_matches_oracle(dtype):
+    """linear_attention(..., log_decay=...) as a torch op: autograd
+    gradients through la_forward_gated_train and la_backward_gated."""
+    cfg = I.PrefillConfig("bwd_gated_op", B=1, H=2, n=333, d=64, dtype=dtype,
+                          mapk=I.MAP_ELU1, gate=(-2.0, -0.5))
+    x = make(cfg, 23)
+    q, k, v = (dev(x[n]).requires_grad_(True) for n in ("q", "k", "v"))
+    out = K.linear_attention(q, k, v, "elu1", log_decay=dev(x["log_decay"]))
+    out.backward(dev(x["dout"]))
+    torch.cuda.synchronize()
+    refs = oracle.backward_gated(f64(x["q"]), f64(x["k"]), f64(x["v"]),
+                                 f64(x["dout"]), oracle.MAP_ELU1, None,
+                                 f64(x["log_decay"]), oracle.LD_POSITION)
+    for t, r in zip((q, k, v), refs):
+        assert rel(t.grad, r) <= GTOL[dtype]

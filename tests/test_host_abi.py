@@ -341,6 +341,59 @@ def test_backward_rejects_null_workspace(lib):
     assert "workspace" in lib.la_last_error().decode()
 
 
+def test_backward_gated_workspace_bytes(lib):
+    import torch
+    a256 = lambda x: (x + 255) // 256 * 256
+    rows = 2 * 3 * 100
+    # a decay per position always takes the column-block roles: bf16 at
+    # d = 128 keeps K', Q' rows (elu + 1) and no segment aggregates
+    assert K.backward_workspace_bytes(2, 3, 100, 128, gated=True) == (
+        a256(rows * 160 * 2) + 2 * a256(rows * 128 * 2))
+    assert K.backward_workspace_bytes(2, 3, 100, 64, "identity",
+                                      gated=True) == a256(rows * 96 * 2)
+    assert K.backward_workspace_bytes(2, 3, 100, 32, dtype=torch.float32,
+                                      gated=True) == (
+        a256(rows * 64 * 4) + 2 * a256(rows * 32 * 4))
+    # not built: the Performer map, d != d_feat, other d; empty sizes
+    assert K.backward_workspace_bytes(2, 3, 100, 64, "performer",
+                                      gated=True) == 0
+    assert K.backward_workspace_bytes(2, 3, 100, 48, gated=True) == 0
+    assert K.backward_workspace_bytes(2, 3, 0, 64, gated=True) == 0
+
+
+def test_gated_train_and_backward_reject(lib):
+    # host-side validation only: nothing is enqueued
+    vp = ctypes.c_void_p(16)
+    bwd = lambda lay, mapk, lam, ws: lib.la_backward_gated(
+        vp, vp, vp, vp, vp, vp, vp, vp, vp, 1, 1, 64, 64, 64, mapk, None,
+        lam, lay, B.LA_BF16, ws, None)
+    assert bwd(B.LD_CHANNEL, B.MAP_ELU1, vp, vp) == B.LA_ERR_UNSUPPORTED
+    assert bwd(B.LD_BOTH, B.MAP_ELU1, vp, vp) == B.LA_ERR_UNSUPPORTED
+    assert bwd(7, B.MAP_ELU1, vp, vp) == B.LA_ERR_INVALID_ARG
+    assert bwd(B.LD_POSITION, B.MAP_PERFORMER, vp, vp) == B.LA_ERR_UNSUPPORTED
+    assert bwd(B.LD_POSITION, B.MAP_ELU1, None, vp) == B.LA_ERR_INVALID_ARG
+    assert bwd(B.LD_POSITION, B.MAP_ELU1, vp, None) == B.LA_ERR_WORKSPACE
+    fwd = lambda lay, den, lam: lib.la_forward_gated_train(
+        vp, vp, vp, vp, den, 1, 1, 64, 64, 64, B.MAP_ELU1, None, lam, lay,
+        B.LA_BF16, vp, None)
+    assert fwd(B.LD_CHANNEL, vp, vp) == B.LA_ERR_UNSUPPORTED
+    assert fwd(B.LD_POSITION, None, vp) == B.LA_ERR_INVALID_ARG
+    assert fwd(B.LD_POSITION, vp, None) == B.LA_ERR_INVALID_ARG
+
+
+def test_binding_rejects_decay_with_log_decay():
+    import torch
+    x = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
+    den = torch.ones(1, 1, 64)
+    lam = torch.zeros(1, 1, 64)
+    with pytest.raises(ValueError):
+        K.backward(x, x, x, x, den, x, decay=torch.ones(1), log_decay=lam)
+    with pytest.raises(ValueError):
+        K.backward(x, x, x, x, den, x, log_decay=torch.zeros(1, 1, 63))
+    with pytest.raises(TypeError):
+        K.forward_train(x, x, x, log_decay=lam.double())
+
+
 def test_binding_backward_rejects_small_workspace():
     import torch
     x = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
