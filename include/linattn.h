@@ -336,8 +336,8 @@ la_status la_backward_gated(const void *q, const void *k, const void *v,
 
 /*
  * la_backward_gated_workspace_bytes -- device workspace la_backward_gated
- * needs: per row the prepared G row (d + 2 values padded to a multiple of
- * 32) and, for LA_MAP_ELU1, the features phi(k) and phi(q), all in dtype.
+ * needs: that of la_backward for the same sizes (the segment state sums
+ * carry each segment's sum of log2 gamma in space la_backward reserves).
  * Pure host function; 0 for arguments la_backward_gated would reject and
  * for empty sizes.
  */

@@ -618,16 +618,15 @@ la_status la_forward_train(const void *q, const void *k, const void *v,
 
 namespace {
 // Workspace of la_backward: G~ rows, then (elu + 1, column-block kernel)
-// K' and Q', then the segment aggregates of the segmented roles.  With a
-// decay per position (gated) only the column-block kernel runs.
+// K' and Q', then the segment aggregates of the segmented roles (and, for
+// a decay per position, each segment's sum of log2 gamma).
 size_t backward_ws(int64_t units, int64_t n, int d, int map, int dtype,
-                   size_t *kf_off, size_t *agg_off = nullptr,
-                   bool gated = false) {
+                   size_t *kf_off, size_t *agg_off = nullptr) {
   const size_t es = elem_size(dtype);
   const size_t g = align256(static_cast<size_t>(units * n) *
                             la::backward_gwidth(d) * es);
   const size_t f = align256(static_cast<size_t>(units * n) * d * es);
-  const int nseg = gated ? 0 : la::backward_segments(units, n, d, dtype);
+  const int nseg = la::backward_segments(units, n, d, dtype);
   // the segmented roles map k, q themselves: no K', Q' rows
   const size_t feats = map == LA_MAP_ELU1 && nseg == 0 ? 2 * f : 0;
   const size_t agg =
@@ -734,7 +733,7 @@ size_t la_backward_gated_workspace_bytes(int B, int H, int64_t n, int d,
   if (map == LA_MAP_PERFORMER || !la::backward_supported(d, d_feat)) return 0;
   const int64_t units = static_cast<int64_t>(B) * H;
   if (units * n > (int64_t{1} << 46) || units > (int64_t{1} << 26)) return 0;
-  return backward_ws(units, n, d, map, dtype, nullptr, nullptr, true);
+  return backward_ws(units, n, d, map, dtype, nullptr);
 }
 
 // la_backward (decay [H] or null, lam null) and la_backward_gated (lam, a
@@ -773,11 +772,11 @@ static la_status backward_impl(const void *q, const void *k, const void *v,
     const bool gated = lam != nullptr;
     if (!workspace)
       return fail(LA_ERR_WORKSPACE, "la_backward: workspace of %zu bytes required",
-                  backward_ws(units, n, d, map, dtype, nullptr, nullptr, gated));
+                  backward_ws(units, n, d, map, dtype, nullptr));
     size_t kf_off = 0, agg_off = 0;
     const size_t fbytes = align256(static_cast<size_t>(units * n) * d *
                                    elem_size(dtype));
-    backward_ws(units, n, d, map, dtype, &kf_off, &agg_off, gated);
+    backward_ws(units, n, d, map, dtype, &kf_off, &agg_off);
     la::BwdArgs a;
     a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.den = den;
     a.dq = dq; a.dk = dk; a.dv = dv;
@@ -789,7 +788,7 @@ static la_status backward_impl(const void *q, const void *k, const void *v,
     a.elu1 = map == LA_MAP_ELU1;
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     a.gt = ws;
-    a.nseg = gated ? 0 : la::backward_segments(units, n, d, dtype);
+    a.nseg = la::backward_segments(units, n, d, dtype);
     // K', Q' rows only where the column-block kernel reads them
     const bool feats = a.elu1 && a.nseg == 0;
     a.kf = feats ? ws + kf_off : const_cast<void *>(k);

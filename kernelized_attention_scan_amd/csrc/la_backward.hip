@@ -166,8 +166,8 @@ __device__ __forceinline__ float dphi(float x, bool elu) {  // d phi / d x
 // tab[p] = L_p, tab[C + p] = 1 - gamma_p, tab[2 C + p] = the state-update
 // weight of key p (0 past the valid rows), tab[3 C] = 2^(sum of the chunk).
 template <bool REV>
-__device__ __forceinline__ void gate_table(float lam, float *tab, int lane,
-                                           int rows) {
+__device__ __forceinline__ float gate_table(float lam, float *tab, int lane,
+                                            int rows) {
   constexpr int C = kBC;
   static_assert(C == kWave, "one row per lane");
   constexpr float kLog2e = 1.4426950408889634f;
@@ -189,6 +189,41 @@ __device__ __forceinline__ void gate_table(float lam, float *tab, int lane,
   tab[2 * C + lane] =
       lane < rows ? (REV ? 1.f : beta) * __builtin_amdgcn_exp2f(all - L) : 0.f;
   if (lane == 0) tab[3 * C] = __builtin_amdgcn_exp2f(all);
+  return all;  // the chunk's sum of log2 gamma
+}
+
+// The table's uses: the causal weights of query t's scores against keys
+// s = 16 sb + 4 g + rr (above the diagonal the power may overflow: the
+// select drops it), the entering state's readout weight of query t, and
+// the state-update weights of keys 32 kb + 8 g + e (lo) and + 4 (hi).
+template <bool REV>
+__device__ __forceinline__ void gate_scores(f32x4 &acc, const float *tab,
+                                            int t, int sb, int g) {
+  constexpr int C = kBC;
+  const f32x4 ls = *reinterpret_cast<const f32x4 *>(tab + 16 * sb + 4 * g);
+  const f32x4 bs = *reinterpret_cast<const f32x4 *>(tab + C + 16 * sb + 4 * g);
+  const float lt = tab[t], bt = tab[C + t];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int s = 16 * sb + 4 * g + rr;
+    const float wgt = (REV ? bt : bs[rr]) * __builtin_amdgcn_exp2f(lt - ls[rr]);
+    acc[rr] = s <= t ? acc[rr] * wgt : 0.f;
+  }
+}
+template <bool REV>
+__device__ __forceinline__ float gate_readout(const float *tab, int t) {
+  const float p = __builtin_amdgcn_exp2f(tab[t]);
+  return REV ? tab[kBC + t] * p : p;
+}
+__device__ __forceinline__ void gate_update(const float *tab, int g,
+                                            f32x4 (&wlo)[kBC / 32],
+                                            f32x4 (&whi)[kBC / 32]) {
+#pragma unroll
+  for (int kb2 = 0; kb2 < kBC / 32; ++kb2) {
+    wlo[kb2] = *reinterpret_cast<const f32x4 *>(tab + 2 * kBC + 32 * kb2 + 8 * g);
+    whi[kb2] =
+        *reinterpret_cast<const f32x4 *>(tab + 2 * kBC + 32 * kb2 + 8 * g + 4);
+  }
 }
 
 // One role's workgroup: output columns 16 blk .. 16 blk + 15 of unit.  The
@@ -617,6 +652,14 @@ constexpr int kSegD = 128;                                   // d built
 constexpr int kSegTiles = backward_gwidth(kSegD) / 16;       // NT, at most
 constexpr int kSegSlot = kSWaves * kSegTiles * 256;          // floats
 
+// A decay per position: each segment's sum of log2 gamma over its rows,
+// written by the aggregates launch after all aggregates ([role][unit][seg]).
+__device__ __forceinline__ float *seg_total(const BwdArgs &a, int64_t units,
+                                            int role, int64_t unit, int seg) {
+  return a.agg + 2 * units * a.nseg * static_cast<int64_t>(kSegSlot) +
+         (role * units + unit) * a.nseg + seg;
+}
+
 template <typename T, int ROLE>
 struct SShape {
   static_assert(ROLE == kRoleDQ || ROLE == kRoleDK, "dq, dk layouts");
@@ -629,15 +672,18 @@ struct SShape {
   static constexpr int SX = kBC * LX, SZ = kBC * LZ, SST = D * LX;
   // dq also stages the raw q rows (phi'(q) of its outputs)
   static constexpr int SP = ROLE == kRoleDQ ? SZ : 0;
+  // the powers g^0 .. g^C, or with a decay per position the chunk's table
+  static constexpr int TAB = 3 * kBC + 4;
   static constexpr size_t lds_bytes =
-      sizeof(T) * (2 * SX + SZ + SST + SP) + sizeof(float) * (kBC + 4);
+      sizeof(T) * (2 * SX + SZ + SST + SP) + sizeof(float) * TAB;
   // the aggregates launch stages only Y and Z: two workgroups fit a CU
   static constexpr size_t lds_bytes_agg =
-      sizeof(T) * (SX + SZ) + sizeof(float) * (kBC + 4);
+      sizeof(T) * (SX + SZ) + sizeof(float) * TAB;
   static_assert(D / 16 == kSWaves, "one state column block per wave");
 };
 
-template <typename T, int ROLE, bool DECAY, bool ELU, int PHASE>
+template <typename T, int ROLE, bool DECAY, bool ELU, int PHASE,
+          bool SEL = false>
 __device__ __forceinline__ void seg_role(const BwdArgs &a, int64_t units,
                                          int64_t unit, int seg,
                                          unsigned char *smem) {
@@ -657,15 +703,21 @@ __device__ __forceinline__ void seg_role(const BwdArgs &a, int64_t units,
   T *sST = sZ + F::SZ;                           // S^T copy
   T *sP = sST + F::SST;                          // raw q rows (dq)
   float *gp = reinterpret_cast<float *>(PHASE == 1 ? sST : sP + F::SP);
+  float *tab = gp;  // SEL: the chunk's table (gate_table) instead
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, li = lane & 15;
   const int tb = w % 4, jh = w / 4;
   const int h = static_cast<int>(unit % a.H);
-  const float gdec = DECAY ? a.decay[h] : 1.f, bdec = DECAY ? 1.f - gdec : 1.f;
+  constexpr bool HD = DECAY && !SEL;  // one decay per head
+  const float gdec = HD ? a.decay[h] : 1.f, bdec = HD ? 1.f - gdec : 1.f;
   const float lg = log2f(gdec);
-  for (int i = tid; i <= C; i += kSThreads) gp[i] = pow_int(gdec, lg, i);
+  if constexpr (!SEL)
+    for (int i = tid; i <= C; i += kSThreads) gp[i] = pow_int(gdec, lg, i);
+  const float *lb = SEL ? a.lam + unit * a.n : nullptr;
+  float laml = 0.f;  // SEL, wave 0: lam of processing index `lane`
+  float segl = 0.f;  // SEL, wave 0: the segment's sum of log2 gamma so far
 
   const int64_t n = a.n;
   const T *qb = static_cast<const T *>(a.q) + unit * n * D;
@@ -717,6 +769,16 @@ __device__ __forceinline__ void seg_role(const BwdArgs &a, int64_t units,
     if constexpr (NEED_R1) r1.load(vb, r0, rows, 0, tid);
     r2.load(ROLE == kRoleDQ ? kb : qb, r0, rows, 0, tid);
     if constexpr (PFI) r3.load(qb, r0, rows, 0, tid);
+    if constexpr (SEL) {
+      if (w == 0) {  // rows past the end are out of the resource: lam 0
+        const __amdgpu_buffer_rsrc_t r =
+            make_rsrc(lb + r0, static_cast<unsigned>(rows) * sizeof(float));
+        const int rr = REV && lane < rows ? rows - 1 - lane : lane;
+        laml = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(
+                       r, static_cast<unsigned>(rr) * 4u, 0, 0));
+      }
+    }
   };
   // the same with phi applied (elu + 1 in fp32, rounded once; rows past the
   // end stay zero)
@@ -755,6 +817,8 @@ __device__ __forceinline__ void seg_role(const BwdArgs &a, int64_t units,
     auto trow = [&](int r) { return REV && r < rows ? rows - 1 - r : r; };
     T *sG = ROLE == kRoleDQ ? sX : sY;
     T *sV = ROLE == kRoleDQ ? sY : sX;
+    if constexpr (SEL)
+      if (w == 0) segl += gate_table<REV>(laml, tab, lane, rows);
     if constexpr (NEED_G) put(rg, sG, LX, trow);
     if constexpr (NEED_R1) {
       put(r1, sV, LX, trow);
@@ -782,11 +846,16 @@ __device__ __forceinline__ void seg_role(const BwdArgs &a, int64_t units,
   if constexpr (PHASE == 2) {
     // the entering state: the aggregates before this segment, each carried
     // over the rows between it and this segment (whole chunks)
-    for (int sg = 0; sg < seg; ++sg) {
+    // (SEL: carried over the segments between by their sums of log2 gamma)
+    float between = 0.f;
+    for (int i = 0; i < seg; ++i) {
+      const int sg = SEL ? seg - 1 - i : i;
       const float wgt =
-          DECAY ? pow_int(gdec, lg,
+          SEL   ? __builtin_amdgcn_exp2f(between)
+          : HD  ? pow_int(gdec, lg,
                           static_cast<int64_t>(seg - sg - 1) * cps * C)
                 : 1.f;
+      if constexpr (SEL) between += *seg_total(a, units, ROLE, unit, sg);
       const float *src = slot(sg);
 #pragma unroll
       for (int fb = 0; fb < NT; ++fb)
@@ -801,9 +870,11 @@ __device__ __forceinline__ void seg_role(const BwdArgs &a, int64_t units,
   };
   auto state_update = [&](int c) {
     const int rows = rows_of(c);
-    const float gr = gp[rows];
+    const float gr = SEL ? tab[3 * C] : gp[rows];
     f32x4 wlo[C / 32], whi[C / 32];
-    if constexpr (DECAY) {
+    if constexpr (SEL) {
+      gate_update(tab, g, wlo, whi);
+    } else if constexpr (DECAY) {
 #pragma unroll
       for (int kb2 = 0; kb2 < C / 32; ++kb2)
 #pragma unroll
@@ -846,7 +917,7 @@ __device__ __forceinline__ void seg_role(const BwdArgs &a, int64_t units,
   for (int c = cb; c < ce; ++c) {
     if constexpr (PHASE == 2) {
       const int rows = rows_of(c);
-      const float gt = gp[t + 1];
+      const float gt = SEL ? gate_readout<REV>(tab, t) : gp[t + 1];
       Frag<T> xf[KX / 32];
 #pragma unroll
       for (int kq = 0; kq < KX / 32; ++kq)
@@ -863,12 +934,16 @@ __device__ __forceinline__ void seg_role(const BwdArgs &a, int64_t units,
             acc = mma(fa, xf[kq], acc);
           }
         }
+        if constexpr (SEL) {
+          gate_scores<REV>(acc, tab, t, sb, g);
+        } else {
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int s_ = 16 * sb + 4 * g + rr;
-          acc[rr] = s_ <= t ? acc[rr] * (DECAY ? bdec * gp[s_ <= t ? t - s_ : 0]
-                                               : 1.f)
-                            : 0.f;
+          for (int rr = 0; rr < 4; ++rr) {
+            const int s_ = 16 * sb + 4 * g + rr;
+            acc[rr] = s_ <= t ? acc[rr] * (DECAY ? bdec * gp[s_ <= t ? t - s_ : 0]
+                                                 : 1.f)
+                              : 0.f;
+          }
         }
         pt[sb] = acc;
       }
@@ -925,6 +1000,7 @@ __device__ __forceinline__ void seg_role(const BwdArgs &a, int64_t units,
 #pragma unroll
     for (int fb = 0; fb < NT; ++fb)
       *reinterpret_cast<f32x4 *>(dst + fb * 256) = S[fb];
+    if (SEL && tid == 0) *seg_total(a, units, ROLE, unit, seg) = segl;
   }
 }
 
@@ -942,9 +1018,9 @@ __device__ __forceinline__ void seg_role(const BwdArgs &a, int64_t units,
 constexpr size_t kDkvLds =
     sizeof(bf16) * (2 * SShape<bf16, kRoleDK>::SX + 3 * SShape<bf16, kRoleDK>::SZ +
                     SShape<bf16, kRoleDK>::SST) +
-    sizeof(float) * (kBC + 4);
+    sizeof(float) * SShape<bf16, kRoleDK>::TAB;
 
-template <bool DECAY, bool ELU>
+template <bool DECAY, bool ELU, bool SEL = false>
 __device__ __forceinline__ void seg_dkv(const BwdArgs &a, int64_t units,
                                         int64_t unit, int seg,
                                         unsigned char *smem) {
@@ -960,15 +1036,20 @@ __device__ __forceinline__ void seg_dkv(const BwdArgs &a, int64_t units,
   T *sKr = sK + F::SZ;                  // raw k: phi'(k) of dk's outputs
   T *sST = sKr + F::SZ;                 // S_dk^T: row f of Q', column c of G~
   float *gp = reinterpret_cast<float *>(sST + F::SST);  // g^0 .. g^C
+  float *tab = gp;  // SEL: the chunk's table (gate_table) instead
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, li = lane & 15;
   const int tb = w % 4, jh = w / 4;
   const int h = static_cast<int>(unit % a.H);
-  const float gdec = DECAY ? a.decay[h] : 1.f, bdec = DECAY ? 1.f - gdec : 1.f;
+  constexpr bool HD = DECAY && !SEL;  // one decay per head
+  const float gdec = HD ? a.decay[h] : 1.f, bdec = HD ? 1.f - gdec : 1.f;
   const float lg = log2f(gdec);
-  for (int i = tid; i <= C; i += kSThreads) gp[i] = pow_int(gdec, lg, i);
+  if constexpr (!SEL)
+    for (int i = tid; i <= C; i += kSThreads) gp[i] = pow_int(gdec, lg, i);
+  const float *lb = SEL ? a.lam + unit * a.n : nullptr;
+  float laml = 0.f;  // SEL, wave 0: lam of processing index `lane`
 
   const int64_t n = a.n;
   const T *qb = static_cast<const T *>(a.q) + unit * n * D;
@@ -1010,6 +1091,16 @@ __device__ __forceinline__ void seg_dkv(const BwdArgs &a, int64_t units,
     rv.load(vb, r0, rows, 0, tid);
     rq.load(qb, r0, rows, 0, tid);
     rk.load(kb, r0, rows, 0, tid);
+    if constexpr (SEL) {
+      if (w == 0) {  // rows past the end are out of the resource: lam 0
+        const __amdgpu_buffer_rsrc_t r =
+            make_rsrc(lb + r0, static_cast<unsigned>(rows) * sizeof(float));
+        const int rr = lane < rows ? rows - 1 - lane : lane;
+        laml = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(
+                       r, static_cast<unsigned>(rr) * 4u, 0, 0));
+      }
+    }
   };
   auto put_phi = [&](const SD &sl, T *dst, auto trow, int rows) {
 #pragma unroll
@@ -1053,6 +1144,8 @@ __device__ __forceinline__ void seg_dkv(const BwdArgs &a, int64_t units,
   auto stage = [&](int c) {
     const int rows = rows_of(c);
     auto trow = [&](int r) { return r < rows ? rows - 1 - r : r; };
+    if constexpr (SEL)
+      if (w == 0) gate_table<true>(laml, tab, lane, rows);
     put(rg, sG, trow);
     put(rv, sV, trow);
     if (tid < C) {
@@ -1071,10 +1164,15 @@ __device__ __forceinline__ void seg_dkv(const BwdArgs &a, int64_t units,
   f32x4 S[NT];
 #pragma unroll
   for (int fb = 0; fb < NT; ++fb) S[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int sg = 0; sg < seg; ++sg) {
+  // (SEL: carried over the segments between by their sums of log2 gamma)
+  float between = 0.f;
+  for (int i = 0; i < seg; ++i) {
+    const int sg = SEL ? seg - 1 - i : i;
     const float wgt =
-        DECAY ? pow_int(gdec, lg, static_cast<int64_t>(seg - sg - 1) * cps * C)
-              : 1.f;
+        SEL  ? __builtin_amdgcn_exp2f(between)
+        : HD ? pow_int(gdec, lg, static_cast<int64_t>(seg - sg - 1) * cps * C)
+             : 1.f;
+    if constexpr (SEL) between += *seg_total(a, units, kRoleDK, unit, sg);
     const float *src = a.agg +
                        ((static_cast<int64_t>(kRoleDK) * units + unit) * nseg +
                         sg) * kSegSlot +
@@ -1091,9 +1189,11 @@ __device__ __forceinline__ void seg_dkv(const BwdArgs &a, int64_t units,
   };
   auto state_update = [&](int c) {  // S_dk <- g^r S_dk + sum w G~^T Q'
     const int rows = rows_of(c);
-    const float gr = gp[rows];
+    const float gr = SEL ? tab[3 * C] : gp[rows];
     f32x4 wlo[C / 32], whi[C / 32];
-    if constexpr (DECAY) {
+    if constexpr (SEL) {
+      gate_update(tab, g, wlo, whi);
+    } else if constexpr (DECAY) {
 #pragma unroll
       for (int kb2 = 0; kb2 < C / 32; ++kb2)
 #pragma unroll
@@ -1140,12 +1240,16 @@ __device__ __forceinline__ void seg_dkv(const BwdArgs &a, int64_t units,
           acc = mma(fa, xf[kq], acc);
         }
       }
+      if constexpr (SEL) {
+        gate_scores<true>(acc, tab, t, sb, g);
+      } else {
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int s_ = 16 * sb + 4 * g + rr;
-        acc[rr] = s_ <= t ? acc[rr] * (DECAY ? bdec * gp[s_ <= t ? t - s_ : 0]
-                                             : 1.f)
-                          : 0.f;
+        for (int rr = 0; rr < 4; ++rr) {
+          const int s_ = 16 * sb + 4 * g + rr;
+          acc[rr] = s_ <= t ? acc[rr] * (DECAY ? bdec * gp[s_ <= t ? t - s_ : 0]
+                                               : 1.f)
+                            : 0.f;
+        }
       }
       pt[sb] = acc;
     }
@@ -1163,7 +1267,7 @@ __device__ __forceinline__ void seg_dkv(const BwdArgs &a, int64_t units,
 
   for (int c = cb; c < ce; ++c) {
     const int rows = rows_of(c);
-    const float gt = gp[t + 1];
+    const float gt = SEL ? gate_readout<true>(tab, t) : gp[t + 1];
     const int64_t row = row0_of(c) + (t < rows ? rows - 1 - t : t);
     // ---- dk: queries V+ (KX wide), keys G~, values Q'
     {
@@ -1252,7 +1356,7 @@ __device__ __forceinline__ void seg_dkv(const BwdArgs &a, int64_t units,
 
 // The aggregates launch (PHASE 1) runs two workgroups per CU (four waves
 // per SIMD: at most 128 VGPRs); the readout one.
-template <bool DECAY, bool ELU, int PHASE>
+template <bool DECAY, bool ELU, int PHASE, bool SEL = false>
 __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
     PHASE == 1 ? 4 : 1))) void la_bwd_seg_kernel(BwdArgs a, int64_t units) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -1266,16 +1370,16 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
   if (PHASE == 1 && seg == nseg - 1) return;
   // role 0: dq; role 1: the dk aggregates (PHASE 1), dk and dv (PHASE 2)
   if (role == kRoleDQ) {
-    seg_role<bf16, kRoleDQ, DECAY, ELU, PHASE>(a, units, unit, seg, smem);
+    seg_role<bf16, kRoleDQ, DECAY, ELU, PHASE, SEL>(a, units, unit, seg, smem);
   } else {
     if constexpr (PHASE == 1)
-      seg_role<bf16, kRoleDK, DECAY, ELU, 1>(a, units, unit, seg, smem);
+      seg_role<bf16, kRoleDK, DECAY, ELU, 1, SEL>(a, units, unit, seg, smem);
     else
-      seg_dkv<DECAY, ELU>(a, units, unit, seg, smem);
+      seg_dkv<DECAY, ELU, SEL>(a, units, unit, seg, smem);
   }
 }
 
-template <bool DECAY, bool ELU>
+template <bool DECAY, bool ELU, bool SEL = false>
 hipError_t launch_seg(const BwdArgs &a, int64_t units, hipStream_t s) {
   const int nseg = a.nseg;
   constexpr size_t lds = std::max({SShape<bf16, kRoleDQ>::lds_bytes,
@@ -1287,22 +1391,22 @@ hipError_t launch_seg(const BwdArgs &a, int64_t units, hipStream_t s) {
                 "LDS of one workgroup (two for the aggregates)");
   static const hipError_t once = [] {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&la_bwd_seg_kernel<DECAY, ELU, 1>),
+        reinterpret_cast<const void *>(&la_bwd_seg_kernel<DECAY, ELU, 1, SEL>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds1));
     if (e != hipSuccess) return e;
     return hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&la_bwd_seg_kernel<DECAY, ELU, 2>),
+        reinterpret_cast<const void *>(&la_bwd_seg_kernel<DECAY, ELU, 2, SEL>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   }();
   if (once != hipSuccess) return once;
   const dim3 grid(static_cast<unsigned>(2 * units * nseg)), block(kSThreads);
   if (nseg > 1) {
-    hipLaunchKernelGGL((la_bwd_seg_kernel<DECAY, ELU, 1>), grid, block, lds1,
+    hipLaunchKernelGGL((la_bwd_seg_kernel<DECAY, ELU, 1, SEL>), grid, block, lds1,
                        s, a, units);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((la_bwd_seg_kernel<DECAY, ELU, 2>), grid, block, lds, s, a,
+  hipLaunchKernelGGL((la_bwd_seg_kernel<DECAY, ELU, 2, SEL>), grid, block, lds, s, a,
                      units);
   return hipGetLastError();
 }
@@ -1349,13 +1453,13 @@ hipError_t launch_prep(const BwdArgs &a, int64_t units, hipStream_t s) {
 template <typename T, int D, int DF, bool DECAY, bool ELU, bool FG = false,
           bool SEL = false>
 hipError_t launch_all(const BwdArgs &a, int64_t units, hipStream_t s) {
-  if constexpr (std::is_same_v<T, bf16> && D == kSegD && DF == D && !SEL) {
+  if constexpr (std::is_same_v<T, bf16> && D == kSegD && DF == D) {
     if (a.nseg > 0) {
       // segmented roles map k, q themselves: the preparation pass writes
       // only G~
       hipError_t e = launch_prep<T, D, false>(a, units, s);
       if (e != hipSuccess) return e;
-      return launch_seg<DECAY, ELU>(a, units, s);
+      return launch_seg<DECAY, ELU, SEL>(a, units, s);
     }
   }
   hipError_t e = launch_prep<T, D, ELU>(a, units, s);
@@ -1611,7 +1715,10 @@ int backward_segments(int64_t units, int64_t n, int d, int dtype) {
 size_t backward_agg_floats(int64_t units, int nseg) {
   // aggregates of the dq and dk roles (the fused dk and dv readout takes
   // dk's)
-  return nseg > 1 ? static_cast<size_t>(2 * units * nseg) * kSegSlot : 0;
+  // and, after them, each segment's sum of log2 gamma (a decay per
+  // position; unused otherwise)
+  return nseg > 1 ? static_cast<size_t>(2 * units * nseg) * (kSegSlot + 1)
+                  : 0;
 }
 
 hipError_t launch_backward(const BwdArgs &a, int64_t units, int d, int dtype,

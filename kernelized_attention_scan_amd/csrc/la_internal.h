@@ -177,7 +177,7 @@ struct BwdArgs {
   const float *omega = nullptr;
   // Per-position decay (else null): lam = log(gamma) of every position
   // ([units][n] fp32, the layout la_forward_gated takes); decay is null
-  // then and the column-block kernel runs (nseg = 0).
+  // then.
   const float *lam = nullptr;
 };
 bool backward_supported(int d, int d_feat);

@@ -304,9 +304,9 @@ def test_backward_workspace_bytes(lib):
     # bf16 at d = 128 runs the segmented roles, which map k, q themselves
     # (no K', Q' rows) and keep segment aggregates: 6 units, 100 rows = 2
     # chunks -> 2 segments, 2 roles (dq; dk, whose state dv shares) x 8
-    # waves x 10 feature tiles x 256 floats each
+    # waves x 10 feature tiles x 256 floats each, then one float per segment
     assert K.backward_workspace_bytes(2, 3, 100, 128) == (
-        a256(rows * 160 * 2) + a256(2 * 6 * 2 * 8 * 10 * 256 * 4))
+        a256(rows * 160 * 2) + a256(2 * 6 * 2 * (8 * 10 * 256 + 1) * 4))
     # one chunk: one segment, no aggregates
     assert K.backward_workspace_bytes(2, 3, 64, 128) == a256(384 * 160 * 2)
     assert K.backward_workspace_bytes(2, 3, 100, 128, dtype=torch.float32) == (
@@ -345,10 +345,13 @@ def test_backward_gated_workspace_bytes(lib):
     import torch
     a256 = lambda x: (x + 255) // 256 * 256
     rows = 2 * 3 * 100
-    # a decay per position always takes the column-block roles: bf16 at
-    # d = 128 keeps K', Q' rows (elu + 1) and no segment aggregates
+    # a decay per position runs the same kernels as la_backward: bf16 at
+    # d = 128 takes the segmented roles, whose aggregates are followed by
+    # each segment's sum of log2 gamma (one float per role, unit, segment)
     assert K.backward_workspace_bytes(2, 3, 100, 128, gated=True) == (
-        a256(rows * 160 * 2) + 2 * a256(rows * 128 * 2))
+        a256(rows * 160 * 2) + a256(2 * 6 * 2 * (8 * 10 * 256 + 1) * 4))
+    assert K.backward_workspace_bytes(2, 3, 100, 128, gated=True) == (
+        K.backward_workspace_bytes(2, 3, 100, 128))
     assert K.backward_workspace_bytes(2, 3, 100, 64, "identity",
                                       gated=True) == a256(rows * 96 * 2)
     assert K.backward_workspace_bytes(2, 3, 100, 32, dtype=torch.float32,
