@@ -376,12 +376,13 @@ def prefill_leg(torch, K, I, cfg, args, dev):
 
 
 def backward_algorithmic(cfg):
-    """Per step of the backward: read q, k, v, out, dout and den once, write
-    dq, dk, dv once; flops of the three unnormalised linear attentions it
-    is made of (dq' and dk': widths d + 1 and d'; dv: d' and d), 4 x width
-    x width per token each."""
+    """Per step of the backward: read q, k, v, out, dout and den (and a
+    decay per position, fp32) once, write dq, dk, dv once; flops of the
+    three unnormalised linear attentions it is made of (dq' and dk': widths
+    d + 1 and d'; dv: d' and d), 4 x width x width per token each."""
     d, df = cfg.d, cfg.d_feat
-    byts = cfg.tokens * (8 * d * esize(cfg.dtype) + 4)
+    byts = cfg.tokens * (8 * d * esize(cfg.dtype) + 4 +
+                         (4 if cfg.gate is not None else 0))
     flops = cfg.tokens * (2 * 4 * (d + 1) * df + 4 * df * d)
     return byts, flops
 
@@ -391,7 +392,6 @@ def backward_leg(torch, K, I, cfg, args, dev):
     that produces out and den runs once, before the timed region)."""
     mapname = I.MAP_NAMES[cfg.mapk]
     byts, flops = backward_algorithmic(cfg)
-    byts += 4 * cfg.tokens if cfg.gate is not None else 0  # lam, fp32
     x = I.make_prefill(cfg, args.seed)
     s = {k: (None if t is None else t.to(dev)) for k, t in x.items()}
     g = torch.Generator("cpu").manual_seed(args.seed + 7)

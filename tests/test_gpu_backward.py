@@ -307,13 +307,16 @@ def test_backward_gated_grid(case, dtype):
     assert rel(out, ref_out) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_backward_gated_resets(dtype):
+def test_backward_gated_resets(dtype, d):
     """lam = -inf (gamma = 0: the state restarts) at scattered positions,
     one of them a chunk's first row and one its last, and very negative
     values elsewhere among ordinary ones: the kernel floors lam at -104,
-    where exp(lam) is 0 in fp32 as it is for -inf."""
-    cfg = I.PrefillConfig("bwd_gated_resets", B=1, H=2, n=300, d=64,
+    where exp(lam) is 0 in fp32 as it is for -inf.  (bf16 at d = 128 runs
+    the segmented roles, here one chunk per segment, so the resets also
+    sit on segment edges.)"""
+    cfg = I.PrefillConfig("bwd_gated_resets", B=1, H=2, n=300, d=d,
                           dtype=dtype, mapk=I.MAP_ELU1, gate=(-2.0, -0.5))
     lam = I.make_prefill(cfg, 11)["log_decay"].clone()
     lam[0, 0, [0, 64, 127, 200]] = -float("inf")
