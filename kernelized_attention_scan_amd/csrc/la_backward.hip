@@ -1415,15 +1415,23 @@ hipError_t launch_seg(const BwdArgs &a, int64_t units, hipStream_t s) {
 // dk, the last units nv dv (nq = d'/16, nv = d/16).  Within a role the
 // blocks of one unit get indices of one XCD (workgroups are dispatched to
 // the 8 XCDs round-robin), so the rows they all read come from its L2.
+// PART 0 runs all roles; the Performer map (d' > d) runs the dq and dk
+// roles (PART 1) and the dv role (PART 2) as two launches, since dv's
+// d'-wide tiles need more than twice the LDS of the others, which then fit
+// four workgroups to a compute unit.
+template <typename T, int DF, int PART>
+constexpr int bwd_waves() {
+  return sizeof(T) != 2 ? 1 : PART == 1 && DF > 128 ? 4 : DF <= 128 ? 3 : 2;
+}
 template <typename T, int D, int DF, bool DECAY, bool ELU, bool FG = false,
-          bool SEL = false>
+          bool SEL = false, int PART = 0>
 __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(
-    sizeof(T) == 2 ? (DF <= 128 ? 3 : 2) : 1)))
+    bwd_waves<T, DF, PART>())))
 void la_bwd_kernel(BwdArgs a, int64_t units) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int nq = DF / 16, nv = D / 16;
-  const int64_t b = blockIdx.x;
   const int64_t cq = units * nq;
+  const int64_t b = PART == 2 ? blockIdx.x + 2 * cq : blockIdx.x;
   const int role = b < cq ? kRoleDQ : b < 2 * cq ? kRoleDK : kRoleDV;
   int64_t i = role == kRoleDQ ? b : role == kRoleDK ? b - cq : b - 2 * cq;
   const int nblk = role == kRoleDV ? nv : nq;
@@ -1431,12 +1439,16 @@ void la_bwd_kernel(BwdArgs a, int64_t units) {
   if (span % 8 == 0) i = (i % 8) * (span / 8) + i / 8;
   const int64_t unit = i / nblk;
   const int blk = static_cast<int>(i % nblk);
-  if (role == kRoleDQ)
-    bwd_role<T, D, DF, kRoleDQ, DECAY, ELU, FG, SEL>(a, unit, blk, smem);
-  else if (role == kRoleDK)
-    bwd_role<T, D, DF, kRoleDK, DECAY, ELU, FG, SEL>(a, unit, blk, smem);
-  else
+  if constexpr (PART == 2) {
     bwd_role<T, D, DF, kRoleDV, DECAY, ELU, FG, SEL>(a, unit, blk, smem);
+  } else {
+    if (role == kRoleDQ)
+      bwd_role<T, D, DF, kRoleDQ, DECAY, ELU, FG, SEL>(a, unit, blk, smem);
+    else if (role == kRoleDK)
+      bwd_role<T, D, DF, kRoleDK, DECAY, ELU, FG, SEL>(a, unit, blk, smem);
+    else if constexpr (PART == 0)
+      bwd_role<T, D, DF, kRoleDV, DECAY, ELU, FG, SEL>(a, unit, blk, smem);
+  }
 }
 
 template <typename T, int D, bool ELU>
@@ -1464,21 +1476,36 @@ hipError_t launch_all(const BwdArgs &a, int64_t units, hipStream_t s) {
   }
   hipError_t e = launch_prep<T, D, ELU>(a, units, s);
   if (e != hipSuccess) return e;
-  constexpr size_t lds =
-      std::max({BShape<T, D, DF, kRoleDQ, DECAY, SEL>::lds_bytes,
-                BShape<T, D, DF, kRoleDK, DECAY, SEL>::lds_bytes,
-                BShape<T, D, DF, kRoleDV, DECAY, SEL>::lds_bytes});
-  static_assert(lds <= 160 * 1024, "LDS of one workgroup");
-  static const hipError_t once = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(
-          &la_bwd_kernel<T, D, DF, DECAY, ELU, FG, SEL>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-  if (once != hipSuccess) return once;
-  const int64_t blocks = units * (2 * (DF / 16) + D / 16);
-  hipLaunchKernelGGL((la_bwd_kernel<T, D, DF, DECAY, ELU, FG, SEL>),
-                     dim3(static_cast<unsigned>(blocks)), dim3(kBThreads), lds,
-                     s, a, units);
-  return hipGetLastError();
+  using FQ = BShape<T, D, DF, kRoleDQ, DECAY, SEL>;
+  using FK = BShape<T, D, DF, kRoleDK, DECAY, SEL>;
+  using FV = BShape<T, D, DF, kRoleDV, DECAY, SEL>;
+  // one launch of PART with lds bytes and blocks workgroups
+  auto run = [&](auto part, size_t lds, int64_t blocks) -> hipError_t {
+    constexpr int P = decltype(part)::value;
+    auto *k = &la_bwd_kernel<T, D, DF, DECAY, ELU, FG, SEL, P>;
+    static const hipError_t once = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(k),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (once != hipSuccess) return once;
+    hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(blocks)),
+                       dim3(kBThreads), lds, s, a, units);
+    return hipGetLastError();
+  };
+  if constexpr (FG) {
+    constexpr size_t lds1 = std::max(FQ::lds_bytes, FK::lds_bytes);
+    static_assert(lds1 <= 160 * 1024 && FV::lds_bytes <= 160 * 1024,
+                  "LDS of one workgroup");
+    e = run(std::integral_constant<int, 1>{}, lds1, units * 2 * (DF / 16));
+    if (e != hipSuccess) return e;
+    return run(std::integral_constant<int, 2>{}, FV::lds_bytes,
+               units * (D / 16));
+  } else {
+    constexpr size_t lds =
+        std::max({FQ::lds_bytes, FK::lds_bytes, FV::lds_bytes});
+    static_assert(lds <= 160 * 1024, "LDS of one workgroup");
+    return run(std::integral_constant<int, 0>{}, lds,
+               units * (2 * (DF / 16) + D / 16));
+  }
 }
 
 // Performer map ("Linear attention research 2026" page, Performer random
@@ -1490,49 +1517,68 @@ hipError_t launch_all(const BwdArgs &a, int64_t units, hipStream_t s) {
 // when q'_t is scaled (q'_t mu_t / q'_t . nu_t), so q'_t . dq'_t = 0.  It is
 // dropped there (with_sum = 0): computed from rounded operands it would
 // only add the noise of a cancelling sum of d' terms.
-// 64 rows per step: u = gx' * phi(x) ([row][r]) and omega ([c][r], kept for
-// the whole kernel) in LDS, the product u omega^T on the matrix cores in
-// fp32 (v_mfma_f32_16x16x4_f32: exact products, fp32 sums); each wave takes
-// every fourth 16 x 16 output tile.  Rows past the end are skipped.
+// 64 rows per step: u = gx' * phi(x) ([row][r]) in LDS, the product
+// u omega^T on the matrix cores in fp32 (v_mfma_f32_16x16x4_f32: exact
+// products, fp32 sums); each wave takes every fourth 16 x 16 output tile,
+// whose columns are always the same one or two blocks of 16 rows of omega:
+// their fragments are loaded once per workgroup and kept in registers (at
+// most 64 values per lane for d * d' <= 16384), which leaves LDS to u and
+// lets two workgroups share a compute unit.  Rows past the end are skipped.
 constexpr int kPfRows = 64;
 template <int D, int DF>
 constexpr size_t pf_grad_lds() {
-  return sizeof(float) * (static_cast<size_t>(D + kPfRows) * (DF + 4) + kPfRows);
+  return sizeof(float) * (static_cast<size_t>(kPfRows) * (DF + 4) + kPfRows);
 }
 
 template <typename T, int D, int DF>
-__global__ __launch_bounds__(kBThreads) void la_bwd_pf_grad_kernel(
+__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(
+    2))) void la_bwd_pf_grad_kernel(
     const T *__restrict__ xf, const float *__restrict__ gf,
     const T *__restrict__ x, T *__restrict__ dx,
     const float *__restrict__ omega, int64_t rows, int with_sum) {
   constexpr int PR = kPfRows, L = DF + 4;  // row stride of omega and u
   constexpr int VEC = 16 / sizeof(T);
-  constexpr int NT = (PR / 16) * (D / 16), TPW = (NT + kBWaves - 1) / kBWaves;
+  constexpr int NT = (PR / 16) * (D / 16), TPW = NT / kBWaves;
   constexpr int TPR = DF / VEC;            // fill threads per row
+  // column blocks of omega a wave's tiles use: tile w + kBWaves m has
+  // column block (w + kBWaves m) % (D / 16), which is block j = that / 4
+  // of the wave's own list w % (D / 16) + kBWaves j
+  constexpr int NCB = D / 16, NB = (NCB + kBWaves - 1) / kBWaves;
   static_assert(DF % 32 == 0 && D % 16 == 0 && kBThreads % TPR == 0 &&
-                    TPR <= kWave,
+                    TPR <= kWave && NT % kBWaves == 0 &&
+                    (NCB % kBWaves == 0 || kBWaves % NCB == 0),
                 "tiling");
   extern __shared__ __align__(16) unsigned char smem[];
-  float *om = reinterpret_cast<float *>(smem);  // [D][L]: omega
-  float *u = om + D * L;                        // [PR][L]
+  float *u = reinterpret_cast<float *>(smem);   // [PR][L]
   float *su = u + PR * L;                       // [PR]
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = tid >> 6, g = lane >> 4, li = lane & 15;
-  for (int i = tid; i < D * DF; i += kBThreads)
-    om[(i / DF) * L + i % DF] = omega[i];
+  Frag<float> of[NB][DF / 32];  // omega rows of the wave's column blocks
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int kb = 0; kb < DF / 32; ++kb)
+      load_frag8(of[j][kb],
+                 omega + (16 * (w % NCB + kBWaves * j) + li) * DF + 32 * kb +
+                     8 * g);
   const int64_t nsteps = (rows + PR - 1) / PR;
   for (int64_t st = blockIdx.x; st < nsteps; st += gridDim.x) {
     const int64_t row0 = st * PR;
-    __syncthreads();  // om ready; the previous step's u, su are read
-    // fill: TPR consecutive threads take one row, VEC features each; all
-    // of a thread's loads are issued before any is used
-    constexpr int FI = PR * TPR / kBThreads;
-    static_assert(PR * TPR % kBThreads == 0, "whole fill rounds");
+    __syncthreads();  // the previous step's u, su are read
+    // fill: TPR consecutive threads take one row, VEC features each; the
+    // loads of each batch of 4 rounds (of all, when there are fewer) are
+    // issued before any is used
+    constexpr int FA = PR * TPR / kBThreads;  // fill rounds
+    constexpr int FH = FA > 4 ? FA / 4 : 1, FI = FA / FH;
+    static_assert(PR * TPR % kBThreads == 0 && FA % FH == 0,
+                  "whole fill rounds");
+#pragma unroll
+    for (int hf = 0; hf < FH; ++hf) {
     f32x4 gl[FI][VEC / 4];
     u32x4 xl[FI];
 #pragma unroll
     for (int it = 0; it < FI; ++it) {
-      const int p = tid + kBThreads * it;
+      const int p = tid + kBThreads * (FI * hf + it);
       const int rr = p / TPR, f0 = (p % TPR) * VEC;
       const int64_t off = (row0 + rr) * DF + f0;
       const bool in = row0 + rr < rows;
@@ -1545,7 +1591,7 @@ __global__ __launch_bounds__(kBThreads) void la_bwd_pf_grad_kernel(
     }
 #pragma unroll
     for (int it = 0; it < FI; ++it) {
-      const int p = tid + kBThreads * it;
+      const int p = tid + kBThreads * (FI * hf + it);
       const int rr = p / TPR, f0 = (p % TPR) * VEC;
       float a[VEC], b[VEC];
 #pragma unroll
@@ -1563,37 +1609,34 @@ __global__ __launch_bounds__(kBThreads) void la_bwd_pf_grad_kernel(
       part = sum_group<TPR>(part);
       if (p % TPR == 0) su[rr] = with_sum ? part : 0.f;
     }
+    }
     __syncthreads();
     f32x4 acc[TPW];
 #pragma unroll
     for (int m = 0; m < TPW; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
+#pragma unroll
     for (int kb = 0; kb < DF / 32; ++kb) {
 #pragma unroll
       for (int m = 0; m < TPW; ++m) {
-        const int t = w + kBWaves * m;
-        if (t < NT) {
-          const int mt = t / (D / 16), nt = t % (D / 16);
-          Frag<float> fa, fb;
-          load_frag8(fa, u + (16 * mt + li) * L + 32 * kb + 8 * g);
-          load_frag8(fb, om + (16 * nt + li) * L + 32 * kb + 8 * g);
-          acc[m] = mma(fa, fb, acc[m]);
-        }
+        // (w < kBWaves: block j of tile m is known at compile time)
+        const int mt = (w + kBWaves * m) / NCB;
+        const int j = NCB >= kBWaves ? m % (NCB / kBWaves) : 0;
+        Frag<float> fa;
+        load_frag8(fa, u + (16 * mt + li) * L + 32 * kb + 8 * g);
+        acc[m] = mma(fa, of[j][kb], acc[m]);
       }
     }
 #pragma unroll
     for (int m = 0; m < TPW; ++m) {
       const int t = w + kBWaves * m;
-      if (t < NT) {
-        const int mt = t / (D / 16), nt = t % (D / 16);
+      const int mt = t / NCB, nt = t % NCB;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int rl = 16 * mt + 4 * g + r;
-          const int64_t row = row0 + rl;
-          if (row < rows) {
-            const int64_t o = row * D + 16 * nt + li;
-            dx[o] = from_f32<T>(acc[m][r] - to_f32(x[o]) * su[rl]);
-          }
+      for (int r = 0; r < 4; ++r) {
+        const int rl = 16 * mt + 4 * g + r;
+        const int64_t row = row0 + rl;
+        if (row < rows) {
+          const int64_t o = row * D + 16 * nt + li;
+          dx[o] = from_f32<T>(acc[m][r] - to_f32(x[o]) * su[rl]);
         }
       }
     }
@@ -1605,10 +1648,9 @@ __global__ __launch_bounds__(kBThreads) void la_bwd_pf_grad_kernel(
 // workspace in fp32, dv to its output), then dq and dk through the map.
 template <typename T, int D, int DF>
 hipError_t launch_pf(const BwdArgs &a, int64_t units, hipStream_t s) {
-  hipError_t e = launch_prep<T, D, false>(a, units, s);
-  if (e != hipSuccess) return e;
-  e = a.decay ? launch_all<T, D, DF, true, false, true>(a, units, s)
-              : launch_all<T, D, DF, false, false, true>(a, units, s);
+  // (launch_all runs the preparation pass first)
+  hipError_t e = a.decay ? launch_all<T, D, DF, true, false, true>(a, units, s)
+                         : launch_all<T, D, DF, false, false, true>(a, units, s);
   if (e != hipSuccess) return e;
   constexpr size_t lds = pf_grad_lds<D, DF>();
   static_assert(lds <= 160 * 1024, "LDS of the conversion pass");
