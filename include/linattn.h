@@ -323,8 +323,7 @@ la_status la_forward_gated_train(const void *q, const void *k, const void *v,
  *              below -104 act as -104 (gamma = 0 in fp32 either way).
  *   layout   : LA_LD_POSITION; the other layouts return LA_ERR_UNSUPPORTED.
  *   workspace: device, at least la_backward_gated_workspace_bytes(...).
- *   Supported: ELU1, IDENTITY with d == d_feat in {16, 32, 64, 128};
- *              PERFORMER returns LA_ERR_UNSUPPORTED.
+ *   Supported: the sizes la_backward supports, for all three maps.
  */
 la_status la_backward_gated(const void *q, const void *k, const void *v,
                             const void *out, const float *den,
@@ -336,8 +335,9 @@ la_status la_backward_gated(const void *q, const void *k, const void *v,
 
 /*
  * la_backward_gated_workspace_bytes -- device workspace la_backward_gated
- * needs: that of la_backward for the same sizes (the segment state sums
- * carry each segment's sum of log2 gamma in space la_backward reserves).
+ * needs: that of la_backward for the same sizes and map (the segment state
+ * sums carry each segment's sum of log2 gamma in space la_backward
+ * reserves).
  * Pure host function; 0 for arguments la_backward_gated would reject and
  * for empty sizes.
  */

@@ -675,8 +675,8 @@ static la_status backward_performer(const void *q, const void *k,
                                     void *dq, void *dk, void *dv, int B, int H,
                                     int64_t n, int d, int d_feat,
                                     const float *omega, const float *decay,
-                                    la_dtype dtype, void *workspace,
-                                    void *stream) {
+                                    const float *lam, la_dtype dtype,
+                                    void *workspace, void *stream) {
   if (!la::backward_performer_supported(d, d_feat))
     return fail(LA_ERR_UNSUPPORTED,
                 "la_backward PERFORMER: d in {32, 64, 128}, d_feat in {32, "
@@ -701,7 +701,8 @@ static la_status backward_performer(const void *q, const void *k,
   la::BwdArgs a;
   a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.den = den;
   a.dq = dq; a.dk = dk; a.dv = dv;
-  a.decay = decay;
+  a.decay = lam ? nullptr : decay;
+  a.lam = lam;
   a.H = H;
   a.n = n;
   a.dqk = d;
@@ -730,9 +731,13 @@ size_t la_backward_gated_workspace_bytes(int B, int H, int64_t n, int d,
                                          la_dtype dtype) {
   if (B <= 0 || H <= 0 || n <= 0 || !valid_dtype(dtype) || !valid_map(map))
     return 0;
-  if (map == LA_MAP_PERFORMER || !la::backward_supported(d, d_feat)) return 0;
+  if (map == LA_MAP_PERFORMER ? !la::backward_performer_supported(d, d_feat)
+                              : !la::backward_supported(d, d_feat))
+    return 0;
   const int64_t units = static_cast<int64_t>(B) * H;
   if (units * n > (int64_t{1} << 46) || units > (int64_t{1} << 26)) return 0;
+  if (map == LA_MAP_PERFORMER)
+    return backward_ws_performer(units, n, d, d_feat, dtype, nullptr, nullptr);
   return backward_ws(units, n, d, map, dtype, nullptr);
 }
 
@@ -757,8 +762,8 @@ static la_status backward_impl(const void *q, const void *k, const void *v,
       return fail(LA_ERR_INVALID_ARG, "ELU1 needs d_feat == d");
     if (map == LA_MAP_PERFORMER)
       return backward_performer(q, k, v, out, den, dout, dq, dk, dv, B, H, n,
-                                d, d_feat, omega, decay, dtype, workspace,
-                                stream);
+                                d, d_feat, omega, decay, lam, dtype,
+                                workspace, stream);
     if (!la::backward_supported(d, d_feat))
       return fail(LA_ERR_UNSUPPORTED,
                   "la_backward: d = d_feat in {16, 32, 64, 128} is built "
@@ -827,9 +832,6 @@ la_status la_backward_gated(const void *q, const void *k, const void *v,
   if (layout != LA_LD_POSITION)
     return fail(LA_ERR_UNSUPPORTED,
                 "la_backward_gated: only LA_LD_POSITION is built");
-  if (map == LA_MAP_PERFORMER)
-    return fail(LA_ERR_UNSUPPORTED,
-                "la_backward_gated: the PERFORMER map is not built");
   if (!log_decay && static_cast<int64_t>(B) * H > 0 && n > 0)
     return fail(LA_ERR_INVALID_ARG, "null log_decay");
   return backward_impl(q, k, v, out, den, dout, dq, dk, dv, B, H, n, d,

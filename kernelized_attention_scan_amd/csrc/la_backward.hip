@@ -1649,8 +1649,10 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(
 template <typename T, int D, int DF>
 hipError_t launch_pf(const BwdArgs &a, int64_t units, hipStream_t s) {
   // (launch_all runs the preparation pass first)
-  hipError_t e = a.decay ? launch_all<T, D, DF, true, false, true>(a, units, s)
-                         : launch_all<T, D, DF, false, false, true>(a, units, s);
+  hipError_t e =
+      a.lam     ? launch_all<T, D, DF, true, false, true, true>(a, units, s)
+      : a.decay ? launch_all<T, D, DF, true, false, true>(a, units, s)
+                : launch_all<T, D, DF, false, false, true>(a, units, s);
   if (e != hipSuccess) return e;
   constexpr size_t lds = pf_grad_lds<D, DF>();
   static_assert(lds <= 160 * 1024, "LDS of the conversion pass");

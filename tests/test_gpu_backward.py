@@ -364,6 +364,38 @@ def test_backward_gated_full_size_every_unit():
     assert max(worst) <= GTOL[torch.bfloat16]
 
 
+GATED_PF = [
+    # (name, B, H, n, d, m, dtype): the Performer map with a decay per
+    # position (features, column-block roles with the decay tables, the
+    # map's chain rule)
+    ("d64_m256_bf16", 1, 2, 300, 64, 256, torch.bfloat16),
+    ("d32_m64_fp32", 2, 1, 200, 32, 64, torch.float32),
+    ("d128_m128_bf16_one_chunk", 1, 2, 50, 128, 128, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("case", GATED_PF, ids=[c[0] for c in GATED_PF])
+def test_backward_gated_performer(case):
+    name, B, H, n, d, m, dtype = case
+    cfg = I.PERFORMER.replace(B=B, H=H, n=n, d=d, m=m, dtype=dtype,
+                              gate=(-2.0, -0.5))
+    x = make(cfg, 31)
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    om, ld = dev(x["omega"]), dev(x["log_decay"])
+    out, den = K.forward_train(q, k, v, "performer", omega=om, log_decay=ld)
+    grads = K.backward(q, k, v, out, den, dev(x["dout"]), "performer",
+                       omega=om, log_decay=ld)
+    torch.cuda.synchronize()
+    ref = oracle.backward_gated(f64(x["q"]), f64(x["k"]), f64(x["v"]),
+                                f64(x["dout"]), I.MAP_PERFORMER,
+                                f64(x["omega"]), f64(x["log_decay"]),
+                                oracle.LD_POSITION)
+    errs = [rel(gq, r) for gq, r in zip(grads, ref)]
+    print(f"gated performer {name}: dq {errs[0]:.2e} dk {errs[1]:.2e} "
+          f"dv {errs[2]:.2e}", flush=True)
+    assert max(errs) <= GTOL[dtype], errs
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_autograd_op_gated_matches_oracle(dtype):
     """linear_attention(..., log_decay=...) as a torch op: autograd

@@ -357,8 +357,12 @@ def test_backward_gated_workspace_bytes(lib):
     assert K.backward_workspace_bytes(2, 3, 100, 32, dtype=torch.float32,
                                       gated=True) == (
         a256(rows * 64 * 4) + 2 * a256(rows * 32 * 4))
-    # not built: the Performer map, d != d_feat, other d; empty sizes
+    # the Performer map: as la_backward's; not built: d != d_feat, other
+    # d; empty sizes
     assert K.backward_workspace_bytes(2, 3, 100, 64, "performer",
+                                      d_feat=256, gated=True) == (
+        K.backward_workspace_bytes(2, 3, 100, 64, "performer", d_feat=256))
+    assert K.backward_workspace_bytes(2, 3, 100, 16, "performer",
                                       gated=True) == 0
     assert K.backward_workspace_bytes(2, 3, 100, 48, gated=True) == 0
     assert K.backward_workspace_bytes(2, 3, 0, 64, gated=True) == 0
@@ -373,7 +377,8 @@ def test_gated_train_and_backward_reject(lib):
     assert bwd(B.LD_CHANNEL, B.MAP_ELU1, vp, vp) == B.LA_ERR_UNSUPPORTED
     assert bwd(B.LD_BOTH, B.MAP_ELU1, vp, vp) == B.LA_ERR_UNSUPPORTED
     assert bwd(7, B.MAP_ELU1, vp, vp) == B.LA_ERR_INVALID_ARG
-    assert bwd(B.LD_POSITION, B.MAP_PERFORMER, vp, vp) == B.LA_ERR_UNSUPPORTED
+    # the Performer map needs omega
+    assert bwd(B.LD_POSITION, B.MAP_PERFORMER, vp, vp) == B.LA_ERR_INVALID_ARG
     assert bwd(B.LD_POSITION, B.MAP_ELU1, None, vp) == B.LA_ERR_INVALID_ARG
     assert bwd(B.LD_POSITION, B.MAP_ELU1, vp, None) == B.LA_ERR_WORKSPACE
     fwd = lambda lay, den, lam: lib.la_forward_gated_train(
