@@ -412,3 +412,59 @@ def test_autograd_op_gated_matches_oracle(dtype):
                                  f64(x["log_decay"]), oracle.LD_POSITION)
     for t, r in zip((q, k, v), refs):
         assert rel(t.grad, r) <= GTOL[dtype]
+
+
+def test_backward_random_shapes():
+    """Seeded random configurations of the whole backward, run in one
+    sequence on the binding's shared workspace: map (elu + 1, identity,
+    Performer), d and d' within the built sizes, ragged n, B and H, no
+    decay, a decay per head or a decay per position, and the storage type;
+    every unit's gradients against the oracle's adjoint."""
+    rng = np.random.default_rng(20261203)
+    worst = {torch.bfloat16: 0.0, torch.float32: 0.0}
+    for i in range(24):
+        dtype = [torch.bfloat16, torch.float32][int(rng.integers(2))]
+        mp = ["elu1", "identity", "performer"][int(rng.integers(3))]
+        if mp == "performer":
+            d = int(rng.choice([32, 64, 128]))
+            m = int(rng.choice([m for m in (32, 64, 128, 256)
+                                if d * m <= 16384]))
+        else:
+            d = int(rng.choice([16, 32, 64, 128]))
+            m = d
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        n = int(rng.integers(1, 700))
+        kind = ["none", "head", "position"][int(rng.integers(3))]
+        mapk = {"elu1": I.MAP_ELU1, "identity": I.MAP_IDENTITY,
+                "performer": I.MAP_PERFORMER}[mp]
+        base = I.PERFORMER if mp == "performer" else I.ELU1_CAUSAL
+        cfg = base.replace(B=B, H=H, n=n, d=d, m=m, dtype=dtype, mapk=mapk,
+                           decay=(-2.0, -0.5) if kind == "head" else None,
+                           gate=(-2.0, -0.5) if kind == "position" else None)
+        print(f"case {i}: {mp} d={d} m={m} B={B} H={H} n={n} {kind} "
+              f"{dtype}", flush=True)
+        x = make(cfg, 100 + i)
+        q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+        om, dec, ld = dev(x["omega"]), dev(x["decay"]), dev(x["log_decay"])
+        out, den = K.forward_train(q, k, v, mp, decay=dec, omega=om,
+                                   log_decay=ld)
+        grads = K.backward(q, k, v, out, den, dev(x["dout"]), mp, decay=dec,
+                           omega=om, log_decay=ld)
+        torch.cuda.synchronize()
+        if kind == "position":
+            ref = oracle.backward_gated(f64(x["q"]), f64(x["k"]), f64(x["v"]),
+                                        f64(x["dout"]), mapk, f64(x["omega"]),
+                                        f64(x["log_decay"]),
+                                        oracle.LD_POSITION)
+        else:
+            ref = oracle.backward(f64(x["q"]), f64(x["k"]), f64(x["v"]),
+                                  f64(x["dout"]), mapk, f64(x["omega"]),
+                                  f64(x["decay"]))
+        if n == 1:   # dq = dk = 0 exactly: compare dv only (see above)
+            errs = [rel(grads[2], ref[2])]
+        else:
+            errs = [rel(gq, r) for gq, r in zip(grads, ref)]
+        worst[dtype] = max(worst[dtype], max(errs))
+        assert max(errs) <= GTOL[dtype], (i, errs)
+    print(f"random shapes: worst bf16 {worst[torch.bfloat16]:.2e}, "
+          f"fp32 {worst[torch.float32]:.2e}", flush=True)
