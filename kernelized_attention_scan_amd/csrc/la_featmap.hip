@@ -75,13 +75,36 @@ __global__ __launch_bounds__(kFmThreads) void la_featmap_performer_kernel(
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, li = lane & 15;
 
-  // omega [D][m] -> omega^T hi/lo [m][DP] (zero padding for D < 32).
-  for (int i = tid; i < m * DP; i += kFmThreads) {
-    const int r = i % m, c = i / m;
-    bf16 hi = from_f32<bf16>(0.f), lo = from_f32<bf16>(0.f);
-    if (c < D) split_bf16(omega[c * m + r], hi, lo);
-    sWh[r * LW + c] = hi;
-    sWl[r * LW + c] = lo;
+  // omega [D][m] -> omega^T hi/lo [m][DP] (zero padding for D < 32): each
+  // thread takes 4 consecutive features of one row of omega per piece, and
+  // the loads of 8 pieces are issued before any is written (one round trip
+  // to the cache per 8 pieces instead of one per value)
+  {
+    const int m4 = m / 4, pieces = m4 * DP;
+    constexpr int BATCH = 8;
+    for (int base = tid; base < pieces; base += kFmThreads * BATCH) {
+      f32x4 v[BATCH];
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j) {
+        const int i = base + kFmThreads * j, c = i / m4, r = 4 * (i % m4);
+        v[j] = i < pieces && c < D
+                   ? *reinterpret_cast<const f32x4 *>(omega + c * m + r)
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j) {
+        const int i = base + kFmThreads * j, c = i / m4, r = 4 * (i % m4);
+        if (i < pieces) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            bf16 hi, lo;
+            split_bf16(v[j][e], hi, lo);
+            sWh[(r + e) * LW + c] = hi;
+            sWl[(r + e) * LW + c] = lo;
+          }
+        }
+      }
+    }
   }
   __syncthreads();
   const float inv_sqrt_m = 1.f / sqrtf(static_cast<float>(m));
@@ -140,8 +163,10 @@ hipError_t run_performer(const void *x, void *y, const float *omega,
       reinterpret_cast<const void *>(&la_featmap_performer_kernel<Tin, Tout, D>),
       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (once != hipSuccess) return once;
+  // one round of resident workgroups (two per compute unit), each filling
+  // omega^T once and then taking every grid-th tile
   const int64_t tiles = (rows + 63) / 64;
-  const int64_t grid = tiles < 1024 ? tiles : 1024;
+  const int64_t grid = tiles < 2 * kCUs ? tiles : 2 * kCUs;
   hipLaunchKernelGGL((la_featmap_performer_kernel<Tin, Tout, D>), dim3(grid),
                      dim3(kFmThreads), lds, s, static_cast<const Tin *>(x),
                      static_cast<Tout *>(y), omega, rows, m);
